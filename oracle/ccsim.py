@@ -1,0 +1,732 @@
+"""ccsim -- a plain, slow, step-by-step CPU simulator of the collective schedules.
+
+TEST INFRASTRUCTURE ONLY.  This module is the oracle that the HIP library is
+checked against.  Only the test suite, the smoke check and the CPU-baseline leg
+of the benchmark may import it; the product path (the C-ABI library and its
+Python binding) never does, and this module imports nothing from the product.
+It shares no code, table or constant generator with the HIP path.
+
+Every function below follows a passage of the source pages, cited by page
+title and section.  Page keys used in the comments:
+
+  [MLSys-6]  MLSys textbook vol. 2, ch. 6 "集合通信" (gptbert.com)
+  [Slides]   "集合通信与分片矩阵乘法" slide deck (hs-black.github.io)
+  [AR-notes] "AllReduce" algorithm notes (t6page.pages.dev)
+  [Lesson3]  "第 3 课：分布式通信原语" course lesson (hsthanb4.github.io)
+  [Blog]     "分布式大模型集合通信" blog post (bowenei.github.io)
+
+Conventions (see each function for the passage it follows):
+
+* N logical ranks; each rank r holds a 1-D array x_r of M elements.
+* Chunk c of a rank's vector is [b_c, b_{c+1}) with b_c = floor(c*M/N).  The
+  pages split evenly and require N | M ([Lesson3], simulator exercise); floor
+  boundaries are the plain generalisation and agree with the even split
+  whenever N divides M.
+* Element types: "int32" (two's-complement wrap for SUM and PROD), "f32",
+  and "bf16" carried as uint16 bit patterns.  bf16 inputs are widened exactly
+  to float32, every partial result stays float32 across all steps, and the
+  final value is rounded once to bf16 (round to nearest, ties to even).
+* A step that combines data does  acc_local = op(acc_local, incoming)  with a
+  snapshot of everything sent in that step taken before any rank updates
+  ([Lesson3], reference answer: the sends of one step are copied first so
+  that no rank reads data another rank already updated in the same step).
+* Float MAX is the IEEE-754-2019 "maximum": NaN if either operand is NaN,
+  +0 counts as larger than -0.  It is commutative and associative, so every
+  schedule reaches the same bits; SUM and PROD are not associative in floating
+  point ([MLSys-6], "六种核心原语": different schedules change the low bits),
+  which is why this simulator performs the steps themselves.
+
+Parity is pinned by tests/test_oracle_*.py against the worked examples the
+pages print, their step tables, closed forms, brute force on tiny inputs and an
+fp64 error bound; nothing in this module is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Callable, Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+DTYPES = ("int32", "f32", "bf16")
+OPS = ("sum", "max", "prod")
+
+
+# --------------------------------------------------------------------------
+# bf16 <-> f32 by definition
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 exactly.
+
+    bf16 is the upper half of an IEEE binary32 word, so the widening appends
+    sixteen zero bits; no rounding is involved.
+    """
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _bf16_value_f64(hi16: np.ndarray) -> np.ndarray:
+    """Numeric value (float64) of bf16 patterns, with the all-ones-exponent
+    finite continuation 2**128 used for the overflow candidate."""
+    hi16 = hi16.astype(np.uint32)
+    mag = hi16 & 0x7FFF
+    sign = np.where(hi16 & 0x8000, -1.0, 1.0)
+    out = (mag.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    # the pattern just above the largest finite bf16 is +inf; for rounding
+    # decisions it stands for the value 2**128 (unbounded exponent range)
+    out = np.where(mag == 0x7F80, 2.0 ** 128, out)
+    return sign * np.abs(out)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even) by definition.
+
+    For each finite x, take the two bf16 neighbours that bracket it (the
+    truncation toward zero and the next value away from zero), measure both
+    distances exactly in float64 and keep the nearer one; on a tie keep the one
+    whose last mantissa bit is 0.  A value that rounds to 2**128 or beyond is an
+    overflow and becomes +-inf.  NaN maps to a quiet NaN with the same sign.
+    """
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    with np.errstate(invalid="ignore", over="ignore"):
+        return _f32_to_bf16_bits(x)
+
+
+def _f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    u = x.view(np.uint32)
+    lo = (u >> np.uint32(16)).astype(np.uint32)          # truncation toward zero
+    hi = lo + np.uint32(1)                                # next bf16 away from zero
+    xv = x.astype(np.float64)
+    d_lo = np.abs(xv - _bf16_value_f64(lo))
+    d_hi = np.abs(_bf16_value_f64(hi) - xv)
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo & 1) == 1))
+    r = np.where(take_hi, hi, lo).astype(np.uint32)
+    # exact bf16 values (low half zero) are returned unchanged
+    r = np.where((u & 0xFFFF) == 0, lo, r)
+    nan = np.isnan(x)
+    r = np.where(nan, (lo | 0x0040), r)
+    inf = np.isinf(x)
+    r = np.where(inf, lo, r)
+    return (r & 0xFFFF).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# element types and the combine operator
+# --------------------------------------------------------------------------
+
+def to_acc(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Input buffer -> accumulator array (int32, or float32 for f32/bf16)."""
+    if dtype == "int32":
+        return np.array(x, dtype=np.int32, copy=True)
+    if dtype == "f32":
+        return np.array(x, dtype=np.float32, copy=True)
+    if dtype == "bf16":
+        return bf16_bits_to_f32(np.asarray(x, dtype=np.uint16)).copy()
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def from_acc(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Accumulator -> output buffer type (bf16 rounds once, here)."""
+    if dtype == "int32":
+        return np.array(a, dtype=np.int32, copy=True)
+    if dtype == "f32":
+        return np.array(a, dtype=np.float32, copy=True)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _fmax_ieee(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    out = np.where(a > b, a, b)
+    both_zero = (a == 0) & (b == 0)
+    z = (a.view(np.uint32) & b.view(np.uint32)).view(np.float32)
+    out = np.where(both_zero, z, out)
+    nan = np.isnan(a) | np.isnan(b)
+    return np.where(nan, np.float32(np.nan), out).astype(np.float32)
+
+
+def combine(op: str, local: np.ndarray, incoming: np.ndarray) -> np.ndarray:
+    """The elementwise reduction operator: local (+) incoming.
+
+    SUM, MAX and PROD are the operators the pages name ([Lesson3], "核心概念"
+    item 1; [Blog], "Reduce & All Reduce").  Integer SUM and PROD wrap modulo
+    2**32 (NumPy int32 array arithmetic wraps).
+    """
+    if local.dtype == np.int32:
+        if op == "sum":
+            return np.add(local, incoming, dtype=np.int32)
+        if op == "prod":
+            return np.multiply(local, incoming, dtype=np.int32)
+        if op == "max":
+            return np.maximum(local, incoming)
+    else:
+        local = local.astype(np.float32, copy=False)
+        incoming = incoming.astype(np.float32, copy=False)
+        if op == "sum":
+            return np.add(local, incoming, dtype=np.float32)
+        if op == "prod":
+            return np.multiply(local, incoming, dtype=np.float32)
+        if op == "max":
+            return _fmax_ieee(local, incoming)
+    raise ValueError(f"unknown op {op!r}")
+
+
+# --------------------------------------------------------------------------
+# chunking
+# --------------------------------------------------------------------------
+
+def chunk_bounds(M: int, N: int) -> List[int]:
+    """b_c = floor(c*M/N) for c = 0..N: N contiguous chunks, possibly empty
+    when M < N ([Lesson3], simulator: each rank views its tensor as N blocks)."""
+    return [(c * M) // N for c in range(N + 1)]
+
+
+def chunk_of(idx: np.ndarray, M: int, N: int) -> np.ndarray:
+    """Chunk index of each element index (the chunk c with b_c <= e < b_{c+1})."""
+    b = np.asarray(chunk_bounds(M, N), dtype=np.int64)
+    return np.searchsorted(b, np.asarray(idx, dtype=np.int64), side="right") - 1
+
+
+# --------------------------------------------------------------------------
+# step trace / accounting record
+# --------------------------------------------------------------------------
+
+@dataclass
+class Trace:
+    """What a simulated schedule did: per step, the (src, dst, what, count)
+    transfers, and per rank the number of values sent."""
+    steps: List[List[Tuple[int, int, object, int]]] = field(default_factory=list)
+    sent: List[int] = field(default_factory=list)
+
+    @property
+    def nsteps(self) -> int:
+        return len(self.steps)
+
+
+# --------------------------------------------------------------------------
+# ring schedule
+# --------------------------------------------------------------------------
+
+def _ring_rs_phase(acc: List[np.ndarray], b: List[int], op: str, off: int,
+                   tr: Trace) -> None:
+    """Ring ReduceScatter phase, N-1 steps.
+
+    At step s rank r sends its chunk (r - s + off) mod N to rank r+1 and
+    combines the chunk (r - s - 1 + off) mod N received from rank r-1 into its
+    own copy ([AR-notes], "算法一：Ring AllReduce", 阶段 1; [Slides], "环形
+    ReduceScatter"; [Lesson3], simulator reference answer).  off = 0 is the
+    pages' formula, used inside AllReduce: rank r ends owning chunk (r+1) mod N.
+    off = -1 is the standalone ReduceScatter, whose contract puts chunk r on
+    rank r ([Slides], primitives table and the 3-rank example).
+    """
+    N = len(acc)
+    for s in range(N - 1):
+        send_idx = [(r - s + off) % N for r in range(N)]
+        sent = [acc[r][b[send_idx[r]]:b[send_idx[r] + 1]].copy() for r in range(N)]
+        step = []
+        for r in range(N):
+            src = (r - 1) % N
+            recv_idx = (r - s - 1 + off) % N
+            assert recv_idx == send_idx[src]
+            lo, hi = b[recv_idx], b[recv_idx + 1]
+            acc[r][lo:hi] = combine(op, acc[r][lo:hi], sent[src])
+            tr.sent[src] += hi - lo
+            step.append((src, r, recv_idx, hi - lo))
+        tr.steps.append(step)
+
+
+def _ring_ag_phase(acc: List[np.ndarray], b: List[int], own: List[int],
+                   tr: Trace) -> None:
+    """Ring AllGather phase, N-1 steps: each rank forwards what it received in
+    the previous step ([Slides], "环形 AllGather"; [Lesson3], simulator phase 2).
+    own[r] is the chunk rank r holds complete at the start.  At step s rank r
+    sends chunk (own[r] - s) mod N and stores chunk (own[r-1] - s) mod N."""
+    N = len(acc)
+    for s in range(N - 1):
+        send_idx = [(own[r] - s) % N for r in range(N)]
+        sent = [acc[r][b[send_idx[r]]:b[send_idx[r] + 1]].copy() for r in range(N)]
+        step = []
+        for r in range(N):
+            src = (r - 1) % N
+            recv_idx = send_idx[src]
+            lo, hi = b[recv_idx], b[recv_idx + 1]
+            acc[r][lo:hi] = sent[src]
+            tr.sent[src] += hi - lo
+            step.append((src, r, recv_idx, hi - lo))
+        tr.steps.append(step)
+
+
+def ring_all_reduce(xs: Sequence[np.ndarray], op: str = "sum", dtype: str = "f32",
+                    trace: Optional[Trace] = None) -> List[np.ndarray]:
+    """Ring AllReduce = ring ReduceScatter then ring AllGather, 2(N-1) steps
+    ([MLSys-6], "Ring AllReduce", Algorithm 1; [AR-notes], "语义与分解" and
+    "算法一"; [Slides], "2(N−1)/N 是怎么来的").  Returns each rank's output."""
+    N = len(xs)
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    acc = [to_acc(x, dtype) for x in xs]
+    b = chunk_bounds(M, N)
+    _ring_rs_phase(acc, b, op, 0, tr)
+    _ring_ag_phase(acc, b, [(r + 1) % N for r in range(N)], tr)
+    return [from_acc(a, dtype) for a in acc]
+
+
+def ring_reduce_scatter(xs: Sequence[np.ndarray], op: str = "sum", dtype: str = "f32",
+                        trace: Optional[Trace] = None) -> List[np.ndarray]:
+    """Standalone ring ReduceScatter: rank r returns the reduced chunk r
+    (recvcount = M/N; the pages' send buffer is N chunks of equal size,
+    [Slides], "环形 ReduceScatter": V is the per-rank output times N)."""
+    N = len(xs)
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    acc = [to_acc(x, dtype) for x in xs]
+    b = chunk_bounds(M, N)
+    _ring_rs_phase(acc, b, op, -1, tr)
+    return [from_acc(acc[r][b[r]:b[r + 1]], dtype) for r in range(N)]
+
+
+def ring_all_gather(shards: Sequence[np.ndarray], dtype: str = "f32",
+                    trace: Optional[Trace] = None) -> List[np.ndarray]:
+    """Standalone ring AllGather: rank r's shard lands in slot r of every
+    rank's output ([Slides], "环形 AllGather" and the primitives table)."""
+    N = len(shards)
+    S = int(np.asarray(shards[0]).shape[0])
+    M = N * S
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    b = chunk_bounds(M, N)
+    acc = []
+    for r in range(N):
+        a = np.zeros(M, dtype=np.asarray(shards[r]).dtype)
+        a[b[r]:b[r + 1]] = shards[r]
+        acc.append(a)
+    _ring_ag_phase(acc, b, list(range(N)), tr)
+    return [a.copy() for a in acc]
+
+
+def ring_fold_elements(vals: np.ndarray, idx: np.ndarray, M: int, op: str,
+                       dtype: str, standalone_rs: bool = False) -> np.ndarray:
+    """Closed form of the ring's fold for a sample of element indices.
+
+    vals[r, k] is rank r's input at element idx[k].  Following one chunk c
+    through the ReduceScatter steps above, its partial starts at rank c (c+1
+    for the standalone ReduceScatter) and each step folds in the next rank's
+    value as op(next_rank_value, partial), N-1 times.  This is the same
+    arithmetic as ring_all_reduce, written without steps, so that full-size
+    outputs can be checked at sampled positions.
+    """
+    vals = np.asarray(vals)
+    N = vals.shape[0]
+    c = chunk_of(idx, M, N)
+    start = (c + (1 if standalone_rs else 0)) % N
+    cols = np.arange(vals.shape[1])
+    acc = to_acc(vals[start, cols], dtype)
+    for j in range(1, N):
+        acc = combine(op, to_acc(vals[(start + j) % N, cols], dtype), acc)
+    return from_acc(acc, dtype)
+
+
+# --------------------------------------------------------------------------
+# recursive halving-doubling (N = 2**k)
+# --------------------------------------------------------------------------
+
+def _is_pow2(n: int) -> bool:
+    return n >= 1 and (n & (n - 1)) == 0
+
+
+def _blk_elems(b: List[int], lo: int, hi: int) -> Tuple[int, int]:
+    return b[lo], b[hi]
+
+
+def _hd_rs_phase(acc: List[np.ndarray], b: List[int], op: str, tr: Trace) -> None:
+    """Recursive halving ReduceScatter: at the step with distance d = N/2, N/4,
+    ..., 1, rank i exchanges with i XOR d ([AR-notes], "算法二：Recursive
+    Halving-Doubling", table tbl-cc-ar-hd-trace: pairs (0,4)(1,5)... first,
+    moving M/2, then M/4, M/8).  Each rank's current block range of chunks is
+    halved: the rank whose bit d is 0 keeps the lower half, the other the upper
+    half, and it combines the partner's copy of the half it keeps.  After the
+    phase rank i holds chunk i."""
+    N = len(acc)
+    rng = [(0, N)] * N
+    d = N // 2
+    while d >= 1:
+        keep, send = [], []
+        for i in range(N):
+            lo, hi = rng[i]
+            mid = (lo + hi) // 2
+            if i & d == 0:
+                keep.append((lo, mid)); send.append((mid, hi))
+            else:
+                keep.append((mid, hi)); send.append((lo, mid))
+        snap = []
+        for i in range(N):
+            e0, e1 = _blk_elems(b, *send[i])
+            snap.append(acc[i][e0:e1].copy())
+        step = []
+        for i in range(N):
+            p = i ^ d
+            assert send[p] == keep[i]
+            e0, e1 = _blk_elems(b, *keep[i])
+            acc[i][e0:e1] = combine(op, acc[i][e0:e1], snap[p])
+            tr.sent[p] += e1 - e0
+            step.append((p, i, keep[i], e1 - e0))
+            rng[i] = keep[i]
+        tr.steps.append(step)
+        d //= 2
+
+
+def _hd_ag_phase(acc: List[np.ndarray], b: List[int], tr: Trace) -> None:
+    """Recursive doubling AllGather, the reverse of the halving phase: at
+    distance d = 1, 2, ..., N/2 partners swap their block ranges and the held
+    range doubles ([AR-notes], "算法二", 阶段 2)."""
+    N = len(acc)
+    rng = [(i, i + 1) for i in range(N)]
+    d = 1
+    while d < N:
+        snap = []
+        for i in range(N):
+            e0, e1 = _blk_elems(b, *rng[i])
+            snap.append(acc[i][e0:e1].copy())
+        step = []
+        new = list(rng)
+        for i in range(N):
+            p = i ^ d
+            e0, e1 = _blk_elems(b, *rng[p])
+            acc[i][e0:e1] = snap[p]
+            tr.sent[p] += e1 - e0
+            step.append((p, i, rng[p], e1 - e0))
+            new[i] = (min(rng[i][0], rng[p][0]), max(rng[i][1], rng[p][1]))
+        rng = new
+        tr.steps.append(step)
+        d *= 2
+
+
+def hd_all_reduce(xs, op="sum", dtype="f32", trace=None):
+    """Halving-doubling AllReduce: 2*log2(N) steps ([AR-notes], "算法二";
+    [Blog], "Recursive Halving-Doubling")."""
+    N = len(xs)
+    if not _is_pow2(N):
+        raise ValueError("halving-doubling needs N = 2**k")
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    acc = [to_acc(x, dtype) for x in xs]
+    b = chunk_bounds(M, N)
+    _hd_rs_phase(acc, b, op, tr)
+    _hd_ag_phase(acc, b, tr)
+    return [from_acc(a, dtype) for a in acc]
+
+
+def hd_reduce_scatter(xs, op="sum", dtype="f32", trace=None):
+    N = len(xs)
+    if not _is_pow2(N):
+        raise ValueError("halving-doubling needs N = 2**k")
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    acc = [to_acc(x, dtype) for x in xs]
+    b = chunk_bounds(M, N)
+    _hd_rs_phase(acc, b, op, tr)
+    return [from_acc(acc[r][b[r]:b[r + 1]], dtype) for r in range(N)]
+
+
+def hd_all_gather(shards, dtype="f32", trace=None):
+    N = len(shards)
+    if not _is_pow2(N):
+        raise ValueError("halving-doubling needs N = 2**k")
+    S = int(np.asarray(shards[0]).shape[0])
+    M = N * S
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    b = chunk_bounds(M, N)
+    acc = []
+    for r in range(N):
+        a = np.zeros(M, dtype=np.asarray(shards[r]).dtype)
+        a[b[r]:b[r + 1]] = shards[r]
+        acc.append(a)
+    _hd_ag_phase(acc, b, tr)
+    return [a.copy() for a in acc]
+
+
+def hd_fold_elements(vals: np.ndarray, idx: np.ndarray, M: int, op: str,
+                     dtype: str) -> np.ndarray:
+    """Closed form of the halving phase for sampled elements of chunk c:
+    S_N(j) = x_j and S_d(j) = op(S_2d(j), S_2d(j XOR d)) for d = N/2 .. 1;
+    the result for chunk c is S_1(c)."""
+    vals = np.asarray(vals)
+    N = vals.shape[0]
+    c = chunk_of(idx, M, N)
+    cols = np.arange(vals.shape[1])
+    S = [to_acc(vals[j], dtype) for j in range(N)]
+    d = N // 2
+    while d >= 1:
+        S = [combine(op, S[j], S[j ^ d]) for j in range(N)]
+        d //= 2
+    stacked = np.stack(S)
+    return from_acc(stacked[c, cols], dtype)
+
+
+# --------------------------------------------------------------------------
+# butterfly (recursive doubling with full exchange), N = 2**k
+# --------------------------------------------------------------------------
+
+def butterfly_all_reduce(xs, op="sum", dtype="f32", trace=None):
+    """Butterfly AllReduce: log2(N) steps; at step k rank i pairs with
+    i XOR 2**k, both exchange the full vector and combine it ([AR-notes],
+    "算法四：Butterfly (Recursive Doubling)": distance 1, then 2, then 4)."""
+    N = len(xs)
+    if not _is_pow2(N):
+        raise ValueError("butterfly needs N = 2**k")
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    v = [to_acc(x, dtype) for x in xs]
+    k = 1
+    while k < N:
+        snap = [a.copy() for a in v]
+        step = []
+        for i in range(N):
+            p = i ^ k
+            v[i] = combine(op, v[i], snap[p])
+            tr.sent[p] += M
+            step.append((p, i, "all", M))
+        tr.steps.append(step)
+        k *= 2
+    return [from_acc(a, dtype) for a in v]
+
+
+def butterfly_fold_elements(vals: np.ndarray, rank: int, op: str, dtype: str) -> np.ndarray:
+    """Closed form of butterfly's result on one rank: a pairwise tree over the
+    sequence x_{rank XOR t}, t = 0..N-1, nearest pairs combined first."""
+    vals = np.asarray(vals)
+    N = vals.shape[0]
+    seq = [to_acc(vals[rank ^ t], dtype) for t in range(N)]
+    while len(seq) > 1:
+        seq = [combine(op, seq[2 * i], seq[2 * i + 1]) for i in range(len(seq) // 2)]
+    return from_acc(seq[0], dtype)
+
+
+# --------------------------------------------------------------------------
+# broadcast
+# --------------------------------------------------------------------------
+
+def broadcast(xs, root: int, schedule: str = "ring", trace=None):
+    """Broadcast: every rank ends with the root's buffer ([Slides], "Broadcast：
+    一份数据发给所有人").  schedule "ring" forwards along the chain root,
+    root+1, ...; "binomial" doubles the holders each step, the pattern of the
+    rank-0 example in [Blog], "Recursive Halving-Doubling"."""
+    N = len(xs)
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    have = {root: np.array(xs[root], copy=True)}
+    out = [np.array(x, copy=True) for x in xs]
+    if schedule == "ring":
+        for s in range(N - 1):
+            src, dst = (root + s) % N, (root + s + 1) % N
+            have[dst] = have[src].copy()
+            tr.sent[src] += M
+            tr.steps.append([(src, dst, "all", M)])
+    elif schedule == "binomial":
+        k = 1
+        while k < N:
+            step = []
+            for rel in range(k):
+                if rel + k < N:
+                    src, dst = (root + rel) % N, (root + rel + k) % N
+                    have[dst] = have[src].copy()
+                    tr.sent[src] += M
+                    step.append((src, dst, "all", M))
+            tr.steps.append(step)
+            k *= 2
+    else:
+        raise ValueError(schedule)
+    for r in range(N):
+        out[r] = have[r]
+    return out
+
+
+# --------------------------------------------------------------------------
+# AllToAll(v)
+# --------------------------------------------------------------------------
+
+def all_to_all(sends: Sequence[np.ndarray], counts: np.ndarray, row: int = 1,
+               pairwise: bool = False, trace=None) -> List[np.ndarray]:
+    """AllToAll(v): rank i's send buffer holds N consecutive blocks, block j
+    (counts[i][j] rows of `row` elements) destined for rank j; rank j's receive
+    buffer holds the blocks from ranks 0..N-1 in source order.  No arithmetic,
+    no duplication: a blocked transpose ([Slides], "AllToAll：分布式的转置";
+    [Blog], "All to All").
+
+    pairwise=True performs the schedule of [Blog], "Pairwise（成对）算法": at
+    step k rank i sends to (i+k) mod N and receives from (i-k) mod N; step 0
+    is the local block.  The trace records, per step, the largest block moved
+    (the max term of that section's time formula)."""
+    N = len(sends)
+    C = np.asarray(counts, dtype=np.int64).reshape(N, N)
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    sd = np.zeros((N, N + 1), dtype=np.int64)
+    sd[:, 1:] = np.cumsum(C, axis=1)                  # send displacement of block j on rank i
+    rd = np.zeros((N + 1, N), dtype=np.int64)
+    rd[1:, :] = np.cumsum(C, axis=0)                  # recv displacement of block from i on rank j
+    recv = [np.zeros(int(rd[N, j]) * row, dtype=np.asarray(sends[0]).dtype) for j in range(N)]
+
+    def move(i, j):
+        n = int(C[i, j])
+        s0 = int(sd[i, j]) * row
+        r0 = int(rd[i, j]) * row
+        recv[j][r0:r0 + n * row] = np.asarray(sends[i])[s0:s0 + n * row]
+        if i != j:
+            tr.sent[i] += n * row
+        return n
+
+    if pairwise:
+        for k in range(N):
+            step = []
+            for i in range(N):
+                j = (i + k) % N
+                n = move(i, j)
+                step.append((i, j, "block", n * row))
+            tr.steps.append(step)
+    else:
+        for i in range(N):
+            for j in range(N):
+                move(i, j)
+    return recv
+
+
+def pairwise_time_model(counts: np.ndarray, alpha: float, beta: float) -> float:
+    """T = (N-1) alpha + beta * sum_{k=1..N-1} max_i n_{i,(i+k) mod N}
+    ([Blog], "Pairwise（成对）算法", performance model)."""
+    C = np.asarray(counts)
+    N = C.shape[0]
+    t = 0.0
+    for k in range(1, N):
+        t += alpha + beta * max(C[i, (i + k) % N] for i in range(N))
+    return t
+
+
+# --------------------------------------------------------------------------
+# DDP-style gradient buckets
+# --------------------------------------------------------------------------
+
+def bucket_pack(sizes_elems: Sequence[int], elem_bytes: int, cap_bytes: int) -> List[List[int]]:
+    """Group tensors into buckets in reverse order of the list, closing a
+    bucket when the next tensor would push it past the cap; a tensor larger
+    than the cap gets a bucket of its own ([MLSys-6], "Bucket fusion": buckets
+    of about 25 MB, parameters in reverse forward order)."""
+    buckets: List[List[int]] = []
+    cur: List[int] = []
+    cur_bytes = 0
+    for t in reversed(range(len(sizes_elems))):
+        nb = int(sizes_elems[t]) * elem_bytes
+        if cur and cur_bytes + nb > cap_bytes:
+            buckets.append(cur)
+            cur, cur_bytes = [], 0
+        cur.append(t)
+        cur_bytes += nb
+    if cur:
+        buckets.append(cur)
+    return buckets
+
+
+def bucketed_all_reduce(tensors_per_rank: Sequence[Sequence[np.ndarray]], buckets: List[List[int]],
+                        algo: str = "ring", op: str = "sum", dtype: str = "bf16"):
+    """All-reduce every bucket as one flat vector (the bucket's tensors laid out
+    back to back in bucket order), then split the result back into tensors."""
+    N = len(tensors_per_rank)
+    fn = {"ring": ring_all_reduce, "hd": hd_all_reduce, "butterfly": butterfly_all_reduce}[algo]
+    out = [[None] * len(tensors_per_rank[0]) for _ in range(N)]
+    for bk in buckets:
+        flat = [np.concatenate([np.asarray(tensors_per_rank[r][t]) for t in bk]) for r in range(N)]
+        red = fn(flat, op, dtype)
+        for r in range(N):
+            pos = 0
+            for t in bk:
+                n = np.asarray(tensors_per_rank[r][t]).shape[0]
+                out[r][t] = red[r][pos:pos + n]
+                pos += n
+    return out
+
+
+# --------------------------------------------------------------------------
+# closed forms: plain results and accounting
+# --------------------------------------------------------------------------
+
+def plain_reduce(xs: Sequence[np.ndarray], op: str, dtype: str) -> np.ndarray:
+    """The plain definition B = (+)_j A_j ([AR-notes], "语义与分解", eq.
+    cc-ar-semantic), computed order-free where the operator allows: integers in
+    int64 then wrapped to int32, float MAX elementwise.  For float SUM the
+    order-free reference is the float64 sum (not rounded)."""
+    if dtype == "int32":
+        a = np.stack([np.asarray(x, dtype=np.int64) for x in xs])
+        if op == "sum":
+            r = a.sum(axis=0)
+            return ((r + 2 ** 31) % 2 ** 32 - 2 ** 31).astype(np.int32)
+        if op == "max":
+            return a.max(axis=0).astype(np.int32)
+        if op == "prod":
+            r = np.ones(a.shape[1], dtype=np.int64)
+            for row in a:
+                r = ((r * row) + 2 ** 31) % 2 ** 32 - 2 ** 31
+            return r.astype(np.int32)
+    if op == "max":
+        # maximum never rounds: reduce in the accumulator type, exact in any order
+        m = to_acc(xs[0], dtype)
+        for x in xs[1:]:
+            m = _fmax_ieee(m, to_acc(x, dtype))
+        return from_acc(m, dtype)
+    f = np.stack([to_acc(x, dtype).astype(np.float64) for x in xs])
+    if op == "sum":
+        return f.sum(axis=0)
+    if op == "prod":
+        return np.prod(f, axis=0)
+    raise ValueError(op)
+
+
+def ring_values_sent_per_rank(M: int, N: int, coll: str = "all_reduce") -> List[int]:
+    """Values each rank sends under the ring schedule, counted chunk by chunk
+    ([Lesson3], simulator: bytes_sent_per_rank; equals 2(N-1)M/N when N | M)."""
+    b = chunk_bounds(M, N)
+    size = [b[c + 1] - b[c] for c in range(N)]
+    out = []
+    for r in range(N):
+        rs = sum(size[(r - s) % N] for s in range(N - 1))
+        rs_sa = sum(size[(r - s - 1) % N] for s in range(N - 1))
+        ag = sum(size[(r + 1 - s) % N] for s in range(N - 1))
+        ag_sa = sum(size[(r - s) % N] for s in range(N - 1))
+        out.append({"all_reduce": rs + ag, "reduce_scatter": rs_sa, "all_gather": ag_sa}[coll])
+    return out
+
+
+BUSBW_FACTOR = {
+    "all_reduce": lambda n: 2.0 * (n - 1) / n,
+    "reduce_scatter": lambda n: (n - 1) / n,
+    "all_gather": lambda n: (n - 1) / n,
+    "all_to_all": lambda n: (n - 1) / n,
+    "broadcast": lambda n: 1.0,
+}
+
+
+def busbw(coll: str, size_bytes: float, seconds: float, n: int) -> float:
+    """busbw = (S / t) * factor ([Slides], "algbw 与 busbw"; [AR-notes],
+    eq. cc-ar-busbw), in bytes per second."""
+    return size_bytes / seconds * BUSBW_FACTOR[coll](n)
+
+
+def ring_time_model(M_bytes: float, N: int, alpha: float, beta_s_per_byte: float) -> float:
+    """T = 2(N-1) alpha + 2 (N-1)/N * M * beta ([Lesson3], "理论通信量与网络
+    延迟模型", beta in seconds per byte)."""
+    return 2 * (N - 1) * alpha + 2.0 * (N - 1) / N * M_bytes * beta_s_per_byte
+
+
+def norm_rel_error(y: np.ndarray, ref64: np.ndarray) -> float:
+    """||y - ref||_2 / ||ref||_2 in float64."""
+    y = np.asarray(y, dtype=np.float64)
+    ref64 = np.asarray(ref64, dtype=np.float64)
+    den = np.linalg.norm(ref64)
+    return float(np.linalg.norm(y - ref64) / den) if den > 0 else float(np.linalg.norm(y - ref64))
