@@ -1,0 +1,180 @@
+/*
+ * cc.h -- C ABI of the collective-reduction engine (libcc.so).
+ *
+ * N logical ranks live in one GPU's HBM as rank-strided buffers: rank r's
+ * buffer starts at  base + r * rank_stride_bytes.  One call carries all N
+ * ranks' buffers and performs the whole collective on the caller's HIP stream.
+ *
+ * The calls follow the primitive table of the slide deck "集合通信与分片矩阵乘法"
+ * (slide "I · 原语 · 小结": Broadcast, AllReduce, AllGather, ReduceScatter,
+ * AllToAll) and the schedules of the "AllReduce" algorithm notes (算法一 Ring,
+ * 算法二 Recursive Halving-Doubling, 算法四 Butterfly).
+ *
+ * Common rules for every collective call:
+ *  - Asynchronous: the call validates, enqueues kernels on `stream` (a
+ *    hipStream_t; NULL is the null stream) and returns.  Completion is stream
+ *    order, as for the pages' asynchronous collective kernels (slide "NCCL：
+ *    GPU 上用的那个库").
+ *  - No call allocates device memory.  A schedule that needs staging (see
+ *    cc_workspace_size) reads it from cfg->workspace, owned by the caller.
+ *  - The caller owns every buffer; the library keeps no pointer after return.
+ *  - Element types: CC_INT32 (SUM and PROD wrap modulo 2^32), CC_FLOAT32 and
+ *    CC_BFLOAT16.  bf16 is read, widened to fp32, every partial result stays
+ *    fp32 through all steps, and the final value is rounded once to bf16
+ *    (nearest, ties to even).
+ *  - Float MAX is IEEE-754-2019 maximum (NaN if either operand is NaN; +0 is
+ *    larger than -0), so it is order-free.  fp32/bf16 SUM and PROD follow the
+ *    chosen schedule's association exactly (the textbook ch. 6 "集合通信",
+ *    section "六种核心原语": reduction order changes the low bits).
+ *  - Chunks: a rank's vector of M elements is cut into N contiguous chunks,
+ *    chunk c = [floor(c*M/N), floor((c+1)*M/N)).
+ *  - Alignment: bases and strides that are not 16-byte multiples are legal;
+ *    they run a slower element-wise path.
+ *  - Errors are returned, never raised: CC_ERR_INVALID_ARG for bad arguments
+ *    (nranks outside [1, CC_MAX_RANKS], NULL base with a non-zero count,
+ *    rank buffers that overlap each other, send and recv buffers that overlap
+ *    where the call needs them disjoint, root outside [0, N), a workspace
+ *    smaller than cc_workspace_size reports, negative fuse_depth),
+ *    CC_ERR_UNSUPPORTED for a schedule the collective does not have,
+ *    CC_ERR_NO_DEVICE when no GPU is visible, CC_ERR_HIP for a launch error.
+ *    cc_last_error() returns a message for the last failing call on the
+ *    calling thread.
+ */
+#ifndef CC_H_
+#define CC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CC_MAX_RANKS 64
+
+typedef enum {
+  CC_OK = 0,
+  CC_ERR_INVALID_ARG = 1,
+  CC_ERR_UNSUPPORTED = 2,
+  CC_ERR_NO_DEVICE = 3,
+  CC_ERR_HIP = 4
+} cc_status_t;
+
+typedef enum { CC_INT32 = 0, CC_FLOAT32 = 1, CC_BFLOAT16 = 2 } cc_dtype_t;
+
+/* Elementwise operators named by the course lesson "第 3 课：分布式通信原语"
+ * (核心概念, item 1: SUM, MAX, PROD). */
+typedef enum { CC_SUM = 0, CC_MAX = 1, CC_PROD = 2 } cc_op_t;
+
+typedef enum {
+  CC_ALGO_RING = 0,             /* AllReduce notes, 算法一 */
+  CC_ALGO_HALVING_DOUBLING = 1, /* AllReduce notes, 算法二; needs N = 2^k */
+  CC_ALGO_BUTTERFLY = 2         /* AllReduce notes, 算法四; AllReduce only, N = 2^k */
+} cc_algo_t;
+
+typedef enum {
+  CC_COLL_ALL_REDUCE = 0,
+  CC_COLL_REDUCE_SCATTER = 1,
+  CC_COLL_ALL_GATHER = 2,
+  CC_COLL_BROADCAST = 3,
+  CC_COLL_ALL_TO_ALL = 4
+} cc_coll_t;
+
+/* How a schedule is executed.
+ *  fuse_depth = 0: fully fused -- one kernel folds every rank's contribution
+ *                  in registers in the schedule's order and writes the result
+ *                  to every destination (read N*M, write N*M for AllReduce).
+ *  fuse_depth = 1: stepwise -- one kernel per schedule step, each doing the
+ *                  step's reads, combines and writes in HBM.
+ *  fuse_depth = k: ring only -- k consecutive ring steps per kernel.
+ *  workspace / workspace_bytes: caller-owned device memory, at least what
+ *  cc_workspace_size returns for the same arguments (may be NULL/0 when that
+ *  is 0).  A NULL cfg means {CC_ALGO_RING, 0, NULL, 0}. */
+typedef struct {
+  cc_algo_t algo;
+  int fuse_depth;
+  void* workspace;
+  size_t workspace_bytes;
+} cc_config_t;
+
+/* N rank buffers: rank r at (char*)base + r * rank_stride_bytes (device memory). */
+typedef struct {
+  void* base;
+  size_t rank_stride_bytes;
+} cc_rankbuf_t;
+
+/* hipStream_t, passed as an opaque pointer. */
+typedef void* cc_stream_t;
+
+/* AllReduce: every rank's recv = (+) over ranks of send, `count` elements per
+ * rank (slides "Reduce 与 AllReduce"; AllReduce notes, 语义与分解).  In place
+ * iff send.base == recv.base with equal strides; otherwise the send and recv
+ * rank buffers must not overlap.  Schedules: ring, halving-doubling, butterfly. */
+cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype,
+                          cc_op_t op, int nranks, const cc_config_t* cfg, cc_stream_t stream);
+
+/* ReduceScatter: send holds nranks*recvcount elements per rank; rank r's recv
+ * (recvcount elements) gets the reduction of chunk r over all ranks (slides
+ * "Scatter 与 ReduceScatter").  send and recv must not overlap.  Schedules:
+ * ring (each chunk's fold starts at the rank after its owner and ends at the
+ * owner), halving-doubling. */
+cc_status_t cc_reduce_scatter(cc_rankbuf_t send, cc_rankbuf_t recv, size_t recvcount,
+                              cc_dtype_t dtype, cc_op_t op, int nranks, const cc_config_t* cfg,
+                              cc_stream_t stream);
+
+/* AllGather: rank r's send (sendcount elements) lands in slot r of every
+ * rank's recv (nranks*sendcount elements) (slides "Gather 与 AllGather").
+ * No arithmetic.  send and recv must not overlap.  Schedules: ring,
+ * halving-doubling. */
+cc_status_t cc_all_gather(cc_rankbuf_t send, cc_rankbuf_t recv, size_t sendcount,
+                          cc_dtype_t dtype, int nranks, const cc_config_t* cfg,
+                          cc_stream_t stream);
+
+/* Broadcast: every rank's recv = the root's send, `count` elements (slides
+ * "Broadcast：一份数据发给所有人").  Only the root's send buffer is read.
+ * In place iff send.base == recv.base with equal strides.  Schedules: ring
+ * (chain root, root+1, ...), halving-doubling (binomial doubling from the
+ * root, any N; blog "分布式大模型集合通信", RHD section's rank-0 example). */
+cc_status_t cc_broadcast(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype,
+                         int root, int nranks, const cc_config_t* cfg, cc_stream_t stream);
+
+/* AllToAll(v): a blocked transpose (slides "AllToAll：分布式的转置").
+ * counts: host array [nranks*nranks], counts[i*nranks + j] = rows rank i sends
+ * to rank j; a row is elem_per_row elements.  Rank i's send buffer holds its
+ * blocks for j = 0..N-1 back to back; rank j's recv buffer receives the blocks
+ * from i = 0..N-1 back to back (displacements are the exclusive prefix sums).
+ * Every recv buffer must fit within the recv stride and must not overlap any
+ * send buffer.  Schedules: ring = the pairwise schedule (blog, "Pairwise（成对）
+ * 算法": at step k rank i sends to i+k) when fuse_depth >= 1; fused direct copy
+ * when fuse_depth = 0. */
+cc_status_t cc_all_to_all(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* counts,
+                          size_t elem_per_row, cc_dtype_t dtype, int nranks,
+                          const cc_config_t* cfg, cc_stream_t stream);
+
+/* Bytes of caller-owned device workspace the given collective needs.  count is
+ * the per-rank element count of the collective's own count argument. */
+cc_status_t cc_workspace_size(cc_coll_t coll, const cc_config_t* cfg, int nranks, size_t count,
+                              cc_dtype_t dtype, size_t* bytes);
+
+/* Simulated-network accounting of a schedule: the largest number of bytes any
+ * rank sends, and the number of communication steps.  Ring AllReduce sends
+ * 2(N-1)M/N elements per rank when N divides M (textbook ch. 6, Ring
+ * AllReduce; lesson 3 simulator's per-rank counter).  count is the per-rank
+ * count of the collective (all_reduce, broadcast: the vector; reduce_scatter:
+ * recvcount; all_gather: sendcount; all_to_all: elements per source-destination
+ * block of a uniform exchange, sent over the pairwise schedule). */
+cc_status_t cc_get_traffic(cc_coll_t coll, cc_algo_t algo, int nranks, size_t count,
+                           cc_dtype_t dtype, uint64_t* max_bytes_sent_per_rank, int* steps);
+
+/* The chunk boundaries used by every schedule: bounds[c] = floor(c*count/nranks),
+ * c = 0..nranks (bounds must hold nranks+1 entries). */
+cc_status_t cc_chunk_bounds(size_t count, int nranks, size_t* bounds);
+
+const char* cc_status_string(cc_status_t status);
+const char* cc_last_error(void);
+const char* cc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CC_H_ */

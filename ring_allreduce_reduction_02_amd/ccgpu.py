@@ -1,0 +1,216 @@
+"""ctypes binding of libcc.so (include/cc.h), same names as the C ABI.
+
+Argument marshalling only: every step of every collective runs in the HIP
+kernels of libcc.so.  PyTorch provides the device memory and the stream.
+
+Rank-strided buffers are 2-D tensors ``t[N, L]`` whose rows are contiguous
+(``t.stride(1) == 1``) and whose row stride may exceed L (padding between
+ranks), e.g. ``torch.empty(N, L + pad, device="cuda")[:, :L]``.  Rank r's
+buffer is row r.
+
+If the library has not been built this module raises on first use: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcc.so")
+
+CC_OK, CC_ERR_INVALID_ARG, CC_ERR_UNSUPPORTED, CC_ERR_NO_DEVICE, CC_ERR_HIP = range(5)
+DTYPES = {"int32": 0, "f32": 1, "bf16": 2}
+OPS = {"sum": 0, "max": 1, "prod": 2}
+ALGOS = {"ring": 0, "hd": 1, "butterfly": 2}
+COLLS = {"all_reduce": 0, "reduce_scatter": 1, "all_gather": 2, "broadcast": 3, "all_to_all": 4}
+ESIZE = {"int32": 4, "f32": 4, "bf16": 2}
+MAX_RANKS = 64
+
+
+class RankBuf(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("rank_stride_bytes", ctypes.c_size_t)]
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int), ("fuse_depth", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class CCError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_STATUS = {0: "CC_OK", 1: "CC_ERR_INVALID_ARG", 2: "CC_ERR_UNSUPPORTED", 3: "CC_ERR_NO_DEVICE", 4: "CC_ERR_HIP"}
+_lib: Optional[ctypes.CDLL] = None
+
+EXPORTS = {
+    "cc_all_reduce": [RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                      ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_reduce_scatter": [RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                          ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_all_gather": [RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                      ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_broadcast": [RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                     ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_all_to_all": [RankBuf, RankBuf, ctypes.POINTER(ctypes.c_size_t), ctypes.c_size_t, ctypes.c_int,
+                      ctypes.c_int, ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_workspace_size": [ctypes.c_int, ctypes.POINTER(Config), ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
+                          ctypes.POINTER(ctypes.c_size_t)],
+    "cc_get_traffic": [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
+                       ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)],
+    "cc_chunk_bounds": [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
+    "cc_status_string": [ctypes.c_int],
+    "cc_last_error": [],
+    "cc_version": [],
+}
+
+
+def load() -> ctypes.CDLL:
+    """Load libcc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m ring_allreduce_reduction_02_amd.build_lib`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, args in EXPORTS.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_char_p if name in ("cc_status_string", "cc_last_error", "cc_version") else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != CC_OK:
+        raise CCError(status, load().cc_last_error().decode())
+
+
+def dtype_name(t) -> str:
+    import torch
+    m = {torch.int32: "int32", torch.float32: "f32", torch.bfloat16: "bf16"}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def rankbuf(t) -> RankBuf:
+    """A [N, L] tensor with contiguous rows -> cc_rankbuf_t."""
+    if t.dim() != 2:
+        raise ValueError("rank-strided buffers are 2-D tensors [nranks, elements]")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("each rank's row must be contiguous")
+    if not t.is_cuda:
+        raise ValueError("buffers must be device tensors")
+    return RankBuf(t.data_ptr(), t.stride(0) * t.element_size())
+
+
+def config(algo: str = "ring", fuse_depth: int = 0, workspace=None) -> Config:
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return Config(ALGOS[algo], int(fuse_depth), ws_ptr, ws_bytes)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_size(coll: str, nranks: int, count: int, dtype: str, algo: str = "ring",
+                   fuse_depth: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    cfg = Config(ALGOS[algo], int(fuse_depth), None, 0)
+    _check(load().cc_workspace_size(COLLS[coll], ctypes.byref(cfg), nranks, count, DTYPES[dtype],
+                                    ctypes.byref(out)))
+    return out.value
+
+
+def make_workspace(coll: str, nranks: int, count: int, dtype: str, algo: str = "ring",
+                   fuse_depth: int = 0, device="cuda"):
+    """Allocate (with torch) the workspace a schedule needs, or None."""
+    import torch
+    n = workspace_size(coll, nranks, count, dtype, algo, fuse_depth)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def get_traffic(coll: str, nranks: int, count: int, dtype: str, algo: str = "ring"):
+    """(max bytes any rank sends, steps) of the simulated network."""
+    b = ctypes.c_uint64(0)
+    s = ctypes.c_int(0)
+    _check(load().cc_get_traffic(COLLS[coll], ALGOS[algo], nranks, count, DTYPES[dtype], ctypes.byref(b),
+                                 ctypes.byref(s)))
+    return b.value, s.value
+
+
+def chunk_bounds(count: int, nranks: int):
+    arr = (ctypes.c_size_t * (nranks + 1))()
+    _check(load().cc_chunk_bounds(count, nranks, arr))
+    return list(arr)
+
+
+def all_reduce(send, recv=None, op: str = "sum", algo: str = "ring", fuse_depth: int = 0,
+               workspace=None, stream=None) -> None:
+    """recv[r] = (+)_j send[j] for every rank r; send/recv are [N, M]."""
+    recv = send if recv is None else recv
+    N, M = send.shape
+    if tuple(recv.shape) != (N, M) or recv.dtype != send.dtype:
+        raise ValueError("recv must match send")
+    cfg = config(algo, fuse_depth, workspace)
+    _check(load().cc_all_reduce(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], OPS[op], N,
+                                ctypes.byref(cfg), _stream(stream)))
+
+
+def reduce_scatter(send, recv, op: str = "sum", algo: str = "ring", fuse_depth: int = 0,
+                   workspace=None, stream=None) -> None:
+    """send [N, N*S] -> recv [N, S]: rank r gets the reduced chunk r."""
+    N, S = recv.shape
+    if tuple(send.shape) != (N, N * S) or recv.dtype != send.dtype:
+        raise ValueError("send must be [N, N*S] for recv [N, S]")
+    cfg = config(algo, fuse_depth, workspace)
+    _check(load().cc_reduce_scatter(rankbuf(send), rankbuf(recv), S, DTYPES[dtype_name(send)], OPS[op], N,
+                                    ctypes.byref(cfg), _stream(stream)))
+
+
+def all_gather(send, recv, algo: str = "ring", fuse_depth: int = 0, stream=None) -> None:
+    """send [N, S] -> recv [N, N*S]: slot r of every rank holds rank r's send."""
+    N, S = send.shape
+    if tuple(recv.shape) != (N, N * S) or recv.dtype != send.dtype:
+        raise ValueError("recv must be [N, N*S] for send [N, S]")
+    cfg = config(algo, fuse_depth)
+    _check(load().cc_all_gather(rankbuf(send), rankbuf(recv), S, DTYPES[dtype_name(send)], N,
+                                ctypes.byref(cfg), _stream(stream)))
+
+
+def broadcast(send, recv=None, root: int = 0, algo: str = "ring", fuse_depth: int = 0, stream=None) -> None:
+    """recv[r] = send[root] for every r; send/recv are [N, M]."""
+    recv = send if recv is None else recv
+    N, M = recv.shape
+    if tuple(send.shape) != (N, M) or recv.dtype != send.dtype:
+        raise ValueError("recv must match send")
+    cfg = config(algo, fuse_depth)
+    _check(load().cc_broadcast(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], root, N,
+                               ctypes.byref(cfg), _stream(stream)))
+
+
+def all_to_all(send, recv, counts: Sequence[Sequence[int]], elem_per_row: int = 1, fuse_depth: int = 0,
+               stream=None) -> None:
+    """Blocked transpose with per-(source, destination) row counts."""
+    N = send.shape[0]
+    flat = [int(v) for row in counts for v in row]
+    if len(flat) != N * N or recv.shape[0] != N:
+        raise ValueError("counts must be N x N")
+    arr = (ctypes.c_size_t * (N * N))(*flat)
+    cfg = config("ring", fuse_depth)
+    _check(load().cc_all_to_all(rankbuf(send), rankbuf(recv), arr, elem_per_row, DTYPES[dtype_name(send)], N,
+                                ctypes.byref(cfg), _stream(stream)))
+
+
+def raw(fn: str, *args):
+    """Call a C-ABI function with raw ctypes arguments; returns the status."""
+    return getattr(load(), fn)(*args)

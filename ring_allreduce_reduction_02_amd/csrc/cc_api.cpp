@@ -1,0 +1,524 @@
+// C ABI of the collective-reduction engine: argument validation, schedule
+// planning and kernel dispatch.  Declared in include/cc.h.
+
+#include "../../include/cc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "cc_launch.h"
+
+using namespace cc;
+
+namespace {
+
+thread_local std::string g_err;
+
+cc_status_t fail(cc_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+cc_status_t ok() {
+  g_err.clear();
+  return CC_OK;
+}
+
+cc_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+cc_status_t device_ready() {
+  static std::once_flag once;
+  static int count = -1;
+  std::call_once(once, [] {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess) n = 0;
+    count = n;
+  });
+  if (count <= 0) return fail(CC_ERR_NO_DEVICE, "no HIP device is visible");
+  return CC_OK;
+}
+
+bool is_pow2(int n) { return n >= 1 && (n & (n - 1)) == 0; }
+int ilog2(int n) {
+  int l = 0;
+  while ((1 << l) < n) ++l;
+  return l;
+}
+bool al16(uint64_t v) { return (v & 15u) == 0; }
+bool al16p(const void* p) { return al16((uint64_t)(uintptr_t)p); }
+uint64_t rup(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+const cc_config_t kDefaultCfg = {CC_ALGO_RING, 0, nullptr, 0};
+
+cc_status_t common_checks(int nranks, cc_dtype_t dtype, const cc_config_t* cfg) {
+  if (nranks < 1 || nranks > CC_MAX_RANKS)
+    return fail(CC_ERR_INVALID_ARG, "nranks=%d outside [1, %d]", nranks, CC_MAX_RANKS);
+  if ((int)dtype < 0 || (int)dtype > 2) return fail(CC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if ((int)cfg->algo < 0 || (int)cfg->algo > 2) return fail(CC_ERR_INVALID_ARG, "unknown algo %d", (int)cfg->algo);
+  if (cfg->fuse_depth < 0) return fail(CC_ERR_INVALID_ARG, "fuse_depth=%d is negative", cfg->fuse_depth);
+  return CC_OK;
+}
+
+// nbytes per rank buffer; N buffers at base + r*stride must not overlap each
+// other and the base must be set when there is data.
+cc_status_t check_side(const cc_rankbuf_t& s, uint64_t nbytes, int N, const char* name) {
+  if (nbytes == 0) return CC_OK;
+  if (s.base == nullptr) return fail(CC_ERR_INVALID_ARG, "%s.base is NULL", name);
+  if (N > 1 && s.rank_stride_bytes < nbytes)
+    return fail(CC_ERR_INVALID_ARG, "%s.rank_stride_bytes=%zu is smaller than a rank's %llu bytes", name,
+                s.rank_stride_bytes, (unsigned long long)nbytes);
+  return CC_OK;
+}
+
+// Any byte shared between a rank buffer of `a` and one of `b`?
+bool sides_overlap(const cc_rankbuf_t& a, uint64_t abytes, int an, const cc_rankbuf_t& b, uint64_t bbytes,
+                   int bn) {
+  if (abytes == 0 || bbytes == 0) return false;
+  const uint64_t ab = (uint64_t)(uintptr_t)a.base, bb = (uint64_t)(uintptr_t)b.base;
+  for (int i = 0; i < an; ++i) {
+    const uint64_t a0 = ab + (uint64_t)i * a.rank_stride_bytes, a1 = a0 + abytes;
+    for (int j = 0; j < bn; ++j) {
+      const uint64_t b0 = bb + (uint64_t)j * b.rank_stride_bytes, b1 = b0 + bbytes;
+      if (a0 < b1 && b0 < a1) return true;
+    }
+  }
+  return false;
+}
+
+bool same_side(const cc_rankbuf_t& a, const cc_rankbuf_t& b) {
+  return a.base == b.base && a.rank_stride_bytes == b.rank_stride_bytes;
+}
+
+cc_status_t grid_fits(uint64_t M, int dt) {
+  if (num_tiles(M, dt) > 0x7fffffffull) return fail(CC_ERR_INVALID_ARG, "count too large for one launch");
+  return CC_OK;
+}
+
+Side side(const cc_rankbuf_t& s) { return Side{(char*)s.base, (uint64_t)s.rank_stride_bytes}; }
+
+// ---- workspace sizing (bytes); M is the full per-rank vector length
+uint64_t ws_need(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt) {
+  if (N <= 1 || cfg.fuse_depth == 0) return 0;
+  const uint64_t per_elem = M * 4;
+  const uint64_t per_rank = N * rup(per_elem, 256);
+  const int k = std::min(cfg.fuse_depth, N - 1);
+  if (coll == CC_COLL_ALL_REDUCE) {
+    if (dt != DT_BF16) return 0;
+    if (cfg.algo == CC_ALGO_RING) return k < N - 1 ? per_elem : 0;
+    return N >= 4 ? per_rank : 0;  // halving-doubling and butterfly, fp32 partials per rank
+  }
+  if (coll == CC_COLL_REDUCE_SCATTER) {
+    if (cfg.algo == CC_ALGO_RING) return k < N - 1 ? per_elem : 0;
+    if (cfg.algo == CC_ALGO_HALVING_DOUBLING) return N >= 4 ? per_rank : 0;
+  }
+  return 0;
+}
+
+cc_status_t check_ws(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt) {
+  const uint64_t need = ws_need(coll, cfg, N, M, dt);
+  if (need == 0) return CC_OK;
+  if (cfg.workspace == nullptr || cfg.workspace_bytes < need)
+    return fail(CC_ERR_INVALID_ARG,
+                "this schedule needs %llu bytes of workspace (cc_workspace_size); got %zu",
+                (unsigned long long)need, cfg.workspace ? cfg.workspace_bytes : (size_t)0);
+  return CC_OK;
+}
+
+Side ws_side(const cc_config_t& cfg, uint64_t M) {
+  return Side{(char*)cfg.workspace, rup(M * 4, 256)};
+}
+
+cc_status_t copy_ranks(const cc_rankbuf_t& src, const cc_rankbuf_t& dst, uint64_t nbytes, int N, int esize,
+                       hipStream_t st) {
+  std::vector<CopyDesc> d;
+  for (int r = 0; r < N; ++r)
+    d.push_back(CopyDesc{(const char*)src.base + (uint64_t)r * src.rank_stride_bytes,
+                         (char*)dst.base + (uint64_t)r * dst.rank_stride_bytes, nbytes});
+  for (size_t i = 0; i < d.size(); i += kMaxDesc) {
+    const int n = (int)std::min<size_t>(kMaxDesc, d.size() - i);
+    hipError_t e = launch_copies(d.data() + i, n, esize, st);
+    if (e != hipSuccess) return hip_status(e, "copy launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cc_version(void) { return "cc 0.1.0 (gfx950)"; }
+
+const char* cc_status_string(cc_status_t s) {
+  switch (s) {
+    case CC_OK: return "CC_OK";
+    case CC_ERR_INVALID_ARG: return "CC_ERR_INVALID_ARG";
+    case CC_ERR_UNSUPPORTED: return "CC_ERR_UNSUPPORTED";
+    case CC_ERR_NO_DEVICE: return "CC_ERR_NO_DEVICE";
+    case CC_ERR_HIP: return "CC_ERR_HIP";
+  }
+  return "CC_ERR_UNKNOWN";
+}
+
+const char* cc_last_error(void) { return g_err.c_str(); }
+
+cc_status_t cc_chunk_bounds(size_t count, int nranks, size_t* bounds) {
+  if (nranks < 1 || nranks > CC_MAX_RANKS) return fail(CC_ERR_INVALID_ARG, "nranks=%d", nranks);
+  if (!bounds) return fail(CC_ERR_INVALID_ARG, "bounds is NULL");
+  for (int c = 0; c <= nranks; ++c)
+    bounds[c] = (size_t)(((unsigned __int128)c * count) / (unsigned)nranks);
+  return ok();
+}
+
+cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype, cc_op_t op,
+                          int nranks, const cc_config_t* cfgp, cc_stream_t stream) {
+  const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
+  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  if (s) return s;
+  if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
+  const int N = nranks, dt = (int)dtype, es = elem_size(dt);
+  if (cfg.algo != CC_ALGO_RING && !is_pow2(N))
+    return fail(CC_ERR_UNSUPPORTED, "halving-doubling and butterfly need nranks = 2^k (got %d)", N);
+  if (count == 0) return ok();
+  const uint64_t M = count, nb = M * es;
+  if ((s = check_side(send, nb, N, "send")) || (s = check_side(recv, nb, N, "recv"))) return s;
+  const bool in_place = same_side(send, recv);
+  if (!in_place && sides_overlap(send, nb, N, recv, nb, N))
+    return fail(CC_ERR_INVALID_ARG, "send and recv overlap without being the same buffers");
+  if ((s = grid_fits(M, dt))) return s;
+  if ((s = check_ws(CC_COLL_ALL_REDUCE, cfg, N, M, dt))) return s;
+  if ((s = device_ready())) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (N == 1) return in_place ? ok() : copy_ranks(send, recv, nb, 1, es, st);
+
+  Red r;
+  r.send = side(send);
+  r.recv = side(recv);
+  r.ws = ws_side(cfg, M);
+  r.M = M;
+  r.N = N;
+  r.dt = dt;
+  r.op = (int)op;
+  r.rs_mode = 0;
+  r.vec_ok = al16p(send.base) && al16(send.rank_stride_bytes) && al16p(recv.base) && al16(recv.rank_stride_bytes) &&
+             (cfg.workspace == nullptr || al16p(cfg.workspace));
+  r.st = st;
+
+  hipError_t e = hipSuccess;
+  if (cfg.algo == CC_ALGO_RING) {
+    if (cfg.fuse_depth == 0) return hip_status(launch_ring_fused(r), "ring all_reduce");
+    const int k = std::min(cfg.fuse_depth, N - 1);
+    const int pin = dt != DT_BF16;
+    for (int s0 = 0; s0 < N - 1 && e == hipSuccess; s0 += k) e = launch_ring_rs_pass(r, s0, std::min(k, N - 1 - s0), pin);
+    Gat g{r.send, r.recv, M, N, es, 0, r.vec_ok, st};
+    for (int s0 = 0; s0 < N - 1 && e == hipSuccess; s0 += k) e = launch_ring_ag_pass(g, s0, std::min(k, N - 1 - s0));
+    return hip_status(e, "ring all_reduce (stepwise)");
+  }
+  const int tree = cfg.algo == CC_ALGO_HALVING_DOUBLING ? TREE_HD : TREE_BFLY;
+  if (cfg.fuse_depth == 0) return hip_status(launch_tree_fused(r, tree), "tree all_reduce");
+  const int acc_recv = dt != DT_BF16;
+  if (tree == TREE_HD) {
+    for (int d = N / 2; d >= 1 && e == hipSuccess; d /= 2) e = launch_hd_rs_step(r, d, d == N / 2, d == 1, acc_recv);
+    Gat g{r.send, r.recv, M, N, es, 0, r.vec_ok, st};
+    for (int d = 1; d < N && e == hipSuccess; d *= 2) e = launch_hd_ag_step(g, d, 0);
+    return hip_status(e, "halving-doubling all_reduce (stepwise)");
+  }
+  for (int d = 1; d < N && e == hipSuccess; d *= 2) e = launch_bfly_step(r, d, d == 1, 2 * d == N, acc_recv);
+  return hip_status(e, "butterfly all_reduce (stepwise)");
+}
+
+cc_status_t cc_reduce_scatter(cc_rankbuf_t send, cc_rankbuf_t recv, size_t recvcount, cc_dtype_t dtype, cc_op_t op,
+                              int nranks, const cc_config_t* cfgp, cc_stream_t stream) {
+  const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
+  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  if (s) return s;
+  if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
+  const int N = nranks, dt = (int)dtype, es = elem_size(dt);
+  if (cfg.algo == CC_ALGO_BUTTERFLY) return fail(CC_ERR_UNSUPPORTED, "butterfly is defined for all_reduce only");
+  if (cfg.algo == CC_ALGO_HALVING_DOUBLING && !is_pow2(N))
+    return fail(CC_ERR_UNSUPPORTED, "halving-doubling needs nranks = 2^k (got %d)", N);
+  if (recvcount == 0) return ok();
+  const uint64_t S = recvcount, M = (uint64_t)N * S;
+  if ((s = check_side(send, M * es, N, "send")) || (s = check_side(recv, S * es, N, "recv"))) return s;
+  if (sides_overlap(send, M * es, N, recv, S * es, N)) return fail(CC_ERR_INVALID_ARG, "send and recv overlap");
+  if ((s = grid_fits(M, dt))) return s;
+  if ((s = check_ws(CC_COLL_REDUCE_SCATTER, cfg, N, M, dt))) return s;
+  if ((s = device_ready())) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (N == 1) return copy_ranks(send, recv, S * es, 1, es, st);
+
+  Red r;
+  r.send = side(send);
+  r.recv = side(recv);
+  r.ws = ws_side(cfg, M);
+  r.M = M;
+  r.N = N;
+  r.dt = dt;
+  r.op = (int)op;
+  r.rs_mode = 1;
+  r.vec_ok = al16p(send.base) && al16(send.rank_stride_bytes) && al16p(recv.base) && al16(recv.rank_stride_bytes) &&
+             al16(S * es) && (cfg.workspace == nullptr || al16p(cfg.workspace));
+  r.st = st;
+  hipError_t e = hipSuccess;
+  if (cfg.algo == CC_ALGO_RING) {
+    if (cfg.fuse_depth == 0) return hip_status(launch_ring_fused(r), "ring reduce_scatter");
+    const int k = std::min(cfg.fuse_depth, N - 1);
+    for (int s0 = 0; s0 < N - 1 && e == hipSuccess; s0 += k) e = launch_ring_rs_pass(r, s0, std::min(k, N - 1 - s0), 0);
+    return hip_status(e, "ring reduce_scatter (stepwise)");
+  }
+  if (cfg.fuse_depth == 0) return hip_status(launch_tree_fused(r, TREE_HD), "halving-doubling reduce_scatter");
+  for (int d = N / 2; d >= 1 && e == hipSuccess; d /= 2) e = launch_hd_rs_step(r, d, d == N / 2, d == 1, 0);
+  return hip_status(e, "halving-doubling reduce_scatter (stepwise)");
+}
+
+cc_status_t cc_all_gather(cc_rankbuf_t send, cc_rankbuf_t recv, size_t sendcount, cc_dtype_t dtype, int nranks,
+                          const cc_config_t* cfgp, cc_stream_t stream) {
+  const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
+  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  if (s) return s;
+  const int N = nranks, dt = (int)dtype, es = elem_size(dt);
+  if (cfg.algo == CC_ALGO_BUTTERFLY) return fail(CC_ERR_UNSUPPORTED, "butterfly is defined for all_reduce only");
+  if (cfg.algo == CC_ALGO_HALVING_DOUBLING && !is_pow2(N))
+    return fail(CC_ERR_UNSUPPORTED, "halving-doubling needs nranks = 2^k (got %d)", N);
+  if (sendcount == 0) return ok();
+  const uint64_t S = sendcount, M = (uint64_t)N * S;
+  if ((s = check_side(send, S * es, N, "send")) || (s = check_side(recv, M * es, N, "recv"))) return s;
+  if (sides_overlap(send, S * es, N, recv, M * es, N)) return fail(CC_ERR_INVALID_ARG, "send and recv overlap");
+  if ((s = grid_fits(M, dt))) return s;
+  if ((s = device_ready())) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (N == 1) return copy_ranks(send, recv, S * es, 1, es, st);
+  Gat g;
+  g.send = side(send);
+  g.recv = side(recv);
+  g.M = M;
+  g.N = N;
+  g.esize = es;
+  g.ag_mode = 1;
+  g.vec_ok = al16p(send.base) && al16(send.rank_stride_bytes) && al16p(recv.base) && al16(recv.rank_stride_bytes) &&
+             al16(S * es);
+  g.st = st;
+  if (cfg.fuse_depth == 0) return hip_status(launch_ag_fused(g), "all_gather");
+  hipError_t e = hipSuccess;
+  if (cfg.algo == CC_ALGO_RING) {
+    const int k = std::min(cfg.fuse_depth, N - 1);
+    for (int s0 = 0; s0 < N - 1 && e == hipSuccess; s0 += k) e = launch_ring_ag_pass(g, s0, std::min(k, N - 1 - s0));
+    return hip_status(e, "ring all_gather (stepwise)");
+  }
+  for (int d = 1; d < N && e == hipSuccess; d *= 2) e = launch_hd_ag_step(g, d, d == 1);
+  return hip_status(e, "halving-doubling all_gather (stepwise)");
+}
+
+cc_status_t cc_broadcast(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype, int root, int nranks,
+                         const cc_config_t* cfgp, cc_stream_t stream) {
+  const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
+  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  if (s) return s;
+  const int N = nranks, dt = (int)dtype, es = elem_size(dt);
+  if (root < 0 || root >= N) return fail(CC_ERR_INVALID_ARG, "root=%d outside [0, %d)", root, N);
+  if (cfg.algo == CC_ALGO_BUTTERFLY) return fail(CC_ERR_UNSUPPORTED, "butterfly is defined for all_reduce only");
+  if (count == 0) return ok();
+  const uint64_t nb = (uint64_t)count * es;
+  if ((s = check_side(recv, nb, N, "recv"))) return s;
+  if (send.base == nullptr) return fail(CC_ERR_INVALID_ARG, "send.base is NULL");
+  const bool in_place = same_side(send, recv);
+  const cc_rankbuf_t src_rank = {(char*)send.base + (uint64_t)root * send.rank_stride_bytes, 0};
+  if (!in_place && sides_overlap(src_rank, nb, 1, recv, nb, N))
+    return fail(CC_ERR_INVALID_ARG, "the root's send buffer overlaps a recv buffer");
+  if (nb / 16 / kUnroll / kBlock > 0x7fffffffull) return fail(CC_ERR_INVALID_ARG, "count too large");
+  if ((s = device_ready())) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const char* src = (const char*)src_rank.base;
+  Side dst = side(recv);
+  const int vec_ok = al16p(src) && al16p(recv.base) && al16(recv.rank_stride_bytes);
+  if (cfg.fuse_depth == 0 || N == 1)
+    return hip_status(launch_bcast(src, dst, N, in_place ? root : -1, nb, vec_ok, st), "broadcast");
+  // stepwise: the root's own output first, then the chain or binomial steps
+  hipError_t e = hipSuccess;
+  auto rank_ptr = [&](int r) { return dst.base + (uint64_t)((r % N + N) % N) * dst.stride; };
+  if (!in_place) {
+    CopyDesc d{src, rank_ptr(root), nb};
+    e = launch_copies(&d, 1, es, st);
+  }
+  if (cfg.algo == CC_ALGO_RING) {
+    for (int s0 = 0; s0 < N - 1 && e == hipSuccess; ++s0) {
+      CopyDesc d{rank_ptr(root + s0), rank_ptr(root + s0 + 1), nb};
+      e = launch_copies(&d, 1, es, st);
+    }
+    return hip_status(e, "ring broadcast (stepwise)");
+  }
+  for (int k = 1; k < N && e == hipSuccess; k *= 2) {
+    std::vector<CopyDesc> d;
+    for (int rel = 0; rel < k && rel + k < N; ++rel) d.push_back(CopyDesc{rank_ptr(root + rel), rank_ptr(root + rel + k), nb});
+    for (size_t i = 0; i < d.size() && e == hipSuccess; i += kMaxDesc)
+      e = launch_copies(d.data() + i, (int)std::min<size_t>(kMaxDesc, d.size() - i), es, st);
+  }
+  return hip_status(e, "binomial broadcast (stepwise)");
+}
+
+cc_status_t cc_all_to_all(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* counts, size_t elem_per_row,
+                          cc_dtype_t dtype, int nranks, const cc_config_t* cfgp, cc_stream_t stream) {
+  const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
+  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  if (s) return s;
+  const int N = nranks, dt = (int)dtype, es = elem_size(dt);
+  if (cfg.algo != CC_ALGO_RING) return fail(CC_ERR_UNSUPPORTED, "all_to_all supports the ring/pairwise schedule only");
+  if (counts == nullptr) return fail(CC_ERR_INVALID_ARG, "counts is NULL");
+  if (elem_per_row == 0) return fail(CC_ERR_INVALID_ARG, "elem_per_row is 0");
+  const unsigned __int128 row_bytes = (unsigned __int128)elem_per_row * es;
+  std::vector<uint64_t> sdisp((size_t)N * N), rdisp((size_t)N * N), stot(N, 0), rtot(N, 0);
+  for (int i = 0; i < N; ++i)
+    for (int j = 0; j < N; ++j) {
+      const unsigned __int128 b = (unsigned __int128)counts[i * N + j] * row_bytes;
+      if (b >> 62) return fail(CC_ERR_INVALID_ARG, "counts[%d][%d] too large", i, j);
+      sdisp[i * N + j] = stot[i];
+      stot[i] += (uint64_t)b;
+      if ((stot[i] >> 62)) return fail(CC_ERR_INVALID_ARG, "send size too large");
+    }
+  for (int j = 0; j < N; ++j)
+    for (int i = 0; i < N; ++i) {
+      rdisp[i * N + j] = rtot[j];
+      rtot[j] += (uint64_t)((unsigned __int128)counts[i * N + j] * row_bytes);
+      if ((rtot[j] >> 62)) return fail(CC_ERR_INVALID_ARG, "recv size too large");
+    }
+  const uint64_t smax = *std::max_element(stot.begin(), stot.end());
+  const uint64_t rmax = *std::max_element(rtot.begin(), rtot.end());
+  if ((s = check_side(send, smax, N, "send")) || (s = check_side(recv, rmax, N, "recv"))) return s;
+  if (sides_overlap(send, smax, N, recv, rmax, N)) return fail(CC_ERR_INVALID_ARG, "send and recv overlap");
+  if (smax == 0) return ok();
+  if (smax / (uint64_t)(kBlock * 4 * 16) > 0x7fffffffull / (uint64_t)N)
+    return fail(CC_ERR_INVALID_ARG, "counts too large for one launch");
+  if ((s = device_ready())) return s;
+  hipStream_t st = (hipStream_t)stream;
+  auto desc = [&](int i, int j) {
+    return CopyDesc{(const char*)send.base + (uint64_t)i * send.rank_stride_bytes + sdisp[i * N + j],
+                    (char*)recv.base + (uint64_t)j * recv.rank_stride_bytes + rdisp[i * N + j],
+                    (uint64_t)((unsigned __int128)counts[i * N + j] * row_bytes)};
+  };
+  hipError_t e = hipSuccess;
+  std::vector<CopyDesc> d;
+  if (cfg.fuse_depth == 0) {
+    for (int j = 0; j < N; ++j)
+      for (int i = 0; i < N; ++i) d.push_back(desc(i, j));
+    for (size_t i = 0; i < d.size() && e == hipSuccess; i += kMaxDesc)
+      e = launch_copies(d.data() + i, (int)std::min<size_t>(kMaxDesc, d.size() - i), es, st);
+    return hip_status(e, "all_to_all");
+  }
+  for (int k = 0; k < N && e == hipSuccess; ++k) {  // pairwise: step k sends i -> i+k
+    d.clear();
+    for (int i = 0; i < N; ++i) d.push_back(desc(i, (i + k) % N));
+    e = launch_copies(d.data(), N, es, st);
+  }
+  return hip_status(e, "pairwise all_to_all");
+}
+
+cc_status_t cc_workspace_size(cc_coll_t coll, const cc_config_t* cfgp, int nranks, size_t count, cc_dtype_t dtype,
+                              size_t* bytes) {
+  const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
+  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  if (s) return s;
+  if (!bytes) return fail(CC_ERR_INVALID_ARG, "bytes is NULL");
+  if ((int)coll < 0 || (int)coll > 4) return fail(CC_ERR_INVALID_ARG, "unknown collective %d", (int)coll);
+  uint64_t M = count;
+  if (coll == CC_COLL_REDUCE_SCATTER) M = (uint64_t)count * nranks;
+  *bytes = (size_t)ws_need(coll, cfg, nranks, M, (int)dtype);
+  return ok();
+}
+
+cc_status_t cc_get_traffic(cc_coll_t coll, cc_algo_t algo, int nranks, size_t count, cc_dtype_t dtype,
+                           uint64_t* max_bytes, int* steps) {
+  cc_config_t cfg = kDefaultCfg;
+  cfg.algo = algo;
+  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  if (s) return s;
+  if (!max_bytes || !steps) return fail(CC_ERR_INVALID_ARG, "NULL output");
+  const int N = nranks;
+  const uint64_t es = elem_size((int)dtype);
+  if (algo != CC_ALGO_RING && coll != CC_COLL_BROADCAST && !is_pow2(N))
+    return fail(CC_ERR_UNSUPPORTED, "needs nranks = 2^k");
+  // chunk sizes of a per-rank vector of M elements
+  auto sizes = [&](uint64_t M) {
+    std::vector<uint64_t> z(N);
+    for (int c = 0; c < N; ++c)
+      z[c] = (uint64_t)(((unsigned __int128)(c + 1) * M) / N - ((unsigned __int128)c * M) / N);
+    return z;
+  };
+  uint64_t best = 0;
+  int st = 0;
+  const int L = ilog2(N);
+  switch (coll) {
+    case CC_COLL_ALL_REDUCE: {
+      const auto z = sizes(count);
+      if (algo == CC_ALGO_RING) {
+        // ReduceScatter sends every chunk but (r+1); AllGather every chunk but (r+2)
+        for (int r = 0; r < N; ++r) {
+          uint64_t t = 0;
+          for (int q = 0; q < N - 1; ++q) t += z[((r - q) % N + N) % N] + z[((r + 1 - q) % N + N) % N];
+          best = std::max(best, t);
+        }
+        st = 2 * (N - 1);
+      } else if (algo == CC_ALGO_HALVING_DOUBLING) {
+        // rank i sends, per halving step with distance d, the half of its
+        // range [i & ~(2d-1), +2d) that does not hold chunk i, and per
+        // doubling step the range [i & ~(d-1), +d) it holds
+        std::vector<uint64_t> pre(N + 1, 0);
+        for (int c = 0; c < N; ++c) pre[c + 1] = pre[c] + z[c];
+        auto span = [&](int b0, int len) { return pre[b0 + len] - pre[b0]; };
+        for (int i = 0; i < N; ++i) {
+          uint64_t t = 0;
+          for (int d = N / 2; d >= 1; d /= 2) t += span((i & ~(2 * d - 1)) + ((i & d) ? 0 : d), d);
+          for (int d = 1; d < N; d *= 2) t += span(i & ~(d - 1), d);
+          best = std::max(best, t);
+        }
+        st = 2 * L;
+      } else {
+        best = (uint64_t)L * count;
+        st = L;
+      }
+      break;
+    }
+    case CC_COLL_REDUCE_SCATTER:
+    case CC_COLL_ALL_GATHER:
+      // count = per-rank shard; every rank sends all chunks but one, for both schedules
+      best = (uint64_t)(N - 1) * count;
+      st = algo == CC_ALGO_RING ? N - 1 : L;
+      if (algo == CC_ALGO_BUTTERFLY) return fail(CC_ERR_UNSUPPORTED, "butterfly is defined for all_reduce only");
+      break;
+    case CC_COLL_BROADCAST:
+      if (algo == CC_ALGO_BUTTERFLY) return fail(CC_ERR_UNSUPPORTED, "butterfly is defined for all_reduce only");
+      if (algo == CC_ALGO_RING) {
+        best = N > 1 ? count : 0;
+        st = N - 1;
+      } else {
+        best = (uint64_t)L * count;  // the root sends in every doubling step
+        st = L;
+      }
+      break;
+    case CC_COLL_ALL_TO_ALL:
+      if (algo != CC_ALGO_RING) return fail(CC_ERR_UNSUPPORTED, "all_to_all supports the pairwise schedule only");
+      best = (uint64_t)(N - 1) * count;  // count = elements per (source, destination) block
+      st = N - 1;
+      break;
+    default:
+      return fail(CC_ERR_INVALID_ARG, "unknown collective");
+  }
+  *max_bytes = best * es;
+  *steps = st;
+  return ok();
+}
+
+}  // extern "C"

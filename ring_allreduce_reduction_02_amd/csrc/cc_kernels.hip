@@ -1,0 +1,1005 @@
+// HIP kernels (gfx950 / CDNA4) of the collective-reduction engine.
+//
+// N logical ranks are rank-strided buffers in one GPU's HBM.  Every kernel
+// gives one thread ownership of an element index e across all N ranks: it
+// does every read, combine and write that the schedule step performs on e.
+// So no step kernel can race with itself, in place or not, and steps are
+// ordered by the stream.
+//
+// The work is streaming and elementwise (one combine per element and rank,
+// a few per byte), so the bound is HBM bandwidth, not the ALUs or matrix
+// cores: the kernels move 16-byte vectors per lane with nontemporal loads and
+// stores, keep partial results in registers, and derive the chunk of a tile
+// once per workgroup so that the rank addresses stay in scalar registers.
+//
+// Schedules (the "AllReduce" algorithm notes, 算法一/二/四; textbook ch. 6
+// "集合通信", Ring AllReduce / Algorithm 1):
+//  * ring: chunk c's ReduceScatter fold starts at rank c (c+1 for a standalone
+//    ReduceScatter) and each step folds in the next rank as
+//    acc = op(x_next, acc); the owner then forwards the result around the
+//    ring (AllGather).
+//  * halving-doubling: distance N/2 first; for every element the fold tree
+//    pairs ranks that differ in the top bit, then the next bit, ...
+//  * butterfly: distance 1 first; the tree pairs neighbours 2j, 2j+1 first.
+// SUM, PROD and the IEEE maximum are commutative bit for bit, so only the
+// association tree matters; it is reproduced exactly.
+
+#include <stdint.h>
+
+#include "cc_launch.h"
+
+namespace cc {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+// ------------------------------------------------------------------ types
+
+template <int DT>
+struct Ty;
+template <>
+struct Ty<DT_I32> {
+  typedef uint32_t A;  // accumulate in uint32: SUM/PROD wrap modulo 2^32
+  static constexpr int V = 4;
+  static constexpr int SZ = 4;
+};
+template <>
+struct Ty<DT_F32> {
+  typedef float A;
+  static constexpr int V = 4;
+  static constexpr int SZ = 4;
+};
+template <>
+struct Ty<DT_BF16> {
+  typedef float A;  // bf16 widened exactly; partials stay fp32
+  static constexpr int V = 8;
+  static constexpr int SZ = 2;
+};
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet, sign kept),
+// overflow carries into the exponent and gives +-inf.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack(u32x4 w, typename Ty<DT>::A* x) {
+  if constexpr (DT == DT_I32) {
+    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+  } else if constexpr (DT == DT_F32) {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+  } else {
+    x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
+    x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xffff0000u);
+    x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xffff0000u);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 pack(const typename Ty<DT>::A* x) {
+  u32x4 w;
+  if constexpr (DT == DT_I32) {
+    w.x = x[0]; w.y = x[1]; w.z = x[2]; w.w = x[3];
+  } else if constexpr (DT == DT_F32) {
+    w.x = __float_as_uint(x[0]); w.y = __float_as_uint(x[1]);
+    w.z = __float_as_uint(x[2]); w.w = __float_as_uint(x[3]);
+  } else {
+    w.x = bf16_rne(x[0]) | (bf16_rne(x[1]) << 16);
+    w.y = bf16_rne(x[2]) | (bf16_rne(x[3]) << 16);
+    w.z = bf16_rne(x[4]) | (bf16_rne(x[5]) << 16);
+    w.w = bf16_rne(x[6]) | (bf16_rne(x[7]) << 16);
+  }
+  return w;
+}
+
+// accumulator <-> its 32-bit pattern (staging buffers hold accumulators)
+template <int DT>
+__device__ __forceinline__ typename Ty<DT>::A from_bits(uint32_t b) {
+  if constexpr (DT == DT_I32) return b; else return __uint_as_float(b);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t to_bits(typename Ty<DT>::A a) {
+  if constexpr (DT == DT_I32) return a; else return __float_as_uint(a);
+}
+
+// one element in the buffer type
+template <int DT>
+__device__ __forceinline__ typename Ty<DT>::A ld1(const char* p) {
+  if constexpr (DT == DT_BF16) return __uint_as_float((uint32_t)(*(const uint16_t*)p) << 16);
+  else if constexpr (DT == DT_F32) return *(const float*)p;
+  else return *(const uint32_t*)p;
+}
+template <int DT>
+__device__ __forceinline__ void st1(char* p, typename Ty<DT>::A v) {
+  if constexpr (DT == DT_BF16) *(uint16_t*)p = (uint16_t)bf16_rne(v);
+  else if constexpr (DT == DT_F32) *(float*)p = v;
+  else *(uint32_t*)p = v;
+}
+// one accumulator in a staging buffer
+template <int DT>
+__device__ __forceinline__ typename Ty<DT>::A ldw1(const char* p) {
+  return from_bits<DT>(*(const uint32_t*)p);
+}
+template <int DT>
+__device__ __forceinline__ void stw1(char* p, typename Ty<DT>::A v) {
+  *(uint32_t*)p = to_bits<DT>(v);
+}
+
+__device__ __forceinline__ u32x4 ldg(const char* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+__device__ __forceinline__ void stg(char* p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4*)p); }
+
+// V accumulators in a staging buffer (4 bytes each, 16-byte aligned)
+template <int DT>
+__device__ __forceinline__ void ldw_vec(const char* p, typename Ty<DT>::A* x) {
+#pragma unroll
+  for (int q = 0; q < Ty<DT>::V / 4; ++q) {
+    u32x4 w = ldg(p + 16 * q);
+    x[4 * q + 0] = from_bits<DT>(w.x); x[4 * q + 1] = from_bits<DT>(w.y);
+    x[4 * q + 2] = from_bits<DT>(w.z); x[4 * q + 3] = from_bits<DT>(w.w);
+  }
+}
+template <int DT>
+__device__ __forceinline__ void stw_vec(char* p, const typename Ty<DT>::A* x) {
+#pragma unroll
+  for (int q = 0; q < Ty<DT>::V / 4; ++q) {
+    u32x4 w;
+    w.x = to_bits<DT>(x[4 * q + 0]); w.y = to_bits<DT>(x[4 * q + 1]);
+    w.z = to_bits<DT>(x[4 * q + 2]); w.w = to_bits<DT>(x[4 * q + 3]);
+    stg(p + 16 * q, w);
+  }
+}
+
+// ------------------------------------------------------------------ operators
+
+__device__ __forceinline__ float fmax_ieee(float a, float b) {
+  if (a != a || b != b) return __uint_as_float(0x7fc00000u);
+  if (a > b) return a;
+  if (b > a) return b;
+  return __uint_as_float(__float_as_uint(a) & __float_as_uint(b));  // +0 beats -0
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ typename Ty<DT>::A opf(typename Ty<DT>::A a, typename Ty<DT>::A b) {
+  if constexpr (DT == DT_I32) {
+    if constexpr (OP == OP_SUM) return a + b;
+    else if constexpr (OP == OP_PROD) return a * b;
+    else return (int32_t)a > (int32_t)b ? a : b;
+  } else {
+    if constexpr (OP == OP_SUM) return a + b;
+    else if constexpr (OP == OP_PROD) return a * b;
+    else return fmax_ieee(a, b);
+  }
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ void opv(const typename Ty<DT>::A* x, typename Ty<DT>::A* acc) {
+#pragma unroll
+  for (int i = 0; i < Ty<DT>::V; ++i) acc[i] = opf<DT, OP>(x[i], acc[i]);
+}
+
+// ------------------------------------------------------------------ chunks
+
+// chunk c holds [floor(c*M/N), floor((c+1)*M/N)); for an element e it is the
+// largest c with floor(c*M/N) <= e, i.e. floor(((e+1)*N - 1) / M).
+__device__ __forceinline__ uint32_t chunk_of(uint64_t e, uint64_t M, uint32_t N) {
+  return (uint32_t)(((e + 1) * (uint64_t)N - 1) / M);
+}
+__device__ __forceinline__ uint64_t bnd(uint32_t c, uint64_t M, uint32_t N) {
+  return ((uint64_t)c * M) / N;
+}
+__device__ __forceinline__ int wrapN(int r, int N) { return r >= N ? r - N : r; }
+__device__ __forceinline__ int modN(int r, int N) { return ((r % N) + N) % N; }
+
+template <int V>
+struct Tile {
+  uint64_t e0, e1;
+  uint32_t c;
+  bool fast;
+};
+
+// The workgroup's element range and, when the whole tile is full-width and
+// lies in one chunk, that chunk (uniform across the workgroup).
+template <int V>
+__device__ __forceinline__ Tile<V> tile_of(uint64_t M, uint32_t N, int vec_ok) {
+  const uint64_t tile = (uint64_t)kBlock * kUnroll * V;
+  Tile<V> t;
+  t.e0 = (uint64_t)blockIdx.x * tile;
+  t.e1 = t.e0 + tile < M ? t.e0 + tile : M;
+  const uint32_t c0 = chunk_of(t.e0, M, N);
+  const uint32_t c1 = chunk_of(t.e1 - 1, M, N);
+  t.c = c0;
+  t.fast = vec_ok && c0 == c1 && (t.e1 - t.e0) == tile;
+  return t;
+}
+
+__device__ __forceinline__ uint64_t vec_elem(uint64_t e0, int u, int V) {
+  return e0 + ((uint64_t)u * kBlock + threadIdx.x) * (uint64_t)V;
+}
+
+// ------------------------------------------------------------------ fused ring
+
+struct FusedArgs {
+  const char* sb;
+  uint64_t ss;
+  char* rb;
+  uint64_t rs;
+  uint64_t M;
+  int N;
+  int rs_mode;
+  int vec_ok;
+};
+
+// AllReduce (rs_mode 0): the N-1 ReduceScatter steps of each chunk folded in
+// registers in ring order, then the AllGather as N stores.  ReduceScatter
+// (rs_mode 1): the fold starts one rank later and only the owner is written.
+template <int DT, int OP, int NR>
+__global__ __launch_bounds__(kBlock) void k_ring_fused(FusedArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const int N = NR > 0 ? NR : a.N;
+  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  if (t.fast) {
+    const int c = (int)t.c;
+    const int start = a.rs_mode ? wrapN(c + 1, N) : c;
+    A acc[kUnroll][V];
+    if constexpr (NR > 0) {
+      u32x4 raw[kUnroll][NR];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t off = vec_elem(t.e0, u, V) * SZ;
+#pragma unroll
+        for (int j = 0; j < NR; ++j) raw[u][j] = ldg(a.sb + (uint64_t)wrapN(start + j, NR) * a.ss + off);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        unpack<DT>(raw[u][0], acc[u]);
+#pragma unroll
+        for (int j = 1; j < NR; ++j) {
+          A x[V];
+          unpack<DT>(raw[u][j], x);
+          opv<DT, OP>(x, acc[u]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t off = vec_elem(t.e0, u, V) * SZ;
+        unpack<DT>(ldg(a.sb + (uint64_t)start * a.ss + off), acc[u]);
+        for (int j = 1; j < N; j += 8) {
+          u32x4 raw[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (j + q < N) raw[q] = ldg(a.sb + (uint64_t)wrapN(start + j + q, N) * a.ss + off);
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (j + q < N) {
+              A x[V];
+              unpack<DT>(raw[q], x);
+              opv<DT, OP>(x, acc[u]);
+            }
+        }
+      }
+    }
+    const uint64_t b0 = a.rs_mode ? bnd((uint32_t)c, a.M, N) : 0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const u32x4 w = pack<DT>(acc[u]);
+      const uint64_t e = vec_elem(t.e0, u, V);
+      if (a.rs_mode) {
+        stg(a.rb + (uint64_t)c * a.rs + (e - b0) * SZ, w);
+      } else {
+        if constexpr (NR > 0) {
+#pragma unroll
+          for (int r = 0; r < NR; ++r) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
+        } else {
+          for (int r = 0; r < N; ++r) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
+        }
+      }
+    }
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      const uint32_t c = chunk_of(e, a.M, N);
+      const int start = a.rs_mode ? wrapN((int)c + 1, N) : (int)c;
+      A acc = ld1<DT>(a.sb + (uint64_t)start * a.ss + e * SZ);
+      for (int j = 1; j < N; ++j)
+        acc = opf<DT, OP>(ld1<DT>(a.sb + (uint64_t)wrapN(start + j, N) * a.ss + e * SZ), acc);
+      if (a.rs_mode) {
+        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - bnd(c, a.M, N)) * SZ, acc);
+      } else {
+        for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fused trees
+
+template <int L>
+__device__ constexpr int bitrev(int t) {
+  int r = 0;
+  for (int i = 0; i < L; ++i)
+    if (t & (1 << i)) r |= 1 << (L - 1 - i);
+  return r;
+}
+template <int NR>
+__device__ constexpr int ilog2() {
+  int l = 0;
+  while ((1 << l) < NR) ++l;
+  return l;
+}
+
+// Pairwise tree over the ranks in load order t = 0..NR-1, adjacent pairs
+// first (a binary counter keeps one partial per level).  For butterfly the
+// order is the rank index itself (distance 1 first); for halving-doubling it
+// is the bit-reversed index, which pairs ranks at distance N/2 first.
+template <int DT, int OP, int NR, int TREE, typename Load>
+__device__ __forceinline__ void tree_fold(Load load, typename Ty<DT>::A* out, int V) {
+  typedef typename Ty<DT>::A A;
+  constexpr int L = ilog2<NR>();
+  constexpr int VM = Ty<DT>::V;
+  A stk[L + 1][VM];
+#pragma unroll
+  for (int t = 0; t < NR; ++t) {
+    const int r = TREE == TREE_HD ? bitrev<L>(t) : t;
+    A v[VM];
+    load(r, v);
+    // t's trailing one bits = the completed subtrees to its left
+    int ones = 0;
+    while ((t >> ones) & 1) ++ones;
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+      if (l < ones) {
+#pragma unroll
+        for (int i = 0; i < VM; ++i)
+          if (i < V) v[i] = opf<DT, OP>(stk[l][i], v[i]);
+      }
+    }
+#pragma unroll
+    for (int l = 0; l <= L; ++l)
+      if (l == ones) {
+#pragma unroll
+        for (int i = 0; i < VM; ++i)
+          if (i < V) stk[l][i] = v[i];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < VM; ++i)
+    if (i < V) out[i] = stk[L][i];
+}
+
+template <int DT, int OP, int NR, int TREE>
+__global__ __launch_bounds__(kBlock) void k_tree_fused(FusedArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const Tile<V> t = tile_of<V>(a.M, NR, a.vec_ok);
+  if (t.fast) {
+    const int c = (int)t.c;
+    const uint64_t b0 = a.rs_mode ? bnd((uint32_t)c, a.M, NR) : 0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t e = vec_elem(t.e0, u, V);
+      A acc[V];
+      tree_fold<DT, OP, NR, TREE>(
+          [&](int r, A* v) { unpack<DT>(ldg(a.sb + (uint64_t)r * a.ss + e * SZ), v); }, acc, V);
+      const u32x4 w = pack<DT>(acc);
+      if (a.rs_mode) {
+        stg(a.rb + (uint64_t)c * a.rs + (e - b0) * SZ, w);
+      } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
+      }
+    }
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      A acc[V];
+      tree_fold<DT, OP, NR, TREE>(
+          [&](int r, A* v) { v[0] = ld1<DT>(a.sb + (uint64_t)r * a.ss + e * SZ); }, acc, 1);
+      if (a.rs_mode) {
+        const uint32_t c = chunk_of(e, a.M, NR);
+        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - bnd(c, a.M, NR)) * SZ, acc[0]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc[0]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ ring steps
+
+struct PassArgs {
+  const char* sb;
+  uint64_t ss;
+  char* rb;
+  uint64_t rs;
+  char* wb;  // staging: one accumulator per element (the chunk's in-flight partial)
+  uint64_t M;
+  int N;
+  int rs_mode;
+  int vec_ok;
+  int s0;
+  int k;
+  int pin_recv;  // partials live in the receiving rank's recv buffer
+};
+
+// Ring ReduceScatter steps s0 .. s0+k-1 for every chunk: the partial that the
+// step-(s0-1) receiver holds is read, the next k ranks' contributions are
+// folded in, and the result is left where the step-(s0+k-1) receiver holds it.
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const int N = a.N;
+  const bool fin = a.s0 + a.k == N - 1;
+  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  if (t.fast) {
+    const int c = (int)t.c;
+    const int start = a.rs_mode ? wrapN(c + 1, N) : c;
+    const uint64_t b0 = bnd((uint32_t)c, a.M, N);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t e = vec_elem(t.e0, u, V);
+      A acc[V];
+      if (a.s0 == 0)
+        unpack<DT>(ldg(a.sb + (uint64_t)start * a.ss + e * SZ), acc);
+      else if (a.pin_recv)
+        unpack<DT>(ldg(a.rb + (uint64_t)wrapN(start + a.s0, N) * a.rs + e * SZ), acc);
+      else
+        ldw_vec<DT>(a.wb + e * 4, acc);
+      for (int j = a.s0 + 1; j <= a.s0 + a.k; ++j) {
+        A x[V];
+        unpack<DT>(ldg(a.sb + (uint64_t)wrapN(start + j, N) * a.ss + e * SZ), x);
+        opv<DT, OP>(x, acc);
+      }
+      if (fin) {
+        if (a.rs_mode)
+          stg(a.rb + (uint64_t)c * a.rs + (e - b0) * SZ, pack<DT>(acc));
+        else
+          stg(a.rb + (uint64_t)wrapN(start + N - 1, N) * a.rs + e * SZ, pack<DT>(acc));
+      } else if (a.pin_recv) {
+        stg(a.rb + (uint64_t)wrapN(start + a.s0 + a.k, N) * a.rs + e * SZ, pack<DT>(acc));
+      } else {
+        stw_vec<DT>(a.wb + e * 4, acc);
+      }
+    }
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      const uint32_t c = chunk_of(e, a.M, N);
+      const int start = a.rs_mode ? wrapN((int)c + 1, N) : (int)c;
+      A acc;
+      if (a.s0 == 0)
+        acc = ld1<DT>(a.sb + (uint64_t)start * a.ss + e * SZ);
+      else if (a.pin_recv)
+        acc = ld1<DT>(a.rb + (uint64_t)wrapN(start + a.s0, N) * a.rs + e * SZ);
+      else
+        acc = ldw1<DT>(a.wb + e * 4);
+      for (int j = a.s0 + 1; j <= a.s0 + a.k; ++j)
+        acc = opf<DT, OP>(ld1<DT>(a.sb + (uint64_t)wrapN(start + j, N) * a.ss + e * SZ), acc);
+      if (fin) {
+        if (a.rs_mode)
+          st1<DT>(a.rb + (uint64_t)c * a.rs + (e - bnd(c, a.M, N)) * SZ, acc);
+        else
+          st1<DT>(a.rb + (uint64_t)wrapN(start + N - 1, N) * a.rs + e * SZ, acc);
+      } else if (a.pin_recv) {
+        st1<DT>(a.rb + (uint64_t)wrapN(start + a.s0 + a.k, N) * a.rs + e * SZ, acc);
+      } else {
+        stw1<DT>(a.wb + e * 4, acc);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ halving-doubling steps
+
+struct StepArgs {
+  const char* sb;
+  uint64_t ss;
+  char* rb;
+  uint64_t rs;
+  char* wb;      // rank-strided accumulators (staging)
+  uint64_t ws;
+  uint64_t M;
+  int N;
+  int rs_mode;
+  int vec_ok;
+  int d;         // partner distance of this step
+  int first;     // operands come from the send buffers
+  int last;      // results are final (buffer type)
+  int acc_recv;  // intermediate accumulators live in recv (else in wb)
+};
+
+template <int DT>
+__device__ __forceinline__ void step_load_vec(const StepArgs& a, int r, uint64_t e, typename Ty<DT>::A* x) {
+  constexpr int SZ = Ty<DT>::SZ;
+  if (a.first) unpack<DT>(ldg(a.sb + (uint64_t)r * a.ss + e * SZ), x);
+  else if (a.acc_recv) unpack<DT>(ldg(a.rb + (uint64_t)r * a.rs + e * SZ), x);
+  else ldw_vec<DT>(a.wb + (uint64_t)r * a.ws + e * 4, x);
+}
+template <int DT>
+__device__ __forceinline__ typename Ty<DT>::A step_load1(const StepArgs& a, int r, uint64_t e) {
+  constexpr int SZ = Ty<DT>::SZ;
+  if (a.first) return ld1<DT>(a.sb + (uint64_t)r * a.ss + e * SZ);
+  if (a.acc_recv) return ld1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ);
+  return ldw1<DT>(a.wb + (uint64_t)r * a.ws + e * 4);
+}
+// intermediate (not last) store of rank r's accumulator
+template <int DT>
+__device__ __forceinline__ void step_store_vec(const StepArgs& a, int r, uint64_t e, const typename Ty<DT>::A* x) {
+  constexpr int SZ = Ty<DT>::SZ;
+  if (a.acc_recv) stg(a.rb + (uint64_t)r * a.rs + e * SZ, pack<DT>(x));
+  else stw_vec<DT>(a.wb + (uint64_t)r * a.ws + e * 4, x);
+}
+template <int DT>
+__device__ __forceinline__ void step_store1(const StepArgs& a, int r, uint64_t e, typename Ty<DT>::A x) {
+  constexpr int SZ = Ty<DT>::SZ;
+  if (a.acc_recv) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, x);
+  else stw1<DT>(a.wb + (uint64_t)r * a.ws + e * 4, x);
+}
+
+// Recursive-halving step with distance d: before it, rank i holds the block
+// range of the ranks that share its bits at and above d; the ranks agreeing
+// with chunk c on those bits keep c and combine the partner's copy of it.
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_hd_rs_step(StepArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const int N = a.N, d = a.d;
+  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  if (t.fast) {
+    const int c = (int)t.c;
+    const int base = c & ~(d - 1);
+    const uint64_t b0 = bnd((uint32_t)c, a.M, N);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t e = vec_elem(t.e0, u, V);
+      for (int m = 0; m < d; ++m) {
+        const int i = base | m, p = i ^ d;
+        A x[V], y[V];
+        step_load_vec<DT>(a, i, e, x);
+        step_load_vec<DT>(a, p, e, y);
+        opv<DT, OP>(y, x);  // x = op(y, x): commutative, the tree is what counts
+        if (a.last) {
+          if (a.rs_mode) stg(a.rb + (uint64_t)c * a.rs + (e - b0) * SZ, pack<DT>(x));
+          else stg(a.rb + (uint64_t)c * a.rs + e * SZ, pack<DT>(x));
+        } else {
+          step_store_vec<DT>(a, i, e, x);
+        }
+      }
+    }
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      const uint32_t c = chunk_of(e, a.M, N);
+      const int base = (int)c & ~(d - 1);
+      for (int m = 0; m < d; ++m) {
+        const int i = base | m, p = i ^ d;
+        A v = opf<DT, OP>(step_load1<DT>(a, p, e), step_load1<DT>(a, i, e));
+        if (a.last) {
+          if (a.rs_mode) st1<DT>(a.rb + (uint64_t)c * a.rs + (e - bnd(c, a.M, N)) * SZ, v);
+          else st1<DT>(a.rb + (uint64_t)c * a.rs + e * SZ, v);
+        } else {
+          step_store1<DT>(a, i, e, v);
+        }
+      }
+    }
+  }
+}
+
+// Butterfly step with distance d: every pair (i, i+d), i without bit d,
+// exchanges the full vector and both keep op of the two.
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_bfly_step(StepArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const int N = a.N, d = a.d;
+  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  if (t.fast) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t e = vec_elem(t.e0, u, V);
+      for (int i = 0; i < N; ++i) {
+        if (i & d) continue;
+        const int p = i | d;
+        A x[V], y[V];
+        step_load_vec<DT>(a, i, e, x);
+        step_load_vec<DT>(a, p, e, y);
+        opv<DT, OP>(y, x);
+        if (a.last) {
+          const u32x4 w = pack<DT>(x);
+          stg(a.rb + (uint64_t)i * a.rs + e * SZ, w);
+          stg(a.rb + (uint64_t)p * a.rs + e * SZ, w);
+        } else {
+          step_store_vec<DT>(a, i, e, x);
+          step_store_vec<DT>(a, p, e, x);
+        }
+      }
+    }
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      for (int i = 0; i < N; ++i) {
+        if (i & d) continue;
+        const int p = i | d;
+        A v = opf<DT, OP>(step_load1<DT>(a, p, e), step_load1<DT>(a, i, e));
+        if (a.last) {
+          st1<DT>(a.rb + (uint64_t)i * a.rs + e * SZ, v);
+          st1<DT>(a.rb + (uint64_t)p * a.rs + e * SZ, v);
+        } else {
+          step_store1<DT>(a, i, e, v);
+          step_store1<DT>(a, p, e, v);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ gathers
+
+struct GatArgs {
+  const char* sb;
+  uint64_t ss;
+  char* rb;
+  uint64_t rs;
+  uint64_t M;
+  int N;
+  int mode;  // 0: AllGather phase of AllReduce (all in recv); 1: standalone
+  int vec_ok;
+  int s0;
+  int k;
+};
+
+// Ring AllGather steps s0 .. s0+k-1: chunk c is copied from the rank that
+// holds it before step s0 to the next k ranks along the ring.  In the
+// AllReduce the owner of chunk c is rank c-1; in the standalone AllGather
+// rank c starts with chunk c (its send buffer) and also keeps a copy.
+template <int SZ>
+__global__ __launch_bounds__(kBlock) void k_ring_ag_pass(GatArgs a) {
+  constexpr int V = 16 / SZ;
+  const int N = a.N;
+  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  if (t.fast) {
+    const int c = (int)t.c;
+    const uint64_t b0 = bnd((uint32_t)c, a.M, N);
+    const bool from_send = a.mode == 1 && a.s0 == 0;
+    const int holder = a.mode == 0 ? modN(c - 1 + a.s0, N) : wrapN(c + a.s0, N);
+    const int first_dst = a.mode == 0 ? wrapN(holder + 1, N) : wrapN(holder + 1, N);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t e = vec_elem(t.e0, u, V);
+      const u32x4 w = from_send ? ldg(a.sb + (uint64_t)c * a.ss + (e - b0) * SZ)
+                                : ldg(a.rb + (uint64_t)holder * a.rs + e * SZ);
+      if (from_send) stg(a.rb + (uint64_t)c * a.rs + e * SZ, w);
+      for (int q = 0; q < a.k; ++q) stg(a.rb + (uint64_t)modN(first_dst + q, N) * a.rs + e * SZ, w);
+    }
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      const int c = (int)chunk_of(e, a.M, N);
+      const bool from_send = a.mode == 1 && a.s0 == 0;
+      const int holder = a.mode == 0 ? modN(c - 1 + a.s0, N) : wrapN(c + a.s0, N);
+      const char* src = from_send ? a.sb + (uint64_t)c * a.ss + (e - bnd((uint32_t)c, a.M, N)) * SZ
+                                  : a.rb + (uint64_t)holder * a.rs + e * SZ;
+      if constexpr (SZ == 2) {
+        const uint16_t v = *(const uint16_t*)src;
+        if (from_send) *(uint16_t*)(a.rb + (uint64_t)c * a.rs + e * SZ) = v;
+        for (int q = 0; q < a.k; ++q) *(uint16_t*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v;
+      } else {
+        const uint32_t v = *(const uint32_t*)src;
+        if (from_send) *(uint32_t*)(a.rb + (uint64_t)c * a.rs + e * SZ) = v;
+        for (int q = 0; q < a.k; ++q) *(uint32_t*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v;
+      }
+    }
+  }
+}
+
+// Recursive-doubling AllGather step with distance d: the ranks whose partner
+// (rank XOR d) holds chunk c receive it.
+template <int SZ>
+__global__ __launch_bounds__(kBlock) void k_hd_ag_step(GatArgs a) {
+  constexpr int V = 16 / SZ;
+  const int N = a.N, d = a.s0, first = a.k;  // s0 carries d, k carries "first"
+  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  if (t.fast) {
+    const int c = (int)t.c;
+    const uint64_t b0 = bnd((uint32_t)c, a.M, N);
+    const int base = (c ^ d) & ~(d - 1);
+    const bool from_send = a.mode == 1 && first;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t e = vec_elem(t.e0, u, V);
+      if (from_send) {
+        const u32x4 w = ldg(a.sb + (uint64_t)c * a.ss + (e - b0) * SZ);
+        stg(a.rb + (uint64_t)c * a.rs + e * SZ, w);
+        stg(a.rb + (uint64_t)(c ^ 1) * a.rs + e * SZ, w);
+      } else {
+        for (int m = 0; m < d; ++m) {
+          const int i = base | m, p = i ^ d;
+          stg(a.rb + (uint64_t)i * a.rs + e * SZ, ldg(a.rb + (uint64_t)p * a.rs + e * SZ));
+        }
+      }
+    }
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      const int c = (int)chunk_of(e, a.M, N);
+      const int base = (c ^ d) & ~(d - 1);
+      if (a.mode == 1 && first) {
+        const char* src = a.sb + (uint64_t)c * a.ss + (e - bnd((uint32_t)c, a.M, N)) * SZ;
+        for (int q = 0; q < 2; ++q) {
+          char* dst = a.rb + (uint64_t)(q ? (c ^ 1) : c) * a.rs + e * SZ;
+          if constexpr (SZ == 2) *(uint16_t*)dst = *(const uint16_t*)src;
+          else *(uint32_t*)dst = *(const uint32_t*)src;
+        }
+      } else {
+        for (int m = 0; m < d; ++m) {
+          const int i = base | m, p = i ^ d;
+          const char* src = a.rb + (uint64_t)p * a.rs + e * SZ;
+          char* dst = a.rb + (uint64_t)i * a.rs + e * SZ;
+          if constexpr (SZ == 2) *(uint16_t*)dst = *(const uint16_t*)src;
+          else *(uint32_t*)dst = *(const uint32_t*)src;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ copies
+
+struct BcArgs {
+  const char* src;
+  char* db;
+  uint64_t ds;
+  uint64_t nbytes;
+  int N;
+  int skip;
+  int vec_ok;
+};
+
+// One read of the root's buffer, N (or N-1) writes.
+__global__ __launch_bounds__(kBlock) void k_bcast(BcArgs a) {
+  const uint64_t tile = (uint64_t)kBlock * kUnroll * 16;
+  const uint64_t b0 = (uint64_t)blockIdx.x * tile;
+  const uint64_t b1 = b0 + tile < a.nbytes ? b0 + tile : a.nbytes;
+  if (a.vec_ok && b1 - b0 == tile) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t off = b0 + ((uint64_t)u * kBlock + threadIdx.x) * 16;
+      const u32x4 w = ldg(a.src + off);
+      for (int r = 0; r < a.N; ++r)
+        if (r != a.skip) stg(a.db + (uint64_t)r * a.ds + off, w);
+    }
+  } else {
+    for (uint64_t b = b0 + threadIdx.x; b < b1; b += kBlock) {
+      const uint8_t v = (uint8_t)a.src[b];
+      for (int r = 0; r < a.N; ++r)
+        if (r != a.skip) a.db[(uint64_t)r * a.ds + b] = (char)v;
+    }
+  }
+}
+
+struct CopyArgs {
+  const char* src[kMaxDesc];
+  char* dst[kMaxDesc];
+  uint64_t bytes[kMaxDesc];
+  uint64_t tpre[kMaxDesc + 1];  // prefix sums of tiles per descriptor
+  uint64_t vecmask;             // bit i: descriptor i is 16-byte aligned
+  int n;
+  int esize;
+};
+
+constexpr uint64_t kCopyTile = (uint64_t)kBlock * 4 * 16;
+
+// Flat tiling over a list of copies: workgroup b copies tile (b - tpre[k]) of
+// descriptor k, so skewed block sizes still spread over the whole chip.
+__global__ __launch_bounds__(kBlock) void k_copies(CopyArgs a) {
+  const uint64_t b = blockIdx.x;
+  int k = 0;
+  while (k + 1 < a.n && b >= a.tpre[k + 1]) ++k;
+  const uint64_t o0 = (b - a.tpre[k]) * kCopyTile;
+  const uint64_t nb = a.bytes[k];
+  const uint64_t o1 = o0 + kCopyTile < nb ? o0 + kCopyTile : nb;
+  const char* src = a.src[k];
+  char* dst = a.dst[k];
+  if (((a.vecmask >> k) & 1) && o1 - o0 == kCopyTile) {
+    u32x4 w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = ldg(src + o0 + ((uint64_t)u * kBlock + threadIdx.x) * 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) stg(dst + o0 + ((uint64_t)u * kBlock + threadIdx.x) * 16, w[u]);
+  } else if (((a.vecmask >> k) & 1)) {
+    for (uint64_t o = o0 + (uint64_t)threadIdx.x * 16; o < o1; o += (uint64_t)kBlock * 16)
+      stg(dst + o, ldg(src + o));
+  } else {
+    for (uint64_t o = o0 + threadIdx.x; o < o1; o += kBlock) dst[o] = src[o];
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+template <typename F>
+hipError_t by_dt_op(int dt, int op, F f) {
+  switch (dt * 3 + op) {
+    case 0: return f(IC<DT_I32>{}, IC<OP_SUM>{});
+    case 1: return f(IC<DT_I32>{}, IC<OP_MAX>{});
+    case 2: return f(IC<DT_I32>{}, IC<OP_PROD>{});
+    case 3: return f(IC<DT_F32>{}, IC<OP_SUM>{});
+    case 4: return f(IC<DT_F32>{}, IC<OP_MAX>{});
+    case 5: return f(IC<DT_F32>{}, IC<OP_PROD>{});
+    case 6: return f(IC<DT_BF16>{}, IC<OP_SUM>{});
+    case 7: return f(IC<DT_BF16>{}, IC<OP_MAX>{});
+    case 8: return f(IC<DT_BF16>{}, IC<OP_PROD>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+FusedArgs fused_args(const Red& r) {
+  FusedArgs a;
+  a.sb = r.send.base; a.ss = r.send.stride;
+  a.rb = r.recv.base; a.rs = r.recv.stride;
+  a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_ring_fused(const Red& r) {
+  const FusedArgs a = fused_args(r);
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    switch (r.N) {
+      case 2: hipLaunchKernelGGL((k_ring_fused<DT, OP, 2>), grid, blk, 0, r.st, a); break;
+      case 3: hipLaunchKernelGGL((k_ring_fused<DT, OP, 3>), grid, blk, 0, r.st, a); break;
+      case 4: hipLaunchKernelGGL((k_ring_fused<DT, OP, 4>), grid, blk, 0, r.st, a); break;
+      case 8: hipLaunchKernelGGL((k_ring_fused<DT, OP, 8>), grid, blk, 0, r.st, a); break;
+      case 16: hipLaunchKernelGGL((k_ring_fused<DT, OP, 16>), grid, blk, 0, r.st, a); break;
+      default: hipLaunchKernelGGL((k_ring_fused<DT, OP, 0>), grid, blk, 0, r.st, a); break;
+    }
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_tree_fused(const Red& r, int tree) {
+  const FusedArgs a = fused_args(r);
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+#define CC_TREE_CASE(NR)                                                                      \
+  case NR:                                                                                    \
+    if (tree == TREE_HD)                                                                      \
+      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_HD>), grid, blk, 0, r.st, a);         \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_BFLY>), grid, blk, 0, r.st, a);       \
+    break;
+    switch (r.N) {
+      CC_TREE_CASE(2)
+      CC_TREE_CASE(4)
+      CC_TREE_CASE(8)
+      CC_TREE_CASE(16)
+      CC_TREE_CASE(32)
+      CC_TREE_CASE(64)
+      default: return hipErrorInvalidValue;
+    }
+#undef CC_TREE_CASE
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv) {
+  PassArgs a;
+  a.sb = r.send.base; a.ss = r.send.stride;
+  a.rb = r.recv.base; a.rs = r.recv.stride;
+  a.wb = r.ws.base;
+  a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
+  a.s0 = s0; a.k = k; a.pin_recv = partial_in_recv;
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    hipLaunchKernelGGL((k_ring_pass<DT, OP>), grid, blk, 0, r.st, a);
+    return hipGetLastError();
+  });
+}
+
+static StepArgs step_args(const Red& r, int d, int first, int last, int acc_in_recv) {
+  StepArgs a;
+  a.sb = r.send.base; a.ss = r.send.stride;
+  a.rb = r.recv.base; a.rs = r.recv.stride;
+  a.wb = r.ws.base; a.ws = r.ws.stride;
+  a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
+  a.d = d; a.first = first; a.last = last; a.acc_recv = acc_in_recv;
+  return a;
+}
+
+hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_in_recv) {
+  const StepArgs a = step_args(r, d, first, last, acc_in_recv);
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    hipLaunchKernelGGL((k_hd_rs_step<DT, OP>), grid, blk, 0, r.st, a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_bfly_step(const Red& r, int d, int first, int last, int acc_in_recv) {
+  const StepArgs a = step_args(r, d, first, last, acc_in_recv);
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    hipLaunchKernelGGL((k_bfly_step<DT, OP>), grid, blk, 0, r.st, a);
+    return hipGetLastError();
+  });
+}
+
+static GatArgs gat_args(const Gat& g, int s0, int k) {
+  GatArgs a;
+  a.sb = g.send.base; a.ss = g.send.stride;
+  a.rb = g.recv.base; a.rs = g.recv.stride;
+  a.M = g.M; a.N = g.N; a.mode = g.ag_mode; a.vec_ok = g.vec_ok;
+  a.s0 = s0; a.k = k;
+  return a;
+}
+
+static unsigned gat_tiles(const Gat& g) {
+  const uint64_t tile = (uint64_t)kBlock * kUnroll * (16 / g.esize);
+  return (unsigned)((g.M + tile - 1) / tile);
+}
+
+hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k) {
+  const GatArgs a = gat_args(g, s0, k);
+  const dim3 grid(gat_tiles(g)), blk(kBlock);
+  if (g.esize == 2) hipLaunchKernelGGL((k_ring_ag_pass<2>), grid, blk, 0, g.st, a);
+  else hipLaunchKernelGGL((k_ring_ag_pass<4>), grid, blk, 0, g.st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ag_fused(const Gat& g) { return launch_ring_ag_pass(g, 0, g.N - 1); }
+
+hipError_t launch_hd_ag_step(const Gat& g, int d, int first) {
+  const GatArgs a = gat_args(g, d, first);
+  const dim3 grid(gat_tiles(g)), blk(kBlock);
+  if (g.esize == 2) hipLaunchKernelGGL((k_hd_ag_step<2>), grid, blk, 0, g.st, a);
+  else hipLaunchKernelGGL((k_hd_ag_step<4>), grid, blk, 0, g.st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bcast(const char* src, Side dst, int N, int skip, uint64_t nbytes, int vec_ok,
+                        hipStream_t st) {
+  BcArgs a;
+  a.src = src; a.db = dst.base; a.ds = dst.stride; a.nbytes = nbytes;
+  a.N = N; a.skip = skip; a.vec_ok = vec_ok;
+  const uint64_t tile = (uint64_t)kBlock * kUnroll * 16;
+  const dim3 grid((unsigned)((nbytes + tile - 1) / tile)), blk(kBlock);
+  hipLaunchKernelGGL(k_bcast, grid, blk, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copies(const CopyDesc* d, int n, int esize, hipStream_t st) {
+  CopyArgs a;
+  a.n = 0; a.esize = esize; a.vecmask = 0; a.tpre[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    if (d[i].bytes == 0) continue;
+    const int j = a.n++;
+    a.src[j] = d[i].src; a.dst[j] = d[i].dst; a.bytes[j] = d[i].bytes;
+    a.tpre[j + 1] = a.tpre[j] + (d[i].bytes + kCopyTile - 1) / kCopyTile;
+    if ((((uintptr_t)d[i].src | (uintptr_t)d[i].dst | d[i].bytes) & 15u) == 0) a.vecmask |= 1ull << j;
+  }
+  if (a.n == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.tpre[a.n]), blk(kBlock);
+  hipLaunchKernelGGL(k_copies, grid, blk, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace cc

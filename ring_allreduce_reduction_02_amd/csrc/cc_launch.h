@@ -1,0 +1,88 @@
+// Internal interface between the C ABI (cc_api.cpp) and the kernels
+// (cc_kernels.hip).  Host-side only; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cc {
+
+enum Dt { DT_I32 = 0, DT_F32 = 1, DT_BF16 = 2 };
+enum Op { OP_SUM = 0, OP_MAX = 1, OP_PROD = 2 };
+enum Tree { TREE_HD = 0, TREE_BFLY = 1 };
+
+inline int elem_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
+// elements per 16-byte vector
+inline int vec_elems(int dt) { return 16 / elem_size(dt); }
+
+constexpr int kBlock = 256;   // threads per workgroup (4 wavefronts of 64)
+constexpr int kUnroll = 2;    // 16-byte vectors per thread per tile
+constexpr int kMaxDesc = 64;  // copy descriptors per launch
+
+// Rank-strided view: rank r at base + r * stride (bytes).
+struct Side {
+  char* base;
+  uint64_t stride;
+};
+
+// One reduction launch over the full per-rank vector of M elements, split in
+// N chunks [floor(c*M/N), floor((c+1)*M/N)).
+struct Red {
+  Side send;
+  Side recv;
+  Side ws;        // staging (accumulator type, 4 bytes per element), or {nullptr,0}
+  uint64_t M;
+  int N;
+  int dt;
+  int op;
+  int rs_mode;    // 0: AllReduce output on every rank; 1: ReduceScatter output (chunk c on rank c)
+  int vec_ok;     // all addresses of the 16-byte path are 16-byte aligned
+  hipStream_t st;
+};
+
+// Tiles of kBlock*kUnroll vectors.
+inline uint64_t num_tiles(uint64_t M, int dt) {
+  const uint64_t tile = (uint64_t)kBlock * kUnroll * vec_elems(dt);
+  return (M + tile - 1) / tile;
+}
+
+// ---- reductions
+hipError_t launch_ring_fused(const Red& r);
+hipError_t launch_tree_fused(const Red& r, int tree);
+// ring ReduceScatter steps [s0, s0+k); partial_in_recv: partials stay in the
+// receiving rank's recv buffer (AllReduce, int32/fp32), else in r.ws.
+hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv);
+// halving step with distance d; acc_in_recv as above (else r.ws is rank-strided).
+hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_in_recv);
+// butterfly step with distance d.
+hipError_t launch_bfly_step(const Red& r, int d, int first, int last, int acc_in_recv);
+
+// ---- gathers (no arithmetic).  ag_mode 0: AllGather phase of an AllReduce,
+// everything in recv; 1: standalone AllGather, rank c's shard in send.
+struct Gat {
+  Side send;
+  Side recv;
+  uint64_t M;     // full per-rank vector (recv) length
+  int N;
+  int esize;      // bytes per element
+  int ag_mode;
+  int vec_ok;
+  hipStream_t st;
+};
+hipError_t launch_ag_fused(const Gat& g);
+hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k);
+hipError_t launch_hd_ag_step(const Gat& g, int d, int first);
+
+// ---- broadcast: one source to N rank buffers (skip < 0: write all)
+hipError_t launch_bcast(const char* src, Side dst, int N, int skip, uint64_t nbytes, int vec_ok,
+                        hipStream_t st);
+
+// ---- descriptor copy: up to kMaxDesc (src, dst, bytes) copies in one launch
+struct CopyDesc {
+  const char* src;
+  char* dst;
+  uint64_t bytes;
+};
+hipError_t launch_copies(const CopyDesc* d, int n, int esize, hipStream_t st);
+
+}  // namespace cc

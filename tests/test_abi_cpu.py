@@ -1,0 +1,191 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/cc.h
+declares, validates arguments before touching a device, and its host-side
+accounting (chunk bounds, traffic, workspace sizes) matches the oracle.
+
+Calls with fake device addresses only run where no GPU is visible: every one
+of them must be rejected by validation before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import ccsim as cs
+from ring_allreduce_reduction_02_amd import ccgpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+no_gpu_only = pytest.mark.skipif(_has_gpu(), reason="fake device addresses are only used where no GPU is visible")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ccgpu.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "cc.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    names = set(re.findall(r"\b(cc_[a-z_]+)\s*\(", hdr))
+    assert {"cc_all_reduce", "cc_reduce_scatter", "cc_all_gather", "cc_broadcast", "cc_all_to_all"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(ccgpu.EXPORTS) == names
+
+
+def test_status_strings_and_version(lib):
+    for code, name in ((0, "CC_OK"), (1, "CC_ERR_INVALID_ARG"), (2, "CC_ERR_UNSUPPORTED"),
+                       (3, "CC_ERR_NO_DEVICE"), (4, "CC_ERR_HIP")):
+        assert lib.cc_status_string(code).decode() == name
+    assert b"cc" in lib.cc_version()
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 16, 64])
+def test_chunk_bounds_match_oracle(N):
+    for M in (0, 1, N - 1, N, N + 1, 8 * N + 3, 1_048_576, 67_108_864, 2 ** 40 + 7):
+        assert ccgpu.chunk_bounds(M, N) == cs.chunk_bounds(M, N)
+
+
+@pytest.mark.parametrize("N", [2, 3, 4, 5, 8, 16])
+def test_ring_traffic_matches_oracle_trace(N):
+    for M in (N, 3 * N + 1, 100, 7):
+        for dt, es in (("f32", 4), ("bf16", 2)):
+            tr = cs.Trace()
+            cs.ring_all_reduce([np.zeros(M, dtype=np.float32)] * N, "sum", "f32", tr)
+            b, s = ccgpu.get_traffic("all_reduce", N, M, dt, "ring")
+            assert (b, s) == (max(tr.sent) * es, tr.nsteps)
+
+
+@pytest.mark.parametrize("N", [2, 4, 8, 16])
+def test_hd_butterfly_traffic_matches_oracle_trace(N):
+    for M in (N, 5 * N + 3, 37):
+        tr = cs.Trace()
+        cs.hd_all_reduce([np.zeros(M, dtype=np.int32)] * N, "sum", "int32", tr)
+        assert ccgpu.get_traffic("all_reduce", N, M, "int32", "hd") == (max(tr.sent) * 4, tr.nsteps)
+        tr = cs.Trace()
+        cs.butterfly_all_reduce([np.zeros(M, dtype=np.int32)] * N, "sum", "int32", tr)
+        assert ccgpu.get_traffic("all_reduce", N, M, "int32", "butterfly") == (max(tr.sent) * 4, tr.nsteps)
+
+
+@pytest.mark.parametrize("N", [2, 3, 4, 8])
+def test_rs_ag_bcast_a2a_traffic_match_oracle(N):
+    S = 5
+    tr = cs.Trace(); cs.ring_reduce_scatter([np.zeros(N * S, dtype=np.int32)] * N, "sum", "int32", tr)
+    assert ccgpu.get_traffic("reduce_scatter", N, S, "int32", "ring") == (max(tr.sent) * 4, tr.nsteps)
+    tr = cs.Trace(); cs.ring_all_gather([np.zeros(S, dtype=np.int32)] * N, "int32", tr)
+    assert ccgpu.get_traffic("all_gather", N, S, "int32", "ring") == (max(tr.sent) * 4, tr.nsteps)
+    if N & (N - 1) == 0:
+        tr = cs.Trace(); cs.hd_reduce_scatter([np.zeros(N * S, dtype=np.int32)] * N, "sum", "int32", tr)
+        assert ccgpu.get_traffic("reduce_scatter", N, S, "int32", "hd") == (max(tr.sent) * 4, tr.nsteps)
+        tr = cs.Trace(); cs.hd_all_gather([np.zeros(S, dtype=np.int32)] * N, "int32", tr)
+        assert ccgpu.get_traffic("all_gather", N, S, "int32", "hd") == (max(tr.sent) * 4, tr.nsteps)
+    for sch, algo in (("ring", "ring"), ("binomial", "hd")):
+        tr = cs.Trace(); cs.broadcast([np.zeros(S, dtype=np.int32)] * N, 0, sch, tr)
+        assert ccgpu.get_traffic("broadcast", N, S, "int32", algo) == (max(tr.sent) * 4, tr.nsteps)
+    C = np.full((N, N), 3)
+    tr = cs.Trace()
+    cs.all_to_all([np.zeros(3 * N, dtype=np.int32)] * N, C, 1, pairwise=True, trace=tr)
+    b, s = ccgpu.get_traffic("all_to_all", N, 3, "int32", "ring")
+    assert b == max(tr.sent) * 4 and s == N - 1     # the local block (step 0) costs no link
+
+
+def test_workspace_sizes():
+    assert ccgpu.workspace_size("all_reduce", 8, 1000, "f32", "ring", 0) == 0
+    assert ccgpu.workspace_size("all_reduce", 8, 1000, "f32", "ring", 1) == 0       # partials in recv
+    assert ccgpu.workspace_size("all_reduce", 8, 1000, "bf16", "ring", 1) == 4000   # fp32 partial per element
+    assert ccgpu.workspace_size("all_reduce", 8, 1000, "bf16", "ring", 7) == 0      # one pass: no partials
+    assert ccgpu.workspace_size("all_reduce", 8, 1000, "bf16", "hd", 1) == 8 * 4096
+    assert ccgpu.workspace_size("reduce_scatter", 4, 10, "f32", "ring", 1) == 160
+    assert ccgpu.workspace_size("reduce_scatter", 4, 10, "f32", "hd", 1) == 4 * 256
+    assert ccgpu.workspace_size("reduce_scatter", 2, 10, "f32", "hd", 1) == 0
+    assert ccgpu.workspace_size("all_gather", 8, 10, "f32", "hd", 1) == 0
+
+
+# ---------------------------------------------------------------- validation
+
+FAKE = 0x7F0000000000    # never dereferenced: every call below fails validation first
+
+
+def _rb(base, stride):
+    return ccgpu.RankBuf(base, stride)
+
+
+def _ar(send, recv, count, N, dtype=1, op=0, cfg=None):
+    c = cfg if cfg is not None else ccgpu.Config(0, 0, None, 0)
+    return ccgpu.raw("cc_all_reduce", send, recv, count, dtype, op, N, ctypes.byref(c), None)
+
+
+@no_gpu_only
+def test_all_reduce_rejects_bad_arguments():
+    ok_s, ok_r = _rb(FAKE, 4096), _rb(FAKE + (1 << 30), 4096)
+    assert _ar(ok_s, ok_r, 100, 0) == ccgpu.CC_ERR_INVALID_ARG           # nranks < 1
+    assert _ar(ok_s, ok_r, 100, 65) == ccgpu.CC_ERR_INVALID_ARG          # nranks > 64
+    assert _ar(ok_s, ok_r, 100, 4, dtype=7) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 4, op=9) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(_rb(None, 4096), ok_r, 100, 4) == ccgpu.CC_ERR_INVALID_ARG  # NULL base
+    assert _ar(_rb(FAKE, 200), ok_r, 100, 4) == ccgpu.CC_ERR_INVALID_ARG   # ranks overlap (400 B > stride)
+    assert _ar(ok_s, _rb(FAKE + 100, 4096), 100, 4) == ccgpu.CC_ERR_INVALID_ARG   # send/recv overlap
+    assert _ar(ok_s, ok_r, 100, 3, cfg=ccgpu.Config(1, 0, None, 0)) == ccgpu.CC_ERR_UNSUPPORTED
+    assert _ar(ok_s, ok_r, 100, 6, cfg=ccgpu.Config(2, 0, None, 0)) == ccgpu.CC_ERR_UNSUPPORTED
+    assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(0, -1, None, 0)) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(5, 0, None, 0)) == ccgpu.CC_ERR_INVALID_ARG
+    # bf16 stepwise ring needs a workspace
+    assert _ar(ok_s, ok_r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, None, 0)) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, FAKE + (2 << 30), 399)) == ccgpu.CC_ERR_INVALID_ARG
+    assert "workspace" in ccgpu.load().cc_last_error().decode()
+    # interleaved send/recv rows in one allocation do not overlap: only the device is missing
+    inter_s, inter_r = _rb(FAKE, 800), _rb(FAKE + 400, 800)
+    assert _ar(inter_s, inter_r, 100, 4) == ccgpu.CC_ERR_NO_DEVICE
+    # zero count is a no-op
+    assert _ar(_rb(None, 0), _rb(None, 0), 0, 4) == ccgpu.CC_OK
+
+
+@no_gpu_only
+def test_valid_calls_report_no_device():
+    s, r = _rb(FAKE, 4096), _rb(FAKE + (1 << 30), 4096)
+    assert _ar(s, r, 100, 4) == ccgpu.CC_ERR_NO_DEVICE
+    assert _ar(s, s, 100, 4) == ccgpu.CC_ERR_NO_DEVICE     # in place
+    assert "device" in ccgpu.load().cc_last_error().decode()
+
+
+@no_gpu_only
+def test_other_collectives_reject_bad_arguments():
+    L = ccgpu.load()
+    cfg = ccgpu.Config(0, 0, None, 0)
+    s, r = _rb(FAKE, 1 << 20), _rb(FAKE + (1 << 30), 1 << 20)
+    # reduce_scatter: butterfly undefined; HD needs 2^k; recv overlapping send
+    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 4, ctypes.byref(ccgpu.Config(2, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 3, ctypes.byref(ccgpu.Config(1, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    assert L.cc_reduce_scatter(s, _rb(FAKE + 8, 1 << 20), 10, 1, 0, 4, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
+    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 4, ctypes.byref(ccgpu.Config(0, 1, None, 0)), None) == ccgpu.CC_ERR_INVALID_ARG  # ws
+    # all_gather: recv stride too small for N*S elements
+    assert L.cc_all_gather(s, _rb(FAKE + (1 << 30), 100), 10, 1, 4, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
+    assert L.cc_all_gather(s, r, 10, 1, 4, ctypes.byref(ccgpu.Config(2, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    # broadcast: root out of range, butterfly
+    assert L.cc_broadcast(s, r, 10, 1, 4, 4, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
+    assert L.cc_broadcast(s, r, 10, 1, -1, 4, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
+    assert L.cc_broadcast(s, r, 10, 1, 0, 4, ctypes.byref(ccgpu.Config(2, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    # all_to_all: NULL counts, zero row, recv block does not fit the stride, HD
+    counts = (ctypes.c_size_t * 4)(1, 2, 3, 4)
+    assert L.cc_all_to_all(s, r, None, 1, 1, 2, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
+    assert L.cc_all_to_all(s, r, counts, 0, 1, 2, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
+    big = (ctypes.c_size_t * 4)(1, 1 << 20, 1, 1)
+    assert L.cc_all_to_all(s, r, big, 1, 1, 2, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
+    assert L.cc_all_to_all(s, r, counts, 1, 1, 2, ctypes.byref(ccgpu.Config(1, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    assert L.cc_all_to_all(s, r, counts, 1, 1, 2, ctypes.byref(cfg), None) == ccgpu.CC_ERR_NO_DEVICE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        ccgpu.rankbuf(torch.zeros(2, 3))
