@@ -1,0 +1,290 @@
+#!/usr/bin/env python
+"""Benchmark of the ring AllReduce on one MI355X.
+
+Workload: ring AllReduce SUM of synthetic gradients, N = 8 logical ranks,
+M = 67,108,864 fp32 elements per rank (256 MiB each), Gaussian values with
+sigma = 1e-3, the rank buffers 64 KiB + 256 B apart.  One step is one
+cc_all_reduce call (the fused ring kernel) over inputs already resident in
+HBM.  The step's algorithmic traffic is 2*N*M*4 bytes (read every rank's
+input once, write every rank's output once).
+
+Prints one JSON line: achieved GB/s (value) and its fraction of the 8 TB/s
+HBM peak, the simulated ring busbw, the roofline object of the fused kernel
+(with HBM bytes from committed rocprofv3 counters when they match the
+current kernel source), the oracle's time on the host cores for a bounded
+sample, a bf16 twin and an alpha-beta calibration of the stepwise ring.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "achieved HBM GB/s (% of peak) + simulated busbw for N-rank ring AllReduce"
+KERNEL_SRC = os.path.join(ROOT, "ring_allreduce_reduction_02_amd", "csrc", "cc_kernels.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "ring_fused_f32_n8_m67108864_pmc.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def rank_tensor(N, M, dtype, pad_bytes, device):
+    import torch
+    es = torch.tensor([], dtype=dtype).element_size()
+    S = M + pad_bytes // es
+    return torch.empty(N * S, dtype=dtype, device=device).view(N, S)[:, :M]
+
+
+def upload(xs, t):
+    import numpy as np
+    import torch
+    for r, x in enumerate(xs):
+        h = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if x.dtype == np.uint16 else torch.from_numpy(x)
+        t[r].copy_(h, non_blocking=False)
+
+
+def time_launches(fn, steps, warmup):
+    """Warm up, then time `steps` launches with a HIP event pair around each
+    launch (on the launching stream) and a pair around the whole region."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [a.elapsed_time(b) for a, b in evs]
+    return {"total_ms": t0.elapsed_time(t1), "per_launch_ms": per, "wall_s": wall}
+
+
+def traffic_from_profile(nbytes_alg):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs,
+    scaled by the copy-kernel calibration; None if the kernel changed."""
+    if not os.path.exists(PMC_FILE):
+        return None, "no counter file"
+    with open(PMC_FILE) as f:
+        p = json.load(f)
+    if p.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    fetch = p["fetch_kib_per_dispatch"] * 1024.0 * p["fetch_scale"]
+    write = p["write_kib_per_dispatch"] * 1024.0 * p["write_scale"]
+    return fetch + write, "rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE (scaled by a plain copy)"
+
+
+def cpu_baseline(N, M_sample):
+    """The oracle as it stands, on the host cores, on a bounded sample."""
+    import numpy as np
+
+    from oracle import ccsim
+    from ring_allreduce_reduction_02_amd import synth
+    xs = synth.gradient_inputs(N, M_sample, "f32")
+    times = []
+    for _ in range(3):
+        t = time.perf_counter()
+        ccsim.ring_all_reduce(xs, "sum", "f32")
+        times.append(time.perf_counter() - t)
+    t = sorted(times)[1]
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": 2 * N * M_sample * 4 / t / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"ring AllReduce SUM, N={N}, M={M_sample} fp32 per rank (1/{67108864 // M_sample} of the workload), "
+                  f"step-explicit NumPy simulator, median of 3 runs = {t:.3f} s",
+        "host_logical_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+        "cpu_model": cpu_model or platform.processor(),
+    }
+
+
+def alpha_beta(send, recv, N, steps=10, warmup=3):
+    """Stepwise ring (one kernel per ring step) over per-rank sizes from
+    4 KiB to 256 MiB; fit T = alpha * 2(N-1) + beta * bytes sent per rank."""
+    from ring_allreduce_reduction_02_amd import calib, ccgpu
+    M_full = send.shape[1]
+    sizes = [1 << k for k in range(10, 27, 2)]   # elements: 1 Ki .. 64 Mi fp32 (4 KiB .. 256 MiB)
+    sizes = [m for m in sizes if m <= M_full]
+    st, by, ts, pts, fused_b, fused_t = [], [], [], [], [], []
+    for m in sizes:
+        s, r = send[:, :m], recv[:, :m]
+        res = time_launches(lambda: ccgpu.all_reduce(s, r, algo="ring", fuse_depth=1), steps, warmup)
+        t = sorted(res["per_launch_ms"])[len(res["per_launch_ms"]) // 2] / 1e3
+        b, n = ccgpu.get_traffic("all_reduce", N, m, "f32", "ring")
+        st.append(n); by.append(b); ts.append(t)
+        pts.append({"bytes_per_rank": m * 4, "stepwise_us": t * 1e6})
+        resf = time_launches(lambda: ccgpu.all_reduce(s, r, algo="ring", fuse_depth=0), steps, warmup)
+        tf = sorted(resf["per_launch_ms"])[len(resf["per_launch_ms"]) // 2] / 1e3
+        fused_b.append(2 * N * m * 4); fused_t.append(tf)
+        pts[-1]["fused_us"] = tf * 1e6
+    fit = calib.fit_alpha_beta(st, by, ts)
+    fit["fused_fit"] = calib.fit_fixed_plus_bandwidth(fused_b, fused_t)
+    fit["nranks"] = N
+    fit["schedule"] = "ring, one kernel per step (fuse_depth=1), fp32 SUM"
+    fit["points"] = pts
+    return fit
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ranks", type=int, default=8)
+    ap.add_argument("--count", type=int, default=67_108_864)
+    ap.add_argument("--dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--algo", default="ring", choices=["ring", "hd", "butterfly"])
+    ap.add_argument("--fuse-depth", type=int, default=0)
+    ap.add_argument("--pad-bytes", type=int, default=65_792)
+    ap.add_argument("--cpu-sample", type=int, default=16_777_216)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the bf16 twin and the alpha-beta calibration")
+    ap.add_argument("--copy-probe-bytes", type=int, default=0,
+                    help="before timing, run a plain device copy of this many bytes 3 times "
+                         "(a known-size kernel for scaling HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the N logical ranks live in one GPU's HBM; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ccgpu.load()
+    dev = "cuda:0"
+    N, M = args.ranks, args.count
+    tdt = torch.float32 if args.dtype == "f32" else torch.bfloat16
+    es = 4 if args.dtype == "f32" else 2
+    log(f"generating {N} x {M} {args.dtype} synthetic gradients")
+    xs = synth.gradient_inputs(N, M, args.dtype)
+    send = rank_tensor(N, M, tdt, args.pad_bytes, dev)
+    recv = rank_tensor(N, M, tdt, args.pad_bytes, dev)
+    upload(xs, send)
+    del xs
+    ws = ccgpu.make_workspace("all_reduce", N, M, args.dtype, args.algo, args.fuse_depth, dev)
+    if args.copy_probe_bytes:
+        a = torch.empty(args.copy_probe_bytes, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step():
+        ccgpu.all_reduce(send, recv, op="sum", algo=args.algo, fuse_depth=args.fuse_depth, workspace=ws)
+
+    log("timing")
+    res = time_launches(step, args.steps, args.warmup)
+    ms_per_step = res["total_ms"] / args.steps
+    alg_bytes = 2 * N * M * es
+    value = alg_bytes / (ms_per_step / 1e3) / 1e9
+    per = res["per_launch_ms"]
+    avg_launch_ms = sum(per) / len(per)
+    achieved = alg_bytes / (avg_launch_ms / 1e3) / 1e9
+    busbw = (M * es) / (ms_per_step / 1e3) * 2 * (N - 1) / N / 1e9
+    traffic, traffic_src = traffic_from_profile(alg_bytes)
+    kname = {"ring": "k_ring_fused", "hd": "k_tree_fused", "butterfly": "k_tree_fused"}[args.algo]
+    if args.fuse_depth:
+        kname = "stepwise schedule (several kernels per step)"
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"ring_allreduce_sum_n{N}_m{M}_{args.dtype}",
+            "nranks": N,
+            "count_per_rank": M,
+            "algo": args.algo,
+            "fuse_depth": args.fuse_depth,
+            "rank_stride_bytes": send.stride(0) * es,
+            "values": "Gaussian, sigma=1e-3" + (" (bf16 rounding of the fp32 samples)" if args.dtype == "bf16" else ""),
+            "parallelism": f"{N} logical ranks in one GPU's HBM",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
+        "busbw_GBps": round(busbw, 2),
+        "algorithmic_bytes_per_step": alg_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kname,
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "traffic_source": traffic_src,
+            "avg_launch_ms": round(avg_launch_ms, 5),
+            "min_launch_ms": round(min(per), 5),
+        },
+    }
+    if not args.no_extras and args.dtype == "f32" and args.algo == "ring" and args.fuse_depth == 0:
+        log("bf16 twin")
+        xb = synth.gradient_inputs(N, M, "bf16")
+        sb = rank_tensor(N, M, torch.bfloat16, args.pad_bytes, dev)
+        rb = rank_tensor(N, M, torch.bfloat16, args.pad_bytes, dev)
+        upload(xb, sb)
+        del xb
+        rb16 = time_launches(lambda: ccgpu.all_reduce(sb, rb, algo="ring", fuse_depth=0), args.steps, args.warmup)
+        ms16 = rb16["total_ms"] / args.steps
+        out["bf16_twin"] = {"ms_per_step": round(ms16, 5),
+                            "GBps": round(2 * N * M * 2 / (ms16 / 1e3) / 1e9, 2),
+                            "pct_of_peak": round(100 * 2 * N * M * 2 / (ms16 / 1e3) / 1e9 / PEAK_HBM_GBPS, 2)}
+        del sb, rb
+        torch.cuda.empty_cache()
+        log("alpha-beta calibration")
+        out["alpha_beta"] = alpha_beta(send, recv, N)
+    if not args.no_cpu_baseline:
+        log("oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(N, min(args.cpu_sample, M))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

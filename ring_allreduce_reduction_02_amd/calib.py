@@ -1,0 +1,50 @@
+"""alpha-beta calibration of a schedule on this GPU.
+
+The pages model a step as a fixed cost plus a per-byte cost and ask that the
+model be fitted on the same collective, dtype, rank count and algorithm that
+is being predicted (textbook ch. 6 "集合通信", section "绘制地形图：网络性能建模";
+lesson 3, "理论通信量与网络延迟模型", where beta is seconds per byte).  Here a
+"step" is one ring step of the stepwise schedule and a "byte" is one byte a
+rank sends on the simulated ring, so
+
+    T = alpha * steps + beta * bytes_sent_per_rank
+
+is fitted by non-negative least squares.  n* = alpha / beta is the message
+size (bytes per rank and step) at which the two terms are equal.
+"""
+from __future__ import annotations
+
+from typing import Dict, Sequence
+
+import numpy as np
+
+
+def fit_alpha_beta(steps: Sequence[float], bytes_sent: Sequence[float], seconds: Sequence[float]) -> Dict[str, float]:
+    from scipy.optimize import nnls
+
+    A = np.stack([np.asarray(steps, dtype=np.float64), np.asarray(bytes_sent, dtype=np.float64)], axis=1)
+    t = np.asarray(seconds, dtype=np.float64)
+    # weight each point by 1/t so small and large messages count alike
+    w = 1.0 / t
+    sol, _ = nnls(A * w[:, None], t * w)
+    alpha, beta = float(sol[0]), float(sol[1])
+    pred = A @ sol
+    return {
+        "alpha_us_per_step": alpha * 1e6,
+        "beta_ps_per_byte": beta * 1e12,
+        "link_GBps": (1.0 / beta / 1e9) if beta > 0 else float("inf"),
+        "n_star_bytes": alpha / beta if beta > 0 else float("inf"),
+        "max_rel_residual": float(np.max(np.abs(pred - t) / t)),
+    }
+
+
+def fit_fixed_plus_bandwidth(bytes_moved: Sequence[float], seconds: Sequence[float]) -> Dict[str, float]:
+    """T = t0 + bytes / BW for a fused launch (least squares, 1/t weights)."""
+    from scipy.optimize import nnls
+
+    b = np.asarray(bytes_moved, dtype=np.float64)
+    t = np.asarray(seconds, dtype=np.float64)
+    A = np.stack([np.ones_like(b), b], axis=1)
+    w = 1.0 / t
+    sol, _ = nnls(A * w[:, None], t * w)
+    return {"t0_us": float(sol[0]) * 1e6, "bw_GBps": (1.0 / sol[1] / 1e9) if sol[1] > 0 else float("inf")}

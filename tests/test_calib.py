@@ -1,0 +1,33 @@
+"""The alpha-beta fit recovers a known alpha and beta from synthetic timings."""
+import numpy as np
+import pytest
+
+from ring_allreduce_reduction_02_amd import calib
+
+
+def test_alpha_beta_recovery():
+    alpha, beta = 3.5e-6, 1 / 600e9
+    N = 8
+    steps = [2 * (N - 1)] * 9
+    sizes = [4096 * 4 ** k for k in range(9)]
+    sent = [2 * (N - 1) * s // N for s in sizes]
+    t = [alpha * n + beta * b for n, b in zip(steps, sent)]
+    fit = calib.fit_alpha_beta(steps, sent, t)
+    assert fit["alpha_us_per_step"] == pytest.approx(alpha * 1e6, rel=1e-6)
+    assert fit["link_GBps"] == pytest.approx(600, rel=1e-6)
+    assert fit["n_star_bytes"] == pytest.approx(alpha / beta, rel=1e-6)
+
+
+def test_fused_fit_recovery():
+    b = np.array([2 ** k for k in range(12, 32, 2)], dtype=float)
+    t = 4e-6 + b / 6.2e12
+    fit = calib.fit_fixed_plus_bandwidth(b, t)
+    assert fit["t0_us"] == pytest.approx(4.0, rel=1e-6)
+    assert fit["bw_GBps"] == pytest.approx(6200, rel=1e-6)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess, sys, os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
