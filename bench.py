@@ -95,19 +95,20 @@ def traffic_from_profile(nbytes_alg):
     return fetch + write, "rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE (scaled by a plain copy)"
 
 
-def cpu_baseline(N, M_sample):
-    """The oracle as it stands, on the host cores, on a bounded sample."""
-    import numpy as np
-
+def cpu_baseline(N, M_sample, min_seconds=10.0, max_runs=25):
+    """The oracle as it stands, on the host cores: the step-explicit ring
+    simulator on the same workload, repeated until at least `min_seconds` of
+    CPU work (median run reported)."""
     from oracle import ccsim
     from ring_allreduce_reduction_02_amd import synth
     xs = synth.gradient_inputs(N, M_sample, "f32")
     times = []
-    for _ in range(3):
+    t_all = time.perf_counter()
+    while len(times) < max_runs and (time.perf_counter() - t_all < min_seconds or len(times) < 3):
         t = time.perf_counter()
         ccsim.ring_all_reduce(xs, "sum", "f32")
         times.append(time.perf_counter() - t)
-    t = sorted(times)[1]
+    t = sorted(times)[len(times) // 2]
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -122,8 +123,8 @@ def cpu_baseline(N, M_sample):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"ring AllReduce SUM, N={N}, M={M_sample} fp32 per rank (1/{67108864 // M_sample} of the workload), "
-                  f"step-explicit NumPy simulator, median of 3 runs = {t:.3f} s",
+        "sample": f"ring AllReduce SUM, N={N}, M={M_sample} fp32 per rank, step-explicit NumPy simulator "
+                  f"(single-threaded elementwise ops), {len(times)} runs in {sum(times):.1f} s, median {t:.3f} s",
         "host_logical_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
         "cpu_model": cpu_model or platform.processor(),
@@ -168,7 +169,8 @@ def main():
     ap.add_argument("--algo", default="ring", choices=["ring", "hd", "butterfly"])
     ap.add_argument("--fuse-depth", type=int, default=0)
     ap.add_argument("--pad-bytes", type=int, default=65_792)
-    ap.add_argument("--cpu-sample", type=int, default=16_777_216)
+    ap.add_argument("--blocks-per-cu", type=int, default=0, help="occupancy cap passed to the library (0 = its default)")
+    ap.add_argument("--cpu-sample", type=int, default=67_108_864)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the bf16 twin and the alpha-beta calibration")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
@@ -210,7 +212,8 @@ def main():
         del a, b
 
     def step():
-        ccgpu.all_reduce(send, recv, op="sum", algo=args.algo, fuse_depth=args.fuse_depth, workspace=ws)
+        ccgpu.all_reduce(send, recv, op="sum", algo=args.algo, fuse_depth=args.fuse_depth, workspace=ws,
+                         blocks_per_cu=args.blocks_per_cu)
 
     log("timing")
     res = time_launches(step, args.steps, args.warmup)
@@ -244,6 +247,7 @@ def main():
             "count_per_rank": M,
             "algo": args.algo,
             "fuse_depth": args.fuse_depth,
+            "blocks_per_cu": args.blocks_per_cu,
             "rank_stride_bytes": send.stride(0) * es,
             "values": "Gaussian, sigma=1e-3" + (" (bf16 rounding of the fp32 samples)" if args.dtype == "bf16" else ""),
             "parallelism": f"{N} logical ranks in one GPU's HBM",

@@ -34,7 +34,8 @@
  *    (nranks outside [1, CC_MAX_RANKS], NULL base with a non-zero count,
  *    rank buffers that overlap each other, send and recv buffers that overlap
  *    where the call needs them disjoint, root outside [0, N), a workspace
- *    smaller than cc_workspace_size reports, negative fuse_depth),
+ *    smaller than cc_workspace_size reports, negative fuse_depth or
+ *    blocks_per_cu),
  *    CC_ERR_UNSUPPORTED for a schedule the collective does not have,
  *    CC_ERR_NO_DEVICE when no GPU is visible, CC_ERR_HIP for a launch error.
  *    cc_last_error() returns a message for the last failing call on the
@@ -89,12 +90,17 @@ typedef enum {
  *  fuse_depth = k: ring only -- k consecutive ring steps per kernel.
  *  workspace / workspace_bytes: caller-owned device memory, at least what
  *  cc_workspace_size returns for the same arguments (may be NULL/0 when that
- *  is 0).  A NULL cfg means {CC_ALGO_RING, 0, NULL, 0}. */
+ *  is 0).
+ *  blocks_per_cu: cap on resident workgroups per compute unit (occupancy) for
+ *  the call's kernels; 0 lets the library choose (it keeps a few tens of KiB
+ *  of loads in flight per CU, which streams HBM best).  Negative is invalid.
+ *  A NULL cfg means {CC_ALGO_RING, 0, NULL, 0, 0}. */
 typedef struct {
   cc_algo_t algo;
   int fuse_depth;
   void* workspace;
   size_t workspace_bytes;
+  int blocks_per_cu;
 } cc_config_t;
 
 /* N rank buffers: rank r at (char*)base + r * rank_stride_bytes (device memory). */

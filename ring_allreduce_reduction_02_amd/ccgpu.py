@@ -35,7 +35,8 @@ class RankBuf(ctypes.Structure):
 
 class Config(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int), ("fuse_depth", ctypes.c_int),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("blocks_per_cu", ctypes.c_int)]
 
 
 class CCError(RuntimeError):
@@ -110,10 +111,10 @@ def rankbuf(t) -> RankBuf:
     return RankBuf(t.data_ptr(), t.stride(0) * t.element_size())
 
 
-def config(algo: str = "ring", fuse_depth: int = 0, workspace=None) -> Config:
+def config(algo: str = "ring", fuse_depth: int = 0, workspace=None, blocks_per_cu: int = 0) -> Config:
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    return Config(ALGOS[algo], int(fuse_depth), ws_ptr, ws_bytes)
+    return Config(ALGOS[algo], int(fuse_depth), ws_ptr, ws_bytes, int(blocks_per_cu))
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -125,7 +126,7 @@ def _stream(stream) -> ctypes.c_void_p:
 def workspace_size(coll: str, nranks: int, count: int, dtype: str, algo: str = "ring",
                    fuse_depth: int = 0) -> int:
     out = ctypes.c_size_t(0)
-    cfg = Config(ALGOS[algo], int(fuse_depth), None, 0)
+    cfg = Config(ALGOS[algo], int(fuse_depth), None, 0, 0)
     _check(load().cc_workspace_size(COLLS[coll], ctypes.byref(cfg), nranks, count, DTYPES[dtype],
                                     ctypes.byref(out)))
     return out.value
@@ -155,58 +156,59 @@ def chunk_bounds(count: int, nranks: int):
 
 
 def all_reduce(send, recv=None, op: str = "sum", algo: str = "ring", fuse_depth: int = 0,
-               workspace=None, stream=None) -> None:
+               workspace=None, stream=None, blocks_per_cu: int = 0) -> None:
     """recv[r] = (+)_j send[j] for every rank r; send/recv are [N, M]."""
     recv = send if recv is None else recv
     N, M = send.shape
     if tuple(recv.shape) != (N, M) or recv.dtype != send.dtype:
         raise ValueError("recv must match send")
-    cfg = config(algo, fuse_depth, workspace)
+    cfg = config(algo, fuse_depth, workspace, blocks_per_cu)
     _check(load().cc_all_reduce(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], OPS[op], N,
                                 ctypes.byref(cfg), _stream(stream)))
 
 
 def reduce_scatter(send, recv, op: str = "sum", algo: str = "ring", fuse_depth: int = 0,
-                   workspace=None, stream=None) -> None:
+                   workspace=None, stream=None, blocks_per_cu: int = 0) -> None:
     """send [N, N*S] -> recv [N, S]: rank r gets the reduced chunk r."""
     N, S = recv.shape
     if tuple(send.shape) != (N, N * S) or recv.dtype != send.dtype:
         raise ValueError("send must be [N, N*S] for recv [N, S]")
-    cfg = config(algo, fuse_depth, workspace)
+    cfg = config(algo, fuse_depth, workspace, blocks_per_cu)
     _check(load().cc_reduce_scatter(rankbuf(send), rankbuf(recv), S, DTYPES[dtype_name(send)], OPS[op], N,
                                     ctypes.byref(cfg), _stream(stream)))
 
 
-def all_gather(send, recv, algo: str = "ring", fuse_depth: int = 0, stream=None) -> None:
+def all_gather(send, recv, algo: str = "ring", fuse_depth: int = 0, stream=None, blocks_per_cu: int = 0) -> None:
     """send [N, S] -> recv [N, N*S]: slot r of every rank holds rank r's send."""
     N, S = send.shape
     if tuple(recv.shape) != (N, N * S) or recv.dtype != send.dtype:
         raise ValueError("recv must be [N, N*S] for send [N, S]")
-    cfg = config(algo, fuse_depth)
+    cfg = config(algo, fuse_depth, None, blocks_per_cu)
     _check(load().cc_all_gather(rankbuf(send), rankbuf(recv), S, DTYPES[dtype_name(send)], N,
                                 ctypes.byref(cfg), _stream(stream)))
 
 
-def broadcast(send, recv=None, root: int = 0, algo: str = "ring", fuse_depth: int = 0, stream=None) -> None:
+def broadcast(send, recv=None, root: int = 0, algo: str = "ring", fuse_depth: int = 0, stream=None,
+              blocks_per_cu: int = 0) -> None:
     """recv[r] = send[root] for every r; send/recv are [N, M]."""
     recv = send if recv is None else recv
     N, M = recv.shape
     if tuple(send.shape) != (N, M) or recv.dtype != send.dtype:
         raise ValueError("recv must match send")
-    cfg = config(algo, fuse_depth)
+    cfg = config(algo, fuse_depth, None, blocks_per_cu)
     _check(load().cc_broadcast(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], root, N,
                                ctypes.byref(cfg), _stream(stream)))
 
 
 def all_to_all(send, recv, counts: Sequence[Sequence[int]], elem_per_row: int = 1, fuse_depth: int = 0,
-               stream=None) -> None:
+               stream=None, blocks_per_cu: int = 0) -> None:
     """Blocked transpose with per-(source, destination) row counts."""
     N = send.shape[0]
     flat = [int(v) for row in counts for v in row]
     if len(flat) != N * N or recv.shape[0] != N:
         raise ValueError("counts must be N x N")
     arr = (ctypes.c_size_t * (N * N))(*flat)
-    cfg = config("ring", fuse_depth)
+    cfg = config("ring", fuse_depth, None, blocks_per_cu)
     _check(load().cc_all_to_all(rankbuf(send), rankbuf(recv), arr, elem_per_row, DTYPES[dtype_name(send)], N,
                                 ctypes.byref(cfg), _stream(stream)))
 

@@ -63,7 +63,7 @@ bool al16(uint64_t v) { return (v & 15u) == 0; }
 bool al16p(const void* p) { return al16((uint64_t)(uintptr_t)p); }
 uint64_t rup(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-const cc_config_t kDefaultCfg = {CC_ALGO_RING, 0, nullptr, 0};
+const cc_config_t kDefaultCfg = {CC_ALGO_RING, 0, nullptr, 0, 0};
 
 cc_status_t common_checks(int nranks, cc_dtype_t dtype, const cc_config_t* cfg) {
   if (nranks < 1 || nranks > CC_MAX_RANKS)
@@ -71,6 +71,7 @@ cc_status_t common_checks(int nranks, cc_dtype_t dtype, const cc_config_t* cfg) 
   if ((int)dtype < 0 || (int)dtype > 2) return fail(CC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if ((int)cfg->algo < 0 || (int)cfg->algo > 2) return fail(CC_ERR_INVALID_ARG, "unknown algo %d", (int)cfg->algo);
   if (cfg->fuse_depth < 0) return fail(CC_ERR_INVALID_ARG, "fuse_depth=%d is negative", cfg->fuse_depth);
+  if (cfg->blocks_per_cu < 0) return fail(CC_ERR_INVALID_ARG, "blocks_per_cu=%d is negative", cfg->blocks_per_cu);
   return CC_OK;
 }
 
@@ -111,6 +112,14 @@ cc_status_t grid_fits(uint64_t M, int dt) {
 
 Side side(const cc_rankbuf_t& s) { return Side{(char*)s.base, (uint64_t)s.rank_stride_bytes}; }
 
+// floor(c*M/N), c = 0..N: the chunk boundaries every schedule uses
+struct Bounds {
+  uint64_t b[kMaxRanks + 1];
+  Bounds(uint64_t M, int N) {
+    for (int c = 0; c <= N; ++c) b[c] = (uint64_t)(((unsigned __int128)c * M) / (unsigned)N);
+  }
+};
+
 // ---- workspace sizing (bytes); M is the full per-rank vector length
 uint64_t ws_need(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt) {
   if (N <= 1 || cfg.fuse_depth == 0) return 0;
@@ -144,14 +153,14 @@ Side ws_side(const cc_config_t& cfg, uint64_t M) {
 }
 
 cc_status_t copy_ranks(const cc_rankbuf_t& src, const cc_rankbuf_t& dst, uint64_t nbytes, int N, int esize,
-                       hipStream_t st) {
+                       int blocks_per_cu, hipStream_t st) {
   std::vector<CopyDesc> d;
   for (int r = 0; r < N; ++r)
     d.push_back(CopyDesc{(const char*)src.base + (uint64_t)r * src.rank_stride_bytes,
                          (char*)dst.base + (uint64_t)r * dst.rank_stride_bytes, nbytes});
   for (size_t i = 0; i < d.size(); i += kMaxDesc) {
     const int n = (int)std::min<size_t>(kMaxDesc, d.size() - i);
-    hipError_t e = launch_copies(d.data() + i, n, esize, st);
+    hipError_t e = launch_copies(d.data() + i, n, esize, blocks_per_cu, st);
     if (e != hipSuccess) return hip_status(e, "copy launch");
   }
   return ok();
@@ -203,13 +212,16 @@ cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc
   if ((s = check_ws(CC_COLL_ALL_REDUCE, cfg, N, M, dt))) return s;
   if ((s = device_ready())) return s;
   hipStream_t st = (hipStream_t)stream;
-  if (N == 1) return in_place ? ok() : copy_ranks(send, recv, nb, 1, es, st);
+  if (N == 1) return in_place ? ok() : copy_ranks(send, recv, nb, 1, es, cfg.blocks_per_cu, st);
 
+  const Bounds bd(M, N);
   Red r;
   r.send = side(send);
   r.recv = side(recv);
   r.ws = ws_side(cfg, M);
   r.M = M;
+  r.bnd = bd.b;
+  r.blocks_per_cu = cfg.blocks_per_cu;
   r.N = N;
   r.dt = dt;
   r.op = (int)op;
@@ -224,7 +236,7 @@ cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc
     const int k = std::min(cfg.fuse_depth, N - 1);
     const int pin = dt != DT_BF16;
     for (int s0 = 0; s0 < N - 1 && e == hipSuccess; s0 += k) e = launch_ring_rs_pass(r, s0, std::min(k, N - 1 - s0), pin);
-    Gat g{r.send, r.recv, M, N, es, 0, r.vec_ok, st};
+    Gat g{r.send, r.recv, M, bd.b, cfg.blocks_per_cu, N, es, 0, r.vec_ok, st};
     for (int s0 = 0; s0 < N - 1 && e == hipSuccess; s0 += k) e = launch_ring_ag_pass(g, s0, std::min(k, N - 1 - s0));
     return hip_status(e, "ring all_reduce (stepwise)");
   }
@@ -233,7 +245,7 @@ cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc
   const int acc_recv = dt != DT_BF16;
   if (tree == TREE_HD) {
     for (int d = N / 2; d >= 1 && e == hipSuccess; d /= 2) e = launch_hd_rs_step(r, d, d == N / 2, d == 1, acc_recv);
-    Gat g{r.send, r.recv, M, N, es, 0, r.vec_ok, st};
+    Gat g{r.send, r.recv, M, bd.b, cfg.blocks_per_cu, N, es, 0, r.vec_ok, st};
     for (int d = 1; d < N && e == hipSuccess; d *= 2) e = launch_hd_ag_step(g, d, 0);
     return hip_status(e, "halving-doubling all_reduce (stepwise)");
   }
@@ -259,13 +271,16 @@ cc_status_t cc_reduce_scatter(cc_rankbuf_t send, cc_rankbuf_t recv, size_t recvc
   if ((s = check_ws(CC_COLL_REDUCE_SCATTER, cfg, N, M, dt))) return s;
   if ((s = device_ready())) return s;
   hipStream_t st = (hipStream_t)stream;
-  if (N == 1) return copy_ranks(send, recv, S * es, 1, es, st);
+  if (N == 1) return copy_ranks(send, recv, S * es, 1, es, cfg.blocks_per_cu, st);
 
+  const Bounds bd(M, N);
   Red r;
   r.send = side(send);
   r.recv = side(recv);
   r.ws = ws_side(cfg, M);
   r.M = M;
+  r.bnd = bd.b;
+  r.blocks_per_cu = cfg.blocks_per_cu;
   r.N = N;
   r.dt = dt;
   r.op = (int)op;
@@ -301,11 +316,14 @@ cc_status_t cc_all_gather(cc_rankbuf_t send, cc_rankbuf_t recv, size_t sendcount
   if ((s = grid_fits(M, dt))) return s;
   if ((s = device_ready())) return s;
   hipStream_t st = (hipStream_t)stream;
-  if (N == 1) return copy_ranks(send, recv, S * es, 1, es, st);
+  if (N == 1) return copy_ranks(send, recv, S * es, 1, es, cfg.blocks_per_cu, st);
+  const Bounds bd(M, N);
   Gat g;
   g.send = side(send);
   g.recv = side(recv);
   g.M = M;
+  g.bnd = bd.b;
+  g.blocks_per_cu = cfg.blocks_per_cu;
   g.N = N;
   g.esize = es;
   g.ag_mode = 1;
@@ -339,25 +357,25 @@ cc_status_t cc_broadcast(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_
   const cc_rankbuf_t src_rank = {(char*)send.base + (uint64_t)root * send.rank_stride_bytes, 0};
   if (!in_place && sides_overlap(src_rank, nb, 1, recv, nb, N))
     return fail(CC_ERR_INVALID_ARG, "the root's send buffer overlaps a recv buffer");
-  if (nb / 16 / kUnroll / kBlock > 0x7fffffffull) return fail(CC_ERR_INVALID_ARG, "count too large");
+  if (nb / 2048 > 0x7fffffffull) return fail(CC_ERR_INVALID_ARG, "count too large");
   if ((s = device_ready())) return s;
   hipStream_t st = (hipStream_t)stream;
   const char* src = (const char*)src_rank.base;
   Side dst = side(recv);
   const int vec_ok = al16p(src) && al16p(recv.base) && al16(recv.rank_stride_bytes);
   if (cfg.fuse_depth == 0 || N == 1)
-    return hip_status(launch_bcast(src, dst, N, in_place ? root : -1, nb, vec_ok, st), "broadcast");
+    return hip_status(launch_bcast(src, dst, N, in_place ? root : -1, nb, vec_ok, cfg.blocks_per_cu, st), "broadcast");
   // stepwise: the root's own output first, then the chain or binomial steps
   hipError_t e = hipSuccess;
   auto rank_ptr = [&](int r) { return dst.base + (uint64_t)((r % N + N) % N) * dst.stride; };
   if (!in_place) {
     CopyDesc d{src, rank_ptr(root), nb};
-    e = launch_copies(&d, 1, es, st);
+    e = launch_copies(&d, 1, es, cfg.blocks_per_cu, st);
   }
   if (cfg.algo == CC_ALGO_RING) {
     for (int s0 = 0; s0 < N - 1 && e == hipSuccess; ++s0) {
       CopyDesc d{rank_ptr(root + s0), rank_ptr(root + s0 + 1), nb};
-      e = launch_copies(&d, 1, es, st);
+      e = launch_copies(&d, 1, es, cfg.blocks_per_cu, st);
     }
     return hip_status(e, "ring broadcast (stepwise)");
   }
@@ -365,7 +383,7 @@ cc_status_t cc_broadcast(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_
     std::vector<CopyDesc> d;
     for (int rel = 0; rel < k && rel + k < N; ++rel) d.push_back(CopyDesc{rank_ptr(root + rel), rank_ptr(root + rel + k), nb});
     for (size_t i = 0; i < d.size() && e == hipSuccess; i += kMaxDesc)
-      e = launch_copies(d.data() + i, (int)std::min<size_t>(kMaxDesc, d.size() - i), es, st);
+      e = launch_copies(d.data() + i, (int)std::min<size_t>(kMaxDesc, d.size() - i), es, cfg.blocks_per_cu, st);
   }
   return hip_status(e, "binomial broadcast (stepwise)");
 }
@@ -400,7 +418,7 @@ cc_status_t cc_all_to_all(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* co
   if ((s = check_side(send, smax, N, "send")) || (s = check_side(recv, rmax, N, "recv"))) return s;
   if (sides_overlap(send, smax, N, recv, rmax, N)) return fail(CC_ERR_INVALID_ARG, "send and recv overlap");
   if (smax == 0) return ok();
-  if (smax / (uint64_t)(kBlock * 4 * 16) > 0x7fffffffull / (uint64_t)N)
+  if (smax / 2048 > (0x7fffffffull - kMaxDesc) / (uint64_t)N)
     return fail(CC_ERR_INVALID_ARG, "counts too large for one launch");
   if ((s = device_ready())) return s;
   hipStream_t st = (hipStream_t)stream;
@@ -415,13 +433,13 @@ cc_status_t cc_all_to_all(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* co
     for (int j = 0; j < N; ++j)
       for (int i = 0; i < N; ++i) d.push_back(desc(i, j));
     for (size_t i = 0; i < d.size() && e == hipSuccess; i += kMaxDesc)
-      e = launch_copies(d.data() + i, (int)std::min<size_t>(kMaxDesc, d.size() - i), es, st);
+      e = launch_copies(d.data() + i, (int)std::min<size_t>(kMaxDesc, d.size() - i), es, cfg.blocks_per_cu, st);
     return hip_status(e, "all_to_all");
   }
   for (int k = 0; k < N && e == hipSuccess; ++k) {  // pairwise: step k sends i -> i+k
     d.clear();
     for (int i = 0; i < N; ++i) d.push_back(desc(i, (i + k) % N));
-    e = launch_copies(d.data(), N, es, st);
+    e = launch_copies(d.data(), N, es, cfg.blocks_per_cu, st);
   }
   return hip_status(e, "pairwise all_to_all");
 }

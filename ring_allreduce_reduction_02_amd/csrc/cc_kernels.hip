@@ -64,10 +64,10 @@ struct Ty<DT_BF16> {
 // fp32 -> bf16, round to nearest even; NaN stays NaN (quiet, sign kept),
 // overflow carries into the exponent and gives +-inf.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded;   // a select, not a branch
 }
 
 template <int DT>
@@ -191,13 +191,13 @@ __device__ __forceinline__ void opv(const typename Ty<DT>::A* x, typename Ty<DT>
 
 // ------------------------------------------------------------------ chunks
 
-// chunk c holds [floor(c*M/N), floor((c+1)*M/N)); for an element e it is the
-// largest c with floor(c*M/N) <= e, i.e. floor(((e+1)*N - 1) / M).
-__device__ __forceinline__ uint32_t chunk_of(uint64_t e, uint64_t M, uint32_t N) {
-  return (uint32_t)(((e + 1) * (uint64_t)N - 1) / M);
-}
-__device__ __forceinline__ uint64_t bnd(uint32_t c, uint64_t M, uint32_t N) {
-  return ((uint64_t)c * M) / N;
+// Chunk c holds [bnd[c], bnd[c+1]) with bnd[c] = floor(c*M/N) (computed on the
+// host).  The chunk of an element e is the number of inner boundaries at or
+// below e; with a workgroup-uniform e the loop runs on the scalar unit.
+__device__ __forceinline__ uint32_t chunk_in(const uint64_t* bnd, int N, uint64_t e) {
+  uint32_t c = 0;
+  for (int i = 1; i < N; ++i) c += bnd[i] <= e ? 1u : 0u;
+  return c;
 }
 __device__ __forceinline__ int wrapN(int r, int N) { return r >= N ? r - N : r; }
 __device__ __forceinline__ int modN(int r, int N) { return ((r % N) + N) % N; }
@@ -212,15 +212,15 @@ struct Tile {
 // The workgroup's element range and, when the whole tile is full-width and
 // lies in one chunk, that chunk (uniform across the workgroup).
 template <int V>
-__device__ __forceinline__ Tile<V> tile_of(uint64_t M, uint32_t N, int vec_ok) {
+__device__ __forceinline__ Tile<V> tile_of(uint64_t M, const uint64_t* bnd, int N, int vec_ok) {
   const uint64_t tile = (uint64_t)kBlock * kUnroll * V;
   Tile<V> t;
   t.e0 = (uint64_t)blockIdx.x * tile;
   t.e1 = t.e0 + tile < M ? t.e0 + tile : M;
-  const uint32_t c0 = chunk_of(t.e0, M, N);
-  const uint32_t c1 = chunk_of(t.e1 - 1, M, N);
+  const uint32_t c0 = chunk_in(bnd, N, t.e0);
+  const uint32_t c1 = chunk_in(bnd, N, t.e1 - 1);
   t.c = c0;
-  t.fast = vec_ok && c0 == c1 && (t.e1 - t.e0) == tile;
+  t.fast = vec_ok && (t.e1 - t.e0) == tile && c0 == c1;
   return t;
 }
 
@@ -239,6 +239,7 @@ struct FusedArgs {
   int N;
   int rs_mode;
   int vec_ok;
+  uint64_t bnd[kMaxRanks + 1];
 };
 
 // AllReduce (rs_mode 0): the N-1 ReduceScatter steps of each chunk folded in
@@ -249,75 +250,76 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(FusedArgs a) {
   typedef typename Ty<DT>::A A;
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
+  static_assert(kUnroll == 1, "one 16-byte vector per thread");
   const int N = NR > 0 ? NR : a.N;
-  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
+    // Every rank's tile starts at a workgroup-uniform address; a lane adds
+    // its own 16-byte offset (scalar base + 32-bit vector offset).
     const int c = (int)t.c;
     const int start = a.rs_mode ? wrapN(c + 1, N) : c;
-    A acc[kUnroll][V];
+    const uint32_t lane = threadIdx.x * 16u;
+    const uint64_t eb = t.e0 * SZ;
+    const char* const s0 = a.sb + eb;
+    A acc[V];
     if constexpr (NR > 0) {
-      u32x4 raw[kUnroll][NR];
+      u32x4 raw[NR];
+      const char* p = s0 + (uint64_t)start * a.ss;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t off = vec_elem(t.e0, u, V) * SZ;
-#pragma unroll
-        for (int j = 0; j < NR; ++j) raw[u][j] = ldg(a.sb + (uint64_t)wrapN(start + j, NR) * a.ss + off);
+      for (int j = 0; j < NR; ++j) {
+        raw[j] = ldg(p + lane);
+        p = (start + j + 1 == NR) ? s0 : p + a.ss;
       }
+      unpack<DT>(raw[0], acc);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        unpack<DT>(raw[u][0], acc[u]);
-#pragma unroll
-        for (int j = 1; j < NR; ++j) {
-          A x[V];
-          unpack<DT>(raw[u][j], x);
-          opv<DT, OP>(x, acc[u]);
-        }
+      for (int j = 1; j < NR; ++j) {
+        A x[V];
+        unpack<DT>(raw[j], x);
+        opv<DT, OP>(x, acc);
       }
     } else {
+      const char* p = s0 + (uint64_t)start * a.ss;
+      unpack<DT>(ldg(p + lane), acc);
+      int r = start;
+      for (int j = 1; j < N; j += 8) {
+        u32x4 raw[8];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t off = vec_elem(t.e0, u, V) * SZ;
-        unpack<DT>(ldg(a.sb + (uint64_t)start * a.ss + off), acc[u]);
-        for (int j = 1; j < N; j += 8) {
-          u32x4 raw[8];
+        for (int q = 0; q < 8; ++q)
+          if (j + q < N) {
+            r = r + 1 == N ? 0 : r + 1;
+            p = r == 0 ? s0 : p + a.ss;
+            raw[q] = ldg(p + lane);
+          }
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (j + q < N) raw[q] = ldg(a.sb + (uint64_t)wrapN(start + j + q, N) * a.ss + off);
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (j + q < N) {
-              A x[V];
-              unpack<DT>(raw[q], x);
-              opv<DT, OP>(x, acc[u]);
-            }
-        }
+        for (int q = 0; q < 8; ++q)
+          if (j + q < N) {
+            A x[V];
+            unpack<DT>(raw[q], x);
+            opv<DT, OP>(x, acc);
+          }
       }
     }
-    const uint64_t b0 = a.rs_mode ? bnd((uint32_t)c, a.M, N) : 0;
+    const u32x4 w = pack<DT>(acc);
+    if (a.rs_mode) {
+      stg(a.rb + (uint64_t)c * a.rs + (t.e0 - a.bnd[c]) * SZ + lane, w);
+    } else {
+      char* d = a.rb + eb;
+      if constexpr (NR > 0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const u32x4 w = pack<DT>(acc[u]);
-      const uint64_t e = vec_elem(t.e0, u, V);
-      if (a.rs_mode) {
-        stg(a.rb + (uint64_t)c * a.rs + (e - b0) * SZ, w);
+        for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
       } else {
-        if constexpr (NR > 0) {
-#pragma unroll
-          for (int r = 0; r < NR; ++r) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
-        } else {
-          for (int r = 0; r < N; ++r) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
-        }
+        for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
       }
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = chunk_of(e, a.M, N);
+      const uint32_t c = chunk_in(a.bnd, N, e);
       const int start = a.rs_mode ? wrapN((int)c + 1, N) : (int)c;
       A acc = ld1<DT>(a.sb + (uint64_t)start * a.ss + e * SZ);
       for (int j = 1; j < N; ++j)
         acc = opf<DT, OP>(ld1<DT>(a.sb + (uint64_t)wrapN(start + j, N) * a.ss + e * SZ), acc);
       if (a.rs_mode) {
-        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - bnd(c, a.M, N)) * SZ, acc);
+        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, acc);
       } else {
         for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc);
       }
@@ -385,23 +387,23 @@ __global__ __launch_bounds__(kBlock) void k_tree_fused(FusedArgs a) {
   typedef typename Ty<DT>::A A;
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
-  const Tile<V> t = tile_of<V>(a.M, NR, a.vec_ok);
+  static_assert(kUnroll == 1, "one 16-byte vector per thread");
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, NR, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
-    const uint64_t b0 = a.rs_mode ? bnd((uint32_t)c, a.M, NR) : 0;
+    const uint32_t lane = threadIdx.x * 16u;
+    const uint64_t eb = t.e0 * SZ;
+    const char* const s0 = a.sb + eb;
+    A acc[V];
+    tree_fold<DT, OP, NR, TREE>(
+        [&](int r, A* v) { unpack<DT>(ldg(s0 + (uint64_t)r * a.ss + lane), v); }, acc, V);
+    const u32x4 w = pack<DT>(acc);
+    if (a.rs_mode) {
+      stg(a.rb + (uint64_t)c * a.rs + (t.e0 - a.bnd[c]) * SZ + lane, w);
+    } else {
+      char* d = a.rb + eb;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint64_t e = vec_elem(t.e0, u, V);
-      A acc[V];
-      tree_fold<DT, OP, NR, TREE>(
-          [&](int r, A* v) { unpack<DT>(ldg(a.sb + (uint64_t)r * a.ss + e * SZ), v); }, acc, V);
-      const u32x4 w = pack<DT>(acc);
-      if (a.rs_mode) {
-        stg(a.rb + (uint64_t)c * a.rs + (e - b0) * SZ, w);
-      } else {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
-      }
+      for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
@@ -409,8 +411,8 @@ __global__ __launch_bounds__(kBlock) void k_tree_fused(FusedArgs a) {
       tree_fold<DT, OP, NR, TREE>(
           [&](int r, A* v) { v[0] = ld1<DT>(a.sb + (uint64_t)r * a.ss + e * SZ); }, acc, 1);
       if (a.rs_mode) {
-        const uint32_t c = chunk_of(e, a.M, NR);
-        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - bnd(c, a.M, NR)) * SZ, acc[0]);
+        const uint32_t c = chunk_in(a.bnd, NR, e);
+        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, acc[0]);
       } else {
 #pragma unroll
         for (int r = 0; r < NR; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc[0]);
@@ -434,6 +436,7 @@ struct PassArgs {
   int s0;
   int k;
   int pin_recv;  // partials live in the receiving rank's recv buffer
+  uint64_t bnd[kMaxRanks + 1];
 };
 
 // Ring ReduceScatter steps s0 .. s0+k-1 for every chunk: the partial that the
@@ -446,11 +449,11 @@ __global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N;
   const bool fin = a.s0 + a.k == N - 1;
-  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const int start = a.rs_mode ? wrapN(c + 1, N) : c;
-    const uint64_t b0 = bnd((uint32_t)c, a.M, N);
+    const uint64_t b0 = a.bnd[c];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint64_t e = vec_elem(t.e0, u, V);
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = chunk_of(e, a.M, N);
+      const uint32_t c = chunk_in(a.bnd, N, e);
       const int start = a.rs_mode ? wrapN((int)c + 1, N) : (int)c;
       A acc;
       if (a.s0 == 0)
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
         acc = opf<DT, OP>(ld1<DT>(a.sb + (uint64_t)wrapN(start + j, N) * a.ss + e * SZ), acc);
       if (fin) {
         if (a.rs_mode)
-          st1<DT>(a.rb + (uint64_t)c * a.rs + (e - bnd(c, a.M, N)) * SZ, acc);
+          st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, acc);
         else
           st1<DT>(a.rb + (uint64_t)wrapN(start + N - 1, N) * a.rs + e * SZ, acc);
       } else if (a.pin_recv) {
@@ -521,6 +524,7 @@ struct StepArgs {
   int first;     // operands come from the send buffers
   int last;      // results are final (buffer type)
   int acc_recv;  // intermediate accumulators live in recv (else in wb)
+  uint64_t bnd[kMaxRanks + 1];
 };
 
 template <int DT>
@@ -560,11 +564,11 @@ __global__ __launch_bounds__(kBlock) void k_hd_rs_step(StepArgs a) {
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N, d = a.d;
-  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const int base = c & ~(d - 1);
-    const uint64_t b0 = bnd((uint32_t)c, a.M, N);
+    const uint64_t b0 = a.bnd[c];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint64_t e = vec_elem(t.e0, u, V);
@@ -584,13 +588,13 @@ __global__ __launch_bounds__(kBlock) void k_hd_rs_step(StepArgs a) {
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = chunk_of(e, a.M, N);
+      const uint32_t c = chunk_in(a.bnd, N, e);
       const int base = (int)c & ~(d - 1);
       for (int m = 0; m < d; ++m) {
         const int i = base | m, p = i ^ d;
         A v = opf<DT, OP>(step_load1<DT>(a, p, e), step_load1<DT>(a, i, e));
         if (a.last) {
-          if (a.rs_mode) st1<DT>(a.rb + (uint64_t)c * a.rs + (e - bnd(c, a.M, N)) * SZ, v);
+          if (a.rs_mode) st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, v);
           else st1<DT>(a.rb + (uint64_t)c * a.rs + e * SZ, v);
         } else {
           step_store1<DT>(a, i, e, v);
@@ -608,7 +612,7 @@ __global__ __launch_bounds__(kBlock) void k_bfly_step(StepArgs a) {
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N, d = a.d;
-  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -661,6 +665,7 @@ struct GatArgs {
   int vec_ok;
   int s0;
   int k;
+  uint64_t bnd[kMaxRanks + 1];
 };
 
 // Ring AllGather steps s0 .. s0+k-1: chunk c is copied from the rank that
@@ -671,10 +676,10 @@ template <int SZ>
 __global__ __launch_bounds__(kBlock) void k_ring_ag_pass(GatArgs a) {
   constexpr int V = 16 / SZ;
   const int N = a.N;
-  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
-    const uint64_t b0 = bnd((uint32_t)c, a.M, N);
+    const uint64_t b0 = a.bnd[c];
     const bool from_send = a.mode == 1 && a.s0 == 0;
     const int holder = a.mode == 0 ? modN(c - 1 + a.s0, N) : wrapN(c + a.s0, N);
     const int first_dst = a.mode == 0 ? wrapN(holder + 1, N) : wrapN(holder + 1, N);
@@ -688,10 +693,10 @@ __global__ __launch_bounds__(kBlock) void k_ring_ag_pass(GatArgs a) {
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const int c = (int)chunk_of(e, a.M, N);
+      const int c = (int)chunk_in(a.bnd, N, e);
       const bool from_send = a.mode == 1 && a.s0 == 0;
       const int holder = a.mode == 0 ? modN(c - 1 + a.s0, N) : wrapN(c + a.s0, N);
-      const char* src = from_send ? a.sb + (uint64_t)c * a.ss + (e - bnd((uint32_t)c, a.M, N)) * SZ
+      const char* src = from_send ? a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ
                                   : a.rb + (uint64_t)holder * a.rs + e * SZ;
       if constexpr (SZ == 2) {
         const uint16_t v = *(const uint16_t*)src;
@@ -712,10 +717,10 @@ template <int SZ>
 __global__ __launch_bounds__(kBlock) void k_hd_ag_step(GatArgs a) {
   constexpr int V = 16 / SZ;
   const int N = a.N, d = a.s0, first = a.k;  // s0 carries d, k carries "first"
-  const Tile<V> t = tile_of<V>(a.M, N, a.vec_ok);
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
-    const uint64_t b0 = bnd((uint32_t)c, a.M, N);
+    const uint64_t b0 = a.bnd[c];
     const int base = (c ^ d) & ~(d - 1);
     const bool from_send = a.mode == 1 && first;
 #pragma unroll
@@ -734,10 +739,10 @@ __global__ __launch_bounds__(kBlock) void k_hd_ag_step(GatArgs a) {
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const int c = (int)chunk_of(e, a.M, N);
+      const int c = (int)chunk_in(a.bnd, N, e);
       const int base = (c ^ d) & ~(d - 1);
       if (a.mode == 1 && first) {
-        const char* src = a.sb + (uint64_t)c * a.ss + (e - bnd((uint32_t)c, a.M, N)) * SZ;
+        const char* src = a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ;
         for (int q = 0; q < 2; ++q) {
           char* dst = a.rb + (uint64_t)(q ? (c ^ 1) : c) * a.rs + e * SZ;
           if constexpr (SZ == 2) *(uint16_t*)dst = *(const uint16_t*)src;
@@ -768,21 +773,20 @@ struct BcArgs {
   int vec_ok;
 };
 
+constexpr int kCopyBlock = 128;
+constexpr uint64_t kBcastTile = (uint64_t)kCopyBlock * 16;
+
 // One read of the root's buffer, N (or N-1) writes.
-__global__ __launch_bounds__(kBlock) void k_bcast(BcArgs a) {
-  const uint64_t tile = (uint64_t)kBlock * kUnroll * 16;
-  const uint64_t b0 = (uint64_t)blockIdx.x * tile;
-  const uint64_t b1 = b0 + tile < a.nbytes ? b0 + tile : a.nbytes;
-  if (a.vec_ok && b1 - b0 == tile) {
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint64_t off = b0 + ((uint64_t)u * kBlock + threadIdx.x) * 16;
-      const u32x4 w = ldg(a.src + off);
-      for (int r = 0; r < a.N; ++r)
-        if (r != a.skip) stg(a.db + (uint64_t)r * a.ds + off, w);
-    }
+__global__ __launch_bounds__(kCopyBlock) void k_bcast(BcArgs a) {
+  const uint64_t b0 = (uint64_t)blockIdx.x * kBcastTile;
+  const uint64_t b1 = b0 + kBcastTile < a.nbytes ? b0 + kBcastTile : a.nbytes;
+  if (a.vec_ok && b1 - b0 == kBcastTile) {
+    const uint64_t off = b0 + (uint64_t)threadIdx.x * 16;
+    const u32x4 w = ldg(a.src + off);
+    for (int r = 0; r < a.N; ++r)
+      if (r != a.skip) stg(a.db + (uint64_t)r * a.ds + off, w);
   } else {
-    for (uint64_t b = b0 + threadIdx.x; b < b1; b += kBlock) {
+    for (uint64_t b = b0 + threadIdx.x; b < b1; b += kCopyBlock) {
       const uint8_t v = (uint8_t)a.src[b];
       for (int r = 0; r < a.N; ++r)
         if (r != a.skip) a.db[(uint64_t)r * a.ds + b] = (char)v;
@@ -800,30 +804,28 @@ struct CopyArgs {
   int esize;
 };
 
-constexpr uint64_t kCopyTile = (uint64_t)kBlock * 4 * 16;
+constexpr uint64_t kCopyTile = (uint64_t)kCopyBlock * 16;
 
 // Flat tiling over a list of copies: workgroup b copies tile (b - tpre[k]) of
-// descriptor k, so skewed block sizes still spread over the whole chip.
-__global__ __launch_bounds__(kBlock) void k_copies(CopyArgs a) {
+// descriptor k (found by binary search), so skewed block sizes still spread
+// over the whole chip.
+__global__ __launch_bounds__(kCopyBlock) void k_copies(CopyArgs a) {
   const uint64_t b = blockIdx.x;
-  int k = 0;
-  while (k + 1 < a.n && b >= a.tpre[k + 1]) ++k;
+  int lo = 0, hi = a.n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (b >= a.tpre[mid]) lo = mid; else hi = mid;
+  }
+  const int k = lo;
   const uint64_t o0 = (b - a.tpre[k]) * kCopyTile;
   const uint64_t nb = a.bytes[k];
   const uint64_t o1 = o0 + kCopyTile < nb ? o0 + kCopyTile : nb;
   const char* src = a.src[k];
   char* dst = a.dst[k];
-  if (((a.vecmask >> k) & 1) && o1 - o0 == kCopyTile) {
-    u32x4 w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) w[u] = ldg(src + o0 + ((uint64_t)u * kBlock + threadIdx.x) * 16);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) stg(dst + o0 + ((uint64_t)u * kBlock + threadIdx.x) * 16, w[u]);
-  } else if (((a.vecmask >> k) & 1)) {
-    for (uint64_t o = o0 + (uint64_t)threadIdx.x * 16; o < o1; o += (uint64_t)kBlock * 16)
-      stg(dst + o, ldg(src + o));
+  if ((a.vecmask >> k) & 1) {
+    for (uint64_t o = o0 + (uint64_t)threadIdx.x * 16; o < o1; o += kCopyTile) stg(dst + o, ldg(src + o));
   } else {
-    for (uint64_t o = o0 + threadIdx.x; o < o1; o += kBlock) dst[o] = src[o];
+    for (uint64_t o = o0 + threadIdx.x; o < o1; o += kCopyBlock) dst[o] = src[o];
   }
 }
 
@@ -850,23 +852,69 @@ FusedArgs fused_args(const Red& r) {
   a.sb = r.send.base; a.ss = r.send.stride;
   a.rb = r.recv.base; a.rs = r.recv.stride;
   a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
+  for (int c = 0; c <= r.N; ++c) a.bnd[c] = r.bnd[c];
   return a;
 }
 
+struct DevInfo {
+  int lds_per_cu = 0;
+  int lds_per_block = 0;
+};
+
+DevInfo dev_info() {
+  static DevInfo cache[64];
+  static bool have[64] = {};
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) d = 0;
+  if (!have[d]) {
+    DevInfo i;
+    if (hipDeviceGetAttribute(&i.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, d) != hipSuccess)
+      i.lds_per_cu = 0;
+    if (hipDeviceGetAttribute(&i.lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, d) != hipSuccess)
+      i.lds_per_block = 0;
+    cache[d] = i;
+    have[d] = true;
+  }
+  return cache[d];
+}
+
+}  // namespace
+
+unsigned lds_for_blocks_per_cu(int blocks) {
+  if (blocks <= 0) return 0;
+  const DevInfo i = dev_info();
+  if (i.lds_per_cu <= 0 || i.lds_per_block <= 0) return 0;
+  unsigned lds = (unsigned)(i.lds_per_cu / blocks) & ~255u;
+  if (lds > (unsigned)i.lds_per_block) lds = (unsigned)i.lds_per_block;
+  return lds;
+}
+
+// About 32 KiB of loads in flight per CU serves HBM best for these streams.
+int default_blocks_per_cu(uint64_t bytes_per_block) {
+  if (bytes_per_block == 0) return 0;
+  int b = (int)((32768 + bytes_per_block / 2) / bytes_per_block);
+  return b < 1 ? 1 : (b > 16 ? 16 : b);
+}
+
+namespace {
+unsigned occupancy_lds(int requested, uint64_t bytes_per_block) {
+  return lds_for_blocks_per_cu(requested > 0 ? requested : default_blocks_per_cu(bytes_per_block));
+}
 }  // namespace
 
 hipError_t launch_ring_fused(const Red& r) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * r.N);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     switch (r.N) {
-      case 2: hipLaunchKernelGGL((k_ring_fused<DT, OP, 2>), grid, blk, 0, r.st, a); break;
-      case 3: hipLaunchKernelGGL((k_ring_fused<DT, OP, 3>), grid, blk, 0, r.st, a); break;
-      case 4: hipLaunchKernelGGL((k_ring_fused<DT, OP, 4>), grid, blk, 0, r.st, a); break;
-      case 8: hipLaunchKernelGGL((k_ring_fused<DT, OP, 8>), grid, blk, 0, r.st, a); break;
-      case 16: hipLaunchKernelGGL((k_ring_fused<DT, OP, 16>), grid, blk, 0, r.st, a); break;
-      default: hipLaunchKernelGGL((k_ring_fused<DT, OP, 0>), grid, blk, 0, r.st, a); break;
+      case 2: hipLaunchKernelGGL((k_ring_fused<DT, OP, 2>), grid, blk, lds, r.st, a); break;
+      case 3: hipLaunchKernelGGL((k_ring_fused<DT, OP, 3>), grid, blk, lds, r.st, a); break;
+      case 4: hipLaunchKernelGGL((k_ring_fused<DT, OP, 4>), grid, blk, lds, r.st, a); break;
+      case 8: hipLaunchKernelGGL((k_ring_fused<DT, OP, 8>), grid, blk, lds, r.st, a); break;
+      case 16: hipLaunchKernelGGL((k_ring_fused<DT, OP, 16>), grid, blk, lds, r.st, a); break;
+      default: hipLaunchKernelGGL((k_ring_fused<DT, OP, 0>), grid, blk, lds, r.st, a); break;
     }
     return hipGetLastError();
   });
@@ -875,14 +923,15 @@ hipError_t launch_ring_fused(const Red& r) {
 hipError_t launch_tree_fused(const Red& r, int tree) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * r.N);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
 #define CC_TREE_CASE(NR)                                                                      \
   case NR:                                                                                    \
     if (tree == TREE_HD)                                                                      \
-      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_HD>), grid, blk, 0, r.st, a);         \
+      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_HD>), grid, blk, lds, r.st, a);       \
     else                                                                                      \
-      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_BFLY>), grid, blk, 0, r.st, a);       \
+      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_BFLY>), grid, blk, lds, r.st, a);     \
     break;
     switch (r.N) {
       CC_TREE_CASE(2)
@@ -905,10 +954,12 @@ hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv)
   a.wb = r.ws.base;
   a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
   a.s0 = s0; a.k = k; a.pin_recv = partial_in_recv;
+  for (int c = 0; c <= r.N; ++c) a.bnd[c] = r.bnd[c];
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * (k + 1));
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_ring_pass<DT, OP>), grid, blk, 0, r.st, a);
+    hipLaunchKernelGGL((k_ring_pass<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }
@@ -920,15 +971,17 @@ static StepArgs step_args(const Red& r, int d, int first, int last, int acc_in_r
   a.wb = r.ws.base; a.ws = r.ws.stride;
   a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
   a.d = d; a.first = first; a.last = last; a.acc_recv = acc_in_recv;
+  for (int c = 0; c <= r.N; ++c) a.bnd[c] = r.bnd[c];
   return a;
 }
 
 hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_in_recv) {
   const StepArgs a = step_args(r, d, first, last, acc_in_recv);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * 2 * d);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_hd_rs_step<DT, OP>), grid, blk, 0, r.st, a);
+    hipLaunchKernelGGL((k_hd_rs_step<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }
@@ -936,9 +989,10 @@ hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_i
 hipError_t launch_bfly_step(const Red& r, int d, int first, int last, int acc_in_recv) {
   const StepArgs a = step_args(r, d, first, last, acc_in_recv);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * r.N);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_bfly_step<DT, OP>), grid, blk, 0, r.st, a);
+    hipLaunchKernelGGL((k_bfly_step<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }
@@ -949,6 +1003,7 @@ static GatArgs gat_args(const Gat& g, int s0, int k) {
   a.rb = g.recv.base; a.rs = g.recv.stride;
   a.M = g.M; a.N = g.N; a.mode = g.ag_mode; a.vec_ok = g.vec_ok;
   a.s0 = s0; a.k = k;
+  for (int c = 0; c <= g.N; ++c) a.bnd[c] = g.bnd[c];
   return a;
 }
 
@@ -960,8 +1015,10 @@ static unsigned gat_tiles(const Gat& g) {
 hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k) {
   const GatArgs a = gat_args(g, s0, k);
   const dim3 grid(gat_tiles(g)), blk(kBlock);
-  if (g.esize == 2) hipLaunchKernelGGL((k_ring_ag_pass<2>), grid, blk, 0, g.st, a);
-  else hipLaunchKernelGGL((k_ring_ag_pass<4>), grid, blk, 0, g.st, a);
+  // one load, k (or k+1) stores per thread: keep the reads deep
+  const unsigned lds = g.blocks_per_cu > 0 ? lds_for_blocks_per_cu(g.blocks_per_cu) : 0;
+  if (g.esize == 2) hipLaunchKernelGGL((k_ring_ag_pass<2>), grid, blk, lds, g.st, a);
+  else hipLaunchKernelGGL((k_ring_ag_pass<4>), grid, blk, lds, g.st, a);
   return hipGetLastError();
 }
 
@@ -970,26 +1027,27 @@ hipError_t launch_ag_fused(const Gat& g) { return launch_ring_ag_pass(g, 0, g.N 
 hipError_t launch_hd_ag_step(const Gat& g, int d, int first) {
   const GatArgs a = gat_args(g, d, first);
   const dim3 grid(gat_tiles(g)), blk(kBlock);
-  if (g.esize == 2) hipLaunchKernelGGL((k_hd_ag_step<2>), grid, blk, 0, g.st, a);
-  else hipLaunchKernelGGL((k_hd_ag_step<4>), grid, blk, 0, g.st, a);
+  const unsigned lds = g.blocks_per_cu > 0 ? lds_for_blocks_per_cu(g.blocks_per_cu) : 0;
+  if (g.esize == 2) hipLaunchKernelGGL((k_hd_ag_step<2>), grid, blk, lds, g.st, a);
+  else hipLaunchKernelGGL((k_hd_ag_step<4>), grid, blk, lds, g.st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_bcast(const char* src, Side dst, int N, int skip, uint64_t nbytes, int vec_ok,
-                        hipStream_t st) {
+                        int blocks_per_cu, hipStream_t st) {
   BcArgs a;
   a.src = src; a.db = dst.base; a.ds = dst.stride; a.nbytes = nbytes;
   a.N = N; a.skip = skip; a.vec_ok = vec_ok;
-  const uint64_t tile = (uint64_t)kBlock * kUnroll * 16;
-  const dim3 grid((unsigned)((nbytes + tile - 1) / tile)), blk(kBlock);
-  hipLaunchKernelGGL(k_bcast, grid, blk, 0, st, a);
+  const dim3 grid((unsigned)((nbytes + kBcastTile - 1) / kBcastTile)), blk(kCopyBlock);
+  const unsigned lds = blocks_per_cu > 0 ? lds_for_blocks_per_cu(blocks_per_cu) : 0;
+  hipLaunchKernelGGL(k_bcast, grid, blk, lds, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_copies(const CopyDesc* d, int n, int esize, hipStream_t st) {
+hipError_t launch_copies(const CopyDesc* d, int n, int esize, int blocks_per_cu, hipStream_t st) {
   CopyArgs a;
   a.n = 0; a.esize = esize; a.vecmask = 0; a.tpre[0] = 0;
-  for (int i = 0; i < n; ++i) {
+  for (int i = 0; i < n && i < kMaxDesc; ++i) {
     if (d[i].bytes == 0) continue;
     const int j = a.n++;
     a.src[j] = d[i].src; a.dst[j] = d[i].dst; a.bytes[j] = d[i].bytes;
@@ -997,8 +1055,9 @@ hipError_t launch_copies(const CopyDesc* d, int n, int esize, hipStream_t st) {
     if ((((uintptr_t)d[i].src | (uintptr_t)d[i].dst | d[i].bytes) & 15u) == 0) a.vecmask |= 1ull << j;
   }
   if (a.n == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.tpre[a.n]), blk(kBlock);
-  hipLaunchKernelGGL(k_copies, grid, blk, 0, st, a);
+  const dim3 grid((unsigned)a.tpre[a.n]), blk(kCopyBlock);
+  const unsigned lds = blocks_per_cu > 0 ? lds_for_blocks_per_cu(blocks_per_cu) : 0;
+  hipLaunchKernelGGL(k_copies, grid, blk, lds, st, a);
   return hipGetLastError();
 }
 

@@ -15,9 +15,19 @@ inline int elem_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
 // elements per 16-byte vector
 inline int vec_elems(int dt) { return 16 / elem_size(dt); }
 
-constexpr int kBlock = 256;   // threads per workgroup (4 wavefronts of 64)
-constexpr int kUnroll = 2;    // 16-byte vectors per thread per tile
-constexpr int kMaxDesc = 64;  // copy descriptors per launch
+constexpr int kBlock = 128;    // threads per workgroup of the reduction kernels (2 wavefronts)
+constexpr int kUnroll = 1;     // 16-byte vectors per thread per tile
+constexpr int kMaxDesc = 64;   // copy descriptors per launch
+constexpr int kMaxRanks = 64;
+
+// Occupancy: the kernels stream HBM with no reuse, and the DRAM serves a
+// mixed read/write stream best when each CU keeps only a few tens of KiB of
+// loads in flight.  A launch caps the workgroups per CU by reserving dynamic
+// LDS (the kernels do not use it); blocks_per_cu = 0 picks the default.
+// dynamic LDS bytes that limit a launch to `blocks` workgroups per CU
+unsigned lds_for_blocks_per_cu(int blocks);
+// default cap for a kernel that keeps `bytes_per_block` of loads in flight
+int default_blocks_per_cu(uint64_t bytes_per_block);
 
 // Rank-strided view: rank r at base + r * stride (bytes).
 struct Side {
@@ -32,6 +42,8 @@ struct Red {
   Side recv;
   Side ws;        // staging (accumulator type, 4 bytes per element), or {nullptr,0}
   uint64_t M;
+  const uint64_t* bnd;  // host array of N+1 chunk boundaries floor(c*M/N)
+  int blocks_per_cu;    // occupancy cap (0 = default)
   int N;
   int dt;
   int op;
@@ -63,6 +75,8 @@ struct Gat {
   Side send;
   Side recv;
   uint64_t M;     // full per-rank vector (recv) length
+  const uint64_t* bnd;  // host array of N+1 chunk boundaries
+  int blocks_per_cu;
   int N;
   int esize;      // bytes per element
   int ag_mode;
@@ -75,7 +89,7 @@ hipError_t launch_hd_ag_step(const Gat& g, int d, int first);
 
 // ---- broadcast: one source to N rank buffers (skip < 0: write all)
 hipError_t launch_bcast(const char* src, Side dst, int N, int skip, uint64_t nbytes, int vec_ok,
-                        hipStream_t st);
+                        int blocks_per_cu, hipStream_t st);
 
 // ---- descriptor copy: up to kMaxDesc (src, dst, bytes) copies in one launch
 struct CopyDesc {
@@ -83,6 +97,6 @@ struct CopyDesc {
   char* dst;
   uint64_t bytes;
 };
-hipError_t launch_copies(const CopyDesc* d, int n, int esize, hipStream_t st);
+hipError_t launch_copies(const CopyDesc* d, int n, int esize, int blocks_per_cu, hipStream_t st);
 
 }  // namespace cc

@@ -1,0 +1,135 @@
+"""Summarize rocprofv3 CSV output for one kernel into a short text record.
+
+Reads a --kernel-trace --stats run (<name>_kernel_stats.csv) and two --pmc runs
+(FETCH_SIZE, WRITE_SIZE; <name>_counter_collection.csv) of the same command.
+The counters are scaled by what they read for a plain device copy of known
+size that ran in the same process (the copy-probe kernel), because on this
+part FETCH_SIZE under-reports by a constant factor.
+
+    python -m ring_allreduce_reduction_02_amd.profsum \\
+        --trace gpurun_out/prof_trace --fetch gpurun_out/prof_fetch --write gpurun_out/prof_write \\
+        --kernel "k_ring_fused<1, 0, 8>" --copy-bytes 1073741824 --alg-bytes 4294967296 \\
+        --out profiles/ring_fused_f32_n8_m67108864 --command "..."
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _one(path_glob: str) -> str:
+    hits = sorted(glob.glob(path_glob, recursive=True))
+    if not hits:
+        raise FileNotFoundError(path_glob)
+    return hits[0]
+
+
+def counter_means(run_dir: str, counter: str):
+    rows = list(csv.DictReader(open(_one(os.path.join(run_dir, "**", "*counter_collection.csv")))))
+    agg = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        agg.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in agg.items()}
+
+
+def pick(means, needle):
+    for k, v in means.items():
+        if needle in k:
+            return k, v
+    raise KeyError(needle)
+
+
+def kernel_stats(trace_dir: str, needle: str):
+    rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
+    for r in rows:
+        if needle in r["Name"]:
+            return r
+    raise KeyError(needle)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--kernel", required=True, help="substring of the kernel name")
+    ap.add_argument("--copy-bytes", type=int, required=True)
+    ap.add_argument("--alg-bytes", type=int, required=True, help="algorithmic bytes per launch")
+    ap.add_argument("--out", required=True, help="output path without extension")
+    ap.add_argument("--trace-command", required=True)
+    ap.add_argument("--pmc-command", required=True)
+    ap.add_argument("--workload", required=True)
+    args = ap.parse_args()
+
+    st = kernel_stats(args.trace, args.kernel)
+    fetch = counter_means(args.fetch, "FETCH_SIZE")
+    write = counter_means(args.write, "WRITE_SIZE")
+    kname, (f_kib, f_n) = pick(fetch, args.kernel)
+    _, (w_kib, w_n) = pick(write, args.kernel)
+    _, (cf_kib, _) = pick(fetch, COPY_KERNEL)
+    _, (cw_kib, _) = pick(write, COPY_KERNEL)
+    fetch_scale = args.copy_bytes / (cf_kib * 1024.0)
+    write_scale = args.copy_bytes / (cw_kib * 1024.0)
+    traffic = f_kib * 1024.0 * fetch_scale + w_kib * 1024.0 * write_scale
+    avg_ns = float(st["AverageNs"])
+    rec = {
+        "kernel": kname,
+        "workload": args.workload,
+        "kernel_source_sha256_16": source_hash(os.path.join(HERE, "csrc", "cc_kernels.hip")),
+        "calls": int(st["Calls"]),
+        "avg_ns": avg_ns,
+        "min_ns": float(st["MinNs"]),
+        "max_ns": float(st["MaxNs"]),
+        "fetch_kib_per_dispatch": f_kib,
+        "write_kib_per_dispatch": w_kib,
+        "fetch_dispatches": f_n,
+        "write_dispatches": w_n,
+        "copy_probe_bytes": args.copy_bytes,
+        "copy_fetch_kib": cf_kib,
+        "copy_write_kib": cw_kib,
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "traffic_bytes_per_launch": traffic,
+        "algorithmic_bytes_per_launch": args.alg_bytes,
+        "traffic_over_algorithmic": traffic / args.alg_bytes,
+        "achieved_GBps_from_trace": args.alg_bytes / avg_ns,
+        "trace_command": args.trace_command,
+        "pmc_command": args.pmc_command,
+    }
+    with open(args.out + "_pmc.json", "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(args.out + ".md", "w") as f:
+        f.write(f"# {args.workload}\n\n")
+        f.write(f"Kernel: `{kname}`  (source sha256/16 `{rec['kernel_source_sha256_16']}`)\n\n")
+        f.write("## rocprofv3 --kernel-trace --stats\n\n")
+        f.write(f"Command: `{args.trace_command}`\n\n")
+        f.write("| calls | avg us | min us | max us | algorithmic GB | GB/s at avg |\n|---|---|---|---|---|---|\n")
+        f.write(f"| {rec['calls']} | {avg_ns / 1e3:.2f} | {rec['min_ns'] / 1e3:.2f} | {rec['max_ns'] / 1e3:.2f} | "
+                f"{args.alg_bytes / 1e9:.3f} | {rec['achieved_GBps_from_trace']:.1f} |\n\n")
+        f.write("## rocprofv3 --pmc (one counter per run)\n\n")
+        f.write(f"Command (run once with FETCH_SIZE, once with WRITE_SIZE): `{args.pmc_command}`\n\n")
+        f.write("| counter | kernel KiB/dispatch | plain copy of "
+                f"{args.copy_bytes} B reads KiB | scale | kernel bytes |\n|---|---|---|---|---|\n")
+        f.write(f"| FETCH_SIZE | {f_kib:.1f} | {cf_kib:.1f} | {fetch_scale:.4f} | {f_kib * 1024 * fetch_scale:.4e} |\n")
+        f.write(f"| WRITE_SIZE | {w_kib:.1f} | {cw_kib:.1f} | {write_scale:.4f} | {w_kib * 1024 * write_scale:.4e} |\n\n")
+        f.write(f"HBM traffic per launch {traffic:.4e} B = {rec['traffic_over_algorithmic']:.4f} x the algorithmic "
+                f"{args.alg_bytes} B.\n")
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    main()

@@ -121,7 +121,7 @@ def _rb(base, stride):
 
 
 def _ar(send, recv, count, N, dtype=1, op=0, cfg=None):
-    c = cfg if cfg is not None else ccgpu.Config(0, 0, None, 0)
+    c = cfg if cfg is not None else ccgpu.Config(0, 0, None, 0, 0)
     return ccgpu.raw("cc_all_reduce", send, recv, count, dtype, op, N, ctypes.byref(c), None)
 
 
@@ -135,13 +135,14 @@ def test_all_reduce_rejects_bad_arguments():
     assert _ar(_rb(None, 4096), ok_r, 100, 4) == ccgpu.CC_ERR_INVALID_ARG  # NULL base
     assert _ar(_rb(FAKE, 200), ok_r, 100, 4) == ccgpu.CC_ERR_INVALID_ARG   # ranks overlap (400 B > stride)
     assert _ar(ok_s, _rb(FAKE + 100, 4096), 100, 4) == ccgpu.CC_ERR_INVALID_ARG   # send/recv overlap
-    assert _ar(ok_s, ok_r, 100, 3, cfg=ccgpu.Config(1, 0, None, 0)) == ccgpu.CC_ERR_UNSUPPORTED
-    assert _ar(ok_s, ok_r, 100, 6, cfg=ccgpu.Config(2, 0, None, 0)) == ccgpu.CC_ERR_UNSUPPORTED
-    assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(0, -1, None, 0)) == ccgpu.CC_ERR_INVALID_ARG
-    assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(5, 0, None, 0)) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 3, cfg=ccgpu.Config(1, 0, None, 0, 0)) == ccgpu.CC_ERR_UNSUPPORTED
+    assert _ar(ok_s, ok_r, 100, 6, cfg=ccgpu.Config(2, 0, None, 0, 0)) == ccgpu.CC_ERR_UNSUPPORTED
+    assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(0, -1, None, 0, 0)) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(5, 0, None, 0, 0)) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(0, 0, None, 0, -2)) == ccgpu.CC_ERR_INVALID_ARG
     # bf16 stepwise ring needs a workspace
-    assert _ar(ok_s, ok_r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, None, 0)) == ccgpu.CC_ERR_INVALID_ARG
-    assert _ar(ok_s, ok_r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, FAKE + (2 << 30), 399)) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, None, 0, 0)) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, FAKE + (2 << 30), 399, 0)) == ccgpu.CC_ERR_INVALID_ARG
     assert "workspace" in ccgpu.load().cc_last_error().decode()
     # interleaved send/recv rows in one allocation do not overlap: only the device is missing
     inter_s, inter_r = _rb(FAKE, 800), _rb(FAKE + 400, 800)
@@ -161,27 +162,27 @@ def test_valid_calls_report_no_device():
 @no_gpu_only
 def test_other_collectives_reject_bad_arguments():
     L = ccgpu.load()
-    cfg = ccgpu.Config(0, 0, None, 0)
+    cfg = ccgpu.Config(0, 0, None, 0, 0)
     s, r = _rb(FAKE, 1 << 20), _rb(FAKE + (1 << 30), 1 << 20)
     # reduce_scatter: butterfly undefined; HD needs 2^k; recv overlapping send
-    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 4, ctypes.byref(ccgpu.Config(2, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
-    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 3, ctypes.byref(ccgpu.Config(1, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 4, ctypes.byref(ccgpu.Config(2, 0, None, 0, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 3, ctypes.byref(ccgpu.Config(1, 0, None, 0, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
     assert L.cc_reduce_scatter(s, _rb(FAKE + 8, 1 << 20), 10, 1, 0, 4, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
-    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 4, ctypes.byref(ccgpu.Config(0, 1, None, 0)), None) == ccgpu.CC_ERR_INVALID_ARG  # ws
+    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 4, ctypes.byref(ccgpu.Config(0, 1, None, 0, 0)), None) == ccgpu.CC_ERR_INVALID_ARG  # ws
     # all_gather: recv stride too small for N*S elements
     assert L.cc_all_gather(s, _rb(FAKE + (1 << 30), 100), 10, 1, 4, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
-    assert L.cc_all_gather(s, r, 10, 1, 4, ctypes.byref(ccgpu.Config(2, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    assert L.cc_all_gather(s, r, 10, 1, 4, ctypes.byref(ccgpu.Config(2, 0, None, 0, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
     # broadcast: root out of range, butterfly
     assert L.cc_broadcast(s, r, 10, 1, 4, 4, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
     assert L.cc_broadcast(s, r, 10, 1, -1, 4, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
-    assert L.cc_broadcast(s, r, 10, 1, 0, 4, ctypes.byref(ccgpu.Config(2, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    assert L.cc_broadcast(s, r, 10, 1, 0, 4, ctypes.byref(ccgpu.Config(2, 0, None, 0, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
     # all_to_all: NULL counts, zero row, recv block does not fit the stride, HD
     counts = (ctypes.c_size_t * 4)(1, 2, 3, 4)
     assert L.cc_all_to_all(s, r, None, 1, 1, 2, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
     assert L.cc_all_to_all(s, r, counts, 0, 1, 2, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
     big = (ctypes.c_size_t * 4)(1, 1 << 20, 1, 1)
     assert L.cc_all_to_all(s, r, big, 1, 1, 2, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
-    assert L.cc_all_to_all(s, r, counts, 1, 1, 2, ctypes.byref(ccgpu.Config(1, 0, None, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
+    assert L.cc_all_to_all(s, r, counts, 1, 1, 2, ctypes.byref(ccgpu.Config(1, 0, None, 0, 0)), None) == ccgpu.CC_ERR_UNSUPPORTED
     assert L.cc_all_to_all(s, r, counts, 1, 1, 2, ctypes.byref(cfg), None) == ccgpu.CC_ERR_NO_DEVICE
 
 
