@@ -157,6 +157,35 @@ cc_status_t cc_all_to_all(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* co
                           size_t elem_per_row, cc_dtype_t dtype, int nranks,
                           const cc_config_t* cfg, cc_stream_t stream);
 
+/* Bucketed AllReduce (textbook ch. 6, "Bucket fusion": gradients grouped into
+ * buckets, one AllReduce per bucket).  Bucket b is the element range
+ * [offsets[b], offsets[b] + counts[b]) of every rank's buffer; each bucket is
+ * all-reduced on its own, with its own N chunks, exactly as cc_all_reduce on
+ * that range would do (same bits).  Buckets must not overlap; empty buckets
+ * are skipped.  The fused schedules (fuse_depth 0) with nranks <= 16 run up
+ * to 16 buckets per kernel launch; otherwise each bucket runs as its own
+ * cc_all_reduce.  A stepwise schedule's workspace is sized by
+ * cc_workspace_size(CC_COLL_ALL_REDUCE, ..., largest bucket count, ...).
+ * offsets and counts are host arrays of nbuckets entries.  Errors as for
+ * cc_all_reduce, plus CC_ERR_INVALID_ARG for overlapping buckets or a bucket
+ * beyond the rank stride. */
+cc_status_t cc_all_reduce_buckets(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* offsets,
+                                  const size_t* counts, int nbuckets, cc_dtype_t dtype, cc_op_t op,
+                                  int nranks, const cc_config_t* cfg, cc_stream_t stream);
+
+/* Host-side bucket plan for cc_all_reduce_buckets (textbook ch. 6, "Bucket
+ * fusion": parameters in reverse forward order, buckets of about 25 MB).
+ * Tensors t = ntensors-1 .. 0 are packed greedily: a bucket is closed when
+ * the next tensor would push it past cap_bytes, a tensor larger than the cap
+ * gets a bucket of its own; tensors sit back to back inside a bucket, and
+ * each bucket starts at a multiple of align_elems elements.  Outputs (host
+ * arrays the caller owns, each with room for ntensors entries):
+ * bucket_of[t], tensor_offset[t] (element offset in the per-rank flat
+ * buffer), bucket_offset[b], bucket_count[b], and *nbuckets.  No device work. */
+cc_status_t cc_bucket_plan(const size_t* sizes, int ntensors, size_t elem_bytes, size_t cap_bytes,
+                           size_t align_elems, int* bucket_of, size_t* tensor_offset,
+                           size_t* bucket_offset, size_t* bucket_count, int* nbuckets);
+
 /* Bytes of caller-owned device workspace the given collective needs.  count is
  * the per-rank element count of the collective's own count argument. */
 cc_status_t cc_workspace_size(cc_coll_t coll, const cc_config_t* cfg, int nranks, size_t count,

@@ -59,6 +59,12 @@ EXPORTS = {
                      ctypes.POINTER(Config), ctypes.c_void_p],
     "cc_all_to_all": [RankBuf, RankBuf, ctypes.POINTER(ctypes.c_size_t), ctypes.c_size_t, ctypes.c_int,
                       ctypes.c_int, ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_all_reduce_buckets": [RankBuf, RankBuf, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t),
+                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(Config),
+                              ctypes.c_void_p],
+    "cc_bucket_plan": [ctypes.POINTER(ctypes.c_size_t), ctypes.c_int, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_size_t,
+                       ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t),
+                       ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int)],
     "cc_workspace_size": [ctypes.c_int, ctypes.POINTER(Config), ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
                           ctypes.POINTER(ctypes.c_size_t)],
     "cc_get_traffic": [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
@@ -165,6 +171,41 @@ def all_reduce(send, recv=None, op: str = "sum", algo: str = "ring", fuse_depth:
     cfg = config(algo, fuse_depth, workspace, blocks_per_cu)
     _check(load().cc_all_reduce(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], OPS[op], N,
                                 ctypes.byref(cfg), _stream(stream)))
+
+
+def bucket_plan(sizes: Sequence[int], elem_bytes: int, cap_bytes: int, align_elems: int = 1):
+    """Host bucket plan (cc_bucket_plan): returns (bucket_of, tensor_offset,
+    bucket_offset, bucket_count) as Python lists."""
+    n = len(sizes)
+    cap = max(n, 1)
+    sz = (ctypes.c_size_t * cap)(*[int(v) for v in sizes])
+    bof = (ctypes.c_int * cap)()
+    toff = (ctypes.c_size_t * cap)()
+    boff = (ctypes.c_size_t * cap)()
+    bcnt = (ctypes.c_size_t * cap)()
+    nb = ctypes.c_int(0)
+    _check(load().cc_bucket_plan(sz, n, elem_bytes, cap_bytes, align_elems, bof, toff, boff, bcnt, ctypes.byref(nb)))
+    k = nb.value
+    return list(bof)[:n], list(toff)[:n], list(boff)[:k], list(bcnt)[:k]
+
+
+def all_reduce_buckets(send, recv, offsets: Sequence[int], counts: Sequence[int], op: str = "sum",
+                       algo: str = "ring", fuse_depth: int = 0, workspace=None, stream=None,
+                       blocks_per_cu: int = 0) -> None:
+    """Independent AllReduces over element ranges [offsets[b], +counts[b]) of
+    the [N, L] rank buffers (cc_all_reduce_buckets)."""
+    recv = send if recv is None else recv
+    N = send.shape[0]
+    if tuple(recv.shape) != tuple(send.shape) or recv.dtype != send.dtype:
+        raise ValueError("recv must match send")
+    nb = len(offsets)
+    if len(counts) != nb:
+        raise ValueError("offsets and counts differ in length")
+    off = (ctypes.c_size_t * max(nb, 1))(*[int(v) for v in offsets])
+    cnt = (ctypes.c_size_t * max(nb, 1))(*[int(v) for v in counts])
+    cfg = config(algo, fuse_depth, workspace, blocks_per_cu)
+    _check(load().cc_all_reduce_buckets(rankbuf(send), rankbuf(recv), off, cnt, nb, DTYPES[dtype_name(send)],
+                                        OPS[op], N, ctypes.byref(cfg), _stream(stream)))
 
 
 def reduce_scatter(send, recv, op: str = "sum", algo: str = "ring", fuse_depth: int = 0,

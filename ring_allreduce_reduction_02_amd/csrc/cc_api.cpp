@@ -166,6 +166,9 @@ cc_status_t copy_ranks(const cc_rankbuf_t& src, const cc_rankbuf_t& dst, uint64_
   return ok();
 }
 
+cc_status_t run_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, uint64_t M, int dt, int op, int N,
+                           const cc_config_t& cfg, hipStream_t st);
+
 }  // namespace
 
 extern "C" {
@@ -211,7 +214,19 @@ cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc
   if ((s = grid_fits(M, dt))) return s;
   if ((s = check_ws(CC_COLL_ALL_REDUCE, cfg, N, M, dt))) return s;
   if ((s = device_ready())) return s;
-  hipStream_t st = (hipStream_t)stream;
+  return run_all_reduce(send, recv, M, dt, (int)op, N, cfg, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// An AllReduce whose arguments are validated.
+cc_status_t run_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, uint64_t M, int dt, int op, int N,
+                           const cc_config_t& cfg, hipStream_t st) {
+  const int es = elem_size(dt);
+  const uint64_t nb = M * es;
+  const bool in_place = same_side(send, recv);
   if (N == 1) return in_place ? ok() : copy_ranks(send, recv, nb, 1, es, cfg.blocks_per_cu, st);
 
   const Bounds bd(M, N);
@@ -224,7 +239,7 @@ cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc
   r.blocks_per_cu = cfg.blocks_per_cu;
   r.N = N;
   r.dt = dt;
-  r.op = (int)op;
+  r.op = op;
   r.rs_mode = 0;
   r.vec_ok = al16p(send.base) && al16(send.rank_stride_bytes) && al16p(recv.base) && al16(recv.rank_stride_bytes) &&
              (cfg.workspace == nullptr || al16p(cfg.workspace));
@@ -251,6 +266,115 @@ cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc
   }
   for (int d = 1; d < N && e == hipSuccess; d *= 2) e = launch_bfly_step(r, d, d == 1, 2 * d == N, acc_recv);
   return hip_status(e, "butterfly all_reduce (stepwise)");
+}
+
+}  // namespace
+
+extern "C" {
+
+cc_status_t cc_all_reduce_buckets(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* offsets, const size_t* counts,
+                                  int nbuckets, cc_dtype_t dtype, cc_op_t op, int nranks, const cc_config_t* cfgp,
+                                  cc_stream_t stream) {
+  const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
+  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  if (s) return s;
+  if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
+  const int N = nranks, dt = (int)dtype, es = elem_size(dt);
+  if (cfg.algo != CC_ALGO_RING && !is_pow2(N))
+    return fail(CC_ERR_UNSUPPORTED, "halving-doubling and butterfly need nranks = 2^k (got %d)", N);
+  if (nbuckets < 0) return fail(CC_ERR_INVALID_ARG, "nbuckets=%d is negative", nbuckets);
+  if (nbuckets == 0) return ok();
+  if (!offsets || !counts) return fail(CC_ERR_INVALID_ARG, "offsets or counts is NULL");
+  // buckets: non-empty ranges, pairwise disjoint, within every rank buffer
+  std::vector<std::pair<uint64_t, uint64_t>> rg;
+  uint64_t extent = 0, maxlen = 0;
+  for (int b = 0; b < nbuckets; ++b) {
+    if (counts[b] == 0) continue;
+    const unsigned __int128 end = (unsigned __int128)offsets[b] + counts[b];
+    if (end >> 60) return fail(CC_ERR_INVALID_ARG, "bucket %d out of range", b);
+    rg.push_back({offsets[b], (uint64_t)end});
+    extent = std::max(extent, (uint64_t)end);
+    maxlen = std::max(maxlen, (uint64_t)counts[b]);
+  }
+  if (rg.empty()) return ok();
+  std::vector<std::pair<uint64_t, uint64_t>> sorted = rg;
+  std::sort(sorted.begin(), sorted.end());
+  for (size_t i = 1; i < sorted.size(); ++i)
+    if (sorted[i].first < sorted[i - 1].second) return fail(CC_ERR_INVALID_ARG, "buckets overlap");
+  const uint64_t nb = extent * es;
+  if ((s = check_side(send, nb, N, "send")) || (s = check_side(recv, nb, N, "recv"))) return s;
+  const bool in_place = same_side(send, recv);
+  if (!in_place && sides_overlap(send, nb, N, recv, nb, N))
+    return fail(CC_ERR_INVALID_ARG, "send and recv overlap without being the same buffers");
+  if ((s = grid_fits(maxlen, dt))) return s;
+  if ((s = check_ws(CC_COLL_ALL_REDUCE, cfg, N, maxlen, dt))) return s;
+  if ((s = device_ready())) return s;
+  hipStream_t st = (hipStream_t)stream;
+  auto sub = [&](const cc_rankbuf_t& x, uint64_t off) {
+    return cc_rankbuf_t{(char*)x.base + off * es, x.rank_stride_bytes};
+  };
+  const bool one_launch = cfg.fuse_depth == 0 && N > 1 && N <= kMaxSegRanks && maxlen < (1ull << 32) &&
+                          num_tiles(maxlen, dt) * kMaxSeg < 0x7fffffffull;
+  if (!one_launch) {
+    for (const auto& r : rg)
+      if ((s = run_all_reduce(sub(send, r.first), sub(recv, r.first), r.second - r.first, dt, (int)op, N, cfg, st)))
+        return s;
+    return ok();
+  }
+  SegLaunch L;
+  L.send = side(send);
+  L.recv = side(recv);
+  L.N = N;
+  L.dt = dt;
+  L.op = (int)op;
+  L.alg = (int)cfg.algo;
+  L.blocks_per_cu = cfg.blocks_per_cu;
+  L.st = st;
+  for (size_t i = 0; i < rg.size(); i += kMaxSeg) {
+    L.nseg = (int)std::min<size_t>(kMaxSeg, rg.size() - i);
+    for (int k = 0; k < L.nseg; ++k) {
+      L.off[k] = rg[i + k].first;
+      L.len[k] = rg[i + k].second - rg[i + k].first;
+    }
+    hipError_t e = launch_fused_seg(L);
+    if (e != hipSuccess) return hip_status(e, "bucketed all_reduce");
+  }
+  return ok();
+}
+
+cc_status_t cc_bucket_plan(const size_t* sizes, int ntensors, size_t elem_bytes, size_t cap_bytes,
+                           size_t align_elems, int* bucket_of, size_t* tensor_offset, size_t* bucket_offset,
+                           size_t* bucket_count, int* nbuckets) {
+  if (ntensors < 0) return fail(CC_ERR_INVALID_ARG, "ntensors=%d is negative", ntensors);
+  if (!nbuckets) return fail(CC_ERR_INVALID_ARG, "nbuckets is NULL");
+  if (ntensors > 0 && (!sizes || !bucket_of || !tensor_offset || !bucket_offset || !bucket_count))
+    return fail(CC_ERR_INVALID_ARG, "NULL array");
+  if (elem_bytes == 0 || align_elems == 0) return fail(CC_ERR_INVALID_ARG, "elem_bytes and align_elems must be > 0");
+  // reverse order (the order gradients become ready in backward), greedy:
+  // close the bucket when the next tensor would push it past the cap; a
+  // tensor larger than the cap gets a bucket of its own
+  int nb = 0;
+  uint64_t cur_bytes = 0, pos = 0;
+  for (int t = ntensors - 1; t >= 0; --t) {
+    const unsigned __int128 tb = (unsigned __int128)sizes[t] * elem_bytes;
+    if (tb >> 60) return fail(CC_ERR_INVALID_ARG, "tensor %d too large", t);
+    if (nb == 0 || (cur_bytes > 0 && cur_bytes + (uint64_t)tb > cap_bytes)) {
+      // open a new bucket at the next aligned offset
+      const uint64_t start = nb == 0 ? 0 : rup(bucket_offset[nb - 1] + bucket_count[nb - 1], align_elems);
+      bucket_offset[nb] = start;
+      bucket_count[nb] = 0;
+      pos = start;
+      cur_bytes = 0;
+      ++nb;
+    }
+    bucket_of[t] = nb - 1;
+    tensor_offset[t] = pos;
+    pos += sizes[t];
+    bucket_count[nb - 1] += sizes[t];
+    cur_bytes += (uint64_t)tb;
+  }
+  *nbuckets = nb;
+  return ok();
 }
 
 cc_status_t cc_reduce_scatter(cc_rankbuf_t send, cc_rankbuf_t recv, size_t recvcount, cc_dtype_t dtype, cc_op_t op,

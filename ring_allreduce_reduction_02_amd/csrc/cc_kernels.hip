@@ -228,106 +228,7 @@ __device__ __forceinline__ uint64_t vec_elem(uint64_t e0, int u, int V) {
   return e0 + ((uint64_t)u * kBlock + threadIdx.x) * (uint64_t)V;
 }
 
-// ------------------------------------------------------------------ fused ring
-
-struct FusedArgs {
-  const char* sb;
-  uint64_t ss;
-  char* rb;
-  uint64_t rs;
-  uint64_t M;
-  int N;
-  int rs_mode;
-  int vec_ok;
-  uint64_t bnd[kMaxRanks + 1];
-};
-
-// AllReduce (rs_mode 0): the N-1 ReduceScatter steps of each chunk folded in
-// registers in ring order, then the AllGather as N stores.  ReduceScatter
-// (rs_mode 1): the fold starts one rank later and only the owner is written.
-template <int DT, int OP, int NR>
-__global__ __launch_bounds__(kBlock) void k_ring_fused(FusedArgs a) {
-  typedef typename Ty<DT>::A A;
-  constexpr int V = Ty<DT>::V;
-  constexpr int SZ = Ty<DT>::SZ;
-  static_assert(kUnroll == 1, "one 16-byte vector per thread");
-  const int N = NR > 0 ? NR : a.N;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
-  if (t.fast) {
-    // Every rank's tile starts at a workgroup-uniform address; a lane adds
-    // its own 16-byte offset (scalar base + 32-bit vector offset).
-    const int c = (int)t.c;
-    const int start = a.rs_mode ? wrapN(c + 1, N) : c;
-    const uint32_t lane = threadIdx.x * 16u;
-    const uint64_t eb = t.e0 * SZ;
-    const char* const s0 = a.sb + eb;
-    A acc[V];
-    if constexpr (NR > 0) {
-      u32x4 raw[NR];
-      const char* p = s0 + (uint64_t)start * a.ss;
-#pragma unroll
-      for (int j = 0; j < NR; ++j) {
-        raw[j] = ldg(p + lane);
-        p = (start + j + 1 == NR) ? s0 : p + a.ss;
-      }
-      unpack<DT>(raw[0], acc);
-#pragma unroll
-      for (int j = 1; j < NR; ++j) {
-        A x[V];
-        unpack<DT>(raw[j], x);
-        opv<DT, OP>(x, acc);
-      }
-    } else {
-      const char* p = s0 + (uint64_t)start * a.ss;
-      unpack<DT>(ldg(p + lane), acc);
-      int r = start;
-      for (int j = 1; j < N; j += 8) {
-        u32x4 raw[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (j + q < N) {
-            r = r + 1 == N ? 0 : r + 1;
-            p = r == 0 ? s0 : p + a.ss;
-            raw[q] = ldg(p + lane);
-          }
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (j + q < N) {
-            A x[V];
-            unpack<DT>(raw[q], x);
-            opv<DT, OP>(x, acc);
-          }
-      }
-    }
-    const u32x4 w = pack<DT>(acc);
-    if (a.rs_mode) {
-      stg(a.rb + (uint64_t)c * a.rs + (t.e0 - a.bnd[c]) * SZ + lane, w);
-    } else {
-      char* d = a.rb + eb;
-      if constexpr (NR > 0) {
-#pragma unroll
-        for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
-      } else {
-        for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
-      }
-    }
-  } else {
-    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = chunk_in(a.bnd, N, e);
-      const int start = a.rs_mode ? wrapN((int)c + 1, N) : (int)c;
-      A acc = ld1<DT>(a.sb + (uint64_t)start * a.ss + e * SZ);
-      for (int j = 1; j < N; ++j)
-        acc = opf<DT, OP>(ld1<DT>(a.sb + (uint64_t)wrapN(start + j, N) * a.ss + e * SZ), acc);
-      if (a.rs_mode) {
-        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, acc);
-      } else {
-        for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc);
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ fused trees
+// ------------------------------------------------------------------ fold orders
 
 template <int L>
 __device__ constexpr int bitrev(int t) {
@@ -382,41 +283,209 @@ __device__ __forceinline__ void tree_fold(Load load, typename Ty<DT>::A* out, in
     if (i < V) out[i] = stk[L][i];
 }
 
-template <int DT, int OP, int NR, int TREE>
-__global__ __launch_bounds__(kBlock) void k_tree_fused(FusedArgs a) {
+enum Alg { ALG_RING = 0, ALG_HD = 1, ALG_BFLY = 2 };
+
+// Fold of one 16-byte vector of every rank, rank r's vector at
+// s0 + r*ss + lane (s0 and ss workgroup-uniform, lane the lane's offset).
+// Ring: the chain x_start, x_start+1, ... folded as acc = op(x_next, acc);
+// trees: as above.  N is NR when NR > 0.
+template <int DT, int OP, int NR, int ALG>
+__device__ __forceinline__ void fold_vec(const char* s0, uint64_t ss, int N, int start, uint32_t lane,
+                                         typename Ty<DT>::A* acc) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  if constexpr (ALG != ALG_RING) {
+    tree_fold<DT, OP, NR, ALG == ALG_HD ? TREE_HD : TREE_BFLY>(
+        [&](int r, A* v) { unpack<DT>(ldg(s0 + (uint64_t)r * ss + lane), v); }, acc, V);
+  } else if constexpr (NR > 0) {
+    u32x4 raw[NR];
+    const char* p = s0 + (uint64_t)start * ss;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      raw[j] = ldg(p + lane);
+      p = (start + j + 1 == NR) ? s0 : p + ss;
+    }
+    unpack<DT>(raw[0], acc);
+#pragma unroll
+    for (int j = 1; j < NR; ++j) {
+      A x[V];
+      unpack<DT>(raw[j], x);
+      opv<DT, OP>(x, acc);
+    }
+  } else {
+    const char* p = s0 + (uint64_t)start * ss;
+    unpack<DT>(ldg(p + lane), acc);
+    int r = start;
+    for (int j = 1; j < N; j += 8) {
+      u32x4 raw[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (j + q < N) {
+          r = r + 1 == N ? 0 : r + 1;
+          p = r == 0 ? s0 : p + ss;
+          raw[q] = ldg(p + lane);
+        }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (j + q < N) {
+          A x[V];
+          unpack<DT>(raw[q], x);
+          opv<DT, OP>(x, acc);
+        }
+    }
+  }
+}
+
+// The same fold for one element at byte offset `off` of every rank.
+template <int DT, int OP, int NR, int ALG>
+__device__ __forceinline__ typename Ty<DT>::A fold_elem(const char* sb, uint64_t ss, int N, int start,
+                                                        uint64_t off) {
+  typedef typename Ty<DT>::A A;
+  if constexpr (ALG != ALG_RING) {
+    A acc[Ty<DT>::V];
+    tree_fold<DT, OP, NR, ALG == ALG_HD ? TREE_HD : TREE_BFLY>(
+        [&](int r, A* v) { v[0] = ld1<DT>(sb + (uint64_t)r * ss + off); }, acc, 1);
+    return acc[0];
+  } else {
+    A acc = ld1<DT>(sb + (uint64_t)start * ss + off);
+    for (int j = 1; j < N; ++j) acc = opf<DT, OP>(ld1<DT>(sb + (uint64_t)wrapN(start + j, N) * ss + off), acc);
+    return acc;
+  }
+}
+
+// ------------------------------------------------------------------ fused kernels
+
+struct FusedArgs {
+  const char* sb;
+  uint64_t ss;
+  char* rb;
+  uint64_t rs;
+  uint64_t M;
+  int N;
+  int rs_mode;
+  int vec_ok;
+  uint64_t bnd[kMaxRanks + 1];
+};
+
+// AllReduce (rs_mode 0): every chunk's N-1 ReduceScatter steps folded in
+// registers in the schedule's order, then the AllGather as N stores.
+// ReduceScatter (rs_mode 1, ring and halving-doubling): only the owner is
+// written; the ring's fold then starts one rank later.
+template <int DT, int OP, int NR, int ALG>
+__device__ __forceinline__ void fused_body(const FusedArgs& a) {
   typedef typename Ty<DT>::A A;
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
   static_assert(kUnroll == 1, "one 16-byte vector per thread");
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, NR, a.vec_ok);
+  const int N = NR > 0 ? NR : a.N;
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
+    // Every rank's tile starts at a workgroup-uniform address; a lane adds
+    // its own 16-byte offset (scalar base + 32-bit vector offset).
     const int c = (int)t.c;
+    const int start = (ALG == ALG_RING && a.rs_mode) ? wrapN(c + 1, N) : c;
     const uint32_t lane = threadIdx.x * 16u;
     const uint64_t eb = t.e0 * SZ;
-    const char* const s0 = a.sb + eb;
     A acc[V];
-    tree_fold<DT, OP, NR, TREE>(
-        [&](int r, A* v) { unpack<DT>(ldg(s0 + (uint64_t)r * a.ss + lane), v); }, acc, V);
+    fold_vec<DT, OP, NR, ALG>(a.sb + eb, a.ss, N, start, lane, acc);
     const u32x4 w = pack<DT>(acc);
     if (a.rs_mode) {
       stg(a.rb + (uint64_t)c * a.rs + (t.e0 - a.bnd[c]) * SZ + lane, w);
     } else {
       char* d = a.rb + eb;
+      if constexpr (NR > 0) {
 #pragma unroll
-      for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
+        for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
+      } else {
+        for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
+      }
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      A acc[V];
-      tree_fold<DT, OP, NR, TREE>(
-          [&](int r, A* v) { v[0] = ld1<DT>(a.sb + (uint64_t)r * a.ss + e * SZ); }, acc, 1);
+      const uint32_t c = chunk_in(a.bnd, N, e);
+      const int start = (ALG == ALG_RING && a.rs_mode) ? wrapN((int)c + 1, N) : (int)c;
+      const A acc = fold_elem<DT, OP, NR, ALG>(a.sb, a.ss, N, start, e * SZ);
       if (a.rs_mode) {
-        const uint32_t c = chunk_in(a.bnd, NR, e);
-        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, acc[0]);
+        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, acc);
       } else {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc[0]);
+        for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc);
       }
+    }
+  }
+}
+
+template <int DT, int OP, int NR>
+__global__ __launch_bounds__(kBlock) void k_ring_fused(FusedArgs a) {
+  fused_body<DT, OP, NR, ALG_RING>(a);
+}
+
+template <int DT, int OP, int NR, int TREE>
+__global__ __launch_bounds__(kBlock) void k_tree_fused(FusedArgs a) {
+  fused_body<DT, OP, NR, TREE == TREE_HD ? ALG_HD : ALG_BFLY>(a);
+}
+
+// ------------------------------------------------------------------ bucketed AllReduce
+
+// Up to kMaxSeg independent AllReduces over element ranges (buckets) of the
+// same rank buffers; bucket k has its own N chunks (boundaries relative to
+// the bucket start).  Workgroup b works on tile (b - tile0[k]) of bucket k.
+struct SegArgs {
+  const char* sb;
+  uint64_t ss;
+  char* rb;
+  uint64_t rs;
+  int N;
+  int nseg;
+  uint32_t vecmask;                           // bit k: bucket k's start is 16-byte aligned
+  uint32_t tile0[kMaxSeg + 1];                // prefix sums of tiles per bucket
+  uint64_t off[kMaxSeg];                      // element offset of bucket k in every rank buffer
+  uint32_t bnd[kMaxSeg][kMaxSegRanks + 1];    // chunk boundaries of bucket k, relative to it
+};
+
+template <int DT, int OP, int NR, int ALG>
+__global__ __launch_bounds__(kBlock) void k_fused_seg(SegArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const int N = NR > 0 ? NR : a.N;
+  const uint32_t b = blockIdx.x;
+  int lo = 0, hi = a.nseg;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (b >= a.tile0[mid]) lo = mid; else hi = mid;
+  }
+  const int k = lo;
+  const uint32_t* bk = a.bnd[k];
+  const uint64_t len = bk[N];
+  const uint64_t tile = (uint64_t)kBlock * V;
+  const uint64_t e0 = (uint64_t)(b - a.tile0[k]) * tile;
+  const uint64_t e1 = e0 + tile < len ? e0 + tile : len;
+  uint32_t c0 = 0, c1 = 0;
+  for (int i = 1; i < N; ++i) {
+    c0 += bk[i] <= e0 ? 1u : 0u;
+    c1 += bk[i] <= e1 - 1 ? 1u : 0u;
+  }
+  const uint64_t base = a.off[k];
+  if (((a.vecmask >> k) & 1) && e1 - e0 == tile && c0 == c1) {
+    const uint32_t lane = threadIdx.x * 16u;
+    const uint64_t eb = (base + e0) * SZ;
+    A acc[V];
+    fold_vec<DT, OP, NR, ALG>(a.sb + eb, a.ss, N, (int)c0, lane, acc);
+    const u32x4 w = pack<DT>(acc);
+    char* d = a.rb + eb;
+    if constexpr (NR > 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
+    } else {
+      for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
+    }
+  } else {
+    for (uint64_t e = e0 + threadIdx.x; e < e1; e += kBlock) {
+      uint32_t c = 0;
+      for (int i = 1; i < N; ++i) c += bk[i] <= e ? 1u : 0u;
+      const uint64_t off = (base + e) * SZ;
+      const A acc = fold_elem<DT, OP, NR, ALG>(a.sb, a.ss, N, (int)c, off);
+      for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + off, acc);
     }
   }
 }
@@ -1059,6 +1128,54 @@ hipError_t launch_copies(const CopyDesc* d, int n, int esize, int blocks_per_cu,
   const unsigned lds = blocks_per_cu > 0 ? lds_for_blocks_per_cu(blocks_per_cu) : 0;
   hipLaunchKernelGGL(k_copies, grid, blk, lds, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_fused_seg(const SegLaunch& L) {
+  SegArgs a;
+  a.sb = L.send.base; a.ss = L.send.stride;
+  a.rb = L.recv.base; a.rs = L.recv.stride;
+  a.N = L.N; a.nseg = L.nseg; a.vecmask = 0;
+  const int es = elem_size(L.dt);
+  const uint64_t tile = (uint64_t)kBlock * vec_elems(L.dt);
+  const bool sides_al = ((((uintptr_t)L.send.base | (uintptr_t)L.recv.base | L.send.stride | L.recv.stride) & 15u) == 0);
+  a.tile0[0] = 0;
+  for (int k = 0; k < L.nseg; ++k) {
+    a.off[k] = L.off[k];
+    for (int c = 0; c <= L.N; ++c) a.bnd[k][c] = (uint32_t)(((unsigned __int128)c * L.len[k]) / (unsigned)L.N);
+    a.tile0[k + 1] = a.tile0[k] + (uint32_t)((L.len[k] + tile - 1) / tile);
+    if (sides_al && ((L.off[k] * es) & 15u) == 0) a.vecmask |= 1u << k;
+  }
+  if (a.tile0[L.nseg] == 0) return hipSuccess;
+  const dim3 grid(a.tile0[L.nseg]), blk(kBlock);
+  const unsigned lds = occupancy_lds(L.blocks_per_cu, (uint64_t)kBlock * 16 * L.N);
+  return by_dt_op(L.dt, L.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    if (L.alg == ALG_RING) {
+      switch (L.N) {
+        case 4: hipLaunchKernelGGL((k_fused_seg<DT, OP, 4, ALG_RING>), grid, blk, lds, L.st, a); break;
+        case 8: hipLaunchKernelGGL((k_fused_seg<DT, OP, 8, ALG_RING>), grid, blk, lds, L.st, a); break;
+        case 16: hipLaunchKernelGGL((k_fused_seg<DT, OP, 16, ALG_RING>), grid, blk, lds, L.st, a); break;
+        default: hipLaunchKernelGGL((k_fused_seg<DT, OP, 0, ALG_RING>), grid, blk, lds, L.st, a); break;
+      }
+    } else {
+#define CC_SEG_CASE(NR)                                                                        \
+  case NR:                                                                                     \
+    if (L.alg == ALG_HD)                                                                       \
+      hipLaunchKernelGGL((k_fused_seg<DT, OP, NR, ALG_HD>), grid, blk, lds, L.st, a);          \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_fused_seg<DT, OP, NR, ALG_BFLY>), grid, blk, lds, L.st, a);        \
+    break;
+      switch (L.N) {
+        CC_SEG_CASE(2)
+        CC_SEG_CASE(4)
+        CC_SEG_CASE(8)
+        CC_SEG_CASE(16)
+        default: return hipErrorInvalidValue;
+      }
+#undef CC_SEG_CASE
+    }
+    return hipGetLastError();
+  });
 }
 
 }  // namespace cc

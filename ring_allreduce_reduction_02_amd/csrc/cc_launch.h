@@ -69,6 +69,25 @@ hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_i
 // butterfly step with distance d.
 hipError_t launch_bfly_step(const Red& r, int d, int first, int last, int acc_in_recv);
 
+// ---- bucketed AllReduce: up to kMaxSeg independent fused AllReduces over
+// element ranges [off, off+len) of the same rank buffers, in one launch.
+constexpr int kMaxSeg = 16;
+constexpr int kMaxSegRanks = 16;
+struct SegLaunch {
+  Side send;
+  Side recv;
+  int N;
+  int dt;
+  int op;
+  int alg;          // 0 ring, 1 halving-doubling, 2 butterfly
+  int blocks_per_cu;
+  int nseg;
+  uint64_t off[kMaxSeg];
+  uint64_t len[kMaxSeg];   // each < 2^32
+  hipStream_t st;
+};
+hipError_t launch_fused_seg(const SegLaunch& s);
+
 // ---- gathers (no arithmetic).  ag_mode 0: AllGather phase of an AllReduce,
 // everything in recv; 1: standalone AllGather, rank c's shard in send.
 struct Gat {
