@@ -81,6 +81,35 @@ def time_launches(fn, steps, warmup):
     return {"total_ms": t0.elapsed_time(t1), "per_launch_ms": per, "wall_s": wall}
 
 
+def time_graph(fn, reps=20, per_graph=1):
+    """GPU time per call of fn without host launch overhead: `per_graph` calls
+    captured into one HIP graph (torch.cuda.CUDAGraph), replayed `reps` times
+    between HIP events.  The captured kernels are the library's own (no
+    memset nodes)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * per_graph)
+
+
 def traffic_from_profile(nbytes_alg):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs,
     scaled by the copy-kernel calibration; None if the kernel changed."""
@@ -131,9 +160,11 @@ def cpu_baseline(N, M_sample, min_seconds=10.0, max_runs=25):
     }
 
 
-def alpha_beta(send, recv, N, steps=10, warmup=3):
+def alpha_beta(send, recv, N):
     """Stepwise ring (one kernel per ring step) over per-rank sizes from
-    4 KiB to 256 MiB; fit T = alpha * 2(N-1) + beta * bytes sent per rank."""
+    4 KiB to 256 MiB, GPU time from HIP-graph replays; fit
+    T = alpha * 2(N-1) + beta * bytes sent per rank.  The fused kernel's
+    T = t0 + bytes / BW is fitted on the same sizes."""
     from ring_allreduce_reduction_02_amd import calib, ccgpu
     M_full = send.shape[1]
     sizes = [1 << k for k in range(10, 27, 2)]   # elements: 1 Ki .. 64 Mi fp32 (4 KiB .. 256 MiB)
@@ -141,21 +172,109 @@ def alpha_beta(send, recv, N, steps=10, warmup=3):
     st, by, ts, pts, fused_b, fused_t = [], [], [], [], [], []
     for m in sizes:
         s, r = send[:, :m], recv[:, :m]
-        res = time_launches(lambda: ccgpu.all_reduce(s, r, algo="ring", fuse_depth=1), steps, warmup)
-        t = sorted(res["per_launch_ms"])[len(res["per_launch_ms"]) // 2] / 1e3
+        per = 16 if m <= (1 << 20) else 2
+        t = time_graph(lambda: ccgpu.all_reduce(s, r, algo="ring", fuse_depth=1), 10, per) / 1e3
         b, n = ccgpu.get_traffic("all_reduce", N, m, "f32", "ring")
         st.append(n); by.append(b); ts.append(t)
-        pts.append({"bytes_per_rank": m * 4, "stepwise_us": t * 1e6})
-        resf = time_launches(lambda: ccgpu.all_reduce(s, r, algo="ring", fuse_depth=0), steps, warmup)
-        tf = sorted(resf["per_launch_ms"])[len(resf["per_launch_ms"]) // 2] / 1e3
+        tf = time_graph(lambda: ccgpu.all_reduce(s, r, algo="ring", fuse_depth=0), 10, per) / 1e3
         fused_b.append(2 * N * m * 4); fused_t.append(tf)
-        pts[-1]["fused_us"] = tf * 1e6
+        pts.append({"bytes_per_rank": m * 4, "stepwise_us": round(t * 1e6, 3), "fused_us": round(tf * 1e6, 3)})
     fit = calib.fit_alpha_beta(st, by, ts)
     fit["fused_fit"] = calib.fit_fixed_plus_bandwidth(fused_b, fused_t)
     fit["nranks"] = N
-    fit["schedule"] = "ring, one kernel per step (fuse_depth=1), fp32 SUM"
+    fit["schedule"] = "ring, one kernel per step (fuse_depth=1), fp32 SUM; GPU time from HIP-graph replays"
     fit["points"] = pts
     return fit
+
+
+def _avg_ms(fn, steps=10, warmup=3):
+    r = time_launches(fn, steps, warmup)
+    return r["total_ms"] / steps
+
+
+def workloads(dev):
+    """The other workloads, timed with inputs resident in HBM (inputs drawn on
+    the device; their parity is checked by the tests).  GB/s = algorithmic
+    bytes / time."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu, synth
+    out = {}
+    gen = torch.Generator(device=dev).manual_seed(synth.SEED)
+
+    # int32 ring AllReduce, N=4, M=1,048,576 (32 MiB per call): one buffer set
+    # (cache-resident) and 32 rotating sets (1 GiB, beyond the 256 MB cache)
+    N, M = 4, 1 << 20
+    sets = [(torch.randint(-1000, 1001, (N, M), generator=gen, device=dev, dtype=torch.int32),
+             torch.empty(N, M, device=dev, dtype=torch.int32)) for _ in range(32)]
+    alg = 2 * N * M * 4
+    ms1 = time_graph(lambda: ccgpu.all_reduce(sets[0][0], sets[0][1]), 10, 32)
+
+    def rot():
+        for s_, r_ in sets:
+            ccgpu.all_reduce(s_, r_)
+    msr = time_graph(rot, 10, 1) / 32
+    host = _avg_ms(lambda: ccgpu.all_reduce(sets[0][0], sets[0][1]), 50, 10)
+    out["int32_ring_n4_m1048576"] = {"same_set_us": round(ms1 * 1e3, 2), "same_set_GBps": round(alg / ms1 / 1e6, 1),
+                                     "rotating_1GiB_us": round(msr * 1e3, 2),
+                                     "rotating_1GiB_GBps": round(alg / msr / 1e6, 1),
+                                     "eager_python_call_us": round(host * 1e3, 2),
+                                     "timing": "HIP-graph replays (GPU time); eager figure includes host launch cost"}
+    del sets
+    torch.cuda.empty_cache()
+
+    # bucketed bf16 gradient sync, N=8, 120 tensors in 25 MiB buckets
+    N = 8
+    sizes = synth.tensor_sizes_log_uniform()
+    _, _, boff, bcnt = ccgpu.bucket_plan(sizes, 2, 25 * 1024 * 1024, 128)
+    extent = boff[-1] + bcnt[-1]
+    send = (torch.randn(N, extent, generator=gen, device=dev) * 1e-2).to(torch.bfloat16)
+    recv = torch.empty_like(send)
+    alg = 2 * N * sum(bcnt) * 2
+    b = {"tensors": len(sizes), "buckets": len(boff), "elements_per_rank": sum(bcnt)}
+    for algo in ("ring", "hd", "butterfly"):
+        ms = _avg_ms(lambda: ccgpu.all_reduce_buckets(send, recv, boff, bcnt, algo=algo))
+        b[algo] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
+    ms = _avg_ms(lambda: [ccgpu.all_reduce(send[:, o:o + c], recv[:, o:o + c]) for o, c in zip(boff, bcnt)], 5, 2)
+    b["ring_one_launch_per_bucket"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
+    out["bucketed_bf16_n8"] = b
+    del send, recv
+    torch.cuda.empty_cache()
+
+    # ZeRO-3 style standalone ReduceScatter then AllGather, N=16, M=33,554,432 fp32
+    N, M = 16, 1 << 25
+    S = M // N
+    send = torch.rand(N, M, generator=gen, device=dev) * 2 - 1
+    shard = torch.empty(N, S, device=dev)
+    full = torch.empty(N, M, device=dev)
+    alg = (N + 1) * M * 4
+    z = {}
+    for algo in ("ring", "hd"):
+        ms = _avg_ms(lambda: ccgpu.reduce_scatter(send, shard, algo=algo))
+        z[f"reduce_scatter_{algo}"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
+    ms = _avg_ms(lambda: ccgpu.all_gather(shard, full))
+    z["all_gather"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
+    out["zero3_rs_ag_n16_m33554432_f32"] = z
+    del send, shard, full
+    torch.cuda.empty_cache()
+
+    # MoE AllToAll(v) dispatch and combine, N=8, 4096 tokens, top-8 of 64, hidden 7168 bf16
+    N, H = 8, 7168
+    C = synth.moe_counts(N)
+    Ls, Lr = int(C.sum(1).max()), int(C.sum(0).max())
+    send = torch.randn(N, Ls * H, generator=gen, device=dev).to(torch.bfloat16)
+    recv = torch.empty(N, Lr * H, device=dev, dtype=torch.bfloat16)
+    alg = 2 * int(C.sum()) * H * 2
+    m = {"rows_received": C.sum(0).tolist(), "skew_max_over_mean": round(float(C.sum(0).max() / C.sum(0).mean()), 3)}
+    for fd, name in ((0, "direct"), (1, "pairwise")):
+        ms = _avg_ms(lambda: ccgpu.all_to_all(send, recv, C.tolist(), H, fuse_depth=fd))
+        m[f"dispatch_{name}"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
+    ms = _avg_ms(lambda: ccgpu.all_to_all(recv, send, C.T.tolist(), H))
+    m["combine_direct"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
+    out["moe_alltoall_n8_t4096_h7168_bf16"] = m
+    del send, recv
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -172,7 +291,8 @@ def main():
     ap.add_argument("--blocks-per-cu", type=int, default=0, help="occupancy cap passed to the library (0 = its default)")
     ap.add_argument("--cpu-sample", type=int, default=67_108_864)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the bf16 twin and the alpha-beta calibration")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the bf16 twin, the alpha-beta calibration and the other workloads")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="before timing, run a plain device copy of this many bytes 3 times "
                          "(a known-size kernel for scaling HBM counters)")
@@ -284,6 +404,10 @@ def main():
         torch.cuda.empty_cache()
         log("alpha-beta calibration")
         out["alpha_beta"] = alpha_beta(send, recv, N)
+        del send, recv, ws
+        torch.cuda.empty_cache()
+        log("other workloads")
+        out["workloads"] = workloads(dev)
     if not args.no_cpu_baseline:
         log("oracle on the host")
         out["cpu_baseline"] = cpu_baseline(N, min(args.cpu_sample, M))

@@ -313,7 +313,7 @@ cc_status_t cc_all_reduce_buckets(cc_rankbuf_t send, cc_rankbuf_t recv, const si
   auto sub = [&](const cc_rankbuf_t& x, uint64_t off) {
     return cc_rankbuf_t{(char*)x.base + off * es, x.rank_stride_bytes};
   };
-  const bool one_launch = cfg.fuse_depth == 0 && N > 1 && N <= kMaxSegRanks && maxlen < (1ull << 32) &&
+  const bool one_launch = cfg.fuse_depth == 0 && N > 1 && N <= kMaxSegRanks && maxlen < (1ull << 31) &&
                           num_tiles(maxlen, dt) * kMaxSeg < 0x7fffffffull;
   if (!one_launch) {
     for (const auto& r : rg)

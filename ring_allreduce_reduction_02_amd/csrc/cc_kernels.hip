@@ -449,21 +449,33 @@ __global__ __launch_bounds__(kBlock) void k_fused_seg(SegArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   const int N = NR > 0 ? NR : a.N;
   const uint32_t b = blockIdx.x;
-  int lo = 0, hi = a.nseg;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (b >= a.tile0[mid]) lo = mid; else hi = mid;
-  }
-  const int k = lo;
+  // bucket of this workgroup: an unrolled scan, so the prefix loads are
+  // independent (one scalar-memory round trip instead of a search chain)
+  // (unused prefix entries hold 0x7fffffff, above any workgroup index)
+  // b >= t  <=>  the sign bit of t - 1 - b (all values < 2^31): integer
+  // arithmetic on the scalar unit, no per-compare vector round trip
+  uint32_t k = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSeg; ++i) k += (a.tile0[i] - 1u - b) >> 31;
   const uint32_t* bk = a.bnd[k];
   const uint64_t len = bk[N];
   const uint64_t tile = (uint64_t)kBlock * V;
   const uint64_t e0 = (uint64_t)(b - a.tile0[k]) * tile;
   const uint64_t e1 = e0 + tile < len ? e0 + tile : len;
-  uint32_t c0 = 0, c1 = 0;
-  for (int i = 1; i < N; ++i) {
-    c0 += bk[i] <= e0 ? 1u : 0u;
-    c1 += bk[i] <= e1 - 1 ? 1u : 0u;
+  // chunk count: f >= bnd  <=>  f - bnd >= 0 (bucket lengths are < 2^31)
+  const int32_t f0 = (int32_t)e0, f1 = (int32_t)(e1 - 1);
+  int32_t c0 = 0, c1 = 0;
+  if constexpr (NR > 0) {
+#pragma unroll
+    for (int i = 1; i < NR; ++i) {
+      c0 += 1 + ((f0 - (int32_t)bk[i]) >> 31);
+      c1 += 1 + ((f1 - (int32_t)bk[i]) >> 31);
+    }
+  } else {
+    for (int i = 1; i < N; ++i) {
+      c0 += 1 + ((f0 - (int32_t)bk[i]) >> 31);
+      c1 += 1 + ((f1 - (int32_t)bk[i]) >> 31);
+    }
   }
   const uint64_t base = a.off[k];
   if (((a.vecmask >> k) & 1) && e1 - e0 == tile && c0 == c1) {
@@ -953,28 +965,42 @@ unsigned lds_for_blocks_per_cu(int blocks) {
   if (blocks <= 0) return 0;
   const DevInfo i = dev_info();
   if (i.lds_per_cu <= 0 || i.lds_per_block <= 0) return 0;
-  unsigned lds = (unsigned)(i.lds_per_cu / blocks) & ~255u;
+  // rounded down to 2 KiB so the allocation granularity cannot round it up
+  // past LDS/blocks (which would leave room for one workgroup fewer)
+  unsigned lds = (unsigned)(i.lds_per_cu / blocks) & ~2047u;
   if (lds > (unsigned)i.lds_per_block) lds = (unsigned)i.lds_per_block;
   return lds;
 }
 
-// About 32 KiB of loads in flight per CU serves HBM best for these streams.
-int default_blocks_per_cu(uint64_t bytes_per_block) {
-  if (bytes_per_block == 0) return 0;
-  int b = (int)((32768 + bytes_per_block / 2) / bytes_per_block);
-  return b < 1 ? 1 : (b > 16 ? 16 : b);
+// Workgroups per CU for a kernel moving `traffic` bytes (loads + stores) per
+// workgroup, aiming at `target` bytes in flight per CU.  Measured on the
+// MI355X: a balanced read/write stream (fused AllReduce) streams best near
+// 64 KiB per CU, a read- or write-dominated one (ReduceScatter, AllGather)
+// near 144 KiB, broadcast near 72 KiB; more in flight thrashes the DRAM,
+// less leaves it idle.
+int default_blocks_per_cu(uint64_t traffic, uint64_t target, int min_blocks) {
+  if (traffic == 0) return 0;
+  int b = (int)((target + traffic / 2) / traffic);
+  if (b < min_blocks) b = min_blocks;
+  return b > 16 ? 16 : b;
 }
 
 namespace {
-unsigned occupancy_lds(int requested, uint64_t bytes_per_block) {
-  return lds_for_blocks_per_cu(requested > 0 ? requested : default_blocks_per_cu(bytes_per_block));
+constexpr uint64_t kBalancedTarget = 64 * 1024;
+constexpr uint64_t kSkewedTarget = 144 * 1024;
+constexpr uint64_t kBcastTarget = 72 * 1024;
+constexpr uint64_t kVecBytes = (uint64_t)kBlock * kUnroll * 16;   // one vector access of a workgroup
+
+unsigned occupancy_lds(int requested, uint64_t traffic, uint64_t target, int min_blocks = 1) {
+  return lds_for_blocks_per_cu(requested > 0 ? requested : default_blocks_per_cu(traffic, target, min_blocks));
 }
 }  // namespace
 
 hipError_t launch_ring_fused(const Red& r) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * r.N);
+  const unsigned lds = r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
+                                 : occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     switch (r.N) {
@@ -992,7 +1018,8 @@ hipError_t launch_ring_fused(const Red& r) {
 hipError_t launch_tree_fused(const Red& r, int tree) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * r.N);
+  const unsigned lds = r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
+                                 : occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
 #define CC_TREE_CASE(NR)                                                                      \
@@ -1025,7 +1052,7 @@ hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv)
   a.s0 = s0; a.k = k; a.pin_recv = partial_in_recv;
   for (int c = 0; c <= r.N; ++c) a.bnd[c] = r.bnd[c];
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * (k + 1));
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * (k + 2), kSkewedTarget);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     hipLaunchKernelGGL((k_ring_pass<DT, OP>), grid, blk, lds, r.st, a);
@@ -1047,7 +1074,7 @@ static StepArgs step_args(const Red& r, int d, int first, int last, int acc_in_r
 hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_in_recv) {
   const StepArgs a = step_args(r, d, first, last, acc_in_recv);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * 2 * d);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 3 * d, kSkewedTarget);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     hipLaunchKernelGGL((k_hd_rs_step<DT, OP>), grid, blk, lds, r.st, a);
@@ -1058,7 +1085,7 @@ hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_i
 hipError_t launch_bfly_step(const Red& r, int d, int first, int last, int acc_in_recv) {
   const StepArgs a = step_args(r, d, first, last, acc_in_recv);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = occupancy_lds(r.blocks_per_cu, (uint64_t)kBlock * kUnroll * 16 * r.N);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kSkewedTarget);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     hipLaunchKernelGGL((k_bfly_step<DT, OP>), grid, blk, lds, r.st, a);
@@ -1084,8 +1111,7 @@ static unsigned gat_tiles(const Gat& g) {
 hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k) {
   const GatArgs a = gat_args(g, s0, k);
   const dim3 grid(gat_tiles(g)), blk(kBlock);
-  // one load, k (or k+1) stores per thread: keep the reads deep
-  const unsigned lds = g.blocks_per_cu > 0 ? lds_for_blocks_per_cu(g.blocks_per_cu) : 0;
+  const unsigned lds = occupancy_lds(g.blocks_per_cu, kVecBytes * (k + 2), kSkewedTarget);
   if (g.esize == 2) hipLaunchKernelGGL((k_ring_ag_pass<2>), grid, blk, lds, g.st, a);
   else hipLaunchKernelGGL((k_ring_ag_pass<4>), grid, blk, lds, g.st, a);
   return hipGetLastError();
@@ -1096,7 +1122,7 @@ hipError_t launch_ag_fused(const Gat& g) { return launch_ring_ag_pass(g, 0, g.N 
 hipError_t launch_hd_ag_step(const Gat& g, int d, int first) {
   const GatArgs a = gat_args(g, d, first);
   const dim3 grid(gat_tiles(g)), blk(kBlock);
-  const unsigned lds = g.blocks_per_cu > 0 ? lds_for_blocks_per_cu(g.blocks_per_cu) : 0;
+  const unsigned lds = occupancy_lds(g.blocks_per_cu, kVecBytes * 2 * d, kSkewedTarget);
   if (g.esize == 2) hipLaunchKernelGGL((k_hd_ag_step<2>), grid, blk, lds, g.st, a);
   else hipLaunchKernelGGL((k_hd_ag_step<4>), grid, blk, lds, g.st, a);
   return hipGetLastError();
@@ -1108,7 +1134,8 @@ hipError_t launch_bcast(const char* src, Side dst, int N, int skip, uint64_t nby
   a.src = src; a.db = dst.base; a.ds = dst.stride; a.nbytes = nbytes;
   a.N = N; a.skip = skip; a.vec_ok = vec_ok;
   const dim3 grid((unsigned)((nbytes + kBcastTile - 1) / kBcastTile)), blk(kCopyBlock);
-  const unsigned lds = blocks_per_cu > 0 ? lds_for_blocks_per_cu(blocks_per_cu) : 0;
+  const int nw = skip >= 0 ? N - 1 : N;
+  const unsigned lds = occupancy_lds(blocks_per_cu, kBcastTile * (nw + 1), kBcastTarget);
   hipLaunchKernelGGL(k_bcast, grid, blk, lds, st, a);
   return hipGetLastError();
 }
@@ -1138,6 +1165,7 @@ hipError_t launch_fused_seg(const SegLaunch& L) {
   const int es = elem_size(L.dt);
   const uint64_t tile = (uint64_t)kBlock * vec_elems(L.dt);
   const bool sides_al = ((((uintptr_t)L.send.base | (uintptr_t)L.recv.base | L.send.stride | L.recv.stride) & 15u) == 0);
+  for (int k = 0; k <= kMaxSeg; ++k) a.tile0[k] = 0x7fffffffu;
   a.tile0[0] = 0;
   for (int k = 0; k < L.nseg; ++k) {
     a.off[k] = L.off[k];
@@ -1147,7 +1175,7 @@ hipError_t launch_fused_seg(const SegLaunch& L) {
   }
   if (a.tile0[L.nseg] == 0) return hipSuccess;
   const dim3 grid(a.tile0[L.nseg]), blk(kBlock);
-  const unsigned lds = occupancy_lds(L.blocks_per_cu, (uint64_t)kBlock * 16 * L.N);
+  const unsigned lds = occupancy_lds(L.blocks_per_cu, kVecBytes * 2 * L.N, kBalancedTarget, 2);
   return by_dt_op(L.dt, L.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     if (L.alg == ALG_RING) {

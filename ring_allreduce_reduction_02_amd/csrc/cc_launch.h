@@ -26,8 +26,9 @@ constexpr int kMaxRanks = 64;
 // LDS (the kernels do not use it); blocks_per_cu = 0 picks the default.
 // dynamic LDS bytes that limit a launch to `blocks` workgroups per CU
 unsigned lds_for_blocks_per_cu(int blocks);
-// default cap for a kernel that keeps `bytes_per_block` of loads in flight
-int default_blocks_per_cu(uint64_t bytes_per_block);
+// default cap for a kernel moving `traffic` bytes per workgroup, aiming at
+// `target` bytes in flight per CU, at least `min_blocks`
+int default_blocks_per_cu(uint64_t traffic, uint64_t target, int min_blocks);
 
 // Rank-strided view: rank r at base + r * stride (bytes).
 struct Side {
@@ -83,7 +84,7 @@ struct SegLaunch {
   int blocks_per_cu;
   int nseg;
   uint64_t off[kMaxSeg];
-  uint64_t len[kMaxSeg];   // each < 2^32
+  uint64_t len[kMaxSeg];   // each < 2^31
   hipStream_t st;
 };
 hipError_t launch_fused_seg(const SegLaunch& s);
