@@ -161,41 +161,116 @@ def cpu_baseline(N, M_sample, min_seconds=10.0, max_runs=25):
     }
 
 
-def alpha_beta(send, recv, N):
-    """Stepwise ring (one kernel per ring step) over per-rank sizes from
-    4 KiB to 256 MiB, GPU time from HIP-graph replays; fit
-    T = alpha * 2(N-1) + beta * bytes sent per rank.  The fused kernel's
-    T = t0 + bytes / BW is fitted on the same sizes."""
-    from ring_allreduce_reduction_02_amd import calib, ccgpu
-    M_full = send.shape[1]
-    sizes = [1 << k for k in range(10, 27, 2)]   # elements: 1 Ki .. 64 Mi fp32 (4 KiB .. 256 MiB)
-    sizes = [m for m in sizes if m <= M_full]
-    st, by, ts, pts, fused_b, fused_t = [], [], [], [], [], []
-    # steady clocks before the smallest, most clock-sensitive points
+def pad_sweep(src, N, M, dev, pads=(0, 256, 4096, 65_792), steps=10):
+    """The headline AllReduce with rank buffers `pad` bytes apart beyond the
+    payload (same data, copied on the device)."""
     import torch
-    for _ in range(40):
-        ccgpu.all_reduce(send, recv, algo="ring", fuse_depth=0)
-    torch.cuda.synchronize()
-    for m in sizes:
-        s, r = send[:, :m], recv[:, :m]
-        per = 16 if m <= (1 << 20) else 2
-        t = time_graph(lambda: ccgpu.all_reduce(s, r, algo="ring", fuse_depth=1), 10, per) / 1e3
-        b, n = ccgpu.get_traffic("all_reduce", N, m, "f32", "ring")
-        st.append(n); by.append(b); ts.append(t)
-        tf = time_graph(lambda: ccgpu.all_reduce(s, r, algo="ring", fuse_depth=0), 10, per) / 1e3
-        fused_b.append(2 * N * m * 4); fused_t.append(tf)
-        pts.append({"bytes_per_rank": m * 4, "stepwise_us": round(t * 1e6, 3), "fused_us": round(tf * 1e6, 3)})
-    fit = calib.fit_alpha_beta(st, by, ts)
-    fit["fused_fit"] = calib.fit_fixed_plus_bandwidth(fused_b, fused_t)
-    fit["nranks"] = N
-    fit["schedule"] = "ring, one kernel per step (fuse_depth=1), fp32 SUM; GPU time from HIP-graph replays"
-    fit["points"] = pts
-    return fit
+
+    from ring_allreduce_reduction_02_amd import ccgpu
+    res = {}
+    for pad in pads:
+        s = rank_tensor(N, M, src.dtype, pad, dev)
+        r = rank_tensor(N, M, src.dtype, pad, dev)
+        s.copy_(src)
+        t = time_launches(lambda: ccgpu.all_reduce(s, r), steps, 3)
+        per = sorted(t["per_launch_ms"])
+        ms = per[len(per) // 2]
+        res[str(pad)] = {"median_launch_ms": round(ms, 5), "min_launch_ms": round(per[0], 5),
+                         "GBps": round(2 * N * M * src.element_size() / ms / 1e6, 1)}
+        del s, r
+        torch.cuda.empty_cache()
+    return res
+
+
+def _time_gpu(fn, reps, per):
+    """GPU time of fn from graph replays; eager back-to-back launches between
+    HIP events if the call cannot be captured."""
+    try:
+        return time_graph(fn, reps, per), "graph"
+    except Exception:  # noqa: BLE001 - capture unsupported for this launch kind
+        import torch
+        torch.cuda.synchronize()
+        r = time_launches(fn, reps * per, 3)
+        return r["total_ms"] / (reps * per), "eager"
+
+
+def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30):
+    """Stepwise ring AllReduce (fp32 SUM) at N = 4, 8, 16 over per-rank sizes
+    4 KiB .. 1 GiB (x4), GPU time from HIP-graph replays, in two variants:
+    one kernel per ring step, and all steps in one cooperative launch with a
+    grid barrier between steps.  Fits T = alpha * 2(N-1) + beta * bytes sent
+    per rank per N, and over all N together with a per-call constant t0
+    (T = t0 + alpha * steps + beta * bytes).  The fused kernel's
+    T = t0 + bytes / BW is fitted on the same sizes."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import calib, ccgpu
+    sizes = [m for m in (1 << k for k in range(10, 29, 2)) if m * 4 <= max_bytes]
+    gen = torch.Generator(device=dev).manual_seed(20261202)
+    out = {"schedule": "ring AllReduce, fp32 SUM, fuse_depth=1 (one ring step per pass)",
+           "variants": {"kernel_per_step": "one kernel launch per ring step",
+                        "grid_barrier": "one cooperative launch, grid barrier between ring steps"},
+           "per_n": {}}
+    glob = {"kernel_per_step": ([], [], []), "grid_barrier": ([], [], [])}
+    for N in ranks:
+        send = torch.randn(N, sizes[-1], generator=gen, device=dev) * 1e-3
+        recv = torch.empty_like(send)
+        ws = ccgpu.make_workspace("all_reduce", N, sizes[-1], "f32", "ring", 1, dev, grid_sync=True)
+        # steady clocks before the smallest, most clock-sensitive points
+        for _ in range(10):
+            ccgpu.all_reduce(send, recv, fuse_depth=0)
+        torch.cuda.synchronize()
+        pts, st, by, t_ks, t_gb, fb, ft, how = [], [], [], [], [], [], [], set()
+        for m in sizes:
+            s, r = send[:, :m], recv[:, :m]
+            per = 16 if m <= (1 << 20) else 2
+            b, n = ccgpu.get_traffic("all_reduce", N, m, "f32", "ring")
+            tk, h1 = _time_gpu(lambda: ccgpu.all_reduce(s, r, fuse_depth=1), 10, per)
+            tg, h2 = _time_gpu(lambda: ccgpu.all_reduce(s, r, fuse_depth=1, workspace=ws, grid_sync=True), 10, per)
+            tf, h3 = _time_gpu(lambda: ccgpu.all_reduce(s, r, fuse_depth=0), 10, per)
+            how |= {h1, h2, h3}
+            st.append(n); by.append(b); t_ks.append(tk / 1e3); t_gb.append(tg / 1e3)
+            fb.append(2 * N * m * 4); ft.append(tf / 1e3)
+            pts.append({"bytes_per_rank": m * 4, "kernel_per_step_us": round(tk * 1e3, 3),
+                        "grid_barrier_us": round(tg * 1e3, 3), "fused_us": round(tf * 1e3, 3)})
+        torch.cuda.synchronize()
+        timed_out = ccgpu.grid_sync_timed_out(ws)
+        out["per_n"][str(N)] = {
+            "kernel_per_step": calib.fit_alpha_beta(st, by, t_ks),
+            "grid_barrier": calib.fit_alpha_beta(st, by, t_gb),
+            "fused": calib.fit_fixed_plus_bandwidth(fb, ft),
+            "points": pts,
+            "timing": sorted(how),
+            "barrier_timed_out": timed_out,
+        }
+        for key, ts in (("kernel_per_step", t_ks), ("grid_barrier", t_gb)):
+            glob[key][0].extend(st); glob[key][1].extend(by); glob[key][2].extend(ts)
+        del send, recv, ws
+        torch.cuda.empty_cache()
+    out["all_n"] = {k: calib.fit_launch_alpha_beta(*v) for k, v in glob.items()}
+    return out
 
 
 def _avg_ms(fn, steps=10, warmup=3):
     r = time_launches(fn, steps, warmup)
     return r["total_ms"] / steps
+
+
+def norm_rel_err_fp64(send, recv, offsets, counts, step=1 << 24):
+    """max over ranks of ||y_r - y64|| / ||y64|| over the given element
+    ranges, y64 = the order-free fp64 sum of the inputs (a measurement of the
+    output, computed with torch on the device in slices)."""
+    import torch
+    N = send.shape[0]
+    num = torch.zeros(N, dtype=torch.float64, device=send.device)
+    den = torch.zeros((), dtype=torch.float64, device=send.device)
+    for o, c in zip(offsets, counts):
+        for a in range(o, o + c, step):
+            e = min(a + step, o + c)
+            y64 = send[:, a:e].to(torch.float64).sum(0)
+            num += ((recv[:, a:e].to(torch.float64) - y64) ** 2).sum(1)
+            den += (y64 ** 2).sum()
+    return float((num / den).sqrt().max().item())
 
 
 def workloads(dev):
@@ -209,21 +284,22 @@ def workloads(dev):
     gen = torch.Generator(device=dev).manual_seed(synth.SEED)
 
     # int32 ring AllReduce, N=4, M=1,048,576 (32 MiB per call): one buffer set
-    # (cache-resident) and 32 rotating sets (1 GiB, beyond the 256 MB cache)
+    # (cache-resident) and 64 rotating sets (2 GiB, beyond the 256 MB cache)
     N, M = 4, 1 << 20
+    nsets = 64
     sets = [(torch.randint(-1000, 1001, (N, M), generator=gen, device=dev, dtype=torch.int32),
-             torch.empty(N, M, device=dev, dtype=torch.int32)) for _ in range(32)]
+             torch.empty(N, M, device=dev, dtype=torch.int32)) for _ in range(nsets)]
     alg = 2 * N * M * 4
     ms1 = time_graph(lambda: ccgpu.all_reduce(sets[0][0], sets[0][1]), 10, 32)
 
     def rot():
         for s_, r_ in sets:
             ccgpu.all_reduce(s_, r_)
-    msr = time_graph(rot, 10, 1) / 32
+    msr = time_graph(rot, 10, 1) / nsets
     host = _avg_ms(lambda: ccgpu.all_reduce(sets[0][0], sets[0][1]), 50, 10)
     out["int32_ring_n4_m1048576"] = {"same_set_us": round(ms1 * 1e3, 2), "same_set_GBps": round(alg / ms1 / 1e6, 1),
-                                     "rotating_1GiB_us": round(msr * 1e3, 2),
-                                     "rotating_1GiB_GBps": round(alg / msr / 1e6, 1),
+                                     "rotating_2GiB_us": round(msr * 1e3, 2),
+                                     "rotating_2GiB_GBps": round(alg / msr / 1e6, 1),
                                      "eager_python_call_us": round(host * 1e3, 2),
                                      "timing": "HIP-graph replays (GPU time); eager figure includes host launch cost"}
     del sets
@@ -240,7 +316,8 @@ def workloads(dev):
     b = {"tensors": len(sizes), "buckets": len(boff), "elements_per_rank": sum(bcnt)}
     for algo in ("ring", "hd", "butterfly"):
         ms = _avg_ms(lambda: ccgpu.all_reduce_buckets(send, recv, boff, bcnt, algo=algo))
-        b[algo] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
+        b[algo] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1),
+                   "max_norm_rel_err_vs_fp64": norm_rel_err_fp64(send, recv, boff, bcnt)}
     ms = _avg_ms(lambda: [ccgpu.all_reduce(send[:, o:o + c], recv[:, o:o + c]) for o, c in zip(boff, bcnt)], 5, 2)
     b["ring_one_launch_per_bucket"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
     out["bucketed_bf16_n8"] = b
@@ -390,11 +467,15 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "traffic_source": traffic_src,
+            "traffic_over_algorithmic": round(traffic / alg_bytes, 4) if traffic else None,
             "avg_launch_ms": round(avg_launch_ms, 5),
+            "median_launch_ms": round(sorted(per)[len(per) // 2], 5),
             "min_launch_ms": round(min(per), 5),
         },
     }
     if not args.no_extras and args.dtype == "f32" and args.algo == "ring" and args.fuse_depth == 0:
+        log("rank-stride pad sweep")
+        out["pad_sweep"] = pad_sweep(send, N, M, dev)
         log("bf16 twin")
         xb = synth.gradient_inputs(N, M, "bf16")
         sb = rank_tensor(N, M, torch.bfloat16, args.pad_bytes, dev)
@@ -408,10 +489,10 @@ def main():
                             "pct_of_peak": round(100 * 2 * N * M * 2 / (ms16 / 1e3) / 1e9 / PEAK_HBM_GBPS, 2)}
         del sb, rb
         torch.cuda.empty_cache()
-        log("alpha-beta calibration")
-        out["alpha_beta"] = alpha_beta(send, recv, N)
         del send, recv, ws
         torch.cuda.empty_cache()
+        log("alpha-beta calibration")
+        out["alpha_beta"] = alpha_beta(dev)
         log("other workloads")
         out["workloads"] = workloads(dev)
     if not args.no_cpu_baseline:

@@ -94,13 +94,27 @@ typedef enum {
  *  blocks_per_cu: cap on resident workgroups per compute unit (occupancy) for
  *  the call's kernels; 0 lets the library choose (it keeps a few tens of KiB
  *  of loads in flight per CU, which streams HBM best).  Negative is invalid.
- *  A NULL cfg means {CC_ALGO_RING, 0, NULL, 0, 0}. */
+ *  grid_sync (0 or 1): ring AllReduce with fuse_depth >= 1 only (any other
+ *  collective or schedule returns CC_ERR_UNSUPPORTED).  The passes of
+ *  fuse_depth ring steps run in ONE kernel launch instead of one launch per
+ *  pass: workgroups take tiles from an ordered queue, and no tile of a pass
+ *  starts before every tile of the previous pass is complete -- the
+ *  step-by-step synchronisation of the ring (textbook ch. 6, Ring AllReduce;
+ *  AllReduce notes, 算法一) as a grid-wide barrier.  It needs no co-resident
+ *  grid.  Results are bit-identical to grid_sync = 0.  The workspace then
+ *  starts with 512 bytes of queue words (included in cc_workspace_size; must
+ *  be 16-byte aligned), which the call clears with a kernel before the
+ *  launch.  A wait gives up after 2 s: the uint32 at byte offset 4 of the
+ *  workspace is then 1 (the results are undefined) and the kernel still
+ *  ends; it reads 0 after a good call.
+ *  A NULL cfg means {CC_ALGO_RING, 0, NULL, 0, 0, 0}. */
 typedef struct {
   cc_algo_t algo;
   int fuse_depth;
   void* workspace;
   size_t workspace_bytes;
   int blocks_per_cu;
+  int grid_sync;
 } cc_config_t;
 
 /* N rank buffers: rank r at (char*)base + r * rank_stride_bytes (device memory). */

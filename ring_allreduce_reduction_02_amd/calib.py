@@ -48,3 +48,29 @@ def fit_fixed_plus_bandwidth(bytes_moved: Sequence[float], seconds: Sequence[flo
     w = 1.0 / t
     sol, _ = nnls(A * w[:, None], t * w)
     return {"t0_us": float(sol[0]) * 1e6, "bw_GBps": (1.0 / sol[1] / 1e9) if sol[1] > 0 else float("inf")}
+
+
+def fit_launch_alpha_beta(steps: Sequence[float], bytes_sent: Sequence[float],
+                          seconds: Sequence[float]) -> Dict[str, float]:
+    """T = t0 + alpha * steps + beta * bytes_sent_per_rank: the same model with a
+    per-call constant (the launch of a schedule that runs all its steps in
+    one kernel).  t0 and alpha separate only when the points span several
+    step counts (several rank counts N)."""
+    from scipy.optimize import nnls
+
+    n = np.asarray(steps, dtype=np.float64)
+    b = np.asarray(bytes_sent, dtype=np.float64)
+    t = np.asarray(seconds, dtype=np.float64)
+    A = np.stack([np.ones_like(n), n, b], axis=1)
+    w = 1.0 / t
+    sol, _ = nnls(A * w[:, None], t * w)
+    t0, alpha, beta = (float(v) for v in sol)
+    pred = A @ sol
+    return {
+        "t0_us": t0 * 1e6,
+        "alpha_us_per_step": alpha * 1e6,
+        "beta_ps_per_byte": beta * 1e12,
+        "link_GBps": (1.0 / beta / 1e9) if beta > 0 else float("inf"),
+        "n_star_bytes": alpha / beta if beta > 0 else float("inf"),
+        "max_rel_residual": float(np.max(np.abs(pred - t) / t)),
+    }

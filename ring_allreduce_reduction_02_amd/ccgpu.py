@@ -36,7 +36,7 @@ class RankBuf(ctypes.Structure):
 class Config(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int), ("fuse_depth", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("blocks_per_cu", ctypes.c_int)]
+                ("blocks_per_cu", ctypes.c_int), ("grid_sync", ctypes.c_int)]
 
 
 class CCError(RuntimeError):
@@ -117,10 +117,11 @@ def rankbuf(t) -> RankBuf:
     return RankBuf(t.data_ptr(), t.stride(0) * t.element_size())
 
 
-def config(algo: str = "ring", fuse_depth: int = 0, workspace=None, blocks_per_cu: int = 0) -> Config:
+def config(algo: str = "ring", fuse_depth: int = 0, workspace=None, blocks_per_cu: int = 0,
+           grid_sync: bool = False) -> Config:
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    return Config(ALGOS[algo], int(fuse_depth), ws_ptr, ws_bytes, int(blocks_per_cu))
+    return Config(ALGOS[algo], int(fuse_depth), ws_ptr, ws_bytes, int(blocks_per_cu), int(bool(grid_sync)))
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -130,19 +131,19 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def workspace_size(coll: str, nranks: int, count: int, dtype: str, algo: str = "ring",
-                   fuse_depth: int = 0) -> int:
+                   fuse_depth: int = 0, grid_sync: bool = False) -> int:
     out = ctypes.c_size_t(0)
-    cfg = Config(ALGOS[algo], int(fuse_depth), None, 0, 0)
+    cfg = Config(ALGOS[algo], int(fuse_depth), None, 0, 0, int(bool(grid_sync)))
     _check(load().cc_workspace_size(COLLS[coll], ctypes.byref(cfg), nranks, count, DTYPES[dtype],
                                     ctypes.byref(out)))
     return out.value
 
 
 def make_workspace(coll: str, nranks: int, count: int, dtype: str, algo: str = "ring",
-                   fuse_depth: int = 0, device="cuda"):
+                   fuse_depth: int = 0, device="cuda", grid_sync: bool = False):
     """Allocate (with torch) the workspace a schedule needs, or None."""
     import torch
-    n = workspace_size(coll, nranks, count, dtype, algo, fuse_depth)
+    n = workspace_size(coll, nranks, count, dtype, algo, fuse_depth, grid_sync)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
@@ -162,13 +163,14 @@ def chunk_bounds(count: int, nranks: int):
 
 
 def all_reduce(send, recv=None, op: str = "sum", algo: str = "ring", fuse_depth: int = 0,
-               workspace=None, stream=None, blocks_per_cu: int = 0) -> None:
-    """recv[r] = (+)_j send[j] for every rank r; send/recv are [N, M]."""
+               workspace=None, stream=None, blocks_per_cu: int = 0, grid_sync: bool = False) -> None:
+    """recv[r] = (+)_j send[j] for every rank r; send/recv are [N, M].
+    grid_sync: the stepwise ring's passes in one cooperative launch."""
     recv = send if recv is None else recv
     N, M = send.shape
     if tuple(recv.shape) != (N, M) or recv.dtype != send.dtype:
         raise ValueError("recv must match send")
-    cfg = config(algo, fuse_depth, workspace, blocks_per_cu)
+    cfg = config(algo, fuse_depth, workspace, blocks_per_cu, grid_sync)
     _check(load().cc_all_reduce(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], OPS[op], N,
                                 ctypes.byref(cfg), _stream(stream)))
 
@@ -257,3 +259,10 @@ def all_to_all(send, recv, counts: Sequence[Sequence[int]], elem_per_row: int = 
 def raw(fn: str, *args):
     """Call a C-ABI function with raw ctypes arguments; returns the status."""
     return getattr(load(), fn)(*args)
+
+
+def grid_sync_timed_out(workspace) -> bool:
+    """After a grid_sync call has completed: whether a barrier wait gave up
+    (the uint32 at byte offset 4 of the workspace)."""
+    import torch
+    return int(workspace[4:8].view(torch.int32).item()) != 0

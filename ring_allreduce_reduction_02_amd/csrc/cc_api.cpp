@@ -63,15 +63,20 @@ bool al16(uint64_t v) { return (v & 15u) == 0; }
 bool al16p(const void* p) { return al16((uint64_t)(uintptr_t)p); }
 uint64_t rup(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-const cc_config_t kDefaultCfg = {CC_ALGO_RING, 0, nullptr, 0, 0};
+const cc_config_t kDefaultCfg = {CC_ALGO_RING, 0, nullptr, 0, 0, 0};
 
-cc_status_t common_checks(int nranks, cc_dtype_t dtype, const cc_config_t* cfg) {
+cc_status_t common_checks(cc_coll_t coll, int nranks, cc_dtype_t dtype, const cc_config_t* cfg) {
   if (nranks < 1 || nranks > CC_MAX_RANKS)
     return fail(CC_ERR_INVALID_ARG, "nranks=%d outside [1, %d]", nranks, CC_MAX_RANKS);
   if ((int)dtype < 0 || (int)dtype > 2) return fail(CC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if ((int)cfg->algo < 0 || (int)cfg->algo > 2) return fail(CC_ERR_INVALID_ARG, "unknown algo %d", (int)cfg->algo);
   if (cfg->fuse_depth < 0) return fail(CC_ERR_INVALID_ARG, "fuse_depth=%d is negative", cfg->fuse_depth);
   if (cfg->blocks_per_cu < 0) return fail(CC_ERR_INVALID_ARG, "blocks_per_cu=%d is negative", cfg->blocks_per_cu);
+  if (cfg->grid_sync != 0 && cfg->grid_sync != 1)
+    return fail(CC_ERR_INVALID_ARG, "grid_sync=%d is neither 0 nor 1", cfg->grid_sync);
+  if (cfg->grid_sync &&
+      (coll != CC_COLL_ALL_REDUCE || cfg->algo != CC_ALGO_RING || cfg->fuse_depth < 1))
+    return fail(CC_ERR_UNSUPPORTED, "grid_sync runs the stepwise ring AllReduce only (algo ring, fuse_depth >= 1)");
   return CC_OK;
 }
 
@@ -121,7 +126,18 @@ struct Bounds {
 };
 
 // ---- workspace sizing (bytes); M is the full per-rank vector length
+uint64_t ws_need_data(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt);
+
+// grid_sync: the queue words take the first kBarBytes, staging follows
+constexpr uint64_t kBarBytes = 512;
+static_assert(kQueueWords * 4 <= kBarBytes, "queue words fit");
+bool uses_barrier(const cc_config_t& cfg, int N) { return cfg.grid_sync && N > 1; }
+
 uint64_t ws_need(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt) {
+  return (uses_barrier(cfg, N) ? kBarBytes : 0) + ws_need_data(coll, cfg, N, M, dt);
+}
+
+uint64_t ws_need_data(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt) {
   if (N <= 1 || cfg.fuse_depth == 0) return 0;
   const uint64_t per_elem = M * 4;
   const uint64_t per_rank = N * rup(per_elem, 256);
@@ -145,11 +161,15 @@ cc_status_t check_ws(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, 
     return fail(CC_ERR_INVALID_ARG,
                 "this schedule needs %llu bytes of workspace (cc_workspace_size); got %zu",
                 (unsigned long long)need, cfg.workspace ? cfg.workspace_bytes : (size_t)0);
+  if (uses_barrier(cfg, N) && ((uintptr_t)cfg.workspace & 15u))
+    return fail(CC_ERR_INVALID_ARG, "grid_sync needs a 16-byte aligned workspace");
   return CC_OK;
 }
 
-Side ws_side(const cc_config_t& cfg, uint64_t M) {
-  return Side{(char*)cfg.workspace, rup(M * 4, 256)};
+Side ws_side(const cc_config_t& cfg, uint64_t M, int N) {
+  char* base = (char*)cfg.workspace;
+  if (base && uses_barrier(cfg, N)) base += kBarBytes;
+  return Side{base, rup(M * 4, 256)};
 }
 
 cc_status_t copy_ranks(const cc_rankbuf_t& src, const cc_rankbuf_t& dst, uint64_t nbytes, int N, int esize,
@@ -199,7 +219,7 @@ cc_status_t cc_chunk_bounds(size_t count, int nranks, size_t* bounds) {
 cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype, cc_op_t op,
                           int nranks, const cc_config_t* cfgp, cc_stream_t stream) {
   const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
-  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  cc_status_t s = common_checks(CC_COLL_ALL_REDUCE, nranks, dtype, &cfg);
   if (s) return s;
   if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
   const int N = nranks, dt = (int)dtype, es = elem_size(dt);
@@ -233,7 +253,7 @@ cc_status_t run_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, uint64_t M, int
   Red r;
   r.send = side(send);
   r.recv = side(recv);
-  r.ws = ws_side(cfg, M);
+  r.ws = ws_side(cfg, M, N);
   r.M = M;
   r.bnd = bd.b;
   r.blocks_per_cu = cfg.blocks_per_cu;
@@ -249,6 +269,7 @@ cc_status_t run_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, uint64_t M, int
   if (cfg.algo == CC_ALGO_RING) {
     if (cfg.fuse_depth == 0) return hip_status(launch_ring_fused(r), "ring all_reduce");
     const int k = std::min(cfg.fuse_depth, N - 1);
+    if (cfg.grid_sync) return hip_status(launch_ring_queue(r, k, (unsigned*)cfg.workspace), "ring all_reduce (one launch)");
     const int pin = dt != DT_BF16;
     for (int s0 = 0; s0 < N - 1 && e == hipSuccess; s0 += k) e = launch_ring_rs_pass(r, s0, std::min(k, N - 1 - s0), pin);
     Gat g{r.send, r.recv, M, bd.b, cfg.blocks_per_cu, N, es, 0, r.vec_ok, st};
@@ -276,7 +297,7 @@ cc_status_t cc_all_reduce_buckets(cc_rankbuf_t send, cc_rankbuf_t recv, const si
                                   int nbuckets, cc_dtype_t dtype, cc_op_t op, int nranks, const cc_config_t* cfgp,
                                   cc_stream_t stream) {
   const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
-  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  cc_status_t s = common_checks(CC_COLL_ALL_REDUCE, nranks, dtype, &cfg);
   if (s) return s;
   if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
   const int N = nranks, dt = (int)dtype, es = elem_size(dt);
@@ -380,7 +401,7 @@ cc_status_t cc_bucket_plan(const size_t* sizes, int ntensors, size_t elem_bytes,
 cc_status_t cc_reduce_scatter(cc_rankbuf_t send, cc_rankbuf_t recv, size_t recvcount, cc_dtype_t dtype, cc_op_t op,
                               int nranks, const cc_config_t* cfgp, cc_stream_t stream) {
   const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
-  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  cc_status_t s = common_checks(CC_COLL_REDUCE_SCATTER, nranks, dtype, &cfg);
   if (s) return s;
   if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
   const int N = nranks, dt = (int)dtype, es = elem_size(dt);
@@ -401,7 +422,7 @@ cc_status_t cc_reduce_scatter(cc_rankbuf_t send, cc_rankbuf_t recv, size_t recvc
   Red r;
   r.send = side(send);
   r.recv = side(recv);
-  r.ws = ws_side(cfg, M);
+  r.ws = ws_side(cfg, M, N);
   r.M = M;
   r.bnd = bd.b;
   r.blocks_per_cu = cfg.blocks_per_cu;
@@ -427,7 +448,7 @@ cc_status_t cc_reduce_scatter(cc_rankbuf_t send, cc_rankbuf_t recv, size_t recvc
 cc_status_t cc_all_gather(cc_rankbuf_t send, cc_rankbuf_t recv, size_t sendcount, cc_dtype_t dtype, int nranks,
                           const cc_config_t* cfgp, cc_stream_t stream) {
   const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
-  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  cc_status_t s = common_checks(CC_COLL_ALL_GATHER, nranks, dtype, &cfg);
   if (s) return s;
   const int N = nranks, dt = (int)dtype, es = elem_size(dt);
   if (cfg.algo == CC_ALGO_BUTTERFLY) return fail(CC_ERR_UNSUPPORTED, "butterfly is defined for all_reduce only");
@@ -468,7 +489,7 @@ cc_status_t cc_all_gather(cc_rankbuf_t send, cc_rankbuf_t recv, size_t sendcount
 cc_status_t cc_broadcast(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype, int root, int nranks,
                          const cc_config_t* cfgp, cc_stream_t stream) {
   const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
-  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  cc_status_t s = common_checks(CC_COLL_BROADCAST, nranks, dtype, &cfg);
   if (s) return s;
   const int N = nranks, dt = (int)dtype, es = elem_size(dt);
   if (root < 0 || root >= N) return fail(CC_ERR_INVALID_ARG, "root=%d outside [0, %d)", root, N);
@@ -515,7 +536,7 @@ cc_status_t cc_broadcast(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_
 cc_status_t cc_all_to_all(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* counts, size_t elem_per_row,
                           cc_dtype_t dtype, int nranks, const cc_config_t* cfgp, cc_stream_t stream) {
   const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
-  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  cc_status_t s = common_checks(CC_COLL_ALL_TO_ALL, nranks, dtype, &cfg);
   if (s) return s;
   const int N = nranks, dt = (int)dtype, es = elem_size(dt);
   if (cfg.algo != CC_ALGO_RING) return fail(CC_ERR_UNSUPPORTED, "all_to_all supports the ring/pairwise schedule only");
@@ -571,7 +592,7 @@ cc_status_t cc_all_to_all(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* co
 cc_status_t cc_workspace_size(cc_coll_t coll, const cc_config_t* cfgp, int nranks, size_t count, cc_dtype_t dtype,
                               size_t* bytes) {
   const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
-  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  cc_status_t s = common_checks(coll, nranks, dtype, &cfg);
   if (s) return s;
   if (!bytes) return fail(CC_ERR_INVALID_ARG, "bytes is NULL");
   if ((int)coll < 0 || (int)coll > 4) return fail(CC_ERR_INVALID_ARG, "unknown collective %d", (int)coll);
@@ -585,7 +606,7 @@ cc_status_t cc_get_traffic(cc_coll_t coll, cc_algo_t algo, int nranks, size_t co
                            uint64_t* max_bytes, int* steps) {
   cc_config_t cfg = kDefaultCfg;
   cfg.algo = algo;
-  cc_status_t s = common_checks(nranks, dtype, &cfg);
+  cc_status_t s = common_checks(coll, nranks, dtype, &cfg);
   if (s) return s;
   if (!max_bytes || !steps) return fail(CC_ERR_INVALID_ARG, "NULL output");
   const int N = nranks;

@@ -212,16 +212,20 @@ struct Tile {
 // The workgroup's element range and, when the whole tile is full-width and
 // lies in one chunk, that chunk (uniform across the workgroup).
 template <int V>
-__device__ __forceinline__ Tile<V> tile_of(uint64_t M, const uint64_t* bnd, int N, int vec_ok) {
+__device__ __forceinline__ Tile<V> tile_at(uint64_t idx, uint64_t M, const uint64_t* bnd, int N, int vec_ok) {
   const uint64_t tile = (uint64_t)kBlock * kUnroll * V;
   Tile<V> t;
-  t.e0 = (uint64_t)blockIdx.x * tile;
+  t.e0 = idx * tile;
   t.e1 = t.e0 + tile < M ? t.e0 + tile : M;
   const uint32_t c0 = chunk_in(bnd, N, t.e0);
   const uint32_t c1 = chunk_in(bnd, N, t.e1 - 1);
   t.c = c0;
   t.fast = vec_ok && (t.e1 - t.e0) == tile && c0 == c1;
   return t;
+}
+template <int V>
+__device__ __forceinline__ Tile<V> tile_of(uint64_t M, const uint64_t* bnd, int N, int vec_ok) {
+  return tile_at<V>(blockIdx.x, M, bnd, N, vec_ok);
 }
 
 __device__ __forceinline__ uint64_t vec_elem(uint64_t e0, int u, int V) {
@@ -524,13 +528,13 @@ struct PassArgs {
 // step-(s0-1) receiver holds is read, the next k ranks' contributions are
 // folded in, and the result is left where the step-(s0+k-1) receiver holds it.
 template <int DT, int OP>
-__global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
+__device__ __forceinline__ void ring_pass_tile(const PassArgs& a, uint64_t tile, int s0, int k) {
   typedef typename Ty<DT>::A A;
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N;
-  const bool fin = a.s0 + a.k == N - 1;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const bool fin = s0 + k == N - 1;
+  const Tile<V> t = tile_at<V>(tile, a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const int start = a.rs_mode ? wrapN(c + 1, N) : c;
@@ -539,13 +543,13 @@ __global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
     for (int u = 0; u < kUnroll; ++u) {
       const uint64_t e = vec_elem(t.e0, u, V);
       A acc[V];
-      if (a.s0 == 0)
+      if (s0 == 0)
         unpack<DT>(ldg(a.sb + (uint64_t)start * a.ss + e * SZ), acc);
       else if (a.pin_recv)
-        unpack<DT>(ldg(a.rb + (uint64_t)wrapN(start + a.s0, N) * a.rs + e * SZ), acc);
+        unpack<DT>(ldg(a.rb + (uint64_t)wrapN(start + s0, N) * a.rs + e * SZ), acc);
       else
         ldw_vec<DT>(a.wb + e * 4, acc);
-      for (int j = a.s0 + 1; j <= a.s0 + a.k; ++j) {
+      for (int j = s0 + 1; j <= s0 + k; ++j) {
         A x[V];
         unpack<DT>(ldg(a.sb + (uint64_t)wrapN(start + j, N) * a.ss + e * SZ), x);
         opv<DT, OP>(x, acc);
@@ -556,7 +560,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
         else
           stg(a.rb + (uint64_t)wrapN(start + N - 1, N) * a.rs + e * SZ, pack<DT>(acc));
       } else if (a.pin_recv) {
-        stg(a.rb + (uint64_t)wrapN(start + a.s0 + a.k, N) * a.rs + e * SZ, pack<DT>(acc));
+        stg(a.rb + (uint64_t)wrapN(start + s0 + k, N) * a.rs + e * SZ, pack<DT>(acc));
       } else {
         stw_vec<DT>(a.wb + e * 4, acc);
       }
@@ -566,13 +570,13 @@ __global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
       const uint32_t c = chunk_in(a.bnd, N, e);
       const int start = a.rs_mode ? wrapN((int)c + 1, N) : (int)c;
       A acc;
-      if (a.s0 == 0)
+      if (s0 == 0)
         acc = ld1<DT>(a.sb + (uint64_t)start * a.ss + e * SZ);
       else if (a.pin_recv)
-        acc = ld1<DT>(a.rb + (uint64_t)wrapN(start + a.s0, N) * a.rs + e * SZ);
+        acc = ld1<DT>(a.rb + (uint64_t)wrapN(start + s0, N) * a.rs + e * SZ);
       else
         acc = ldw1<DT>(a.wb + e * 4);
-      for (int j = a.s0 + 1; j <= a.s0 + a.k; ++j)
+      for (int j = s0 + 1; j <= s0 + k; ++j)
         acc = opf<DT, OP>(ld1<DT>(a.sb + (uint64_t)wrapN(start + j, N) * a.ss + e * SZ), acc);
       if (fin) {
         if (a.rs_mode)
@@ -580,12 +584,17 @@ __global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
         else
           st1<DT>(a.rb + (uint64_t)wrapN(start + N - 1, N) * a.rs + e * SZ, acc);
       } else if (a.pin_recv) {
-        st1<DT>(a.rb + (uint64_t)wrapN(start + a.s0 + a.k, N) * a.rs + e * SZ, acc);
+        st1<DT>(a.rb + (uint64_t)wrapN(start + s0 + k, N) * a.rs + e * SZ, acc);
       } else {
         stw1<DT>(a.wb + e * 4, acc);
       }
     }
   }
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_ring_pass(PassArgs a) {
+  ring_pass_tile<DT, OP>(a, blockIdx.x, a.s0, a.k);
 }
 
 // ------------------------------------------------------------------ halving-doubling steps
@@ -754,15 +763,15 @@ struct GatArgs {
 // AllReduce the owner of chunk c is rank c-1; in the standalone AllGather
 // rank c starts with chunk c (its send buffer) and also keeps a copy.
 template <int SZ>
-__global__ __launch_bounds__(kBlock) void k_ring_ag_pass(GatArgs a) {
+__device__ __forceinline__ void ring_ag_tile(const GatArgs& a, uint64_t tile, int s0, int k) {
   constexpr int V = 16 / SZ;
   const int N = a.N;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = tile_at<V>(tile, a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const uint64_t b0 = a.bnd[c];
-    const bool from_send = a.mode == 1 && a.s0 == 0;
-    const int holder = a.mode == 0 ? modN(c - 1 + a.s0, N) : wrapN(c + a.s0, N);
+    const bool from_send = a.mode == 1 && s0 == 0;
+    const int holder = a.mode == 0 ? modN(c - 1 + s0, N) : wrapN(c + s0, N);
     const int first_dst = a.mode == 0 ? wrapN(holder + 1, N) : wrapN(holder + 1, N);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -770,26 +779,125 @@ __global__ __launch_bounds__(kBlock) void k_ring_ag_pass(GatArgs a) {
       const u32x4 w = from_send ? ldg(a.sb + (uint64_t)c * a.ss + (e - b0) * SZ)
                                 : ldg(a.rb + (uint64_t)holder * a.rs + e * SZ);
       if (from_send) stg(a.rb + (uint64_t)c * a.rs + e * SZ, w);
-      for (int q = 0; q < a.k; ++q) stg(a.rb + (uint64_t)modN(first_dst + q, N) * a.rs + e * SZ, w);
+      for (int q = 0; q < k; ++q) stg(a.rb + (uint64_t)modN(first_dst + q, N) * a.rs + e * SZ, w);
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
       const int c = (int)chunk_in(a.bnd, N, e);
-      const bool from_send = a.mode == 1 && a.s0 == 0;
-      const int holder = a.mode == 0 ? modN(c - 1 + a.s0, N) : wrapN(c + a.s0, N);
+      const bool from_send = a.mode == 1 && s0 == 0;
+      const int holder = a.mode == 0 ? modN(c - 1 + s0, N) : wrapN(c + s0, N);
       const char* src = from_send ? a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ
                                   : a.rb + (uint64_t)holder * a.rs + e * SZ;
       if constexpr (SZ == 2) {
         const uint16_t v = *(const uint16_t*)src;
         if (from_send) *(uint16_t*)(a.rb + (uint64_t)c * a.rs + e * SZ) = v;
-        for (int q = 0; q < a.k; ++q) *(uint16_t*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v;
+        for (int q = 0; q < k; ++q) *(uint16_t*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v;
       } else {
         const uint32_t v = *(const uint32_t*)src;
         if (from_send) *(uint32_t*)(a.rb + (uint64_t)c * a.rs + e * SZ) = v;
-        for (int q = 0; q < a.k; ++q) *(uint32_t*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v;
+        for (int q = 0; q < k; ++q) *(uint32_t*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v;
       }
     }
   }
+}
+
+template <int SZ>
+__global__ __launch_bounds__(kBlock) void k_ring_ag_pass(GatArgs a) {
+  ring_ag_tile<SZ>(a, blockIdx.x, a.s0, a.k);
+}
+
+// ------------------------------------------------------------------ one-launch stepwise ring
+
+// The stepwise ring AllReduce in one launch.  The passes (k ring steps each;
+// ReduceScatter passes, then AllGather passes) are cut into claims of
+// `claim` tiles; workgroups take claims from a queue in global order, and a
+// claim of pass p starts only after every claim of pass p-1 has completed --
+// a grid-wide barrier between steps.  Because claims are handed out in order,
+// every claim a waiting workgroup depends on is held by a running workgroup,
+// so the schedule cannot deadlock whatever number of workgroups is resident.
+//
+// bar[0]: next claim; bar[1]: timed-out flag; bar[2 + p]: completed claims
+// of pass p.  All are cleared by k_clear_words before the launch.  A wait
+// gives up after spin_ticks of the constant-rate wall clock and sets bar[1];
+// once it is set no later wait of the launch waits, so every wave always
+// exits (the results are then undefined and bar[1] tells the caller).
+struct QueueArgs {
+  PassArgs p;   // ReduceScatter passes (s0, k unused)
+  GatArgs g;    // AllGather passes (s0, k unused)
+  unsigned* bar;
+  uint64_t spin_ticks;
+  uint64_t ntiles;    // tiles per pass
+  uint32_t claim;     // tiles per claim
+  uint32_t nclaims;   // claims per pass
+  int k;              // ring steps per pass
+  int npass;          // ReduceScatter passes (as many AllGather passes follow)
+};
+
+// thread 0 only: wait until *w reaches target (or the launch has timed out)
+__device__ __forceinline__ void wait_count(unsigned* w, unsigned target, unsigned* flag, uint64_t spin_ticks) {
+  const uint64_t t0 = wall_clock64();
+  while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
+    if (wall_clock64() - t0 > spin_ticks) {
+      __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// The claim index is shared through the first word of the launch's dynamic
+// LDS (the occupancy reservation, at least 16 bytes): a static __shared__
+// word would come on top of a reservation that may already be the whole LDS.
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_ring_queue(QueueArgs a) {
+  extern __shared__ unsigned lds_words[];
+  unsigned& s_q = lds_words[0];
+  const int N = a.p.N, k = a.k, P = a.npass;
+  const unsigned total = 2u * (unsigned)P * a.nclaims;
+  int ready = 0;  // claims of passes <= ready may start
+  for (;;) {
+    if (threadIdx.x == 0) s_q = __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const unsigned q = s_q;
+    if (q >= total) break;
+    const int pass = (int)(q / a.nclaims);
+    const uint64_t t0 = (uint64_t)(q - (unsigned)pass * a.nclaims) * a.claim;
+    const uint64_t t1 = t0 + a.claim < a.ntiles ? t0 + a.claim : a.ntiles;
+    if (pass > ready) {
+      if (threadIdx.x == 0) {
+        wait_count(a.bar + 2 + (pass - 1), a.nclaims, a.bar + 1, a.spin_ticks);
+        // drop lines this CU and its L2 cached before pass-1 completed (one
+        // invalidation serves the whole workgroup: its waves share the CU)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      __syncthreads();
+      ready = pass;
+    }
+    if (pass < P) {
+      const int s0 = pass * k, kk = k < N - 1 - s0 ? k : N - 1 - s0;
+      for (uint64_t t = t0; t < t1; ++t) ring_pass_tile<DT, OP>(a.p, t, s0, kk);
+    } else {
+      const int s0 = (pass - P) * k, kk = k < N - 1 - s0 ? k : N - 1 - s0;
+      for (uint64_t t = t0; t < t1; ++t) ring_ag_tile<Ty<DT>::SZ>(a.g, t, s0, kk);
+    }
+    // publish the claim: every wave waits for its stores to reach the L2,
+    // then one write-back of the L2 makes them visible to the other XCDs'
+    // caches before the claim is counted
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __builtin_amdgcn_s_waitcnt(0);  // the write-back has completed
+      __hip_atomic_fetch_add(a.bar + 2 + pass, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Clears the queue words before the launch (a kernel, not a memset, so the
+// pair can be captured in a graph).
+__global__ void k_clear_words(unsigned* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
 // Recursive-doubling AllGather step with distance d: the ranks whose partner
@@ -1056,6 +1164,54 @@ hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv)
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     hipLaunchKernelGGL((k_ring_pass<DT, OP>), grid, blk, lds, r.st, a);
+    return hipGetLastError();
+  });
+}
+
+constexpr int kQueueBlocksPerCu = 4;
+
+hipError_t launch_ring_queue(const Red& r, int k, unsigned* bar) {
+  QueueArgs a;
+  PassArgs& p = a.p;
+  p.sb = r.send.base; p.ss = r.send.stride;
+  p.rb = r.recv.base; p.rs = r.recv.stride;
+  p.wb = r.ws.base;
+  p.M = r.M; p.N = r.N; p.rs_mode = 0; p.vec_ok = r.vec_ok;
+  p.s0 = 0; p.k = k; p.pin_recv = r.dt != DT_BF16;
+  GatArgs& g = a.g;
+  g.sb = r.send.base; g.ss = r.send.stride;
+  g.rb = r.recv.base; g.rs = r.recv.stride;
+  g.M = r.M; g.N = r.N; g.mode = 0; g.vec_ok = r.vec_ok; g.s0 = 0; g.k = k;
+  for (int c = 0; c <= r.N; ++c) p.bnd[c] = g.bnd[c] = r.bnd[c];
+  a.bar = bar;
+  a.k = k;
+  a.npass = (r.N - 1 + k - 1) / k;
+  a.ntiles = num_tiles(r.M, r.dt);
+  int dev = 0, rate_khz = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || rate_khz <= 0)
+    rate_khz = 100000;
+  a.spin_ticks = (uint64_t)rate_khz * 2000;  // 2 s
+  // about one claim per resident workgroup and pass.  Each claim ends with a
+  // write-back of its XCD's L2, which costs about half a microsecond and
+  // serialises within the XCD, so the default keeps claims few and large:
+  // 4 workgroups per CU.
+  const int bpc = r.blocks_per_cu > 0 ? r.blocks_per_cu : kQueueBlocksPerCu;
+  const uint64_t slots = (uint64_t)bpc * (uint64_t)(cus > 0 ? cus : 1);
+  a.claim = (uint32_t)((a.ntiles + slots - 1) / slots);
+  a.nclaims = (uint32_t)((a.ntiles + a.claim - 1) / a.claim);
+  unsigned lds = lds_for_blocks_per_cu(bpc);
+  if (lds < 16) lds = 16;  // the claim word
+  const DevInfo di = dev_info();
+  if (di.lds_per_block > 0 && lds > (unsigned)di.lds_per_block) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(256), 0, r.st, bar, 2 + 2 * a.npass);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 grid(a.nclaims), blk(kBlock);
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    hipLaunchKernelGGL((k_ring_queue<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }

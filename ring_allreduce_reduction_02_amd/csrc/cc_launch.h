@@ -65,6 +65,11 @@ hipError_t launch_tree_fused(const Red& r, int tree);
 // ring ReduceScatter steps [s0, s0+k); partial_in_recv: partials stay in the
 // receiving rank's recv buffer (AllReduce, int32/fp32), else in r.ws.
 hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv);
+// the ring AllReduce as passes of k steps in one launch, every tile of a pass
+// waiting for all tiles of the previous one; bar: kQueueWords device words
+// (cleared by a kernel first).
+constexpr int kQueueWords = 2 + 2 * (kMaxRanks - 1);
+hipError_t launch_ring_queue(const Red& r, int k, unsigned* bar);
 // halving step with distance d; acc_in_recv as above (else r.ws is rank-strided).
 hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_in_recv);
 // butterfly step with distance d.

@@ -109,6 +109,26 @@ def test_workspace_sizes():
     assert ccgpu.workspace_size("reduce_scatter", 4, 10, "f32", "hd", 1) == 4 * 256
     assert ccgpu.workspace_size("reduce_scatter", 2, 10, "f32", "hd", 1) == 0
     assert ccgpu.workspace_size("all_gather", 8, 10, "f32", "hd", 1) == 0
+    # one-launch stepwise ring: 512 bytes of queue words come first
+    assert ccgpu.workspace_size("all_reduce", 8, 1000, "f32", "ring", 1, grid_sync=True) == 512
+    assert ccgpu.workspace_size("all_reduce", 8, 1000, "bf16", "ring", 1, grid_sync=True) == 512 + 4000
+    assert ccgpu.workspace_size("all_reduce", 8, 1000, "bf16", "ring", 7, grid_sync=True) == 512
+    assert ccgpu.workspace_size("all_reduce", 1, 1000, "f32", "ring", 1, grid_sync=True) == 0   # a copy
+
+
+def test_grid_sync_only_for_the_stepwise_ring_all_reduce():
+    def ws(coll, algo, fd, gs):
+        out = ctypes.c_size_t(0)
+        cfg = ccgpu.Config(ccgpu.ALGOS[algo], fd, None, 0, 0, gs)
+        return ccgpu.load().cc_workspace_size(ccgpu.COLLS[coll], ctypes.byref(cfg), 8, 100, 1, ctypes.byref(out))
+    assert ws("all_reduce", "ring", 1, 1) == ccgpu.CC_OK
+    assert ws("all_reduce", "ring", 0, 1) == ccgpu.CC_ERR_UNSUPPORTED       # fused: no steps to separate
+    assert ws("all_reduce", "hd", 1, 1) == ccgpu.CC_ERR_UNSUPPORTED
+    assert ws("all_reduce", "butterfly", 1, 1) == ccgpu.CC_ERR_UNSUPPORTED
+    for coll in ("reduce_scatter", "all_gather", "broadcast", "all_to_all"):
+        assert ws(coll, "ring", 1, 1) == ccgpu.CC_ERR_UNSUPPORTED, coll
+    assert ws("all_reduce", "ring", 1, 2) == ccgpu.CC_ERR_INVALID_ARG
+    assert ws("all_reduce", "ring", 1, -1) == ccgpu.CC_ERR_INVALID_ARG
 
 
 # ---------------------------------------------------------------- validation
@@ -144,6 +164,11 @@ def test_all_reduce_rejects_bad_arguments():
     assert _ar(ok_s, ok_r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, None, 0, 0)) == ccgpu.CC_ERR_INVALID_ARG
     assert _ar(ok_s, ok_r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, FAKE + (2 << 30), 399, 0)) == ccgpu.CC_ERR_INVALID_ARG
     assert "workspace" in ccgpu.load().cc_last_error().decode()
+    # grid_sync: needs the barrier words, 16-byte aligned
+    assert _ar(ok_s, ok_r, 100, 8, cfg=ccgpu.Config(0, 1, None, 0, 0, 1)) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 8, cfg=ccgpu.Config(0, 1, FAKE + (2 << 30) + 4, 512, 0, 1)) == ccgpu.CC_ERR_INVALID_ARG
+    assert "aligned" in ccgpu.load().cc_last_error().decode()
+    assert _ar(ok_s, ok_r, 100, 8, cfg=ccgpu.Config(2, 1, FAKE + (2 << 30), 512, 0, 1)) == ccgpu.CC_ERR_UNSUPPORTED
     # interleaved send/recv rows in one allocation do not overlap: only the device is missing
     inter_s, inter_r = _rb(FAKE, 800), _rb(FAKE + 400, 800)
     assert _ar(inter_s, inter_r, 100, 4) == ccgpu.CC_ERR_NO_DEVICE

@@ -26,6 +26,21 @@ def test_fused_fit_recovery():
     assert fit["bw_GBps"] == pytest.approx(6200, rel=1e-6)
 
 
+def test_launch_alpha_beta_recovery_over_several_rank_counts():
+    t0, alpha, beta = 6e-6, 1.2e-6, 1 / 450e9
+    steps, sent, t = [], [], []
+    for N in (4, 8, 16):
+        for s in [4096 * 4 ** k for k in range(10)]:
+            steps.append(2 * (N - 1))
+            sent.append(2 * (N - 1) * s // N)
+            t.append(t0 + alpha * steps[-1] + beta * sent[-1])
+    fit = calib.fit_launch_alpha_beta(steps, sent, t)
+    assert fit["t0_us"] == pytest.approx(6.0, rel=1e-5)
+    assert fit["alpha_us_per_step"] == pytest.approx(1.2, rel=1e-5)
+    assert fit["link_GBps"] == pytest.approx(450, rel=1e-5)
+    assert fit["max_rel_residual"] < 1e-9
+
+
 def test_bench_refuses_more_than_one_gpu():
     import subprocess, sys, os
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -14,7 +14,7 @@ from tests.gpu_util import DEV, alloc_ranks, bits, download, upload
 
 pytestmark = pytest.mark.gpu
 
-# fp32 tiles hold 2048 elements, bf16 tiles 4096: these span several tiles,
+# fp32 tiles hold 512 elements, bf16 tiles 1024: these span several tiles,
 # straddle chunk boundaries and leave ragged tails
 SIZES = [1, 13, 6151, 20485]
 RING_NS = [2, 3, 4, 5, 8, 16, 17]
