@@ -404,19 +404,26 @@ def _hd_ag_phase(acc: List[np.ndarray], b: List[int], tr: Trace) -> None:
         d *= 2
 
 
+def _hd_core(acc: List[np.ndarray], op: str, tr: Trace) -> None:
+    M = int(acc[0].shape[0])
+    b = chunk_bounds(M, len(acc))
+    _hd_rs_phase(acc, b, op, tr)
+    _hd_ag_phase(acc, b, tr)
+
+
 def hd_all_reduce(xs, op="sum", dtype="f32", trace=None):
     """Halving-doubling AllReduce: 2*log2(N) steps ([AR-notes], "算法二";
-    [Blog], "Recursive Halving-Doubling")."""
+    [Blog], "Recursive Halving-Doubling").  For N not a power of two the
+    first 2r ranks are folded in pairs before and restored after
+    (_with_pair_fold), r = N - 2**floor(log2 N)."""
     N = len(xs)
-    if not _is_pow2(N):
-        raise ValueError("halving-doubling needs N = 2**k")
-    M = int(np.asarray(xs[0]).shape[0])
     tr = trace if trace is not None else Trace()
     tr.sent = [0] * N
     acc = [to_acc(x, dtype) for x in xs]
-    b = chunk_bounds(M, N)
-    _hd_rs_phase(acc, b, op, tr)
-    _hd_ag_phase(acc, b, tr)
+    if _is_pow2(N):
+        _hd_core(acc, op, tr)
+    else:
+        _with_pair_fold(acc, op, tr, _hd_core)
     return [from_acc(a, dtype) for a in acc]
 
 
@@ -455,15 +462,18 @@ def hd_fold_elements(vals: np.ndarray, idx: np.ndarray, M: int, op: str,
                      dtype: str) -> np.ndarray:
     """Closed form of the halving phase for sampled elements of chunk c:
     S_N(j) = x_j and S_d(j) = op(S_2d(j), S_2d(j XOR d)) for d = N/2 .. 1;
-    the result for chunk c is S_1(c)."""
+    the result for chunk c is S_1(c).  For N not a power of two the sequence
+    starts from the pair-folded values w_v (see _pair_folded_values) over the
+    m = 2**floor(log2 N) remaining ranks, whose vector is cut into m chunks."""
     vals = np.asarray(vals)
     N = vals.shape[0]
-    c = chunk_of(idx, M, N)
+    S = _pair_folded_values(vals, op, dtype)
+    m = len(S)
+    c = chunk_of(idx, M, m)
     cols = np.arange(vals.shape[1])
-    S = [to_acc(vals[j], dtype) for j in range(N)]
-    d = N // 2
+    d = m // 2
     while d >= 1:
-        S = [combine(op, S[j], S[j ^ d]) for j in range(N)]
+        S = [combine(op, S[j], S[j ^ d]) for j in range(m)]
         d //= 2
     stacked = np.stack(S)
     return from_acc(stacked[c, cols], dtype)
@@ -473,17 +483,9 @@ def hd_fold_elements(vals: np.ndarray, idx: np.ndarray, M: int, op: str,
 # butterfly (recursive doubling with full exchange), N = 2**k
 # --------------------------------------------------------------------------
 
-def butterfly_all_reduce(xs, op="sum", dtype="f32", trace=None):
-    """Butterfly AllReduce: log2(N) steps; at step k rank i pairs with
-    i XOR 2**k, both exchange the full vector and combine it ([AR-notes],
-    "算法四：Butterfly (Recursive Doubling)": distance 1, then 2, then 4)."""
-    N = len(xs)
-    if not _is_pow2(N):
-        raise ValueError("butterfly needs N = 2**k")
-    M = int(np.asarray(xs[0]).shape[0])
-    tr = trace if trace is not None else Trace()
-    tr.sent = [0] * N
-    v = [to_acc(x, dtype) for x in xs]
+def _butterfly_core(v: List[np.ndarray], op: str, tr: Trace) -> None:
+    N = len(v)
+    M = int(v[0].shape[0])
     k = 1
     while k < N:
         snap = [a.copy() for a in v]
@@ -495,18 +497,410 @@ def butterfly_all_reduce(xs, op="sum", dtype="f32", trace=None):
             step.append((p, i, "all", M))
         tr.steps.append(step)
         k *= 2
+
+
+def butterfly_all_reduce(xs, op="sum", dtype="f32", trace=None):
+    """Butterfly AllReduce: log2(N) steps; at step k rank i pairs with
+    i XOR 2**k, both exchange the full vector and combine it ([AR-notes],
+    "算法四：Butterfly (Recursive Doubling)": distance 1, then 2, then 4).
+    For N not a power of two the first 2r ranks are folded in pairs before
+    and restored after, as for halving-doubling ([AR-notes], 算法四,
+    "非 2^k 处理")."""
+    N = len(xs)
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    v = [to_acc(x, dtype) for x in xs]
+    if _is_pow2(N):
+        _butterfly_core(v, op, tr)
+    else:
+        _with_pair_fold(v, op, tr, _butterfly_core)
     return [from_acc(a, dtype) for a in v]
 
 
 def butterfly_fold_elements(vals: np.ndarray, rank: int, op: str, dtype: str) -> np.ndarray:
     """Closed form of butterfly's result on one rank: a pairwise tree over the
-    sequence x_{rank XOR t}, t = 0..N-1, nearest pairs combined first."""
+    sequence x_{rank XOR t}, t = 0..N-1, nearest pairs combined first.  For N
+    not a power of two the tree runs over the pair-folded values w_v of the
+    m remaining ranks, taken from the virtual rank that `rank` belongs to
+    (rank // 2 for the first 2r ranks, rank - r after them)."""
     vals = np.asarray(vals)
     N = vals.shape[0]
-    seq = [to_acc(vals[rank ^ t], dtype) for t in range(N)]
+    w = _pair_folded_values(vals, op, dtype)
+    m = len(w)
+    r = N - m
+    v = rank // 2 if rank < 2 * r else rank - r
+    seq = [w[v ^ t] for t in range(m)]
     while len(seq) > 1:
         seq = [combine(op, seq[2 * i], seq[2 * i + 1]) for i in range(len(seq) // 2)]
     return from_acc(seq[0], dtype)
+
+
+# --------------------------------------------------------------------------
+# N not a power of two: fold pairs first, restore them last
+# --------------------------------------------------------------------------
+
+def _pair_fold_layout(N: int) -> Tuple[int, List[int]]:
+    """r = N - 2**floor(log2 N) and the ranks that take part in the
+    power-of-two schedule: 0, 2, ..., 2r-2 (each holding its pair's fold),
+    then 2r .. N-1 ([Blog], RHD "非 2 的整数次幂场景": the 2r ranks of part1 are
+    reduced pairwise into r ranks, the block of p' = 2**floor(log2 p) ranks
+    runs halving-doubling, and the folded ranks get the result back)."""
+    m = 1 << (N.bit_length() - 1)
+    r = N - m
+    return r, [2 * v for v in range(r)] + list(range(2 * r, N))
+
+
+def _with_pair_fold(acc: List[np.ndarray], op: str, tr: Trace,
+                    core: Callable[[List[np.ndarray], str, Trace], None]) -> None:
+    """Pre-step: rank 2i+1 (i < r) sends its vector to rank 2i, which combines
+    it, op(own, incoming).  The m = N - r active ranks run `core` as virtual
+    ranks 0..m-1.  Post-step: rank 2i sends the result to rank 2i+1.  The two
+    extra steps cost 2 alpha + 2 M beta ([AR-notes], "拓扑要求与非 2^k 处理")."""
+    N = len(acc)
+    M = int(acc[0].shape[0])
+    r, active = _pair_fold_layout(N)
+    snap = {2 * i + 1: acc[2 * i + 1].copy() for i in range(r)}
+    step = []
+    for i in range(r):
+        acc[2 * i] = combine(op, acc[2 * i], snap[2 * i + 1])
+        tr.sent[2 * i + 1] += M
+        step.append((2 * i + 1, 2 * i, "all", M))
+    tr.steps.append(step)
+    sub = Trace()
+    sub.sent = [0] * len(active)
+    vacc = [acc[a] for a in active]
+    core(vacc, op, sub)
+    for v, a in enumerate(active):
+        acc[a] = vacc[v]
+        tr.sent[a] += sub.sent[v]
+    for st in sub.steps:
+        tr.steps.append([(active[s], active[d], what, n) for (s, d, what, n) in st])
+    step = []
+    for i in range(r):
+        acc[2 * i + 1] = acc[2 * i].copy()
+        tr.sent[2 * i] += M
+        step.append((2 * i, 2 * i + 1, "all", M))
+    tr.steps.append(step)
+
+
+def _pair_folded_values(vals: np.ndarray, op: str, dtype: str) -> List[np.ndarray]:
+    """w_v = op(x_{2v}, x_{2v+1}) for v < r, x_{v+r} otherwise (accumulator
+    type): the values the m active ranks start the power-of-two schedule with."""
+    N = vals.shape[0]
+    m = 1 << (N.bit_length() - 1)
+    r = N - m
+    return [combine(op, to_acc(vals[2 * v], dtype), to_acc(vals[2 * v + 1], dtype)) if v < r
+            else to_acc(vals[v + r], dtype) for v in range(m)]
+
+
+# --------------------------------------------------------------------------
+# binary tree AllReduce (reduce up, broadcast down), any N
+# --------------------------------------------------------------------------
+
+def tree_all_reduce(xs, op="sum", dtype="f32", trace=None):
+    """Tree AllReduce ([MLSys-6], "Tree AllReduce"): in the reduce phase the
+    leaves send to their parents and every parent combines what it receives
+    and passes it up, reaching the root after log2(N) steps; the broadcast
+    phase sends the root's result back down in as many steps.  The tree is
+    the one whose link use the passage counts -- N/2 senders at the leaf
+    level, N/4 at the next, two nodes at the root: at distance d = 1, 2, 4,
+    ... rank i with i mod 2d = d sends its partial to rank i - d, which
+    combines op(own, incoming).  The broadcast doubles the holders from rank 0
+    (distance D/2, ..., 1 with D the power of two at or above N).  For N not
+    a power of two the ranks from N up are absent.  The root rounds bf16 once
+    and the broadcast copies the rounded result."""
+    N = len(xs)
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    acc = [to_acc(x, dtype) for x in xs]
+    d = 1
+    while d < N:
+        senders = list(range(d, N, 2 * d))
+        snap = {i: acc[i].copy() for i in senders}
+        step = []
+        for i in senders:
+            acc[i - d] = combine(op, acc[i - d], snap[i])
+            tr.sent[i] += M
+            step.append((i, i - d, "all", M))
+        tr.steps.append(step)
+        d *= 2
+    out: List[Optional[np.ndarray]] = [None] * N
+    out[0] = from_acc(acc[0], dtype)
+    d //= 2
+    while d >= 1:
+        step = []
+        for i in range(0, N, 2 * d):
+            if i + d < N:
+                out[i + d] = out[i].copy()
+                tr.sent[i] += M
+                step.append((i, i + d, "all", M))
+        tr.steps.append(step)
+        d //= 2
+    return out
+
+
+def tree_fold_elements(vals: np.ndarray, op: str, dtype: str) -> np.ndarray:
+    """Closed form of the tree's result: T(lo, n) over the ranks lo..lo+n-1
+    is x_lo for n = 1, else op(T(lo, h), T(lo + h, n - h)) with h the largest
+    power of two below n -- the subtree that rank lo gathers before its
+    partner at distance h sends the rest."""
+    vals = np.asarray(vals)
+
+    def T(lo: int, n: int) -> np.ndarray:
+        if n == 1:
+            return to_acc(vals[lo], dtype)
+        h = 1 << ((n - 1).bit_length() - 1)
+        return combine(op, T(lo, h), T(lo + h, n - h))
+
+    return from_acc(T(0, vals.shape[0]), dtype)
+
+
+# --------------------------------------------------------------------------
+# double binary tree
+# --------------------------------------------------------------------------
+
+def dbt_trees(N: int) -> Tuple[Dict[int, List[int]], int, Dict[int, List[int]], int]:
+    """The two complementary trees ([AR-notes], "算法三：Double Binary Tree":
+    T1 and T2 complementary, the leaves of one are internal nodes of the
+    other; [MLSys-6], "双二叉树").  The pages fix only that property; the
+    construction read here: T1 is the in-order binary tree over ranks
+    1..N-1 -- rank x whose lowest set bit is b has the left child x - b/2 and
+    the right child x + c, c the largest of b/2, b/4, ... with x + c < N (no
+    right child if there is none) -- rooted at the largest power of two below
+    N, with rank 0 on top of that root as its parent.  T2 is T1 with every
+    rank x renamed (x + 1) mod N.  For N = 2**k the leaves of T1 are the odd
+    ranks and those of T2 the even ranks.  Returns (children, top) of T1 and
+    of T2; children lists are left first."""
+    ch1: Dict[int, List[int]] = {x: [] for x in range(N)}
+    if N >= 2:
+        root = 1 << ((N - 1).bit_length() - 1)
+        ch1[0] = [root]
+        for x in range(1, N):
+            bl = x & -x
+            if bl >= 2:
+                ch1[x].append(x - bl // 2)
+                c = bl // 2
+                while c >= 1 and x + c >= N:
+                    c //= 2
+                if c >= 1:
+                    ch1[x].append(x + c)
+    ch2 = {(x + 1) % N: [(y + 1) % N for y in ys] for x, ys in ch1.items()}
+    return ch1, 0, ch2, 1 % N
+
+
+def _tree_heights(ch: Dict[int, List[int]], top: int) -> Dict[int, int]:
+    h: Dict[int, int] = {}
+
+    def H(x: int) -> int:
+        if x not in h:
+            h[x] = 1 + max((H(y) for y in ch[x]), default=-1)
+        return h[x]
+
+    H(top)
+    return h
+
+
+def _tree_depths(ch: Dict[int, List[int]], top: int) -> Dict[int, int]:
+    dep = {top: 0}
+    todo = [top]
+    while todo:
+        x = todo.pop()
+        for y in ch[x]:
+            dep[y] = dep[x] + 1
+            todo.append(y)
+    return dep
+
+
+def double_tree_all_reduce(xs, op="sum", dtype="f32", trace=None):
+    """Double binary tree AllReduce ([AR-notes], "算法三": the message is cut
+    in two halves, each half does a Reduce and a Broadcast on one of the two
+    trees, both trees at once).  Elements [0, M//2) use T1 and [M//2, M) T2.
+    Reduce: at step t every node of height t sends its partial up; a node's
+    partial is op(op(own, partial of left child), partial of right child),
+    children folded left first once both have arrived.  Broadcast: at step t
+    the nodes of depth t send the top's result (bf16 rounded once at the top)
+    to their children.  The two trees share the step counter."""
+    N = len(xs)
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    acc = [to_acc(x, dtype) for x in xs]
+    out = [np.empty(M, dtype=np.uint16 if dtype == "bf16" else acc[0].dtype) for _ in range(N)]
+    if N == 1:
+        return [from_acc(acc[0], dtype)]
+    ch1, top1, ch2, top2 = dbt_trees(N)
+    h = M // 2
+    trees = [(ch1, top1, 0, h), (ch2, top2, h, M)]
+    hts = [_tree_heights(c, t) for c, t, _, _ in trees]
+    deps = [_tree_depths(c, t) for c, t, _, _ in trees]
+    H = max(hts[0][trees[0][1]], hts[1][trees[1][1]])
+    parents = [{y: x for x, ys in c.items() for y in ys} for c, _, _, _ in trees]
+    inbox: List[Dict[int, np.ndarray]] = [dict(), dict()]
+    for t in range(H):
+        step = []
+        for k, (ch, top, lo, hi) in enumerate(trees):
+            for x in sorted(x for x in ch if hts[k][x] == t and x != top):
+                part = acc[x][lo:hi].copy()
+                for y in ch[x]:
+                    part = combine(op, part, inbox[k][y])
+                inbox[k][x] = part
+                tr.sent[x] += hi - lo
+                step.append((x, parents[k][x], (lo, hi), hi - lo))
+        tr.steps.append(step)
+    for k, (ch, top, lo, hi) in enumerate(trees):
+        part = acc[top][lo:hi].copy()
+        for y in ch[top]:
+            part = combine(op, part, inbox[k][y])
+        out[top][lo:hi] = from_acc(part, dtype)
+    for t in range(H):
+        step = []
+        for k, (ch, top, lo, hi) in enumerate(trees):
+            for x in sorted(x for x in ch if deps[k][x] == t):
+                for y in ch[x]:
+                    out[y][lo:hi] = out[x][lo:hi]
+                    tr.sent[x] += hi - lo
+                    step.append((x, y, (lo, hi), hi - lo))
+        tr.steps.append(step)
+    return out
+
+
+def dbt_fold_elements(vals: np.ndarray, idx: np.ndarray, M: int, op: str, dtype: str) -> np.ndarray:
+    """Closed form of the double tree's result at sampled elements: the
+    recursive subtree fold F(x) = op(op(x_x, F(left)), F(right)) of T1 for
+    idx < M//2 and of T2 otherwise, evaluated at the top."""
+    vals = np.asarray(vals)
+    N = vals.shape[0]
+    idx = np.asarray(idx)
+    if N == 1:
+        return from_acc(to_acc(vals[0], dtype), dtype)
+    ch1, top1, ch2, top2 = dbt_trees(N)
+
+    def F(ch, x, cols):
+        a = to_acc(vals[x, cols], dtype)
+        for y in ch[x]:
+            a = combine(op, a, F(ch, y, cols))
+        return a
+
+    out = np.empty(len(idx), dtype=np.uint16 if dtype == "bf16" else to_acc(vals[0, :1], dtype).dtype)
+    first = idx < M // 2
+    cols = np.arange(len(idx))
+    if first.any():
+        out[first] = from_acc(F(ch1, top1, cols[first]), dtype)
+    if (~first).any():
+        out[~first] = from_acc(F(ch2, top2, cols[~first]), dtype)
+    return out
+
+
+# --------------------------------------------------------------------------
+# 2-port ring
+# --------------------------------------------------------------------------
+
+def ring2_chain_lengths(N: int) -> Tuple[int, int]:
+    """(a, b): the clockwise chain of a chunk covers the a ranks before its
+    owner, the counter-clockwise chain the b ranks after it; a + b = N - 1."""
+    return (N - 1 + 1) // 2, (N - 1) // 2
+
+
+def ring2_all_reduce(xs, op="sum", dtype="f32", trace=None):
+    """2-port ring AllReduce ([AR-notes], "2-port Ring 优化": with two DMA
+    engines the chunks go round the ring in both directions and the number of
+    steps halves).  Reading: chunk c is owned by rank c.  Its ReduceScatter
+    runs two chains toward the owner at once: a clockwise one that starts at
+    rank c-a and moves +1 per step, and a counter-clockwise one that starts
+    at rank c+b and moves -1 per step (a = ceil((N-1)/2), b = floor((N-1)/2));
+    a rank folds its own value into the partial it receives, op(own,
+    partial); the owner folds its own value into the clockwise partial,
+    keeps the counter-clockwise partial until then, and ends with
+    op(op(x_c, P_cw), P_ccw).  The AllGather sends the finished chunk a ranks
+    clockwise and b ranks counter-clockwise.  Each step a rank sends one
+    chunk on each port."""
+    N = len(xs)
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    acc = [to_acc(x, dtype) for x in xs]
+    own = [a.copy() for a in acc]
+    bnd = chunk_bounds(M, N)
+    a, b = ring2_chain_lengths(N)
+    held_ccw: Dict[int, np.ndarray] = {}
+    for s in range(a):
+        snap = []
+        for c in range(N):
+            lo, hi = bnd[c], bnd[c + 1]
+            # clockwise: the partial at rank c-a+s moves to c-a+s+1
+            src = (c - a + s) % N
+            snap.append(("cw", c, src, (src + 1) % N, acc[src][lo:hi].copy()))
+            if s < b:
+                src = (c + b - s) % N
+                snap.append(("ccw", c, src, (src - 1) % N, acc[src][lo:hi].copy()))
+        step = []
+        for kind, c, src, dst, part in snap:
+            lo, hi = bnd[c], bnd[c + 1]
+            if dst == c and kind == "ccw":
+                held_ccw[c] = part
+            elif dst == c:
+                acc[c][lo:hi] = combine(op, own[c][lo:hi], part)
+            else:
+                acc[dst][lo:hi] = combine(op, own[dst][lo:hi], part)
+            tr.sent[src] += hi - lo
+            step.append((src, dst, (kind, c), hi - lo))
+        tr.steps.append(step)
+    res = [None] * N
+    for c in range(N):
+        lo, hi = bnd[c], bnd[c + 1]
+        if c in held_ccw:
+            acc[c][lo:hi] = combine(op, acc[c][lo:hi], held_ccw[c])
+    out = [np.empty(M, dtype=np.uint16 if dtype == "bf16" else acc[0].dtype) for _ in range(N)]
+    for c in range(N):
+        lo, hi = bnd[c], bnd[c + 1]
+        out[c][lo:hi] = from_acc(acc[c][lo:hi], dtype)
+    for s in range(a):
+        snap = []
+        for c in range(N):
+            lo, hi = bnd[c], bnd[c + 1]
+            src = (c + s) % N
+            snap.append(("cw", c, src, (src + 1) % N, out[src][lo:hi].copy()))
+            if s < b:
+                src = (c - s) % N
+                snap.append(("ccw", c, src, (src - 1) % N, out[src][lo:hi].copy()))
+        step = []
+        for kind, c, src, dst, v in snap:
+            lo, hi = bnd[c], bnd[c + 1]
+            out[dst][lo:hi] = v
+            tr.sent[src] += hi - lo
+            step.append((src, dst, (kind, c), hi - lo))
+        tr.steps.append(step)
+    return out
+
+
+def ring2_port(entry) -> int:
+    """Port of a 2-port ring transfer in a Trace: 0 clockwise, 1 the other way."""
+    return 0 if entry[2][0] == "cw" else 1
+
+
+def ring2_fold_elements(vals: np.ndarray, idx: np.ndarray, M: int, op: str, dtype: str) -> np.ndarray:
+    """Closed form of the 2-port ring at sampled elements of chunk c:
+    P_cw folds x_{c-a}, then x_{c-a+1} ... x_{c-1} as op(next, partial);
+    P_ccw folds x_{c+b}, then x_{c+b-1} ... x_{c+1}; out = op(op(x_c, P_cw),
+    P_ccw) (without P_ccw when b = 0)."""
+    vals = np.asarray(vals)
+    N = vals.shape[0]
+    c = chunk_of(idx, M, N)
+    cols = np.arange(vals.shape[1])
+    a, b = ring2_chain_lengths(N)
+    if N == 1:
+        return from_acc(to_acc(vals[0, cols], dtype), dtype)
+    pcw = to_acc(vals[(c - a) % N, cols], dtype)
+    for j in range(a - 1, 0, -1):
+        pcw = combine(op, to_acc(vals[(c - j) % N, cols], dtype), pcw)
+    out = combine(op, to_acc(vals[c, cols], dtype), pcw)
+    if b > 0:
+        pccw = to_acc(vals[(c + b) % N, cols], dtype)
+        for j in range(b - 1, 0, -1):
+            pccw = combine(op, to_acc(vals[(c + j) % N, cols], dtype), pccw)
+        out = combine(op, out, pccw)
+    return from_acc(out, dtype)
 
 
 # --------------------------------------------------------------------------
@@ -722,6 +1116,36 @@ def ring_time_model(M_bytes: float, N: int, alpha: float, beta_s_per_byte: float
     """T = 2(N-1) alpha + 2 (N-1)/N * M * beta ([Lesson3], "理论通信量与网络
     延迟模型", beta in seconds per byte)."""
     return 2 * (N - 1) * alpha + 2.0 * (N - 1) / N * M_bytes * beta_s_per_byte
+
+
+def step_time_model(tr: Trace, elem_bytes: float, alpha: float, beta_s_per_byte: float,
+                    port_of: Optional[Callable[[tuple], int]] = None) -> float:
+    """Time of a simulated schedule under the alpha-beta model, one step after
+    the other: each step costs alpha plus beta times the largest number of
+    bytes one rank sends through one port in it ([Lesson3], "理论通信量与网络
+    延迟模型"; one port per rank unless port_of assigns transfers to ports, as
+    for the 2-port ring whose two DMA engines send one chunk each per step,
+    [AR-notes], "2-port Ring 优化")."""
+    T = 0.0
+    for st in tr.steps:
+        per: Dict[Tuple[int, int], int] = {}
+        for e in st:
+            key = (e[0], port_of(e) if port_of else 0)
+            per[key] = per.get(key, 0) + e[3]
+        worst = max(per.values(), default=0)
+        T += alpha + worst * elem_bytes * beta_s_per_byte
+    return T
+
+
+def ring_tree_crossover(N: int, alpha: float, beta_s_per_byte: float) -> Dict[str, float]:
+    """Message size (bytes) at which ring and tree AllReduce take the same
+    time ([MLSys-6], "算法切换点"): 'exact' solves
+    2(N-1)a + 2(N-1)/N M b = 2 log2(N) a + 2 log2(N) M b, 'log' is the
+    passage's large-N form N a / (b log2 N) with beta as a rate, and 'rough'
+    drops the logarithm (N a / b)."""
+    lg = math.log2(N)
+    exact = (2 * (N - 1) - 2 * lg) * alpha / ((2 * lg - 2.0 * (N - 1) / N) * beta_s_per_byte)
+    return {"exact": exact, "log": N * alpha / beta_s_per_byte / lg, "rough": N * alpha / beta_s_per_byte}
 
 
 def norm_rel_error(y: np.ndarray, ref64: np.ndarray) -> float:

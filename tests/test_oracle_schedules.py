@@ -128,7 +128,10 @@ def test_step_counts():
 
 
 def test_pow2_schedules_reject_other_n():
+    """Halving-doubling ReduceScatter / AllGather need N = 2^k; the AllReduces
+    take any N by folding the first 2r ranks in pairs (tests/test_oracle_f1.py)."""
     xs = [np.zeros(6, dtype=np.int32)] * 3
-    for fn in (cs.hd_all_reduce, cs.butterfly_all_reduce, cs.hd_reduce_scatter):
-        with pytest.raises(ValueError):
-            fn(xs, "sum", "int32")
+    with pytest.raises(ValueError):
+        cs.hd_reduce_scatter(xs, "sum", "int32")
+    with pytest.raises(ValueError):
+        cs.hd_all_gather([np.zeros(2, dtype=np.int32)] * 3, "int32")
