@@ -67,10 +67,32 @@ typedef enum { CC_INT32 = 0, CC_FLOAT32 = 1, CC_BFLOAT16 = 2 } cc_dtype_t;
  * (核心概念, item 1: SUM, MAX, PROD). */
 typedef enum { CC_SUM = 0, CC_MAX = 1, CC_PROD = 2 } cc_op_t;
 
+/* Schedules.  Only CC_ALGO_RING and CC_ALGO_HALVING_DOUBLING (N = 2^k) serve
+ * ReduceScatter and AllGather; broadcast takes ring (chain) and
+ * halving-doubling (binomial doubling); AllToAll the ring (pairwise) only.
+ * Every schedule serves AllReduce, for any N:
+ *   HALVING_DOUBLING, BUTTERFLY with N not a power of two fold ranks
+ *     (2i, 2i+1), i < r = N - 2^floor(log2 N), into 2i first and copy the
+ *     result back last (AllReduce notes, 算法二 "非 2^k 处理", 算法四; blog
+ *     "分布式大模型集合通信", RHD "非 2 的整数次幂场景");
+ *   TREE: binomial reduce to rank 0 (rank i with i mod 2d = d sends to i-d at
+ *     distance d = 1, 2, 4 ...), broadcast back (textbook ch. 6, "Tree
+ *     AllReduce");
+ *   DOUBLE_TREE: elements [0, M/2) on tree T1, the rest on T2 -- T1 the
+ *     in-order binary tree over ranks 1..N-1 under rank 0, T2 the same with
+ *     ranks renamed x+1 mod N, complementary leaves for N = 2^k (AllReduce
+ *     notes, 算法三; textbook ch. 6, "双二叉树"); a node folds
+ *     op(op(own, left child), right child);
+ *   RING_2PORT: chunk c folded toward rank c by a clockwise chain over the
+ *     N/2 ranks before it and a counter-clockwise chain over the (N-1)/2 ranks
+ *     after it, op(op(x_c, cw), ccw) (AllReduce notes, "2-port Ring 优化"). */
 typedef enum {
   CC_ALGO_RING = 0,             /* AllReduce notes, 算法一 */
-  CC_ALGO_HALVING_DOUBLING = 1, /* AllReduce notes, 算法二; needs N = 2^k */
-  CC_ALGO_BUTTERFLY = 2         /* AllReduce notes, 算法四; AllReduce only, N = 2^k */
+  CC_ALGO_HALVING_DOUBLING = 1, /* AllReduce notes, 算法二 */
+  CC_ALGO_BUTTERFLY = 2,        /* AllReduce notes, 算法四; AllReduce only */
+  CC_ALGO_TREE = 3,             /* AllReduce only */
+  CC_ALGO_DOUBLE_TREE = 4,      /* AllReduce only */
+  CC_ALGO_RING_2PORT = 5        /* AllReduce only */
 } cc_algo_t;
 
 typedef enum {
@@ -87,7 +109,11 @@ typedef enum {
  *                  to every destination (read N*M, write N*M for AllReduce).
  *  fuse_depth = 1: stepwise -- one kernel per schedule step, each doing the
  *                  step's reads, combines and writes in HBM.
- *  fuse_depth = k: ring only -- k consecutive ring steps per kernel.
+ *  fuse_depth = k: ring only -- k consecutive ring steps per kernel (other
+ *                  schedules treat k > 1 as 1).  The fused DOUBLE_TREE
+ *                  kernel holds every rank's vector in registers and serves
+ *                  N <= 16; beyond that its stepwise schedule runs (same
+ *                  bits, and the stepwise workspace).
  *  workspace / workspace_bytes: caller-owned device memory, at least what
  *  cc_workspace_size returns for the same arguments (may be NULL/0 when that
  *  is 0).
@@ -218,6 +244,44 @@ cc_status_t cc_get_traffic(cc_coll_t coll, cc_algo_t algo, int nranks, size_t co
 /* The chunk boundaries used by every schedule: bounds[c] = floor(c*count/nranks),
  * c = 0..nranks (bounds must hold nranks+1 entries). */
 cc_status_t cc_chunk_bounds(size_t count, int nranks, size_t* bounds);
+
+/* Introspection of the stepwise AllReduce schedules that run as descriptor
+ * steps -- TREE, DOUBLE_TREE, RING_2PORT, and HALVING_DOUBLING / BUTTERFLY
+ * with N not a power of two: the exact operations the kernels perform, step
+ * by step, so that a host program can replay them (tests do, against an
+ * independent simulator).  One record per operation on elements
+ * [lo, lo+len) of the named ranks:
+ *   CC_PLAN_COPY:  out[dst] = out[in1]                 (finished values)
+ *   otherwise:     v = local; if IN1: v = op(v, in1); if IN2: v = op(v, in2)
+ *                  local = send[dst] if LOCAL_SEND else partial[dst];
+ *                  in1 / in2 = send of the rank if *_SEND else its partial;
+ *                  v -> out[dst] rounded if FINAL, else -> partial[dst];
+ *                  BOTH: the same value also for rank in1.
+ * Operations of one step read nothing another operation of that step
+ * writes.  out is cc_all_reduce's recv; partials are fp32/int32 values per
+ * rank and element.  With records == NULL only *nrecords is set; otherwise
+ * cap must hold all of them (CC_ERR_INVALID_ARG if not).  CC_ERR_UNSUPPORTED
+ * for the schedules with kernels of their own (ring; halving-doubling and
+ * butterfly with N = 2^k) and for nranks < 2. */
+#define CC_PLAN_LOCAL_SEND 1u
+#define CC_PLAN_IN1 2u
+#define CC_PLAN_IN1_SEND 4u
+#define CC_PLAN_IN2 8u
+#define CC_PLAN_IN2_SEND 16u
+#define CC_PLAN_FINAL 32u
+#define CC_PLAN_BOTH 64u
+#define CC_PLAN_COPY 128u
+typedef struct {
+  uint32_t step;
+  uint32_t flags;
+  int32_t dst;
+  int32_t in1;
+  int32_t in2;
+  uint64_t lo;
+  uint64_t len;
+} cc_plan_op_t;
+cc_status_t cc_all_reduce_plan(cc_algo_t algo, int nranks, size_t count, cc_plan_op_t* records, size_t cap,
+                               size_t* nrecords);
 
 const char* cc_status_string(cc_status_t status);
 const char* cc_last_error(void);

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libcc.so")
 CC_OK, CC_ERR_INVALID_ARG, CC_ERR_UNSUPPORTED, CC_ERR_NO_DEVICE, CC_ERR_HIP = range(5)
 DTYPES = {"int32": 0, "f32": 1, "bf16": 2}
 OPS = {"sum": 0, "max": 1, "prod": 2}
-ALGOS = {"ring": 0, "hd": 1, "butterfly": 2}
+ALGOS = {"ring": 0, "hd": 1, "butterfly": 2, "tree": 3, "double_tree": 4, "ring_2port": 5}
 COLLS = {"all_reduce": 0, "reduce_scatter": 1, "all_gather": 2, "broadcast": 3, "all_to_all": 4}
 ESIZE = {"int32": 4, "f32": 4, "bf16": 2}
 MAX_RANKS = 64
@@ -37,6 +37,14 @@ class Config(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int), ("fuse_depth", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("blocks_per_cu", ctypes.c_int), ("grid_sync", ctypes.c_int)]
+
+
+class PlanOp(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_uint32), ("flags", ctypes.c_uint32), ("dst", ctypes.c_int32),
+                ("in1", ctypes.c_int32), ("in2", ctypes.c_int32), ("lo", ctypes.c_uint64), ("len", ctypes.c_uint64)]
+
+
+PLAN_FLAGS = {"local_send": 1, "in1": 2, "in1_send": 4, "in2": 8, "in2_send": 16, "final": 32, "both": 64, "copy": 128}
 
 
 class CCError(RuntimeError):
@@ -70,6 +78,8 @@ EXPORTS = {
     "cc_get_traffic": [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
                        ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)],
     "cc_chunk_bounds": [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
+    "cc_all_reduce_plan": [ctypes.c_int, ctypes.c_int, ctypes.c_size_t, ctypes.POINTER(PlanOp), ctypes.c_size_t,
+                           ctypes.POINTER(ctypes.c_size_t)],
     "cc_status_string": [ctypes.c_int],
     "cc_last_error": [],
     "cc_version": [],
@@ -173,6 +183,17 @@ def all_reduce(send, recv=None, op: str = "sum", algo: str = "ring", fuse_depth:
     cfg = config(algo, fuse_depth, workspace, blocks_per_cu, grid_sync)
     _check(load().cc_all_reduce(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], OPS[op], N,
                                 ctypes.byref(cfg), _stream(stream)))
+
+
+def all_reduce_plan(algo: str, nranks: int, count: int):
+    """The descriptor steps a stepwise AllReduce runs (cc_all_reduce_plan), as
+    a list of dicts with keys step, flags, dst, in1, in2, lo, len."""
+    L = load()
+    n = ctypes.c_size_t(0)
+    _check(L.cc_all_reduce_plan(ALGOS[algo], nranks, count, None, 0, ctypes.byref(n)))
+    recs = (PlanOp * max(n.value, 1))()
+    _check(L.cc_all_reduce_plan(ALGOS[algo], nranks, count, recs, n.value, ctypes.byref(n)))
+    return [{f: getattr(recs[i], f) for f, _ in PlanOp._fields_} for i in range(n.value)]
 
 
 def bucket_plan(sizes: Sequence[int], elem_bytes: int, cap_bytes: int, align_elems: int = 1):

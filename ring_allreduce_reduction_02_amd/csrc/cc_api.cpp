@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "cc_launch.h"
+#include "cc_sched.h"
 
 using namespace cc;
 
@@ -69,7 +70,9 @@ cc_status_t common_checks(cc_coll_t coll, int nranks, cc_dtype_t dtype, const cc
   if (nranks < 1 || nranks > CC_MAX_RANKS)
     return fail(CC_ERR_INVALID_ARG, "nranks=%d outside [1, %d]", nranks, CC_MAX_RANKS);
   if ((int)dtype < 0 || (int)dtype > 2) return fail(CC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  if ((int)cfg->algo < 0 || (int)cfg->algo > 2) return fail(CC_ERR_INVALID_ARG, "unknown algo %d", (int)cfg->algo);
+  if ((int)cfg->algo < 0 || (int)cfg->algo > 5) return fail(CC_ERR_INVALID_ARG, "unknown algo %d", (int)cfg->algo);
+  if ((int)cfg->algo >= CC_ALGO_TREE && coll != CC_COLL_ALL_REDUCE)
+    return fail(CC_ERR_UNSUPPORTED, "tree, double tree and 2-port ring are AllReduce schedules");
   if (cfg->fuse_depth < 0) return fail(CC_ERR_INVALID_ARG, "fuse_depth=%d is negative", cfg->fuse_depth);
   if (cfg->blocks_per_cu < 0) return fail(CC_ERR_INVALID_ARG, "blocks_per_cu=%d is negative", cfg->blocks_per_cu);
   if (cfg->grid_sync != 0 && cfg->grid_sync != 1)
@@ -125,6 +128,28 @@ struct Bounds {
   }
 };
 
+// ---- AllReduce schedules that run as descriptor steps
+// the descriptor-step schedule of an AllReduce, or -1 (kernels of its own)
+int sched_of(int algo, int N) {
+  switch (algo) {
+    case CC_ALGO_TREE: return SCHED_TREE;
+    case CC_ALGO_DOUBLE_TREE: return SCHED_DBT;
+    case CC_ALGO_RING_2PORT: return SCHED_RING2;
+    case CC_ALGO_HALVING_DOUBLING: return is_pow2(N) ? -1 : SCHED_HD_PAIRS;
+    case CC_ALGO_BUTTERFLY: return is_pow2(N) ? -1 : SCHED_BFLY_PAIRS;
+  }
+  return -1;
+}
+
+constexpr int kDbtFusedMaxRanks = 16;
+
+// whether an AllReduce runs descriptor steps: the stepwise form of those
+// schedules, and the double tree beyond its fused kernel's rank limit
+bool runs_steps(const cc_config_t& cfg, int N) {
+  if (N < 2 || sched_of(cfg.algo, N) < 0) return false;
+  return cfg.fuse_depth >= 1 || (cfg.algo == CC_ALGO_DOUBLE_TREE && N > kDbtFusedMaxRanks);
+}
+
 // ---- workspace sizing (bytes); M is the full per-rank vector length
 uint64_t ws_need_data(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt);
 
@@ -138,9 +163,12 @@ uint64_t ws_need(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int 
 }
 
 uint64_t ws_need_data(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt) {
-  if (N <= 1 || cfg.fuse_depth == 0) return 0;
+  if (N <= 1) return 0;
   const uint64_t per_elem = M * 4;
   const uint64_t per_rank = N * rup(per_elem, 256);
+  // descriptor steps keep fp32 partials per rank for bf16
+  if (coll == CC_COLL_ALL_REDUCE && runs_steps(cfg, N)) return dt == DT_BF16 ? per_rank : 0;
+  if (cfg.fuse_depth == 0) return 0;
   const int k = std::min(cfg.fuse_depth, N - 1);
   if (coll == CC_COLL_ALL_REDUCE) {
     if (dt != DT_BF16) return 0;
@@ -223,8 +251,6 @@ cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc
   if (s) return s;
   if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
   const int N = nranks, dt = (int)dtype, es = elem_size(dt);
-  if (cfg.algo != CC_ALGO_RING && !is_pow2(N))
-    return fail(CC_ERR_UNSUPPORTED, "halving-doubling and butterfly need nranks = 2^k (got %d)", N);
   if (count == 0) return ok();
   const uint64_t M = count, nb = M * es;
   if ((s = check_side(send, nb, N, "send")) || (s = check_side(recv, nb, N, "recv"))) return s;
@@ -276,6 +302,27 @@ cc_status_t run_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, uint64_t M, int
     for (int s0 = 0; s0 < N - 1 && e == hipSuccess; s0 += k) e = launch_ring_ag_pass(g, s0, std::min(k, N - 1 - s0));
     return hip_status(e, "ring all_reduce (stepwise)");
   }
+  const int sch = sched_of(cfg.algo, N);
+  if (sch >= 0) {
+    if (runs_steps(cfg, N)) {
+      const Plan p = build_plan((SchedAlg)sch, N, M);
+      for (const auto& stp : p.steps)
+        for (size_t i = 0; i < stp.size() && e == hipSuccess; i += kMaxGDesc)
+          e = launch_gsteps(r, stp.data() + i, (int)std::min<size_t>(kMaxGDesc, stp.size() - i));
+      return hip_status(e, "all_reduce (descriptor steps)");
+    }
+    int m = 1;
+    while (2 * m <= N) m *= 2;
+    switch (cfg.algo) {
+      case CC_ALGO_TREE:
+        return hip_status(launch_tree_shaped(r, TREE_BFLY, m == N ? m : 2 * m, N, 0), "tree all_reduce");
+      case CC_ALGO_DOUBLE_TREE: return hip_status(launch_dbt_fused(r), "double tree all_reduce");
+      case CC_ALGO_RING_2PORT: return hip_status(launch_ring2_fused(r), "2-port ring all_reduce");
+      default:
+        return hip_status(launch_tree_shaped(r, cfg.algo == CC_ALGO_HALVING_DOUBLING ? TREE_HD : TREE_BFLY, m, m, N - m),
+                          "pair-folded all_reduce");
+    }
+  }
   const int tree = cfg.algo == CC_ALGO_HALVING_DOUBLING ? TREE_HD : TREE_BFLY;
   if (cfg.fuse_depth == 0) return hip_status(launch_tree_fused(r, tree), "tree all_reduce");
   const int acc_recv = dt != DT_BF16;
@@ -301,9 +348,7 @@ cc_status_t cc_all_reduce_buckets(cc_rankbuf_t send, cc_rankbuf_t recv, const si
   if (s) return s;
   if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
   const int N = nranks, dt = (int)dtype, es = elem_size(dt);
-  if (cfg.algo != CC_ALGO_RING && !is_pow2(N))
-    return fail(CC_ERR_UNSUPPORTED, "halving-doubling and butterfly need nranks = 2^k (got %d)", N);
-  if (nbuckets < 0) return fail(CC_ERR_INVALID_ARG, "nbuckets=%d is negative", nbuckets);
+    if (nbuckets < 0) return fail(CC_ERR_INVALID_ARG, "nbuckets=%d is negative", nbuckets);
   if (nbuckets == 0) return ok();
   if (!offsets || !counts) return fail(CC_ERR_INVALID_ARG, "offsets or counts is NULL");
   // buckets: non-empty ranges, pairwise disjoint, within every rank buffer
@@ -334,7 +379,9 @@ cc_status_t cc_all_reduce_buckets(cc_rankbuf_t send, cc_rankbuf_t recv, const si
   auto sub = [&](const cc_rankbuf_t& x, uint64_t off) {
     return cc_rankbuf_t{(char*)x.base + off * es, x.rank_stride_bytes};
   };
-  const bool one_launch = cfg.fuse_depth == 0 && N > 1 && N <= kMaxSegRanks && maxlen < (1ull << 31) &&
+  const bool seg_alg = cfg.algo == CC_ALGO_RING ||
+                       ((cfg.algo == CC_ALGO_HALVING_DOUBLING || cfg.algo == CC_ALGO_BUTTERFLY) && is_pow2(N));
+  const bool one_launch = seg_alg && cfg.fuse_depth == 0 && N > 1 && N <= kMaxSegRanks && maxlen < (1ull << 31) &&
                           num_tiles(maxlen, dt) * kMaxSeg < 0x7fffffffull;
   if (!one_launch) {
     for (const auto& r : rg)
@@ -602,6 +649,33 @@ cc_status_t cc_workspace_size(cc_coll_t coll, const cc_config_t* cfgp, int nrank
   return ok();
 }
 
+static_assert(CC_PLAN_LOCAL_SEND == GD_LOCAL_SEND && CC_PLAN_IN1 == GD_IN1 && CC_PLAN_IN1_SEND == GD_IN1_SEND &&
+                  CC_PLAN_IN2 == GD_IN2 && CC_PLAN_IN2_SEND == GD_IN2_SEND && CC_PLAN_FINAL == GD_FINAL &&
+                  CC_PLAN_BOTH == GD_BOTH && CC_PLAN_COPY == GD_COPY,
+              "public plan flags are the kernel's");
+
+cc_status_t cc_all_reduce_plan(cc_algo_t algo, int nranks, size_t count, cc_plan_op_t* records, size_t cap,
+                               size_t* nrecords) {
+  cc_config_t cfg = kDefaultCfg;
+  cfg.algo = algo;
+  cc_status_t s = common_checks(CC_COLL_ALL_REDUCE, nranks, CC_FLOAT32, &cfg);
+  if (s) return s;
+  if (!nrecords) return fail(CC_ERR_INVALID_ARG, "nrecords is NULL");
+  if (nranks < 2 || sched_of(algo, nranks) < 0)
+    return fail(CC_ERR_UNSUPPORTED, "this schedule runs kernels of its own (no descriptor plan)");
+  const Plan p = build_plan((SchedAlg)sched_of(algo, nranks), nranks, count);
+  size_t n = 0;
+  for (const auto& st : p.steps) n += st.size();
+  *nrecords = n;
+  if (!records) return ok();
+  if (cap < n) return fail(CC_ERR_INVALID_ARG, "cap=%zu is smaller than the %zu records", cap, n);
+  size_t i = 0;
+  for (size_t k = 0; k < p.steps.size(); ++k)
+    for (const GDesc& g : p.steps[k])
+      records[i++] = cc_plan_op_t{(uint32_t)k, g.flags, g.dst, g.in1, g.in2, g.lo, g.len};
+  return ok();
+}
+
 cc_status_t cc_get_traffic(cc_coll_t coll, cc_algo_t algo, int nranks, size_t count, cc_dtype_t dtype,
                            uint64_t* max_bytes, int* steps) {
   cc_config_t cfg = kDefaultCfg;
@@ -611,6 +685,17 @@ cc_status_t cc_get_traffic(cc_coll_t coll, cc_algo_t algo, int nranks, size_t co
   if (!max_bytes || !steps) return fail(CC_ERR_INVALID_ARG, "NULL output");
   const int N = nranks;
   const uint64_t es = elem_size((int)dtype);
+  if (coll == CC_COLL_ALL_REDUCE && sched_of(algo, N) >= 0) {
+    if (N < 2) {
+      *max_bytes = 0;
+      *steps = 0;
+      return ok();
+    }
+    const Plan p = build_plan((SchedAlg)sched_of(algo, N), N, count);
+    *max_bytes = *std::max_element(p.sent.begin(), p.sent.end()) * es;
+    *steps = p.net_steps;
+    return ok();
+  }
   if (algo != CC_ALGO_RING && coll != CC_COLL_BROADCAST && !is_pow2(N))
     return fail(CC_ERR_UNSUPPORTED, "needs nranks = 2^k");
   // chunk sizes of a per-rank vector of M elements

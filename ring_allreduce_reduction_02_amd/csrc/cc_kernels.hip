@@ -248,43 +248,60 @@ __device__ constexpr int ilog2() {
   return l;
 }
 
-// Pairwise tree over the ranks in load order t = 0..NR-1, adjacent pairs
-// first (a binary counter keeps one partial per level).  For butterfly the
-// order is the rank index itself (distance 1 first); for halving-doubling it
-// is the bit-reversed index, which pairs ranks at distance N/2 first.
+// Pairwise tree over the leaves in load order t = 0..n-1 (n <= NR), adjacent
+// pairs first (a binary counter keeps one partial per level).  For butterfly
+// and the binomial tree the order is the leaf index itself (distance 1
+// first); for halving-doubling it is the bit-reversed index, which pairs
+// leaves at distance NR/2 first.  When n < NR the partials left on the levels
+// set in n are merged from the smallest up, lower leaves on the left: the
+// binomial tree's result at rank 0 when leaves n.. are absent.
 template <int DT, int OP, int NR, int TREE, typename Load>
-__device__ __forceinline__ void tree_fold(Load load, typename Ty<DT>::A* out, int V) {
+__device__ __forceinline__ void tree_fold(Load load, typename Ty<DT>::A* out, int V, int n) {
   typedef typename Ty<DT>::A A;
   constexpr int L = ilog2<NR>();
   constexpr int VM = Ty<DT>::V;
   A stk[L + 1][VM];
 #pragma unroll
   for (int t = 0; t < NR; ++t) {
-    const int r = TREE == TREE_HD ? bitrev<L>(t) : t;
-    A v[VM];
-    load(r, v);
-    // t's trailing one bits = the completed subtrees to its left
-    int ones = 0;
-    while ((t >> ones) & 1) ++ones;
+    if (t < n) {
+      const int r = TREE == TREE_HD ? bitrev<L>(t) : t;
+      A v[VM];
+      load(r, v);
+      // t's trailing one bits = the completed subtrees to its left
+      int ones = 0;
+      while ((t >> ones) & 1) ++ones;
 #pragma unroll
-    for (int l = 0; l < L; ++l) {
-      if (l < ones) {
+      for (int l = 0; l < L; ++l) {
+        if (l < ones) {
 #pragma unroll
-        for (int i = 0; i < VM; ++i)
-          if (i < V) v[i] = opf<DT, OP>(stk[l][i], v[i]);
+          for (int i = 0; i < VM; ++i)
+            if (i < V) v[i] = opf<DT, OP>(stk[l][i], v[i]);
+        }
       }
+#pragma unroll
+      for (int l = 0; l <= L; ++l)
+        if (l == ones) {
+#pragma unroll
+          for (int i = 0; i < VM; ++i)
+            if (i < V) stk[l][i] = v[i];
+        }
     }
-#pragma unroll
-    for (int l = 0; l <= L; ++l)
-      if (l == ones) {
-#pragma unroll
-        for (int i = 0; i < VM; ++i)
-          if (i < V) stk[l][i] = v[i];
-      }
   }
+  if (n == NR) {
 #pragma unroll
-  for (int i = 0; i < VM; ++i)
-    if (i < V) out[i] = stk[L][i];
+    for (int i = 0; i < VM; ++i)
+      if (i < V) out[i] = stk[L][i];
+    return;
+  }
+  bool have = false;
+#pragma unroll
+  for (int l = 0; l <= L; ++l)
+    if ((n >> l) & 1) {
+#pragma unroll
+      for (int i = 0; i < VM; ++i)
+        if (i < V) out[i] = have ? opf<DT, OP>(stk[l][i], out[i]) : stk[l][i];
+      have = true;
+    }
 }
 
 enum Alg { ALG_RING = 0, ALG_HD = 1, ALG_BFLY = 2 };
@@ -293,14 +310,36 @@ enum Alg { ALG_RING = 0, ALG_HD = 1, ALG_BFLY = 2 };
 // s0 + r*ss + lane (s0 and ss workgroup-uniform, lane the lane's offset).
 // Ring: the chain x_start, x_start+1, ... folded as acc = op(x_next, acc);
 // trees: as above.  N is NR when NR > 0.
+// Trees (halving-doubling, butterfly, binomial): leaf v of the tree is rank
+// v + pairs, except that the first `pairs` leaves are the pair folds
+// op(x_2v, x_2v+1) (N not a power of two: the first 2r ranks fold in pairs
+// before the power-of-two schedule); `leaves` of them exist.
+struct TreeShape {
+  int leaves;
+  int pairs;
+};
+
 template <int DT, int OP, int NR, int ALG>
 __device__ __forceinline__ void fold_vec(const char* s0, uint64_t ss, int N, int start, uint32_t lane,
-                                         typename Ty<DT>::A* acc) {
+                                         typename Ty<DT>::A* acc, TreeShape ts = TreeShape{NR, 0}) {
   typedef typename Ty<DT>::A A;
   constexpr int V = Ty<DT>::V;
   if constexpr (ALG != ALG_RING) {
     tree_fold<DT, OP, NR, ALG == ALG_HD ? TREE_HD : TREE_BFLY>(
-        [&](int r, A* v) { unpack<DT>(ldg(s0 + (uint64_t)r * ss + lane), v); }, acc, V);
+        [&](int v, A* x) {
+          if (v < ts.pairs) {
+            const char* p = s0 + (uint64_t)(2 * v) * ss + lane;
+            const u32x4 a = ldg(p), b = ldg(p + ss);
+            A y[V];
+            unpack<DT>(a, x);
+            unpack<DT>(b, y);
+#pragma unroll
+            for (int i = 0; i < V; ++i) x[i] = opf<DT, OP>(x[i], y[i]);
+          } else {
+            unpack<DT>(ldg(s0 + (uint64_t)(v + ts.pairs) * ss + lane), x);
+          }
+        },
+        acc, V, ts.leaves);
   } else if constexpr (NR > 0) {
     u32x4 raw[NR];
     const char* p = s0 + (uint64_t)start * ss;
@@ -343,12 +382,19 @@ __device__ __forceinline__ void fold_vec(const char* s0, uint64_t ss, int N, int
 // The same fold for one element at byte offset `off` of every rank.
 template <int DT, int OP, int NR, int ALG>
 __device__ __forceinline__ typename Ty<DT>::A fold_elem(const char* sb, uint64_t ss, int N, int start,
-                                                        uint64_t off) {
+                                                        uint64_t off, TreeShape ts = TreeShape{NR, 0}) {
   typedef typename Ty<DT>::A A;
   if constexpr (ALG != ALG_RING) {
     A acc[Ty<DT>::V];
     tree_fold<DT, OP, NR, ALG == ALG_HD ? TREE_HD : TREE_BFLY>(
-        [&](int r, A* v) { v[0] = ld1<DT>(sb + (uint64_t)r * ss + off); }, acc, 1);
+        [&](int v, A* x) {
+          if (v < ts.pairs)
+            x[0] = opf<DT, OP>(ld1<DT>(sb + (uint64_t)(2 * v) * ss + off),
+                               ld1<DT>(sb + (uint64_t)(2 * v + 1) * ss + off));
+          else
+            x[0] = ld1<DT>(sb + (uint64_t)(v + ts.pairs) * ss + off);
+        },
+        acc, 1, ts.leaves);
     return acc[0];
   } else {
     A acc = ld1<DT>(sb + (uint64_t)start * ss + off);
@@ -368,6 +414,8 @@ struct FusedArgs {
   int N;
   int rs_mode;
   int vec_ok;
+  int tree_leaves;  // trees: leaves of the power-of-two tree (<= NR)
+  int tree_pairs;   // trees: leading leaves that are pair folds
   uint64_t bnd[kMaxRanks + 1];
 };
 
@@ -381,8 +429,14 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
   static_assert(kUnroll == 1, "one 16-byte vector per thread");
-  const int N = NR > 0 ? NR : a.N;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  // ring: N ranks (NR when fixed at compile time); trees: the runtime rank
+  // count, NR being the tree's leaf slots
+  const int N = (ALG == ALG_RING && NR > 0) ? NR : a.N;
+  // a tree AllReduce folds every element the same way whatever its chunk,
+  // so only a ReduceScatter needs the chunk of a tile
+  const int tiling = (ALG != ALG_RING && !a.rs_mode) ? 1 : N;
+  const TreeShape ts{a.tree_leaves, a.tree_pairs};
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, tiling, a.vec_ok);
   if (t.fast) {
     // Every rank's tile starts at a workgroup-uniform address; a lane adds
     // its own 16-byte offset (scalar base + 32-bit vector offset).
@@ -391,13 +445,13 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     const uint32_t lane = threadIdx.x * 16u;
     const uint64_t eb = t.e0 * SZ;
     A acc[V];
-    fold_vec<DT, OP, NR, ALG>(a.sb + eb, a.ss, N, start, lane, acc);
+    fold_vec<DT, OP, NR, ALG>(a.sb + eb, a.ss, N, start, lane, acc, ts);
     const u32x4 w = pack<DT>(acc);
     if (a.rs_mode) {
       stg(a.rb + (uint64_t)c * a.rs + (t.e0 - a.bnd[c]) * SZ + lane, w);
     } else {
       char* d = a.rb + eb;
-      if constexpr (NR > 0) {
+      if constexpr (ALG == ALG_RING && NR > 0) {
 #pragma unroll
         for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
       } else {
@@ -406,9 +460,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = chunk_in(a.bnd, N, e);
+      const uint32_t c = chunk_in(a.bnd, tiling, e);
       const int start = (ALG == ALG_RING && a.rs_mode) ? wrapN((int)c + 1, N) : (int)c;
-      const A acc = fold_elem<DT, OP, NR, ALG>(a.sb, a.ss, N, start, e * SZ);
+      const A acc = fold_elem<DT, OP, NR, ALG>(a.sb, a.ss, N, start, e * SZ, ts);
       if (a.rs_mode) {
         st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, acc);
       } else {
@@ -423,9 +477,190 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(FusedArgs a) {
   fused_body<DT, OP, NR, ALG_RING>(a);
 }
 
+// Halving-doubling (TREE_HD) and butterfly / binomial tree (TREE_BFLY) over
+// NR leaf slots; the binomial tree leaves slots N.. empty, N not a power of
+// two folds the first 2r ranks in pairs into the leading leaves.
 template <int DT, int OP, int NR, int TREE>
 __global__ __launch_bounds__(kBlock) void k_tree_fused(FusedArgs a) {
   fused_body<DT, OP, NR, TREE == TREE_HD ? ALG_HD : ALG_BFLY>(a);
+}
+
+// ------------------------------------------------------------------ double binary tree
+
+// Fold of the in-order binary tree over the leaf slots x[0..n) (n <= NR):
+// slot y with lowest set bit 2^j (j >= 1) has the left child y - 2^(j-1) and
+// the right child y + c, c the largest of 2^(j-1), 2^(j-2), ... with
+// y + c < n (none if there is none); a node is op(op(own, left), right).
+// Slot 0 sits on top of the root, the largest power of two below n.
+// Subtrees are folded level by level, every slot index fixed at compile
+// time; the clipping of right children near n only selects among them.
+template <int DT, int OP, int NR>
+__device__ __forceinline__ void dbt_fold(typename Ty<DT>::A (*x)[Ty<DT>::V], int n, int V,
+                                         typename Ty<DT>::A* out) {
+  constexpr int L = ilog2<NR>();
+#pragma unroll
+  for (int j = 1; j < L; ++j) {
+    const int b = 1 << j;
+#pragma unroll
+    for (int y = b; y < NR; y += 2 * b) {
+      if (y < n) {
+#pragma unroll
+        for (int i = 0; i < Ty<DT>::V; ++i)
+          if (i < V) x[y][i] = opf<DT, OP>(x[y][i], x[y - b / 2][i]);
+        bool done = false;
+#pragma unroll
+        for (int c = b / 2; c >= 1; c /= 2)
+          if (!done && y + c < NR && y + c < n) {
+#pragma unroll
+            for (int i = 0; i < Ty<DT>::V; ++i)
+              if (i < V) x[y][i] = opf<DT, OP>(x[y][i], x[y + c][i]);
+            done = true;
+          }
+      }
+    }
+  }
+  bool done = false;
+#pragma unroll
+  for (int p2 = NR / 2; p2 >= 1; p2 /= 2)
+    if (!done && p2 <= n - 1) {
+#pragma unroll
+      for (int i = 0; i < Ty<DT>::V; ++i)
+        if (i < V) out[i] = opf<DT, OP>(x[0][i], x[p2][i]);
+      done = true;
+    }
+  if (!done) {
+#pragma unroll
+    for (int i = 0; i < Ty<DT>::V; ++i)
+      if (i < V) out[i] = x[0][i];
+  }
+}
+
+// Double binary tree AllReduce: elements [0, M/2) use the tree above over
+// ranks in order, [M/2, M) the same tree with rank p in slot p-1 (slot s
+// holds rank s+1 mod N).  The host passes bnd = {0, M/2, M} so a tile lies in
+// one half on the vector path.
+template <int DT, int OP, int NR>
+__global__ __launch_bounds__(kBlock) void k_dbt_fused(FusedArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const int N = a.N;
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, 2, a.vec_ok);
+  if (t.fast) {
+    const int half = (int)t.c;
+    const uint32_t lane = threadIdx.x * 16u;
+    const uint64_t eb = t.e0 * SZ;
+    A x[NR][V];
+#pragma unroll
+    for (int s = 0; s < NR; ++s)
+      if (s < N) {
+        const int r = half == 0 ? s : (s + 1 == N ? 0 : s + 1);
+        unpack<DT>(ldg(a.sb + eb + (uint64_t)r * a.ss + lane), x[s]);
+      }
+    A acc[V];
+    dbt_fold<DT, OP, NR>(x, N, V, acc);
+    const u32x4 w = pack<DT>(acc);
+    char* d = a.rb + eb;
+    for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      const int half = e >= a.bnd[1] ? 1 : 0;
+      A x[NR][V];
+#pragma unroll
+      for (int s = 0; s < NR; ++s)
+        if (s < N) {
+          const int r = half == 0 ? s : (s + 1 == N ? 0 : s + 1);
+          x[s][0] = ld1<DT>(a.sb + (uint64_t)r * a.ss + e * SZ);
+        }
+      A acc[V];
+      dbt_fold<DT, OP, NR>(x, N, 1, acc);
+      for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc[0]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 2-port ring
+
+// Fold of a chain of `len` ranks starting at `first` and stepping by `dir`
+// (+1 or -1 mod N): acc = x_first, then acc = op(x_next, acc) -- the order a
+// partial picks up contributions as it travels rank to rank.  Loads are
+// issued eight at a time.
+template <int DT, int OP>
+__device__ __forceinline__ void chain_vec(const char* s0, uint64_t ss, int N, int first, int dir, int len,
+                                          uint32_t lane, typename Ty<DT>::A* acc) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  int r = first;
+  unpack<DT>(ldg(s0 + (uint64_t)r * ss + lane), acc);
+  for (int j = 1; j < len; j += 8) {
+    u32x4 raw[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (j + q < len) {
+        r += dir;
+        r = r == N ? 0 : (r < 0 ? N - 1 : r);
+        raw[q] = ldg(s0 + (uint64_t)r * ss + lane);
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (j + q < len) {
+        A y[V];
+        unpack<DT>(raw[q], y);
+        opv<DT, OP>(y, acc);
+      }
+  }
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ typename Ty<DT>::A chain_elem(const char* sb, uint64_t ss, int N, int first, int dir,
+                                                         int len, uint64_t off) {
+  typedef typename Ty<DT>::A A;
+  int r = first;
+  A acc = ld1<DT>(sb + (uint64_t)r * ss + off);
+  for (int j = 1; j < len; ++j) {
+    r += dir;
+    r = r == N ? 0 : (r < 0 ? N - 1 : r);
+    acc = opf<DT, OP>(ld1<DT>(sb + (uint64_t)r * ss + off), acc);
+  }
+  return acc;
+}
+
+// 2-port ring AllReduce: chunk c (owned by rank c) is folded by a clockwise
+// chain over ranks c-a .. c (the owner last) and a counter-clockwise chain
+// over ranks c+b .. c+1, a = N/2, b = (N-1)/2; the result op(cw, ccw) goes
+// to every rank.
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_ring2_fused(FusedArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const int N = a.N;
+  const int ca = N / 2, cb = (N - 1) / 2;
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  if (t.fast) {
+    const int c = (int)t.c;
+    const uint32_t lane = threadIdx.x * 16u;
+    const uint64_t eb = t.e0 * SZ;
+    A acc[V];
+    chain_vec<DT, OP>(a.sb + eb, a.ss, N, c - ca < 0 ? c - ca + N : c - ca, 1, ca + 1, lane, acc);
+    if (cb > 0) {
+      A acc2[V];
+      chain_vec<DT, OP>(a.sb + eb, a.ss, N, c + cb >= N ? c + cb - N : c + cb, -1, cb, lane, acc2);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = opf<DT, OP>(acc[i], acc2[i]);
+    }
+    const u32x4 w = pack<DT>(acc);
+    char* d = a.rb + eb;
+    for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      const int c = (int)chunk_in(a.bnd, N, e);
+      A acc = chain_elem<DT, OP>(a.sb, a.ss, N, c - ca < 0 ? c - ca + N : c - ca, 1, ca + 1, e * SZ);
+      if (cb > 0)
+        acc = opf<DT, OP>(acc, chain_elem<DT, OP>(a.sb, a.ss, N, c + cb >= N ? c + cb - N : c + cb, -1, cb, e * SZ));
+      for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ bucketed AllReduce
@@ -806,6 +1041,136 @@ __global__ __launch_bounds__(kBlock) void k_ring_ag_pass(GatArgs a) {
   ring_ag_tile<SZ>(a, blockIdx.x, a.s0, a.k);
 }
 
+// ------------------------------------------------------------------ descriptor steps
+
+// One step of a schedule given as descriptors (tree, double tree, 2-port
+// ring, halving-doubling and butterfly for N not a power of two).  Each
+// descriptor covers elements [lo, lo+len) of the ranks it names:
+//   copy:     recv[dst] = recv[in1]                       (finished values)
+//   combine:  v = op(op(local, in1), in2)  (in1, in2 optional)
+//             local = send[dst] or partial[dst]; in1/in2 = send or partial
+//             of their rank; v goes to partial[dst] or, final, rounded to
+//             recv[dst]; `both` stores it for rank in1 too (the butterfly's
+//             pairwise exchange, done by one thread for both ranks).
+// partial[r] is recv[r] when the accumulator type is the element type
+// (int32, fp32), else an fp32 rank-strided staging buffer.
+struct GArgs {
+  const char* sb;
+  uint64_t ss;
+  char* rb;
+  uint64_t rs;
+  char* wb;       // fp32 partials (bf16), or nullptr: partials in recv
+  uint64_t ws;
+  int n;
+  uint64_t vecmask;
+  uint32_t tpre[kMaxGDesc + 1];
+  GDesc d[kMaxGDesc];
+};
+
+template <int DT>
+__device__ __forceinline__ char* part_ptr(const GArgs& a, int r, uint64_t e) {
+  return a.wb ? a.wb + (uint64_t)r * a.ws + e * 4 : a.rb + (uint64_t)r * a.rs + e * Ty<DT>::SZ;
+}
+
+template <int DT>
+__device__ __forceinline__ void part_load_vec(const GArgs& a, int r, uint64_t e, typename Ty<DT>::A* v) {
+  if (a.wb)
+    ldw_vec<DT>(a.wb + (uint64_t)r * a.ws + e * 4, v);
+  else
+    unpack<DT>(ldg(a.rb + (uint64_t)r * a.rs + e * Ty<DT>::SZ), v);
+}
+
+template <int DT>
+__device__ __forceinline__ void part_store_vec(const GArgs& a, int r, uint64_t e, const typename Ty<DT>::A* v) {
+  if (a.wb)
+    stw_vec<DT>(a.wb + (uint64_t)r * a.ws + e * 4, v);
+  else
+    stg(a.rb + (uint64_t)r * a.rs + e * Ty<DT>::SZ, pack<DT>(v));
+}
+
+template <int DT>
+__device__ __forceinline__ typename Ty<DT>::A part_load1(const GArgs& a, int r, uint64_t e) {
+  return a.wb ? ldw1<DT>(a.wb + (uint64_t)r * a.ws + e * 4) : ld1<DT>(a.rb + (uint64_t)r * a.rs + e * Ty<DT>::SZ);
+}
+
+template <int DT>
+__device__ __forceinline__ void part_store1(const GArgs& a, int r, uint64_t e, typename Ty<DT>::A v) {
+  if (a.wb)
+    stw1<DT>(a.wb + (uint64_t)r * a.ws + e * 4, v);
+  else
+    st1<DT>(a.rb + (uint64_t)r * a.rs + e * Ty<DT>::SZ, v);
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_gsteps(GArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const uint32_t b = blockIdx.x;
+  int k = 0;
+  for (int step = kMaxGDesc / 2; step >= 1; step /= 2)
+    if (k + step < a.n && a.tpre[k + step] <= b) k += step;
+  const GDesc& g = a.d[k];
+  const uint64_t tile = (uint64_t)kBlock * V;
+  const uint64_t e0 = g.lo + (uint64_t)(b - a.tpre[k]) * tile;
+  const uint64_t e1 = e0 + tile < g.lo + g.len ? e0 + tile : g.lo + g.len;
+  const unsigned f = g.flags;
+  if (((a.vecmask >> k) & 1) && e1 - e0 == tile) {
+    const uint64_t e = e0 + (uint64_t)threadIdx.x * V;
+    if (f & GD_COPY) {
+      stg(a.rb + (uint64_t)g.dst * a.rs + e * SZ, ldg(a.rb + (uint64_t)g.in1 * a.rs + e * SZ));
+      return;
+    }
+    A acc[V], y[V];
+    if (f & GD_LOCAL_SEND) unpack<DT>(ldg(a.sb + (uint64_t)g.dst * a.ss + e * SZ), acc);
+    else part_load_vec<DT>(a, g.dst, e, acc);
+    if (f & GD_IN1) {
+      if (f & GD_IN1_SEND) unpack<DT>(ldg(a.sb + (uint64_t)g.in1 * a.ss + e * SZ), y);
+      else part_load_vec<DT>(a, g.in1, e, y);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = opf<DT, OP>(acc[i], y[i]);
+    }
+    if (f & GD_IN2) {
+      if (f & GD_IN2_SEND) unpack<DT>(ldg(a.sb + (uint64_t)g.in2 * a.ss + e * SZ), y);
+      else part_load_vec<DT>(a, g.in2, e, y);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = opf<DT, OP>(acc[i], y[i]);
+    }
+    if (f & GD_FINAL) {
+      const u32x4 w = pack<DT>(acc);
+      stg(a.rb + (uint64_t)g.dst * a.rs + e * SZ, w);
+      if (f & GD_BOTH) stg(a.rb + (uint64_t)g.in1 * a.rs + e * SZ, w);
+    } else {
+      part_store_vec<DT>(a, g.dst, e, acc);
+      if (f & GD_BOTH) part_store_vec<DT>(a, g.in1, e, acc);
+    }
+  } else {
+    for (uint64_t e = e0 + threadIdx.x; e < e1; e += kBlock) {
+      if (f & GD_COPY) {
+        if constexpr (SZ == 2)
+          *(uint16_t*)(a.rb + (uint64_t)g.dst * a.rs + e * 2) = *(const uint16_t*)(a.rb + (uint64_t)g.in1 * a.rs + e * 2);
+        else
+          *(uint32_t*)(a.rb + (uint64_t)g.dst * a.rs + e * 4) = *(const uint32_t*)(a.rb + (uint64_t)g.in1 * a.rs + e * 4);
+        continue;
+      }
+      A acc = (f & GD_LOCAL_SEND) ? ld1<DT>(a.sb + (uint64_t)g.dst * a.ss + e * SZ) : part_load1<DT>(a, g.dst, e);
+      if (f & GD_IN1)
+        acc = opf<DT, OP>(acc, (f & GD_IN1_SEND) ? ld1<DT>(a.sb + (uint64_t)g.in1 * a.ss + e * SZ)
+                                                  : part_load1<DT>(a, g.in1, e));
+      if (f & GD_IN2)
+        acc = opf<DT, OP>(acc, (f & GD_IN2_SEND) ? ld1<DT>(a.sb + (uint64_t)g.in2 * a.ss + e * SZ)
+                                                  : part_load1<DT>(a, g.in2, e));
+      if (f & GD_FINAL) {
+        st1<DT>(a.rb + (uint64_t)g.dst * a.rs + e * SZ, acc);
+        if (f & GD_BOTH) st1<DT>(a.rb + (uint64_t)g.in1 * a.rs + e * SZ, acc);
+      } else {
+        part_store1<DT>(a, g.dst, e, acc);
+        if (f & GD_BOTH) part_store1<DT>(a, g.in1, e, acc);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ one-launch stepwise ring
 
 // The stepwise ring AllReduce in one launch.  The passes (k ring steps each;
@@ -1041,6 +1406,7 @@ FusedArgs fused_args(const Red& r) {
   a.sb = r.send.base; a.ss = r.send.stride;
   a.rb = r.recv.base; a.rs = r.recv.stride;
   a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
+  a.tree_leaves = r.N; a.tree_pairs = 0;
   for (int c = 0; c <= r.N; ++c) a.bnd[c] = r.bnd[c];
   return a;
 }
@@ -1147,6 +1513,97 @@ hipError_t launch_tree_fused(const Red& r, int tree) {
       default: return hipErrorInvalidValue;
     }
 #undef CC_TREE_CASE
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_tree_shaped(const Red& r, int tree, int nr, int leaves, int pairs) {
+  FusedArgs a = fused_args(r);
+  a.tree_leaves = leaves;
+  a.tree_pairs = pairs;
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+#define CC_SHAPED_CASE(NR)                                                                    \
+  case NR:                                                                                    \
+    if (tree == TREE_HD)                                                                      \
+      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_HD>), grid, blk, lds, r.st, a);       \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_BFLY>), grid, blk, lds, r.st, a);     \
+    break;
+    switch (nr) {
+      CC_SHAPED_CASE(2)
+      CC_SHAPED_CASE(4)
+      CC_SHAPED_CASE(8)
+      CC_SHAPED_CASE(16)
+      CC_SHAPED_CASE(32)
+      CC_SHAPED_CASE(64)
+      default: return hipErrorInvalidValue;
+    }
+#undef CC_SHAPED_CASE
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_dbt_fused(const Red& r) {
+  FusedArgs a = fused_args(r);
+  a.bnd[0] = 0;
+  a.bnd[1] = r.M / 2;
+  a.bnd[2] = r.M;
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
+  int nr = 2;
+  while (nr < r.N) nr *= 2;
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    switch (nr) {
+      case 2: hipLaunchKernelGGL((k_dbt_fused<DT, OP, 2>), grid, blk, lds, r.st, a); break;
+      case 4: hipLaunchKernelGGL((k_dbt_fused<DT, OP, 4>), grid, blk, lds, r.st, a); break;
+      case 8: hipLaunchKernelGGL((k_dbt_fused<DT, OP, 8>), grid, blk, lds, r.st, a); break;
+      case 16: hipLaunchKernelGGL((k_dbt_fused<DT, OP, 16>), grid, blk, lds, r.st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_ring2_fused(const Red& r) {
+  const FusedArgs a = fused_args(r);
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    hipLaunchKernelGGL((k_ring2_fused<DT, OP>), grid, blk, lds, r.st, a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_gsteps(const Red& r, const GDesc* d, int n) {
+  GArgs a;
+  a.sb = r.send.base; a.ss = r.send.stride;
+  a.rb = r.recv.base; a.rs = r.recv.stride;
+  a.wb = r.ws.base; a.ws = r.ws.stride;
+  a.n = 0; a.vecmask = 0; a.tpre[0] = 0;
+  const int es = elem_size(r.dt);
+  const uint64_t tile = (uint64_t)kBlock * vec_elems(r.dt);
+  for (int i = 0; i < n && a.n < kMaxGDesc; ++i) {
+    if (d[i].len == 0) continue;
+    const int j = a.n++;
+    a.d[j] = d[i];
+    a.tpre[j + 1] = a.tpre[j] + (uint32_t)((d[i].len + tile - 1) / tile);
+    // vector path: the element offset keeps 16-byte alignment for the
+    // elements and for the fp32 partials
+    const bool al = r.vec_ok && ((d[i].lo * es) & 15u) == 0 && (!a.wb || ((d[i].lo * 4) & 15u) == 0);
+    if (al) a.vecmask |= 1ull << j;
+  }
+  for (int j = a.n; j < kMaxGDesc; ++j) a.tpre[j + 1] = a.tpre[a.n];
+  if (a.n == 0) return hipSuccess;
+  const dim3 grid(a.tpre[a.n]), blk(kBlock);
+  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 4, kSkewedTarget);
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    hipLaunchKernelGGL((k_gsteps<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }

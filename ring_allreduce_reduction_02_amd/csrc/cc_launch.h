@@ -75,6 +75,39 @@ hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_i
 // butterfly step with distance d.
 hipError_t launch_bfly_step(const Red& r, int d, int first, int last, int acc_in_recv);
 
+// ---- tree-shaped fused AllReduces for schedules beyond the power-of-two ones
+// binomial tree (TREE_BFLY order over `leaves` = N of NR = 2^ceil(log2 N)
+// slots), and halving-doubling / butterfly for N not a power of two (NR = m =
+// 2^floor(log2 N) leaves, the first `pairs` = N - m of them pair folds)
+hipError_t launch_tree_shaped(const Red& r, int tree, int nr, int leaves, int pairs);
+// double binary tree (N <= 16) and 2-port ring (any N)
+hipError_t launch_dbt_fused(const Red& r);
+hipError_t launch_ring2_fused(const Red& r);
+
+// ---- descriptor steps (GDesc flags)
+enum : unsigned {
+  GD_LOCAL_SEND = 1u,   // local operand from send[dst] (else partial[dst])
+  GD_IN1 = 2u,          // combine with in1
+  GD_IN1_SEND = 4u,     // in1 from send (else partial)
+  GD_IN2 = 8u,          // combine with in2 after in1
+  GD_IN2_SEND = 16u,
+  GD_FINAL = 32u,       // write the rounded result to recv[dst] (else partial[dst])
+  GD_BOTH = 64u,        // also store the result for rank in1
+  GD_COPY = 128u,       // recv[dst] = recv[in1], no arithmetic
+};
+struct GDesc {
+  uint64_t lo;
+  uint64_t len;
+  int dst;
+  int in1;
+  int in2;
+  unsigned flags;
+};
+constexpr int kMaxGDesc = 64;
+// one step: descriptors whose destination ranges do not overlap; partials in
+// r.ws (fp32, rank-strided) when it is set, else in recv
+hipError_t launch_gsteps(const Red& r, const GDesc* d, int n);
+
 // ---- bucketed AllReduce: up to kMaxSeg independent fused AllReduces over
 // element ranges [off, off+len) of the same rank buffers, in one launch.
 constexpr int kMaxSeg = 16;

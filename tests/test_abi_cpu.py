@@ -155,10 +155,11 @@ def test_all_reduce_rejects_bad_arguments():
     assert _ar(_rb(None, 4096), ok_r, 100, 4) == ccgpu.CC_ERR_INVALID_ARG  # NULL base
     assert _ar(_rb(FAKE, 200), ok_r, 100, 4) == ccgpu.CC_ERR_INVALID_ARG   # ranks overlap (400 B > stride)
     assert _ar(ok_s, _rb(FAKE + 100, 4096), 100, 4) == ccgpu.CC_ERR_INVALID_ARG   # send/recv overlap
-    assert _ar(ok_s, ok_r, 100, 3, cfg=ccgpu.Config(1, 0, None, 0, 0)) == ccgpu.CC_ERR_UNSUPPORTED
-    assert _ar(ok_s, ok_r, 100, 6, cfg=ccgpu.Config(2, 0, None, 0, 0)) == ccgpu.CC_ERR_UNSUPPORTED
+    # halving-doubling and butterfly AllReduce take any N (pair fold): only the device is missing
+    assert _ar(ok_s, ok_r, 100, 3, cfg=ccgpu.Config(1, 0, None, 0, 0)) == ccgpu.CC_ERR_NO_DEVICE
+    assert _ar(ok_s, ok_r, 100, 6, cfg=ccgpu.Config(2, 0, None, 0, 0)) == ccgpu.CC_ERR_NO_DEVICE
     assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(0, -1, None, 0, 0)) == ccgpu.CC_ERR_INVALID_ARG
-    assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(5, 0, None, 0, 0)) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(6, 0, None, 0, 0)) == ccgpu.CC_ERR_INVALID_ARG
     assert _ar(ok_s, ok_r, 100, 4, cfg=ccgpu.Config(0, 0, None, 0, -2)) == ccgpu.CC_ERR_INVALID_ARG
     # bf16 stepwise ring needs a workspace
     assert _ar(ok_s, ok_r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, None, 0, 0)) == ccgpu.CC_ERR_INVALID_ARG

@@ -64,6 +64,8 @@ def test_bucketed_all_reduce_validation():
     assert call([], []) == ccgpu.CC_OK
     assert call([0, 10], [20, 5]) == ccgpu.CC_ERR_INVALID_ARG            # overlap
     assert call([0], [2000]) == ccgpu.CC_ERR_INVALID_ARG                 # beyond the 4096 B stride
-    assert call([0], [10], N=3, cfg_=ccgpu.Config(1, 0, None, 0, 0)) == ccgpu.CC_ERR_UNSUPPORTED
+    # halving-doubling with N = 3 runs each bucket as its own pair-folded AllReduce
+    assert call([0], [10], N=3, cfg_=ccgpu.Config(1, 0, None, 0, 0)) == ccgpu.CC_ERR_NO_DEVICE
+    assert call([0], [10], N=4, cfg_=ccgpu.Config(7, 0, None, 0, 0)) == ccgpu.CC_ERR_INVALID_ARG   # unknown algo
     assert L.cc_all_reduce_buckets(s, r, None, None, 2, 1, 0, 4, ctypes.byref(cfg), None) == ccgpu.CC_ERR_INVALID_ARG
     assert call([0, 40], [10, 0]) == ccgpu.CC_ERR_NO_DEVICE               # valid: only the device is missing
