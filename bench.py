@@ -256,6 +256,68 @@ def _avg_ms(fn, steps=10, warmup=3):
     return r["total_ms"] / steps
 
 
+def schedules(dev):
+    """Every AllReduce schedule on one GPU: fused throughput at the headline
+    size (N = 8, 67,108,864 fp32 per rank; N = 12 for the pair-folded
+    halving-doubling and butterfly), and the stepwise schedules over per-rank
+    sizes 4 KiB .. 64 MiB at N = 8 (HIP-graph replays) with an alpha-beta fit
+    each, the measured ring/tree crossover and the model's crossover from the
+    ring's fitted alpha and beta."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import calib, ccgpu
+    out = {"fused": {}, "stepwise_n8": {}}
+    gen = torch.Generator(device=dev).manual_seed(20261202)
+    N, M = 8, 1 << 26
+    send = torch.randn(N, M, generator=gen, device=dev) * 1e-3
+    recv = torch.empty_like(send)
+    for algo in ("ring", "hd", "butterfly", "tree", "double_tree", "ring_2port"):
+        ms = _avg_ms(lambda: ccgpu.all_reduce(send, recv, algo=algo), 10, 3)
+        out["fused"][f"{algo}_n8"] = {"ms": round(ms, 4), "GBps": round(2 * N * M * 4 / ms / 1e6, 1)}
+    del send, recv
+    torch.cuda.empty_cache()
+    N12, M12 = 12, 1 << 25
+    send = torch.randn(N12, M12, generator=gen, device=dev) * 1e-3
+    recv = torch.empty_like(send)
+    for algo in ("hd", "butterfly"):
+        ms = _avg_ms(lambda: ccgpu.all_reduce(send, recv, algo=algo), 10, 3)
+        out["fused"][f"{algo}_n12_pair_folded"] = {"ms": round(ms, 4), "GBps": round(2 * N12 * M12 * 4 / ms / 1e6, 1)}
+    del send, recv
+    torch.cuda.empty_cache()
+
+    sizes = [1 << k for k in range(10, 25, 2)]          # 1 Ki .. 16 Mi fp32 = 4 KiB .. 64 MiB per rank
+    send = torch.randn(N, sizes[-1], generator=gen, device=dev) * 1e-3
+    recv = torch.empty_like(send)
+    for _ in range(10):
+        ccgpu.all_reduce(send, recv)
+    torch.cuda.synchronize()
+    times = {}
+    for algo in ("ring", "hd", "butterfly", "tree", "double_tree", "ring_2port"):
+        pts, st, by, ts = [], [], [], []
+        for m in sizes:
+            s_, r_ = send[:, :m], recv[:, :m]
+            per = 16 if m <= (1 << 20) else 2
+            t, how = _time_gpu(lambda: ccgpu.all_reduce(s_, r_, algo=algo, fuse_depth=1), 10, per)
+            b, n = ccgpu.get_traffic("all_reduce", N, m, "f32", algo)
+            st.append(n); by.append(b); ts.append(t / 1e3)
+            pts.append({"bytes_per_rank": m * 4, "us": round(t * 1e3, 3), "steps": n, "max_bytes_sent_per_rank": b})
+        times[algo] = ts
+        out["stepwise_n8"][algo] = {"fit": calib.fit_alpha_beta(st, by, ts), "points": pts}
+    ring_fit = out["stepwise_n8"]["ring"]["fit"]
+    model = calib.ring_tree_crossover(N, ring_fit["alpha_us_per_step"] * 1e-6, ring_fit["beta_ps_per_byte"] * 1e-12)
+    measured = {}
+    for other in ("tree", "double_tree", "butterfly"):
+        first = next((sizes[i] * 4 for i in range(len(sizes)) if times["ring"][i] < times[other][i]), None)
+        measured[f"ring_faster_than_{other}_from_bytes_per_rank"] = first
+    out["crossover_n8"] = {"measured": measured, "model_from_ring_fit_bytes": model,
+                           "note": "model: the pages' T_ring = T_tree with the ring's fitted alpha, beta; "
+                                   "on one GPU a tree step's HBM traffic scales with its number of senders, "
+                                   "which the per-link model does not see"}
+    del send, recv
+    torch.cuda.empty_cache()
+    return out
+
+
 def norm_rel_err_fp64(send, recv, offsets, counts, step=1 << 24):
     """max over ranks of ||y_r - y64|| / ||y64|| over the given element
     ranges, y64 = the order-free fp64 sum of the inputs (a measurement of the
@@ -495,6 +557,8 @@ def main():
         out["alpha_beta"] = alpha_beta(dev)
         log("other workloads")
         out["workloads"] = workloads(dev)
+        log("schedules")
+        out["schedules"] = schedules(dev)
     if not args.no_cpu_baseline:
         log("oracle on the host")
         out["cpu_baseline"] = cpu_baseline(N, min(args.cpu_sample, M))

@@ -74,3 +74,16 @@ def fit_launch_alpha_beta(steps: Sequence[float], bytes_sent: Sequence[float],
         "n_star_bytes": alpha / beta if beta > 0 else float("inf"),
         "max_rel_residual": float(np.max(np.abs(pred - t) / t)),
     }
+
+
+def ring_tree_crossover(N: int, alpha: float, beta_s_per_byte: float) -> Dict[str, float]:
+    """Per-rank message size (bytes) at which the ring and the tree AllReduce
+    models take equal time (textbook ch. 6, "算法切换点"):
+    2(N-1) a + 2 (N-1)/N M b = 2 log2(N) a + 2 log2(N) M b solved for M
+    ('exact'), and the large-N forms N a / (b log2 N) ('log') and N a / b
+    ('rough') the passage simplifies it to."""
+    import math
+    lg = math.log2(N)
+    den = (2 * lg - 2.0 * (N - 1) / N) * beta_s_per_byte
+    exact = (2 * (N - 1) - 2 * lg) * alpha / den if den > 0 else float("inf")
+    return {"exact": exact, "log": N * alpha / beta_s_per_byte / lg, "rough": N * alpha / beta_s_per_byte}

@@ -255,7 +255,11 @@ __device__ constexpr int ilog2() {
 // leaves at distance NR/2 first.  When n < NR the partials left on the levels
 // set in n are merged from the smallest up, lower leaves on the left: the
 // binomial tree's result at rank 0 when leaves n.. are absent.
-template <int DT, int OP, int NR, int TREE, typename Load>
+// The code stays straight-line so that every load can be issued before the
+// folds that wait for it: with n < NR (FULL false) the stack updates of
+// absent leaves are discarded by selects, and with CLAMP their loads read
+// leaf n-1 again (a loader that reads registers takes the leaf as is).
+template <int DT, int OP, int NR, int TREE, bool FULL, bool CLAMP = !FULL, typename Load>
 __device__ __forceinline__ void tree_fold(Load load, typename Ty<DT>::A* out, int V, int n) {
   typedef typename Ty<DT>::A A;
   constexpr int L = ilog2<NR>();
@@ -263,31 +267,33 @@ __device__ __forceinline__ void tree_fold(Load load, typename Ty<DT>::A* out, in
   A stk[L + 1][VM];
 #pragma unroll
   for (int t = 0; t < NR; ++t) {
-    if (t < n) {
-      const int r = TREE == TREE_HD ? bitrev<L>(t) : t;
-      A v[VM];
+    const int r = TREE == TREE_HD ? bitrev<L>(t) : t;
+    A v[VM];
+    if constexpr (CLAMP)
+      load(r < n ? r : n - 1, v);
+    else
       load(r, v);
-      // t's trailing one bits = the completed subtrees to its left
-      int ones = 0;
-      while ((t >> ones) & 1) ++ones;
+    // t's trailing one bits = the completed subtrees to its left
+    int ones = 0;
+    while ((t >> ones) & 1) ++ones;
 #pragma unroll
-      for (int l = 0; l < L; ++l) {
-        if (l < ones) {
+    for (int l = 0; l < L; ++l) {
+      if (l < ones) {
 #pragma unroll
-          for (int i = 0; i < VM; ++i)
-            if (i < V) v[i] = opf<DT, OP>(stk[l][i], v[i]);
-        }
+        for (int i = 0; i < VM; ++i)
+          if (i < V) v[i] = opf<DT, OP>(stk[l][i], v[i]);
       }
-#pragma unroll
-      for (int l = 0; l <= L; ++l)
-        if (l == ones) {
-#pragma unroll
-          for (int i = 0; i < VM; ++i)
-            if (i < V) stk[l][i] = v[i];
-        }
     }
+    const bool keep = FULL || t < n;
+#pragma unroll
+    for (int l = 0; l <= L; ++l)
+      if (l == ones) {
+#pragma unroll
+        for (int i = 0; i < VM; ++i)
+          if (i < V) stk[l][i] = keep ? v[i] : stk[l][i];
+      }
   }
-  if (n == NR) {
+  if (FULL || n == NR) {
 #pragma unroll
     for (int i = 0; i < VM; ++i)
       if (i < V) out[i] = stk[L][i];
@@ -304,7 +310,16 @@ __device__ __forceinline__ void tree_fold(Load load, typename Ty<DT>::A* out, in
     }
 }
 
-enum Alg { ALG_RING = 0, ALG_HD = 1, ALG_BFLY = 2 };
+// ALG_BTREE: the binomial tree over exactly NR ranks (NR not a power of two),
+// its leaf count fixed at compile time.
+enum Alg { ALG_RING = 0, ALG_HD = 1, ALG_BFLY = 2, ALG_BTREE = 3 };
+
+template <int N>
+__device__ constexpr int pow2_ceil() {
+  int p = 1;
+  while (p < N) p *= 2;
+  return p;
+}
 
 // Fold of one 16-byte vector of every rank, rank r's vector at
 // s0 + r*ss + lane (s0 and ss workgroup-uniform, lane the lane's offset).
@@ -324,22 +339,33 @@ __device__ __forceinline__ void fold_vec(const char* s0, uint64_t ss, int N, int
                                          typename Ty<DT>::A* acc, TreeShape ts = TreeShape{NR, 0}) {
   typedef typename Ty<DT>::A A;
   constexpr int V = Ty<DT>::V;
-  if constexpr (ALG != ALG_RING) {
-    tree_fold<DT, OP, NR, ALG == ALG_HD ? TREE_HD : TREE_BFLY>(
+  if constexpr (ALG == ALG_BTREE) {
+    tree_fold<DT, OP, pow2_ceil<NR>(), TREE_BFLY, false, false>(
         [&](int v, A* x) {
-          if (v < ts.pairs) {
-            const char* p = s0 + (uint64_t)(2 * v) * ss + lane;
-            const u32x4 a = ldg(p), b = ldg(p + ss);
-            A y[V];
-            unpack<DT>(a, x);
-            unpack<DT>(b, y);
-#pragma unroll
-            for (int i = 0; i < V; ++i) x[i] = opf<DT, OP>(x[i], y[i]);
-          } else {
-            unpack<DT>(ldg(s0 + (uint64_t)(v + ts.pairs) * ss + lane), x);
-          }
+          if (v < NR) unpack<DT>(ldg(s0 + (uint64_t)v * ss + lane), x);
         },
-        acc, V, ts.leaves);
+        acc, V, NR);
+  } else if constexpr (ALG != ALG_RING) {
+    constexpr int TR = ALG == ALG_HD ? TREE_HD : TREE_BFLY;
+    if (ts.leaves == NR && ts.pairs == 0) {
+      tree_fold<DT, OP, NR, TR, true>(
+          [&](int v, A* x) { unpack<DT>(ldg(s0 + (uint64_t)v * ss + lane), x); }, acc, V, NR);
+    } else {
+      // leaf v: op(x_2v, x_2v+1) for v < pairs, else x_(v+pairs); both loads
+      // are issued either way (the second repeats the first's address)
+      tree_fold<DT, OP, NR, TR, false>(
+          [&](int v, A* x) {
+            const bool pr = v < ts.pairs;
+            const char* p = s0 + (uint64_t)(pr ? 2 * v : v + ts.pairs) * ss + lane;
+            const u32x4 ra = ldg(p), rb = ldg(pr ? p + ss : p);
+            A y[V];
+            unpack<DT>(ra, x);
+            unpack<DT>(rb, y);
+#pragma unroll
+            for (int i = 0; i < V; ++i) x[i] = pr ? opf<DT, OP>(x[i], y[i]) : x[i];
+          },
+          acc, V, ts.leaves);
+    }
   } else if constexpr (NR > 0) {
     u32x4 raw[NR];
     const char* p = s0 + (uint64_t)start * ss;
@@ -384,9 +410,17 @@ template <int DT, int OP, int NR, int ALG>
 __device__ __forceinline__ typename Ty<DT>::A fold_elem(const char* sb, uint64_t ss, int N, int start,
                                                         uint64_t off, TreeShape ts = TreeShape{NR, 0}) {
   typedef typename Ty<DT>::A A;
-  if constexpr (ALG != ALG_RING) {
+  if constexpr (ALG == ALG_BTREE) {
     A acc[Ty<DT>::V];
-    tree_fold<DT, OP, NR, ALG == ALG_HD ? TREE_HD : TREE_BFLY>(
+    tree_fold<DT, OP, pow2_ceil<NR>(), TREE_BFLY, false, false>(
+        [&](int v, A* x) {
+          if (v < NR) x[0] = ld1<DT>(sb + (uint64_t)v * ss + off);
+        },
+        acc, 1, NR);
+    return acc[0];
+  } else if constexpr (ALG != ALG_RING) {
+    A acc[Ty<DT>::V];
+    tree_fold<DT, OP, NR, ALG == ALG_HD ? TREE_HD : TREE_BFLY, false>(
         [&](int v, A* x) {
           if (v < ts.pairs)
             x[0] = opf<DT, OP>(ld1<DT>(sb + (uint64_t)(2 * v) * ss + off),
@@ -485,6 +519,12 @@ __global__ __launch_bounds__(kBlock) void k_tree_fused(FusedArgs a) {
   fused_body<DT, OP, NR, TREE == TREE_HD ? ALG_HD : ALG_BFLY>(a);
 }
 
+// Binomial tree over exactly N ranks, N not a power of two.
+template <int DT, int OP, int N>
+__global__ __launch_bounds__(kBlock) void k_btree_fused(FusedArgs a) {
+  fused_body<DT, OP, N, ALG_BTREE>(a);
+}
+
 // ------------------------------------------------------------------ double binary tree
 
 // Fold of the in-order binary tree over the leaf slots x[0..n) (n <= NR):
@@ -550,13 +590,21 @@ __global__ __launch_bounds__(kBlock) void k_dbt_fused(FusedArgs a) {
     const int half = (int)t.c;
     const uint32_t lane = threadIdx.x * 16u;
     const uint64_t eb = t.e0 * SZ;
-    A x[NR][V];
+    // slot s holds rank s (first half) or s+1 mod N (second half): a scalar
+    // pointer walk; all loads are issued before any is used
+    const char* const b0 = a.sb + eb;
+    const char* p = half ? b0 + a.ss : b0;
+    u32x4 raw[NR];
 #pragma unroll
     for (int s = 0; s < NR; ++s)
       if (s < N) {
-        const int r = half == 0 ? s : (s + 1 == N ? 0 : s + 1);
-        unpack<DT>(ldg(a.sb + eb + (uint64_t)r * a.ss + lane), x[s]);
+        raw[s] = ldg(p + lane);
+        p = (half && s + 2 == N) ? b0 : p + a.ss;
       }
+    A x[NR][V];
+#pragma unroll
+    for (int s = 0; s < NR; ++s)
+      if (s < N) unpack<DT>(raw[s], x[s]);
     A acc[V];
     dbt_fold<DT, OP, NR>(x, N, V, acc);
     const u32x4 w = pack<DT>(acc);
@@ -629,12 +677,15 @@ __device__ __forceinline__ typename Ty<DT>::A chain_elem(const char* sb, uint64_
 // chain over ranks c-a .. c (the owner last) and a counter-clockwise chain
 // over ranks c+b .. c+1, a = N/2, b = (N-1)/2; the result op(cw, ccw) goes
 // to every rank.
-template <int DT, int OP>
+// NR > 0: N <= NR (N == NR when EXACT, a compile-time rank count); every
+// rank's vector is loaded first, in ring order from rank c-a, then both
+// chains fold from registers.  NR = 0: any N, the chains load as they go.
+template <int DT, int OP, int NR, bool EXACT>
 __global__ __launch_bounds__(kBlock) void k_ring2_fused(FusedArgs a) {
   typedef typename Ty<DT>::A A;
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
-  const int N = a.N;
+  const int N = EXACT ? NR : a.N;
   const int ca = N / 2, cb = (N - 1) / 2;
   const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
@@ -642,12 +693,48 @@ __global__ __launch_bounds__(kBlock) void k_ring2_fused(FusedArgs a) {
     const uint32_t lane = threadIdx.x * 16u;
     const uint64_t eb = t.e0 * SZ;
     A acc[V];
-    chain_vec<DT, OP>(a.sb + eb, a.ss, N, c - ca < 0 ? c - ca + N : c - ca, 1, ca + 1, lane, acc);
-    if (cb > 0) {
-      A acc2[V];
-      chain_vec<DT, OP>(a.sb + eb, a.ss, N, c + cb >= N ? c + cb - N : c + cb, -1, cb, lane, acc2);
+    if constexpr (NR > 0) {
+      // raw[j] = rank c - a + j: the clockwise chain is raw[0..a], the
+      // counter-clockwise chain raw[N-1] down to raw[a+1]
+      u32x4 raw[NR];
+      int r = c - ca < 0 ? c - ca + N : c - ca;
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = opf<DT, OP>(acc[i], acc2[i]);
+      for (int j = 0; j < NR; ++j)
+        if (j < N) {
+          raw[j] = ldg(a.sb + eb + (uint64_t)r * a.ss + lane);
+          r = r + 1 == N ? 0 : r + 1;
+        }
+      unpack<DT>(raw[0], acc);
+#pragma unroll
+      for (int j = 1; j < NR; ++j)
+        if (j <= ca) {
+          A y[V];
+          unpack<DT>(raw[j], y);
+          opv<DT, OP>(y, acc);
+        }
+      if (cb > 0) {
+        A acc2[V];
+#pragma unroll
+        for (int j = NR - 1; j >= 1; --j)
+          if (j == N - 1) unpack<DT>(raw[j], acc2);
+#pragma unroll
+        for (int j = NR - 2; j >= 1; --j)
+          if (j < N - 1 && j > ca) {
+            A y[V];
+            unpack<DT>(raw[j], y);
+            opv<DT, OP>(y, acc2);
+          }
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = opf<DT, OP>(acc[i], acc2[i]);
+      }
+    } else {
+      chain_vec<DT, OP>(a.sb + eb, a.ss, N, c - ca < 0 ? c - ca + N : c - ca, 1, ca + 1, lane, acc);
+      if (cb > 0) {
+        A acc2[V];
+        chain_vec<DT, OP>(a.sb + eb, a.ss, N, c + cb >= N ? c + cb - N : c + cb, -1, cb, lane, acc2);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = opf<DT, OP>(acc[i], acc2[i]);
+      }
     }
     const u32x4 w = pack<DT>(acc);
     char* d = a.rb + eb;
@@ -1525,6 +1612,19 @@ hipError_t launch_tree_shaped(const Red& r, int tree, int nr, int leaves, int pa
   const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    if (tree == TREE_BFLY && pairs == 0 && leaves < nr && leaves <= 16) {
+      // binomial tree with a compile-time rank count
+      switch (leaves) {
+#define CC_BTREE_CASE(NN) \
+  case NN: hipLaunchKernelGGL((k_btree_fused<DT, OP, NN>), grid, blk, lds, r.st, a); break;
+        CC_BTREE_CASE(3) CC_BTREE_CASE(5) CC_BTREE_CASE(6) CC_BTREE_CASE(7) CC_BTREE_CASE(9)
+        CC_BTREE_CASE(10) CC_BTREE_CASE(11) CC_BTREE_CASE(12) CC_BTREE_CASE(13) CC_BTREE_CASE(14)
+        CC_BTREE_CASE(15)
+#undef CC_BTREE_CASE
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
 #define CC_SHAPED_CASE(NR)                                                                    \
   case NR:                                                                                    \
     if (tree == TREE_HD)                                                                      \
@@ -1574,7 +1674,14 @@ hipError_t launch_ring2_fused(const Red& r) {
   const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_ring2_fused<DT, OP>), grid, blk, lds, r.st, a);
+    switch (r.N) {
+      case 4: hipLaunchKernelGGL((k_ring2_fused<DT, OP, 4, true>), grid, blk, lds, r.st, a); break;
+      case 8: hipLaunchKernelGGL((k_ring2_fused<DT, OP, 8, true>), grid, blk, lds, r.st, a); break;
+      case 16: hipLaunchKernelGGL((k_ring2_fused<DT, OP, 16, true>), grid, blk, lds, r.st, a); break;
+      default:
+        if (r.N <= 16) hipLaunchKernelGGL((k_ring2_fused<DT, OP, 16, false>), grid, blk, lds, r.st, a);
+        else hipLaunchKernelGGL((k_ring2_fused<DT, OP, 0, false>), grid, blk, lds, r.st, a);
+    }
     return hipGetLastError();
   });
 }

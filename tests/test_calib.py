@@ -41,6 +41,18 @@ def test_launch_alpha_beta_recovery_over_several_rank_counts():
     assert fit["max_rel_residual"] < 1e-9
 
 
+def test_ring_tree_crossover_balances_the_two_models():
+    a, b = 5e-6, 1 / 50e9
+    for N in (8, 64, 100, 1024):
+        c = calib.ring_tree_crossover(N, a, b)
+        lg = np.log2(N)
+        ring = 2 * (N - 1) * a + 2 * (N - 1) / N * c["exact"] * b
+        tree = 2 * lg * a + 2 * lg * c["exact"] * b
+        assert ring == pytest.approx(tree)
+    # the passage's printed example: about 3.8 MB for alpha 5 us, 50 GB/s, N = 100
+    assert calib.ring_tree_crossover(100, a, b)["log"] / 1e6 == pytest.approx(3.76, abs=0.01)
+
+
 def test_bench_refuses_more_than_one_gpu():
     import subprocess, sys, os
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
