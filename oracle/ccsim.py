@@ -904,6 +904,163 @@ def ring2_fold_elements(vals: np.ndarray, idx: np.ndarray, M: int, op: str, dtyp
 
 
 # --------------------------------------------------------------------------
+# hierarchical (multi-dimensional) AllReduce
+# --------------------------------------------------------------------------
+
+def hier_coords(r: int, dims: Sequence[int]) -> List[int]:
+    """Coordinates of rank r, level 0 (the innermost, fastest network level)
+    varying fastest: r = r_0 + p_0 (r_1 + p_1 (r_2 + ...))."""
+    out = []
+    for p in dims:
+        out.append(r % p)
+        r //= p
+    return out
+
+
+def hier_groups(dims: Sequence[int], level: int) -> List[List[int]]:
+    """The groups of level `level`: ranks that agree on every coordinate but
+    that level's, each listed by its coordinate at the level."""
+    N = int(np.prod(dims))
+    step = int(np.prod(dims[:level])) if level else 1
+    groups = []
+    for r in range(N):
+        if hier_coords(r, dims)[level] == 0:
+            groups.append([r + k * step for k in range(dims[level])])
+    return groups
+
+
+def hierarchical_all_reduce(xs, dims: Sequence[int], op: str = "sum", dtype: str = "f32",
+                            trace: Optional[Trace] = None):
+    """Multi-dimensional AllReduce ([AR-notes], "算法五：多维分层 AllReduce":
+    N = prod p_i, a ReduceScatter per level from the innermost out, then the
+    AllGathers in reverse order; [MLSys-6], "分层全归约": ReduceScatter inside
+    the node, AllReduce among the ranks holding the same shard across nodes,
+    AllGather inside the node).  Reading: levels 0 .. d-2 run standalone ring
+    ReduceScatters within their groups (the member with coordinate c keeps
+    chunk c of the group's current range, the fold starting one member after
+    it); the outermost level runs a ring AllReduce on that shard; the levels
+    then run ring AllGathers back to the full vector.  Partials stay in the
+    accumulator type throughout; bf16 rounds once at the end."""
+    dims = [int(p) for p in dims]
+    N = int(np.prod(dims))
+    if len(xs) != N:
+        raise ValueError("len(xs) must be prod(dims)")
+    M = int(np.asarray(xs[0]).shape[0])
+    tr = trace if trace is not None else Trace()
+    tr.sent = [0] * N
+    acc = [to_acc(x, dtype) for x in xs]
+    rng = [(0, M)] * N
+    d = len(dims)
+
+    def run(members, fn):
+        lo, hi = rng[members[0]]
+        assert all(rng[m] == (lo, hi) for m in members)
+        views = [acc[m][lo:hi] for m in members]
+        sub = Trace()
+        sub.sent = [0] * len(members)
+        fn(views, sub)
+        return lo, hi, sub
+
+    def merge_steps(per_group):
+        # groups of one level run side by side: their k-th steps are one step
+        depth = max((len(sub.steps) for _, sub in per_group), default=0)
+        for k in range(depth):
+            step = []
+            for members, sub in per_group:
+                if k < len(sub.steps):
+                    step.extend((members[s], members[t], w, n) for (s, t, w, n) in sub.steps[k])
+            tr.steps.append(step)
+        for members, sub in per_group:
+            for j, m in enumerate(members):
+                tr.sent[m] += sub.sent[j]
+
+    for i in range(d - 1):
+        per = []
+        for members in hier_groups(dims, i):
+            lo, hi, sub = run(members, lambda v, t: _ring_rs_phase(v, chunk_bounds(len(v[0]), len(v)), op, -1, t))
+            b = chunk_bounds(hi - lo, len(members))
+            for c, m in enumerate(members):
+                rng[m] = (lo + b[c], lo + b[c + 1])
+            per.append((members, sub))
+        merge_steps(per)
+    per = []
+    for members in hier_groups(dims, d - 1):
+        def ar(v, t):
+            p = len(v)
+            b = chunk_bounds(len(v[0]), p)
+            _ring_rs_phase(v, b, op, 0, t)
+            _ring_ag_phase(v, b, [(r + 1) % p for r in range(p)], t)
+        _, _, sub = run(members, ar)
+        per.append((members, sub))
+    merge_steps(per)
+    for i in range(d - 2, -1, -1):
+        per = []
+        for members in hier_groups(dims, i):
+            # the group's parent range is the union of its members' chunks
+            lo = min(rng[m][0] for m in members)
+            hi = max(rng[m][1] for m in members)
+            for m in members:
+                rng[m] = (lo, hi)
+            _, _, sub = run(members, lambda v, t: _ring_ag_phase(v, chunk_bounds(len(v[0]), len(v)),
+                                                                  list(range(len(v))), t))
+            per.append((members, sub))
+        merge_steps(per)
+    return [from_acc(a, dtype) for a in acc]
+
+
+def hier_fold_elements(vals: np.ndarray, idx: np.ndarray, M: int, dims: Sequence[int], op: str,
+                       dtype: str) -> np.ndarray:
+    """Closed form of the hierarchical AllReduce at sampled elements: the
+    element's chunk c_i at every level (splitting the range it is in p_i
+    ways, level by level), then nested ring chains -- the outermost over its
+    coordinate starting at c_(d-1) (AllReduce order), each inner one over its
+    coordinate starting at c_i + 1 (standalone ReduceScatter order), every
+    chain folding op(next, partial)."""
+    vals = np.asarray(vals)
+    dims = [int(p) for p in dims]
+    d = len(dims)
+    strides = [int(np.prod(dims[:i])) for i in range(d)]
+    out = []
+    for k, e in enumerate(np.asarray(idx)):
+        lo, hi = 0, M
+        cs = []
+        for p in dims:
+            b = chunk_bounds(hi - lo, p)
+            c = int(np.searchsorted(np.asarray(b), e - lo, side="right") - 1)
+            cs.append(c)
+            lo, hi = lo + b[c], lo + b[c + 1]
+
+        def F(level, base):
+            p = dims[level]
+            start = (cs[level] + (0 if level == d - 1 else 1)) % p
+
+            def leaf(coord):
+                r = base + coord * strides[level]
+                return to_acc(vals[r:r + 1, k], dtype) if level == 0 else F(level - 1, r)
+
+            a = leaf(start)
+            for j in range(1, p):
+                a = combine(op, leaf((start + j) % p), a)
+            return a
+
+        out.append(F(d - 1, 0))
+    return from_acc(np.concatenate(out) if out else np.zeros(0, np.float32 if dtype != "int32" else np.int32), dtype)
+
+
+def multidim_time_model(M_bytes: float, dims: Sequence[int], alphas: Sequence[float],
+                        betas_s_per_byte: Sequence[float]) -> List[float]:
+    """Per-level times of the multi-dimensional AllReduce ([AR-notes], eq.
+    cc-ar-multidim, BlueConnect): level i costs 2(p_i - 1) alpha_i +
+    2 (p_i - 1)/p_i * M / P_(i-1) * beta_i, P_(i-1) the product of the inner
+    levels' sizes; the total is their sum."""
+    out, P = [], 1
+    for p, a, b in zip(dims, alphas, betas_s_per_byte):
+        out.append(2 * (p - 1) * a + 2.0 * (p - 1) / p * M_bytes / P * b)
+        P *= p
+    return out
+
+
+# --------------------------------------------------------------------------
 # broadcast
 # --------------------------------------------------------------------------
 
