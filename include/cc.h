@@ -283,6 +283,63 @@ typedef struct {
 cc_status_t cc_all_reduce_plan(cc_algo_t algo, int nranks, size_t count, cc_plan_op_t* records, size_t cap,
                                size_t* nrecords);
 
+/* Hierarchical (multi-dimensional) AllReduce (AllReduce notes, 算法五
+ * "多维分层 AllReduce" and its BlueConnect example; textbook ch. 6,
+ * "分层全归约": ReduceScatter inside the node, AllReduce across nodes among
+ * the ranks holding the same shard, AllGather inside the node).
+ * The N = dims[0] * ... * dims[ndims-1] ranks form a grid, rank
+ * r = r_0 + dims[0] (r_1 + dims[1] (r_2 + ...)), level 0 the innermost (the
+ * fastest network tier).  A group of level i is the dims[i] ranks that
+ * differ only in coordinate i.  Levels 0 .. ndims-2 run standalone ring
+ * ReduceScatters inside their groups: the member with coordinate c keeps
+ * chunk c of the group's current range (the range split at floor bounds),
+ * its fold starting one member after it.  The outermost level runs a ring
+ * AllReduce (as cc_all_reduce, schedule ring) on the shard each rank then
+ * holds, and ring AllGathers run back out, level ndims-2 first.  Each
+ * receiving member folds op(own, incoming): along a group the chain is
+ * op(next, partial).  Levels of size 1 do nothing; when
+ * dims[ndims-1] == 1 no AllReduce runs and the AllGathers follow the
+ * ReduceScatters.  bf16 partials stay fp32 and are rounded once.
+ * ndims in 1..8, every dims[i] >= 1, the product in 1..CC_MAX_RANKS, at
+ * most 4 levels of size > 1 (CC_ERR_UNSUPPORTED beyond).  cfg: algo must be
+ * CC_ALGO_RING and grid_sync 0 (CC_ERR_UNSUPPORTED otherwise).
+ *  fuse_depth = 0: one kernel folds every element's nested chains in
+ *                  registers and writes every rank's result;
+ *  fuse_depth >= 1: one kernel per ring step of the schedule, the groups of
+ *                  a level side by side; partials live in recv (int32,
+ *                  fp32) or in the workspace (bf16, fp32 per rank and
+ *                  element: cc_hierarchical_workspace_size).
+ * When the outermost level is the only one of size > 1, the call runs
+ * cc_all_reduce's ring kernels (the same values; fuse_depth as there).
+ * In place iff send.base == recv.base with equal strides; otherwise send and
+ * recv must not overlap.  Errors as for cc_all_reduce. */
+cc_status_t cc_all_reduce_hierarchical(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype,
+                                       cc_op_t op, int ndims, const int* dims, const cc_config_t* cfg,
+                                       cc_stream_t stream);
+
+/* Bytes of caller-owned device workspace cc_all_reduce_hierarchical needs
+ * for these arguments. */
+cc_status_t cc_hierarchical_workspace_size(int ndims, const int* dims, const cc_config_t* cfg, size_t count,
+                                           cc_dtype_t dtype, size_t* bytes);
+
+/* Simulated-network accounting of the hierarchical AllReduce, per level i
+ * (host arrays of ndims entries): level_bytes[i] = the largest number of
+ * bytes any rank sends inside its level-i group, level_steps[i] = the ring
+ * steps of that level (2 (dims[i] - 1): ReduceScatter and AllGather, or the
+ * AllReduce at the outermost level).  With N a multiple of every group's
+ * chunking, rank traffic at level i is 2 (p_i - 1) / p_i of the data the
+ * level works on: count / (dims[0] ... dims[i-1]) elements (the BlueConnect
+ * per-level cost). */
+cc_status_t cc_hierarchical_traffic(int ndims, const int* dims, size_t count, cc_dtype_t dtype,
+                                    uint64_t* level_bytes, int* level_steps);
+
+/* The stepwise hierarchical AllReduce as operation records, exactly as
+ * cc_all_reduce_plan describes them (the records the fuse_depth >= 1 kernels
+ * execute; also for a lone outermost level, whose ring kernels reach the
+ * same values).  CC_ERR_UNSUPPORTED when the product of dims is 1. */
+cc_status_t cc_hierarchical_plan(int ndims, const int* dims, size_t count, cc_plan_op_t* records, size_t cap,
+                                 size_t* nrecords);
+
 const char* cc_status_string(cc_status_t status);
 const char* cc_last_error(void);
 const char* cc_version(void);

@@ -14,7 +14,7 @@ size (bytes per rank and step) at which the two terms are equal.
 """
 from __future__ import annotations
 
-from typing import Dict, Sequence
+from typing import Dict, List, Sequence
 
 import numpy as np
 
@@ -87,3 +87,16 @@ def ring_tree_crossover(N: int, alpha: float, beta_s_per_byte: float) -> Dict[st
     den = (2 * lg - 2.0 * (N - 1) / N) * beta_s_per_byte
     exact = (2 * (N - 1) - 2 * lg) * alpha / den if den > 0 else float("inf")
     return {"exact": exact, "log": N * alpha / beta_s_per_byte / lg, "rough": N * alpha / beta_s_per_byte}
+
+
+def multidim_time(M_bytes: float, dims: Sequence[int], alphas: Sequence[float],
+                  betas: Sequence[float]) -> List[float]:
+    """Per-level time of the hierarchical AllReduce (AllReduce notes, 算法五,
+    BlueConnect cost): level i runs 2 (p_i - 1) steps of latency alpha_i and
+    sends 2 (p_i - 1) / p_i of the M / (p_0 ... p_(i-1)) bytes it works on at
+    beta_i seconds per byte.  The flat ring is the one-level case."""
+    out, shard = [], float(M_bytes)
+    for p, a, b in zip(dims, alphas, betas):
+        out.append(2 * (p - 1) * a + 2 * (p - 1) / p * shard * b)
+        shard /= p
+    return out

@@ -80,6 +80,14 @@ EXPORTS = {
     "cc_chunk_bounds": [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
     "cc_all_reduce_plan": [ctypes.c_int, ctypes.c_int, ctypes.c_size_t, ctypes.POINTER(PlanOp), ctypes.c_size_t,
                            ctypes.POINTER(ctypes.c_size_t)],
+    "cc_all_reduce_hierarchical": [RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_hierarchical_workspace_size": [ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(Config),
+                                       ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
+    "cc_hierarchical_traffic": [ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.c_size_t, ctypes.c_int,
+                                ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)],
+    "cc_hierarchical_plan": [ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.c_size_t, ctypes.POINTER(PlanOp),
+                             ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)],
     "cc_status_string": [ctypes.c_int],
     "cc_last_error": [],
     "cc_version": [],
@@ -193,6 +201,61 @@ def all_reduce_plan(algo: str, nranks: int, count: int):
     _check(L.cc_all_reduce_plan(ALGOS[algo], nranks, count, None, 0, ctypes.byref(n)))
     recs = (PlanOp * max(n.value, 1))()
     _check(L.cc_all_reduce_plan(ALGOS[algo], nranks, count, recs, n.value, ctypes.byref(n)))
+    return [{f: getattr(recs[i], f) for f, _ in PlanOp._fields_} for i in range(n.value)]
+
+
+def _dims(dims: Sequence[int]):
+    return len(dims), (ctypes.c_int * max(len(dims), 1))(*[int(p) for p in dims])
+
+
+def hierarchical_workspace_size(dims: Sequence[int], count: int, dtype: str, fuse_depth: int = 0) -> int:
+    nd, arr = _dims(dims)
+    out = ctypes.c_size_t(0)
+    cfg = Config(ALGOS["ring"], int(fuse_depth), None, 0, 0, 0)
+    _check(load().cc_hierarchical_workspace_size(nd, arr, ctypes.byref(cfg), count, DTYPES[dtype],
+                                                 ctypes.byref(out)))
+    return out.value
+
+
+def make_hierarchical_workspace(dims: Sequence[int], count: int, dtype: str, fuse_depth: int = 0, device="cuda"):
+    """Allocate (with torch) the workspace of a hierarchical AllReduce, or None."""
+    import torch
+    n = hierarchical_workspace_size(dims, count, dtype, fuse_depth)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def all_reduce_hierarchical(send, recv=None, dims: Sequence[int] = (), op: str = "sum", fuse_depth: int = 0,
+                            workspace=None, stream=None, blocks_per_cu: int = 0) -> None:
+    """Hierarchical AllReduce over the rank grid dims (level 0 innermost,
+    prod(dims) = N); send/recv are [N, M]."""
+    recv = send if recv is None else recv
+    N, M = send.shape
+    if tuple(recv.shape) != (N, M) or recv.dtype != send.dtype:
+        raise ValueError("recv must match send")
+    nd, arr = _dims(dims)
+    cfg = config("ring", fuse_depth, workspace, blocks_per_cu)
+    _check(load().cc_all_reduce_hierarchical(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], OPS[op],
+                                             nd, arr, ctypes.byref(cfg), _stream(stream)))
+
+
+def hierarchical_traffic(dims: Sequence[int], count: int, dtype: str):
+    """Per level: (largest bytes any rank sends inside its group, ring steps)."""
+    nd, arr = _dims(dims)
+    b = (ctypes.c_uint64 * max(nd, 1))()
+    st = (ctypes.c_int * max(nd, 1))()
+    _check(load().cc_hierarchical_traffic(nd, arr, count, DTYPES[dtype], b, st))
+    return [(b[i], st[i]) for i in range(nd)]
+
+
+def hierarchical_plan(dims: Sequence[int], count: int):
+    """The descriptor steps of the stepwise hierarchical AllReduce, as
+    all_reduce_plan returns them."""
+    L = load()
+    nd, arr = _dims(dims)
+    n = ctypes.c_size_t(0)
+    _check(L.cc_hierarchical_plan(nd, arr, count, None, 0, ctypes.byref(n)))
+    recs = (PlanOp * max(n.value, 1))()
+    _check(L.cc_hierarchical_plan(nd, arr, count, recs, n.value, ctypes.byref(n)))
     return [{f: getattr(recs[i], f) for f, _ in PlanOp._fields_} for i in range(n.value)]
 
 

@@ -217,6 +217,108 @@ cc_status_t copy_ranks(const cc_rankbuf_t& src, const cc_rankbuf_t& dst, uint64_
 cc_status_t run_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, uint64_t M, int dt, int op, int N,
                            const cc_config_t& cfg, hipStream_t st);
 
+// the launch arguments of a validated AllReduce over M elements, chunked (or
+// segmented) at bnd[0..N]
+Red red_of(cc_rankbuf_t send, cc_rankbuf_t recv, uint64_t M, const uint64_t* bnd, int dt, int op, int N,
+           const cc_config_t& cfg, hipStream_t st) {
+  Red r;
+  r.send = side(send);
+  r.recv = side(recv);
+  r.ws = ws_side(cfg, M, N);
+  r.M = M;
+  r.bnd = bnd;
+  r.blocks_per_cu = cfg.blocks_per_cu;
+  r.N = N;
+  r.dt = dt;
+  r.op = op;
+  r.rs_mode = 0;
+  r.vec_ok = al16p(send.base) && al16(send.rank_stride_bytes) && al16p(recv.base) && al16(recv.rank_stride_bytes) &&
+             (cfg.workspace == nullptr || al16p(cfg.workspace));
+  r.st = st;
+  return r;
+}
+
+// ---- hierarchical AllReduce
+struct Hier {
+  std::vector<int> dims;       // as given, level 0 first
+  std::vector<int> p, stride;  // the levels of size > 1: sizes and rank strides
+  std::vector<int> at;         // their index in dims
+  int N = 1;
+  int top = 0;                 // index in p of the AllReduce level; p.size() when none runs
+};
+
+constexpr int kMaxHierDims = 8;
+
+cc_status_t hier_args(int ndims, const int* dims, Hier* h) {
+  if (ndims < 1 || ndims > kMaxHierDims)
+    return fail(CC_ERR_INVALID_ARG, "ndims=%d outside [1, %d]", ndims, kMaxHierDims);
+  if (!dims) return fail(CC_ERR_INVALID_ARG, "dims is NULL");
+  h->dims.assign(dims, dims + ndims);
+  int64_t n = 1;
+  for (int i = 0; i < ndims; ++i) {
+    if (dims[i] < 1) return fail(CC_ERR_INVALID_ARG, "dims[%d]=%d is below 1", i, dims[i]);
+    n *= dims[i];
+    if (n > CC_MAX_RANKS) return fail(CC_ERR_INVALID_ARG, "the product of dims exceeds %d ranks", CC_MAX_RANKS);
+  }
+  h->N = (int)n;
+  hier_levels(h->dims, &h->p, &h->stride);
+  h->at.clear();
+  for (int i = 0; i < ndims; ++i)
+    if (dims[i] > 1) h->at.push_back(i);
+  if ((int)h->p.size() > kMaxHierLevels)
+    return fail(CC_ERR_UNSUPPORTED, "%d levels of size > 1; at most %d are supported", (int)h->p.size(),
+                kMaxHierLevels);
+  h->top = dims[ndims - 1] > 1 ? (int)h->p.size() - 1 : (int)h->p.size();
+  return CC_OK;
+}
+
+// a lone outermost level: the flat ring AllReduce
+bool hier_flat(const Hier& h) { return h.p.size() == 1 && h.top == 0; }
+
+cc_status_t hier_cfg_checks(const cc_config_t& cfg, int N, cc_dtype_t dtype) {
+  cc_status_t s = common_checks(CC_COLL_ALL_REDUCE, N, dtype, &cfg);
+  if (s) return s;
+  if (cfg.algo != CC_ALGO_RING)
+    return fail(CC_ERR_UNSUPPORTED, "the hierarchical AllReduce runs ring schedules at every level (algo ring)");
+  if (cfg.grid_sync) return fail(CC_ERR_UNSUPPORTED, "grid_sync is not available for the hierarchical AllReduce");
+  return CC_OK;
+}
+
+uint64_t hier_ws(const Hier& h, const cc_config_t& cfg, uint64_t M, int dt) {
+  if (h.N < 2) return 0;
+  if (hier_flat(h)) return ws_need(CC_COLL_ALL_REDUCE, cfg, h.N, M, dt);
+  if (cfg.fuse_depth == 0 || dt != DT_BF16) return 0;
+  return (uint64_t)h.N * rup(M * 4, 256);  // fp32 partials per rank
+}
+
+// The N segments of the vector: the level-0 chunks (floor bounds), each split
+// into its level-1 chunks, and so on; bnd[0..N] their bounds, seg[s] their
+// chunk index at every level of size > 1 (8 bits each).
+void hier_segments(const Hier& h, uint64_t M, uint64_t* bnd, uint32_t* seg) {
+  struct S {
+    uint64_t lo, hi;
+    uint32_t code;
+  };
+  std::vector<S> cur{S{0, M, 0u}};
+  for (size_t i = 0; i < h.p.size(); ++i) {
+    std::vector<S> nx;
+    const unsigned q = (unsigned)h.p[i];
+    for (const S& x : cur)
+      for (unsigned c = 0; c < q; ++c) {
+        const uint64_t span = x.hi - x.lo;
+        const uint64_t a = x.lo + (uint64_t)(((unsigned __int128)c * span) / q);
+        const uint64_t b = x.lo + (uint64_t)(((unsigned __int128)(c + 1) * span) / q);
+        nx.push_back(S{a, b, x.code | (c << (8 * i))});
+      }
+    cur.swap(nx);
+  }
+  for (size_t s = 0; s < cur.size(); ++s) {
+    bnd[s] = cur[s].lo;
+    seg[s] = cur[s].code;
+  }
+  bnd[cur.size()] = M;
+}
+
 }  // namespace
 
 extern "C" {
@@ -276,20 +378,7 @@ cc_status_t run_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, uint64_t M, int
   if (N == 1) return in_place ? ok() : copy_ranks(send, recv, nb, 1, es, cfg.blocks_per_cu, st);
 
   const Bounds bd(M, N);
-  Red r;
-  r.send = side(send);
-  r.recv = side(recv);
-  r.ws = ws_side(cfg, M, N);
-  r.M = M;
-  r.bnd = bd.b;
-  r.blocks_per_cu = cfg.blocks_per_cu;
-  r.N = N;
-  r.dt = dt;
-  r.op = op;
-  r.rs_mode = 0;
-  r.vec_ok = al16p(send.base) && al16(send.rank_stride_bytes) && al16p(recv.base) && al16(recv.rank_stride_bytes) &&
-             (cfg.workspace == nullptr || al16p(cfg.workspace));
-  r.st = st;
+  Red r = red_of(send, recv, M, bd.b, dt, op, N, cfg, st);
 
   hipError_t e = hipSuccess;
   if (cfg.algo == CC_ALGO_RING) {
@@ -664,6 +753,96 @@ cc_status_t cc_all_reduce_plan(cc_algo_t algo, int nranks, size_t count, cc_plan
   if (nranks < 2 || sched_of(algo, nranks) < 0)
     return fail(CC_ERR_UNSUPPORTED, "this schedule runs kernels of its own (no descriptor plan)");
   const Plan p = build_plan((SchedAlg)sched_of(algo, nranks), nranks, count);
+  size_t n = 0;
+  for (const auto& st : p.steps) n += st.size();
+  *nrecords = n;
+  if (!records) return ok();
+  if (cap < n) return fail(CC_ERR_INVALID_ARG, "cap=%zu is smaller than the %zu records", cap, n);
+  size_t i = 0;
+  for (size_t k = 0; k < p.steps.size(); ++k)
+    for (const GDesc& g : p.steps[k])
+      records[i++] = cc_plan_op_t{(uint32_t)k, g.flags, g.dst, g.in1, g.in2, g.lo, g.len};
+  return ok();
+}
+
+cc_status_t cc_all_reduce_hierarchical(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype,
+                                       cc_op_t op, int ndims, const int* dims, const cc_config_t* cfgp,
+                                       cc_stream_t stream) {
+  const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
+  Hier h;
+  cc_status_t s = hier_args(ndims, dims, &h);
+  if (s || (s = hier_cfg_checks(cfg, h.N, dtype))) return s;
+  if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
+  const int N = h.N, dt = (int)dtype, es = elem_size(dt);
+  if (count == 0) return ok();
+  const uint64_t M = count, nb = M * es;
+  if ((s = check_side(send, nb, N, "send")) || (s = check_side(recv, nb, N, "recv"))) return s;
+  if (!same_side(send, recv) && sides_overlap(send, nb, N, recv, nb, N))
+    return fail(CC_ERR_INVALID_ARG, "send and recv overlap without being the same buffers");
+  if ((s = grid_fits(M, dt))) return s;
+  const uint64_t need = hier_ws(h, cfg, M, dt);
+  if (need && (cfg.workspace == nullptr || cfg.workspace_bytes < need))
+    return fail(CC_ERR_INVALID_ARG, "this schedule needs %llu bytes of workspace (cc_hierarchical_workspace_size); got %zu",
+                (unsigned long long)need, cfg.workspace ? cfg.workspace_bytes : (size_t)0);
+  if ((s = device_ready())) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (N == 1 || hier_flat(h)) return run_all_reduce(send, recv, M, dt, (int)op, N, cfg, st);
+  uint64_t bnd[kMaxRanks + 1];
+  uint32_t seg[kMaxRanks];
+  hier_segments(h, M, bnd, seg);
+  Red r = red_of(send, recv, M, bnd, dt, (int)op, N, cfg, st);
+  if (cfg.fuse_depth == 0)
+    return hip_status(launch_hier_fused(r, h.p.data(), h.stride.data(), (int)h.p.size(), h.top, bnd, seg),
+                      "hierarchical all_reduce");
+  const Plan p = build_hier_plan(h.dims, M);
+  hipError_t e = hipSuccess;
+  for (const auto& stp : p.steps)
+    for (size_t i = 0; i < stp.size() && e == hipSuccess; i += kMaxGDesc)
+      e = launch_gsteps(r, stp.data() + i, (int)std::min<size_t>(kMaxGDesc, stp.size() - i));
+  return hip_status(e, "hierarchical all_reduce (stepwise)");
+}
+
+cc_status_t cc_hierarchical_workspace_size(int ndims, const int* dims, const cc_config_t* cfgp, size_t count,
+                                           cc_dtype_t dtype, size_t* bytes) {
+  const cc_config_t& cfg = cfgp ? *cfgp : kDefaultCfg;
+  Hier h;
+  cc_status_t s = hier_args(ndims, dims, &h);
+  if (s || (s = hier_cfg_checks(cfg, h.N, dtype))) return s;
+  if (!bytes) return fail(CC_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = (size_t)hier_ws(h, cfg, count, (int)dtype);
+  return ok();
+}
+
+cc_status_t cc_hierarchical_traffic(int ndims, const int* dims, size_t count, cc_dtype_t dtype, uint64_t* level_bytes,
+                                    int* level_steps) {
+  Hier h;
+  cc_status_t s = hier_args(ndims, dims, &h);
+  if (s) return s;
+  if ((int)dtype < 0 || (int)dtype > 2) return fail(CC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!level_bytes || !level_steps) return fail(CC_ERR_INVALID_ARG, "NULL output");
+  for (int i = 0; i < ndims; ++i) {
+    level_bytes[i] = 0;
+    level_steps[i] = 0;
+  }
+  if (h.N < 2) return ok();
+  const Plan p = build_hier_plan(h.dims, count);
+  const uint64_t es = elem_size((int)dtype);
+  for (size_t j = 0; j < h.p.size(); ++j) {
+    const auto& v = p.level_sent[j];
+    level_bytes[h.at[j]] = *std::max_element(v.begin(), v.end()) * es;
+    level_steps[h.at[j]] = 2 * (h.p[j] - 1);
+  }
+  return ok();
+}
+
+cc_status_t cc_hierarchical_plan(int ndims, const int* dims, size_t count, cc_plan_op_t* records, size_t cap,
+                                 size_t* nrecords) {
+  Hier h;
+  cc_status_t s = hier_args(ndims, dims, &h);
+  if (s) return s;
+  if (!nrecords) return fail(CC_ERR_INVALID_ARG, "nrecords is NULL");
+  if (h.N < 2) return fail(CC_ERR_UNSUPPORTED, "a single rank has no schedule");
+  const Plan p = build_hier_plan(h.dims, count);
   size_t n = 0;
   for (const auto& st : p.steps) n += st.size();
   *nrecords = n;

@@ -199,6 +199,13 @@ __device__ __forceinline__ uint32_t chunk_in(const uint64_t* bnd, int N, uint64_
   for (int i = 1; i < N; ++i) c += bnd[i] <= e ? 1u : 0u;
   return c;
 }
+// The same chunk when the bounds are exactly floor(c*M/N), as they are for
+// every schedule's chunks: floor(c*M/N) <= e holds for c <= ((e+1)*N - 1)/M,
+// so one division replaces the scan (per-element lookups in tiles that span
+// many small chunks).
+__device__ __forceinline__ uint32_t chunk_of(uint64_t M, int N, uint64_t e) {
+  return (uint32_t)(((e + 1) * (uint64_t)N - 1) / M);
+}
 __device__ __forceinline__ int wrapN(int r, int N) { return r >= N ? r - N : r; }
 __device__ __forceinline__ int modN(int r, int N) { return ((r % N) + N) % N; }
 
@@ -494,7 +501,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = chunk_in(a.bnd, tiling, e);
+      const uint32_t c = (tiling == 1 ? 0u : chunk_of(a.M, tiling, e));
       const int start = (ALG == ALG_RING && a.rs_mode) ? wrapN((int)c + 1, N) : (int)c;
       const A acc = fold_elem<DT, OP, NR, ALG>(a.sb, a.ss, N, start, e * SZ, ts);
       if (a.rs_mode) {
@@ -523,6 +530,179 @@ __global__ __launch_bounds__(kBlock) void k_tree_fused(FusedArgs a) {
 template <int DT, int OP, int N>
 __global__ __launch_bounds__(kBlock) void k_btree_fused(FusedArgs a) {
   fused_body<DT, OP, N, ALG_BTREE>(a);
+}
+
+// ------------------------------------------------------------------ hierarchical AllReduce
+
+// Rank r = sum of c_i * stride[i] over the (at most kMaxHierLevels)
+// non-trivial levels.  The vector splits into N segments -- the level-0
+// chunks, each split into its level-1 chunks, and so on -- each with one
+// chunk index per level (seg[s], 8 bits per level); bnd holds their bounds.
+// An element's value is the nested ring chains of the pages' decomposition:
+// the outermost level (top; nd when the outermost level of the hierarchy
+// has size 1 and no AllReduce runs) folds its members from chunk index c
+// (AllReduce order), every other level from c + 1 (standalone
+// ReduceScatter order), each chain op(next, partial), the members' values
+// being the inner levels' chains.
+struct HierArgs {
+  const char* sb;
+  uint64_t ss;
+  char* rb;
+  uint64_t rs;
+  uint64_t M;
+  int N;
+  int nd;
+  int top;
+  int vec_ok;
+  int p[kMaxHierLevels];
+  int stride[kMaxHierLevels];
+  uint32_t seg[kMaxRanks];
+  uint64_t bnd[kMaxRanks + 1];
+};
+
+// First coordinate of each level's chain for segment s: the top level
+// starts at its chunk index c (AllReduce order), every other level at c + 1.
+__device__ __forceinline__ int hier_first(const HierArgs& a, uint32_t seg, int i) {
+  const int c = (int)((seg >> (8 * i)) & 255u);
+  if (i == a.top) return c;
+  return c + 1 == a.p[i] ? 0 : c + 1;
+}
+
+// acc = x (first member of a chain) or op(x, acc)
+template <int DT, int OP, int VN>
+__device__ __forceinline__ void hier_join(bool first, const typename Ty<DT>::A (&x)[VN],
+                                          typename Ty<DT>::A (&acc)[VN]) {
+#pragma unroll
+  for (int k = 0; k < VN; ++k) acc[k] = first ? x[k] : opf<DT, OP>(x[k], acc[k]);
+}
+
+// The levels of one segment, uniform across the workgroup: sizes (1 beyond
+// nd), first coordinate of each chain, rank strides.
+struct HierLv {
+  int p[kMaxHierLevels], f[kMaxHierLevels], sd[kMaxHierLevels];
+};
+
+__device__ __forceinline__ HierLv hier_lv(const HierArgs& a, uint32_t seg) {
+  HierLv L;
+#pragma unroll
+  for (int i = 0; i < kMaxHierLevels; ++i) {
+    L.p[i] = i < a.nd ? a.p[i] : 1;
+    L.f[i] = i < a.nd ? hier_first(a, seg, i) : 0;
+    L.sd[i] = i < a.nd ? a.stride[i] : 0;
+  }
+  return L;
+}
+
+// A position in the walk over the N leaves in fold order (level 0 fastest):
+// j[i] counts the members of level i's chain already passed, c[i] is the
+// coordinate of the current one.  Every index is a compile-time constant, so
+// the state lives in scalar registers.
+struct HierPos {
+  int c[kMaxHierLevels], j[kMaxHierLevels];
+};
+
+__device__ __forceinline__ HierPos hier_begin(const HierLv& L) {
+  HierPos w;
+#pragma unroll
+  for (int i = 0; i < kMaxHierLevels; ++i) {
+    w.c[i] = L.f[i];
+    w.j[i] = 0;
+  }
+  return w;
+}
+
+__device__ __forceinline__ int hier_rank(const HierLv& L, const HierPos& w) {
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxHierLevels; ++i) r += w.c[i] * L.sd[i];
+  return r;
+}
+
+// next leaf; after the last one the walk starts over at the first
+__device__ __forceinline__ void hier_step(const HierLv& L, HierPos& w) {
+  bool carry = true;
+#pragma unroll
+  for (int i = 0; i < kMaxHierLevels; ++i) {
+    if (carry) {
+      if (w.j[i] + 1 < L.p[i]) {
+        ++w.j[i];
+        w.c[i] = w.c[i] + 1 == L.p[i] ? 0 : w.c[i] + 1;
+        carry = false;
+      } else {
+        w.j[i] = 0;
+        w.c[i] = L.f[i];
+      }
+    }
+  }
+}
+
+// Folds the leaf at walk position w into the chain accumulators: the level-0
+// chain takes it, and every level whose chain it completes passes its value
+// on to the level above.
+template <int DT, int OP, int VN>
+__device__ __forceinline__ void hier_take(const HierLv& L, const HierPos& w, const typename Ty<DT>::A (&x)[VN],
+                                          typename Ty<DT>::A (&a0)[VN], typename Ty<DT>::A (&a1)[VN],
+                                          typename Ty<DT>::A (&a2)[VN], typename Ty<DT>::A (&a3)[VN]) {
+  hier_join<DT, OP, VN>(w.j[0] == 0, x, a0);
+  if (w.j[0] + 1 == L.p[0]) {
+    hier_join<DT, OP, VN>(w.j[1] == 0, a0, a1);
+    if (w.j[1] + 1 == L.p[1]) {
+      hier_join<DT, OP, VN>(w.j[2] == 0, a1, a2);
+      if (w.j[2] + 1 == L.p[2]) hier_join<DT, OP, VN>(w.j[3] == 0, a2, a3);
+    }
+  }
+}
+
+constexpr int kHierBatch = 8;  // leaves loaded ahead of their folds
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  static_assert(kMaxHierLevels == 4, "four levels");
+  const int N = a.N;
+  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  if (t.fast) {
+    const uint32_t lane = threadIdx.x * 16u;
+    const char* s0 = a.sb + t.e0 * SZ;
+    const HierLv L = hier_lv(a, a.seg[t.c]);
+    HierPos ld = hier_begin(L), fw = ld;
+    A a0[V], a1[V], a2[V], a3[V];
+    for (int l0 = 0; l0 < N; l0 += kHierBatch) {
+      // every load of the batch is issued before the first fold; past the
+      // last leaf the walk has wrapped to valid ranks whose values go unused
+      u32x4 raw[kHierBatch];
+#pragma unroll
+      for (int q = 0; q < kHierBatch; ++q) {
+        raw[q] = ldg(s0 + (uint64_t)hier_rank(L, ld) * a.ss + lane);
+        hier_step(L, ld);
+      }
+#pragma unroll
+      for (int q = 0; q < kHierBatch; ++q)
+        if (l0 + q < N) {
+          A x[V];
+          unpack<DT>(raw[q], x);
+          hier_take<DT, OP, V>(L, fw, x, a0, a1, a2, a3);
+          hier_step(L, fw);
+        }
+    }
+    const u32x4 o = pack<DT>(a3);
+    char* d = a.rb + t.e0 * SZ;
+    for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, o);
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      const HierLv L = hier_lv(a, a.seg[chunk_in(a.bnd, N, e)]);
+      HierPos fw = hier_begin(L);
+      A a0[1], a1[1], a2[1], a3[1];
+      for (int l = 0; l < N; ++l) {
+        A x[1] = {ld1<DT>(a.sb + (uint64_t)hier_rank(L, fw) * a.ss + e * SZ)};
+        hier_take<DT, OP, 1>(L, fw, x, a0, a1, a2, a3);
+        hier_step(L, fw);
+      }
+      for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, a3[0]);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ double binary tree
@@ -741,7 +921,7 @@ __global__ __launch_bounds__(kBlock) void k_ring2_fused(FusedArgs a) {
     for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const int c = (int)chunk_in(a.bnd, N, e);
+      const int c = (int)chunk_of(a.M, N, e);
       A acc = chain_elem<DT, OP>(a.sb, a.ss, N, c - ca < 0 ? c - ca + N : c - ca, 1, ca + 1, e * SZ);
       if (cb > 0)
         acc = opf<DT, OP>(acc, chain_elem<DT, OP>(a.sb, a.ss, N, c + cb >= N ? c + cb - N : c + cb, -1, cb, e * SZ));
@@ -889,7 +1069,7 @@ __device__ __forceinline__ void ring_pass_tile(const PassArgs& a, uint64_t tile,
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = chunk_in(a.bnd, N, e);
+      const uint32_t c = chunk_of(a.M, N, e);
       const int start = a.rs_mode ? wrapN((int)c + 1, N) : (int)c;
       A acc;
       if (s0 == 0)
@@ -1000,7 +1180,7 @@ __global__ __launch_bounds__(kBlock) void k_hd_rs_step(StepArgs a) {
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = chunk_in(a.bnd, N, e);
+      const uint32_t c = chunk_of(a.M, N, e);
       const int base = (int)c & ~(d - 1);
       for (int m = 0; m < d; ++m) {
         const int i = base | m, p = i ^ d;
@@ -1105,7 +1285,7 @@ __device__ __forceinline__ void ring_ag_tile(const GatArgs& a, uint64_t tile, in
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const int c = (int)chunk_in(a.bnd, N, e);
+      const int c = (int)chunk_of(a.M, N, e);
       const bool from_send = a.mode == 1 && s0 == 0;
       const int holder = a.mode == 0 ? modN(c - 1 + s0, N) : wrapN(c + s0, N);
       const char* src = from_send ? a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ
@@ -1380,7 +1560,7 @@ __global__ __launch_bounds__(kBlock) void k_hd_ag_step(GatArgs a) {
     }
   } else {
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const int c = (int)chunk_in(a.bnd, N, e);
+      const int c = (int)chunk_of(a.M, N, e);
       const int base = (c ^ d) & ~(d - 1);
       if (a.mode == 1 && first) {
         const char* src = a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ;
@@ -1555,13 +1735,26 @@ constexpr uint64_t kVecBytes = (uint64_t)kBlock * kUnroll * 16;   // one vector 
 unsigned occupancy_lds(int requested, uint64_t traffic, uint64_t target, int min_blocks = 1) {
   return lds_for_blocks_per_cu(requested > 0 ? requested : default_blocks_per_cu(traffic, target, min_blocks));
 }
+
+// Fused AllReduce kernels with a runtime rank count keep one batch of leaf
+// loads in flight per thread (8, plus the first leaf for the ring) whatever N
+// is, so the byte rule above undersizes them at small N.  Measured on the
+// MI355X (fused fp32 SUM, 2 GiB per buffer, 2 to 6 workgroups per CU): the
+// ring streams best with 4 up to N = 8, 3 up to 16 and 2 beyond; the
+// hierarchical kernel, whose per-leaf walk is longer, with 4 up to N = 8 and
+// 3 beyond.
+int batched_ring_blocks_per_cu(int N) { return N <= 8 ? 4 : N <= 16 ? 3 : 2; }
+int hier_blocks_per_cu(int N) { return N <= 8 ? 4 : 3; }
 }  // namespace
 
 hipError_t launch_ring_fused(const Red& r) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
-                                 : occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
+  const bool runtime_n = r.N != 2 && r.N != 3 && r.N != 4 && r.N != 8 && r.N != 16;
+  const unsigned lds =
+      r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
+      : runtime_n ? lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu : batched_ring_blocks_per_cu(r.N))
+                  : occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     switch (r.N) {
@@ -1682,6 +1875,28 @@ hipError_t launch_ring2_fused(const Red& r) {
         if (r.N <= 16) hipLaunchKernelGGL((k_ring2_fused<DT, OP, 16, false>), grid, blk, lds, r.st, a);
         else hipLaunchKernelGGL((k_ring2_fused<DT, OP, 0, false>), grid, blk, lds, r.st, a);
     }
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int nd, int top, const uint64_t* segbnd,
+                             const uint32_t* seg) {
+  if (nd < 1 || nd > kMaxHierLevels || top < 0 || top > nd || r.N < 2 || r.N > kMaxRanks) return hipErrorInvalidValue;
+  HierArgs a;
+  a.sb = r.send.base; a.ss = r.send.stride;
+  a.rb = r.recv.base; a.rs = r.recv.stride;
+  a.M = r.M; a.N = r.N; a.nd = nd; a.top = top; a.vec_ok = r.vec_ok;
+  for (int i = 0; i < kMaxHierLevels; ++i) {
+    a.p[i] = i < nd ? p[i] : 1;
+    a.stride[i] = i < nd ? stride[i] : 0;
+  }
+  for (int s = 0; s < r.N; ++s) a.seg[s] = seg[s];
+  for (int s = 0; s <= r.N; ++s) a.bnd[s] = segbnd[s];
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu : hier_blocks_per_cu(r.N));
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    hipLaunchKernelGGL((k_hier_fused<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }

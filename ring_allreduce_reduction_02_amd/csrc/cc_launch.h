@@ -84,6 +84,14 @@ hipError_t launch_tree_shaped(const Red& r, int tree, int nr, int leaves, int pa
 hipError_t launch_dbt_fused(const Red& r);
 hipError_t launch_ring2_fused(const Red& r);
 
+// ---- hierarchical AllReduce, fused: nd (<= kMaxHierLevels) non-trivial
+// levels of sizes p[] and rank strides stride[], level `top` running the
+// AllReduce (nd: none); segbnd[0..N] bounds the N segments of the vector,
+// seg[s] their chunk index per level (8 bits each)
+constexpr int kMaxHierLevels = 4;
+hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int nd, int top, const uint64_t* segbnd,
+                             const uint32_t* seg);
+
 // ---- descriptor steps (GDesc flags)
 enum : unsigned {
   GD_LOCAL_SEND = 1u,   // local operand from send[dst] (else partial[dst])

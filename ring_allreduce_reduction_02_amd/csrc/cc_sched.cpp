@@ -269,6 +269,126 @@ Plan pairs(int N, uint64_t M, bool hd) {
 
 }  // namespace
 
+void hier_levels(const std::vector<int>& dims, std::vector<int>* p, std::vector<int>* stride) {
+  p->clear();
+  stride->clear();
+  int st = 1;
+  for (int q : dims) {
+    if (q > 1) {
+      p->push_back(q);
+      stride->push_back(st);
+    }
+    st *= q;
+  }
+}
+
+// Multi-dimensional AllReduce (AllReduce notes, 算法五; textbook ch. 6,
+// "分层全归约"), one ring step per kernel step, all groups of a level side by
+// side.  At an inner level the member at coordinate k receives, at ring step
+// s, chunk (k-s-2) mod p of the group's range from member k-1 and folds
+// op(own, incoming) -- the standalone ReduceScatter, after which member c
+// holds chunk c; "own" is the rank's send buffer at the first level it takes
+// part in and its partial after that.  The outermost level runs the ring
+// AllReduce (chunk (k-s-1) at step s, member k then holding chunk k+1, the
+// last fold written rounded to recv), its AllGather, and the inner levels'
+// AllGathers copy finished ranges back out.
+Plan build_hier_plan(const std::vector<int>& dims, uint64_t M) {
+  std::vector<int> p, stride;
+  hier_levels(dims, &p, &stride);
+  int N = 1;
+  for (int q : dims) N *= q;
+  Builder b(N, M);
+  const int d = (int)p.size();
+  b.p.level_sent.assign(d, std::vector<uint64_t>(N, 0));
+  std::vector<uint64_t> lo(N, 0), hi(N, M);
+  auto groups = [&](int i) {
+    std::vector<std::vector<int>> g;
+    for (int r = 0; r < N; ++r)
+      if ((r / stride[i]) % p[i] == 0) {
+        std::vector<int> m(p[i]);
+        for (int k = 0; k < p[i]; ++k) m[k] = r + k * stride[i];
+        g.push_back(m);
+      }
+    return g;
+  };
+  auto piece = [&](int r, int parts, int c, uint64_t* a, uint64_t* len) {
+    const uint64_t span = hi[r] - lo[r];
+    *a = lo[r] + bound(span, parts, c);
+    *len = bound(span, parts, c + 1) - bound(span, parts, c);
+  };
+  auto send_at = [&](int level, int r, uint64_t n) {
+    b.send(r, n);
+    b.p.level_sent[level][r] += n;
+  };
+  // ReduceScatter (off = -1 inner, 0 outermost) of one level
+  auto reduce_scatter = [&](int i, int off, bool last_final) {
+    const auto gs = groups(i);
+    const int q = p[i];
+    for (int s = 0; s < q - 1; ++s) {
+      for (const auto& g : gs)
+        for (int k = 0; k < q; ++k) {
+          const int m = g[k], snd = g[(k - 1 + q) % q];
+          const int ci = md(k - s - 1 + off, q);
+          uint64_t a, len;
+          piece(m, q, ci, &a, &len);
+          b.add(combine(a, len, m, i == 0, snd, i == 0 && s == 0, -1, false, last_final && s == q - 2));
+          send_at(i, snd, len);
+        }
+      b.flush();
+    }
+  };
+  auto all_gather = [&](int i, bool ar_owners) {
+    const auto gs = groups(i);
+    const int q = p[i];
+    for (int s = 0; s < q - 1; ++s) {
+      for (const auto& g : gs)
+        for (int k = 0; k < q; ++k) {
+          const int c = md((ar_owners ? k + 1 : k) - s, q);
+          uint64_t a, len;
+          piece(g[k], q, c, &a, &len);
+          b.add(copy(a, len, g[(k + 1) % q], g[k]));
+          send_at(i, g[k], len);
+        }
+      b.flush();
+    }
+  };
+  // the outermost level of the hierarchy runs the AllReduce; when it has
+  // size 1 every non-trivial level is an inner one, and the last
+  // ReduceScatter writes the finished values
+  const bool top = dims.back() > 1;
+  const int inner = top ? d - 1 : d;
+  for (int i = 0; i < inner; ++i) {
+    reduce_scatter(i, -1, !top && i == inner - 1);
+    for (const auto& g : groups(i))
+      for (int k = 0; k < p[i]; ++k) {
+        uint64_t a, len;
+        piece(g[k], p[i], k, &a, &len);
+        lo[g[k]] = a;
+        hi[g[k]] = a + len;
+      }
+  }
+  if (top) {
+    reduce_scatter(d - 1, 0, true);
+    all_gather(d - 1, true);
+  }
+  for (int i = inner - 1; i >= 0; --i) {
+    for (const auto& g : groups(i)) {
+      uint64_t l = lo[g[0]], h = hi[g[0]];
+      for (int m : g) {
+        l = std::min(l, lo[m]);
+        h = std::max(h, hi[m]);
+      }
+      for (int m : g) {
+        lo[m] = l;
+        hi[m] = h;
+      }
+    }
+    all_gather(i, false);
+  }
+  b.p.net_steps = (int)b.p.steps.size();
+  return b.p;
+}
+
 // T1: the in-order binary tree over ranks 1..N-1 (x with lowest set bit b
 // has the left child x - b/2 and the right child x + c, c the largest of
 // b/2, b/4, ... with x + c < N), rooted at the largest power of two below N,

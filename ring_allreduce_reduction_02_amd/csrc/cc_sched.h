@@ -20,7 +20,20 @@ struct Plan {
   // the simulated network: values each rank sends, and the number of steps
   std::vector<uint64_t> sent;
   int net_steps = 0;
+  // hierarchical schedules: values each rank sends at each level
+  std::vector<std::vector<uint64_t>> level_sent;
 };
+
+// Hierarchical AllReduce over dims (level 0 innermost, rank r = r_0 +
+// p_0 (r_1 + p_1 (...))): standalone ring ReduceScatters inside the groups of
+// levels 0 .. d-2, a ring AllReduce inside the outermost groups, ring
+// AllGathers back.  Levels of size 1 do nothing (with an outermost level of
+// size 1 no AllReduce runs); prod(dims) >= 2.  level_sent is indexed by the
+// levels of size > 1.
+Plan build_hier_plan(const std::vector<int>& dims, uint64_t M);
+
+// The non-trivial levels of dims: their sizes and rank strides.
+void hier_levels(const std::vector<int>& dims, std::vector<int>* p, std::vector<int>* stride);
 
 // N >= 2; M elements per rank.
 Plan build_plan(SchedAlg alg, int N, uint64_t M);

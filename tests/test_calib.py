@@ -58,3 +58,14 @@ def test_bench_refuses_more_than_one_gpu():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_multidim_time_matches_the_oracle_model():
+    """The bench's per-level model equals the oracle's BlueConnect model and
+    gives Napkin Math 1.6's 8 x 8 GPU budget (about 8.3 ms for 1 GB at 450 and
+    50 GB/s)."""
+    from oracle import ccsim as cs
+    for dims in ((8, 8), (3, 2, 2), (4, 1, 2), (64,)):
+        a, b = [1e-6 * (i + 1) for i in range(len(dims))], [1e-11 * (i + 2) for i in range(len(dims))]
+        assert calib.multidim_time(1e8, dims, a, b) == pytest.approx(cs.multidim_time_model(1e8, dims, a, b))
+    assert sum(calib.multidim_time(1e9, (8, 8), (0, 0), (1 / 450e9, 1 / 50e9))) == pytest.approx(8.26e-3, abs=1e-5)
