@@ -385,6 +385,96 @@ def hierarchical(dev):
     return out
 
 
+def alltoall_variants(dev):
+    """AllToAll variants on the MoE workload (8 ranks, 4096 tokens each, top-8
+    of 64 experts with Zipf loads, rows of 7168 bf16): the capacity-padded
+    dispatch and combine at C = 1 and 1.25 against the dropless AllToAll(v),
+    the hierarchical exchange at 2 and 4 ranks per node, and the pairwise
+    schedule's model (blog, Pairwise performance model) fitted on uniform
+    exchanges and checked on the routed counts.  GB/s counts the bytes the
+    kernels read and write."""
+    import numpy as np
+    import torch
+
+    from ring_allreduce_reduction_02_amd import calib, ccgpu, synth
+    N, H, T, K, E = 8, 7168, 4096, 8, 64
+    rowb = H * 2
+    ch = synth.moe_routing(N, T, E, K)
+    Ce = np.stack([np.bincount(c.reshape(-1), minlength=E) for c in ch]).astype(np.int64)  # rows per (source, expert)
+    C = Ce.reshape(N, N, E // N).sum(axis=2)                                                 # rows per (source, rank)
+    gen = torch.Generator(device=dev).manual_seed(20261204)
+    Ls, Lr = int(Ce.sum(1).max()), int(C.sum(0).max())
+    send = torch.randn(N, Ls * H, generator=gen, device=dev).to(torch.bfloat16)
+    out = {"tokens_per_rank": T, "topk": K, "experts": E, "hidden": H,
+           "rows_per_expert_max_over_mean": round(float(Ce.sum(0).max() / Ce.sum(0).mean()), 2)}
+    recv = torch.empty(N, Lr * H, device=dev, dtype=torch.bfloat16)
+    ms = _avg_ms(lambda: ccgpu.all_to_all(send, recv, C.tolist(), H))
+    moved = 2 * int(C.sum()) * rowb
+    out["dropless_direct"] = {"ms": round(ms, 4), "GBps": round(moved / ms / 1e6, 1), "wire_rows": int(C.sum())}
+    del recv
+    torch.cuda.empty_cache()
+    for num, den in ((1, 1), (5, 4)):
+        cap = ccgpu.moe_capacity(1, T, K, E, num, den)
+        exp = torch.empty(N, E * cap * H, device=dev, dtype=torch.bfloat16)
+        kept = int(np.minimum(Ce, cap).sum())
+        wire = N * E * cap
+        d_moved = kept * rowb + wire * rowb                 # kept rows read, every slot written
+        c_moved = kept * rowb + int(Ce.sum()) * rowb        # kept rows read, every token row written
+        r = {"capacity": cap, "dropped_rows": int(Ce.sum()) - kept,
+             "dropped_frac": round(1 - kept / int(Ce.sum()), 4),
+             "wire_rows": wire, "wire_over_dropless": round(wire / int(C.sum()), 3)}
+        for fd, name in ((0, "direct"), (1, "pairwise")):
+            ms = _avg_ms(lambda f=fd: ccgpu.moe_dispatch_padded(send, exp, Ce.tolist(), cap, H, fuse_depth=f))
+            r[f"dispatch_{name}"] = {"ms": round(ms, 4), "GBps": round(d_moved / ms / 1e6, 1)}
+        ms = _avg_ms(lambda: ccgpu.moe_combine_padded(exp, send, Ce.tolist(), cap, H))
+        r["combine_direct"] = {"ms": round(ms, 4), "GBps": round(c_moved / ms / 1e6, 1)}
+        out[f"padded_C{num / den:g}"] = r
+        del exp
+        torch.cuda.empty_cache()
+    recv = torch.empty(N, Lr * H, device=dev, dtype=torch.bfloat16)
+    for L in (2, 4):
+        ws = ccgpu.make_all_to_all_hierarchical_workspace(C.tolist(), H, "bf16", L, dev)
+        ms = _avg_ms(lambda: ccgpu.all_to_all_hierarchical(send, recv, C.tolist(), L, H, workspace=ws))
+        tr = ccgpu.all_to_all_traffic(C.tolist(), H, "bf16", L)
+        phases = ("flat", "aggregate", "exchange", "distribute")
+        # every block is copied once in phase 1; inter-node bytes twice more
+        moved_h = 2 * (int(C.sum()) * rowb + 2 * tr[2][1])
+        out[f"hierarchical_L{L}"] = {
+            "ms": round(ms, 4), "GBps_moved": round(moved_h / ms / 1e6, 1),
+            "transfers": {ph: f for ph, (f, _, _) in zip(phases, tr)},
+            "bytes": {ph: t for ph, (_, t, _) in zip(phases, tr)}}
+        del ws
+        torch.cuda.empty_cache()
+    # pairwise model: fit T = alpha * (launched steps) + beta * sum_k max_i n_(i,i+k) on uniform exchanges
+    pts, st, by, ts = [], [], [], []
+    for rows in (1, 4, 16, 64, 256, 1024):
+        U = [[rows] * N for _ in range(N)]
+        su = send[:, :N * rows * H]
+        ru = recv[:, :N * rows * H]
+        t, how = _time_gpu(lambda: ccgpu.all_to_all(su, ru, U, H, fuse_depth=1), 10, 4 if rows <= 64 else 1)
+        mx, _ = ccgpu.all_to_all_step_bytes(U, H, "bf16")
+        st.append(N); by.append(sum(mx)); ts.append(t / 1e3)
+        pts.append({"rows_per_block": rows, "us": round(t * 1e3, 2), "timing": how})
+    fit = calib.fit_alpha_beta(st, by, ts)
+    mx, tot = ccgpu.all_to_all_step_bytes(C.tolist(), H, "bf16")
+    t_moe, how = _time_gpu(lambda: ccgpu.all_to_all(send, recv, C.tolist(), H, fuse_depth=1), 10, 1)
+    a, b = fit["alpha_us_per_step"] * 1e-6, fit["beta_ps_per_byte"] * 1e-12
+    out["pairwise_model"] = {
+        "uniform_fit": fit, "uniform_points": pts,
+        "moe_step_max_bytes": mx, "moe_step_total_bytes": tot,
+        "moe_measured_us": round(t_moe * 1e3, 2),
+        "moe_predicted_us": round((N * a + b * sum(mx)) * 1e6, 2),
+        "moe_predicted_pages_form_us": round(calib.pairwise_time(mx, a, b) * 1e6, 2),
+        # uniform exchanges have step total = N x step max, so the same fit prices
+        # total bytes at beta / N: the one-HBM reading of a step
+        "moe_predicted_from_step_totals_us": round((N * a + b / N * sum(tot)) * 1e6, 2),
+        "note": "one GPU: a step moves all N blocks through the one HBM, so its time follows the step's total "
+                "bytes, not its largest block; the predicted figure uses the largest block as the blog's model does"}
+    del send, recv
+    torch.cuda.empty_cache()
+    return out
+
+
 def norm_rel_err_fp64(send, recv, offsets, counts, step=1 << 24):
     """max over ranks of ||y_r - y64|| / ||y64|| over the given element
     ranges, y64 = the order-free fp64 sum of the inputs (a measurement of the
@@ -628,6 +718,8 @@ def main():
         out["schedules"] = schedules(dev)
         log("hierarchical")
         out["hierarchical"] = hierarchical(dev)
+        log("alltoall variants")
+        out["alltoall_variants"] = alltoall_variants(dev)
     if not args.no_cpu_baseline:
         log("oracle on the host")
         out["cpu_baseline"] = cpu_baseline(N, min(args.cpu_sample, M))

@@ -340,6 +340,105 @@ cc_status_t cc_hierarchical_traffic(int ndims, const int* dims, size_t count, cc
 cc_status_t cc_hierarchical_plan(int ndims, const int* dims, size_t count, cc_plan_op_t* records, size_t cap,
                                  size_t* nrecords);
 
+/* ---- AllToAll variants around MoE routing (textbook ch. 6, "MoE AllToAll 中的
+ * 动态路由与专家负载失衡"; blog, "Pairwise（成对）算法").  Every variant is a
+ * pure copy: results are bit-identical whatever the schedule.  cfg: algo must
+ * be CC_ALGO_RING (CC_ERR_UNSUPPORTED otherwise); fuse_depth 0 runs every
+ * transfer at once (direct), fuse_depth >= 1 the pairwise schedule (at step k
+ * rank r sends to r + k) where stated. */
+
+/* Expert capacity ceil(nranks * tokens * topk / nexperts * C) with the
+ * capacity factor C = factor_num / factor_den, in exact integer arithmetic
+ * (textbook ch. 6, "容量因子与有界分配").  With nranks = 1 it is the rows one
+ * source may send to one expert, the block size of cc_moe_dispatch_padded. */
+cc_status_t cc_moe_capacity(int nranks, size_t tokens, int topk, int nexperts, int factor_num, int factor_den,
+                            size_t* capacity);
+
+/* Capacity-padded MoE dispatch (textbook ch. 6, "容量因子与有界分配": fixed
+ * expert buffers, rows beyond the capacity dropped, free slots padded so the
+ * exchange is uniform).  counts: host array [nranks * nexperts], counts[i*E+e]
+ * = rows source rank i routes to expert e; nexperts is a multiple of nranks and
+ * expert e lives on rank e / (E/nranks) as local expert e % (E/nranks).
+ * send (token side): rank i's rows sorted by expert, back to back.
+ * recv (expert side): rank j holds, for source i = 0..N-1 and then local
+ * expert l, a block of `capacity` rows: the first min(count, capacity) rows of
+ * i's block for expert j*E/N + l, in order, then zero rows (E*capacity rows
+ * per rank).  A row is elem_per_row elements.  send and recv must not overlap.
+ * fuse_depth >= 1: pairwise, step k carries the blocks of the pairs (i, i+k). */
+cc_status_t cc_moe_dispatch_padded(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* counts, int nexperts,
+                                   size_t capacity, size_t elem_per_row, cc_dtype_t dtype, int nranks,
+                                   const cc_config_t* cfg, cc_stream_t stream);
+
+/* The combine exchange, the transpose of cc_moe_dispatch_padded: send is the
+ * expert side (its layout), recv the token side (its layout); rank i gets back
+ * the rows its dispatched rows occupied, and zero rows where a row was dropped.
+ * fuse_depth >= 1: pairwise, step k carries expert rank j's blocks for rank
+ * j + k. */
+cc_status_t cc_moe_combine_padded(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* counts, int nexperts,
+                                  size_t capacity, size_t elem_per_row, cc_dtype_t dtype, int nranks,
+                                  const cc_config_t* cfg, cc_stream_t stream);
+
+/* Hierarchical AllToAll(v) (textbook ch. 6, "分层 MoE 交换": aggregate inside
+ * the node, exchange between nodes, distribute inside the node).  The nranks
+ * ranks form nranks/local_size nodes of local_size ranks (rank r on node
+ * r / local_size).  Same arguments and result as cc_all_to_all.  Phases:
+ * (1) blocks between ranks of one node go to their destination, and rank
+ * (n, l) moves its blocks for node n2 != n into the payload of the aggregator
+ * (n, n2 mod local_size), ordered by source then destination local index;
+ * (2) one transfer per ordered node pair, aggregator -> receiver
+ * (n2, n mod local_size); (3) the receiver copies each block to its
+ * destination.  Inter-node transfers fall from one per rank pair to one per
+ * node pair.  The payloads are staged in the caller's workspace
+ * (cc_all_to_all_hierarchical_workspace_size; 2 areas of the inter-node
+ * bytes, each rounded up to 256); it must not overlap send or recv.
+ * fuse_depth has no effect. */
+cc_status_t cc_all_to_all_hierarchical(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* counts,
+                                       size_t elem_per_row, cc_dtype_t dtype, int nranks, int local_size,
+                                       const cc_config_t* cfg, cc_stream_t stream);
+cc_status_t cc_all_to_all_hierarchical_workspace_size(const size_t* counts, size_t elem_per_row, cc_dtype_t dtype,
+                                                      int nranks, int local_size, size_t* bytes);
+
+/* Accounting of an AllToAll(v) exchange (counts as cc_all_to_all), entry 0
+ * the flat exchange, entries 1..3 the hierarchical phases (aggregate,
+ * exchange, distribute) for the given local_size: transfers between
+ * different ranks (a source's aggregated payload for one node counts once,
+ * every other non-empty block once), their total bytes, and the most bytes
+ * one rank sends.  Host arrays of 4 entries. */
+cc_status_t cc_all_to_all_traffic(const size_t* counts, size_t elem_per_row, cc_dtype_t dtype, int nranks,
+                                  int local_size, int* flows, uint64_t* total_bytes, uint64_t* max_rank_bytes);
+
+/* The pairwise schedule's per-step bytes (blog, "Pairwise（成对）算法",
+ * performance model T = (N-1) a + b * sum_k max_i n_(i,(i+k) mod N)): for
+ * k = 0..N-1, step_max[k] = max over i of the bytes of block (i, i+k), and
+ * step_total[k] their sum (step 0 is the local block).  Host arrays of
+ * nranks entries. */
+cc_status_t cc_all_to_all_step_bytes(const size_t* counts, size_t elem_per_row, cc_dtype_t dtype, int nranks,
+                                     uint64_t* step_max, uint64_t* step_total);
+
+/* The copies the AllToAll variants above perform, as plain records (tests
+ * replay them on the host): for the given arguments -- validated exactly as
+ * the call would -- every copy in launch order, step (or phase) by step.
+ * src and dst are the byte addresses the kernels would touch (derived from
+ * the rank buffers and workspace given; they are never dereferenced here);
+ * src = 0 means "fill dst with zero bytes".  kind selects the call:
+ * CC_A2A_MOE_DISPATCH / CC_A2A_MOE_COMBINE take counts [nranks*nexperts],
+ * nexperts and capacity (local_size is ignored); CC_A2A_HIERARCHICAL takes
+ * counts [nranks*nranks] and local_size (nexperts, capacity ignored).
+ * With records == NULL only *nrecords is set; otherwise cap must hold all of
+ * them (CC_ERR_INVALID_ARG if not). */
+typedef enum { CC_A2A_MOE_DISPATCH = 1, CC_A2A_MOE_COMBINE = 2, CC_A2A_HIERARCHICAL = 3 } cc_a2a_kind_t;
+typedef struct {
+  uint32_t step;
+  uint32_t reserved;
+  uint64_t src;
+  uint64_t dst;
+  uint64_t bytes;
+} cc_copy_op_t;
+cc_status_t cc_all_to_all_plan(cc_a2a_kind_t kind, cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* counts,
+                               int nexperts, size_t capacity, size_t elem_per_row, cc_dtype_t dtype, int nranks,
+                               int local_size, const cc_config_t* cfg, cc_copy_op_t* records, size_t cap,
+                               size_t* nrecords);
+
 const char* cc_status_string(cc_status_t status);
 const char* cc_last_error(void);
 const char* cc_version(void);

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcc.so")
 
-SOURCES = [os.path.join(CSRC, "cc_kernels.hip"), os.path.join(CSRC, "cc_api.cpp"), os.path.join(CSRC, "cc_sched.cpp")]
+SOURCES = [os.path.join(CSRC, "cc_kernels.hip"), os.path.join(CSRC, "cc_api.cpp"), os.path.join(CSRC, "cc_sched.cpp"),
+           os.path.join(CSRC, "cc_alltoall.cpp")]
 
 FLAGS = [
     "--offload-arch=gfx950",

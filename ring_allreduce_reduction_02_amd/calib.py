@@ -100,3 +100,11 @@ def multidim_time(M_bytes: float, dims: Sequence[int], alphas: Sequence[float],
         out.append(2 * (p - 1) * a + 2 * (p - 1) / p * shard * b)
         shard /= p
     return out
+
+
+def pairwise_time(step_max_bytes: Sequence[float], alpha: float, beta: float) -> float:
+    """Pairwise AllToAll time (blog, Pairwise performance model): steps
+    k = 1..N-1 each cost alpha + beta * (largest block of the step);
+    step_max_bytes[k] is that block for k = 0..N-1 (step 0, the local block,
+    is not a transfer)."""
+    return sum(alpha + beta * float(b) for b in list(step_max_bytes)[1:])

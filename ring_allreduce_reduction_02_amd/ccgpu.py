@@ -88,6 +88,24 @@ EXPORTS = {
                                 ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int)],
     "cc_hierarchical_plan": [ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.c_size_t, ctypes.POINTER(PlanOp),
                              ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)],
+    "cc_moe_capacity": [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                        ctypes.POINTER(ctypes.c_size_t)],
+    "cc_moe_dispatch_padded": [RankBuf, RankBuf, ctypes.POINTER(ctypes.c_size_t), ctypes.c_int, ctypes.c_size_t,
+                               ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_moe_combine_padded": [RankBuf, RankBuf, ctypes.POINTER(ctypes.c_size_t), ctypes.c_int, ctypes.c_size_t,
+                              ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_all_to_all_hierarchical": [RankBuf, RankBuf, ctypes.POINTER(ctypes.c_size_t), ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_all_to_all_hierarchical_workspace_size": [ctypes.POINTER(ctypes.c_size_t), ctypes.c_size_t, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
+    "cc_all_to_all_traffic": [ctypes.POINTER(ctypes.c_size_t), ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_uint64),
+                              ctypes.POINTER(ctypes.c_uint64)],
+    "cc_all_to_all_step_bytes": [ctypes.POINTER(ctypes.c_size_t), ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                 ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)],
+    "cc_all_to_all_plan": [ctypes.c_int, RankBuf, RankBuf, ctypes.POINTER(ctypes.c_size_t), ctypes.c_int,
+                           ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                           ctypes.POINTER(Config), ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)],
     "cc_status_string": [ctypes.c_int],
     "cc_last_error": [],
     "cc_version": [],
@@ -338,6 +356,115 @@ def all_to_all(send, recv, counts: Sequence[Sequence[int]], elem_per_row: int = 
     cfg = config("ring", fuse_depth, None, blocks_per_cu)
     _check(load().cc_all_to_all(rankbuf(send), rankbuf(recv), arr, elem_per_row, DTYPES[dtype_name(send)], N,
                                 ctypes.byref(cfg), _stream(stream)))
+
+
+def _sizes(rows: Sequence[Sequence[int]], n: int, m: int, what: str):
+    flat = [int(v) for row in rows for v in row]
+    if len(flat) != n * m:
+        raise ValueError(f"{what} must be {n} x {m}")
+    return (ctypes.c_size_t * max(len(flat), 1))(*flat)
+
+
+def moe_capacity(nranks: int, tokens: int, topk: int, nexperts: int, factor_num: int, factor_den: int) -> int:
+    """ceil(nranks * tokens * topk / nexperts * factor_num / factor_den)."""
+    out = ctypes.c_size_t(0)
+    _check(load().cc_moe_capacity(nranks, tokens, topk, nexperts, factor_num, factor_den, ctypes.byref(out)))
+    return out.value
+
+
+def moe_dispatch_padded(send, recv, counts: Sequence[Sequence[int]], capacity: int, elem_per_row: int = 1,
+                        fuse_depth: int = 0, stream=None, blocks_per_cu: int = 0) -> None:
+    """Token side send [N, rows] -> expert side recv [N, E*capacity*elem_per_row];
+    counts is N x E (rows per source and expert)."""
+    N, E = send.shape[0], len(counts[0]) if len(counts) else 0
+    arr = _sizes(counts, N, E, "counts")
+    cfg = config("ring", fuse_depth, None, blocks_per_cu)
+    _check(load().cc_moe_dispatch_padded(rankbuf(send), rankbuf(recv), arr, E, capacity, elem_per_row,
+                                         DTYPES[dtype_name(send)], N, ctypes.byref(cfg), _stream(stream)))
+
+
+def moe_combine_padded(send, recv, counts: Sequence[Sequence[int]], capacity: int, elem_per_row: int = 1,
+                       fuse_depth: int = 0, stream=None, blocks_per_cu: int = 0) -> None:
+    """Expert side send -> token side recv, the transpose of moe_dispatch_padded."""
+    N, E = send.shape[0], len(counts[0]) if len(counts) else 0
+    arr = _sizes(counts, N, E, "counts")
+    cfg = config("ring", fuse_depth, None, blocks_per_cu)
+    _check(load().cc_moe_combine_padded(rankbuf(send), rankbuf(recv), arr, E, capacity, elem_per_row,
+                                        DTYPES[dtype_name(send)], N, ctypes.byref(cfg), _stream(stream)))
+
+
+def all_to_all_hierarchical_workspace_size(counts: Sequence[Sequence[int]], elem_per_row: int, dtype: str,
+                                           local_size: int) -> int:
+    N = len(counts)
+    out = ctypes.c_size_t(0)
+    _check(load().cc_all_to_all_hierarchical_workspace_size(_sizes(counts, N, N, "counts"), elem_per_row,
+                                                            DTYPES[dtype], N, local_size, ctypes.byref(out)))
+    return out.value
+
+
+def make_all_to_all_hierarchical_workspace(counts, elem_per_row: int, dtype: str, local_size: int, device="cuda"):
+    import torch
+    n = all_to_all_hierarchical_workspace_size(counts, elem_per_row, dtype, local_size)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def all_to_all_hierarchical(send, recv, counts: Sequence[Sequence[int]], local_size: int, elem_per_row: int = 1,
+                            workspace=None, stream=None, blocks_per_cu: int = 0) -> None:
+    """AllToAll(v) as aggregate / exchange / distribute over nodes of
+    local_size ranks; same result as all_to_all."""
+    N = send.shape[0]
+    arr = _sizes(counts, N, N, "counts")
+    cfg = config("ring", 0, workspace, blocks_per_cu)
+    _check(load().cc_all_to_all_hierarchical(rankbuf(send), rankbuf(recv), arr, elem_per_row,
+                                             DTYPES[dtype_name(send)], N, local_size, ctypes.byref(cfg),
+                                             _stream(stream)))
+
+
+def all_to_all_traffic(counts: Sequence[Sequence[int]], elem_per_row: int, dtype: str, local_size: int):
+    """[flat, aggregate, exchange, distribute]: (transfers, total bytes, most bytes one rank sends)."""
+    N = len(counts)
+    f = (ctypes.c_int * 4)()
+    t = (ctypes.c_uint64 * 4)()
+    m = (ctypes.c_uint64 * 4)()
+    _check(load().cc_all_to_all_traffic(_sizes(counts, N, N, "counts"), elem_per_row, DTYPES[dtype], N, local_size,
+                                        f, t, m))
+    return [(f[k], t[k], m[k]) for k in range(4)]
+
+
+def all_to_all_step_bytes(counts: Sequence[Sequence[int]], elem_per_row: int, dtype: str):
+    """Pairwise steps k = 0..N-1: (max block bytes, total block bytes)."""
+    N = len(counts)
+    mx = (ctypes.c_uint64 * N)()
+    tt = (ctypes.c_uint64 * N)()
+    _check(load().cc_all_to_all_step_bytes(_sizes(counts, N, N, "counts"), elem_per_row, DTYPES[dtype], N, mx, tt))
+    return list(mx), list(tt)
+
+
+class CopyOp(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_uint32), ("reserved", ctypes.c_uint32), ("src", ctypes.c_uint64),
+                ("dst", ctypes.c_uint64), ("bytes", ctypes.c_uint64)]
+
+
+A2A_KINDS = {"moe_dispatch": 1, "moe_combine": 2, "hierarchical": 3}
+
+
+def all_to_all_plan(kind: str, send: RankBuf, recv: RankBuf, counts: Sequence[Sequence[int]], nranks: int,
+                    elem_per_row: int, dtype: str, nexperts: int = 0, capacity: int = 0, local_size: int = 1,
+                    fuse_depth: int = 0, workspace: int = 0, workspace_bytes: int = 0):
+    """The copies an AllToAll variant performs (cc_all_to_all_plan), for rank
+    buffers given as raw RankBuf addresses: list of (step, src, dst, bytes),
+    src 0 meaning a zero fill."""
+    L = load()
+    flat = [int(v) for row in counts for v in row]
+    arr = (ctypes.c_size_t * max(len(flat), 1))(*flat)
+    cfg = Config(ALGOS["ring"], int(fuse_depth), workspace or None, workspace_bytes, 0, 0)
+    n = ctypes.c_size_t(0)
+    args = (A2A_KINDS[kind], send, recv, arr, nexperts, capacity, elem_per_row, DTYPES[dtype], nranks, local_size,
+            ctypes.byref(cfg))
+    _check(L.cc_all_to_all_plan(*args, None, 0, ctypes.byref(n)))
+    recs = (CopyOp * max(n.value, 1))()
+    _check(L.cc_all_to_all_plan(*args, ctypes.cast(recs, ctypes.c_void_p), n.value, ctypes.byref(n)))
+    return [(recs[i].step, recs[i].src, recs[i].dst, recs[i].bytes) for i in range(n.value)]
 
 
 def raw(fn: str, *args):

@@ -13,12 +13,14 @@
 #include <string>
 #include <vector>
 
+#include "cc_api_internal.h"
 #include "cc_launch.h"
 #include "cc_sched.h"
 
 using namespace cc;
 
-namespace {
+namespace cc {
+namespace api {
 
 thread_local std::string g_err;
 
@@ -64,7 +66,7 @@ bool al16(uint64_t v) { return (v & 15u) == 0; }
 bool al16p(const void* p) { return al16((uint64_t)(uintptr_t)p); }
 uint64_t rup(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-const cc_config_t kDefaultCfg = {CC_ALGO_RING, 0, nullptr, 0, 0, 0};
+extern const cc_config_t kDefaultCfg = {CC_ALGO_RING, 0, nullptr, 0, 0, 0};
 
 cc_status_t common_checks(cc_coll_t coll, int nranks, cc_dtype_t dtype, const cc_config_t* cfg) {
   if (nranks < 1 || nranks > CC_MAX_RANKS)
@@ -112,6 +114,13 @@ bool sides_overlap(const cc_rankbuf_t& a, uint64_t abytes, int an, const cc_rank
 bool same_side(const cc_rankbuf_t& a, const cc_rankbuf_t& b) {
   return a.base == b.base && a.rank_stride_bytes == b.rank_stride_bytes;
 }
+
+}  // namespace api
+}  // namespace cc
+
+using namespace cc::api;
+
+namespace {
 
 cc_status_t grid_fits(uint64_t M, int dt) {
   if (num_tiles(M, dt) > 0x7fffffffull) return fail(CC_ERR_INVALID_ARG, "count too large for one launch");

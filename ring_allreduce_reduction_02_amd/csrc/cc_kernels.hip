@@ -1643,7 +1643,14 @@ __global__ __launch_bounds__(kCopyBlock) void k_copies(CopyArgs a) {
   const uint64_t o1 = o0 + kCopyTile < nb ? o0 + kCopyTile : nb;
   const char* src = a.src[k];
   char* dst = a.dst[k];
-  if ((a.vecmask >> k) & 1) {
+  if (src == nullptr) {  // a fill descriptor: zeros
+    if ((a.vecmask >> k) & 1) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (uint64_t o = o0 + (uint64_t)threadIdx.x * 16; o < o1; o += kCopyTile) stg(dst + o, z);
+    } else {
+      for (uint64_t o = o0 + threadIdx.x; o < o1; o += kCopyBlock) dst[o] = 0;
+    }
+  } else if ((a.vecmask >> k) & 1) {
     for (uint64_t o = o0 + (uint64_t)threadIdx.x * 16; o < o1; o += kCopyTile) stg(dst + o, ldg(src + o));
   } else {
     for (uint64_t o = o0 + threadIdx.x; o < o1; o += kCopyBlock) dst[o] = src[o];

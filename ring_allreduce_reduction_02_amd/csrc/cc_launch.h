@@ -157,7 +157,8 @@ hipError_t launch_hd_ag_step(const Gat& g, int d, int first);
 hipError_t launch_bcast(const char* src, Side dst, int N, int skip, uint64_t nbytes, int vec_ok,
                         int blocks_per_cu, hipStream_t st);
 
-// ---- descriptor copy: up to kMaxDesc (src, dst, bytes) copies in one launch
+// ---- descriptor copy: up to kMaxDesc (src, dst, bytes) copies in one launch;
+// a NULL src fills dst with zero bytes
 struct CopyDesc {
   const char* src;
   char* dst;

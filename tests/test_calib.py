@@ -69,3 +69,12 @@ def test_multidim_time_matches_the_oracle_model():
         a, b = [1e-6 * (i + 1) for i in range(len(dims))], [1e-11 * (i + 2) for i in range(len(dims))]
         assert calib.multidim_time(1e8, dims, a, b) == pytest.approx(cs.multidim_time_model(1e8, dims, a, b))
     assert sum(calib.multidim_time(1e9, (8, 8), (0, 0), (1 / 450e9, 1 / 50e9))) == pytest.approx(8.26e-3, abs=1e-5)
+
+
+def test_pairwise_time_matches_the_oracle_model():
+    from oracle import ccsim as cs
+    g = np.random.default_rng(2)
+    for N in (2, 3, 8):
+        C = g.integers(0, 1000, size=(N, N))
+        mx = [max(int(C[i, (i + k) % N]) for i in range(N)) for k in range(N)]
+        assert calib.pairwise_time(mx, 3e-6, 2e-11) == pytest.approx(cs.pairwise_time_model(C, 3e-6, 2e-11))
