@@ -475,6 +475,67 @@ def alltoall_variants(dev):
     return out
 
 
+def int8_ef(dev):
+    """Block-wise INT8 AllReduce with error feedback at the headline shape
+    (8 ranks, 67,108,864 gradients each): the fused kernel and the two-kernel
+    form (message in a workspace) beside the plain fused ring AllReduce, for
+    float32 and bf16 gradients; GB/s counts the bytes the kernels move
+    (gradients read, error accumulators read and written, results written).
+    The wire side: the message is M + 4 M / 128 bytes per rank against 4 M
+    for float32 (3.88x less).  Accuracy: one step's norm-wise error against
+    the float64 sum, and over 10 steps the error of the running sum of the
+    results against the true running sum (bounded by the last accumulators,
+    the telescoping identity)."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu
+    N, M = 8, 1 << 26
+    gen = torch.Generator(device=dev).manual_seed(20261205)
+    out = {"ranks": N, "count": M, "message_bytes_per_rank": ccgpu.int8_message_bytes(M),
+           "float32_bytes_per_rank": 4 * M, "wire_ratio": round(4 * M / ccgpu.int8_message_bytes(M), 4)}
+    for dtype in ("f32", "bf16"):
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        es = 4 if dtype == "f32" else 2
+        g = (torch.randn(N, M, generator=gen, device=dev) * 1e-3).to(tdt)
+        e = torch.zeros(N, M, device=dev)
+        r = torch.empty_like(g)
+        ms_f = _avg_ms(lambda: ccgpu.all_reduce_int8_ef(g, e, r, fuse_depth=0))
+        ws = torch.empty(ccgpu.int8_ef_workspace_size(N, M, dtype, 1), dtype=torch.uint8, device=dev)
+        ms_2 = _avg_ms(lambda: ccgpu.all_reduce_int8_ef(g, e, r, fuse_depth=1, workspace=ws))
+        ms_p = _avg_ms(lambda: ccgpu.all_reduce(g, r, algo="ring"))
+        fused_bytes = N * M * (2 * es + 8)
+        two_bytes = N * M * (es + 8) + 2 * N * ccgpu.int8_message_bytes(M) + N * M * es
+        out[dtype] = {
+            "fused_ms": round(ms_f, 4), "fused_GBps": round(fused_bytes / ms_f / 1e6, 1),
+            "fused_pct_of_peak": round(100 * fused_bytes / ms_f / 1e6 / PEAK_HBM_GBPS, 2),
+            "two_kernel_ms": round(ms_2, 4), "two_kernel_GBps": round(two_bytes / ms_2 / 1e6, 1),
+            "plain_ring_ms": round(ms_p, 4),
+        }
+        del g, e, r, ws
+        torch.cuda.empty_cache()
+    # accuracy over steps (float32 gradients, 1,048,576 per rank)
+    Ms = 1 << 20
+    e = torch.zeros(N, Ms, device=dev)
+    run_v = torch.zeros(Ms, dtype=torch.float64, device=dev)
+    run_g = torch.zeros(Ms, dtype=torch.float64, device=dev)
+    step_err = []
+    for t in range(10):
+        g = torch.randn(N, Ms, generator=gen, device=dev) * 1e-3
+        exact = g.double().sum(0)
+        r = torch.empty_like(g)
+        ccgpu.all_reduce_int8_ef(g, e, r)
+        torch.cuda.synchronize()
+        step_err.append(float((r[0].double() - exact).norm() / exact.norm()))
+        run_v += r[0].double()
+        run_g += exact
+    resid = float(e.double().sum(0).norm())
+    out["accuracy_f32_1048576"] = {
+        "step_norm_rel_err": [round(x, 6) for x in step_err],
+        "running_sum_norm_rel_err_after_10": float((run_v - run_g).norm() / run_g.norm()),
+        "running_sum_err_norm": float((run_v - run_g).norm()), "sum_of_last_accumulators_norm": resid}
+    return out
+
+
 def norm_rel_err_fp64(send, recv, offsets, counts, step=1 << 24):
     """max over ranks of ||y_r - y64|| / ||y64|| over the given element
     ranges, y64 = the order-free fp64 sum of the inputs (a measurement of the
@@ -720,6 +781,8 @@ def main():
         out["hierarchical"] = hierarchical(dev)
         log("alltoall variants")
         out["alltoall_variants"] = alltoall_variants(dev)
+        log("int8 error feedback")
+        out["int8_ef"] = int8_ef(dev)
     if not args.no_cpu_baseline:
         log("oracle on the host")
         out["cpu_baseline"] = cpu_baseline(N, min(args.cpu_sample, M))

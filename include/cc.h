@@ -439,6 +439,49 @@ cc_status_t cc_all_to_all_plan(cc_a2a_kind_t kind, cc_rankbuf_t send, cc_rankbuf
                                int local_size, const cc_config_t* cfg, cc_copy_op_t* records, size_t cap,
                                size_t* nrecords);
 
+/* ---- Block-wise INT8 compression with error feedback (textbook ch. 6,
+ * "量化：降低精度", "梯度通信的分块量化", "错误反馈与残差累积").
+ * Per rank and per block of CC_QUANT_BLOCK consecutive elements of the rank's
+ * vector (blocks from element 0, the last one possibly short), in float32,
+ * one IEEE operation at a time:
+ *   u = g + e;  s = max|u| / 127;  q = round-half-even(u / s) clamped to
+ *   [-127, 127] (q = 0 when s = 0);  v = q * s;  e <- u - v.
+ * g is the gradient (float32, or bf16 widened exactly), e a float32 error
+ * accumulator the caller keeps from step to step (start it at zero).  The
+ * message a rank would send is q (1 byte per element) plus the scales (one
+ * float32 per block): count + 4 ceil(count / 128) bytes, 3.88x smaller than
+ * float32.  The AllReduce of the compressed contributions sums the v of all
+ * ranks in float32 in the ring AllReduce's order (chunk c's fold starts at
+ * rank c) and gives every rank the sum (bf16: rounded once).  dtype is
+ * CC_FLOAT32 or CC_BFLOAT16 (CC_ERR_UNSUPPORTED otherwise); cfg.algo must be
+ * CC_ALGO_RING.  All buffers are rank-strided device memory. */
+#define CC_QUANT_BLOCK 128
+
+/* The compression step: reads grad, updates err, writes q (int8, count per
+ * rank) and scales (float32, ceil(count/128) per rank).  No two of the four
+ * may overlap. */
+cc_status_t cc_quantize_ef(cc_rankbuf_t grad, cc_rankbuf_t err, cc_rankbuf_t q, cc_rankbuf_t scales, size_t count,
+                           cc_dtype_t dtype, int nranks, const cc_config_t* cfg, cc_stream_t stream);
+
+/* The reduction side: recv (dtype) of every rank = the ring-order float32 sum
+ * of the dequantized messages of all ranks.  recv must not overlap q or
+ * scales. */
+cc_status_t cc_all_reduce_dequant(cc_rankbuf_t q, cc_rankbuf_t scales, cc_rankbuf_t recv, size_t count,
+                                  cc_dtype_t dtype, int nranks, const cc_config_t* cfg, cc_stream_t stream);
+
+/* Compression with error feedback and the AllReduce of the compressed
+ * contributions in one call: recv = the sum of every rank's v, err updated.
+ * fuse_depth 0: one kernel, no message in memory; fuse_depth >= 1: the two
+ * calls above, the message in the caller's workspace
+ * (cc_int8_ef_workspace_size).  Same bits either way.  In place iff
+ * grad.base == recv.base with equal strides; err overlaps neither. */
+cc_status_t cc_all_reduce_int8_ef(cc_rankbuf_t grad, cc_rankbuf_t err, cc_rankbuf_t recv, size_t count,
+                                  cc_dtype_t dtype, int nranks, const cc_config_t* cfg, cc_stream_t stream);
+cc_status_t cc_int8_ef_workspace_size(const cc_config_t* cfg, int nranks, size_t count, cc_dtype_t dtype,
+                                      size_t* bytes);
+/* count + 4 ceil(count / CC_QUANT_BLOCK): the bytes of one rank's message. */
+cc_status_t cc_int8_message_bytes(size_t count, size_t* bytes);
+
 const char* cc_status_string(cc_status_t status);
 const char* cc_last_error(void);
 const char* cc_version(void);

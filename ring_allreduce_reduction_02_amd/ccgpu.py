@@ -106,6 +106,15 @@ EXPORTS = {
     "cc_all_to_all_plan": [ctypes.c_int, RankBuf, RankBuf, ctypes.POINTER(ctypes.c_size_t), ctypes.c_int,
                            ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                            ctypes.POINTER(Config), ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)],
+    "cc_quantize_ef": [RankBuf, RankBuf, RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                       ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_all_reduce_dequant": [RankBuf, RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                              ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_all_reduce_int8_ef": [RankBuf, RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                              ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_int8_ef_workspace_size": [ctypes.POINTER(Config), ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
+                                  ctypes.POINTER(ctypes.c_size_t)],
+    "cc_int8_message_bytes": [ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)],
     "cc_status_string": [ctypes.c_int],
     "cc_last_error": [],
     "cc_version": [],
@@ -465,6 +474,50 @@ def all_to_all_plan(kind: str, send: RankBuf, recv: RankBuf, counts: Sequence[Se
     recs = (CopyOp * max(n.value, 1))()
     _check(L.cc_all_to_all_plan(*args, ctypes.cast(recs, ctypes.c_void_p), n.value, ctypes.byref(n)))
     return [(recs[i].step, recs[i].src, recs[i].dst, recs[i].bytes) for i in range(n.value)]
+
+
+QUANT_BLOCK = 128
+
+
+def quantize_ef(grad, err, q, scales, stream=None, blocks_per_cu: int = 0) -> None:
+    """grad [N, M] (f32/bf16), err [N, M] f32 (updated), q [N, M] int8,
+    scales [N, ceil(M/128)] f32: the compression step with error feedback."""
+    N, M = grad.shape
+    cfg = config("ring", 0, None, blocks_per_cu)
+    _check(load().cc_quantize_ef(rankbuf(grad), rankbuf(err), rankbuf(q), rankbuf(scales), M,
+                                 DTYPES[dtype_name(grad)], N, ctypes.byref(cfg), _stream(stream)))
+
+
+def all_reduce_dequant(q, scales, recv, stream=None, blocks_per_cu: int = 0) -> None:
+    """recv [N, M] (f32/bf16) = ring-order sum of every rank's dequantized message."""
+    N, M = recv.shape
+    cfg = config("ring", 0, None, blocks_per_cu)
+    _check(load().cc_all_reduce_dequant(rankbuf(q), rankbuf(scales), rankbuf(recv), M,
+                                        DTYPES[dtype_name(recv)], N, ctypes.byref(cfg), _stream(stream)))
+
+
+def int8_ef_workspace_size(nranks: int, count: int, dtype: str, fuse_depth: int) -> int:
+    out = ctypes.c_size_t(0)
+    cfg = Config(ALGOS["ring"], int(fuse_depth), None, 0, 0, 0)
+    _check(load().cc_int8_ef_workspace_size(ctypes.byref(cfg), nranks, count, DTYPES[dtype], ctypes.byref(out)))
+    return out.value
+
+
+def all_reduce_int8_ef(grad, err, recv=None, fuse_depth: int = 0, workspace=None, stream=None,
+                       blocks_per_cu: int = 0) -> None:
+    """Compression with error feedback and the AllReduce of the compressed
+    contributions (recv defaults to grad: in place)."""
+    recv = grad if recv is None else recv
+    N, M = grad.shape
+    cfg = config("ring", fuse_depth, workspace, blocks_per_cu)
+    _check(load().cc_all_reduce_int8_ef(rankbuf(grad), rankbuf(err), rankbuf(recv), M, DTYPES[dtype_name(grad)], N,
+                                        ctypes.byref(cfg), _stream(stream)))
+
+
+def int8_message_bytes(count: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().cc_int8_message_bytes(count, ctypes.byref(out)))
+    return out.value
 
 
 def raw(fn: str, *args):

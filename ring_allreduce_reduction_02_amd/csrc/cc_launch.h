@@ -92,6 +92,34 @@ constexpr int kMaxHierLevels = 4;
 hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int nd, int top, const uint64_t* segbnd,
                              const uint32_t* seg);
 
+// ---- INT8 compression with error feedback: blocks of kQBlock elements of a
+// rank's vector, one float32 scale each.  g: gradients (dt), e: float32 error
+// accumulators, q: int8 values, s: float32 scales, r: results (dt); bnd: the
+// N chunks of the ring order.
+constexpr int kQBlock = 128;
+struct QLaunch {
+  const char* g;
+  uint64_t gs;
+  char* e;
+  uint64_t es;
+  char* q;
+  uint64_t qs;
+  char* s;
+  uint64_t ss;
+  char* r;
+  uint64_t rs;
+  uint64_t M;
+  const uint64_t* bnd;
+  int N;
+  int dt;  // DT_F32 or DT_BF16
+  int vec_ok;
+  int blocks_per_cu;
+  hipStream_t st;
+};
+hipError_t launch_quant_ef(const QLaunch& L);        // g, e -> e, q, s
+hipError_t launch_dequant_reduce(const QLaunch& L);  // q, s -> r
+hipError_t launch_quant_ef_fused(const QLaunch& L);  // g, e -> e, r
+
 // ---- descriptor steps (GDesc flags)
 enum : unsigned {
   GD_LOCAL_SEND = 1u,   // local operand from send[dst] (else partial[dst])

@@ -36,7 +36,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(ROOT, "include", "cc.h")).read()
     hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
-    names = set(re.findall(r"\b(cc_[a-z_]+)\s*\(", hdr))
+    names = set(re.findall(r"\b(cc_[a-z0-9_]+)\s*\(", hdr))
     assert {"cc_all_reduce", "cc_reduce_scatter", "cc_all_gather", "cc_broadcast", "cc_all_to_all"} <= names
     for n in names:
         assert hasattr(lib, n), n
