@@ -640,6 +640,60 @@ def workloads(dev):
     return out
 
 
+def profile_section(name, dev, steps, warmup):
+    """Run one kernel of the next-row schedules `steps` times (after `warmup`)
+    for rocprofv3, and return its algorithmic bytes per call: the kernel's
+    HBM reads and writes by the schedule's definition."""
+    import numpy as np
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu, synth
+    gen = torch.Generator(device=dev).manual_seed(20261206)
+    N, M = 8, 1 << 26
+    if name in ("hier_2x2x2", "dbt_n8", "hier_8x8"):
+        if name == "hier_8x8":
+            N, M = 64, 1 << 23
+        x = torch.randn(N, M, generator=gen, device=dev) * 1e-3
+        y = torch.empty_like(x)
+        if name == "dbt_n8":
+            fn = lambda: ccgpu.all_reduce(x, y, algo="double_tree")
+        else:
+            dims = (2, 2, 2) if name == "hier_2x2x2" else (8, 8)
+            fn = lambda: ccgpu.all_reduce_hierarchical(x, y, dims)
+        nbytes = 2 * N * M * 4
+    elif name in ("int8_ef_f32", "int8_quant_f32", "int8_dequant_f32"):
+        g = torch.randn(N, M, generator=gen, device=dev) * 1e-3
+        e = torch.zeros(N, M, device=dev)
+        r = torch.empty_like(g)
+        q = torch.empty(N, M, dtype=torch.int8, device=dev)
+        sc = torch.empty(N, M // 128, device=dev)
+        ccgpu.quantize_ef(g, e, q, sc)
+        if name == "int8_ef_f32":
+            fn, nbytes = (lambda: ccgpu.all_reduce_int8_ef(g, e, r)), N * M * 16
+        elif name == "int8_quant_f32":
+            fn, nbytes = (lambda: ccgpu.quantize_ef(g, e, q, sc)), N * M * 13 + N * (M // 128) * 4
+        else:
+            fn, nbytes = (lambda: ccgpu.all_reduce_dequant(q, sc, r)), N * M * 5 + N * (M // 128) * 4
+    elif name == "moe_padded_c125":
+        H, T, K, E = 7168, 4096, 8, 64
+        ch = synth.moe_routing(N, T, E, K)
+        Ce = np.stack([np.bincount(c.reshape(-1), minlength=E) for c in ch]).astype(np.int64)
+        cap = ccgpu.moe_capacity(1, T, K, E, 5, 4)
+        x = torch.randn(N, int(Ce.sum(1).max()) * H, generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty(N, E * cap * H, device=dev, dtype=torch.bfloat16)
+        fn = lambda: ccgpu.moe_dispatch_padded(x, y, Ce.tolist(), cap, H)
+        nbytes = (int(np.minimum(Ce, cap).sum()) + N * E * cap) * H * 2
+    else:
+        raise SystemExit(f"unknown profile section {name}")
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return nbytes
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -659,6 +713,10 @@ def main():
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="before timing, run a plain device copy of this many bytes 3 times "
                          "(a known-size kernel for scaling HBM counters)")
+    ap.add_argument("--profile-section", default="",
+                    help="run only this kernel of the next-row schedules --steps times (for rocprofv3): "
+                         "hier_2x2x2, hier_8x8, dbt_n8, int8_ef_f32, int8_quant_f32, int8_dequant_f32, "
+                         "moe_padded_c125")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -676,6 +734,17 @@ def main():
         sys.exit(1)
     ccgpu.load()
     dev = "cuda:0"
+    if args.profile_section:
+        if args.copy_probe_bytes:
+            a = torch.empty(args.copy_probe_bytes, dtype=torch.uint8, device=dev).fill_(1)
+            b = torch.empty_like(a)
+            for _ in range(3):
+                b.copy_(a)
+            torch.cuda.synchronize()
+            del a, b
+        nbytes = profile_section(args.profile_section, dev, args.steps, args.warmup)
+        print(json.dumps({"profile_section": args.profile_section, "alg_bytes_per_call": nbytes}), flush=True)
+        return
     N, M = args.ranks, args.count
     tdt = torch.float32 if args.dtype == "f32" else torch.bfloat16
     es = 4 if args.dtype == "f32" else 2
