@@ -81,6 +81,25 @@ def time_launches(fn, steps, warmup):
     return {"total_ms": t0.elapsed_time(t1), "per_launch_ms": per, "wall_s": wall}
 
 
+def time_steps(fn, steps, warmup):
+    """Warm up, then time exactly `steps` back-to-back calls between one HIP
+    event pair on the launching stream, with a device synchronization on both
+    sides (no instrumentation between the calls)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return {"total_ms": t0.elapsed_time(t1), "wall_s": time.perf_counter() - wall0}
+
+
 def time_graph(fn, reps=20, per_graph=1):
     """GPU time per call of fn without host launch overhead: `per_graph` calls
     captured into one HIP graph (torch.cuda.CUDAGraph), replayed `reps` times
@@ -190,7 +209,7 @@ def _time_gpu(fn, reps, per):
     except Exception:  # noqa: BLE001 - capture unsupported for this launch kind
         import torch
         torch.cuda.synchronize()
-        r = time_launches(fn, reps * per, 3)
+        r = time_steps(fn, reps * per, 3)
         return r["total_ms"] / (reps * per), "eager"
 
 
@@ -252,7 +271,7 @@ def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30):
 
 
 def _avg_ms(fn, steps=10, warmup=3):
-    r = time_launches(fn, steps, warmup)
+    r = time_steps(fn, steps, warmup)
     return r["total_ms"] / steps
 
 
@@ -768,11 +787,14 @@ def main():
                          blocks_per_cu=args.blocks_per_cu)
 
     log("timing")
-    res = time_launches(step, args.steps, args.warmup)
+    # the K timed steps run back to back; the per-launch durations behind the
+    # roofline come from a second, instrumented pass of K launches (an event
+    # pair around every launch adds about 5 us per step to the first)
+    res = time_steps(step, args.steps, args.warmup)
     ms_per_step = res["total_ms"] / args.steps
     alg_bytes = 2 * N * M * es
     value = alg_bytes / (ms_per_step / 1e3) / 1e9
-    per = res["per_launch_ms"]
+    per = time_launches(step, args.steps, 2)["per_launch_ms"]
     avg_launch_ms = sum(per) / len(per)
     achieved = alg_bytes / (avg_launch_ms / 1e3) / 1e9
     busbw = (M * es) / (ms_per_step / 1e3) * 2 * (N - 1) / N / 1e9
@@ -831,7 +853,7 @@ def main():
         rb = rank_tensor(N, M, torch.bfloat16, args.pad_bytes, dev)
         upload(xb, sb)
         del xb
-        rb16 = time_launches(lambda: ccgpu.all_reduce(sb, rb, algo="ring", fuse_depth=0), args.steps, args.warmup)
+        rb16 = time_steps(lambda: ccgpu.all_reduce(sb, rb, algo="ring", fuse_depth=0), args.steps, args.warmup)
         ms16 = rb16["total_ms"] / args.steps
         out["bf16_twin"] = {"ms_per_step": round(ms16, 5),
                             "GBps": round(2 * N * M * 2 / (ms16 / 1e3) / 1e9, 2),

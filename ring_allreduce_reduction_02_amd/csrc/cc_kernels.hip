@@ -457,8 +457,24 @@ struct FusedArgs {
   int vec_ok;
   int tree_leaves;  // trees: leaves of the power-of-two tree (<= NR)
   int tree_pairs;   // trees: leading leaves that are pair folds
+  // log2 of the tiles per chunk when every chunk is exactly 2^k full tiles
+  // (M = N 2^k tiles) and the buffers are 16-byte aligned, else -1
+  int tpc_log2;
   uint64_t bnd[kMaxRanks + 1];
 };
+
+// The tile of workgroup idx when every chunk holds exactly 2^tpc_log2 full
+// tiles: its chunk is a shift of the tile index, and it takes the vector path.
+template <int V>
+__device__ __forceinline__ Tile<V> tile_pow2(uint64_t idx, int tpc_log2) {
+  const uint64_t tile = (uint64_t)kBlock * kUnroll * V;
+  Tile<V> t;
+  t.e0 = idx * tile;
+  t.e1 = t.e0 + tile;
+  t.c = (uint32_t)(idx >> tpc_log2);
+  t.fast = true;
+  return t;
+}
 
 // AllReduce (rs_mode 0): every chunk's N-1 ReduceScatter steps folded in
 // registers in the schedule's order, then the AllGather as N stores.
@@ -477,7 +493,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // so only a ReduceScatter needs the chunk of a tile
   const int tiling = (ALG != ALG_RING && !a.rs_mode) ? 1 : N;
   const TreeShape ts{a.tree_leaves, a.tree_pairs};
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, tiling, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, tiling, a.vec_ok);
   if (t.fast) {
     // Every rank's tile starts at a workgroup-uniform address; a lane adds
     // its own 16-byte offset (scalar base + 32-bit vector offset).
@@ -554,6 +570,7 @@ struct HierArgs {
   int nd;
   int top;
   int vec_ok;
+  int tpc_log2;  // segments of exactly 2^k full tiles: log2 of k, else -1
   int p[kMaxHierLevels];
   int stride[kMaxHierLevels];
   uint32_t seg[kMaxRanks];
@@ -662,7 +679,7 @@ __global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   static_assert(kMaxHierLevels == 4, "four levels");
   const int N = a.N;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const uint32_t lane = threadIdx.x * 16u;
     const char* s0 = a.sb + t.e0 * SZ;
@@ -867,7 +884,7 @@ __global__ __launch_bounds__(kBlock) void k_ring2_fused(FusedArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   const int N = EXACT ? NR : a.N;
   const int ca = N / 2, cb = (N - 1) / 2;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const uint32_t lane = threadIdx.x * 16u;
@@ -1023,6 +1040,7 @@ struct PassArgs {
   int s0;
   int k;
   int pin_recv;  // partials live in the receiving rank's recv buffer
+  int tpc_log2;  // chunks of exactly 2^k full tiles: log2 of k, else -1
   uint64_t bnd[kMaxRanks + 1];
 };
 
@@ -1036,7 +1054,7 @@ __device__ __forceinline__ void ring_pass_tile(const PassArgs& a, uint64_t tile,
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N;
   const bool fin = s0 + k == N - 1;
-  const Tile<V> t = tile_at<V>(tile, a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(tile, a.tpc_log2) : tile_at<V>(tile, a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const int start = a.rs_mode ? wrapN(c + 1, N) : c;
@@ -1116,6 +1134,7 @@ struct StepArgs {
   int first;     // operands come from the send buffers
   int last;      // results are final (buffer type)
   int acc_recv;  // intermediate accumulators live in recv (else in wb)
+  int tpc_log2;  // chunks of exactly 2^k full tiles: log2 of k, else -1
   uint64_t bnd[kMaxRanks + 1];
 };
 
@@ -1156,7 +1175,7 @@ __global__ __launch_bounds__(kBlock) void k_hd_rs_step(StepArgs a) {
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N, d = a.d;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const int base = c & ~(d - 1);
@@ -1204,7 +1223,7 @@ __global__ __launch_bounds__(kBlock) void k_bfly_step(StepArgs a) {
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N, d = a.d;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -1257,6 +1276,7 @@ struct GatArgs {
   int vec_ok;
   int s0;
   int k;
+  int tpc_log2;  // chunks of exactly 2^k full tiles: log2 of k, else -1
   uint64_t bnd[kMaxRanks + 1];
 };
 
@@ -1268,7 +1288,7 @@ template <int SZ>
 __device__ __forceinline__ void ring_ag_tile(const GatArgs& a, uint64_t tile, int s0, int k) {
   constexpr int V = 16 / SZ;
   const int N = a.N;
-  const Tile<V> t = tile_at<V>(tile, a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(tile, a.tpc_log2) : tile_at<V>(tile, a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const uint64_t b0 = a.bnd[c];
@@ -1538,7 +1558,7 @@ template <int SZ>
 __global__ __launch_bounds__(kBlock) void k_hd_ag_step(GatArgs a) {
   constexpr int V = 16 / SZ;
   const int N = a.N, d = a.s0, first = a.k;  // s0 carries d, k carries "first"
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const uint64_t b0 = a.bnd[c];
@@ -1677,6 +1697,7 @@ struct QArgs {
   uint64_t M;
   int N;
   int vec_ok;
+  int tpc_log2;  // chunks of exactly 2^k full tiles: log2 of k, else -1
   uint64_t bnd[kMaxRanks + 1];
 };
 
@@ -1827,7 +1848,7 @@ __global__ __launch_bounds__(kBlock) void k_dequant_reduce(QArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   typedef typename QPack<V>::T QT;
   const int N = a.N;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const uint64_t el = t.e0 + (uint64_t)threadIdx.x * V;
     const uint64_t sb = (el / kQBlock) * 4;
@@ -1878,7 +1899,7 @@ __global__ __launch_bounds__(kBlock) void k_quant_ef_fused(QArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   constexpr int B = 4;  // ranks loaded ahead of their compression
   const int N = a.N;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
   if (t.fast) {
     const uint32_t lane = threadIdx.x;
     const uint64_t el = t.e0 + (uint64_t)lane * V;
@@ -1954,12 +1975,29 @@ hipError_t by_dt_op(int dt, int op, F f) {
   return hipErrorInvalidValue;
 }
 
+// log2 of the tiles per chunk when the M elements split into N chunks of
+// exactly 2^k full tiles each (the chunk bounds bnd[c] = floor(c M / N) are
+// then c 2^k tiles), else -1
+int pow2_tiles_per_chunk_v(uint64_t M, int N, int velems, int vec_ok) {
+  const uint64_t tile = (uint64_t)kBlock * kUnroll * velems;
+  if (!vec_ok || N < 1 || M % ((uint64_t)N * tile)) return -1;
+  const uint64_t tpc = M / N / tile;
+  if (tpc == 0 || (tpc & (tpc - 1))) return -1;
+  int k = 0;
+  while ((1ull << k) < tpc) ++k;
+  return k;
+}
+int pow2_tiles_per_chunk(uint64_t M, int N, int dt, int vec_ok) {
+  return pow2_tiles_per_chunk_v(M, N, vec_elems(dt), vec_ok);
+}
+
 FusedArgs fused_args(const Red& r) {
   FusedArgs a;
   a.sb = r.send.base; a.ss = r.send.stride;
   a.rb = r.recv.base; a.rs = r.recv.stride;
   a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
   a.tree_leaves = r.N; a.tree_pairs = 0;
+  a.tpc_log2 = pow2_tiles_per_chunk(r.M, r.N, r.dt, r.vec_ok);
   for (int c = 0; c <= r.N; ++c) a.bnd[c] = r.bnd[c];
   return a;
 }
@@ -2172,6 +2210,8 @@ hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int 
   a.sb = r.send.base; a.ss = r.send.stride;
   a.rb = r.recv.base; a.rs = r.recv.stride;
   a.M = r.M; a.N = r.N; a.nd = nd; a.top = top; a.vec_ok = r.vec_ok;
+  // the N segments are equal when every level splits exactly
+  a.tpc_log2 = pow2_tiles_per_chunk(r.M, r.N, r.dt, r.vec_ok);
   for (int i = 0; i < kMaxHierLevels; ++i) {
     a.p[i] = i < nd ? p[i] : 1;
     a.stride[i] = i < nd ? stride[i] : 0;
@@ -2196,6 +2236,7 @@ QArgs q_args(const QLaunch& L) {
   a.sb = L.s; a.ss = L.ss;
   a.rb = L.r; a.rs = L.rs;
   a.M = L.M; a.N = L.N; a.vec_ok = L.vec_ok;
+  a.tpc_log2 = L.bnd ? pow2_tiles_per_chunk(L.M, L.N, L.dt, L.vec_ok) : -1;
   for (int c = 0; c <= L.N; ++c) a.bnd[c] = L.bnd ? L.bnd[c] : 0;
   return a;
 }
@@ -2282,6 +2323,7 @@ hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv)
   a.wb = r.ws.base;
   a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
   a.s0 = s0; a.k = k; a.pin_recv = partial_in_recv;
+  a.tpc_log2 = pow2_tiles_per_chunk(r.M, r.N, r.dt, r.vec_ok);
   for (int c = 0; c <= r.N; ++c) a.bnd[c] = r.bnd[c];
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
   const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * (k + 2), kSkewedTarget);
@@ -2307,6 +2349,7 @@ hipError_t launch_ring_queue(const Red& r, int k, unsigned* bar) {
   g.rb = r.recv.base; g.rs = r.recv.stride;
   g.M = r.M; g.N = r.N; g.mode = 0; g.vec_ok = r.vec_ok; g.s0 = 0; g.k = k;
   for (int c = 0; c <= r.N; ++c) p.bnd[c] = g.bnd[c] = r.bnd[c];
+  p.tpc_log2 = g.tpc_log2 = pow2_tiles_per_chunk(r.M, r.N, r.dt, r.vec_ok);
   a.bar = bar;
   a.k = k;
   a.npass = (r.N - 1 + k - 1) / k;
@@ -2347,6 +2390,7 @@ static StepArgs step_args(const Red& r, int d, int first, int last, int acc_in_r
   a.wb = r.ws.base; a.ws = r.ws.stride;
   a.M = r.M; a.N = r.N; a.rs_mode = r.rs_mode; a.vec_ok = r.vec_ok;
   a.d = d; a.first = first; a.last = last; a.acc_recv = acc_in_recv;
+  a.tpc_log2 = pow2_tiles_per_chunk(r.M, r.N, r.dt, r.vec_ok);
   for (int c = 0; c <= r.N; ++c) a.bnd[c] = r.bnd[c];
   return a;
 }
@@ -2379,6 +2423,7 @@ static GatArgs gat_args(const Gat& g, int s0, int k) {
   a.rb = g.recv.base; a.rs = g.recv.stride;
   a.M = g.M; a.N = g.N; a.mode = g.ag_mode; a.vec_ok = g.vec_ok;
   a.s0 = s0; a.k = k;
+  a.tpc_log2 = pow2_tiles_per_chunk_v(g.M, g.N, 16 / g.esize, g.vec_ok);
   for (int c = 0; c <= g.N; ++c) a.bnd[c] = g.bnd[c];
   return a;
 }
