@@ -26,6 +26,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "cc_launch.h"
 
 namespace cc {
@@ -163,11 +165,12 @@ __device__ __forceinline__ void stw_vec(char* p, const typename Ty<DT>::A* x) {
 
 // ------------------------------------------------------------------ operators
 
+// NaN if either is NaN, +0 over -0; written as selects so that a fold of
+// loaded values stays straight-line code (its loads can all be in flight).
 __device__ __forceinline__ float fmax_ieee(float a, float b) {
-  if (a != a || b != b) return __uint_as_float(0x7fc00000u);
-  if (a > b) return a;
-  if (b > a) return b;
-  return __uint_as_float(__float_as_uint(a) & __float_as_uint(b));  // +0 beats -0
+  const float eq = __uint_as_float(__float_as_uint(a) & __float_as_uint(b));  // a == b: +0 beats -0
+  const float m = a > b ? a : (a == b ? eq : b);
+  return (a != a || b != b) ? __uint_as_float(0x7fc00000u) : m;
 }
 
 template <int DT, int OP>
@@ -201,10 +204,22 @@ __device__ __forceinline__ uint32_t chunk_in(const uint64_t* bnd, int N, uint64_
 }
 // The same chunk when the bounds are exactly floor(c*M/N), as they are for
 // every schedule's chunks: floor(c*M/N) <= e holds for c <= ((e+1)*N - 1)/M,
-// so one division replaces the scan (per-element lookups in tiles that span
-// many small chunks).
+// so one quotient replaces the scan.  The quotient is below N <= 64: a float
+// estimate through the reciprocal is within 2^-14 of num/M (each of the two
+// conversions, the reciprocal and the product adds at most about 2^-23
+// relative error), so its floor is off by at most one, and one 64-bit
+// remainder check makes it exact -- a few instructions instead of the long
+// expansion of a 64-bit integer division.
+__device__ __forceinline__ float u64_to_f32(uint64_t x) {
+  return (float)(uint32_t)(x >> 32) * 4294967296.0f + (float)(uint32_t)x;
+}
 __device__ __forceinline__ uint32_t chunk_of(uint64_t M, int N, uint64_t e) {
-  return (uint32_t)(((e + 1) * (uint64_t)N - 1) / M);
+  const uint64_t num = (e + 1) * (uint64_t)N - 1;  // < M N
+  uint32_t q = (uint32_t)(u64_to_f32(num) * __builtin_amdgcn_rcpf(u64_to_f32(M)));
+  const int64_t rem = (int64_t)(num - (uint64_t)q * M);
+  if (rem < 0) --q;
+  else if ((uint64_t)rem >= M) ++q;
+  return q;
 }
 __device__ __forceinline__ int wrapN(int r, int N) { return r >= N ? r - N : r; }
 __device__ __forceinline__ int modN(int r, int N) { return ((r % N) + N) % N; }
@@ -233,6 +248,21 @@ __device__ __forceinline__ Tile<V> tile_at(uint64_t idx, uint64_t M, const uint6
 template <int V>
 __device__ __forceinline__ Tile<V> tile_of(uint64_t M, const uint64_t* bnd, int N, int vec_ok) {
   return tile_at<V>(blockIdx.x, M, bnd, N, vec_ok);
+}
+// The same for chunks at the floor bounds floor(c M / N): the chunks of the
+// tile's first and last element by the closed form, a fixed cost instead of
+// a scan over the N+1 bounds (each step of which waits for a scalar load).
+template <int V>
+__device__ __forceinline__ Tile<V> tile_floor(uint64_t idx, uint64_t M, int N, int vec_ok) {
+  const uint64_t tile = (uint64_t)kBlock * kUnroll * V;
+  Tile<V> t;
+  t.e0 = idx * tile;
+  t.e1 = t.e0 + tile < M ? t.e0 + tile : M;
+  const uint32_t c0 = chunk_of(M, N, t.e0);
+  const uint32_t c1 = chunk_of(M, N, t.e1 - 1);
+  t.c = c0;
+  t.fast = vec_ok && (t.e1 - t.e0) == tile && c0 == c1;
+  return t;
 }
 
 __device__ __forceinline__ uint64_t vec_elem(uint64_t e0, int u, int V) {
@@ -493,7 +523,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // so only a ReduceScatter needs the chunk of a tile
   const int tiling = (ALG != ALG_RING && !a.rs_mode) ? 1 : N;
   const TreeShape ts{a.tree_leaves, a.tree_pairs};
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, tiling, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, tiling, a.vec_ok);
   if (t.fast) {
     // Every rank's tile starts at a workgroup-uniform address; a lane adds
     // its own 16-byte offset (scalar base + 32-bit vector offset).
@@ -775,29 +805,35 @@ __device__ __forceinline__ void dbt_fold(typename Ty<DT>::A (*x)[Ty<DT>::V], int
 // Double binary tree AllReduce: elements [0, M/2) use the tree above over
 // ranks in order, [M/2, M) the same tree with rank p in slot p-1 (slot s
 // holds rank s+1 mod N).  The host passes bnd = {0, M/2, M} so a tile lies in
-// one half on the vector path.
-template <int DT, int OP, int NR>
+// one half on the vector path.  EXACT: N == NR, every slot holds a rank and
+// the fold's shape is fixed at compile time (the slot loads then cannot be
+// split by rank-count branches, which would let the compiler wait on each
+// load before issuing the next).
+template <int DT, int OP, int NR, bool EXACT>
 __global__ __launch_bounds__(kBlock) void k_dbt_fused(FusedArgs a) {
   typedef typename Ty<DT>::A A;
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
-  const int N = a.N;
-  const Tile<V> t = tile_of<V>(a.M, a.bnd, 2, a.vec_ok);
+  const int N = EXACT ? NR : a.N;
+  const Tile<V> t = tile_floor<V>(blockIdx.x, a.M, 2, a.vec_ok);
   if (t.fast) {
     const int half = (int)t.c;
     const uint32_t lane = threadIdx.x * 16u;
     const uint64_t eb = t.e0 * SZ;
     // slot s holds rank s (first half) or s+1 mod N (second half): a scalar
-    // pointer walk; all loads are issued before any is used
+    // pointer walk; all loads are issued before any is used.  With a runtime
+    // N the slots past N load rank 0's vector again (a cache hit, never
+    // used): a load under a rank-count branch would make its register a
+    // join of two values, whose copy waits for the load before the next one
+    // is issued.
     const char* const b0 = a.sb + eb;
     const char* p = half ? b0 + a.ss : b0;
     u32x4 raw[NR];
 #pragma unroll
-    for (int s = 0; s < NR; ++s)
-      if (s < N) {
-        raw[s] = ldg(p + lane);
-        p = (half && s + 2 == N) ? b0 : p + a.ss;
-      }
+    for (int s = 0; s < NR; ++s) {
+      raw[s] = ldg((s < N ? p : b0) + lane);
+      p = s >= N ? p : ((half && s + 2 == N) ? b0 : p + a.ss);
+    }
     A x[NR][V];
 #pragma unroll
     for (int s = 0; s < NR; ++s)
@@ -884,7 +920,7 @@ __global__ __launch_bounds__(kBlock) void k_ring2_fused(FusedArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   const int N = EXACT ? NR : a.N;
   const int ca = N / 2, cb = (N - 1) / 2;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const uint32_t lane = threadIdx.x * 16u;
@@ -1054,7 +1090,7 @@ __device__ __forceinline__ void ring_pass_tile(const PassArgs& a, uint64_t tile,
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N;
   const bool fin = s0 + k == N - 1;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(tile, a.tpc_log2) : tile_at<V>(tile, a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(tile, a.tpc_log2) : tile_floor<V>(tile, a.M, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const int start = a.rs_mode ? wrapN(c + 1, N) : c;
@@ -1086,27 +1122,52 @@ __device__ __forceinline__ void ring_pass_tile(const PassArgs& a, uint64_t tile,
       }
     }
   } else {
-    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = chunk_of(a.M, N, e);
-      const int start = a.rs_mode ? wrapN((int)c + 1, N) : (int)c;
-      A acc;
+    // Element-wise (a tile across chunk boundaries, a ragged tail, unaligned
+    // buffers): a thread's V elements, kBlock apart, are all loaded before
+    // any is stored, so their memory latencies overlap; an idle slot loads
+    // the tile's first element and stores nothing.
+    A acc[V];
+    uint64_t ev[V];
+    uint32_t cv[V];
+    int sv[V];
+    bool ok[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const uint64_t e = t.e0 + threadIdx.x + (uint64_t)u * kBlock;
+      ok[u] = e < t.e1;
+      ev[u] = ok[u] ? e : t.e0;
+      cv[u] = chunk_of(a.M, N, ev[u]);
+      sv[u] = a.rs_mode ? wrapN((int)cv[u] + 1, N) : (int)cv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
       if (s0 == 0)
-        acc = ld1<DT>(a.sb + (uint64_t)start * a.ss + e * SZ);
+        acc[u] = ld1<DT>(a.sb + (uint64_t)sv[u] * a.ss + ev[u] * SZ);
       else if (a.pin_recv)
-        acc = ld1<DT>(a.rb + (uint64_t)wrapN(start + s0, N) * a.rs + e * SZ);
+        acc[u] = ld1<DT>(a.rb + (uint64_t)wrapN(sv[u] + s0, N) * a.rs + ev[u] * SZ);
       else
-        acc = ldw1<DT>(a.wb + e * 4);
-      for (int j = s0 + 1; j <= s0 + k; ++j)
-        acc = opf<DT, OP>(ld1<DT>(a.sb + (uint64_t)wrapN(start + j, N) * a.ss + e * SZ), acc);
+        acc[u] = ldw1<DT>(a.wb + ev[u] * 4);
+    }
+    for (int j = s0 + 1; j <= s0 + k; ++j) {
+      A x[V];
+#pragma unroll
+      for (int u = 0; u < V; ++u) x[u] = ld1<DT>(a.sb + (uint64_t)wrapN(sv[u] + j, N) * a.ss + ev[u] * SZ);
+#pragma unroll
+      for (int u = 0; u < V; ++u) acc[u] = opf<DT, OP>(x[u], acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      if (!ok[u]) continue;
+      const uint64_t e = ev[u];
       if (fin) {
         if (a.rs_mode)
-          st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, acc);
+          st1<DT>(a.rb + (uint64_t)cv[u] * a.rs + (e - a.bnd[cv[u]]) * SZ, acc[u]);
         else
-          st1<DT>(a.rb + (uint64_t)wrapN(start + N - 1, N) * a.rs + e * SZ, acc);
+          st1<DT>(a.rb + (uint64_t)wrapN(sv[u] + N - 1, N) * a.rs + e * SZ, acc[u]);
       } else if (a.pin_recv) {
-        st1<DT>(a.rb + (uint64_t)wrapN(start + s0 + k, N) * a.rs + e * SZ, acc);
+        st1<DT>(a.rb + (uint64_t)wrapN(sv[u] + s0 + k, N) * a.rs + e * SZ, acc[u]);
       } else {
-        stw1<DT>(a.wb + e * 4, acc);
+        stw1<DT>(a.wb + e * 4, acc[u]);
       }
     }
   }
@@ -1175,7 +1236,7 @@ __global__ __launch_bounds__(kBlock) void k_hd_rs_step(StepArgs a) {
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N, d = a.d;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const int base = c & ~(d - 1);
@@ -1223,7 +1284,7 @@ __global__ __launch_bounds__(kBlock) void k_bfly_step(StepArgs a) {
   constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
   const int N = a.N, d = a.d;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, N, a.vec_ok);
   if (t.fast) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -1288,7 +1349,7 @@ template <int SZ>
 __device__ __forceinline__ void ring_ag_tile(const GatArgs& a, uint64_t tile, int s0, int k) {
   constexpr int V = 16 / SZ;
   const int N = a.N;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(tile, a.tpc_log2) : tile_at<V>(tile, a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(tile, a.tpc_log2) : tile_floor<V>(tile, a.M, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const uint64_t b0 = a.bnd[c];
@@ -1304,21 +1365,32 @@ __device__ __forceinline__ void ring_ag_tile(const GatArgs& a, uint64_t tile, in
       for (int q = 0; q < k; ++q) stg(a.rb + (uint64_t)modN(first_dst + q, N) * a.rs + e * SZ, w);
     }
   } else {
-    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const int c = (int)chunk_of(a.M, N, e);
-      const bool from_send = a.mode == 1 && s0 == 0;
-      const int holder = a.mode == 0 ? modN(c - 1 + s0, N) : wrapN(c + s0, N);
-      const char* src = from_send ? a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ
-                                  : a.rb + (uint64_t)holder * a.rs + e * SZ;
-      if constexpr (SZ == 2) {
-        const uint16_t v = *(const uint16_t*)src;
-        if (from_send) *(uint16_t*)(a.rb + (uint64_t)c * a.rs + e * SZ) = v;
-        for (int q = 0; q < k; ++q) *(uint16_t*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v;
-      } else {
-        const uint32_t v = *(const uint32_t*)src;
-        if (from_send) *(uint32_t*)(a.rb + (uint64_t)c * a.rs + e * SZ) = v;
-        for (int q = 0; q < k; ++q) *(uint32_t*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v;
-      }
+    // element-wise: a thread's V elements are loaded before any is stored
+    // (an idle slot loads the tile's first element and stores nothing)
+    typedef typename std::conditional<SZ == 2, uint16_t, uint32_t>::type W;
+    const bool from_send = a.mode == 1 && s0 == 0;
+    W v[V];
+    uint64_t ev[V];
+    int cv[V];
+    bool ok[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const uint64_t e = t.e0 + threadIdx.x + (uint64_t)u * kBlock;
+      ok[u] = e < t.e1;
+      ev[u] = ok[u] ? e : t.e0;
+      cv[u] = (int)chunk_of(a.M, N, ev[u]);
+      const int holder = a.mode == 0 ? modN(cv[u] - 1 + s0, N) : wrapN(cv[u] + s0, N);
+      const char* src = from_send ? a.sb + (uint64_t)cv[u] * a.ss + (ev[u] - a.bnd[cv[u]]) * SZ
+                                  : a.rb + (uint64_t)holder * a.rs + ev[u] * SZ;
+      v[u] = *(const W*)src;
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      if (!ok[u]) continue;
+      const uint64_t e = ev[u];
+      const int holder = a.mode == 0 ? modN(cv[u] - 1 + s0, N) : wrapN(cv[u] + s0, N);
+      if (from_send) *(W*)(a.rb + (uint64_t)cv[u] * a.rs + e * SZ) = v[u];
+      for (int q = 0; q < k; ++q) *(W*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v[u];
     }
   }
 }
@@ -1558,7 +1630,7 @@ template <int SZ>
 __global__ __launch_bounds__(kBlock) void k_hd_ag_step(GatArgs a) {
   constexpr int V = 16 / SZ;
   const int N = a.N, d = a.s0, first = a.k;  // s0 carries d, k carries "first"
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, N, a.vec_ok);
   if (t.fast) {
     const int c = (int)t.c;
     const uint64_t b0 = a.bnd[c];
@@ -1848,7 +1920,7 @@ __global__ __launch_bounds__(kBlock) void k_dequant_reduce(QArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   typedef typename QPack<V>::T QT;
   const int N = a.N;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, N, a.vec_ok);
   if (t.fast) {
     const uint64_t el = t.e0 + (uint64_t)threadIdx.x * V;
     const uint64_t sb = (el / kQBlock) * 4;
@@ -1899,7 +1971,7 @@ __global__ __launch_bounds__(kBlock) void k_quant_ef_fused(QArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   constexpr int B = 4;  // ranks loaded ahead of their compression
   const int N = a.N;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, N, a.vec_ok);
   if (t.fast) {
     const uint32_t lane = threadIdx.x;
     const uint64_t el = t.e0 + (uint64_t)lane * V;
@@ -2174,13 +2246,21 @@ hipError_t launch_dbt_fused(const Red& r) {
   while (nr < r.N) nr *= 2;
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+#define CC_DBT_CASE(NR)                                                                       \
+  case NR:                                                                                     \
+    if (r.N == NR)                                                                             \
+      hipLaunchKernelGGL((k_dbt_fused<DT, OP, NR, true>), grid, blk, lds, r.st, a);            \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_dbt_fused<DT, OP, NR, false>), grid, blk, lds, r.st, a);           \
+    break;
     switch (nr) {
-      case 2: hipLaunchKernelGGL((k_dbt_fused<DT, OP, 2>), grid, blk, lds, r.st, a); break;
-      case 4: hipLaunchKernelGGL((k_dbt_fused<DT, OP, 4>), grid, blk, lds, r.st, a); break;
-      case 8: hipLaunchKernelGGL((k_dbt_fused<DT, OP, 8>), grid, blk, lds, r.st, a); break;
-      case 16: hipLaunchKernelGGL((k_dbt_fused<DT, OP, 16>), grid, blk, lds, r.st, a); break;
+      CC_DBT_CASE(2)
+      CC_DBT_CASE(4)
+      CC_DBT_CASE(8)
+      CC_DBT_CASE(16)
       default: return hipErrorInvalidValue;
     }
+#undef CC_DBT_CASE
     return hipGetLastError();
   });
 }

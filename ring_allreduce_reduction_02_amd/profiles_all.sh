@@ -22,7 +22,7 @@ sec hier_2x2x2 "k_hier_fused<1, 0>" 4294967296 hier_fused_f32_2x2x2_m67108864 \
   "fused hierarchical AllReduce, grid 2x2x2 (N=8), M=67108864 fp32 per rank"
 sec hier_8x8 "k_hier_fused<1, 0>" 4294967296 hier_fused_f32_8x8_m8388608 \
   "fused hierarchical AllReduce, grid 8x8 (N=64), M=8388608 fp32 per rank"
-sec dbt_n8 "k_dbt_fused<1, 0, 8>" 4294967296 dbt_fused_f32_n8_m67108864 \
+sec dbt_n8 "k_dbt_fused<1, 0, 8, true>" 4294967296 dbt_fused_f32_n8_m67108864 \
   "fused double binary tree AllReduce, N=8, M=67108864 fp32 per rank"
 sec int8_ef_f32 "k_quant_ef_fused<1>" 8589934592 quant_ef_fused_f32_n8_m67108864 \
   "fused INT8 AllReduce with error feedback, N=8, M=67108864 fp32 gradients per rank"
