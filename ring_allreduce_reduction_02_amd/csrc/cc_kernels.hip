@@ -221,7 +221,31 @@ __device__ __forceinline__ uint32_t chunk_of(uint64_t M, int N, uint64_t e) {
   else if ((uint64_t)rem >= M) ++q;
   return q;
 }
+// The floor bound floor(c M / N) itself, for a per-element chunk c: c M is
+// exact in a double (c <= 64 and M below 2^41), the product with the
+// rounded reciprocal of N is within 2^-5 of c M / N, and one integer check
+// corrects the floor (no 64-bit division, and no load of the bound table
+// with a per-lane index, whose wait would come before the next load).
+__device__ __forceinline__ uint64_t bound_of(uint64_t M, int N, uint32_t c) {
+  const uint64_t x = (uint64_t)c * M;
+  uint64_t q = (uint64_t)((double)x * (1.0 / (double)N));
+  if (q * (uint64_t)N > x) --q;
+  else if ((q + 1) * (uint64_t)N <= x) ++q;
+  return q;
+}
 __device__ __forceinline__ int wrapN(int r, int N) { return r >= N ? r - N : r; }
+// Elements per batch in the element-wise paths: the batch's loads are all in
+// flight together, and four slots keep the registers of a bf16 thread (eight
+// elements) near those of an fp32 one.
+constexpr int kElemBatch = 4;
+// Slots per batch for a fold over NR ranks (a runtime-N ring: four ranks at a
+// time): about 16 loads in flight, which fit the registers the compiler
+// allots; beyond that it issues a slot's loads one after another.
+template <int V, int NR>
+__device__ constexpr int elem_batch() {
+  const int g = 16 / (NR > 0 ? NR : 4);
+  return g < 1 ? 1 : (g > V ? V : (g > kElemBatch ? kElemBatch : g));
+}
 __device__ __forceinline__ int modN(int r, int N) { return ((r % N) + N) % N; }
 
 template <int V>
@@ -442,8 +466,9 @@ __device__ __forceinline__ void fold_vec(const char* s0, uint64_t ss, int N, int
   }
 }
 
-// The same fold for one element at byte offset `off` of every rank.
-template <int DT, int OP, int NR, int ALG>
+// The same fold for one element at byte offset `off` of every rank.  Trees:
+// FULL when every leaf is one rank (ts = {NR, 0}), which loads each once.
+template <int DT, int OP, int NR, int ALG, bool FULL = false>
 __device__ __forceinline__ typename Ty<DT>::A fold_elem(const char* sb, uint64_t ss, int N, int start,
                                                         uint64_t off, TreeShape ts = TreeShape{NR, 0}) {
   typedef typename Ty<DT>::A A;
@@ -456,14 +481,21 @@ __device__ __forceinline__ typename Ty<DT>::A fold_elem(const char* sb, uint64_t
         acc, 1, NR);
     return acc[0];
   } else if constexpr (ALG != ALG_RING) {
+    constexpr int TR = ALG == ALG_HD ? TREE_HD : TREE_BFLY;
     A acc[Ty<DT>::V];
-    tree_fold<DT, OP, NR, ALG == ALG_HD ? TREE_HD : TREE_BFLY, false>(
+    if constexpr (FULL) {
+      tree_fold<DT, OP, NR, TR, true>([&](int v, A* x) { x[0] = ld1<DT>(sb + (uint64_t)v * ss + off); }, acc, 1, NR);
+      return acc[0];
+    }
+    tree_fold<DT, OP, NR, TR, false>(
         [&](int v, A* x) {
-          if (v < ts.pairs)
-            x[0] = opf<DT, OP>(ld1<DT>(sb + (uint64_t)(2 * v) * ss + off),
-                               ld1<DT>(sb + (uint64_t)(2 * v + 1) * ss + off));
-          else
-            x[0] = ld1<DT>(sb + (uint64_t)(v + ts.pairs) * ss + off);
+          // both loads issued either way (the second repeats the first's
+          // address when leaf v is a single rank): straight-line code
+          const bool pr = v < ts.pairs;
+          const uint64_t r0 = pr ? (uint64_t)(2 * v) : (uint64_t)(v + ts.pairs);
+          const A xa = ld1<DT>(sb + r0 * ss + off);
+          const A xb = ld1<DT>(sb + (pr ? r0 + 1 : r0) * ss + off);
+          x[0] = pr ? opf<DT, OP>(xa, xb) : xa;
         },
         acc, 1, ts.leaves);
     return acc[0];
@@ -471,6 +503,44 @@ __device__ __forceinline__ typename Ty<DT>::A fold_elem(const char* sb, uint64_t
     A acc = ld1<DT>(sb + (uint64_t)start * ss + off);
     for (int j = 1; j < N; ++j) acc = opf<DT, OP>(ld1<DT>(sb + (uint64_t)wrapN(start + j, N) * ss + off), acc);
     return acc;
+  }
+}
+
+// The ring fold of one element in each of a thread's V slots (slot u: byte
+// offset off[u], chain from rank st[u]), in fold_elem's order, with the
+// slots' loads in flight together.  With a runtime N the chain goes four
+// ranks at a time; past the chain's end a slot reloads its first rank and a
+// select drops the value, so the code stays straight-line.
+template <int DT, int OP, int NR, int V>
+__device__ __forceinline__ void ring_fold_elems(const char* sb, uint64_t ss, int N, const int* st,
+                                                const uint64_t* off, typename Ty<DT>::A* acc) {
+  typedef typename Ty<DT>::A A;
+#pragma unroll
+  for (int u = 0; u < V; ++u) acc[u] = ld1<DT>(sb + (uint64_t)st[u] * ss + off[u]);
+  if constexpr (NR > 0) {
+#pragma unroll
+    for (int j = 1; j < NR; ++j) {
+      A x[V];
+#pragma unroll
+      for (int u = 0; u < V; ++u) x[u] = ld1<DT>(sb + (uint64_t)wrapN(st[u] + j, NR) * ss + off[u]);
+#pragma unroll
+      for (int u = 0; u < V; ++u) acc[u] = opf<DT, OP>(x[u], acc[u]);
+    }
+  } else {
+    for (int j = 1; j < N; j += 4) {
+      A x[4][V];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+          const int r = j + q < N ? wrapN(st[u] + j + q, N) : st[u];
+          x[q][u] = ld1<DT>(sb + (uint64_t)r * ss + off[u]);
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < V; ++u) acc[u] = j + q < N ? opf<DT, OP>(x[q][u], acc[u]) : acc[u];
+    }
   }
 }
 
@@ -538,22 +608,53 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       stg(a.rb + (uint64_t)c * a.rs + (t.e0 - a.bnd[c]) * SZ + lane, w);
     } else {
       char* d = a.rb + eb;
-      if constexpr (ALG == ALG_RING && NR > 0) {
+      if constexpr (NR > 0) {
+        if (N == NR) {  // the ring with NR > 0, a tree with every leaf slot used
 #pragma unroll
-        for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
+          for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
+        } else {
+          for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
+        }
       } else {
         for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
       }
     }
   } else {
-    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const uint32_t c = (tiling == 1 ? 0u : chunk_of(a.M, tiling, e));
-      const int start = (ALG == ALG_RING && a.rs_mode) ? wrapN((int)c + 1, N) : (int)c;
-      const A acc = fold_elem<DT, OP, NR, ALG>(a.sb, a.ss, N, start, e * SZ, ts);
-      if (a.rs_mode) {
-        st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, acc);
+    // Element-wise (a tile across chunk bounds, a ragged tail, unaligned
+    // buffers): the thread's V elements, kBlock apart, are folded in
+    // batches of G whose loads are in flight at once; an idle slot repeats
+    // the tile's first element and stores nothing.  A tree folds one element
+    // at a time (its fold already has NR loads in flight).
+    constexpr int G = ALG == ALG_RING ? elem_batch<V, NR>() : 1;
+    for (int g0 = 0; g0 < V; g0 += G) {
+      uint64_t ev[G], off[G];
+      uint32_t cv[G];
+      int st[G];
+      bool ok[G];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const uint64_t e = t.e0 + threadIdx.x + (uint64_t)(g0 + u) * kBlock;
+        ok[u] = e < t.e1;
+        ev[u] = ok[u] ? e : t.e0;
+        off[u] = ev[u] * SZ;
+        cv[u] = tiling == 1 ? 0u : chunk_of(a.M, tiling, ev[u]);
+        st[u] = (ALG == ALG_RING && a.rs_mode) ? wrapN((int)cv[u] + 1, N) : (int)cv[u];
+      }
+      A acc[G];
+      if constexpr (ALG == ALG_RING) {
+        ring_fold_elems<DT, OP, NR, G>(a.sb, a.ss, N, st, off, acc);
       } else {
-        for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, acc);
+#pragma unroll
+        for (int u = 0; u < G; ++u) acc[u] = fold_elem<DT, OP, NR, ALG>(a.sb, a.ss, N, st[u], off[u], ts);
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        if (!ok[u]) continue;
+        if (a.rs_mode) {
+          st1<DT>(a.rb + (uint64_t)cv[u] * a.rs + (ev[u] - bound_of(a.M, tiling, cv[u])) * SZ, acc[u]);
+        } else {
+          for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + off[u], acc[u]);
+        }
       }
     }
   }
@@ -1055,7 +1156,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_seg(SegArgs a) {
       uint32_t c = 0;
       for (int i = 1; i < N; ++i) c += bk[i] <= e ? 1u : 0u;
       const uint64_t off = (base + e) * SZ;
-      const A acc = fold_elem<DT, OP, NR, ALG>(a.sb, a.ss, N, (int)c, off);
+      const A acc = fold_elem<DT, OP, NR, ALG, true>(a.sb, a.ss, N, (int)c, off);  // bucket trees: every leaf one rank
       for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + off, acc);
     }
   }
@@ -1123,52 +1224,75 @@ __device__ __forceinline__ void ring_pass_tile(const PassArgs& a, uint64_t tile,
     }
   } else {
     // Element-wise (a tile across chunk boundaries, a ragged tail, unaligned
-    // buffers): a thread's V elements, kBlock apart, are all loaded before
-    // any is stored, so their memory latencies overlap; an idle slot loads
-    // the tile's first element and stores nothing.
-    A acc[V];
-    uint64_t ev[V];
-    uint32_t cv[V];
-    int sv[V];
-    bool ok[V];
+    // buffers): a thread's V elements, kBlock apart, go in batches of G
+    // whose loads are all issued before any is used, so their latencies
+    // overlap; an idle slot loads the tile's first element and stores
+    // nothing.
+    // Two slots per batch: the passes run at up to 16 workgroups per CU
+    // (eight waves per SIMD, 64 registers a lane), which four slots would
+    // exceed.  Tile-relative element offsets keep the per-slot state to two
+    // 32-bit words (offset, chain start); the chunk follows from the start.
+    constexpr int G = 2;
+    const char* const sb0 = a.sb + t.e0 * SZ;
+    char* const rb0 = a.rb + t.e0 * SZ;
+    char* const wb0 = a.wb + t.e0 * 4;
+    for (int g0 = 0; g0 < V; g0 += G) {
+      uint32_t lo[G];
+      int sv[G];
+      bool ok[G];
 #pragma unroll
-    for (int u = 0; u < V; ++u) {
-      const uint64_t e = t.e0 + threadIdx.x + (uint64_t)u * kBlock;
-      ok[u] = e < t.e1;
-      ev[u] = ok[u] ? e : t.e0;
-      cv[u] = chunk_of(a.M, N, ev[u]);
-      sv[u] = a.rs_mode ? wrapN((int)cv[u] + 1, N) : (int)cv[u];
-    }
-#pragma unroll
-    for (int u = 0; u < V; ++u) {
-      if (s0 == 0)
-        acc[u] = ld1<DT>(a.sb + (uint64_t)sv[u] * a.ss + ev[u] * SZ);
-      else if (a.pin_recv)
-        acc[u] = ld1<DT>(a.rb + (uint64_t)wrapN(sv[u] + s0, N) * a.rs + ev[u] * SZ);
-      else
-        acc[u] = ldw1<DT>(a.wb + ev[u] * 4);
-    }
-    for (int j = s0 + 1; j <= s0 + k; ++j) {
-      A x[V];
-#pragma unroll
-      for (int u = 0; u < V; ++u) x[u] = ld1<DT>(a.sb + (uint64_t)wrapN(sv[u] + j, N) * a.ss + ev[u] * SZ);
-#pragma unroll
-      for (int u = 0; u < V; ++u) acc[u] = opf<DT, OP>(x[u], acc[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < V; ++u) {
-      if (!ok[u]) continue;
-      const uint64_t e = ev[u];
-      if (fin) {
-        if (a.rs_mode)
-          st1<DT>(a.rb + (uint64_t)cv[u] * a.rs + (e - a.bnd[cv[u]]) * SZ, acc[u]);
-        else
-          st1<DT>(a.rb + (uint64_t)wrapN(sv[u] + N - 1, N) * a.rs + e * SZ, acc[u]);
-      } else if (a.pin_recv) {
-        st1<DT>(a.rb + (uint64_t)wrapN(sv[u] + s0 + k, N) * a.rs + e * SZ, acc[u]);
-      } else {
-        stw1<DT>(a.wb + e * 4, acc[u]);
+      for (int u = 0; u < G; ++u) {
+        const uint32_t l = threadIdx.x + (uint32_t)(g0 + u) * kBlock;
+        ok[u] = t.e0 + l < t.e1;
+        lo[u] = ok[u] ? l : 0u;
+        const int c = (int)chunk_of(a.M, N, t.e0 + lo[u]);
+        sv[u] = a.rs_mode ? wrapN(c + 1, N) : c;
       }
+      // The running partial's source is the same for the whole pass, so
+      // each source gets the whole body as straight-line code: a per-slot
+      // choice of load would make each loaded register a join of values,
+      // and the copy into it would wait for the load before the next one
+      // issues.
+      auto body = [&](auto first) {
+        A acc[G], x1[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u) acc[u] = first(u);
+        // the pass's first step (k >= 1) in the same straight-line block, so
+        // its loads are issued beside the partial's
+#pragma unroll
+        for (int u = 0; u < G; ++u) x1[u] = ld1<DT>(sb0 + (uint64_t)wrapN(sv[u] + s0 + 1, N) * a.ss + lo[u] * SZ);
+#pragma unroll
+        for (int u = 0; u < G; ++u) acc[u] = opf<DT, OP>(x1[u], acc[u]);
+        for (int j = s0 + 2; j <= s0 + k; ++j) {
+          A x[G];
+#pragma unroll
+          for (int u = 0; u < G; ++u) x[u] = ld1<DT>(sb0 + (uint64_t)wrapN(sv[u] + j, N) * a.ss + lo[u] * SZ);
+#pragma unroll
+          for (int u = 0; u < G; ++u) acc[u] = opf<DT, OP>(x[u], acc[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+          if (!ok[u]) continue;
+          if (fin) {
+            if (a.rs_mode) {
+              const uint32_t c = (uint32_t)(sv[u] == 0 ? N - 1 : sv[u] - 1);
+              st1<DT>(a.rb + (uint64_t)c * a.rs + (t.e0 + lo[u] - bound_of(a.M, N, c)) * SZ, acc[u]);
+            } else {
+              st1<DT>(rb0 + (uint64_t)wrapN(sv[u] + N - 1, N) * a.rs + lo[u] * SZ, acc[u]);
+            }
+          } else if (a.pin_recv) {
+            st1<DT>(rb0 + (uint64_t)wrapN(sv[u] + s0 + k, N) * a.rs + lo[u] * SZ, acc[u]);
+          } else {
+            stw1<DT>(wb0 + lo[u] * 4, acc[u]);
+          }
+        }
+      };
+      if (s0 == 0)
+        body([&](int u) { return ld1<DT>(sb0 + (uint64_t)sv[u] * a.ss + lo[u] * SZ); });
+      else if (a.pin_recv)
+        body([&](int u) { return ld1<DT>(rb0 + (uint64_t)wrapN(sv[u] + s0, N) * a.rs + lo[u] * SZ); });
+      else
+        body([&](int u) { return ldw1<DT>(wb0 + lo[u] * 4); });
     }
   }
 }
@@ -1266,7 +1390,7 @@ __global__ __launch_bounds__(kBlock) void k_hd_rs_step(StepArgs a) {
         const int i = base | m, p = i ^ d;
         A v = opf<DT, OP>(step_load1<DT>(a, p, e), step_load1<DT>(a, i, e));
         if (a.last) {
-          if (a.rs_mode) st1<DT>(a.rb + (uint64_t)c * a.rs + (e - a.bnd[c]) * SZ, v);
+          if (a.rs_mode) st1<DT>(a.rb + (uint64_t)c * a.rs + (e - bound_of(a.M, N, c)) * SZ, v);
           else st1<DT>(a.rb + (uint64_t)c * a.rs + e * SZ, v);
         } else {
           step_store1<DT>(a, i, e, v);
@@ -1367,11 +1491,13 @@ __device__ __forceinline__ void ring_ag_tile(const GatArgs& a, uint64_t tile, in
   } else {
     // element-wise: a thread's V elements are loaded before any is stored
     // (an idle slot loads the tile's first element and stores nothing)
+    // (the chunk's start comes from its closed form: a per-lane read of the
+    // bound table would be a load whose wait precedes the element's load)
     typedef typename std::conditional<SZ == 2, uint16_t, uint32_t>::type W;
     const bool from_send = a.mode == 1 && s0 == 0;
     W v[V];
     uint64_t ev[V];
-    int cv[V];
+    int cv[V], hv[V];
     bool ok[V];
 #pragma unroll
     for (int u = 0; u < V; ++u) {
@@ -1379,18 +1505,18 @@ __device__ __forceinline__ void ring_ag_tile(const GatArgs& a, uint64_t tile, in
       ok[u] = e < t.e1;
       ev[u] = ok[u] ? e : t.e0;
       cv[u] = (int)chunk_of(a.M, N, ev[u]);
-      const int holder = a.mode == 0 ? modN(cv[u] - 1 + s0, N) : wrapN(cv[u] + s0, N);
-      const char* src = from_send ? a.sb + (uint64_t)cv[u] * a.ss + (ev[u] - a.bnd[cv[u]]) * SZ
-                                  : a.rb + (uint64_t)holder * a.rs + ev[u] * SZ;
+      const int h = cv[u] - 1 + s0;  // in [-1, 2N - 2]
+      hv[u] = a.mode == 0 ? (h < 0 ? h + N : wrapN(h, N)) : wrapN(cv[u] + s0, N);
+      const char* src = from_send ? a.sb + (uint64_t)cv[u] * a.ss + (ev[u] - bound_of(a.M, N, (uint32_t)cv[u])) * SZ
+                                  : a.rb + (uint64_t)hv[u] * a.rs + ev[u] * SZ;
       v[u] = *(const W*)src;
     }
 #pragma unroll
     for (int u = 0; u < V; ++u) {
       if (!ok[u]) continue;
       const uint64_t e = ev[u];
-      const int holder = a.mode == 0 ? modN(cv[u] - 1 + s0, N) : wrapN(cv[u] + s0, N);
       if (from_send) *(W*)(a.rb + (uint64_t)cv[u] * a.rs + e * SZ) = v[u];
-      for (int q = 0; q < k; ++q) *(W*)(a.rb + (uint64_t)modN(holder + 1 + q, N) * a.rs + e * SZ) = v[u];
+      for (int q = 0; q < k; ++q) *(W*)(a.rb + (uint64_t)wrapN(hv[u] + 1 + q, N) * a.rs + e * SZ) = v[u];
     }
   }
 }
@@ -1655,7 +1781,7 @@ __global__ __launch_bounds__(kBlock) void k_hd_ag_step(GatArgs a) {
       const int c = (int)chunk_of(a.M, N, e);
       const int base = (c ^ d) & ~(d - 1);
       if (a.mode == 1 && first) {
-        const char* src = a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ;
+        const char* src = a.sb + (uint64_t)c * a.ss + (e - bound_of(a.M, N, (uint32_t)c)) * SZ;
         for (int q = 0; q < 2; ++q) {
           char* dst = a.rb + (uint64_t)(q ? (c ^ 1) : c) * a.rs + e * SZ;
           if constexpr (SZ == 2) *(uint16_t*)dst = *(const uint16_t*)src;
@@ -2397,6 +2523,7 @@ hipError_t launch_gsteps(const Red& r, const GDesc* d, int n) {
 }
 
 hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv) {
+  if (k < 1 || s0 < 0 || s0 + k > r.N - 1) return hipErrorInvalidValue;  // a pass folds at least one step
   PassArgs a;
   a.sb = r.send.base; a.ss = r.send.stride;
   a.rb = r.recv.base; a.rs = r.recv.stride;
@@ -2417,6 +2544,7 @@ hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv)
 constexpr int kQueueBlocksPerCu = 4;
 
 hipError_t launch_ring_queue(const Red& r, int k, unsigned* bar) {
+  if (k < 1 || r.N < 2) return hipErrorInvalidValue;  // every pass folds at least one step
   QueueArgs a;
   PassArgs& p = a.p;
   p.sb = r.send.base; p.ss = r.send.stride;
