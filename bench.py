@@ -180,7 +180,7 @@ def cpu_baseline(N, M_sample, min_seconds=10.0, max_runs=25):
     }
 
 
-def pad_sweep(src, N, M, dev, pads=(0, 256, 4096, 65_792), steps=10):
+def pad_sweep(src, N, M, dev, pads=(0, 65_792, 262_144, 2_097_152), steps=10):
     """The headline AllReduce with rank buffers `pad` bytes apart beyond the
     payload (same data, copied on the device)."""
     import torch
@@ -213,7 +213,7 @@ def _time_gpu(fn, reps, per):
         return r["total_ms"] / (reps * per), "eager"
 
 
-def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30, pad_bytes=65_792):
+def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30, pad_bytes=262_144):
     """Stepwise ring AllReduce (fp32 SUM) at N = 4, 8, 16 over per-rank sizes
     4 KiB .. 1 GiB (x4), GPU time from HIP-graph replays, in two variants:
     one kernel per ring step, and all steps in one cooperative launch with a
@@ -232,8 +232,8 @@ def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30, pad_bytes=65_792):
            "per_n": {}}
     glob = {"kernel_per_step": ([], [], []), "grid_barrier": ([], [], [])}
     for N in ranks:
-        # rank rows padded like the headline's (64 KiB + 256 B): a stride of
-        # exactly 1 GiB puts every rank's same offset on the same HBM channels
+        # rank rows padded like the headline's: a stride of exactly 1 GiB
+        # puts every rank's same offset on the same HBM channels
         send = rank_tensor(N, sizes[-1], torch.float32, pad_bytes, dev)
         send.copy_(torch.randn(N, sizes[-1], generator=gen, device=dev) * 1e-3)
         recv = rank_tensor(N, sizes[-1], torch.float32, pad_bytes, dev)
@@ -726,7 +726,7 @@ def main():
     ap.add_argument("--dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--algo", default="ring", choices=["ring", "hd", "butterfly"])
     ap.add_argument("--fuse-depth", type=int, default=0)
-    ap.add_argument("--pad-bytes", type=int, default=65_792)
+    ap.add_argument("--pad-bytes", type=int, default=262_144)
     ap.add_argument("--blocks-per-cu", type=int, default=0, help="occupancy cap passed to the library (0 = its default)")
     ap.add_argument("--cpu-sample", type=int, default=67_108_864)
     ap.add_argument("--no-cpu-baseline", action="store_true")
