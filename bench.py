@@ -49,6 +49,16 @@ def rank_tensor(N, M, dtype, pad_bytes, device):
     return torch.empty(N * S, dtype=dtype, device=device).view(N, S)[:, :M]
 
 
+def randn_ranks(N, M, gen, device, pad_bytes):
+    """N x M fp32 Gaussian (sigma 1e-3) rank rows, M*4 + pad_bytes apart."""
+    import torch
+    # sampled in place: a torch copy here would share its kernel with the
+    # copy probe whose counters scale the profiles' HBM traffic
+    t = rank_tensor(N, M, torch.float32, pad_bytes, device)
+    t.normal_(0.0, 1e-3, generator=gen)
+    return t
+
+
 def upload(xs, t):
     import numpy as np
     import torch
@@ -278,7 +288,7 @@ def _avg_ms(fn, steps=10, warmup=3):
     return r["total_ms"] / steps
 
 
-def schedules(dev):
+def schedules(dev, pad_bytes=262_144):
     """Every AllReduce schedule on one GPU: fused throughput at the headline
     size (N = 8, 67,108,864 fp32 per rank; N = 12 for the pair-folded
     halving-doubling and butterfly), and the stepwise schedules over per-rank
@@ -291,8 +301,9 @@ def schedules(dev):
     out = {"fused": {}, "stepwise_n8": {}}
     gen = torch.Generator(device=dev).manual_seed(20261202)
     N, M = 8, 1 << 26
-    send = torch.randn(N, M, generator=gen, device=dev) * 1e-3
-    recv = torch.empty_like(send)
+    # the headline's layout: 256 MiB rows, `pad_bytes` apart
+    send = randn_ranks(N, M, gen, dev, pad_bytes)
+    recv = rank_tensor(N, M, torch.float32, pad_bytes, dev)
     for algo in ("ring", "hd", "butterfly", "tree", "double_tree", "ring_2port"):
         ms = _avg_ms(lambda: ccgpu.all_reduce(send, recv, algo=algo), 10, 3)
         out["fused"][f"{algo}_n8"] = {"ms": round(ms, 4), "GBps": round(2 * N * M * 4 / ms / 1e6, 1)}
@@ -308,8 +319,8 @@ def schedules(dev):
     torch.cuda.empty_cache()
 
     sizes = [1 << k for k in range(10, 25, 2)]          # 1 Ki .. 16 Mi fp32 = 4 KiB .. 64 MiB per rank
-    send = torch.randn(N, sizes[-1], generator=gen, device=dev) * 1e-3
-    recv = torch.empty_like(send)
+    send = randn_ranks(N, sizes[-1], gen, dev, pad_bytes)
+    recv = rank_tensor(N, sizes[-1], torch.float32, pad_bytes, dev)
     for _ in range(10):
         ccgpu.all_reduce(send, recv)
     torch.cuda.synchronize()
@@ -340,7 +351,7 @@ def schedules(dev):
     return out
 
 
-def hierarchical(dev):
+def hierarchical(dev, pad_bytes=262_144):
     """Hierarchical AllReduce on one GPU: fused throughput of two- and
     three-level rank grids against the flat ring at the same N (8 ranks of
     67,108,864 fp32; 64 ranks of 8,388,608), the stepwise form against the
@@ -353,9 +364,12 @@ def hierarchical(dev):
     from ring_allreduce_reduction_02_amd import calib, ccgpu
     out = {"fused": {}, "stepwise": {}, "level_traffic": {}, "two_tier_model": {}}
     gen = torch.Generator(device=dev).manual_seed(20261203)
+    # 8 ranks of 256 MiB in the headline's layout; 64 ranks of 32 MiB
+    # unpadded (a 256 KiB pad aliases at 64 ranks: 4.0 against 5.7 TB/s)
     for N, M, grids in ((8, 1 << 26, [(8,), (4, 2), (2, 4), (2, 2, 2)]), (64, 1 << 23, [(64,), (8, 8), (4, 4, 4)])):
-        send = torch.randn(N, M, generator=gen, device=dev) * 1e-3
-        recv = torch.empty_like(send)
+        pad = pad_bytes if N == 8 else 0
+        send = randn_ranks(N, M, gen, dev, pad)
+        recv = rank_tensor(N, M, torch.float32, pad, dev)
         for dims in grids:
             if len(dims) == 1:
                 fn = lambda: ccgpu.all_reduce(send, recv, algo="ring")
@@ -662,7 +676,7 @@ def workloads(dev):
     return out
 
 
-def profile_section(name, dev, steps, warmup):
+def profile_section(name, dev, steps, warmup, pad_bytes=262_144):
     """Run one kernel of the next-row schedules `steps` times (after `warmup`)
     for rocprofv3, and return its algorithmic bytes per call: the kernel's
     HBM reads and writes by the schedule's definition."""
@@ -673,10 +687,11 @@ def profile_section(name, dev, steps, warmup):
     gen = torch.Generator(device=dev).manual_seed(20261206)
     N, M = 8, 1 << 26
     if name in ("hier_2x2x2", "dbt_n8", "hier_8x8"):
+        pad = pad_bytes
         if name == "hier_8x8":
-            N, M = 64, 1 << 23
-        x = torch.randn(N, M, generator=gen, device=dev) * 1e-3
-        y = torch.empty_like(x)
+            N, M, pad = 64, 1 << 23, 0   # 64 ranks of 32 MiB stream best unpadded
+        x = randn_ranks(N, M, gen, dev, pad)
+        y = rank_tensor(N, M, torch.float32, pad, dev)
         if name == "dbt_n8":
             fn = lambda: ccgpu.all_reduce(x, y, algo="double_tree")
         else:
@@ -764,7 +779,7 @@ def main():
                 b.copy_(a)
             torch.cuda.synchronize()
             del a, b
-        nbytes = profile_section(args.profile_section, dev, args.steps, args.warmup)
+        nbytes = profile_section(args.profile_section, dev, args.steps, args.warmup, args.pad_bytes)
         print(json.dumps({"profile_section": args.profile_section, "alg_bytes_per_call": nbytes}), flush=True)
         return
     N, M = args.ranks, args.count
@@ -870,9 +885,9 @@ def main():
         log("other workloads")
         out["workloads"] = workloads(dev)
         log("schedules")
-        out["schedules"] = schedules(dev)
+        out["schedules"] = schedules(dev, args.pad_bytes)
         log("hierarchical")
-        out["hierarchical"] = hierarchical(dev)
+        out["hierarchical"] = hierarchical(dev, args.pad_bytes)
         log("alltoall variants")
         out["alltoall_variants"] = alltoall_variants(dev)
         log("int8 error feedback")
