@@ -2273,10 +2273,15 @@ hipError_t launch_ring_fused(const Red& r) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
   const bool runtime_n = r.N != 2 && r.N != 3 && r.N != 4 && r.N != 8 && r.N != 16;
+  // A bf16 lane unpacks, folds and rounds eight elements per 16-byte vector
+  // (fp32: four), so from 8 ranks on it wants more bytes in flight: at
+  // N = 8 (128 MiB rows) 6.43 TB/s with 3 workgroups per CU against
+  // 6.19-6.21 at the byte rule's 2; at N = 16 the rule's 2 stays best.
+  const uint64_t target = (r.dt == DT_BF16 && r.N >= 8) ? kBalancedTarget * 3 / 2 : kBalancedTarget;
   const unsigned lds =
       r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
       : runtime_n ? lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu : batched_ring_blocks_per_cu(r.N))
-                  : occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
+                  : occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, target, 2);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     switch (r.N) {
