@@ -1,21 +1,23 @@
 #!/bin/bash
 # Regenerates every summary under profiles/ from the rocprofv3 output
-# directories that the commands named in each summary write under
-# gpurun_out/ (trace: prof_trace, ps_<section>_trace; counters: *_fetch,
-# *_write).  Run from the repository root after those commands.
+# directories that the commands named in each summary write under rocprof/
+# (trace: prof_trace, ps_<section>_trace; counters: *_fetch, *_write).  Run
+# from the repository root after those commands; the first argument, if
+# any, is where those directories are now (default: rocprof).
 set -e
+ROOT="${1:-rocprof}"
 sum() {  # section dir prefix, kernel, algorithmic bytes per launch, output, workload, trace cmd args
-  python -m ring_allreduce_reduction_02_amd.profsum --trace "gpurun_out/$1_trace" --fetch "gpurun_out/$1_fetch" \
-    --write "gpurun_out/$1_write" --kernel "$2" --copy-bytes 1073741824 --alg-bytes "$3" --out "profiles/$4" \
+  python -m ring_allreduce_reduction_02_amd.profsum --trace "$ROOT/$1_trace" --fetch "$ROOT/$1_fetch" \
+    --write "$ROOT/$1_write" --kernel "$2" --copy-bytes 1073741824 --alg-bytes "$3" --out "profiles/$4" \
     --workload "$5" --trace-command "$6" --pmc-command "$7" > /dev/null
 }
-T="rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o ring -- python3 bench.py --steps 30 --warmup 5 --no-extras --no-cpu-baseline"
-P="rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o ring -- python3 bench.py --steps 5 --warmup 1 --no-extras --no-cpu-baseline --copy-probe-bytes 1073741824"
+T="rocprofv3 --kernel-trace --stats -f csv -d rocprof/prof_trace -o ring -- python3 bench.py --steps 30 --warmup 5 --no-extras --no-cpu-baseline"
+P="rocprofv3 --pmc FETCH_SIZE -f csv -d rocprof/prof_fetch -o ring -- python3 bench.py --steps 5 --warmup 1 --no-extras --no-cpu-baseline --copy-probe-bytes 1073741824"
 sum prof "k_ring_fused<1, 0, 8>" 4294967296 ring_fused_f32_n8_m67108864 \
   "fused ring AllReduce, N=8 logical ranks, M=67108864 fp32 per rank" "$T" "$P"
 sec() {  # section, kernel, bytes, output, workload
-  local t="rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/ps_$1_trace -o k -- python3 bench.py --profile-section $1 --steps 20 --warmup 2"
-  local p="rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/ps_$1_fetch -o k -- python3 bench.py --profile-section $1 --steps 5 --warmup 1 --copy-probe-bytes 1073741824"
+  local t="rocprofv3 --kernel-trace --stats -f csv -d rocprof/ps_$1_trace -o k -- python3 bench.py --profile-section $1 --steps 20 --warmup 2"
+  local p="rocprofv3 --pmc FETCH_SIZE -f csv -d rocprof/ps_$1_fetch -o k -- python3 bench.py --profile-section $1 --steps 5 --warmup 1 --copy-probe-bytes 1073741824"
   sum "ps_$1" "$2" "$3" "$4" "$5" "$t" "$p"
 }
 sec hier_2x2x2 "k_hier_fused<1, 0>" 4294967296 hier_fused_f32_2x2x2_m67108864 \

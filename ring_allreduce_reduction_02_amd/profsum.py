@@ -7,7 +7,7 @@ size that ran in the same process (the copy-probe kernel), because on this
 part FETCH_SIZE under-reports by a constant factor.
 
     python -m ring_allreduce_reduction_02_amd.profsum \\
-        --trace gpurun_out/prof_trace --fetch gpurun_out/prof_fetch --write gpurun_out/prof_write \\
+        --trace rocprof/prof_trace --fetch rocprof/prof_fetch --write rocprof/prof_write \\
         --kernel "k_ring_fused<1, 0, 8>" --copy-bytes 1073741824 --alg-bytes 4294967296 \\
         --out profiles/ring_fused_f32_n8_m67108864 --command "..."
 """
