@@ -2263,10 +2263,11 @@ unsigned occupancy_lds(int requested, uint64_t traffic, uint64_t target, int min
 // is, so the byte rule above undersizes them at small N.  Measured on the
 // MI355X (fused fp32 SUM, 2 GiB per buffer, 2 to 6 workgroups per CU): the
 // ring streams best with 4 up to N = 8, 3 up to 16 and 2 beyond; the
-// hierarchical kernel, whose per-leaf walk is longer, with 4 up to N = 8 and
-// 3 beyond.
+// hierarchical kernel, whose per-leaf walk is longer, with 3 (at 8 ranks in
+// rows 256 MiB + 256 KiB apart 6.26-6.30 TB/s against 6.15-6.17 at 4; in
+// unpadded rows 4 had been ahead by a few percent).
 int batched_ring_blocks_per_cu(int N) { return N <= 8 ? 4 : N <= 16 ? 3 : 2; }
-int hier_blocks_per_cu(int N) { return N <= 8 ? 4 : 3; }
+int hier_blocks_per_cu(int) { return 3; }
 }  // namespace
 
 hipError_t launch_ring_fused(const Red& r) {
