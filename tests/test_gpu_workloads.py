@@ -54,7 +54,8 @@ def test_gradient_ring_n8_full_size(dtype):
     N, M = 8, 67_108_864
     say(f"generating N={N} M={M} {dtype}")
     xs = synth.gradient_inputs(N, M, dtype)
-    pad = 16448 // (4 if dtype == "f32" else 2)      # 64 KiB + 256 B between ranks (bytes / elem)
+    # the layout bench.py times: rank rows 256 KiB beyond the payload apart
+    pad = 262_144 // (4 if dtype == "f32" else 2)
     send = upload(xs, dtype, pad=pad)
     recv = alloc_ranks(N, M, dtype, pad=pad)
     idx = sample_idx(M, N)
