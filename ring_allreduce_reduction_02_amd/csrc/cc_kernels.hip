@@ -2261,12 +2261,18 @@ unsigned occupancy_lds(int requested, uint64_t traffic, uint64_t target, int min
 // Fused AllReduce kernels with a runtime rank count keep one batch of leaf
 // loads in flight per thread (8, plus the first leaf for the ring) whatever N
 // is, so the byte rule above undersizes them at small N.  Measured on the
-// MI355X (fused fp32 SUM, 2 GiB per buffer, 2 to 6 workgroups per CU): the
-// ring streams best with 4 up to N = 8, 3 up to 16 and 2 beyond; the
-// hierarchical kernel, whose per-leaf walk is longer, with 3 (at 8 ranks in
-// rows 256 MiB + 256 KiB apart 6.26-6.30 TB/s against 6.15-6.17 at 4; in
-// unpadded rows 4 had been ahead by a few percent).
-int batched_ring_blocks_per_cu(int N) { return N <= 8 ? 4 : N <= 16 ? 3 : 2; }
+// MI355X (fused SUM, 2 GiB per buffer, 2 to 8 workgroups per CU): the fp32
+// ring streams best with 4 up to N = 8, 3 up to 16 and 2 beyond.  A bf16
+// lane also unpacks and rounds eight elements per vector and wants more
+// workgroups: 6 up to N = 6 (N = 5: 6.32 TB/s against 5.69 at 4), 4 up to 12
+// (N = 10: 5.92 against 5.50 at 3), 3 up to 16, 2 beyond.  The hierarchical
+// kernel, whose per-leaf walk is longer, takes 3 (at 8 ranks in rows
+// 256 MiB + 256 KiB apart 6.26-6.30 TB/s against 6.15-6.17 at 4; in unpadded
+// rows 4 had been ahead by a few percent).
+int batched_ring_blocks_per_cu(int N, int dt) {
+  if (dt == DT_BF16) return N <= 6 ? 6 : N <= 12 ? 4 : N <= 16 ? 3 : 2;
+  return N <= 8 ? 4 : N <= 16 ? 3 : 2;
+}
 int hier_blocks_per_cu(int) { return 3; }
 }  // namespace
 
@@ -2281,7 +2287,7 @@ hipError_t launch_ring_fused(const Red& r) {
   const uint64_t target = (r.dt == DT_BF16 && r.N >= 8) ? kBalancedTarget * 3 / 2 : kBalancedTarget;
   const unsigned lds =
       r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
-      : runtime_n ? lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu : batched_ring_blocks_per_cu(r.N))
+      : runtime_n ? lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu : batched_ring_blocks_per_cu(r.N, r.dt))
                   : occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, target, 2);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
