@@ -2276,19 +2276,36 @@ int batched_ring_blocks_per_cu(int N, int dt) {
 int hier_blocks_per_cu(int) { return 3; }
 }  // namespace
 
+// LDS reservation of a fused AllReduce that folds all N ranks of a tile and
+// stores N results (2N vector accesses per workgroup).  A bf16 lane unpacks,
+// folds and rounds eight elements per 16-byte vector (fp32: four), so from 8
+// ranks on it wants more bytes in flight: at N = 8 in rows 256 KiB beyond
+// the payload apart, 3 workgroups per CU against the byte rule's 2 took the
+// ring from 6.19-6.21 to 6.43 TB/s and the trees, double tree and 2-port
+// ring up 2.5-3.5% (halving-doubling 6.17 against 6.02); at N = 16 the rule
+// gives 2 either way.
+// (`blocks` > 0 overrides the choice.)
+static unsigned ar_fused_lds(const Red& r, int blocks) {
+  const uint64_t target = (r.dt == DT_BF16 && r.N >= 8) ? kBalancedTarget * 3 / 2 : kBalancedTarget;
+  return occupancy_lds(blocks, kVecBytes * 2 * r.N, target, 2);
+}
+
 hipError_t launch_ring_fused(const Red& r) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
   const bool runtime_n = r.N != 2 && r.N != 3 && r.N != 4 && r.N != 8 && r.N != 16;
-  // A bf16 lane unpacks, folds and rounds eight elements per 16-byte vector
-  // (fp32: four), so from 8 ranks on it wants more bytes in flight: at
-  // N = 8 (128 MiB rows) 6.43 TB/s with 3 workgroups per CU against
-  // 6.19-6.21 at the byte rule's 2; at N = 16 the rule's 2 stays best.
-  const uint64_t target = (r.dt == DT_BF16 && r.N >= 8) ? kBalancedTarget * 3 / 2 : kBalancedTarget;
+  // Two measured exceptions to the byte rule (2 GiB per buffer, rows 256 KiB
+  // beyond the payload apart): at N = 3, 8 workgroups per CU (6.44 fp32 and
+  // 6.45 bf16 TB/s against 6.12 and 6.01 at the rule's 5); at N = 2 in fp32,
+  // 6 (6.21-6.31 against 5.92-6.00 at the rule's 8; bf16 keeps 8).
+  const int ring_bpc = r.blocks_per_cu > 0 ? r.blocks_per_cu
+                       : r.N == 3                     ? 8
+                       : (r.N == 2 && r.dt != DT_BF16) ? 6
+                                                       : 0;
   const unsigned lds =
       r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
       : runtime_n ? lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu : batched_ring_blocks_per_cu(r.N, r.dt))
-                  : occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, target, 2);
+                  : ar_fused_lds(r, ring_bpc);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     switch (r.N) {
@@ -2307,7 +2324,7 @@ hipError_t launch_tree_fused(const Red& r, int tree) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
   const unsigned lds = r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
-                                 : occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
+                                 : ar_fused_lds(r, r.blocks_per_cu);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
 #define CC_TREE_CASE(NR)                                                                      \
@@ -2336,7 +2353,7 @@ hipError_t launch_tree_shaped(const Red& r, int tree, int nr, int leaves, int pa
   a.tree_leaves = leaves;
   a.tree_pairs = pairs;
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
+  const unsigned lds = ar_fused_lds(r, r.blocks_per_cu);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     if (tree == TREE_BFLY && pairs == 0 && leaves < nr && leaves <= 16) {
@@ -2379,7 +2396,7 @@ hipError_t launch_dbt_fused(const Red& r) {
   a.bnd[1] = r.M / 2;
   a.bnd[2] = r.M;
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
+  const unsigned lds = ar_fused_lds(r, r.blocks_per_cu);
   int nr = 2;
   while (nr < r.N) nr *= 2;
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
@@ -2406,7 +2423,7 @@ hipError_t launch_dbt_fused(const Red& r) {
 hipError_t launch_ring2_fused(const Red& r) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kBalancedTarget, 2);
+  const unsigned lds = ar_fused_lds(r, r.blocks_per_cu);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     switch (r.N) {
