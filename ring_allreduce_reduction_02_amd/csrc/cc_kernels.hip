@@ -2290,6 +2290,19 @@ static unsigned ar_fused_lds(const Red& r, int blocks) {
   return occupancy_lds(blocks, kVecBytes * 2 * r.N, target, 2);
 }
 
+// LDS reservation of a fused ReduceScatter (N loads, one store per tile; ring
+// and halving-doubling).  The read-heavy byte rule holds up to 5 ranks but
+// puts too many workgroups on a CU from 8 on.  Measured (2 GiB per buffer,
+// rows 256 KiB beyond the payload apart), fp32 ring: N = 8 6.63 TB/s at 4
+// against 6.44 at the rule's 8, N = 12 6.22 at 4 against 6.12 at 6, N = 16
+// 6.67 at 3 against 6.54 at 4, N = 32 6.65 at 3 against 6.20 at 2;
+// halving-doubling at N = 8: 6.56 (fp32) and 6.79 (bf16) at 4 against 6.25
+// and 6.38 at 8.
+static unsigned rs_fused_lds(const Red& r) {
+  const int b = r.blocks_per_cu > 0 ? r.blocks_per_cu : r.N < 8 ? 0 : r.N <= 12 ? 4 : 3;
+  return occupancy_lds(b, kVecBytes * (r.N + 1), kSkewedTarget);
+}
+
 hipError_t launch_ring_fused(const Red& r) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
@@ -2303,7 +2316,7 @@ hipError_t launch_ring_fused(const Red& r) {
                        : (r.N == 2 && r.dt != DT_BF16) ? 6
                                                        : 0;
   const unsigned lds =
-      r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
+      r.rs_mode ? rs_fused_lds(r)
       : runtime_n ? lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu : batched_ring_blocks_per_cu(r.N, r.dt))
                   : ar_fused_lds(r, ring_bpc);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
@@ -2323,8 +2336,7 @@ hipError_t launch_ring_fused(const Red& r) {
 hipError_t launch_tree_fused(const Red& r, int tree) {
   const FusedArgs a = fused_args(r);
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = r.rs_mode ? occupancy_lds(r.blocks_per_cu, kVecBytes * (r.N + 1), kSkewedTarget)
-                                 : ar_fused_lds(r, r.blocks_per_cu);
+  const unsigned lds = r.rs_mode ? rs_fused_lds(r) : ar_fused_lds(r, r.blocks_per_cu);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
 #define CC_TREE_CASE(NR)                                                                      \
@@ -2679,7 +2691,18 @@ hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k) {
   return hipGetLastError();
 }
 
-hipError_t launch_ag_fused(const Gat& g) { return launch_ring_ag_pass(g, 0, g.N - 1); }
+// The standalone AllGather (one load, N stores per tile) follows the
+// write-heavy byte rule, capped at 10 workgroups per CU: at 2 to 5 ranks the
+// rule's 12-16 overfill the write queues (fp32, 2 GiB per buffer: N = 4
+// 6.15 TB/s at 10 against 5.46 at the rule's 14; N = 2 6.30 against 5.82).
+hipError_t launch_ag_fused(const Gat& g) {
+  Gat c = g;
+  if (c.blocks_per_cu <= 0) {
+    const int b = default_blocks_per_cu(kVecBytes * (uint64_t)(g.N + 1), kSkewedTarget, 1);
+    c.blocks_per_cu = b > 10 ? 10 : b;
+  }
+  return launch_ring_ag_pass(c, 0, g.N - 1);
+}
 
 hipError_t launch_hd_ag_step(const Gat& g, int d, int first) {
   const GatArgs a = gat_args(g, d, first);
