@@ -2228,9 +2228,14 @@ unsigned lds_for_blocks_per_cu(int blocks) {
   if (blocks <= 0) return 0;
   const DevInfo i = dev_info();
   if (i.lds_per_cu <= 0 || i.lds_per_block <= 0) return 0;
-  // rounded down to 2 KiB so the allocation granularity cannot round it up
-  // past LDS/blocks (which would leave room for one workgroup fewer)
-  unsigned lds = (unsigned)(i.lds_per_cu / blocks) & ~2047u;
+  // Rounded down to the allocation granule, so that rounding up cannot push
+  // `blocks` reservations past the CU's LDS.  gfx950 hands out LDS in
+  // 1280-byte granules (160 KiB = 128 of them): measured with workgroups that
+  // record their CU and lifetime, 32 KiB reservations let only 4 share a CU
+  // (5 x 26 granules > 128) and 16 KiB only 9, while 30 KiB let 5 and 20 KiB
+  // let 8; every reservation tried from 14 to 80 KiB matched that count.
+  constexpr unsigned kLdsGranule = 1280;
+  unsigned lds = (unsigned)(i.lds_per_cu / blocks) / kLdsGranule * kLdsGranule;
   if (lds > (unsigned)i.lds_per_block) lds = (unsigned)i.lds_per_block;
   return lds;
 }
@@ -2309,7 +2314,7 @@ hipError_t launch_ring_fused(const Red& r) {
   const bool runtime_n = r.N != 2 && r.N != 3 && r.N != 4 && r.N != 8 && r.N != 16;
   // Two measured exceptions to the byte rule (2 GiB per buffer, rows 256 KiB
   // beyond the payload apart): at N = 3, 8 workgroups per CU (6.44 fp32 and
-  // 6.45 bf16 TB/s against 6.12 and 6.01 at the rule's 5); at N = 2 in fp32,
+  // 6.45 bf16 TB/s against 6.12 and 6.01 at 4); at N = 2 in fp32,
   // 6 (6.21-6.31 against 5.92-6.00 at the rule's 8; bf16 keeps 8).
   const int ring_bpc = r.blocks_per_cu > 0 ? r.blocks_per_cu
                        : r.N == 3                     ? 8
@@ -2692,14 +2697,16 @@ hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k) {
 }
 
 // The standalone AllGather (one load, N stores per tile) follows the
-// write-heavy byte rule, capped at 10 workgroups per CU: at 2 to 5 ranks the
-// rule's 12-16 overfill the write queues (fp32, 2 GiB per buffer: N = 4
-// 6.15 TB/s at 10 against 5.46 at the rule's 14; N = 2 6.30 against 5.82).
+// write-heavy byte rule, capped at 10 workgroups per CU below 6 ranks and at
+// 8 from 6 on: the rule's 11-16 overfill the write queues (fp32, 2 GiB per
+// buffer: N = 4 6.35 TB/s at 10 against 5.46 at the rule's 14; N = 2 6.44
+// against 5.82 at 16; N = 6 6.28 at 8 against 5.91 at 10).
 hipError_t launch_ag_fused(const Gat& g) {
   Gat c = g;
   if (c.blocks_per_cu <= 0) {
     const int b = default_blocks_per_cu(kVecBytes * (uint64_t)(g.N + 1), kSkewedTarget, 1);
-    c.blocks_per_cu = b > 10 ? 10 : b;
+    const int cap = g.N < 6 ? 10 : 8;
+    c.blocks_per_cu = b > cap ? cap : b;
   }
   return launch_ring_ag_pass(c, 0, g.N - 1);
 }
