@@ -2203,6 +2203,7 @@ FusedArgs fused_args(const Red& r) {
 struct DevInfo {
   int lds_per_cu = 0;
   int lds_per_block = 0;
+  int cus = 0;
 };
 
 DevInfo dev_info() {
@@ -2216,6 +2217,7 @@ DevInfo dev_info() {
       i.lds_per_cu = 0;
     if (hipDeviceGetAttribute(&i.lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, d) != hipSuccess)
       i.lds_per_block = 0;
+    if (hipDeviceGetAttribute(&i.cus, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) i.cus = 0;
     cache[d] = i;
     have[d] = true;
   }
@@ -2279,6 +2281,20 @@ int batched_ring_blocks_per_cu(int N, int dt) {
   return N <= 8 ? 4 : N <= 16 ? 3 : 2;
 }
 int hier_blocks_per_cu(int) { return 3; }
+
+// A fused AllReduce grid small enough to be resident all at once (at most 16
+// workgroups per CU) runs best that way: its loads all issue in the first
+// round instead of waiting for a second.  Raises `blocks` to the workgroups
+// per CU that hold the whole grid.  Measured on the int32 ring at N = 4,
+// 1,048,576 elements (2,048 tiles, graph replays): 6.75 us at 8 per CU
+// against 7.35 at the byte rule's 4 with the buffers cache-resident, 8.32
+// against 8.43 from HBM.
+int one_round_blocks(uint64_t tiles, int blocks) {
+  const int cus = dev_info().cus;
+  if (cus <= 0 || tiles > 16ull * (uint64_t)cus) return blocks;
+  const int need = (int)((tiles + cus - 1) / cus);
+  return need > blocks ? need : blocks;
+}
 }  // namespace
 
 // LDS reservation of a fused AllReduce that folds all N ranks of a tile and
@@ -2291,8 +2307,11 @@ int hier_blocks_per_cu(int) { return 3; }
 // gives 2 either way.
 // (`blocks` > 0 overrides the choice.)
 static unsigned ar_fused_lds(const Red& r, int blocks) {
-  const uint64_t target = (r.dt == DT_BF16 && r.N >= 8) ? kBalancedTarget * 3 / 2 : kBalancedTarget;
-  return occupancy_lds(blocks, kVecBytes * 2 * r.N, target, 2);
+  if (blocks <= 0) {
+    const uint64_t target = (r.dt == DT_BF16 && r.N >= 8) ? kBalancedTarget * 3 / 2 : kBalancedTarget;
+    blocks = one_round_blocks(num_tiles(r.M, r.dt), default_blocks_per_cu(kVecBytes * 2 * r.N, target, 2));
+  }
+  return lds_for_blocks_per_cu(blocks);
 }
 
 // LDS reservation of a fused ReduceScatter (N loads, one store per tile; ring
@@ -2322,7 +2341,9 @@ hipError_t launch_ring_fused(const Red& r) {
                                                        : 0;
   const unsigned lds =
       r.rs_mode ? rs_fused_lds(r)
-      : runtime_n ? lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu : batched_ring_blocks_per_cu(r.N, r.dt))
+      : runtime_n ? lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu
+                                                              : one_round_blocks(num_tiles(r.M, r.dt),
+                                                                                 batched_ring_blocks_per_cu(r.N, r.dt)))
                   : ar_fused_lds(r, ring_bpc);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
