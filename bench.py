@@ -42,6 +42,24 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def rank_stride_bytes(row_bytes):
+    """Rank stride for rows of row_bytes: the payload rounded up to a power of
+    two P, plus max(256 KiB, P/1024) (equal offsets of the ranks then spread
+    over the HBM channels)."""
+    p = 1
+    while p < row_bytes:
+        p *= 2
+    return p + max(262_144, p // 1024)
+
+
+def strided_ranks(N, L, dtype, device):
+    """N x L rank rows, rank_stride_bytes(L * element size) apart."""
+    import torch
+    es = torch.tensor([], dtype=dtype).element_size()
+    S = rank_stride_bytes(L * es) // es
+    return torch.empty(N * S, dtype=dtype, device=device).view(N, S)[:, :L]
+
+
 def rank_tensor(N, M, dtype, pad_bytes, device):
     import torch
     es = torch.tensor([], dtype=dtype).element_size()
@@ -626,10 +644,12 @@ def workloads(dev):
     sizes = synth.tensor_sizes_log_uniform()
     _, _, boff, bcnt = ccgpu.bucket_plan(sizes, 2, 25 * 1024 * 1024, 128)
     extent = boff[-1] + bcnt[-1]
-    send = (torch.randn(N, extent, generator=gen, device=dev) * 1e-2).to(torch.bfloat16)
-    recv = torch.empty_like(send)
+    send = strided_ranks(N, extent, torch.bfloat16, dev)
+    send.copy_((torch.randn(N, extent, generator=gen, device=dev) * 1e-2).to(torch.bfloat16))
+    recv = strided_ranks(N, extent, torch.bfloat16, dev)
     alg = 2 * N * sum(bcnt) * 2
-    b = {"tensors": len(sizes), "buckets": len(boff), "elements_per_rank": sum(bcnt)}
+    b = {"tensors": len(sizes), "buckets": len(boff), "elements_per_rank": sum(bcnt),
+         "rank_stride_bytes": rank_stride_bytes(extent * 2)}
     for algo in ("ring", "hd", "butterfly"):
         ms = _avg_ms(lambda: ccgpu.all_reduce_buckets(send, recv, boff, bcnt, algo=algo))
         b[algo] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1),
@@ -643,11 +663,12 @@ def workloads(dev):
     # ZeRO-3 style standalone ReduceScatter then AllGather, N=16, M=33,554,432 fp32
     N, M = 16, 1 << 25
     S = M // N
-    send = torch.rand(N, M, generator=gen, device=dev) * 2 - 1
-    shard = torch.empty(N, S, device=dev)
-    full = torch.empty(N, M, device=dev)
+    send = strided_ranks(N, M, torch.float32, dev)
+    send.uniform_(-1.0, 1.0, generator=gen)
+    shard = strided_ranks(N, S, torch.float32, dev)
+    full = strided_ranks(N, M, torch.float32, dev)
     alg = (N + 1) * M * 4
-    z = {}
+    z = {"rank_stride_bytes": [rank_stride_bytes(M * 4), rank_stride_bytes(S * 4)]}
     for algo in ("ring", "hd"):
         ms = _avg_ms(lambda: ccgpu.reduce_scatter(send, shard, algo=algo))
         z[f"reduce_scatter_{algo}"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
