@@ -44,12 +44,12 @@ def kernel_source_hash() -> str:
 
 def rank_stride_bytes(row_bytes):
     """Rank stride for rows of row_bytes: the payload rounded up to a power of
-    two P, plus max(256 KiB, P/1024) (equal offsets of the ranks then spread
+    two P, plus max(32 KiB, P/1024) (equal offsets of the ranks then spread
     over the HBM channels)."""
-    p = 1
+    p = 256
     while p < row_bytes:
         p *= 2
-    return p + max(262_144, p // 1024)
+    return p + max(32_768, p // 1024)
 
 
 def strided_ranks(N, L, dtype, device):

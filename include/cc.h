@@ -147,10 +147,12 @@ typedef struct {
  * Any stride at least the payload works (unaligned ones take the element-wise
  * path).  On MI355X the stride also sets how the ranks' equal offsets spread
  * over the HBM channels.  Rows a multiple of 2 MiB or of 512 MiB apart can
- * land on the same channels and lose up to a quarter of the bandwidth.  A
- * stride of P + max(256 KiB, P / 1024), P the payload rounded up to a power of
- * two, measured best or within noise of it in every case tried: 8 ranks of
- * 256 MiB (256 MiB + 256 KiB), 16 ranks of 128 MiB, 8 bf16 ranks of 527 MiB
+ * land on the same channels and lose up to a quarter of the bandwidth, and
+ * so can pads that make N x pad a multiple of 16 MiB (64 ranks of 32 MiB
+ * padded by 256 KiB lose a third).  A stride of P + max(32 KiB, P / 1024), P
+ * the payload rounded up to a power of two, measured best or within 1-2% of
+ * the best pad tried for 8 ranks of 256 MiB (256 MiB + 256 KiB), 16 of
+ * 128 MiB, 32 of 64 MiB, 64 of 32 MiB and 8 bf16 ranks of 527 MiB
  * (1 GiB + 1 MiB: 6.35 TB/s against 5.82 with no padding).  The library
  * takes the stride as given. */
 typedef struct {
