@@ -241,7 +241,7 @@ def _time_gpu(fn, reps, per):
         return r["total_ms"] / (reps * per), "eager"
 
 
-def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30, pad_bytes=262_144):
+def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30):
     """Stepwise ring AllReduce (fp32 SUM) at N = 4, 8, 16 over per-rank sizes
     4 KiB .. 1 GiB (x4), GPU time from HIP-graph replays, in two variants:
     one kernel per ring step, and all steps in one cooperative launch with a
@@ -260,11 +260,11 @@ def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30, pad_bytes=262_144):
            "per_n": {}}
     glob = {"kernel_per_step": ([], [], []), "grid_barrier": ([], [], [])}
     for N in ranks:
-        # rank rows padded like the headline's: a stride of exactly 1 GiB
-        # puts every rank's same offset on the same HBM channels
-        send = rank_tensor(N, sizes[-1], torch.float32, pad_bytes, dev)
+        # rank rows by the stride rule (1 GiB + 1 MiB): a stride of exactly
+        # 1 GiB puts every rank's same offset on the same HBM channels
+        send = strided_ranks(N, sizes[-1], torch.float32, dev)
         send.copy_(torch.randn(N, sizes[-1], generator=gen, device=dev) * 1e-3)
-        recv = rank_tensor(N, sizes[-1], torch.float32, pad_bytes, dev)
+        recv = strided_ranks(N, sizes[-1], torch.float32, dev)
         ws = ccgpu.make_workspace("all_reduce", N, sizes[-1], "f32", "ring", 1, dev, grid_sync=True)
         # steady clocks before the smallest, most clock-sensitive points
         for _ in range(10):
@@ -902,7 +902,7 @@ def main():
         del send, recv, ws
         torch.cuda.empty_cache()
         log("alpha-beta calibration")
-        out["alpha_beta"] = alpha_beta(dev, pad_bytes=args.pad_bytes)
+        out["alpha_beta"] = alpha_beta(dev)
         log("other workloads")
         out["workloads"] = workloads(dev)
         log("schedules")
