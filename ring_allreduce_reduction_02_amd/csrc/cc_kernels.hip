@@ -2288,7 +2288,10 @@ int hier_blocks_per_cu(int) { return 3; }
 // per CU that hold the whole grid.  Measured on the int32 ring at N = 4,
 // 1,048,576 elements (2,048 tiles, graph replays): 6.75 us at 8 per CU
 // against 7.35 at the byte rule's 4 with the buffers cache-resident, 8.32
-// against 8.43 from HBM.
+// against 8.43 from HBM.  The fused ReduceScatter, AllGather and
+// hierarchical AllReduce take the same rule (16 rotating buffer sets, fp32,
+// 4,096 tiles: AllGather at N = 16 27.9 us against 32.6, ReduceScatter at
+// N = 16 29.9 against 32.1, hierarchical 4x2 28.3 against 33.3).
 int one_round_blocks(uint64_t tiles, int blocks) {
   const int cus = dev_info().cus;
   if (cus <= 0 || tiles > 16ull * (uint64_t)cus) return blocks;
@@ -2323,8 +2326,9 @@ static unsigned ar_fused_lds(const Red& r, int blocks) {
 // halving-doubling at N = 8: 6.56 (fp32) and 6.79 (bf16) at 4 against 6.25
 // and 6.38 at 8.
 static unsigned rs_fused_lds(const Red& r) {
-  const int b = r.blocks_per_cu > 0 ? r.blocks_per_cu : r.N < 8 ? 0 : r.N <= 12 ? 4 : 3;
-  return occupancy_lds(b, kVecBytes * (r.N + 1), kSkewedTarget);
+  if (r.blocks_per_cu > 0) return lds_for_blocks_per_cu(r.blocks_per_cu);
+  const int b = r.N < 8 ? default_blocks_per_cu(kVecBytes * (r.N + 1), kSkewedTarget, 1) : r.N <= 12 ? 4 : 3;
+  return lds_for_blocks_per_cu(one_round_blocks(num_tiles(r.M, r.dt), b));
 }
 
 hipError_t launch_ring_fused(const Red& r) {
@@ -2492,7 +2496,8 @@ hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int 
   for (int s = 0; s < r.N; ++s) a.seg[s] = seg[s];
   for (int s = 0; s <= r.N; ++s) a.bnd[s] = segbnd[s];
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
-  const unsigned lds = lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu : hier_blocks_per_cu(r.N));
+  const unsigned lds = lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu
+                                                                 : one_round_blocks(num_tiles(r.M, r.dt), hier_blocks_per_cu(r.N)));
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     hipLaunchKernelGGL((k_hier_fused<DT, OP>), grid, blk, lds, r.st, a);
@@ -2727,7 +2732,7 @@ hipError_t launch_ag_fused(const Gat& g) {
   if (c.blocks_per_cu <= 0) {
     const int b = default_blocks_per_cu(kVecBytes * (uint64_t)(g.N + 1), kSkewedTarget, 1);
     const int cap = g.N < 6 ? 10 : 8;
-    c.blocks_per_cu = b > cap ? cap : b;
+    c.blocks_per_cu = one_round_blocks(gat_tiles(g), b > cap ? cap : b);
   }
   return launch_ring_ag_pass(c, 0, g.N - 1);
 }
