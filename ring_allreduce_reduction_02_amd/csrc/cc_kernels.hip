@@ -26,6 +26,7 @@
 
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "cc_launch.h"
@@ -2206,11 +2207,15 @@ struct DevInfo {
   int cus = 0;
 };
 
+// Per-device attributes, queried once per device; the lock makes calls from
+// several host threads safe.
 DevInfo dev_info() {
+  static std::mutex mu;
   static DevInfo cache[64];
   static bool have[64] = {};
   int d = 0;
   if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) d = 0;
+  std::lock_guard<std::mutex> lock(mu);
   if (!have[d]) {
     DevInfo i;
     if (hipDeviceGetAttribute(&i.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, d) != hipSuccess)
