@@ -2278,14 +2278,15 @@ unsigned occupancy_lds(int requested, uint64_t traffic, uint64_t target, int min
 // lane also unpacks and rounds eight elements per vector and wants more
 // workgroups: 6 up to N = 6 (N = 5: 6.32 TB/s against 5.69 at 4), 4 up to 12
 // (N = 10: 5.92 against 5.50 at 3), 3 up to 16, 2 beyond.  The hierarchical
-// kernel, whose per-leaf walk is longer, takes 3 (at 8 ranks in rows
-// 256 MiB + 256 KiB apart 6.26-6.30 TB/s against 6.15-6.17 at 4; in unpadded
-// rows 4 had been ahead by a few percent).
+// kernel, whose per-leaf walk is longer, takes 3 up to 16 ranks (at 8 ranks
+// in rows 256 MiB + 256 KiB apart 6.26-6.30 TB/s against 6.15-6.17 at 4 and
+// 5.85 at 2) and 2 beyond (8x8 5.74 against 5.53 at 3, 4x4x4 5.67 against
+// 5.47, 4x8 5.87 against 5.70; 2 GiB per buffer, unpadded rows).
 int batched_ring_blocks_per_cu(int N, int dt) {
   if (dt == DT_BF16) return N <= 6 ? 6 : N <= 12 ? 4 : N <= 16 ? 3 : 2;
   return N <= 8 ? 4 : N <= 16 ? 3 : 2;
 }
-int hier_blocks_per_cu(int) { return 3; }
+int hier_blocks_per_cu(int N) { return N <= 16 ? 3 : 2; }
 
 // A fused AllReduce grid small enough to be resident all at once (at most 16
 // workgroups per CU) runs best that way: its loads all issue in the first
