@@ -1,18 +1,27 @@
 #!/usr/bin/env python
 """Benchmark of the ring AllReduce on one MI355X.
 
-Workload: ring AllReduce SUM of synthetic gradients, N = 8 logical ranks,
-M = 67,108,864 fp32 elements per rank (256 MiB each), Gaussian values with
-sigma = 1e-3, the rank buffers 64 KiB + 256 B apart.  One step is one
-cc_all_reduce call (the fused ring kernel) over inputs already resident in
-HBM.  The step's algorithmic traffic is 2*N*M*4 bytes (read every rank's
-input once, write every rank's output once).
+Headline workload: ring AllReduce SUM of synthetic gradients, N = 8 logical
+ranks, M = 67,108,864 fp32 elements per rank (256 MiB each), Gaussian values
+with sigma = 1e-3, rank rows 256 MiB + 256 KiB apart (rank_stride_bytes).  One
+step is one cc_all_reduce call (the fused ring kernel) over inputs already
+resident in HBM; its algorithmic traffic is 2*N*M*4 bytes (every rank's input
+read once, every rank's output written once).
 
-Prints one JSON line: achieved GB/s (value) and its fraction of the 8 TB/s
-HBM peak, the simulated ring busbw, the roofline object of the fused kernel
-(with HBM bytes from committed rocprofv3 counters when they match the
-current kernel source), the oracle's time on the host cores for a bounded
-sample, a bf16 twin and an alpha-beta calibration of the stepwise ring.
+stdout carries one JSON object per line:
+  * first, one record per other workload -- the int32 ring at N = 4, the
+    bucketed bf16 gradient sync, the ZeRO-3 ReduceScatter / AllGather at
+    N = 16 and the MoE AllToAll(v) -- each with its timing, rank stride and a
+    bit-for-bit parity verdict against the oracle run on the same inputs;
+  * LAST, the headline line (at most 2 KB): GB/s, ms per step, % of peak,
+    simulated busbw, the fused kernel's roofline (per-launch HIP event
+    durations; HBM traffic from committed rocprofv3 counters while the kernel
+    source is unchanged), the bf16 twin, the alpha-beta fit of the stepwise
+    ring at N = 8, the oracle's time on the host cores, and whether the timed
+    output equals the oracle's bit for bit.
+--extras PATH writes the longer sweeps (rank-stride pads, alpha-beta at
+N = 4, 8, 16, every schedule, hierarchical grids, AllToAll variants, INT8
+with error feedback) to PATH as one JSON document.
 """
 from __future__ import annotations
 
@@ -31,16 +40,24 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (% of peak) + simulated busbw for N-rank ring AllReduce"
 KERNEL_SRC = os.path.join(ROOT, "ring_allreduce_reduction_02_amd", "csrc", "cc_kernels.hip")
 PMC_FILE = os.path.join(ROOT, "profiles", "ring_fused_f32_n8_m67108864_pmc.json")
+HEADLINE_MAX_BYTES = 2048
+BUCKET_CAP_BYTES = 25 * 1024 * 1024
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def emit(rec: dict) -> None:
+    print(json.dumps(rec, separators=(",", ":")), flush=True)
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
+
+# ---------------------------------------------------------------- layout
 
 def rank_stride_bytes(row_bytes):
     """Rank stride for rows of row_bytes: the payload rounded up to a power of
@@ -70,20 +87,44 @@ def rank_tensor(N, M, dtype, pad_bytes, device):
 def randn_ranks(N, M, gen, device, pad_bytes):
     """N x M fp32 Gaussian (sigma 1e-3) rank rows, M*4 + pad_bytes apart."""
     import torch
+    t = rank_tensor(N, M, torch.float32, pad_bytes, device)
     # sampled in place: a torch copy here would share its kernel with the
     # copy probe whose counters scale the profiles' HBM traffic
-    t = rank_tensor(N, M, torch.float32, pad_bytes, device)
     t.normal_(0.0, 1e-3, generator=gen)
     return t
 
 
-def upload(xs, t):
+def _host_tensor(x):
     import numpy as np
     import torch
-    for r, x in enumerate(xs):
-        h = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if x.dtype == np.uint16 else torch.from_numpy(x)
-        t[r].copy_(h, non_blocking=False)
+    x = np.ascontiguousarray(x)
+    return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if x.dtype == np.uint16 else torch.from_numpy(x)
 
+
+def upload(xs, t):
+    """Row r of the device tensor t takes xs[r] (bf16 as uint16 bits); a
+    shorter array fills the row's prefix."""
+    for r, x in enumerate(xs):
+        t[r, :len(x)].copy_(_host_tensor(x), non_blocking=False)
+
+
+def download(t):
+    """[N, L] device tensor -> numpy (bf16 as uint16 bits)."""
+    import numpy as np
+    import torch
+    h = t.detach().cpu().contiguous()
+    if h.dtype == torch.bfloat16:
+        return h.view(torch.int16).numpy().view(np.uint16)
+    return h.numpy()
+
+
+def same_bits(a, b) -> bool:
+    import numpy as np
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# ---------------------------------------------------------------- timing
 
 def time_launches(fn, steps, warmup):
     """Warm up, then time `steps` launches with a HIP event pair around each
@@ -158,77 +199,6 @@ def time_graph(fn, reps=20, per_graph=1):
     return a.elapsed_time(b) / (reps * per_graph)
 
 
-def traffic_from_profile(nbytes_alg):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs,
-    scaled by the copy-kernel calibration; None if the kernel changed."""
-    if not os.path.exists(PMC_FILE):
-        return None, "no counter file"
-    with open(PMC_FILE) as f:
-        p = json.load(f)
-    if p.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None, "kernel changed since the counters were taken"
-    fetch = p["fetch_kib_per_dispatch"] * 1024.0 * p["fetch_scale"]
-    write = p["write_kib_per_dispatch"] * 1024.0 * p["write_scale"]
-    return fetch + write, "rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE (scaled by a plain copy)"
-
-
-def cpu_baseline(N, M_sample, min_seconds=10.0, max_runs=25):
-    """The oracle as it stands, on the host cores: the step-explicit ring
-    simulator on the same workload, repeated until at least `min_seconds` of
-    CPU work (median run reported)."""
-    from oracle import ccsim
-    from ring_allreduce_reduction_02_amd import synth
-    xs = synth.gradient_inputs(N, M_sample, "f32")
-    times = []
-    t_all = time.perf_counter()
-    while len(times) < max_runs and (time.perf_counter() - t_all < min_seconds or len(times) < 3):
-        t = time.perf_counter()
-        ccsim.ring_all_reduce(xs, "sum", "f32")
-        times.append(time.perf_counter() - t)
-    t = sorted(times)[len(times) // 2]
-    cpu_model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {
-        "value": 2 * N * M_sample * 4 / t / 1e9,
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"ring AllReduce SUM, N={N}, M={M_sample} fp32 per rank, step-explicit NumPy simulator "
-                  f"(single-threaded elementwise ops), {len(times)} runs in {sum(times):.1f} s, median {t:.3f} s",
-        "host_logical_cpus": os.cpu_count(),
-        "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
-        "cpu_model": cpu_model or platform.processor(),
-    }
-
-
-def pad_sweep(src, N, M, dev, pads=(0, 65_792, 262_144, 2_097_152), steps=10):
-    """The headline AllReduce with rank buffers `pad` bytes apart beyond the
-    payload (same data, copied on the device)."""
-    import torch
-
-    from ring_allreduce_reduction_02_amd import ccgpu
-    res = {}
-    for pad in pads:
-        s = rank_tensor(N, M, src.dtype, pad, dev)
-        r = rank_tensor(N, M, src.dtype, pad, dev)
-        s.copy_(src)
-        t = time_launches(lambda: ccgpu.all_reduce(s, r), steps, 3)
-        per = sorted(t["per_launch_ms"])
-        ms = per[len(per) // 2]
-        res[str(pad)] = {"median_launch_ms": round(ms, 5), "min_launch_ms": round(per[0], 5),
-                         "GBps": round(2 * N * M * src.element_size() / ms / 1e6, 1)}
-        del s, r
-        torch.cuda.empty_cache()
-    return res
-
-
 def _time_gpu(fn, reps, per):
     """GPU time of fn from graph replays; eager back-to-back launches between
     HIP events if the call cannot be captured."""
@@ -241,11 +211,474 @@ def _time_gpu(fn, reps, per):
         return r["total_ms"] / (reps * per), "eager"
 
 
+def _avg_ms(fn, steps=10, warmup=3):
+    r = time_steps(fn, steps, warmup)
+    return r["total_ms"] / steps
+
+
+def gbps(nbytes, ms):
+    return nbytes / ms / 1e6
+
+
+def traffic_from_profile(pmc_file=PMC_FILE):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs,
+    scaled by the copy-kernel calibration; None if the kernel changed."""
+    if not os.path.exists(pmc_file):
+        return None, "no counter file"
+    with open(pmc_file) as f:
+        p = json.load(f)
+    if p.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    fetch = p["fetch_kib_per_dispatch"] * 1024.0 * p["fetch_scale"]
+    write = p["write_kib_per_dispatch"] * 1024.0 * p["write_scale"]
+    return fetch + write, "rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE (scaled by a plain copy)"
+
+
+# ---------------------------------------------------------------- the oracle leg
+# The only code in this file that runs the oracle: the step-explicit CPU
+# simulator, on the same inputs as the GPU, timed on the host cores.  Its
+# outputs also decide the parity verdicts below.
+
+def _oracle():
+    from oracle import ccsim
+    return ccsim
+
+
+def oracle_run(fn, min_seconds=0.0, max_runs=25):
+    """Run fn() (an oracle call) until min_seconds of CPU time have passed
+    (at least once); returns (median seconds, runs, total seconds, last
+    output)."""
+    times, out = [], None
+    t_all = time.perf_counter()
+    while not times or (len(times) < max_runs and time.perf_counter() - t_all < min_seconds) or \
+            (min_seconds > 0 and len(times) < 3):
+        t = time.perf_counter()
+        out = fn()
+        times.append(time.perf_counter() - t)
+    return sorted(times)[len(times) // 2], len(times), sum(times), out
+
+
+def host_info():
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_logical_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "cpu_model": cpu_model or platform.processor()}
+
+
+def cpu_baseline(xs, dtype, min_seconds=10.0):
+    """The oracle as it stands on the host cores: the step-explicit ring
+    AllReduce simulator on the headline's own inputs, repeated until
+    min_seconds of CPU work (median run reported).  Returns the record and
+    the oracle's output."""
+    cs = _oracle()
+    N, M = len(xs), len(xs[0])
+    es = 4 if dtype == "f32" else 2
+    t, runs, total, out = oracle_run(lambda: cs.ring_all_reduce(xs, "sum", dtype), min_seconds)
+    rec = {"value": round(2 * N * M * es / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"the whole workload (ring AllReduce SUM, N={N}, M={M} {dtype}), step-explicit NumPy "
+                     f"simulator, single-threaded; {runs} runs in {total:.1f} s, median {t:.3f} s"}
+    return rec, out
+
+
+# ---------------------------------------------------------------- headline
+
+def run_headline(args, dev):
+    """The timed steps of the headline AllReduce.  Returns the measurements
+    and the recv buffer downloaded to the host."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu, synth
+    N, M = args.ranks, args.count
+    tdt = torch.float32 if args.dtype == "f32" else torch.bfloat16
+    es = 4 if args.dtype == "f32" else 2
+    log(f"generating {N} x {M} {args.dtype} synthetic gradients")
+    xs = synth.gradient_inputs(N, M, args.dtype)
+    send = rank_tensor(N, M, tdt, args.pad_bytes, dev)
+    recv = rank_tensor(N, M, tdt, args.pad_bytes, dev)
+    upload(xs, send)
+    ws = ccgpu.make_workspace("all_reduce", N, M, args.dtype, args.algo, args.fuse_depth, dev)
+    if args.copy_probe_bytes:
+        copy_probe(args.copy_probe_bytes, dev)
+
+    def step():
+        ccgpu.all_reduce(send, recv, op="sum", algo=args.algo, fuse_depth=args.fuse_depth, workspace=ws,
+                         blocks_per_cu=args.blocks_per_cu)
+
+    log("timing")
+    # the K timed steps run back to back; the per-launch durations behind the
+    # roofline come from a second, instrumented pass of K launches (an event
+    # pair around every launch adds a few us per step to the first)
+    recv.fill_(float("nan"))
+    res = time_steps(step, args.steps, args.warmup)
+    per = time_launches(step, args.steps, 2)["per_launch_ms"]
+    torch.cuda.synchronize()
+    got = download(recv) if not args.no_cpu_baseline else None
+    m = {"N": N, "M": M, "es": es, "ms_per_step": res["total_ms"] / args.steps, "per_launch_ms": per,
+         "rank_stride_bytes": send.stride(0) * es, "xs": xs, "got": got}
+    del send, recv, ws
+    torch.cuda.empty_cache()
+    return m
+
+
+def bf16_twin(args, dev):
+    """The same AllReduce on the bf16 rounding of the same samples."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu, synth
+    N, M = args.ranks, args.count
+    xb = synth.gradient_inputs(N, M, "bf16")
+    sb = rank_tensor(N, M, torch.bfloat16, args.pad_bytes, dev)
+    rb = rank_tensor(N, M, torch.bfloat16, args.pad_bytes, dev)
+    upload(xb, sb)
+    r = time_steps(lambda: ccgpu.all_reduce(sb, rb, algo="ring", fuse_depth=0), args.steps, args.warmup)
+    ms = r["total_ms"] / args.steps
+    out = {"ms_per_step": round(ms, 5), "GBps": round(gbps(2 * N * M * 2, ms), 1),
+           "pct_of_peak": round(100 * gbps(2 * N * M * 2, ms) / PEAK_HBM_GBPS, 2)}
+    got = download(rb) if not args.no_cpu_baseline else None
+    del sb, rb
+    torch.cuda.empty_cache()
+    if got is not None:
+        cs = _oracle()
+        t, _, _, exp = oracle_run(lambda: cs.ring_all_reduce(xb, "sum", "bf16"))
+        out["parity"] = all(same_bits(got[r], exp[r]) for r in range(N))
+        out["oracle_s"] = round(t, 3)
+    return out
+
+
+def alpha_beta_n8(dev, pad_bytes):
+    """alpha-beta fit of the stepwise ring AllReduce (one kernel per ring
+    step, fp32 SUM) at N = 8 over per-rank sizes 4 KiB .. 64 MiB, GPU time
+    from HIP-graph replays: T = alpha * 2(N-1) + beta * bytes sent per rank."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import calib, ccgpu
+    N = 8
+    sizes = [1 << k for k in range(10, 25, 2)]
+    gen = torch.Generator(device=dev).manual_seed(20261202)
+    send = randn_ranks(N, sizes[-1], gen, dev, pad_bytes)
+    recv = rank_tensor(N, sizes[-1], torch.float32, pad_bytes, dev)
+    st, by, ts = [], [], []
+    for m in sizes:
+        s_, r_ = send[:, :m], recv[:, :m]
+        t, _ = _time_gpu(lambda: ccgpu.all_reduce(s_, r_, fuse_depth=1), 10, 16 if m <= (1 << 20) else 2)
+        b, n = ccgpu.get_traffic("all_reduce", N, m, "f32", "ring")
+        st.append(n); by.append(b); ts.append(t / 1e3)
+    fit = calib.fit_alpha_beta(st, by, ts)
+    del send, recv
+    torch.cuda.empty_cache()
+    return {"n": N, "alpha_us": round(fit["alpha_us_per_step"], 3), "beta_ps_per_byte": round(fit["beta_ps_per_byte"], 3),
+            "link_GBps": round(fit["link_GBps"], 1), "n_star_bytes": round(fit["n_star_bytes"]),
+            "sizes": "4KiB..64MiB per rank", "max_rel_residual": round(fit["max_rel_residual"], 3)}
+
+
+def make_headline(m, args, roof, twin, ab, cpu, parity):
+    """The headline record (the last stdout line)."""
+    N, M, es = m["N"], m["M"], m["es"]
+    ms = m["ms_per_step"]
+    alg_bytes = 2 * N * M * es
+    value = gbps(alg_bytes, ms)
+    return {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"ring_allreduce_sum_n{N}_m{M}_{args.dtype}",
+            "nranks": N,
+            "count_per_rank": M,
+            "algo": args.algo,
+            "fuse_depth": args.fuse_depth,
+            "rank_stride_bytes": m["rank_stride_bytes"],
+            "values": "Gaussian sigma=1e-3" + (" (bf16 RNE)" if args.dtype == "bf16" else ""),
+            "parallelism": f"{N} logical ranks in one GPU's HBM",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
+        "busbw_GBps": round((M * es) / (ms / 1e3) * 2 * (N - 1) / N / 1e9, 2),
+        "algorithmic_bytes_per_step": alg_bytes,
+        "parity": parity,
+        "roofline": roof,
+        "bf16_twin": twin,
+        "alpha_beta": ab,
+        "cpu_baseline": cpu,
+    }
+
+
+def headline_line(h: dict) -> str:
+    s = json.dumps(h, separators=(",", ":"))
+    if len(s.encode()) > HEADLINE_MAX_BYTES:
+        raise ValueError(f"headline line is {len(s.encode())} bytes (at most {HEADLINE_MAX_BYTES})")
+    return s
+
+
+def roofline_of(m, args):
+    per = m["per_launch_ms"]
+    alg_bytes = 2 * m["N"] * m["M"] * m["es"]
+    avg = sum(per) / len(per)
+    traffic, _src = traffic_from_profile() if (args.algo == "ring" and args.fuse_depth == 0 and args.dtype == "f32"
+                                                and m["N"] == 8 and m["M"] == 67_108_864) else (None, "")
+    kname = {"ring": "k_ring_fused", "hd": "k_tree_fused", "butterfly": "k_tree_fused"}[args.algo]
+    if args.fuse_depth:
+        kname = "stepwise (several kernels per step)"
+    achieved = gbps(alg_bytes, avg)
+    return {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": round(traffic) if traffic else None,
+            "traffic_over_algorithmic": round(traffic / alg_bytes, 4) if traffic else None,
+            "avg_launch_ms": round(avg, 5), "min_launch_ms": round(min(per), 5)}
+
+
+# ---------------------------------------------------------------- other workloads (one record each)
+
+def rec_int32_ring(dev, nsets=64):
+    """Ring AllReduce SUM, N = 4, M = 1,048,576 int32 uniform in [-1000, 1000]:
+    one buffer set (cache-resident) and `nsets` rotating sets (2 GiB, beyond
+    the 256 MB last-level cache), GPU time from HIP-graph replays."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu, synth
+    N, M = 4, 1 << 20
+    xs = synth.uniform_int32(synth.W_INT_RING, N, M)
+    base = strided_ranks(N, M, torch.int32, dev)
+    upload(xs, base)
+    sets = []
+    for i in range(nsets):
+        s_ = base if i == 0 else strided_ranks(N, M, torch.int32, dev)
+        if i:
+            s_.copy_(base)
+        sets.append((s_, strided_ranks(N, M, torch.int32, dev)))
+    alg = 2 * N * M * 4
+    ms1 = time_graph(lambda: ccgpu.all_reduce(sets[0][0], sets[0][1]), 10, 32)
+
+    def rot():
+        for s_, r_ in sets:
+            ccgpu.all_reduce(s_, r_)
+    msr = time_graph(rot, 10, 1) / nsets
+    torch.cuda.synchronize()
+    got0, got_last = download(sets[0][1]), download(sets[-1][1])
+    cs = _oracle()
+    t, _, _, exp = oracle_run(lambda: cs.ring_all_reduce(xs, "sum", "int32"))
+    par = all(same_bits(got0[r], exp[r]) and same_bits(got_last[r], exp[r]) for r in range(N))
+    del sets, base
+    torch.cuda.empty_cache()
+    return {"section": "int32_ring_n4_m1048576", "dtype": "int32", "algo": "ring",
+            "rank_stride_bytes": rank_stride_bytes(M * 4),
+            "same_set_us": round(ms1 * 1e3, 2), "same_set_GBps": round(gbps(alg, ms1), 1),
+            "rotating_sets": nsets, "rotating_us": round(msr * 1e3, 2), "rotating_GBps": round(gbps(alg, msr), 1),
+            "parity": par, "oracle_s": round(t, 3)}
+
+
+def bucket_layout(N, sizes, tensors):
+    """The bucketed workload's per-rank flat buffers: tensors at the
+    cc_bucket_plan offsets (25 MiB buckets, 128-element aligned), zero
+    between them."""
+    import numpy as np
+
+    from ring_allreduce_reduction_02_amd import ccgpu
+    bof, toff, boff, bcnt = ccgpu.bucket_plan(sizes, 2, BUCKET_CAP_BYTES, 128)
+    extent = boff[-1] + bcnt[-1]
+    host = np.zeros((N, extent), dtype=np.uint16)
+    for r in range(N):
+        for t, x in enumerate(tensors[r]):
+            host[r, toff[t]:toff[t] + len(x)] = x
+    return host, toff, boff, bcnt
+
+
+def rec_buckets(dev):
+    """Bucketed bf16 gradient sync, N = 8: 120 tensors with log-uniform sizes
+    in [4K, 16M] elements, N(0, 1e-2) values, 25 MiB buckets, one fused launch
+    per 16 buckets; ring, halving-doubling and butterfly on the same data,
+    each checked bit for bit against the oracle's per-bucket AllReduce; the
+    per-bucket GB/s of the ring with one launch per bucket."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu, synth
+    N = 8
+    sizes = synth.tensor_sizes_log_uniform()
+    tensors = synth.bucket_tensors(N, sizes)
+    host, toff, boff, bcnt = bucket_layout(N, sizes, tensors)
+    extent = host.shape[1]
+    send = strided_ranks(N, extent, torch.bfloat16, dev)
+    upload(host, send)
+    del host
+    recv = strided_ranks(N, extent, torch.bfloat16, dev)
+    alg = 2 * N * sum(bcnt) * 2
+    cs = _oracle()
+    ref_buckets = cs.bucket_pack(sizes, 2, BUCKET_CAP_BYTES)
+    out = {"section": "bucketed_bf16_n8_120_tensors", "dtype": "bf16", "tensors": len(sizes), "buckets": len(boff),
+           "elements_per_rank": sum(bcnt), "rank_stride_bytes": send.stride(0) * 2}
+    for algo in ("ring", "hd", "butterfly"):
+        ms = _avg_ms(lambda: ccgpu.all_reduce_buckets(send, recv, boff, bcnt, algo=algo))
+        torch.cuda.synchronize()
+        got = download(recv)
+        t, _, _, exp = oracle_run(lambda: cs.bucketed_all_reduce(tensors, ref_buckets, algo, "sum", "bf16"))
+        par = all(same_bits(got[r, toff[k]:toff[k] + len(tensors[r][k])], exp[r][k])
+                  for r in range(N) for k in range(len(sizes)))
+        out[algo] = {"ms": round(ms, 4), "GBps": round(gbps(alg, ms), 1), "parity": par, "oracle_s": round(t, 2)}
+        del got, exp
+    per = []
+    for o, c in zip(boff, bcnt):
+        s_, r_ = send[:, o:o + c], recv[:, o:o + c]
+        t, _ = _time_gpu(lambda: ccgpu.all_reduce(s_, r_), 10, 1)
+        per.append(round(gbps(2 * N * c * 2, t)))
+    out["ring_per_bucket_GBps"] = per
+    del send, recv
+    torch.cuda.empty_cache()
+    return out
+
+
+def rec_zero3(dev):
+    """ZeRO-3-style standalone ReduceScatter then AllGather, N = 16,
+    M = 33,554,432 fp32 uniform [-1, 1) per rank, plus int32 MAX / PROD
+    ReduceScatters on 1,048,576 elements; every output compared whole with
+    the oracle."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu, synth
+    cs = _oracle()
+    N, M = 16, 1 << 25
+    S = M // N
+    xs = synth.uniform_f32(synth.W_ZERO3, N, M)
+    send = strided_ranks(N, M, torch.float32, dev)
+    upload(xs, send)
+    shard = strided_ranks(N, S, torch.float32, dev)
+    full = strided_ranks(N, M, torch.float32, dev)
+    alg = (N + 1) * M * 4
+    out = {"section": "zero3_rs_ag_n16_m33554432_f32",
+           "rank_stride_bytes": [send.stride(0) * 4, shard.stride(0) * 4]}
+    shards = None
+    for algo, oracle_fn in (("hd", cs.hd_reduce_scatter), ("ring", cs.ring_reduce_scatter)):
+        ms = _avg_ms(lambda: ccgpu.reduce_scatter(send, shard, algo=algo))
+        torch.cuda.synchronize()
+        got = download(shard)
+        t, _, _, exp = oracle_run(lambda: oracle_fn(xs, "sum", "f32"))
+        out[f"reduce_scatter_{algo}"] = {"ms": round(ms, 4), "GBps": round(gbps(alg, ms), 1),
+                                         "parity": all(same_bits(got[r], exp[r]) for r in range(N)),
+                                         "oracle_s": round(t, 2)}
+        if algo == "ring":
+            shards = [got[r].copy() for r in range(N)]   # the AllGather below gathers these
+    del xs, send
+    ms = _avg_ms(lambda: ccgpu.all_gather(shard, full))
+    torch.cuda.synchronize()
+    fg = download(full)
+    t, _, _, exp = oracle_run(lambda: cs.ring_all_gather(shards, "f32"))
+    out["all_gather_ring"] = {"ms": round(ms, 4), "GBps": round(gbps(alg, ms), 1),
+                              "parity": all(same_bits(fg[r], exp[r]) for r in range(N)), "oracle_s": round(t, 2)}
+    del fg, exp, shard, full
+    torch.cuda.empty_cache()
+    Mi = 1 << 20
+    ints = {}
+    for op, kind, xs_i in (("max", "full", synth.uniform_int32(synth.W_ZERO3, N, Mi, sub=1)),
+                           ("prod", "small", synth.choice_int32(synth.W_ZERO3, N, Mi, [-2, -1, 1, 2], sub=2)),
+                           ("prod", "full", synth.uniform_int32(synth.W_ZERO3, N, Mi, sub=3))):
+        si = strided_ranks(N, Mi, torch.int32, dev)
+        ri = strided_ranks(N, Mi // N, torch.int32, dev)
+        upload(xs_i, si)
+        ccgpu.reduce_scatter(si, ri, op=op)
+        torch.cuda.synchronize()
+        got = download(ri)
+        exp = cs.ring_reduce_scatter(xs_i, op, "int32")
+        ints[f"{op}_{kind}"] = all(same_bits(got[r], exp[r]) for r in range(N))
+    out["int32_reduce_scatter_parity"] = ints
+    torch.cuda.empty_cache()
+    return out
+
+
+def moe_inputs(N=8, T=4096, E=64, K=8, H=7168):
+    """Counts matrix and tagged bf16 payload rows of the MoE workload."""
+    import numpy as np
+
+    from ring_allreduce_reduction_02_amd import synth
+    ch = synth.moe_routing(N, T, E, K)
+    C = np.zeros((N, N), dtype=np.int64)
+    for i in range(N):
+        _, C[i] = synth.moe_send_layout(ch[i], N, E)
+    rows = [synth.moe_payload_rows(i, int(C[i].sum()), H) for i in range(N)]
+    return C, rows
+
+
+def rec_moe(dev):
+    """MoE AllToAll(v) dispatch and combine, N = 8, 4096 tokens per rank, top-8
+    of 64 experts with Zipf(1.2) loads, rows of 7168 bf16: the dispatch (direct
+    and pairwise) compared with the oracle's blocked transpose byte for byte,
+    the combine (the transposed exchange) with the original rows."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu
+    N, H = 8, 7168
+    C, rows = moe_inputs(N, H=H)
+    Ls, Lr = int(C.sum(1).max()), int(C.sum(0).max())
+    send = strided_ranks(N, Ls * H, torch.bfloat16, dev)
+    upload([r.reshape(-1) for r in rows], send)
+    recv = strided_ranks(N, Lr * H, torch.bfloat16, dev)
+    back = strided_ranks(N, Ls * H, torch.bfloat16, dev)
+    alg = 2 * int(C.sum()) * H * 2
+    out = {"section": "moe_alltoall_n8_t4096_h7168_bf16", "rows_received": C.sum(0).tolist(),
+           "skew_max_over_mean": round(float(C.sum(0).max() / C.sum(0).mean()), 3),
+           "rank_stride_bytes": [send.stride(0) * 2, recv.stride(0) * 2]}
+    cs = _oracle()
+    t, _, _, exp = oracle_run(lambda: cs.all_to_all([r.reshape(-1) for r in rows], C, row=H))
+    for fd, name in ((1, "pairwise"), (0, "direct")):
+        ms = _avg_ms(lambda: ccgpu.all_to_all(send, recv, C.tolist(), H, fuse_depth=fd))
+        torch.cuda.synchronize()
+        got = download(recv)
+        out[f"dispatch_{name}"] = {"ms": round(ms, 4), "GBps": round(gbps(alg, ms), 1),
+                                   "parity": all(same_bits(got[j, :len(exp[j])], exp[j]) for j in range(N))}
+        del got
+    out["oracle_s"] = round(t, 2)
+    ms = _avg_ms(lambda: ccgpu.all_to_all(recv, back, C.T.tolist(), H))
+    torch.cuda.synchronize()
+    got = download(back)
+    out["combine_direct"] = {"ms": round(ms, 4), "GBps": round(gbps(alg, ms), 1),
+                             "round_trip_identical": all(same_bits(got[i, :rows[i].size], rows[i].reshape(-1))
+                                                         for i in range(N))}
+    del send, recv, back
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- extras (--extras PATH)
+
+def pad_sweep(N, M, dev, pads=(0, 65_792, 262_144, 2_097_152), steps=10):
+    """The headline AllReduce with rank buffers `pad` bytes apart beyond the
+    payload."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu
+    gen = torch.Generator(device=dev).manual_seed(20261202)
+    res = {}
+    for pad in pads:
+        s = randn_ranks(N, M, gen, dev, pad)
+        r = rank_tensor(N, M, torch.float32, pad, dev)
+        t = time_launches(lambda: ccgpu.all_reduce(s, r), steps, 3)
+        per = sorted(t["per_launch_ms"])
+        ms = per[len(per) // 2]
+        res[str(pad)] = {"median_launch_ms": round(ms, 5), "min_launch_ms": round(per[0], 5),
+                         "GBps": round(gbps(2 * N * M * 4, ms), 1)}
+        del s, r
+        torch.cuda.empty_cache()
+    return res
+
+
 def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30):
     """Stepwise ring AllReduce (fp32 SUM) at N = 4, 8, 16 over per-rank sizes
     4 KiB .. 1 GiB (x4), GPU time from HIP-graph replays, in two variants:
-    one kernel per ring step, and all steps in one cooperative launch with a
-    grid barrier between steps.  Fits T = alpha * 2(N-1) + beta * bytes sent
+    one kernel per ring step, and all steps in one launch with a grid-wide
+    barrier between steps.  Fits T = alpha * 2(N-1) + beta * bytes sent
     per rank per N, and over all N together with a per-call constant t0
     (T = t0 + alpha * steps + beta * bytes).  The fused kernel's
     T = t0 + bytes / BW is fitted on the same sizes."""
@@ -256,17 +689,14 @@ def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30):
     gen = torch.Generator(device=dev).manual_seed(20261202)
     out = {"schedule": "ring AllReduce, fp32 SUM, fuse_depth=1 (one ring step per pass)",
            "variants": {"kernel_per_step": "one kernel launch per ring step",
-                        "grid_barrier": "one cooperative launch, grid barrier between ring steps"},
+                        "grid_barrier": "one launch, grid barrier between ring steps"},
            "per_n": {}}
     glob = {"kernel_per_step": ([], [], []), "grid_barrier": ([], [], [])}
     for N in ranks:
-        # rank rows by the stride rule (1 GiB + 1 MiB): a stride of exactly
-        # 1 GiB puts every rank's same offset on the same HBM channels
         send = strided_ranks(N, sizes[-1], torch.float32, dev)
-        send.copy_(torch.randn(N, sizes[-1], generator=gen, device=dev) * 1e-3)
+        send.normal_(0.0, 1e-3, generator=gen)
         recv = strided_ranks(N, sizes[-1], torch.float32, dev)
         ws = ccgpu.make_workspace("all_reduce", N, sizes[-1], "f32", "ring", 1, dev, grid_sync=True)
-        # steady clocks before the smallest, most clock-sensitive points
         for _ in range(10):
             ccgpu.all_reduce(send, recv, fuse_depth=0)
         torch.cuda.synchronize()
@@ -284,14 +714,13 @@ def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30):
             pts.append({"bytes_per_rank": m * 4, "kernel_per_step_us": round(tk * 1e3, 3),
                         "grid_barrier_us": round(tg * 1e3, 3), "fused_us": round(tf * 1e3, 3)})
         torch.cuda.synchronize()
-        timed_out = ccgpu.grid_sync_timed_out(ws)
         out["per_n"][str(N)] = {
             "kernel_per_step": calib.fit_alpha_beta(st, by, t_ks),
             "grid_barrier": calib.fit_alpha_beta(st, by, t_gb),
             "fused": calib.fit_fixed_plus_bandwidth(fb, ft),
             "points": pts,
             "timing": sorted(how),
-            "barrier_timed_out": timed_out,
+            "barrier_timed_out": ccgpu.grid_sync_timed_out(ws),
         }
         for key, ts in (("kernel_per_step", t_ks), ("grid_barrier", t_gb)):
             glob[key][0].extend(st); glob[key][1].extend(by); glob[key][2].extend(ts)
@@ -299,11 +728,6 @@ def alpha_beta(dev, ranks=(4, 8, 16), max_bytes=1 << 30):
         torch.cuda.empty_cache()
     out["all_n"] = {k: calib.fit_launch_alpha_beta(*v) for k, v in glob.items()}
     return out
-
-
-def _avg_ms(fn, steps=10, warmup=3):
-    r = time_steps(fn, steps, warmup)
-    return r["total_ms"] / steps
 
 
 def schedules(dev, pad_bytes=262_144):
@@ -319,12 +743,11 @@ def schedules(dev, pad_bytes=262_144):
     out = {"fused": {}, "stepwise_n8": {}}
     gen = torch.Generator(device=dev).manual_seed(20261202)
     N, M = 8, 1 << 26
-    # the headline's layout: 256 MiB rows, `pad_bytes` apart
     send = randn_ranks(N, M, gen, dev, pad_bytes)
     recv = rank_tensor(N, M, torch.float32, pad_bytes, dev)
     for algo in ("ring", "hd", "butterfly", "tree", "double_tree", "ring_2port"):
         ms = _avg_ms(lambda: ccgpu.all_reduce(send, recv, algo=algo), 10, 3)
-        out["fused"][f"{algo}_n8"] = {"ms": round(ms, 4), "GBps": round(2 * N * M * 4 / ms / 1e6, 1)}
+        out["fused"][f"{algo}_n8"] = {"ms": round(ms, 4), "GBps": round(gbps(2 * N * M * 4, ms), 1)}
     del send, recv
     torch.cuda.empty_cache()
     N12, M12 = 12, 1 << 25
@@ -332,7 +755,7 @@ def schedules(dev, pad_bytes=262_144):
     recv = torch.empty_like(send)
     for algo in ("hd", "butterfly"):
         ms = _avg_ms(lambda: ccgpu.all_reduce(send, recv, algo=algo), 10, 3)
-        out["fused"][f"{algo}_n12_pair_folded"] = {"ms": round(ms, 4), "GBps": round(2 * N12 * M12 * 4 / ms / 1e6, 1)}
+        out["fused"][f"{algo}_n12_pair_folded"] = {"ms": round(ms, 4), "GBps": round(gbps(2 * N12 * M12 * 4, ms), 1)}
     del send, recv
     torch.cuda.empty_cache()
 
@@ -394,12 +817,11 @@ def hierarchical(dev, pad_bytes=262_144):
             else:
                 fn = lambda d=dims: ccgpu.all_reduce_hierarchical(send, recv, d)
             ms = _avg_ms(fn, 10, 3)
-            key = "x".join(map(str, dims))
-            out["fused"][key] = {"ms": round(ms, 4), "GBps": round(2 * N * M * 4 / ms / 1e6, 1)}
+            out["fused"]["x".join(map(str, dims))] = {"ms": round(ms, 4), "GBps": round(gbps(2 * N * M * 4, ms), 1)}
         del send, recv
         torch.cuda.empty_cache()
 
-    sizes = [1 << k for k in range(10, 25, 2)]          # 1 Ki .. 16 Mi fp32 = 4 KiB .. 64 MiB per rank
+    sizes = [1 << k for k in range(10, 25, 2)]
     for N, grids in ((8, [(8,), (4, 2), (2, 2, 2)]), (64, [(64,), (8, 8), (4, 4, 4)])):
         top = sizes[-1] if N == 8 else sizes[-2]
         send = torch.randn(N, top, generator=gen, device=dev) * 1e-3
@@ -464,7 +886,7 @@ def alltoall_variants(dev):
     recv = torch.empty(N, Lr * H, device=dev, dtype=torch.bfloat16)
     ms = _avg_ms(lambda: ccgpu.all_to_all(send, recv, C.tolist(), H))
     moved = 2 * int(C.sum()) * rowb
-    out["dropless_direct"] = {"ms": round(ms, 4), "GBps": round(moved / ms / 1e6, 1), "wire_rows": int(C.sum())}
+    out["dropless_direct"] = {"ms": round(ms, 4), "GBps": round(gbps(moved, ms), 1), "wire_rows": int(C.sum())}
     del recv
     torch.cuda.empty_cache()
     for num, den in ((1, 1), (5, 4)):
@@ -479,9 +901,9 @@ def alltoall_variants(dev):
              "wire_rows": wire, "wire_over_dropless": round(wire / int(C.sum()), 3)}
         for fd, name in ((0, "direct"), (1, "pairwise")):
             ms = _avg_ms(lambda f=fd: ccgpu.moe_dispatch_padded(send, exp, Ce.tolist(), cap, H, fuse_depth=f))
-            r[f"dispatch_{name}"] = {"ms": round(ms, 4), "GBps": round(d_moved / ms / 1e6, 1)}
+            r[f"dispatch_{name}"] = {"ms": round(ms, 4), "GBps": round(gbps(d_moved, ms), 1)}
         ms = _avg_ms(lambda: ccgpu.moe_combine_padded(exp, send, Ce.tolist(), cap, H))
-        r["combine_direct"] = {"ms": round(ms, 4), "GBps": round(c_moved / ms / 1e6, 1)}
+        r["combine_direct"] = {"ms": round(ms, 4), "GBps": round(gbps(c_moved, ms), 1)}
         out[f"padded_C{num / den:g}"] = r
         del exp
         torch.cuda.empty_cache()
@@ -494,7 +916,7 @@ def alltoall_variants(dev):
         # every block is copied once in phase 1; inter-node bytes twice more
         moved_h = 2 * (int(C.sum()) * rowb + 2 * tr[2][1])
         out[f"hierarchical_L{L}"] = {
-            "ms": round(ms, 4), "GBps_moved": round(moved_h / ms / 1e6, 1),
+            "ms": round(ms, 4), "GBps_moved": round(gbps(moved_h, ms), 1),
             "transfers": {ph: f for ph, (f, _, _) in zip(phases, tr)},
             "bytes": {ph: t for ph, (_, t, _) in zip(phases, tr)}}
         del ws
@@ -560,20 +982,19 @@ def int8_ef(dev):
         fused_bytes = N * M * (2 * es + 8)
         two_bytes = N * M * (es + 8) + 2 * N * ccgpu.int8_message_bytes(M) + N * M * es
         out[dtype] = {
-            "fused_ms": round(ms_f, 4), "fused_GBps": round(fused_bytes / ms_f / 1e6, 1),
-            "fused_pct_of_peak": round(100 * fused_bytes / ms_f / 1e6 / PEAK_HBM_GBPS, 2),
-            "two_kernel_ms": round(ms_2, 4), "two_kernel_GBps": round(two_bytes / ms_2 / 1e6, 1),
+            "fused_ms": round(ms_f, 4), "fused_GBps": round(gbps(fused_bytes, ms_f), 1),
+            "fused_pct_of_peak": round(100 * gbps(fused_bytes, ms_f) / PEAK_HBM_GBPS, 2),
+            "two_kernel_ms": round(ms_2, 4), "two_kernel_GBps": round(gbps(two_bytes, ms_2), 1),
             "plain_ring_ms": round(ms_p, 4),
         }
         del g, e, r, ws
         torch.cuda.empty_cache()
-    # accuracy over steps (float32 gradients, 1,048,576 per rank)
     Ms = 1 << 20
     e = torch.zeros(N, Ms, device=dev)
     run_v = torch.zeros(Ms, dtype=torch.float64, device=dev)
     run_g = torch.zeros(Ms, dtype=torch.float64, device=dev)
     step_err = []
-    for t in range(10):
+    for _ in range(10):
         g = torch.randn(N, Ms, generator=gen, device=dev) * 1e-3
         exact = g.double().sum(0)
         r = torch.empty_like(g)
@@ -582,132 +1003,102 @@ def int8_ef(dev):
         step_err.append(float((r[0].double() - exact).norm() / exact.norm()))
         run_v += r[0].double()
         run_g += exact
-    resid = float(e.double().sum(0).norm())
     out["accuracy_f32_1048576"] = {
         "step_norm_rel_err": [round(x, 6) for x in step_err],
         "running_sum_norm_rel_err_after_10": float((run_v - run_g).norm() / run_g.norm()),
-        "running_sum_err_norm": float((run_v - run_g).norm()), "sum_of_last_accumulators_norm": resid}
+        "running_sum_err_norm": float((run_v - run_g).norm()),
+        "sum_of_last_accumulators_norm": float(e.double().sum(0).norm())}
     return out
 
 
-def norm_rel_err_fp64(send, recv, offsets, counts, step=1 << 24):
-    """max over ranks of ||y_r - y64|| / ||y64|| over the given element
-    ranges, y64 = the order-free fp64 sum of the inputs (a measurement of the
-    output, computed with torch on the device in slices)."""
-    import torch
-    N = send.shape[0]
-    num = torch.zeros(N, dtype=torch.float64, device=send.device)
-    den = torch.zeros((), dtype=torch.float64, device=send.device)
-    for o, c in zip(offsets, counts):
-        for a in range(o, o + c, step):
-            e = min(a + step, o + c)
-            y64 = send[:, a:e].to(torch.float64).sum(0)
-            num += ((recv[:, a:e].to(torch.float64) - y64) ** 2).sum(1)
-            den += (y64 ** 2).sum()
-    return float((num / den).sqrt().max().item())
-
-
-def workloads(dev):
-    """The other workloads, timed with inputs resident in HBM (inputs drawn on
-    the device; their parity is checked by the tests).  GB/s = algorithmic
-    bytes / time."""
-    import torch
-
-    from ring_allreduce_reduction_02_amd import ccgpu, synth
+def run_extras(path, dev, N, M, pad_bytes):
     out = {}
-    gen = torch.Generator(device=dev).manual_seed(synth.SEED)
+    for name, fn in (("pad_sweep", lambda: pad_sweep(N, M, dev)), ("alpha_beta", lambda: alpha_beta(dev)),
+                     ("schedules", lambda: schedules(dev, pad_bytes)),
+                     ("hierarchical", lambda: hierarchical(dev, pad_bytes)),
+                     ("alltoall_variants", lambda: alltoall_variants(dev)), ("int8_ef", lambda: int8_ef(dev))):
+        log(f"extras: {name}")
+        out[name] = fn()
+        with open(path, "w") as f:
+            json.dump(out, f, indent=1)
 
-    # int32 ring AllReduce, N=4, M=1,048,576 (32 MiB per call): one buffer set
-    # (cache-resident) and 64 rotating sets (2 GiB, beyond the 256 MB cache)
-    N, M = 4, 1 << 20
-    nsets = 64
-    sets = [(torch.randint(-1000, 1001, (N, M), generator=gen, device=dev, dtype=torch.int32),
-             torch.empty(N, M, device=dev, dtype=torch.int32)) for _ in range(nsets)]
-    alg = 2 * N * M * 4
-    ms1 = time_graph(lambda: ccgpu.all_reduce(sets[0][0], sets[0][1]), 10, 32)
 
-    def rot():
-        for s_, r_ in sets:
-            ccgpu.all_reduce(s_, r_)
-    msr = time_graph(rot, 10, 1) / nsets
-    host = _avg_ms(lambda: ccgpu.all_reduce(sets[0][0], sets[0][1]), 50, 10)
-    out["int32_ring_n4_m1048576"] = {"same_set_us": round(ms1 * 1e3, 2), "same_set_GBps": round(alg / ms1 / 1e6, 1),
-                                     "rotating_2GiB_us": round(msr * 1e3, 2),
-                                     "rotating_2GiB_GBps": round(alg / msr / 1e6, 1),
-                                     "eager_python_call_us": round(host * 1e3, 2),
-                                     "timing": "HIP-graph replays (GPU time); eager figure includes host launch cost"}
-    del sets
-    torch.cuda.empty_cache()
+# ---------------------------------------------------------------- rocprofv3 sections
 
-    # bucketed bf16 gradient sync, N=8, 120 tensors in 25 MiB buckets
-    N = 8
-    sizes = synth.tensor_sizes_log_uniform()
-    _, _, boff, bcnt = ccgpu.bucket_plan(sizes, 2, 25 * 1024 * 1024, 128)
-    extent = boff[-1] + bcnt[-1]
-    send = strided_ranks(N, extent, torch.bfloat16, dev)
-    send.copy_((torch.randn(N, extent, generator=gen, device=dev) * 1e-2).to(torch.bfloat16))
-    recv = strided_ranks(N, extent, torch.bfloat16, dev)
-    alg = 2 * N * sum(bcnt) * 2
-    b = {"tensors": len(sizes), "buckets": len(boff), "elements_per_rank": sum(bcnt),
-         "rank_stride_bytes": rank_stride_bytes(extent * 2)}
-    for algo in ("ring", "hd", "butterfly"):
-        ms = _avg_ms(lambda: ccgpu.all_reduce_buckets(send, recv, boff, bcnt, algo=algo))
-        b[algo] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1),
-                   "max_norm_rel_err_vs_fp64": norm_rel_err_fp64(send, recv, boff, bcnt)}
-    ms = _avg_ms(lambda: [ccgpu.all_reduce(send[:, o:o + c], recv[:, o:o + c]) for o, c in zip(boff, bcnt)], 5, 2)
-    b["ring_one_launch_per_bucket"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
-    out["bucketed_bf16_n8"] = b
-    del send, recv
-    torch.cuda.empty_cache()
-
-    # ZeRO-3 style standalone ReduceScatter then AllGather, N=16, M=33,554,432 fp32
-    N, M = 16, 1 << 25
-    S = M // N
-    send = strided_ranks(N, M, torch.float32, dev)
-    send.uniform_(-1.0, 1.0, generator=gen)
-    shard = strided_ranks(N, S, torch.float32, dev)
-    full = strided_ranks(N, M, torch.float32, dev)
-    alg = (N + 1) * M * 4
-    z = {"rank_stride_bytes": [rank_stride_bytes(M * 4), rank_stride_bytes(S * 4)]}
-    for algo in ("ring", "hd"):
-        ms = _avg_ms(lambda: ccgpu.reduce_scatter(send, shard, algo=algo))
-        z[f"reduce_scatter_{algo}"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
-    ms = _avg_ms(lambda: ccgpu.all_gather(shard, full))
-    z["all_gather"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
-    out["zero3_rs_ag_n16_m33554432_f32"] = z
-    del send, shard, full
-    torch.cuda.empty_cache()
-
-    # MoE AllToAll(v) dispatch and combine, N=8, 4096 tokens, top-8 of 64, hidden 7168 bf16
-    N, H = 8, 7168
-    C = synth.moe_counts(N)
-    Ls, Lr = int(C.sum(1).max()), int(C.sum(0).max())
-    send = torch.randn(N, Ls * H, generator=gen, device=dev).to(torch.bfloat16)
-    recv = torch.empty(N, Lr * H, device=dev, dtype=torch.bfloat16)
-    alg = 2 * int(C.sum()) * H * 2
-    m = {"rows_received": C.sum(0).tolist(), "skew_max_over_mean": round(float(C.sum(0).max() / C.sum(0).mean()), 3)}
-    for fd, name in ((0, "direct"), (1, "pairwise")):
-        ms = _avg_ms(lambda: ccgpu.all_to_all(send, recv, C.tolist(), H, fuse_depth=fd))
-        m[f"dispatch_{name}"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
-    ms = _avg_ms(lambda: ccgpu.all_to_all(recv, send, C.T.tolist(), H))
-    m["combine_direct"] = {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1)}
-    out["moe_alltoall_n8_t4096_h7168_bf16"] = m
-    del send, recv
-    torch.cuda.empty_cache()
-    return out
+def copy_probe(nbytes, dev):
+    """A plain device copy of a known size, 3 times: the kernel whose HBM
+    counters scale the profiled kernel's."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def profile_section(name, dev, steps, warmup, pad_bytes=262_144):
-    """Run one kernel of the next-row schedules `steps` times (after `warmup`)
-    for rocprofv3, and return its algorithmic bytes per call: the kernel's
-    HBM reads and writes by the schedule's definition."""
+    """Run one kernel `steps` times (after `warmup`) for rocprofv3, with the
+    workload's own inputs and layout.  Returns (algorithmic bytes per call,
+    kernel launches per call): the bytes the kernel must read and write by
+    the collective's definition."""
     import numpy as np
     import torch
 
     from ring_allreduce_reduction_02_amd import ccgpu, synth
     gen = torch.Generator(device=dev).manual_seed(20261206)
     N, M = 8, 1 << 26
-    if name in ("hier_2x2x2", "dbt_n8", "hier_8x8"):
+    launches = 1
+    if name in ("ring_f32", "ring_bf16"):
+        dt = "f32" if name == "ring_f32" else "bf16"
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        x = rank_tensor(N, M, tdt, pad_bytes, dev)
+        upload(synth.gradient_inputs(N, M, dt), x)
+        y = rank_tensor(N, M, tdt, pad_bytes, dev)
+        fn, nbytes = (lambda: ccgpu.all_reduce(x, y)), 2 * N * M * x.element_size()
+    elif name == "int32_ring_rot":
+        N, M, nsets = 4, 1 << 20, 64
+        base = strided_ranks(N, M, torch.int32, dev)
+        upload(synth.uniform_int32(synth.W_INT_RING, N, M), base)
+        sets = [(base, strided_ranks(N, M, torch.int32, dev))]
+        for _ in range(nsets - 1):
+            s_ = strided_ranks(N, M, torch.int32, dev)
+            s_.copy_(base)
+            sets.append((s_, strided_ranks(N, M, torch.int32, dev)))
+
+        def fn():
+            for s_, r_ in sets:
+                ccgpu.all_reduce(s_, r_)
+        nbytes, launches = 2 * N * M * 4 * nsets, nsets
+    elif name == "buckets_ring":
+        sizes = synth.tensor_sizes_log_uniform()
+        host, _, boff, bcnt = bucket_layout(N, sizes, synth.bucket_tensors(N, sizes))
+        x = strided_ranks(N, host.shape[1], torch.bfloat16, dev)
+        upload(host, x)
+        y = strided_ranks(N, host.shape[1], torch.bfloat16, dev)
+        fn = lambda: ccgpu.all_reduce_buckets(x, y, boff, bcnt)
+        nbytes, launches = 2 * N * sum(bcnt) * 2, (len(boff) + 15) // 16
+    elif name in ("rs_ring_n16", "ag_ring_n16"):
+        N, M = 16, 1 << 25
+        x = strided_ranks(N, M, torch.float32, dev)
+        upload(synth.uniform_f32(synth.W_ZERO3, N, M), x)
+        sh = strided_ranks(N, M // N, torch.float32, dev)
+        ccgpu.reduce_scatter(x, sh)
+        if name == "rs_ring_n16":
+            fn = lambda: ccgpu.reduce_scatter(x, sh)
+        else:
+            y = strided_ranks(N, M, torch.float32, dev)
+            fn = lambda: ccgpu.all_gather(sh, y)
+        nbytes = (N + 1) * M * 4
+    elif name == "moe_dropless":
+        H = 7168
+        C, rows = moe_inputs(N, H=H)
+        x = strided_ranks(N, int(C.sum(1).max()) * H, torch.bfloat16, dev)
+        upload([r.reshape(-1) for r in rows], x)
+        y = strided_ranks(N, int(C.sum(0).max()) * H, torch.bfloat16, dev)
+        fn = lambda: ccgpu.all_to_all(x, y, C.tolist(), H)
+        nbytes = 2 * int(C.sum()) * H * 2
+    elif name in ("hier_2x2x2", "dbt_n8", "hier_8x8"):
         pad = pad_bytes
         if name == "hier_8x8":
             N, M, pad = 64, 1 << 23, 0   # 64 ranks of 32 MiB stream best unpadded
@@ -719,18 +1110,19 @@ def profile_section(name, dev, steps, warmup, pad_bytes=262_144):
             dims = (2, 2, 2) if name == "hier_2x2x2" else (8, 8)
             fn = lambda: ccgpu.all_reduce_hierarchical(x, y, dims)
         nbytes = 2 * N * M * 4
-    elif name in ("int8_ef_f32", "int8_quant_f32", "int8_dequant_f32"):
-        g = torch.randn(N, M, generator=gen, device=dev) * 1e-3
+    elif name in ("int8_ef_f32", "int8_ef_bf16", "int8_quant_f32", "int8_dequant_f32"):
+        tdt = torch.bfloat16 if name == "int8_ef_bf16" else torch.float32
+        g = (torch.randn(N, M, generator=gen, device=dev) * 1e-3).to(tdt)
         e = torch.zeros(N, M, device=dev)
         r = torch.empty_like(g)
         q = torch.empty(N, M, dtype=torch.int8, device=dev)
         sc = torch.empty(N, M // 128, device=dev)
-        ccgpu.quantize_ef(g, e, q, sc)
-        if name == "int8_ef_f32":
-            fn, nbytes = (lambda: ccgpu.all_reduce_int8_ef(g, e, r)), N * M * 16
+        if name in ("int8_ef_f32", "int8_ef_bf16"):
+            fn, nbytes = (lambda: ccgpu.all_reduce_int8_ef(g, e, r)), N * M * (2 * g.element_size() + 8)
         elif name == "int8_quant_f32":
             fn, nbytes = (lambda: ccgpu.quantize_ef(g, e, q, sc)), N * M * 13 + N * (M // 128) * 4
         else:
+            ccgpu.quantize_ef(g, e, q, sc)
             fn, nbytes = (lambda: ccgpu.all_reduce_dequant(q, sc, r)), N * M * 5 + N * (M // 128) * 4
     elif name == "moe_padded_c125":
         H, T, K, E = 7168, 4096, 8, 64
@@ -749,8 +1141,15 @@ def profile_section(name, dev, steps, warmup, pad_bytes=262_144):
     for _ in range(steps):
         fn()
     torch.cuda.synchronize()
-    return nbytes
+    return nbytes, launches
 
+
+PROFILE_SECTIONS = ("ring_f32, ring_bf16, int32_ring_rot, buckets_ring, rs_ring_n16, ag_ring_n16, moe_dropless, "
+                    "hier_2x2x2, hier_8x8, dbt_n8, int8_ef_f32, int8_ef_bf16, int8_quant_f32, int8_dequant_f32, "
+                    "moe_padded_c125")
+
+
+# ---------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -764,17 +1163,16 @@ def main():
     ap.add_argument("--fuse-depth", type=int, default=0)
     ap.add_argument("--pad-bytes", type=int, default=262_144)
     ap.add_argument("--blocks-per-cu", type=int, default=0, help="occupancy cap passed to the library (0 = its default)")
-    ap.add_argument("--cpu-sample", type=int, default=67_108_864)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true",
-                    help="skip the bf16 twin, the alpha-beta calibration and the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle on the host (and with it the parity verdict of the headline)")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the records of the other workloads")
+    ap.add_argument("--no-twin", action="store_true", help="skip the bf16 twin and the alpha-beta fit")
+    ap.add_argument("--extras", default="", metavar="PATH", help="also run the long sweeps and write them to PATH")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="before timing, run a plain device copy of this many bytes 3 times "
                          "(a known-size kernel for scaling HBM counters)")
     ap.add_argument("--profile-section", default="",
-                    help="run only this kernel of the next-row schedules --steps times (for rocprofv3): "
-                         "hier_2x2x2, hier_8x8, dbt_n8, int8_ef_f32, int8_quant_f32, int8_dequant_f32, "
-                         "moe_padded_c125")
+                    help="run only this kernel --steps times (for rocprofv3): " + PROFILE_SECTIONS)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -782,10 +1180,9 @@ def main():
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from ring_allreduce_reduction_02_amd import ccgpu, synth
+    from ring_allreduce_reduction_02_amd import ccgpu
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -794,129 +1191,37 @@ def main():
     dev = "cuda:0"
     if args.profile_section:
         if args.copy_probe_bytes:
-            a = torch.empty(args.copy_probe_bytes, dtype=torch.uint8, device=dev).fill_(1)
-            b = torch.empty_like(a)
-            for _ in range(3):
-                b.copy_(a)
-            torch.cuda.synchronize()
-            del a, b
-        nbytes = profile_section(args.profile_section, dev, args.steps, args.warmup, args.pad_bytes)
-        print(json.dumps({"profile_section": args.profile_section, "alg_bytes_per_call": nbytes}), flush=True)
+            copy_probe(args.copy_probe_bytes, dev)
+        nbytes, launches = profile_section(args.profile_section, dev, args.steps, args.warmup, args.pad_bytes)
+        emit({"profile_section": args.profile_section, "alg_bytes_per_call": nbytes, "launches_per_call": launches,
+              "alg_bytes_per_launch": nbytes // launches})
         return
-    N, M = args.ranks, args.count
-    tdt = torch.float32 if args.dtype == "f32" else torch.bfloat16
-    es = 4 if args.dtype == "f32" else 2
-    log(f"generating {N} x {M} {args.dtype} synthetic gradients")
-    xs = synth.gradient_inputs(N, M, args.dtype)
-    send = rank_tensor(N, M, tdt, args.pad_bytes, dev)
-    recv = rank_tensor(N, M, tdt, args.pad_bytes, dev)
-    upload(xs, send)
-    del xs
-    ws = ccgpu.make_workspace("all_reduce", N, M, args.dtype, args.algo, args.fuse_depth, dev)
-    if args.copy_probe_bytes:
-        a = torch.empty(args.copy_probe_bytes, dtype=torch.uint8, device=dev).fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
 
-    def step():
-        ccgpu.all_reduce(send, recv, op="sum", algo=args.algo, fuse_depth=args.fuse_depth, workspace=ws,
-                         blocks_per_cu=args.blocks_per_cu)
-
-    log("timing")
-    # the K timed steps run back to back; the per-launch durations behind the
-    # roofline come from a second, instrumented pass of K launches (an event
-    # pair around every launch adds about 5 us per step to the first)
-    res = time_steps(step, args.steps, args.warmup)
-    ms_per_step = res["total_ms"] / args.steps
-    alg_bytes = 2 * N * M * es
-    value = alg_bytes / (ms_per_step / 1e3) / 1e9
-    per = time_launches(step, args.steps, 2)["per_launch_ms"]
-    avg_launch_ms = sum(per) / len(per)
-    achieved = alg_bytes / (avg_launch_ms / 1e3) / 1e9
-    busbw = (M * es) / (ms_per_step / 1e3) * 2 * (N - 1) / N / 1e9
-    traffic, traffic_src = traffic_from_profile(alg_bytes)
-    kname = {"ring": "k_ring_fused", "hd": "k_tree_fused", "butterfly": "k_tree_fused"}[args.algo]
-    if args.fuse_depth:
-        kname = "stepwise schedule (several kernels per step)"
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": args.dtype,
-        "data": "synthetic",
-        "config": {
-            "workload": f"ring_allreduce_sum_n{N}_m{M}_{args.dtype}",
-            "nranks": N,
-            "count_per_rank": M,
-            "algo": args.algo,
-            "fuse_depth": args.fuse_depth,
-            "blocks_per_cu": args.blocks_per_cu,
-            "rank_stride_bytes": send.stride(0) * es,
-            "values": "Gaussian, sigma=1e-3" + (" (bf16 rounding of the fp32 samples)" if args.dtype == "bf16" else ""),
-            "parallelism": f"{N} logical ranks in one GPU's HBM",
-        },
-        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
-        "busbw_GBps": round(busbw, 2),
-        "algorithmic_bytes_per_step": alg_bytes,
-        "roofline": {
-            "bound": "hbm",
-            "kernel": kname,
-            "achieved": round(achieved, 2),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": traffic,
-            "traffic_source": traffic_src,
-            "traffic_over_algorithmic": round(traffic / alg_bytes, 4) if traffic else None,
-            "avg_launch_ms": round(avg_launch_ms, 5),
-            "median_launch_ms": round(sorted(per)[len(per) // 2], 5),
-            "min_launch_ms": round(min(per), 5),
-        },
-    }
-    if not args.no_extras and args.dtype == "f32" and args.algo == "ring" and args.fuse_depth == 0:
-        log("rank-stride pad sweep")
-        out["pad_sweep"] = pad_sweep(send, N, M, dev)
-        log("bf16 twin")
-        xb = synth.gradient_inputs(N, M, "bf16")
-        sb = rank_tensor(N, M, torch.bfloat16, args.pad_bytes, dev)
-        rb = rank_tensor(N, M, torch.bfloat16, args.pad_bytes, dev)
-        upload(xb, sb)
-        del xb
-        rb16 = time_steps(lambda: ccgpu.all_reduce(sb, rb, algo="ring", fuse_depth=0), args.steps, args.warmup)
-        ms16 = rb16["total_ms"] / args.steps
-        out["bf16_twin"] = {"ms_per_step": round(ms16, 5),
-                            "GBps": round(2 * N * M * 2 / (ms16 / 1e3) / 1e9, 2),
-                            "pct_of_peak": round(100 * 2 * N * M * 2 / (ms16 / 1e3) / 1e9 / PEAK_HBM_GBPS, 2)}
-        del sb, rb
-        torch.cuda.empty_cache()
-        del send, recv, ws
-        torch.cuda.empty_cache()
-        log("alpha-beta calibration")
-        out["alpha_beta"] = alpha_beta(dev)
-        log("other workloads")
-        out["workloads"] = workloads(dev)
-        log("schedules")
-        out["schedules"] = schedules(dev, args.pad_bytes)
-        log("hierarchical")
-        out["hierarchical"] = hierarchical(dev, args.pad_bytes)
-        log("alltoall variants")
-        out["alltoall_variants"] = alltoall_variants(dev)
-        log("int8 error feedback")
-        out["int8_ef"] = int8_ef(dev)
+    m = run_headline(args, dev)
+    roof = roofline_of(m, args)
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        log("oracle on the host")
-        out["cpu_baseline"] = cpu_baseline(N, min(args.cpu_sample, M))
-    print(json.dumps(out), flush=True)
+        log("oracle on the host (cpu baseline and parity of the timed output)")
+        rec, exp = cpu_baseline(m["xs"], args.dtype)
+        parity = all(same_bits(m["got"][r], exp[r]) for r in range(m["N"]))
+        cpu = rec
+        del exp
+    m["xs"] = m["got"] = None
+    twin = ab = None
+    if not args.no_twin and args.dtype == "f32":
+        log("bf16 twin")
+        twin = bf16_twin(args, dev)
+        log("alpha-beta fit at N=8")
+        ab = alpha_beta_n8(dev, args.pad_bytes)
+    if not args.no_workloads:
+        for name, fn in (("int32 ring", rec_int32_ring), ("buckets", rec_buckets), ("zero3", rec_zero3),
+                         ("moe", rec_moe)):
+            log(f"workload: {name}")
+            emit(fn(dev))
+    if args.extras:
+        run_extras(args.extras, dev, m["N"], m["M"], args.pad_bytes)
+    line = headline_line(make_headline(m, args, roof, twin, ab, cpu, parity))
+    print(line, flush=True)
 
 
 if __name__ == "__main__":
