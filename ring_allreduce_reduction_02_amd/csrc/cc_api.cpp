@@ -122,8 +122,12 @@ using namespace cc::api;
 
 namespace {
 
+// A launch covers num_tiles workgroups of kBlock threads: the grid's x size
+// must fit 31 bits and its work-items 32 bits (HIP rejects a larger launch).
 cc_status_t grid_fits(uint64_t M, int dt) {
-  if (num_tiles(M, dt) > 0x7fffffffull) return fail(CC_ERR_INVALID_ARG, "count too large for one launch");
+  const uint64_t tiles = num_tiles(M, dt);
+  if (tiles > 0x7fffffffull || tiles * (uint64_t)kBlock > 0xffffffffull)
+    return fail(CC_ERR_INVALID_ARG, "count too large for one launch");
   return CC_OK;
 }
 
@@ -191,13 +195,26 @@ uint64_t ws_need_data(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M,
   return 0;
 }
 
-cc_status_t check_ws(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt) {
-  const uint64_t need = ws_need(coll, cfg, N, M, dt);
+// The `need` bytes of workspace the call will use must be given and must
+// share no byte with the send (N x sbytes) or recv (N x rbytes) buffers: the
+// stepwise schedules write partial results there, grid_sync its queue words.
+cc_status_t check_ws_bytes(const cc_config_t& cfg, uint64_t need, const char* sizer, const cc_rankbuf_t& send,
+                           uint64_t sbytes, const cc_rankbuf_t& recv, uint64_t rbytes, int N) {
   if (need == 0) return CC_OK;
   if (cfg.workspace == nullptr || cfg.workspace_bytes < need)
-    return fail(CC_ERR_INVALID_ARG,
-                "this schedule needs %llu bytes of workspace (cc_workspace_size); got %zu",
-                (unsigned long long)need, cfg.workspace ? cfg.workspace_bytes : (size_t)0);
+    return fail(CC_ERR_INVALID_ARG, "this schedule needs %llu bytes of workspace (%s); got %zu",
+                (unsigned long long)need, sizer, cfg.workspace ? cfg.workspace_bytes : (size_t)0);
+  const cc_rankbuf_t ws{cfg.workspace, (size_t)need};
+  if (sides_overlap(ws, need, 1, send, sbytes, N) || sides_overlap(ws, need, 1, recv, rbytes, N))
+    return fail(CC_ERR_INVALID_ARG, "the workspace overlaps the send or recv buffers");
+  return CC_OK;
+}
+
+cc_status_t check_ws(cc_coll_t coll, const cc_config_t& cfg, int N, uint64_t M, int dt, const cc_rankbuf_t& send,
+                     uint64_t sbytes, const cc_rankbuf_t& recv, uint64_t rbytes) {
+  const uint64_t need = ws_need(coll, cfg, N, M, dt);
+  cc_status_t s = check_ws_bytes(cfg, need, "cc_workspace_size", send, sbytes, recv, rbytes, N);
+  if (s || need == 0) return s;
   if (uses_barrier(cfg, N) && ((uintptr_t)cfg.workspace & 15u))
     return fail(CC_ERR_INVALID_ARG, "grid_sync needs a 16-byte aligned workspace");
   return CC_OK;
@@ -369,7 +386,7 @@ cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc
   if (!in_place && sides_overlap(send, nb, N, recv, nb, N))
     return fail(CC_ERR_INVALID_ARG, "send and recv overlap without being the same buffers");
   if ((s = grid_fits(M, dt))) return s;
-  if ((s = check_ws(CC_COLL_ALL_REDUCE, cfg, N, M, dt))) return s;
+  if ((s = check_ws(CC_COLL_ALL_REDUCE, cfg, N, M, dt, send, nb, recv, nb))) return s;
   if ((s = device_ready())) return s;
   return run_all_reduce(send, recv, M, dt, (int)op, N, cfg, (hipStream_t)stream);
 }
@@ -446,7 +463,7 @@ cc_status_t cc_all_reduce_buckets(cc_rankbuf_t send, cc_rankbuf_t recv, const si
   if (s) return s;
   if ((int)op < 0 || (int)op > 2) return fail(CC_ERR_INVALID_ARG, "unknown op %d", (int)op);
   const int N = nranks, dt = (int)dtype, es = elem_size(dt);
-    if (nbuckets < 0) return fail(CC_ERR_INVALID_ARG, "nbuckets=%d is negative", nbuckets);
+  if (nbuckets < 0) return fail(CC_ERR_INVALID_ARG, "nbuckets=%d is negative", nbuckets);
   if (nbuckets == 0) return ok();
   if (!offsets || !counts) return fail(CC_ERR_INVALID_ARG, "offsets or counts is NULL");
   // buckets: non-empty ranges, pairwise disjoint, within every rank buffer
@@ -471,7 +488,7 @@ cc_status_t cc_all_reduce_buckets(cc_rankbuf_t send, cc_rankbuf_t recv, const si
   if (!in_place && sides_overlap(send, nb, N, recv, nb, N))
     return fail(CC_ERR_INVALID_ARG, "send and recv overlap without being the same buffers");
   if ((s = grid_fits(maxlen, dt))) return s;
-  if ((s = check_ws(CC_COLL_ALL_REDUCE, cfg, N, maxlen, dt))) return s;
+  if ((s = check_ws(CC_COLL_ALL_REDUCE, cfg, N, maxlen, dt, send, nb, recv, nb))) return s;
   if ((s = device_ready())) return s;
   hipStream_t st = (hipStream_t)stream;
   auto sub = [&](const cc_rankbuf_t& x, uint64_t off) {
@@ -558,7 +575,7 @@ cc_status_t cc_reduce_scatter(cc_rankbuf_t send, cc_rankbuf_t recv, size_t recvc
   if ((s = check_side(send, M * es, N, "send")) || (s = check_side(recv, S * es, N, "recv"))) return s;
   if (sides_overlap(send, M * es, N, recv, S * es, N)) return fail(CC_ERR_INVALID_ARG, "send and recv overlap");
   if ((s = grid_fits(M, dt))) return s;
-  if ((s = check_ws(CC_COLL_REDUCE_SCATTER, cfg, N, M, dt))) return s;
+  if ((s = check_ws(CC_COLL_REDUCE_SCATTER, cfg, N, M, dt, send, M * es, recv, S * es))) return s;
   if ((s = device_ready())) return s;
   hipStream_t st = (hipStream_t)stream;
   if (N == 1) return copy_ranks(send, recv, S * es, 1, es, cfg.blocks_per_cu, st);
@@ -789,10 +806,8 @@ cc_status_t cc_all_reduce_hierarchical(cc_rankbuf_t send, cc_rankbuf_t recv, siz
   if (!same_side(send, recv) && sides_overlap(send, nb, N, recv, nb, N))
     return fail(CC_ERR_INVALID_ARG, "send and recv overlap without being the same buffers");
   if ((s = grid_fits(M, dt))) return s;
-  const uint64_t need = hier_ws(h, cfg, M, dt);
-  if (need && (cfg.workspace == nullptr || cfg.workspace_bytes < need))
-    return fail(CC_ERR_INVALID_ARG, "this schedule needs %llu bytes of workspace (cc_hierarchical_workspace_size); got %zu",
-                (unsigned long long)need, cfg.workspace ? cfg.workspace_bytes : (size_t)0);
+  if ((s = check_ws_bytes(cfg, hier_ws(h, cfg, M, dt), "cc_hierarchical_workspace_size", send, nb, recv, nb, N)))
+    return s;
   if ((s = device_ready())) return s;
   hipStream_t st = (hipStream_t)stream;
   if (N == 1 || hier_flat(h)) return run_all_reduce(send, recv, M, dt, (int)op, N, cfg, st);

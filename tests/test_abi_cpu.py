@@ -216,3 +216,39 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         ccgpu.rankbuf(torch.zeros(2, 3))
+
+
+@no_gpu_only
+def test_workspace_must_not_overlap_send_or_recv():
+    """A workspace that shares bytes with a rank buffer is refused before any
+    launch (the stepwise schedules write partials there, grid_sync its queue
+    words); one beside the buffers passes validation."""
+    L = ccgpu.load()
+    s, r = _rb(FAKE, 4096), _rb(FAKE + (1 << 30), 4096)
+    need = 512 + 400                        # grid_sync queue words + bf16 partials of 100 elements
+    for ws in (FAKE + 4096 * 3, FAKE + (1 << 30) + 16, FAKE - 256):   # inside send rank 3, recv rank 0, ends in send rank 0
+        c = ccgpu.Config(0, 1, ws, need, 0, 1)
+        assert _ar(s, r, 100, 8, dtype=2, cfg=c) == ccgpu.CC_ERR_INVALID_ARG, hex(ws)
+        assert "overlap" in L.cc_last_error().decode()
+    assert _ar(s, r, 100, 8, dtype=2, cfg=ccgpu.Config(0, 1, FAKE + (2 << 30), need, 0, 1)) == ccgpu.CC_ERR_NO_DEVICE
+    # between two ranks' payloads (the rows are 200 B of a 4096 B stride) is not an overlap
+    gap = ccgpu.Config(0, 1, FAKE + 1024, need, 0, 1)
+    assert _ar(s, r, 100, 8, dtype=2, cfg=gap) == ccgpu.CC_ERR_NO_DEVICE
+    # reduce_scatter (stepwise ring partials) and the hierarchical AllReduce (bf16 partials)
+    c = ccgpu.Config(0, 1, FAKE + 64, 1 << 20, 0)
+    assert L.cc_reduce_scatter(s, r, 10, 1, 0, 4, ctypes.byref(c), None) == ccgpu.CC_ERR_INVALID_ARG
+    dims = (ctypes.c_int * 2)(2, 2)
+    c = ccgpu.Config(0, 1, FAKE + (1 << 30) + 8192, 1 << 20, 0)
+    assert L.cc_all_reduce_hierarchical(s, r, 100, 2, 0, 2, dims, ctypes.byref(c), None) == ccgpu.CC_ERR_INVALID_ARG
+    c = ccgpu.Config(0, 1, FAKE + (2 << 30), 1 << 20, 0)
+    assert L.cc_all_reduce_hierarchical(s, r, 100, 2, 0, 2, dims, ctypes.byref(c), None) == ccgpu.CC_ERR_NO_DEVICE
+
+
+@no_gpu_only
+def test_grid_larger_than_32_bit_work_items_is_refused():
+    """num_tiles * 128 work-items must fit 32 bits: 2^25 tiles of 512 fp32
+    elements is the first count refused, one tile less passes."""
+    s, r = _rb(FAKE, 1 << 40), _rb(FAKE + (1 << 44), 1 << 40)
+    limit = ((1 << 32) // 128) * 512          # elements in 2^25 tiles of 512
+    assert _ar(s, r, limit, 1, dtype=1) == ccgpu.CC_ERR_INVALID_ARG
+    assert _ar(s, r, limit - 512, 1, dtype=1) == ccgpu.CC_ERR_NO_DEVICE

@@ -8,8 +8,9 @@ import numpy as np
 import pytest
 import torch
 
+import bench
 from oracle import ccsim as cs
-from ring_allreduce_reduction_02_amd import ccgpu, synth
+from ring_allreduce_reduction_02_amd import ccgpu
 from tests.gpu_util import DEV
 
 pytestmark = pytest.mark.gpu
@@ -23,49 +24,45 @@ def say(*a):
 
 @pytest.fixture(scope="module")
 def moe():
-    C = synth.moe_counts(N)
+    """Counts and tagged bf16 rows of the seeded synth inputs, in the layout
+    bench.py times."""
+    C, rows = bench.moe_inputs(N, H=H)
     rows_out = C.sum(axis=1)
     rows_in = C.sum(axis=0)
     Ls, Lr = int(rows_out.max()), int(rows_in.max())
     say(f"moe counts: rows sent {rows_out.tolist()}, received {rows_in.tolist()}, "
         f"skew {rows_in.max() / rows_in.mean():.2f}")
-    gen = torch.Generator(device=DEV).manual_seed(synth.SEED + 5)
-    send = torch.randn(N, Ls, H, generator=gen, device=DEV).to(torch.bfloat16)
-    tag = send.view(torch.int16)
-    rid = torch.arange(Ls, device=DEV, dtype=torch.int32)
-    for i in range(N):
-        tag[i, :, 0] = i
-        tag[i, :, 1] = (rid & 0xFFFF).to(torch.int16)
-        tag[i, :, 2] = (rid >> 16).to(torch.int16)
-    return C, send, Ls, Lr
+    send = bench.strided_ranks(N, Ls * H, torch.bfloat16, DEV)
+    bench.upload([r.reshape(-1) for r in rows], send)
+    yield C, rows, send, Ls, Lr
+    del send
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("fd", [0, 1])
 def test_moe_dispatch_and_combine(moe, fd):
-    C, send, Ls, Lr = moe
-    recv = torch.empty(N, Lr, H, dtype=torch.bfloat16, device=DEV)
+    C, rows, send, Ls, Lr = moe
+    recv = bench.strided_ranks(N, Lr * H, torch.bfloat16, DEV).fill_(float("nan"))
     say(f"dispatch fd={fd}")
-    ccgpu.all_to_all(send.view(N, -1), recv.view(N, -1), C.tolist(), H, fuse_depth=fd)
+    ccgpu.all_to_all(send, recv, C.tolist(), H, fuse_depth=fd)
     torch.cuda.synchronize()
-    # expected (source, row) of every received row, from the oracle
-    ids = [np.stack([np.full(int(C[i].sum()), i), np.arange(int(C[i].sum()))], 1).reshape(-1) for i in range(N)]
-    exp = cs.all_to_all(ids, C, row=2)
-    tags = recv.view(torch.int16)[:, :, :3].to(torch.int32).cpu().numpy()
+    got = bench.download(recv)
+    exp = cs.all_to_all([r.reshape(-1) for r in rows], C, row=H)
     for j in range(N):
-        e = exp[j].reshape(-1, 2)
-        n = len(e)
-        got_src = tags[j, :n, 0]
-        got_row = (tags[j, :n, 1] & 0xFFFF) | (tags[j, :n, 2] << 16)
-        assert np.array_equal(got_src, e[:, 0]) and np.array_equal(got_row, e[:, 1]), j
-        # every byte of every row equals its source row
-        src = torch.from_numpy(e[:, 0]).to(DEV)
-        row = torch.from_numpy(e[:, 1]).to(DEV)
-        want = send[src, row]
-        assert torch.equal(recv[j, :n].view(torch.int16), want.view(torch.int16)), j
+        n = len(exp[j])
+        assert np.array_equal(got[j, :n], exp[j]), j
+        # the tags name the (source, row) the oracle's transpose puts there
+        tags = got[j, :n].reshape(-1, H)[:, :3].astype(np.int64)
+        src = np.repeat(np.arange(N), C[:, j])
+        first = np.cumsum(C, axis=1)[:, j] - C[:, j]          # block (i, j)'s first send row
+        row = np.concatenate([np.arange(first[i], first[i] + C[i, j]) for i in range(N)])
+        assert np.array_equal(tags[:, 0], src) and np.array_equal(tags[:, 1] | (tags[:, 2] << 16), row), j
+    del got
     say(f"combine fd={fd}")
-    back = torch.zeros_like(send)
-    ccgpu.all_to_all(recv.view(N, -1), back.view(N, -1), C.T.tolist(), H, fuse_depth=fd)
+    back = bench.strided_ranks(N, Ls * H, torch.bfloat16, DEV).fill_(float("nan"))
+    ccgpu.all_to_all(recv, back, C.T.tolist(), H, fuse_depth=fd)
     torch.cuda.synchronize()
+    got = bench.download(back)
     for i in range(N):
-        n = int(C[i].sum())
-        assert torch.equal(back[i, :n].view(torch.int16), send[i, :n].view(torch.int16)), i
+        n = rows[i].size
+        assert np.array_equal(got[i, :n], rows[i].reshape(-1)), i

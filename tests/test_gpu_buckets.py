@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import bench
 from oracle import ccsim as cs
 from ring_allreduce_reduction_02_amd import ccgpu, synth
 from tests.gpu_util import DEV, bits, np_to_torch, torch_to_np
@@ -94,34 +95,33 @@ def test_buckets_equal_separate_all_reduces():
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), algo
 
 
-def test_full_bucket_workload_sampled():
+@pytest.fixture(scope="module")
+def full_buckets():
     """The 120-tensor, 25 MiB-bucket workload at full size (about 480 MiB of
-    bf16 per rank); inputs drawn on the device, outputs checked at sampled
-    positions of every bucket against the oracle's fold."""
+    bf16 per rank) from the seeded synth inputs, in the layout bench.py times."""
     N = 8
     sizes = synth.tensor_sizes_log_uniform()
-    bof, toff, boff, bcnt = ccgpu.bucket_plan(sizes, 2, CAP, 128)
-    extent = boff[-1] + bcnt[-1]
-    say(f"full bucket workload: {len(boff)} buckets, {extent} bf16 per rank")
-    gen = torch.Generator(device=DEV).manual_seed(synth.SEED)
-    send = (torch.randn(N, extent, generator=gen, device=DEV) * 1e-2).to(torch.bfloat16)
-    recv = torch.empty_like(send)
-    rng = np.random.default_rng(9)
-    for algo in ("ring", "hd", "butterfly"):
-        ccgpu.all_reduce_buckets(send, recv, boff, bcnt, algo=algo)
-        torch.cuda.synchronize()
-        for o, c in zip(boff, bcnt):
-            b = np.array(cs.chunk_bounds(c, N))
-            rel = np.unique(np.concatenate([rng.integers(0, c, size=200), b[1:-1], b[1:-1] - 1, [0, c - 1]]))
-            rel = rel[(rel >= 0) & (rel < c)]
-            idx = torch.from_numpy(o + rel).to(DEV)
-            vals = torch_to_np(send.index_select(1, idx), "bf16")
-            got = torch_to_np(recv.index_select(1, idx), "bf16")
-            if algo == "ring":
-                exp = cs.ring_fold_elements(vals, rel, c, "sum", "bf16")
-            elif algo == "hd":
-                exp = cs.hd_fold_elements(vals, rel, c, "sum", "bf16")
-            else:
-                exp = cs.butterfly_fold_elements(vals, 0, "sum", "bf16")
-            for r in range(N):
-                assert np.array_equal(got[r], exp), (algo, o, r)
+    say("generating the full bucket workload")
+    tensors = synth.bucket_tensors(N, sizes)
+    host, toff, boff, bcnt = bench.bucket_layout(N, sizes, tensors)
+    send = bench.strided_ranks(N, host.shape[1], torch.bfloat16, DEV)
+    bench.upload(host, send)
+    del host
+    yield N, sizes, tensors, toff, boff, bcnt, send
+    del send
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("algo", ["ring", "hd", "butterfly"])
+def test_full_bucket_workload_whole(full_buckets, algo):
+    """Every element of every tensor of every rank against the oracle's
+    per-bucket AllReduce of the same tensors."""
+    N, sizes, tensors, toff, boff, bcnt, send = full_buckets
+    say(f"full bucket workload {algo}: {len(boff)} buckets, {boff[-1] + bcnt[-1]} bf16 per rank")
+    recv = bench.strided_ranks(N, send.shape[1], torch.bfloat16, DEV).fill_(float("nan"))
+    ccgpu.all_reduce_buckets(send, recv, boff, bcnt, algo=algo)
+    torch.cuda.synchronize()
+    got = bench.download(recv)
+    del recv
+    expect = cs.bucketed_all_reduce(tensors, cs.bucket_pack(sizes, 2, CAP), algo, "sum", "bf16")
+    check(got, tensors, toff, expect, f"full {algo}")
