@@ -170,6 +170,26 @@ typedef void* cc_stream_t;
 cc_status_t cc_all_reduce(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype,
                           cc_op_t op, int nranks, const cc_config_t* cfg, cc_stream_t stream);
 
+/* cc_all_reduce for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same collective, schedules, bits and errors as cc_all_reduce, but the
+ * staging a schedule needs (cc_workspace_size: the queue words of grid_sync,
+ * the fp32 partials of bf16 stepwise schedules) comes from a fixed array of
+ * CC_NOALLOC_SCRATCH_BYTES inside the library instead of cfg->workspace.
+ * Each GPU the library runs on holds its own copy of that array until the
+ * process ends; the call itself allocates nothing.  cfg->workspace must be
+ * NULL and cfg->workspace_bytes 0 (CC_ERR_INVALID_ARG otherwise); a schedule
+ * needing more than CC_NOALLOC_SCRATCH_BYTES returns CC_ERR_INVALID_ARG
+ * (cc_all_reduce with a workspace serves it).  Every call on one GPU shares
+ * that GPU's array and the array keeps the last call's contents (the kernels
+ * clear what must start at zero): calls that overlap in time on one GPU --
+ * on different streams, or from different threads -- race and give undefined
+ * results.  Schedules that need no staging (every fused schedule) never touch
+ * the array. */
+#define CC_NOALLOC_SCRATCH_BYTES (16u << 20)
+cc_status_t cc_all_reduce_noalloc(cc_rankbuf_t send, cc_rankbuf_t recv, size_t count, cc_dtype_t dtype,
+                                  cc_op_t op, int nranks, const cc_config_t* cfg, cc_stream_t stream);
+
 /* ReduceScatter: send holds nranks*recvcount elements per rank; rank r's recv
  * (recvcount elements) gets the reduction of chunk r over all ranks (slides
  * "Scatter 与 ReduceScatter").  send and recv must not overlap.  Schedules:

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcc.so")
 
 SOURCES = [os.path.join(CSRC, "cc_kernels.hip"), os.path.join(CSRC, "cc_api.cpp"), os.path.join(CSRC, "cc_sched.cpp"),
-           os.path.join(CSRC, "cc_alltoall.cpp"), os.path.join(CSRC, "cc_compress.cpp")]
+           os.path.join(CSRC, "cc_alltoall.cpp"), os.path.join(CSRC, "cc_compress.cpp"),
+           os.path.join(CSRC, "cc_noalloc.hip")]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -59,6 +59,8 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTS = {
     "cc_all_reduce": [RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                       ctypes.POINTER(Config), ctypes.c_void_p],
+    "cc_all_reduce_noalloc": [RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                              ctypes.POINTER(Config), ctypes.c_void_p],
     "cc_reduce_scatter": [RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                           ctypes.POINTER(Config), ctypes.c_void_p],
     "cc_all_gather": [RankBuf, RankBuf, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
@@ -218,6 +220,22 @@ def all_reduce(send, recv=None, op: str = "sum", algo: str = "ring", fuse_depth:
     cfg = config(algo, fuse_depth, workspace, blocks_per_cu, grid_sync)
     _check(load().cc_all_reduce(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], OPS[op], N,
                                 ctypes.byref(cfg), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def all_reduce_noalloc(send, recv=None, op: str = "sum", algo: str = "ring", fuse_depth: int = 0,
+                       stream=None, blocks_per_cu: int = 0, grid_sync: bool = False) -> None:
+    """all_reduce with the schedule's staging in the library's fixed scratch
+    (cc_all_reduce_noalloc): no workspace argument, nothing allocated."""
+    recv = send if recv is None else recv
+    N, M = send.shape
+    if tuple(recv.shape) != (N, M) or recv.dtype != send.dtype:
+        raise ValueError("recv must match send")
+    cfg = config(algo, fuse_depth, None, blocks_per_cu, grid_sync)
+    _check(load().cc_all_reduce_noalloc(rankbuf(send), rankbuf(recv), M, DTYPES[dtype_name(send)], OPS[op], N,
+                                        ctypes.byref(cfg), _stream(stream)))
 
 
 def all_reduce_plan(algo: str, nranks: int, count: int):
