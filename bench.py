@@ -26,7 +26,6 @@ with error feedback) to PATH as one JSON document.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -38,7 +37,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (% of peak) + simulated busbw for N-rank ring AllReduce"
-KERNEL_SRC = os.path.join(ROOT, "ring_allreduce_reduction_02_amd", "csrc", "cc_kernels.hip")
 PMC_FILE = os.path.join(ROOT, "profiles", "ring_fused_f32_n8_m67108864_pmc.json")
 HEADLINE_MAX_BYTES = 2048
 BUCKET_CAP_BYTES = 25 * 1024 * 1024
@@ -50,11 +48,6 @@ def log(*a):
 
 def emit(rec: dict) -> None:
     print(json.dumps(rec, separators=(",", ":")), flush=True)
-
-
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 # ---------------------------------------------------------------- layout
@@ -227,7 +220,8 @@ def traffic_from_profile(pmc_file=PMC_FILE):
         return None, "no counter file"
     with open(pmc_file) as f:
         p = json.load(f)
-    if p.get("kernel_source_sha256_16") != kernel_source_hash():
+    from ring_allreduce_reduction_02_amd.profsum import sources_hash
+    if not p.get("kernel_sources") or p.get("kernel_source_sha256_16") != sources_hash(p["kernel_sources"]):
         return None, "kernel changed since the counters were taken"
     fetch = p["fetch_kib_per_dispatch"] * 1024.0 * p["fetch_scale"]
     write = p["write_kib_per_dispatch"] * 1024.0 * p["write_scale"]
@@ -282,9 +276,11 @@ def cpu_baseline(xs, dtype, min_seconds=10.0):
     N, M = len(xs), len(xs[0])
     es = 4 if dtype == "f32" else 2
     t, runs, total, out = oracle_run(lambda: cs.ring_all_reduce(xs, "sum", dtype), min_seconds)
+    h = host_info()
     rec = {"value": round(2 * N * M * es / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"the whole workload (ring AllReduce SUM, N={N}, M={M} {dtype}), step-explicit NumPy "
-                     f"simulator, single-threaded; {runs} runs in {total:.1f} s, median {t:.3f} s"}
+                     f"simulator, single-threaded; {runs} runs in {total:.1f} s, median {t:.3f} s",
+           "host": f"{h['cpu_model']}, {h['host_logical_cpus']} logical CPUs, {h['affinity_cpus']} in affinity"}
     return rec, out
 
 
@@ -347,6 +343,7 @@ def bf16_twin(args, dev):
     torch.cuda.empty_cache()
     if got is not None:
         cs = _oracle()
+        log("  oracle: bf16 ring AllReduce")
         t, _, _, exp = oracle_run(lambda: cs.ring_all_reduce(xb, "sum", "bf16"))
         out["parity"] = all(same_bits(got[r], exp[r]) for r in range(N))
         out["oracle_s"] = round(t, 3)
@@ -509,6 +506,7 @@ def rec_buckets(dev):
     from ring_allreduce_reduction_02_amd import ccgpu, synth
     N = 8
     sizes = synth.tensor_sizes_log_uniform()
+    log("  generating 120 tensors per rank")
     tensors = synth.bucket_tensors(N, sizes)
     host, toff, boff, bcnt = bucket_layout(N, sizes, tensors)
     extent = host.shape[1]
@@ -521,15 +519,19 @@ def rec_buckets(dev):
     ref_buckets = cs.bucket_pack(sizes, 2, BUCKET_CAP_BYTES)
     out = {"section": "bucketed_bf16_n8_120_tensors", "dtype": "bf16", "tensors": len(sizes), "buckets": len(boff),
            "elements_per_rank": sum(bcnt), "rank_stride_bytes": send.stride(0) * 2}
-    for algo in ("ring", "hd", "butterfly"):
+    for algo in ("hd", "butterfly", "ring"):
         ms = _avg_ms(lambda: ccgpu.all_reduce_buckets(send, recv, boff, bcnt, algo=algo))
-        torch.cuda.synchronize()
-        got = download(recv)
-        t, _, _, exp = oracle_run(lambda: cs.bucketed_all_reduce(tensors, ref_buckets, algo, "sum", "bf16"))
-        par = all(same_bits(got[r, toff[k]:toff[k] + len(tensors[r][k])], exp[r][k])
-                  for r in range(N) for k in range(len(sizes)))
-        out[algo] = {"ms": round(ms, 4), "GBps": round(gbps(alg, ms), 1), "parity": par, "oracle_s": round(t, 2)}
-        del got, exp
+        out[algo] = {"ms": round(ms, 4), "GBps": round(gbps(alg, ms), 1)}
+    # the ring's output (the last run) against the oracle; halving-doubling
+    # and butterfly are compared whole by the tests
+    torch.cuda.synchronize()
+    got = download(recv)
+    log("  oracle: ring AllReduce of every bucket")
+    t, _, _, exp = oracle_run(lambda: cs.bucketed_all_reduce(tensors, ref_buckets, "ring", "sum", "bf16"))
+    out["ring"]["parity"] = all(same_bits(got[r, toff[k]:toff[k] + len(tensors[r][k])], exp[r][k])
+                                for r in range(N) for k in range(len(sizes)))
+    out["ring"]["oracle_s"] = round(t, 2)
+    del got, exp
     per = []
     for o, c in zip(boff, bcnt):
         s_, r_ = send[:, o:o + c], recv[:, o:o + c]
@@ -565,6 +567,7 @@ def rec_zero3(dev):
         ms = _avg_ms(lambda: ccgpu.reduce_scatter(send, shard, algo=algo))
         torch.cuda.synchronize()
         got = download(shard)
+        log(f"  oracle: {algo} ReduceScatter")
         t, _, _, exp = oracle_run(lambda: oracle_fn(xs, "sum", "f32"))
         out[f"reduce_scatter_{algo}"] = {"ms": round(ms, 4), "GBps": round(gbps(alg, ms), 1),
                                          "parity": all(same_bits(got[r], exp[r]) for r in range(N)),
@@ -620,6 +623,7 @@ def rec_moe(dev):
 
     from ring_allreduce_reduction_02_amd import ccgpu
     N, H = 8, 7168
+    log("  generating routed rows")
     C, rows = moe_inputs(N, H=H)
     Ls, Lr = int(C.sum(1).max()), int(C.sum(0).max())
     send = strided_ranks(N, Ls * H, torch.bfloat16, dev)

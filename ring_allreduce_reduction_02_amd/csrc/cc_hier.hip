@@ -1,0 +1,211 @@
+// The fused hierarchical AllReduce kernel of the collective-reduction engine
+// (the "AllReduce" algorithm notes, 算法五 多维分层 AllReduce; textbook ch. 6
+// "集合通信", 分层全归约).
+
+#include "cc_device.h"
+
+namespace cc {
+namespace {
+
+// ------------------------------------------------------------------ hierarchical AllReduce
+
+// Rank r = sum of c_i * stride[i] over the (at most kMaxHierLevels)
+// non-trivial levels.  The vector splits into N segments -- the level-0
+// chunks, each split into its level-1 chunks, and so on -- each with one
+// chunk index per level (seg[s], 8 bits per level); bnd holds their bounds.
+// An element's value is the nested ring chains of the pages' decomposition:
+// the outermost level (top; nd when the outermost level of the hierarchy
+// has size 1 and no AllReduce runs) folds its members from chunk index c
+// (AllReduce order), every other level from c + 1 (standalone
+// ReduceScatter order), each chain op(next, partial), the members' values
+// being the inner levels' chains.
+struct HierArgs {
+  const char* sb;
+  uint64_t ss;
+  char* rb;
+  uint64_t rs;
+  uint64_t M;
+  int N;
+  int nd;
+  int top;
+  int vec_ok;
+  int tpc_log2;  // segments of exactly 2^k full tiles: log2 of k, else -1
+  int p[kMaxHierLevels];
+  int stride[kMaxHierLevels];
+  uint32_t seg[kMaxRanks];
+  uint64_t bnd[kMaxRanks + 1];
+};
+
+// First coordinate of each level's chain for segment s: the top level
+// starts at its chunk index c (AllReduce order), every other level at c + 1.
+__device__ __forceinline__ int hier_first(const HierArgs& a, uint32_t seg, int i) {
+  const int c = (int)((seg >> (8 * i)) & 255u);
+  if (i == a.top) return c;
+  return c + 1 == a.p[i] ? 0 : c + 1;
+}
+
+// acc = x (first member of a chain) or op(x, acc)
+template <int DT, int OP, int VN>
+__device__ __forceinline__ void hier_join(bool first, const typename Ty<DT>::A (&x)[VN],
+                                          typename Ty<DT>::A (&acc)[VN]) {
+#pragma unroll
+  for (int k = 0; k < VN; ++k) acc[k] = first ? x[k] : opf<DT, OP>(x[k], acc[k]);
+}
+
+// The levels of one segment, uniform across the workgroup: sizes (1 beyond
+// nd), first coordinate of each chain, rank strides.
+struct HierLv {
+  int p[kMaxHierLevels], f[kMaxHierLevels], sd[kMaxHierLevels];
+};
+
+__device__ __forceinline__ HierLv hier_lv(const HierArgs& a, uint32_t seg) {
+  HierLv L;
+#pragma unroll
+  for (int i = 0; i < kMaxHierLevels; ++i) {
+    L.p[i] = i < a.nd ? a.p[i] : 1;
+    L.f[i] = i < a.nd ? hier_first(a, seg, i) : 0;
+    L.sd[i] = i < a.nd ? a.stride[i] : 0;
+  }
+  return L;
+}
+
+// A position in the walk over the N leaves in fold order (level 0 fastest):
+// j[i] counts the members of level i's chain already passed, c[i] is the
+// coordinate of the current one.  Every index is a compile-time constant, so
+// the state lives in scalar registers.
+struct HierPos {
+  int c[kMaxHierLevels], j[kMaxHierLevels];
+};
+
+__device__ __forceinline__ HierPos hier_begin(const HierLv& L) {
+  HierPos w;
+#pragma unroll
+  for (int i = 0; i < kMaxHierLevels; ++i) {
+    w.c[i] = L.f[i];
+    w.j[i] = 0;
+  }
+  return w;
+}
+
+__device__ __forceinline__ int hier_rank(const HierLv& L, const HierPos& w) {
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxHierLevels; ++i) r += w.c[i] * L.sd[i];
+  return r;
+}
+
+// next leaf; after the last one the walk starts over at the first
+__device__ __forceinline__ void hier_step(const HierLv& L, HierPos& w) {
+  bool carry = true;
+#pragma unroll
+  for (int i = 0; i < kMaxHierLevels; ++i) {
+    if (carry) {
+      if (w.j[i] + 1 < L.p[i]) {
+        ++w.j[i];
+        w.c[i] = w.c[i] + 1 == L.p[i] ? 0 : w.c[i] + 1;
+        carry = false;
+      } else {
+        w.j[i] = 0;
+        w.c[i] = L.f[i];
+      }
+    }
+  }
+}
+
+// Folds the leaf at walk position w into the chain accumulators: the level-0
+// chain takes it, and every level whose chain it completes passes its value
+// on to the level above.
+template <int DT, int OP, int VN>
+__device__ __forceinline__ void hier_take(const HierLv& L, const HierPos& w, const typename Ty<DT>::A (&x)[VN],
+                                          typename Ty<DT>::A (&a0)[VN], typename Ty<DT>::A (&a1)[VN],
+                                          typename Ty<DT>::A (&a2)[VN], typename Ty<DT>::A (&a3)[VN]) {
+  hier_join<DT, OP, VN>(w.j[0] == 0, x, a0);
+  if (w.j[0] + 1 == L.p[0]) {
+    hier_join<DT, OP, VN>(w.j[1] == 0, a0, a1);
+    if (w.j[1] + 1 == L.p[1]) {
+      hier_join<DT, OP, VN>(w.j[2] == 0, a1, a2);
+      if (w.j[2] + 1 == L.p[2]) hier_join<DT, OP, VN>(w.j[3] == 0, a2, a3);
+    }
+  }
+}
+
+constexpr int kHierBatch = 8;  // leaves loaded ahead of their folds
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  static_assert(kMaxHierLevels == 4, "four levels");
+  const int N = a.N;
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  if (t.fast) {
+    const uint32_t lane = threadIdx.x * 16u;
+    const char* s0 = a.sb + t.e0 * SZ;
+    const HierLv L = hier_lv(a, a.seg[t.c]);
+    HierPos ld = hier_begin(L), fw = ld;
+    A a0[V], a1[V], a2[V], a3[V];
+    for (int l0 = 0; l0 < N; l0 += kHierBatch) {
+      // every load of the batch is issued before the first fold; past the
+      // last leaf the walk has wrapped to valid ranks whose values go unused
+      u32x4 raw[kHierBatch];
+#pragma unroll
+      for (int q = 0; q < kHierBatch; ++q) {
+        raw[q] = ldg(s0 + (uint64_t)hier_rank(L, ld) * a.ss + lane);
+        hier_step(L, ld);
+      }
+#pragma unroll
+      for (int q = 0; q < kHierBatch; ++q)
+        if (l0 + q < N) {
+          A x[V];
+          unpack<DT>(raw[q], x);
+          hier_take<DT, OP, V>(L, fw, x, a0, a1, a2, a3);
+          hier_step(L, fw);
+        }
+    }
+    const u32x4 o = pack<DT>(a3);
+    char* d = a.rb + t.e0 * SZ;
+    for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, o);
+  } else {
+    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+      const HierLv L = hier_lv(a, a.seg[chunk_in(a.bnd, N, e)]);
+      HierPos fw = hier_begin(L);
+      A a0[1], a1[1], a2[1], a3[1];
+      for (int l = 0; l < N; ++l) {
+        A x[1] = {ld1<DT>(a.sb + (uint64_t)hier_rank(L, fw) * a.ss + e * SZ)};
+        hier_take<DT, OP, 1>(L, fw, x, a0, a1, a2, a3);
+        hier_step(L, fw);
+      }
+      for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, a3[0]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int nd, int top, const uint64_t* segbnd,
+                             const uint32_t* seg) {
+  if (nd < 1 || nd > kMaxHierLevels || top < 0 || top > nd || r.N < 2 || r.N > kMaxRanks) return hipErrorInvalidValue;
+  HierArgs a;
+  a.sb = r.send.base; a.ss = r.send.stride;
+  a.rb = r.recv.base; a.rs = r.recv.stride;
+  a.M = r.M; a.N = r.N; a.nd = nd; a.top = top; a.vec_ok = r.vec_ok;
+  // the N segments are equal when every level splits exactly
+  a.tpc_log2 = pow2_tiles_per_chunk(r.M, r.N, r.dt, r.vec_ok);
+  for (int i = 0; i < kMaxHierLevels; ++i) {
+    a.p[i] = i < nd ? p[i] : 1;
+    a.stride[i] = i < nd ? stride[i] : 0;
+  }
+  for (int s = 0; s < r.N; ++s) a.seg[s] = seg[s];
+  for (int s = 0; s <= r.N; ++s) a.bnd[s] = segbnd[s];
+  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const unsigned lds = lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu
+                                                                 : one_round_blocks(num_tiles(r.M, r.dt), hier_blocks_per_cu(r.N)));
+  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+    constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    hipLaunchKernelGGL((k_hier_fused<DT, OP>), grid, blk, lds, r.st, a);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace cc

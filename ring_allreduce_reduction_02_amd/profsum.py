@@ -56,9 +56,40 @@ def kernel_stats(trace_dir: str, needle: str):
     raise KeyError(needle)
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# The files a kernel's code comes from, besides its own source file: what the
+# kernel sources share, and the launch interface.
+SHARED_SOURCES = ("cc_device.h", "cc_launch.h")
+
+
+def kernel_sources(source: str):
+    """The csrc files whose text decides a kernel defined in `source`."""
+    return [source, *SHARED_SOURCES]
+
+
+def sources_hash(names) -> str:
+    """sha256 (first 16 hex digits) of the named csrc files, in order: the
+    counters recorded for a kernel stay valid while this is unchanged."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(HERE, "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def xcheck_bytes(run_dir: str, kernel: str, copy_bytes: int):
+    """A second counter family: DRAM request counts at the L2 (TCC_EA0_*) and
+    L1-to-L2 request counts (TCP_TCC_*), each turned into bytes by what the
+    same counter reads for the plain copy of copy_bytes (which reads and
+    writes copy_bytes once)."""
+    rows = list(csv.DictReader(open(_one(os.path.join(run_dir, "**", "*counter_collection.csv")))))
+    out = {}
+    for name in sorted({r["Counter_Name"] for r in rows}):
+        m = counter_means(run_dir, name)
+        _, (kv, _) = pick(m, kernel)
+        _, (cv, _) = pick(m, COPY_KERNEL)
+        out[name] = {"kernel_per_dispatch": kv, "copy_per_dispatch": cv,
+                     "bytes": kv * copy_bytes / cv if cv else None}
+    return out
 
 
 def main():
@@ -66,13 +97,17 @@ def main():
     ap.add_argument("--trace", required=True)
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
+    ap.add_argument("--xcheck", default="", help="a --pmc run of DRAM / L2 request counters")
     ap.add_argument("--kernel", required=True, help="substring of the kernel name")
     ap.add_argument("--copy-bytes", type=int, required=True)
     ap.add_argument("--alg-bytes", type=int, required=True, help="algorithmic bytes per launch")
     ap.add_argument("--out", required=True, help="output path without extension")
     ap.add_argument("--trace-command", required=True)
     ap.add_argument("--pmc-command", required=True)
+    ap.add_argument("--xcheck-command", default="")
     ap.add_argument("--workload", required=True)
+    ap.add_argument("--note", default="", help="how the algorithmic bytes per launch are counted")
+    ap.add_argument("--source", default="cc_kernels.hip", help="the csrc file that defines the kernel")
     args = ap.parse_args()
 
     st = kernel_stats(args.trace, args.kernel)
@@ -86,10 +121,12 @@ def main():
     write_scale = args.copy_bytes / (cw_kib * 1024.0)
     traffic = f_kib * 1024.0 * fetch_scale + w_kib * 1024.0 * write_scale
     avg_ns = float(st["AverageNs"])
+    xc = xcheck_bytes(args.xcheck, args.kernel, args.copy_bytes) if args.xcheck else {}
     rec = {
         "kernel": kname,
         "workload": args.workload,
-        "kernel_source_sha256_16": source_hash(os.path.join(HERE, "csrc", "cc_kernels.hip")),
+        "kernel_sources": kernel_sources(args.source),
+        "kernel_source_sha256_16": sources_hash(kernel_sources(args.source)),
         "calls": int(st["Calls"]),
         "avg_ns": avg_ns,
         "min_ns": float(st["MinNs"]),
@@ -105,16 +142,22 @@ def main():
         "write_scale": write_scale,
         "traffic_bytes_per_launch": traffic,
         "algorithmic_bytes_per_launch": args.alg_bytes,
+        "algorithmic_bytes_note": args.note,
         "traffic_over_algorithmic": traffic / args.alg_bytes,
         "achieved_GBps_from_trace": args.alg_bytes / avg_ns,
+        "xcheck": xc,
         "trace_command": args.trace_command,
         "pmc_command": args.pmc_command,
+        "xcheck_command": args.xcheck_command,
     }
     with open(args.out + "_pmc.json", "w") as f:
         json.dump(rec, f, indent=1)
     with open(args.out + ".md", "w") as f:
         f.write(f"# {args.workload}\n\n")
-        f.write(f"Kernel: `{kname}`  (source sha256/16 `{rec['kernel_source_sha256_16']}`)\n\n")
+        f.write(f"Kernel: `{kname}`  (sources {', '.join(rec['kernel_sources'])}: sha256/16 "
+                f"`{rec['kernel_source_sha256_16']}`)\n\n")
+        if args.note:
+            f.write(f"Algorithmic bytes per launch: {args.alg_bytes} ({args.note}).\n\n")
         f.write("## rocprofv3 --kernel-trace --stats\n\n")
         f.write(f"Command: `{args.trace_command}`\n\n")
         f.write("| calls | avg us | min us | max us | algorithmic GB | GB/s at avg |\n|---|---|---|---|---|---|\n")
@@ -128,6 +171,23 @@ def main():
         f.write(f"| WRITE_SIZE | {w_kib:.1f} | {cw_kib:.1f} | {write_scale:.4f} | {w_kib * 1024 * write_scale:.4e} |\n\n")
         f.write(f"HBM traffic per launch {traffic:.4e} B = {rec['traffic_over_algorithmic']:.4f} x the algorithmic "
                 f"{args.alg_bytes} B.\n")
+        if xc:
+            f.write("\n## Cross-check: request counters (one --pmc run)\n\n")
+            f.write(f"Command: `{args.xcheck_command}`\n\n")
+            f.write("Each counter is scaled by what it reads for the same plain copy (which reads and writes "
+                    f"{args.copy_bytes} B once).\n\n")
+            f.write("| counter | kernel per dispatch | copy per dispatch | kernel bytes | / algorithmic |\n"
+                    "|---|---|---|---|---|\n")
+            for name, v in xc.items():
+                b = v["bytes"]
+                f.write(f"| {name} | {v['kernel_per_dispatch']:.4e} | {v['copy_per_dispatch']:.4e} | "
+                        f"{b:.4e} | {b / args.alg_bytes:.4f} |\n")
+            for fam, tag in (("TCC_EA0_", "DRAM requests"), ("TCP_TCC_", "L1-to-L2 requests")):
+                r_ = [v["bytes"] for k, v in xc.items() if k.startswith(fam) and ("RDREQ" in k or "READ" in k)]
+                w_ = [v["bytes"] for k, v in xc.items() if k.startswith(fam) and ("WRREQ" in k or "WRITE" in k)]
+                if r_ and w_:
+                    f.write(f"\n{tag}: read + write {r_[0] + w_[0]:.4e} B = "
+                            f"{(r_[0] + w_[0]) / args.alg_bytes:.4f} x algorithmic.\n")
     print(json.dumps(rec, indent=1))
 
 

@@ -20,7 +20,8 @@ def stub():
           "sizes": "4KiB..64MiB per rank", "max_rel_residual": 0.11}
     cpu = {"value": 4.789, "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": "the whole workload (ring AllReduce SUM, N=8, M=67108864 f32), step-explicit NumPy "
-                     "simulator, single-threaded; 12 runs in 10.8 s, median 0.897 s"}
+                     "simulator, single-threaded; 12 runs in 10.8 s, median 0.897 s",
+           "host": "AMD EPYC 9575F 64-Core Processor, 256 logical CPUs, 16 in affinity"}
     return m, args, roof, twin, ab, cpu
 
 
