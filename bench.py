@@ -976,9 +976,10 @@ def int8_ef(dev):
     for dtype in ("f32", "bf16"):
         tdt = torch.float32 if dtype == "f32" else torch.bfloat16
         es = 4 if dtype == "f32" else 2
-        g = (torch.randn(N, M, generator=gen, device=dev) * 1e-3).to(tdt)
-        e = torch.zeros(N, M, device=dev)
-        r = torch.empty_like(g)
+        g = strided_ranks(N, M, tdt, dev)
+        g.copy_((torch.randn(N, M, generator=gen, device=dev) * 1e-3).to(tdt))
+        e = strided_ranks(N, M, torch.float32, dev).zero_()
+        r = strided_ranks(N, M, tdt, dev)
         ms_f = _avg_ms(lambda: ccgpu.all_reduce_int8_ef(g, e, r, fuse_depth=0))
         ws = torch.empty(ccgpu.int8_ef_workspace_size(N, M, dtype, 1), dtype=torch.uint8, device=dev)
         ms_2 = _avg_ms(lambda: ccgpu.all_reduce_int8_ef(g, e, r, fuse_depth=1, workspace=ws))
@@ -1116,11 +1117,12 @@ def profile_section(name, dev, steps, warmup, pad_bytes=262_144):
         nbytes = 2 * N * M * 4
     elif name in ("int8_ef_f32", "int8_ef_bf16", "int8_quant_f32", "int8_dequant_f32"):
         tdt = torch.bfloat16 if name == "int8_ef_bf16" else torch.float32
-        g = (torch.randn(N, M, generator=gen, device=dev) * 1e-3).to(tdt)
-        e = torch.zeros(N, M, device=dev)
-        r = torch.empty_like(g)
-        q = torch.empty(N, M, dtype=torch.int8, device=dev)
-        sc = torch.empty(N, M // 128, device=dev)
+        g = strided_ranks(N, M, tdt, dev)
+        g.copy_((torch.randn(N, M, generator=gen, device=dev) * 1e-3).to(tdt))
+        e = strided_ranks(N, M, torch.float32, dev).zero_()
+        r = strided_ranks(N, M, tdt, dev)
+        q = strided_ranks(N, M, torch.int8, dev)
+        sc = strided_ranks(N, M // 128, torch.float32, dev)
         if name in ("int8_ef_f32", "int8_ef_bf16"):
             fn, nbytes = (lambda: ccgpu.all_reduce_int8_ef(g, e, r)), N * M * (2 * g.element_size() + 8)
         elif name == "int8_quant_f32":

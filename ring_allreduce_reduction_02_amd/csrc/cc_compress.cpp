@@ -29,8 +29,10 @@ cc_status_t q_checks(int nranks, cc_dtype_t dtype, const cc_config_t& cfg, uint6
   if (cfg.algo != CC_ALGO_RING)
     return fail(CC_ERR_UNSUPPORTED, "the compressed AllReduce folds in the ring order (algo ring)");
   if (cfg.grid_sync) return fail(CC_ERR_UNSUPPORTED, "grid_sync is not available here");
-  const uint64_t tile = (uint64_t)kBlock * vec_elems((int)dtype);
-  if ((M + tile - 1) / tile > 0x7fffffffull) return fail(CC_ERR_INVALID_ARG, "count too large for one launch");
+  // the compression kernels tile by 512 elements (4 per lane): the grid's
+  // work-items must fit 32 bits
+  const uint64_t tiles = (M + 511) / 512;
+  if (tiles * (uint64_t)kBlock > 0xffffffffull) return fail(CC_ERR_INVALID_ARG, "count too large for one launch");
   return CC_OK;
 }
 

@@ -1,5 +1,5 @@
-// Internal interface between the C ABI (cc_api.cpp) and the kernels
-// (cc_kernels.hip).  Host-side only; not installed.
+// Internal interface between the C ABI (cc_api.cpp and the other host
+// sources) and the kernels (cc_*.hip).  Host-side only; not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -193,5 +193,29 @@ struct CopyDesc {
   uint64_t bytes;
 };
 hipError_t launch_copies(const CopyDesc* d, int n, int esize, int blocks_per_cu, hipStream_t st);
+
+// ---- capacity-padded MoE exchange, direct schedule: one launch, one
+// workgroup per output row.  The dispatch writes every expert slot (kept rows
+// copied, the rest zero), the combine every token row (kept rows copied back,
+// dropped ones zero); cnt[i * E + e] = rows token rank i routes to expert e.
+constexpr int kMoeMaxBlocks = 512;  // nranks * nexperts in one launch
+struct MoeLaunch {
+  const char* src;   // the side read: token side (dispatch) or expert side (combine)
+  uint64_t ss;
+  char* dst;
+  uint64_t ds;
+  uint64_t rowb;
+  uint64_t cap;
+  int N;
+  int E;
+  int dispatch;
+  int blocks_per_cu;
+  const uint64_t* cnt;
+  hipStream_t st;
+};
+// false when the exchange does not fit one launch (N * E, 32-bit rows or the
+// grid): the caller then runs copy descriptors
+bool moe_rows_fit(int N, int E, uint64_t cap, const uint64_t* cnt);
+hipError_t launch_moe_rows(const MoeLaunch& L);
 
 }  // namespace cc

@@ -31,6 +31,40 @@ struct QArgs {
   uint64_t bnd[kMaxRanks + 1];
 };
 
+// The compression kernels give every lane 4 consecutive elements of a rank,
+// whatever the gradient type: the error accumulators (float32, 4 bytes per
+// element) are then one 16-byte load and store per lane, and every store
+// instruction of a wavefront writes one contiguous KiB (bf16 gradients and
+// results move 8 bytes per lane, 512 contiguous bytes per instruction).  With
+// 8 bf16 elements per lane the accumulators took two 16-byte stores per lane
+// 32 bytes apart, each instruction covering half of every line it touched,
+// and the DRAM saw 6% more write traffic than the kernel's output.
+constexpr int kQLane = 4;
+constexpr uint64_t kQTile = (uint64_t)kBlock * kQLane;  // 512 elements
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ void ld4(const char* p, float* x) {
+  if constexpr (DT == DT_F32) {
+    unpack<DT_F32>(ldg(p), x);
+  } else {
+    const u32x2 w = __builtin_nontemporal_load((const u32x2*)p);
+    x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
+  }
+}
+template <int DT>
+__device__ __forceinline__ void st4(char* p, const float* x) {
+  if constexpr (DT == DT_F32) {
+    stg(p, pack<DT_F32>(x));
+  } else {
+    u32x2 w;
+    w.x = bf16_rne(x[0]) | (bf16_rne(x[1]) << 16);
+    w.y = bf16_rne(x[2]) | (bf16_rne(x[3]) << 16);
+    __builtin_nontemporal_store(w, (u32x2*)p);
+  }
+}
+
 __device__ __forceinline__ float q_scale(float m) { return m / 127.0f; }
 // q as the integer it is (through int32: rint of a small negative ratio is
 // -0.0, an int8 has no signed zero, and v = q s must then be +0)
@@ -77,23 +111,12 @@ struct QPack<4> {
     for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(w >> (8 * i));
   }
 };
-template <>
-struct QPack<8> {
-  typedef uint2 T;
-  __device__ static T pack(const float* q) {
-    return make_uint2(QPack<4>::pack(q), QPack<4>::pack(q + 4));
-  }
-  __device__ static void unpack(T w, float* q) {
-    QPack<4>::unpack(w.x, q);
-    QPack<4>::unpack(w.y, q + 4);
-  }
-};
 
 // The compression of one lane's V elements of one rank (fast path): returns
 // v and writes e, and the int8 values and the block scale when Q is set.
-template <int DT, bool Q>
+template <bool Q>
 __device__ __forceinline__ void quant_lane(const float* x, const float* e, float* v, char* ep, char* qp, char* sp) {
-  constexpr int V = Ty<DT>::V;
+  constexpr int V = kQLane;
   float u[V], m = 0.0f;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -110,7 +133,6 @@ __device__ __forceinline__ void quant_lane(const float* x, const float* e, float
     en[i] = u[i] - v[i];
   }
   stw_vec<DT_F32>(ep, en);
-  if constexpr (V == 8) stw_vec<DT_F32>(ep + 16, en + 4);
   if constexpr (Q) {
     *(typename QPack<V>::T*)qp = QPack<V>::pack(q);
     if ((threadIdx.x & (kQBlock / V - 1)) == 0) *(float*)sp = s;
@@ -119,12 +141,10 @@ __device__ __forceinline__ void quant_lane(const float* x, const float* e, float
 
 template <int DT>
 __device__ __forceinline__ void load_ge(const QArgs& a, uint64_t e0, int r, uint32_t lane, float* x, float* e) {
-  constexpr int V = Ty<DT>::V;
   constexpr int SZ = Ty<DT>::SZ;
-  unpack<DT>(ldg(a.gb + (uint64_t)r * a.gs + e0 * SZ + lane * 16u), x);
-  const char* ep = a.eb + (uint64_t)r * a.es + (e0 + (uint64_t)lane * V) * 4;
-  unpack<DT_F32>(ldg(ep), e);
-  if constexpr (V == 8) unpack<DT_F32>(ldg(ep + 16), e + 4);
+  const uint64_t el = e0 + (uint64_t)lane * kQLane;
+  ld4<DT>(a.gb + (uint64_t)r * a.gs + el * SZ, x);
+  unpack<DT_F32>(ldg(a.eb + (uint64_t)r * a.es + el * 4), e);
 }
 
 // Element-wise compression of the block starting at element b0 of rank r:
@@ -143,18 +163,17 @@ __device__ __forceinline__ float quant_elem_scale(const QArgs& a, uint64_t b0, u
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_quant_ef(QArgs a) {
   extern __shared__ float qred[];
-  constexpr int V = Ty<DT>::V;
+  constexpr int V = kQLane;
   const int r = blockIdx.y;
-  const uint64_t tile = (uint64_t)kBlock * V;
-  const uint64_t e0 = (uint64_t)blockIdx.x * tile;
-  const uint64_t e1 = e0 + tile < a.M ? e0 + tile : a.M;
-  if (a.vec_ok && e1 - e0 == tile) {
+  const uint64_t e0 = (uint64_t)blockIdx.x * kQTile;
+  const uint64_t e1 = e0 + kQTile < a.M ? e0 + kQTile : a.M;
+  if (a.vec_ok && e1 - e0 == kQTile) {
     const uint32_t lane = threadIdx.x;
     float x[V], e[V], v[V];
     load_ge<DT>(a, e0, r, lane, x, e);
     const uint64_t el = e0 + (uint64_t)lane * V;
-    quant_lane<DT, true>(x, e, v, a.eb + (uint64_t)r * a.es + el * 4, a.qb + (uint64_t)r * a.qs + el,
-                         a.sb + (uint64_t)r * a.ss + (el / kQBlock) * 4);
+    quant_lane<true>(x, e, v, a.eb + (uint64_t)r * a.es + el * 4, a.qb + (uint64_t)r * a.qs + el,
+                     a.sb + (uint64_t)r * a.ss + (el / kQBlock) * 4);
   } else {
     for (uint64_t b0 = e0; b0 < e1; b0 += kQBlock) {
       float u;
@@ -172,43 +191,92 @@ __global__ __launch_bounds__(kBlock) void k_quant_ef(QArgs a) {
 
 // The reduction of the messages: every element folds the dequantized values
 // of all ranks in the ring order of its chunk, and every rank gets the result.
+//
+// A workgroup takes a wide tile of kDqTile elements of every rank: a lane
+// reads 16 consecutive int8 values of a rank with one 16-byte load (and the
+// one block scale they share), so the tile's 16 block scales of a rank are
+// half of a 128-byte line, read by two workgroups.  With one 512-element
+// tile per workgroup (4-byte int8 loads) the eight workgroups sharing a line
+// ran on the eight XCDs and each XCD's L2 fetched it again: 4.35% more HBM
+// traffic than the kernel's algorithmic bytes.  The lane's 16 results go
+// through LDS to the store layout, in which every 16-byte store instruction
+// of a wavefront writes 1 KiB of consecutive output; each wavefront
+// exchanges its own 1024 results, so no workgroup barrier is needed.
+// Measured on the MI355X (8 ranks x 67,108,864, fp32 results, rows 256 MiB
+// apart): 5.75 TB/s at 3 workgroups per CU, against 5.59 for the 512-element
+// tiles; one workgroup looping over two such tiles to read the whole scale
+// line ran at 5.53 at best, and 4-byte loads over eight 512-element tiles per
+// workgroup at 4.79.
+constexpr int kDqLane = 16;                                   // int8 values per lane and load
+constexpr uint64_t kDqTile = (uint64_t)kBlock * kDqLane;      // 2048 elements: 16 blocks
+constexpr unsigned kDqLds = kBlock * kDqLane * 4;             // the transposition's 8 KiB
+
+// An exchange through LDS between the lanes of one wavefront: the LDS serves
+// a wavefront's accesses in issue order, so it takes no workgroup barrier
+// (whose release would also wait for the wavefront's global stores); this
+// waits for the wavefront's LDS writes issued so far and keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void unpack_i8x16(u32x4 w, float* q) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) q[i] = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
+}
+
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_dequant_reduce(QArgs a) {
-  constexpr int V = Ty<DT>::V;
+  extern __shared__ float qlds[];
   constexpr int SZ = Ty<DT>::SZ;
-  typedef typename QPack<V>::T QT;
+  constexpr int VO = Ty<DT>::V;  // output elements per 16-byte store
   const int N = a.N;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, N, a.vec_ok);
-  if (t.fast) {
-    const uint64_t el = t.e0 + (uint64_t)threadIdx.x * V;
+  const uint64_t t0 = (uint64_t)blockIdx.x * kDqTile;
+  const uint64_t t1 = t0 + kDqTile < a.M ? t0 + kDqTile : a.M;
+  const uint32_t c0 = chunk_of(a.M, N, t0);
+  if (a.vec_ok && t1 - t0 == kDqTile && c0 == chunk_of(a.M, N, t1 - 1)) {
+    const uint32_t lane = threadIdx.x, wl = lane & 63u, wv = lane >> 6;
+    const uint64_t el = t0 + (uint64_t)lane * kDqLane;
     const uint64_t sb = (el / kQBlock) * 4;
-    float acc[V];
-    int r = (int)t.c;
+    float acc[kDqLane];
+    int r = (int)c0;
     for (int j0 = 0; j0 < N; j0 += 8) {
-      QT qw[8];
+      u32x4 qw[8];
       float sc[8];
       int rr = r;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {  // past the last rank the loads repeat valid ones
-        qw[k] = *(const QT*)(a.qb + (uint64_t)rr * a.qs + el);
+        qw[k] = ldg(a.qb + (uint64_t)rr * a.qs + el);
         sc[k] = *(const float*)(a.sb + (uint64_t)rr * a.ss + sb);
         if (j0 + k + 1 < N) rr = rr + 1 == N ? 0 : rr + 1;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (j0 + k < N) {
-          float q[V];
-          QPack<V>::unpack(qw[k], q);
+          float q[kDqLane];
+          unpack_i8x16(qw[k], q);
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] = (j0 + k == 0) ? q[i] * sc[k] : q[i] * sc[k] + acc[i];
+          for (int i = 0; i < kDqLane; ++i) acc[i] = (j0 + k == 0) ? q[i] * sc[k] : q[i] * sc[k] + acc[i];
         }
       r = rr;  // the first rank of the next batch (rr moved past the last load)
     }
-    const u32x4 o = pack<DT>(acc);
-    char* d = a.rb + t.e0 * SZ;
-    for (int k = 0; k < N; ++k, d += a.rs) stg(d + threadIdx.x * 16u, o);
+    // the wavefront's 1024 results in element order, then read back in the
+    // store layout: lane wl's store j covers elements j * 64 VO + wl VO ..
+    float* w = qlds + wv * (64 * kDqLane);
+#pragma unroll
+    for (int k = 0; k < kDqLane; k += 4) *(float4*)(w + wl * kDqLane + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+    wave_lds_fence();
+    const uint64_t wbase = t0 + (uint64_t)wv * (64 * kDqLane);
+#pragma unroll
+    for (int j = 0; j < kDqLane / VO; ++j) {
+      const uint32_t x = (uint32_t)j * (64u * VO) + wl * VO;
+      float o[VO];
+#pragma unroll
+      for (int i = 0; i < VO; i += 4) *(float4*)(o + i) = *(const float4*)(w + x + i);
+      const u32x4 ov = pack<DT>(o);
+      char* d = a.rb + (wbase + x) * SZ;
+      for (int k = 0; k < N; ++k, d += a.rs) stg(d, ov);
+    }
   } else {
-    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+    for (uint64_t e = t0 + threadIdx.x; e < t1; e += kBlock) {
       const int c = (int)chunk_of(a.M, N, e);
       float acc = 0.0f;
       for (int j = 0, r = c; j < N; ++j, r = r + 1 == N ? 0 : r + 1) {
@@ -225,7 +293,7 @@ __global__ __launch_bounds__(kBlock) void k_dequant_reduce(QArgs a) {
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_quant_ef_fused(QArgs a) {
   extern __shared__ float qred[];
-  constexpr int V = Ty<DT>::V;
+  constexpr int V = kQLane;
   constexpr int SZ = Ty<DT>::SZ;
   constexpr int B = 4;  // ranks loaded ahead of their compression
   const int N = a.N;
@@ -249,15 +317,14 @@ __global__ __launch_bounds__(kBlock) void k_quant_ef_fused(QArgs a) {
       for (int k = 0; k < B; ++k)
         if (j0 + k < N) {
           float v[V];
-          quant_lane<DT, false>(x[k], e[k], v, a.eb + (uint64_t)rs[k] * a.es + el * 4, nullptr, nullptr);
+          quant_lane<false>(x[k], e[k], v, a.eb + (uint64_t)rs[k] * a.es + el * 4, nullptr, nullptr);
 #pragma unroll
           for (int i = 0; i < V; ++i) acc[i] = (j0 + k == 0) ? v[i] : v[i] + acc[i];
         }
       r = rr;  // the first rank of the next batch (rr moved past the last load)
     }
-    const u32x4 o = pack<DT>(acc);
-    char* d = a.rb + t.e0 * SZ;
-    for (int k = 0; k < N; ++k, d += a.rs) stg(d + lane * 16u, o);
+    char* d = a.rb + el * SZ;
+    for (int k = 0; k < N; ++k, d += a.rs) st4<DT>(d, acc);
   } else {
     // per block: the N scales first (they need every element of the block),
     // then each element folds in the ring order of its own chunk
@@ -298,7 +365,7 @@ QArgs q_args(const QLaunch& L) {
   a.sb = L.s; a.ss = L.ss;
   a.rb = L.r; a.rs = L.rs;
   a.M = L.M; a.N = L.N; a.vec_ok = L.vec_ok;
-  a.tpc_log2 = L.bnd ? pow2_tiles_per_chunk(L.M, L.N, L.dt, L.vec_ok) : -1;
+  a.tpc_log2 = L.bnd ? pow2_tiles_per_chunk_v(L.M, L.N, kQLane, L.vec_ok) : -1;
   for (int c = 0; c <= L.N; ++c) a.bnd[c] = L.bnd ? L.bnd[c] : 0;
   return a;
 }
@@ -311,20 +378,20 @@ unsigned q_lds(int blocks_per_cu, int dflt) {
   return lds < need ? need : lds;
 }
 // Default workgroups per CU, swept on the MI355X at 8 ranks x 67,108,864
-// elements (1 to 16 per CU): the compression step streams best at 16 for
-// float32 gradients (1065 us against 1262 at 8) and 8 for bf16 (1040 us
-// against 1068 at 16), the reduction of the messages at 8 (float32) / 6
-// (bf16), the fused kernel, which keeps four ranks' loads in flight, at 4
-// (float32) / 3 (bf16).
-int quant_blocks_per_cu(int dt) { return dt == DT_F32 ? 16 : 8; }
-int dequant_blocks_per_cu(int dt) { return dt == DT_F32 ? 8 : 6; }
-int qfused_blocks_per_cu(int dt) { return dt == DT_F32 ? 4 : 3; }
+// elements (2 to 16 per CU): the compression step streams best at 16 (float32
+// gradients 6.41 TB/s against 5.69 at 8; bf16 6.46 against 5.17 at 8), the
+// reduction of the messages at 3 (5.75 float32 and 5.71 bf16 results, 5.35
+// and 5.36 at 8), the fused kernel, which keeps four ranks' loads in flight,
+// at 4 for float32 (5.89 TB/s) and 5 for bf16 (5.99 against 5.25 at 3).
+int quant_blocks_per_cu(int) { return 16; }
+int dequant_blocks_per_cu(int) { return 3; }
+int qfused_blocks_per_cu(int dt) { return dt == DT_F32 ? 4 : 5; }
 }  // namespace
 
 hipError_t launch_quant_ef(const QLaunch& L) {
   if (L.N < 1 || L.N > kMaxRanks || (L.dt != DT_F32 && L.dt != DT_BF16)) return hipErrorInvalidValue;
   const QArgs a = q_args(L);
-  const dim3 grid((unsigned)num_tiles(L.M, L.dt), (unsigned)L.N), blk(kBlock);
+  const dim3 grid((unsigned)((L.M + kQTile - 1) / kQTile), (unsigned)L.N), blk(kBlock);
   const unsigned lds = q_lds(L.blocks_per_cu, quant_blocks_per_cu(L.dt));
   if (L.dt == DT_F32) hipLaunchKernelGGL((k_quant_ef<DT_F32>), grid, blk, lds, L.st, a);
   else hipLaunchKernelGGL((k_quant_ef<DT_BF16>), grid, blk, lds, L.st, a);
@@ -333,9 +400,12 @@ hipError_t launch_quant_ef(const QLaunch& L) {
 
 hipError_t launch_dequant_reduce(const QLaunch& L) {
   if (L.N < 1 || L.N > kMaxRanks || (L.dt != DT_F32 && L.dt != DT_BF16) || !L.bnd) return hipErrorInvalidValue;
-  const QArgs a = q_args(L);
-  const dim3 grid((unsigned)num_tiles(L.M, L.dt)), blk(kBlock);
-  const unsigned lds = q_lds(L.blocks_per_cu, dequant_blocks_per_cu(L.dt));
+  const QArgs a = q_args(L);  // vec_ok: int8 rows, scales and results 16-byte aligned (base and stride)
+  const uint64_t tiles = (L.M + kDqTile - 1) / kDqTile;
+  if (tiles > 0x7fffffffull) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles), blk(kBlock);
+  unsigned lds = q_lds(L.blocks_per_cu, dequant_blocks_per_cu(L.dt));
+  if (lds < kDqLds) lds = kDqLds;
   if (L.dt == DT_F32) hipLaunchKernelGGL((k_dequant_reduce<DT_F32>), grid, blk, lds, L.st, a);
   else hipLaunchKernelGGL((k_dequant_reduce<DT_BF16>), grid, blk, lds, L.st, a);
   return hipGetLastError();
@@ -344,7 +414,7 @@ hipError_t launch_dequant_reduce(const QLaunch& L) {
 hipError_t launch_quant_ef_fused(const QLaunch& L) {
   if (L.N < 1 || L.N > kMaxRanks || (L.dt != DT_F32 && L.dt != DT_BF16) || !L.bnd) return hipErrorInvalidValue;
   const QArgs a = q_args(L);
-  const dim3 grid((unsigned)num_tiles(L.M, L.dt)), blk(kBlock);
+  const dim3 grid((unsigned)((L.M + kQTile - 1) / kQTile)), blk(kBlock);
   const unsigned lds = q_lds(L.blocks_per_cu, qfused_blocks_per_cu(L.dt));
   if (L.dt == DT_F32) hipLaunchKernelGGL((k_quant_ef_fused<DT_F32>), grid, blk, lds, L.st, a);
   else hipLaunchKernelGGL((k_quant_ef_fused<DT_BF16>), grid, blk, lds, L.st, a);

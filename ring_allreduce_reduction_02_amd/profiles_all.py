@@ -5,7 +5,8 @@ root on a machine with the GPU):
     python -m ring_allreduce_reduction_02_amd.profiles_all sum DIR [ENTRY ...]
 
 `run` executes, for every entry, a --kernel-trace --stats run and three --pmc
-runs (FETCH_SIZE; WRITE_SIZE; DRAM and L1-to-L2 request counts) of bench.py,
+runs (FETCH_SIZE; WRITE_SIZE; DRAM and L1-to-L2 request counts) of bench.py
+(with --limiter a fourth: wave, VALU and wait cycles),
 each in its own process under a time limit, writing under DIR, and stops at
 the first failure.  `sum` turns DIR into profiles/<entry output>.md and
 _pmc.json with profsum.  The headline kernels (fp32 and bf16 ring AllReduce at
@@ -22,6 +23,10 @@ import sys
 
 COPY_BYTES = 1 << 30
 XCHECK = "TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_DRAM_sum TCP_TCC_READ_REQ_sum TCP_TCC_WRITE_REQ_sum"
+# what the waves do (one run, 8 SQ counters and the GPU's busy clock): with
+# `--limiter`, for naming what bounds a kernel below the HBM roofline
+LIMITER = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_WAIT_INST_ANY "
+           "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_VMEM_RD GRBM_GUI_ACTIVE")
 
 # name: (trace source, kernel name substring, csrc file, profiles/ output, workload)
 ENTRIES = {
@@ -54,14 +59,10 @@ ENTRIES = {
                        "INT8 compression step with error feedback, N=8, M=67108864 fp32 gradients per rank"),
     "int8_dequant_f32": ("section", "k_dequant_reduce<1>", "cc_quant.hip", "dequant_reduce_f32_n8_m67108864",
                          "AllReduce of INT8 messages, N=8, M=67108864 elements per rank, fp32 result"),
-    "moe_padded_c125": ("section", "k_copies", "cc_copy.hip", "copies_moe_dispatch_padded_c125_n8_t4096_h7168",
+    "moe_padded_c125": ("section", "k_moe_rows", "cc_copy.hip", "moe_rows_dispatch_padded_c125_n8_t4096_h7168",
                         "capacity-padded MoE dispatch (C=1.25, capacity 640), N=8, 4096 tokens top-8 of 64 experts, "
                         "rows of 7168 bf16"),
 }
-
-
-def _sec(name):
-    return "ring_f32" if name == "bench" else name
 
 
 def commands(name, d):
@@ -74,7 +75,7 @@ def commands(name, d):
                  f"python3 bench.py --profile-section {name} --steps 20 --warmup 2")
     pmc = {tag: (f"rocprofv3 --pmc {ctr} -f csv -d {d}/{name}_{tag} -o k -- python3 bench.py --profile-section {name} "
                  f"--steps 5 --warmup 1 --copy-probe-bytes {COPY_BYTES}")
-           for tag, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"), ("xcheck", XCHECK))}
+           for tag, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"), ("xcheck", XCHECK), ("limiter", LIMITER))}
     return trace, pmc
 
 
@@ -87,19 +88,18 @@ def _sh(cmd, out, limit):
         sys.exit(r.returncode)
 
 
-def run(d, names):
+def run(d, names, limiter=False):
+    """Every run whose output directory is not there yet (a second call
+    resumes; with limiter, adds the wave-counter runs)."""
     os.makedirs(d, exist_ok=True)
-    did_bench = os.path.exists(os.path.join(d, "bench_trace.out"))
     for name in names:
         trace, pmc = commands(name, d)
-        if ENTRIES[name][0] == "bench":
-            if not did_bench:
-                _sh(trace, os.path.join(d, "bench_trace.out"), 900)
-                did_bench = True
-        else:
-            _sh(trace, os.path.join(d, f"{name}_trace.out"), 300)
-        for tag in ("fetch", "write", "xcheck"):
-            _sh(pmc[tag], os.path.join(d, f"{name}_{tag}.out"), 120)
+        tdir = "bench_trace" if ENTRIES[name][0] == "bench" else f"{name}_trace"
+        if not os.path.isdir(os.path.join(d, tdir)):
+            _sh(trace, os.path.join(d, f"{tdir}.out"), 900 if tdir == "bench_trace" else 300)
+        for tag in ("fetch", "write", "xcheck") + (("limiter",) if limiter else ()):
+            if not os.path.isdir(os.path.join(d, f"{name}_{tag}")):
+                _sh(pmc[tag], os.path.join(d, f"{name}_{tag}.out"), 120)
 
 
 def _alg_bytes(d, name):
@@ -126,16 +126,22 @@ def summarize(d, names):
                "--workload", workload, "--note", note, "--source", csrc]
         if os.path.isdir(f"{d}/{name}_xcheck"):
             cmd += ["--xcheck", f"{d}/{name}_xcheck", "--xcheck-command", pmc["xcheck"]]
+        if os.path.isdir(f"{d}/{name}_limiter"):
+            cmd += ["--limiter", f"{d}/{name}_limiter", "--limiter-command", pmc["limiter"]]
         subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
         print(f"profiles/{out}.md", flush=True)
 
 
 def main():
-    mode, d, names = sys.argv[1], sys.argv[2].rstrip("/"), sys.argv[3:] or list(ENTRIES)
+    args = [a for a in sys.argv[1:] if a != "--limiter"]
+    mode, d, names = args[0], args[1].rstrip("/"), args[2:] or list(ENTRIES)
     for n in names:
         if n not in ENTRIES:
             raise SystemExit(f"unknown entry {n}; known: {', '.join(ENTRIES)}")
-    {"run": run, "sum": summarize}[mode](d, names)
+    if mode == "run":
+        run(d, names, "--limiter" in sys.argv)
+    else:
+        summarize(d, names)
 
 
 if __name__ == "__main__":

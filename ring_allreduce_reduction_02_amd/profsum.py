@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--trace-command", required=True)
     ap.add_argument("--pmc-command", required=True)
     ap.add_argument("--xcheck-command", default="")
+    ap.add_argument("--limiter", default="", help="a --pmc run of wave / VALU / wait counters")
+    ap.add_argument("--limiter-command", default="")
     ap.add_argument("--workload", required=True)
     ap.add_argument("--note", default="", help="how the algorithmic bytes per launch are counted")
     ap.add_argument("--source", default="cc_kernels.hip", help="the csrc file that defines the kernel")
@@ -122,6 +124,7 @@ def main():
     traffic = f_kib * 1024.0 * fetch_scale + w_kib * 1024.0 * write_scale
     avg_ns = float(st["AverageNs"])
     xc = xcheck_bytes(args.xcheck, args.kernel, args.copy_bytes) if args.xcheck else {}
+    lim = limiter_counters(args.limiter, args.kernel) if args.limiter else {}
     rec = {
         "kernel": kname,
         "workload": args.workload,
@@ -146,9 +149,11 @@ def main():
         "traffic_over_algorithmic": traffic / args.alg_bytes,
         "achieved_GBps_from_trace": args.alg_bytes / avg_ns,
         "xcheck": xc,
+        "limiter": lim,
         "trace_command": args.trace_command,
         "pmc_command": args.pmc_command,
         "xcheck_command": args.xcheck_command,
+        "limiter_command": args.limiter_command,
     }
     with open(args.out + "_pmc.json", "w") as f:
         json.dump(rec, f, indent=1)
@@ -188,7 +193,40 @@ def main():
                 if r_ and w_:
                     f.write(f"\n{tag}: read + write {r_[0] + w_[0]:.4e} B = "
                             f"{(r_[0] + w_[0]) / args.alg_bytes:.4f} x algorithmic.\n")
+        if lim:
+            f.write("\n## What the waves do (one --pmc run)\n\n")
+            f.write(f"Command: `{args.limiter_command}`\n\n")
+            f.write("| counter | per dispatch |\n|---|---|\n")
+            for name, v in lim["raw"].items():
+                f.write(f"| {name} | {v:.4e} |\n")
+            f.write("\n| derived | value |\n|---|---|\n")
+            for name, v in lim["derived"].items():
+                f.write(f"| {name} | {v:.4f} |\n")
     print(json.dumps(rec, indent=1))
+
+
+def limiter_counters(run_dir: str, kernel: str):
+    """Per-dispatch wave counters of the kernel and the ratios read from them:
+    the share of the waves' cycles spent issuing VALU instructions, and spent
+    waiting for an operand (a load in flight, mostly), and the VALU busy share
+    of the SIMDs (SQ_ACTIVE_INST_VALU counts per wave in 4-cycle units; 1024
+    SIMDs)."""
+    rows = list(csv.DictReader(open(_one(os.path.join(run_dir, "**", "*counter_collection.csv")))))
+    raw = {}
+    for name in sorted({r["Counter_Name"] for r in rows}):
+        _, (v, _) = pick(counter_means(run_dir, name), kernel)
+        raw[name] = v
+    der = {}
+    if raw.get("SQ_WAVE_CYCLES"):
+        der["valu_cycles_over_wave_cycles"] = raw.get("SQ_ACTIVE_INST_VALU", 0.0) / raw["SQ_WAVE_CYCLES"]
+        der["wait_any_over_wave_cycles"] = raw.get("SQ_WAIT_INST_ANY", 0.0) / raw["SQ_WAVE_CYCLES"]
+    if raw.get("GRBM_GUI_ACTIVE"):
+        der["valu_busy_of_simds"] = raw.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / 1024 / raw["GRBM_GUI_ACTIVE"]
+    if raw.get("SQ_WAVES"):
+        der["valu_insts_per_wave"] = raw.get("SQ_INSTS_VALU", 0.0) / raw["SQ_WAVES"]
+        der["vmem_rd_insts_per_wave"] = raw.get("SQ_INSTS_VMEM_RD", 0.0) / raw["SQ_WAVES"]
+        der["trans_f32_insts_per_wave"] = raw.get("SQ_INSTS_VALU_TRANS_F32", 0.0) / raw["SQ_WAVES"]
+    return {"raw": raw, "derived": der}
 
 
 if __name__ == "__main__":
