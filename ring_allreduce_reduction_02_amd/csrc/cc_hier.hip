@@ -32,9 +32,23 @@ struct HierArgs {
   int tpc_log2;  // segments of exactly 2^k full tiles: log2 of k, else -1
   int p[kMaxHierLevels];
   int stride[kMaxHierLevels];
-  uint32_t seg[kMaxRanks];
-  uint64_t bnd[kMaxRanks + 1];
+  uint32_t seg[kMaxRanks];       // the segments' chunk indices, 8 bits per level
+  uint64_t bnd[kMaxRanks + 1];   // the segments' bounds
 };
+
+// The segment of element e: the flat floor chunk floor(((e + 1) N - 1) / M)
+// of the ring kernels' closed form, settled by the segment bounds.  The
+// nested bounds (each level's floor split of its range) lie within a few
+// elements of the flat floor bounds floor(s M / N), so where segments hold
+// more than a few elements the estimate is the segment or one beside it and
+// the loops take at most one step; they correct any estimate, since the
+// bounds rise from 0 to M.
+__device__ __forceinline__ uint32_t hier_seg(const HierArgs& a, uint64_t e) {
+  uint32_t s = chunk_of(a.M, a.N, e);
+  while (s > 0 && e < a.bnd[s]) --s;
+  while (s + 1 < (uint32_t)a.N && e >= a.bnd[s + 1]) ++s;
+  return s;
+}
 
 // First coordinate of each level's chain for segment s: the top level
 // starts at its chunk index c (AllReduce order), every other level at c + 1.
@@ -138,7 +152,16 @@ __global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   static_assert(kMaxHierLevels == 4, "four levels");
   const int N = a.N;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_of<V>(a.M, a.bnd, N, a.vec_ok);
+  Tile<V> t;
+  if (a.tpc_log2 >= 0) {
+    t = tile_pow2<V>(blockIdx.x, a.tpc_log2);
+  } else {
+    const uint64_t tile = (uint64_t)kBlock * V;
+    t.e0 = (uint64_t)blockIdx.x * tile;
+    t.e1 = t.e0 + tile < a.M ? t.e0 + tile : a.M;
+    t.c = hier_seg(a, t.e0);
+    t.fast = a.vec_ok && t.e1 - t.e0 == tile && t.e1 <= a.bnd[t.c + 1];
+  }
   if (t.fast) {
     const uint32_t lane = threadIdx.x * 16u;
     const char* s0 = a.sb + t.e0 * SZ;
@@ -167,14 +190,36 @@ __global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
     char* d = a.rb + t.e0 * SZ;
     for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, o);
   } else {
+    // a thread's elements are kBlock apart: the segment is looked up again
+    // only when an element leaves the previous one's
+    uint64_t slo = 1, shi = 0;
+    uint32_t scode = 0;
     for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      const HierLv L = hier_lv(a, a.seg[chunk_in(a.bnd, N, e)]);
-      HierPos fw = hier_begin(L);
+      if (e < slo || e >= shi) {
+        const uint32_t sg = hier_seg(a, e);
+        slo = a.bnd[sg];
+        shi = a.bnd[sg + 1];
+        scode = a.seg[sg];
+      }
+      const HierLv L = hier_lv(a, scode);
+      HierPos ld = hier_begin(L), fw = ld;
       A a0[1], a1[1], a2[1], a3[1];
-      for (int l = 0; l < N; ++l) {
-        A x[1] = {ld1<DT>(a.sb + (uint64_t)hier_rank(L, fw) * a.ss + e * SZ)};
-        hier_take<DT, OP, 1>(L, fw, x, a0, a1, a2, a3);
-        hier_step(L, fw);
+      // batches of leaf loads in flight before their folds, as on the
+      // vector path (one load at a time left every element waiting N times)
+      for (int l0 = 0; l0 < N; l0 += kHierBatch) {
+        A raw[kHierBatch];
+#pragma unroll
+        for (int q = 0; q < kHierBatch; ++q) {
+          raw[q] = ld1<DT>(a.sb + (uint64_t)hier_rank(L, ld) * a.ss + e * SZ);
+          hier_step(L, ld);
+        }
+#pragma unroll
+        for (int q = 0; q < kHierBatch; ++q)
+          if (l0 + q < N) {
+            const A x[1] = {raw[q]};
+            hier_take<DT, OP, 1>(L, fw, x, a0, a1, a2, a3);
+            hier_step(L, fw);
+          }
       }
       for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, a3[0]);
     }

@@ -66,20 +66,43 @@ __device__ __forceinline__ void st4(char* p, const float* x) {
 }
 
 __device__ __forceinline__ float q_scale(float m) { return m / 127.0f; }
-// q as the integer it is (through int32: rint of a small negative ratio is
-// -0.0, an int8 has no signed zero, and v = q s must then be +0)
+// q = round-half-even(u / s) clamped to [-127, 127], as the integer it is
+// (through int32: rint of a small negative ratio is -0.0, an int8 has no
+// signed zero, and v = q s must then be +0).
+// The quotient is needed only to the integer it rounds to.  u times the
+// hardware reciprocal of s is within 2.5e-5 of the correctly rounded u / s
+// (|u / s| <= 127 (1 + 2^-24); v_rcp_f32 within 1 ulp, the product within
+// half an ulp); where that estimate lies more than 1e-4 away from every
+// half-integer both round to the same integer, and elsewhere -- ties, NaN,
+// infinities, and scales below 2^-100 whose reciprocal would not be normal --
+// the IEEE division decides.  The results are those of the division alone.
 __device__ __forceinline__ float q_round(float u, float s) {
   if (s == 0.0f) return 0.0f;
-  const float r = __builtin_rintf(u / s);
+  const float est = u * __builtin_amdgcn_rcpf(s);
+  const float frac = fabsf(est - __builtin_truncf(est));
+  float r = __builtin_rintf(est);
+  if (__builtin_expect(!(s >= 0x1p-100f && fabsf(frac - 0.5f) > 1e-4f), 0)) r = __builtin_rintf(u / s);
   return (float)(int32_t)(r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r));
 }
 
-// max over the LANES lanes (a power of two <= 32) holding one block
-template <int LANES>
-__device__ __forceinline__ float lane_group_max(float m) {
-#pragma unroll
-  for (int o = LANES / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  return m;
+// The value of another lane of the same 16-lane row, by DPP (no LDS trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// max over the 32 lanes of a half-wavefront (one 128-element block at 4
+// elements per lane), in every lane of it: within quads by DPP quad
+// permutations (lanes i^1, i^2), across the quads of a 16-lane row by the
+// half-row and row mirrors, and across the two rows by a swizzle that swaps
+// lanes i and i^16.  A shuffle per step (ds_bpermute) cost an LDS round trip
+// and a wait each time.  The maximum does not depend on the order.
+__device__ __forceinline__ float half_wave_max(float m) {
+  m = fmaxf(m, dpp_mov<0xB1>(m));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp_mov<0x4E>(m));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp_mov<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp_mov<0x140>(m));  // row_mirror
+  return fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x401F)));  // xor 16
 }
 
 // max over the 128 threads of the workgroup (two wavefronts); red holds two
@@ -123,7 +146,8 @@ __device__ __forceinline__ void quant_lane(const float* x, const float* e, float
     u[i] = x[i] + e[i];
     m = fmaxf(m, fabsf(u[i]));
   }
-  m = lane_group_max<kQBlock / V>(m);
+  static_assert(kQBlock / V == 32, "a block is half a wavefront");
+  m = half_wave_max(m);
   const float s = q_scale(m);
   float q[V], en[V];
 #pragma unroll

@@ -101,3 +101,56 @@ def test_bound_of():
             for c in range(N + 1):
                 for shift in (-1, 0, 1):
                     assert _bound_est(M, N, c, shift) == c * M // N, (M, N, c, shift)
+
+
+def _hier_seg_est(M, N, bnd, e, shift):
+    """The hierarchical kernel's segment lookup: the flat floor chunk of e
+    (the estimate above), then the steps that settle it on the segment
+    bounds; returns the segment and the number of steps taken."""
+    s = _chunk_est(M, N, e, shift)
+    steps = 0
+    while s > 0 and e < bnd[s]:
+        s -= 1
+        steps += 1
+    while s + 1 < N and e >= bnd[s + 1]:
+        s += 1
+        steps += 1
+    return s, steps
+
+
+def _hier_segments_exact(M, dims):
+    """The nested segments cut exactly: level-0 chunks, each cut into its
+    level-1 chunks, ... as (lo, hi, code)."""
+    cur = [(0, M, 0)]
+    for i, p in enumerate(dims):
+        nxt = []
+        for lo, hi, code in cur:
+            span = hi - lo
+            for c in range(p):
+                nxt.append((lo + c * span // p, lo + (c + 1) * span // p, code | (c << (8 * i))))
+        cur = nxt
+    return cur
+
+
+def test_hier_segment_lookup():
+    """The lookup lands on the segment for any estimate; the nested floor
+    bounds stay within a few elements of the flat ones, so where segments
+    hold more than a few elements the flat chunk of an element is its
+    segment or one beside it and the lookup takes at most one step."""
+    rng = np.random.default_rng(5)
+    grids = [(2, 2, 2), (4, 2), (2, 4), (8, 8), (4, 4, 4), (3, 5), (2, 3, 4, 2), (7, 9), (16, 4)]
+    for dims in grids:
+        N = int(np.prod(dims))
+        for _ in range(40):
+            M = int(rng.integers(1, 1 << int(rng.integers(1, 40))))
+            segs = _hier_segments_exact(M, dims)
+            bnd = [lo for lo, _, _ in segs] + [M]
+            for k, (lo, hi, _) in enumerate(segs):
+                if hi == lo:
+                    continue
+                for e in {lo, hi - 1, (lo + hi) // 2, max(lo, hi - 3), min(hi - 1, lo + 2)}:
+                    for shift in (-1, 0, 1):
+                        s, steps = _hier_seg_est(M, N, bnd, e, shift)
+                        assert s == k, (M, dims, e, shift, s, k)
+                        # with segments of more than a few elements the estimate is off by one at most
+                        assert steps <= 1 or M < 8 * N, (M, dims, e, shift, steps)
