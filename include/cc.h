@@ -38,6 +38,8 @@
  *    blocks_per_cu),
  *    CC_ERR_UNSUPPORTED for a schedule the collective does not have,
  *    CC_ERR_NO_DEVICE when no GPU is visible, CC_ERR_HIP for a launch error.
+ *    Every enum below spans the whole int range (its *_MAX_ENUM member), so
+ *    any int a C caller passes is a value of the type and is validated.
  *    cc_last_error() returns a message for the last failing call on the
  *    calling thread.
  */
@@ -58,14 +60,15 @@ typedef enum {
   CC_ERR_INVALID_ARG = 1,
   CC_ERR_UNSUPPORTED = 2,
   CC_ERR_NO_DEVICE = 3,
-  CC_ERR_HIP = 4
+  CC_ERR_HIP = 4,
+  CC_STATUS_MAX_ENUM = 0x7fffffff
 } cc_status_t;
 
-typedef enum { CC_INT32 = 0, CC_FLOAT32 = 1, CC_BFLOAT16 = 2 } cc_dtype_t;
+typedef enum { CC_INT32 = 0, CC_FLOAT32 = 1, CC_BFLOAT16 = 2, CC_DTYPE_MAX_ENUM = 0x7fffffff } cc_dtype_t;
 
 /* Elementwise operators named by the course lesson "第 3 课：分布式通信原语"
  * (核心概念, item 1: SUM, MAX, PROD). */
-typedef enum { CC_SUM = 0, CC_MAX = 1, CC_PROD = 2 } cc_op_t;
+typedef enum { CC_SUM = 0, CC_MAX = 1, CC_PROD = 2, CC_OP_MAX_ENUM = 0x7fffffff } cc_op_t;
 
 /* Schedules.  Only CC_ALGO_RING and CC_ALGO_HALVING_DOUBLING (N = 2^k) serve
  * ReduceScatter and AllGather; broadcast takes ring (chain) and
@@ -92,7 +95,8 @@ typedef enum {
   CC_ALGO_BUTTERFLY = 2,        /* AllReduce notes, 算法四; AllReduce only */
   CC_ALGO_TREE = 3,             /* AllReduce only */
   CC_ALGO_DOUBLE_TREE = 4,      /* AllReduce only */
-  CC_ALGO_RING_2PORT = 5        /* AllReduce only */
+  CC_ALGO_RING_2PORT = 5,       /* AllReduce only */
+  CC_ALGO_MAX_ENUM = 0x7fffffff
 } cc_algo_t;
 
 typedef enum {
@@ -100,7 +104,8 @@ typedef enum {
   CC_COLL_REDUCE_SCATTER = 1,
   CC_COLL_ALL_GATHER = 2,
   CC_COLL_BROADCAST = 3,
-  CC_COLL_ALL_TO_ALL = 4
+  CC_COLL_ALL_TO_ALL = 4,
+  CC_COLL_MAX_ENUM = 0x7fffffff
 } cc_coll_t;
 
 /* How a schedule is executed.
@@ -459,7 +464,12 @@ cc_status_t cc_all_to_all_step_bytes(const size_t* counts, size_t elem_per_row, 
  * counts [nranks*nranks] and local_size (nexperts, capacity ignored).
  * With records == NULL only *nrecords is set; otherwise cap must hold all of
  * them (CC_ERR_INVALID_ARG if not). */
-typedef enum { CC_A2A_MOE_DISPATCH = 1, CC_A2A_MOE_COMBINE = 2, CC_A2A_HIERARCHICAL = 3 } cc_a2a_kind_t;
+typedef enum {
+  CC_A2A_MOE_DISPATCH = 1,
+  CC_A2A_MOE_COMBINE = 2,
+  CC_A2A_HIERARCHICAL = 3,
+  CC_A2A_MAX_ENUM = 0x7fffffff
+} cc_a2a_kind_t;
 typedef struct {
   uint32_t step;
   uint32_t reserved;

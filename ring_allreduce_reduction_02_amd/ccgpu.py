@@ -18,7 +18,9 @@ import os
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libcc.so")
+# the library built next to this file; CC_LIB_PATH names another build of it
+# (the sanitizer run's)
+LIB_PATH = os.environ.get("CC_LIB_PATH") or os.path.join(HERE, "libcc.so")
 
 CC_OK, CC_ERR_INVALID_ARG, CC_ERR_UNSUPPORTED, CC_ERR_NO_DEVICE, CC_ERR_HIP = range(5)
 DTYPES = {"int32": 0, "f32": 1, "bf16": 2}

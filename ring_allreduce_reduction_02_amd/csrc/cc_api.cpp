@@ -39,7 +39,15 @@ cc_status_t ok() {
   return CC_OK;
 }
 
+// a launch the LDS guard refused on this thread, not yet reported
+thread_local std::string g_refusal;
+
 cc_status_t hip_status(hipError_t e, const char* what) {
+  if (!g_refusal.empty()) {
+    std::string why;
+    why.swap(g_refusal);
+    return fail(CC_ERR_UNSUPPORTED, "%s: %s", what, why.c_str());
+  }
   if (e == hipSuccess) return ok();
   return fail(CC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -116,6 +124,9 @@ bool same_side(const cc_rankbuf_t& a, const cc_rankbuf_t& b) {
 }
 
 }  // namespace api
+
+void refuse_launch(const char* why) { api::g_refusal = why; }
+
 }  // namespace cc
 
 using namespace cc::api;
@@ -358,6 +369,7 @@ const char* cc_status_string(cc_status_t s) {
     case CC_ERR_UNSUPPORTED: return "CC_ERR_UNSUPPORTED";
     case CC_ERR_NO_DEVICE: return "CC_ERR_NO_DEVICE";
     case CC_ERR_HIP: return "CC_ERR_HIP";
+    default: break;
   }
   return "CC_ERR_UNKNOWN";
 }

@@ -192,7 +192,7 @@ hipError_t launch_moe_rows(const MoeLaunch& L) {
   // tokens (top-8 of 64 experts, rows of 14,336 bytes) ran at 5.66 TB/s
   // against 5.49 at full occupancy, the combine at 5.72 against 5.56
   const unsigned lds = lds_for_blocks_per_cu(L.blocks_per_cu > 0 ? L.blocks_per_cu : 8);
-  hipLaunchKernelGGL(k_moe_rows, grid, blk, lds, L.st, a);
+  CC_LAUNCH(k_moe_rows, grid, blk, lds, L.st, a);
   return hipGetLastError();
 }
 
@@ -204,7 +204,7 @@ hipError_t launch_bcast(const char* src, Side dst, int N, int skip, uint64_t nby
   const dim3 grid((unsigned)((nbytes + kBcastTile - 1) / kBcastTile)), blk(kCopyBlock);
   const int nw = skip >= 0 ? N - 1 : N;
   const unsigned lds = occupancy_lds(blocks_per_cu, kBcastTile * (nw + 1), kBcastTarget);
-  hipLaunchKernelGGL(k_bcast, grid, blk, lds, st, a);
+  CC_LAUNCH(k_bcast, grid, blk, lds, st, a);
   return hipGetLastError();
 }
 
@@ -221,7 +221,7 @@ hipError_t launch_copies(const CopyDesc* d, int n, int esize, int blocks_per_cu,
   if (a.n == 0) return hipSuccess;
   const dim3 grid((unsigned)a.tpre[a.n]), blk(kCopyBlock);
   const unsigned lds = blocks_per_cu > 0 ? lds_for_blocks_per_cu(blocks_per_cu) : 0;
-  hipLaunchKernelGGL(k_copies, grid, blk, lds, st, a);
+  CC_LAUNCH(k_copies, grid, blk, lds, st, a);
   return hipGetLastError();
 }
 

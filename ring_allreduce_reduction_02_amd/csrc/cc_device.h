@@ -8,10 +8,12 @@
 
 #include <stdint.h>
 
+#include <cstdio>
 #include <mutex>
 #include <type_traits>
 
 #include "cc_launch.h"
+#include "cc_lds.h"
 
 namespace cc {
 namespace {
@@ -600,7 +602,34 @@ DevInfo dev_info() {
   return cache[d];
 }
 
+// Static LDS of a kernel (its __shared__ declarations), from the runtime.
+unsigned kernel_static_lds(const void* k) {
+  hipFuncAttributes at;
+  return hipFuncGetAttributes(&at, k) == hipSuccess ? (unsigned)at.sharedSizeBytes : 0u;
+}
+
+// A launch whose static plus dynamic LDS would exceed the per-workgroup
+// limit is refused before it reaches the GPU (the call reports
+// CC_ERR_UNSUPPORTED).
+hipError_t refuse_lds(unsigned static_bytes, unsigned dynamic_bytes) {
+  char why[160];
+  snprintf(why, sizeof why, "a kernel's LDS (%u static + %u reserved bytes) exceeds the %d bytes a workgroup may use",
+           static_bytes, dynamic_bytes, dev_info().lds_per_block);
+  refuse_launch(why);
+  return hipErrorInvalidConfiguration;
+}
+
 }  // namespace
+
+// Every kernel launch of the library: the LDS guard, then the launch.  The
+// kernel's static LDS is queried once per launch site and instantiation.
+#define CC_LAUNCH(K, GRID, BLK, LDS, ST, ...)                                                  \
+  do {                                                                                          \
+    static const unsigned cc_static_lds_ = ::cc::kernel_static_lds(reinterpret_cast<const void*>(K)); \
+    if (!lds_fits(cc_static_lds_, (LDS), ::cc::dev_info().lds_per_block))                      \
+      return ::cc::refuse_lds(cc_static_lds_, (LDS));                                           \
+    hipLaunchKernelGGL(K, GRID, BLK, LDS, ST, __VA_ARGS__);                                     \
+  } while (0)
 
 namespace {
 constexpr uint64_t kBalancedTarget = 64 * 1024;

@@ -248,7 +248,7 @@ hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int 
                                                                  : one_round_blocks(num_tiles(r.M, r.dt), hier_blocks_per_cu(r.N)));
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_hier_fused<DT, OP>), grid, blk, lds, r.st, a);
+    CC_LAUNCH((k_hier_fused<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }

@@ -193,12 +193,12 @@ hipError_t launch_ring_fused(const Red& r) {
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     switch (r.N) {
-      case 2: hipLaunchKernelGGL((k_ring_fused<DT, OP, 2>), grid, blk, lds, r.st, a); break;
-      case 3: hipLaunchKernelGGL((k_ring_fused<DT, OP, 3>), grid, blk, lds, r.st, a); break;
-      case 4: hipLaunchKernelGGL((k_ring_fused<DT, OP, 4>), grid, blk, lds, r.st, a); break;
-      case 8: hipLaunchKernelGGL((k_ring_fused<DT, OP, 8>), grid, blk, lds, r.st, a); break;
-      case 16: hipLaunchKernelGGL((k_ring_fused<DT, OP, 16>), grid, blk, lds, r.st, a); break;
-      default: hipLaunchKernelGGL((k_ring_fused<DT, OP, 0>), grid, blk, lds, r.st, a); break;
+      case 2: CC_LAUNCH((k_ring_fused<DT, OP, 2>), grid, blk, lds, r.st, a); break;
+      case 3: CC_LAUNCH((k_ring_fused<DT, OP, 3>), grid, blk, lds, r.st, a); break;
+      case 4: CC_LAUNCH((k_ring_fused<DT, OP, 4>), grid, blk, lds, r.st, a); break;
+      case 8: CC_LAUNCH((k_ring_fused<DT, OP, 8>), grid, blk, lds, r.st, a); break;
+      case 16: CC_LAUNCH((k_ring_fused<DT, OP, 16>), grid, blk, lds, r.st, a); break;
+      default: CC_LAUNCH((k_ring_fused<DT, OP, 0>), grid, blk, lds, r.st, a); break;
     }
     return hipGetLastError();
   });
@@ -213,9 +213,9 @@ hipError_t launch_tree_fused(const Red& r, int tree) {
 #define CC_TREE_CASE(NR)                                                                      \
   case NR:                                                                                    \
     if (tree == TREE_HD)                                                                      \
-      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_HD>), grid, blk, lds, r.st, a);       \
+      CC_LAUNCH((k_tree_fused<DT, OP, NR, TREE_HD>), grid, blk, lds, r.st, a);       \
     else                                                                                      \
-      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_BFLY>), grid, blk, lds, r.st, a);     \
+      CC_LAUNCH((k_tree_fused<DT, OP, NR, TREE_BFLY>), grid, blk, lds, r.st, a);     \
     break;
     switch (r.N) {
       CC_TREE_CASE(2)
@@ -243,7 +243,7 @@ hipError_t launch_tree_shaped(const Red& r, int tree, int nr, int leaves, int pa
       // binomial tree with a compile-time rank count
       switch (leaves) {
 #define CC_BTREE_CASE(NN) \
-  case NN: hipLaunchKernelGGL((k_btree_fused<DT, OP, NN>), grid, blk, lds, r.st, a); break;
+  case NN: CC_LAUNCH((k_btree_fused<DT, OP, NN>), grid, blk, lds, r.st, a); break;
         CC_BTREE_CASE(3) CC_BTREE_CASE(5) CC_BTREE_CASE(6) CC_BTREE_CASE(7) CC_BTREE_CASE(9)
         CC_BTREE_CASE(10) CC_BTREE_CASE(11) CC_BTREE_CASE(12) CC_BTREE_CASE(13) CC_BTREE_CASE(14)
         CC_BTREE_CASE(15)
@@ -255,9 +255,9 @@ hipError_t launch_tree_shaped(const Red& r, int tree, int nr, int leaves, int pa
 #define CC_SHAPED_CASE(NR)                                                                    \
   case NR:                                                                                    \
     if (tree == TREE_HD)                                                                      \
-      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_HD>), grid, blk, lds, r.st, a);       \
+      CC_LAUNCH((k_tree_fused<DT, OP, NR, TREE_HD>), grid, blk, lds, r.st, a);       \
     else                                                                                      \
-      hipLaunchKernelGGL((k_tree_fused<DT, OP, NR, TREE_BFLY>), grid, blk, lds, r.st, a);     \
+      CC_LAUNCH((k_tree_fused<DT, OP, NR, TREE_BFLY>), grid, blk, lds, r.st, a);     \
     break;
     switch (nr) {
       CC_SHAPED_CASE(2)

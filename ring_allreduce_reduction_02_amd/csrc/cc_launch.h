@@ -30,6 +30,11 @@ unsigned lds_for_blocks_per_cu(int blocks);
 // `target` bytes in flight per CU, at least `min_blocks`
 int default_blocks_per_cu(uint64_t traffic, uint64_t target, int min_blocks);
 
+// The launch guard's refusal (cc_device.h): the launch returns
+// hipErrorInvalidConfiguration and the API call reports CC_ERR_UNSUPPORTED
+// with this text.
+void refuse_launch(const char* why);
+
 // Rank-strided view: rank r at base + r * stride (bytes).
 struct Side {
   char* base;

@@ -417,8 +417,8 @@ hipError_t launch_quant_ef(const QLaunch& L) {
   const QArgs a = q_args(L);
   const dim3 grid((unsigned)((L.M + kQTile - 1) / kQTile), (unsigned)L.N), blk(kBlock);
   const unsigned lds = q_lds(L.blocks_per_cu, quant_blocks_per_cu(L.dt));
-  if (L.dt == DT_F32) hipLaunchKernelGGL((k_quant_ef<DT_F32>), grid, blk, lds, L.st, a);
-  else hipLaunchKernelGGL((k_quant_ef<DT_BF16>), grid, blk, lds, L.st, a);
+  if (L.dt == DT_F32) CC_LAUNCH((k_quant_ef<DT_F32>), grid, blk, lds, L.st, a);
+  else CC_LAUNCH((k_quant_ef<DT_BF16>), grid, blk, lds, L.st, a);
   return hipGetLastError();
 }
 
@@ -430,8 +430,8 @@ hipError_t launch_dequant_reduce(const QLaunch& L) {
   const dim3 grid((unsigned)tiles), blk(kBlock);
   unsigned lds = q_lds(L.blocks_per_cu, dequant_blocks_per_cu(L.dt));
   if (lds < kDqLds) lds = kDqLds;
-  if (L.dt == DT_F32) hipLaunchKernelGGL((k_dequant_reduce<DT_F32>), grid, blk, lds, L.st, a);
-  else hipLaunchKernelGGL((k_dequant_reduce<DT_BF16>), grid, blk, lds, L.st, a);
+  if (L.dt == DT_F32) CC_LAUNCH((k_dequant_reduce<DT_F32>), grid, blk, lds, L.st, a);
+  else CC_LAUNCH((k_dequant_reduce<DT_BF16>), grid, blk, lds, L.st, a);
   return hipGetLastError();
 }
 
@@ -440,8 +440,8 @@ hipError_t launch_quant_ef_fused(const QLaunch& L) {
   const QArgs a = q_args(L);
   const dim3 grid((unsigned)((L.M + kQTile - 1) / kQTile)), blk(kBlock);
   const unsigned lds = q_lds(L.blocks_per_cu, qfused_blocks_per_cu(L.dt));
-  if (L.dt == DT_F32) hipLaunchKernelGGL((k_quant_ef_fused<DT_F32>), grid, blk, lds, L.st, a);
-  else hipLaunchKernelGGL((k_quant_ef_fused<DT_BF16>), grid, blk, lds, L.st, a);
+  if (L.dt == DT_F32) CC_LAUNCH((k_quant_ef_fused<DT_F32>), grid, blk, lds, L.st, a);
+  else CC_LAUNCH((k_quant_ef_fused<DT_BF16>), grid, blk, lds, L.st, a);
   return hipGetLastError();
 }
 

@@ -674,7 +674,7 @@ hipError_t launch_gsteps(const Red& r, const GDesc* d, int n) {
   const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 4, kSkewedTarget);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_gsteps<DT, OP>), grid, blk, lds, r.st, a);
+    CC_LAUNCH((k_gsteps<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }
@@ -693,7 +693,7 @@ hipError_t launch_ring_rs_pass(const Red& r, int s0, int k, int partial_in_recv)
   const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * (k + 2), kSkewedTarget);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_ring_pass<DT, OP>), grid, blk, lds, r.st, a);
+    CC_LAUNCH((k_ring_pass<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }
@@ -738,12 +738,12 @@ hipError_t launch_ring_queue(const Red& r, int k, unsigned* bar) {
   if (lds < 16) lds = 16;  // the claim word
   const DevInfo di = dev_info();
   if (di.lds_per_block > 0 && lds > (unsigned)di.lds_per_block) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(256), 0, r.st, bar, 2 + 2 * a.npass);
+  CC_LAUNCH(k_clear_words, dim3(1), dim3(256), 0, r.st, bar, 2 + 2 * a.npass);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 grid(a.nclaims), blk(kBlock);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_ring_queue<DT, OP>), grid, blk, lds, r.st, a);
+    CC_LAUNCH((k_ring_queue<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }
@@ -766,7 +766,7 @@ hipError_t launch_hd_rs_step(const Red& r, int d, int first, int last, int acc_i
   const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 3 * d, kSkewedTarget);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_hd_rs_step<DT, OP>), grid, blk, lds, r.st, a);
+    CC_LAUNCH((k_hd_rs_step<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }
@@ -777,7 +777,7 @@ hipError_t launch_bfly_step(const Red& r, int d, int first, int last, int acc_in
   const unsigned lds = occupancy_lds(r.blocks_per_cu, kVecBytes * 2 * r.N, kSkewedTarget);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    hipLaunchKernelGGL((k_bfly_step<DT, OP>), grid, blk, lds, r.st, a);
+    CC_LAUNCH((k_bfly_step<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
 }
@@ -802,8 +802,8 @@ hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k) {
   const GatArgs a = gat_args(g, s0, k);
   const dim3 grid(gat_tiles(g)), blk(kBlock);
   const unsigned lds = occupancy_lds(g.blocks_per_cu, kVecBytes * (k + 2), kSkewedTarget);
-  if (g.esize == 2) hipLaunchKernelGGL((k_ring_ag_pass<2>), grid, blk, lds, g.st, a);
-  else hipLaunchKernelGGL((k_ring_ag_pass<4>), grid, blk, lds, g.st, a);
+  if (g.esize == 2) CC_LAUNCH((k_ring_ag_pass<2>), grid, blk, lds, g.st, a);
+  else CC_LAUNCH((k_ring_ag_pass<4>), grid, blk, lds, g.st, a);
   return hipGetLastError();
 }
 
@@ -826,8 +826,8 @@ hipError_t launch_hd_ag_step(const Gat& g, int d, int first) {
   const GatArgs a = gat_args(g, d, first);
   const dim3 grid(gat_tiles(g)), blk(kBlock);
   const unsigned lds = occupancy_lds(g.blocks_per_cu, kVecBytes * 2 * d, kSkewedTarget);
-  if (g.esize == 2) hipLaunchKernelGGL((k_hd_ag_step<2>), grid, blk, lds, g.st, a);
-  else hipLaunchKernelGGL((k_hd_ag_step<4>), grid, blk, lds, g.st, a);
+  if (g.esize == 2) CC_LAUNCH((k_hd_ag_step<2>), grid, blk, lds, g.st, a);
+  else CC_LAUNCH((k_hd_ag_step<4>), grid, blk, lds, g.st, a);
   return hipGetLastError();
 }
 

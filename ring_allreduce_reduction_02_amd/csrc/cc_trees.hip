@@ -334,9 +334,9 @@ hipError_t launch_dbt_fused(const Red& r) {
 #define CC_DBT_CASE(NR)                                                                       \
   case NR:                                                                                     \
     if (r.N == NR)                                                                             \
-      hipLaunchKernelGGL((k_dbt_fused<DT, OP, NR, true>), grid, blk, lds, r.st, a);            \
+      CC_LAUNCH((k_dbt_fused<DT, OP, NR, true>), grid, blk, lds, r.st, a);            \
     else                                                                                       \
-      hipLaunchKernelGGL((k_dbt_fused<DT, OP, NR, false>), grid, blk, lds, r.st, a);           \
+      CC_LAUNCH((k_dbt_fused<DT, OP, NR, false>), grid, blk, lds, r.st, a);           \
     break;
     switch (nr) {
       CC_DBT_CASE(2)
@@ -357,12 +357,12 @@ hipError_t launch_ring2_fused(const Red& r) {
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     switch (r.N) {
-      case 4: hipLaunchKernelGGL((k_ring2_fused<DT, OP, 4, true>), grid, blk, lds, r.st, a); break;
-      case 8: hipLaunchKernelGGL((k_ring2_fused<DT, OP, 8, true>), grid, blk, lds, r.st, a); break;
-      case 16: hipLaunchKernelGGL((k_ring2_fused<DT, OP, 16, true>), grid, blk, lds, r.st, a); break;
+      case 4: CC_LAUNCH((k_ring2_fused<DT, OP, 4, true>), grid, blk, lds, r.st, a); break;
+      case 8: CC_LAUNCH((k_ring2_fused<DT, OP, 8, true>), grid, blk, lds, r.st, a); break;
+      case 16: CC_LAUNCH((k_ring2_fused<DT, OP, 16, true>), grid, blk, lds, r.st, a); break;
       default:
-        if (r.N <= 16) hipLaunchKernelGGL((k_ring2_fused<DT, OP, 16, false>), grid, blk, lds, r.st, a);
-        else hipLaunchKernelGGL((k_ring2_fused<DT, OP, 0, false>), grid, blk, lds, r.st, a);
+        if (r.N <= 16) CC_LAUNCH((k_ring2_fused<DT, OP, 16, false>), grid, blk, lds, r.st, a);
+        else CC_LAUNCH((k_ring2_fused<DT, OP, 0, false>), grid, blk, lds, r.st, a);
     }
     return hipGetLastError();
   });
@@ -391,18 +391,18 @@ hipError_t launch_fused_seg(const SegLaunch& L) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     if (L.alg == ALG_RING) {
       switch (L.N) {
-        case 4: hipLaunchKernelGGL((k_fused_seg<DT, OP, 4, ALG_RING>), grid, blk, lds, L.st, a); break;
-        case 8: hipLaunchKernelGGL((k_fused_seg<DT, OP, 8, ALG_RING>), grid, blk, lds, L.st, a); break;
-        case 16: hipLaunchKernelGGL((k_fused_seg<DT, OP, 16, ALG_RING>), grid, blk, lds, L.st, a); break;
-        default: hipLaunchKernelGGL((k_fused_seg<DT, OP, 0, ALG_RING>), grid, blk, lds, L.st, a); break;
+        case 4: CC_LAUNCH((k_fused_seg<DT, OP, 4, ALG_RING>), grid, blk, lds, L.st, a); break;
+        case 8: CC_LAUNCH((k_fused_seg<DT, OP, 8, ALG_RING>), grid, blk, lds, L.st, a); break;
+        case 16: CC_LAUNCH((k_fused_seg<DT, OP, 16, ALG_RING>), grid, blk, lds, L.st, a); break;
+        default: CC_LAUNCH((k_fused_seg<DT, OP, 0, ALG_RING>), grid, blk, lds, L.st, a); break;
       }
     } else {
 #define CC_SEG_CASE(NR)                                                                        \
   case NR:                                                                                     \
     if (L.alg == ALG_HD)                                                                       \
-      hipLaunchKernelGGL((k_fused_seg<DT, OP, NR, ALG_HD>), grid, blk, lds, L.st, a);          \
+      CC_LAUNCH((k_fused_seg<DT, OP, NR, ALG_HD>), grid, blk, lds, L.st, a);          \
     else                                                                                       \
-      hipLaunchKernelGGL((k_fused_seg<DT, OP, NR, ALG_BFLY>), grid, blk, lds, L.st, a);        \
+      CC_LAUNCH((k_fused_seg<DT, OP, NR, ALG_BFLY>), grid, blk, lds, L.st, a);        \
     break;
       switch (L.N) {
         CC_SEG_CASE(2)
