@@ -208,53 +208,61 @@ class Trace:
 # ring schedule
 # --------------------------------------------------------------------------
 
+def _ring_transfers(N: int, s: int, first: Sequence[int]) -> List[Tuple[int, int, int]]:
+    """The transfers of ring step s as (sender, receiver, chunk), one per
+    receiver in rank order: every rank receives from its left neighbour
+    i = (r - 1) mod N, which passes on chunk (first[i] - s) mod N -- the
+    chunk it passed on at step 0, moved back by one per step ([AR-notes],
+    "算法一：Ring AllReduce": at step s rank i sends chunk (i - s) mod N)."""
+    return [((r - 1) % N, r, (first[(r - 1) % N] - s) % N) for r in range(N)]
+
+
+def _synchronous_step(acc: List[np.ndarray], b: List[int], transfers, deliver, tr: Trace) -> None:
+    """One step of the schedule: every message is read off its sender before
+    any receiver changes, then each is handed to deliver(receiver row, lo, hi,
+    payload) ([Lesson3], reference answer: a step's sends are copied first, so
+    that no rank reads data already updated in the same step)."""
+    wire = [(src, dst, c, acc[src][b[c]:b[c + 1]].copy()) for src, dst, c in transfers]
+    for src, dst, c, payload in wire:
+        deliver(acc[dst], b[c], b[c + 1], payload)
+        tr.sent[src] += b[c + 1] - b[c]
+    tr.steps.append([(src, dst, c, b[c + 1] - b[c]) for src, dst, c, _ in wire])
+
+
 def _ring_rs_phase(acc: List[np.ndarray], b: List[int], op: str, off: int,
                    tr: Trace) -> None:
     """Ring ReduceScatter phase, N-1 steps.
 
-    At step s rank r sends its chunk (r - s + off) mod N to rank r+1 and
-    combines the chunk (r - s - 1 + off) mod N received from rank r-1 into its
-    own copy ([AR-notes], "算法一：Ring AllReduce", 阶段 1; [Slides], "环形
-    ReduceScatter"; [Lesson3], simulator reference answer).  off = 0 is the
+    At step s rank r sends its chunk (r - s + off) mod N to rank r+1, which
+    folds it into its own copy as op(own, incoming) ([AR-notes], "算法一：Ring
+    AllReduce", 阶段 1; [Slides], "环形 ReduceScatter").  off = 0 is the
     pages' formula, used inside AllReduce: rank r ends owning chunk (r+1) mod N.
     off = -1 is the standalone ReduceScatter, whose contract puts chunk r on
     rank r ([Slides], primitives table and the 3-rank example).
     """
     N = len(acc)
+    first = [(r + off) % N for r in range(N)]
+
+    def fold(row, lo, hi, payload):
+        row[lo:hi] = combine(op, row[lo:hi], payload)
+
     for s in range(N - 1):
-        send_idx = [(r - s + off) % N for r in range(N)]
-        sent = [acc[r][b[send_idx[r]]:b[send_idx[r] + 1]].copy() for r in range(N)]
-        step = []
-        for r in range(N):
-            src = (r - 1) % N
-            recv_idx = (r - s - 1 + off) % N
-            assert recv_idx == send_idx[src]
-            lo, hi = b[recv_idx], b[recv_idx + 1]
-            acc[r][lo:hi] = combine(op, acc[r][lo:hi], sent[src])
-            tr.sent[src] += hi - lo
-            step.append((src, r, recv_idx, hi - lo))
-        tr.steps.append(step)
+        _synchronous_step(acc, b, _ring_transfers(N, s, first), fold, tr)
 
 
 def _ring_ag_phase(acc: List[np.ndarray], b: List[int], own: List[int],
                    tr: Trace) -> None:
     """Ring AllGather phase, N-1 steps: each rank forwards what it received in
-    the previous step ([Slides], "环形 AllGather"; [Lesson3], simulator phase 2).
-    own[r] is the chunk rank r holds complete at the start.  At step s rank r
-    sends chunk (own[r] - s) mod N and stores chunk (own[r-1] - s) mod N."""
+    the previous step ([Slides], "环形 AllGather").  own[r] is the chunk rank r
+    holds complete at the start: at step s it sends chunk (own[r] - s) mod N,
+    which its right neighbour stores."""
     N = len(acc)
+
+    def store(row, lo, hi, payload):
+        row[lo:hi] = payload
+
     for s in range(N - 1):
-        send_idx = [(own[r] - s) % N for r in range(N)]
-        sent = [acc[r][b[send_idx[r]]:b[send_idx[r] + 1]].copy() for r in range(N)]
-        step = []
-        for r in range(N):
-            src = (r - 1) % N
-            recv_idx = send_idx[src]
-            lo, hi = b[recv_idx], b[recv_idx + 1]
-            acc[r][lo:hi] = sent[src]
-            tr.sent[src] += hi - lo
-            step.append((src, r, recv_idx, hi - lo))
-        tr.steps.append(step)
+        _synchronous_step(acc, b, _ring_transfers(N, s, own), store, tr)
 
 
 def ring_all_reduce(xs: Sequence[np.ndarray], op: str = "sum", dtype: str = "f32",
