@@ -29,6 +29,10 @@ LIMITER = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_
            "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_VMEM_RD GRBM_GUI_ACTIVE")
 
 # name: (trace source, kernel name substring, csrc file, profiles/ output, workload)
+# The default benchmark run also launches the bf16 ring kernel once per
+# gradient bucket: the headline entries time only the dispatches of their own
+# grid (one work-item per 16-byte vector of a rank's M elements).
+BENCH_GRID = {"ring_f32": 67108864 * 4 // 16, "ring_bf16": 67108864 * 2 // 16}
 ENTRIES = {
     "ring_f32": ("bench", "k_ring_fused<1, 0, 8>", "cc_kernels.hip", "ring_fused_f32_n8_m67108864",
                  "fused ring AllReduce, N=8 logical ranks, M=67108864 fp32 per rank (the benchmark's headline)"),
@@ -124,6 +128,8 @@ def summarize(d, names):
                "--copy-bytes", str(COPY_BYTES), "--alg-bytes", str(alg), "--out", f"profiles/{out}",
                "--trace-command", trace, "--pmc-command", pmc["fetch"].replace("FETCH_SIZE", "<FETCH_SIZE|WRITE_SIZE>"),
                "--workload", workload, "--note", note, "--source", csrc]
+        if name in BENCH_GRID:
+            cmd += ["--grid", str(BENCH_GRID[name])]
         if os.path.isdir(f"{d}/{name}_xcheck"):
             cmd += ["--xcheck", f"{d}/{name}_xcheck", "--xcheck-command", pmc["xcheck"]]
         if os.path.isdir(f"{d}/{name}_limiter"):

@@ -56,6 +56,19 @@ def kernel_stats(trace_dir: str, needle: str):
     raise KeyError(needle)
 
 
+def kernel_stats_of_grid(trace_dir: str, needle: str, grid: int):
+    """Stats of the dispatches of the kernel whose grid holds `grid`
+    work-items (x), from the per-dispatch trace: a run that launches the
+    kernel at several sizes then averages only the launches of one size."""
+    rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))))
+    mine = [r for r in rows if needle in r["Kernel_Name"]]
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in mine if int(r["Grid_Size_X"]) == grid]
+    if not durs:
+        raise KeyError(f"{needle} with a grid of {grid}")
+    return {"Calls": len(durs), "AverageNs": sum(durs) / len(durs), "MinNs": min(durs), "MaxNs": max(durs),
+            "other_calls": len(mine) - len(durs)}
+
+
 # The files a kernel's code comes from, besides its own source file: what the
 # kernel sources share, and the launch interface.
 SHARED_SOURCES = ("cc_device.h", "cc_launch.h")
@@ -110,9 +123,11 @@ def main():
     ap.add_argument("--workload", required=True)
     ap.add_argument("--note", default="", help="how the algorithmic bytes per launch are counted")
     ap.add_argument("--source", default="cc_kernels.hip", help="the csrc file that defines the kernel")
+    ap.add_argument("--grid", type=int, default=0,
+                    help="time only the dispatches of this many work-items (x) (0: every dispatch of the kernel)")
     args = ap.parse_args()
 
-    st = kernel_stats(args.trace, args.kernel)
+    st = kernel_stats_of_grid(args.trace, args.kernel, args.grid) if args.grid else kernel_stats(args.trace, args.kernel)
     fetch = counter_means(args.fetch, "FETCH_SIZE")
     write = counter_means(args.write, "WRITE_SIZE")
     kname, (f_kib, f_n) = pick(fetch, args.kernel)
@@ -131,6 +146,8 @@ def main():
         "kernel_sources": kernel_sources(args.source),
         "kernel_source_sha256_16": sources_hash(kernel_sources(args.source)),
         "calls": int(st["Calls"]),
+        "grid_size_x": args.grid or None,
+        "calls_at_other_grids": st.get("other_calls", 0),
         "avg_ns": avg_ns,
         "min_ns": float(st["MinNs"]),
         "max_ns": float(st["MaxNs"]),
@@ -165,6 +182,9 @@ def main():
             f.write(f"Algorithmic bytes per launch: {args.alg_bytes} ({args.note}).\n\n")
         f.write("## rocprofv3 --kernel-trace --stats\n\n")
         f.write(f"Command: `{args.trace_command}`\n\n")
+        if args.grid:
+            f.write(f"Only the dispatches with a grid of {args.grid} work-items are timed; the run also launches the "
+                    f"kernel {rec['calls_at_other_grids']} times at other sizes.\n\n")
         f.write("| calls | avg us | min us | max us | algorithmic GB | GB/s at avg |\n|---|---|---|---|---|---|\n")
         f.write(f"| {rec['calls']} | {avg_ns / 1e3:.2f} | {rec['min_ns'] / 1e3:.2f} | {rec['max_ns'] / 1e3:.2f} | "
                 f"{args.alg_bytes / 1e9:.3f} | {rec['achieved_GBps_from_trace']:.1f} |\n\n")
@@ -205,12 +225,16 @@ def main():
     print(json.dumps(rec, indent=1))
 
 
+XCDS = 8
+
+
 def limiter_counters(run_dir: str, kernel: str):
     """Per-dispatch wave counters of the kernel and the ratios read from them:
     the share of the waves' cycles spent issuing VALU instructions, and spent
     waiting for an operand (a load in flight, mostly), and the VALU busy share
     of the SIMDs (SQ_ACTIVE_INST_VALU counts per wave in 4-cycle units; 1024
-    SIMDs)."""
+    SIMDs; GRBM_GUI_ACTIVE reads as the sum over the 8 XCDs: 1.18e7 for a
+    665.7 us launch is 8 x 2.2 GHz)."""
     rows = list(csv.DictReader(open(_one(os.path.join(run_dir, "**", "*counter_collection.csv")))))
     raw = {}
     for name in sorted({r["Counter_Name"] for r in rows}):
@@ -221,7 +245,7 @@ def limiter_counters(run_dir: str, kernel: str):
         der["valu_cycles_over_wave_cycles"] = raw.get("SQ_ACTIVE_INST_VALU", 0.0) / raw["SQ_WAVE_CYCLES"]
         der["wait_any_over_wave_cycles"] = raw.get("SQ_WAIT_INST_ANY", 0.0) / raw["SQ_WAVE_CYCLES"]
     if raw.get("GRBM_GUI_ACTIVE"):
-        der["valu_busy_of_simds"] = raw.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / 1024 / raw["GRBM_GUI_ACTIVE"]
+        der["valu_busy_of_simds"] = raw.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / 1024 / (raw["GRBM_GUI_ACTIVE"] / XCDS)
     if raw.get("SQ_WAVES"):
         der["valu_insts_per_wave"] = raw.get("SQ_INSTS_VALU", 0.0) / raw["SQ_WAVES"]
         der["vmem_rd_insts_per_wave"] = raw.get("SQ_INSTS_VMEM_RD", 0.0) / raw["SQ_WAVES"]
