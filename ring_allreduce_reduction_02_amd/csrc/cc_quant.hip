@@ -216,91 +216,93 @@ __global__ __launch_bounds__(kBlock) void k_quant_ef(QArgs a) {
 // The reduction of the messages: every element folds the dequantized values
 // of all ranks in the ring order of its chunk, and every rank gets the result.
 //
-// A workgroup takes a wide tile of kDqTile elements of every rank: a lane
-// reads 16 consecutive int8 values of a rank with one 16-byte load (and the
-// one block scale they share), so the tile's 16 block scales of a rank are
-// half of a 128-byte line, read by two workgroups.  With one 512-element
-// tile per workgroup (4-byte int8 loads) the eight workgroups sharing a line
-// ran on the eight XCDs and each XCD's L2 fetched it again: 4.35% more HBM
-// traffic than the kernel's algorithmic bytes.  The lane's 16 results go
-// through LDS to the store layout, in which every 16-byte store instruction
-// of a wavefront writes 1 KiB of consecutive output; each wavefront
-// exchanges its own 1024 results, so no workgroup barrier is needed.
-// Measured on the MI355X (8 ranks x 67,108,864, fp32 results, rows 256 MiB
-// apart): 5.75 TB/s at 3 workgroups per CU, against 5.59 for the 512-element
-// tiles; one workgroup looping over two such tiles to read the whole scale
-// line ran at 5.53 at best, and 4-byte loads over eight 512-element tiles per
-// workgroup at 4.79.
-constexpr int kDqLane = 16;                                   // int8 values per lane and load
-constexpr uint64_t kDqTile = (uint64_t)kBlock * kDqLane;      // 2048 elements: 16 blocks
-constexpr unsigned kDqLds = kBlock * kDqLane * 4;             // the transposition's 8 KiB
+// A workgroup of kDqThreads threads takes a tile of kDqTile elements of every
+// rank, 4 per thread.  The int8 values come in with 16-byte loads (a thread
+// loads 16 values of one rank) and are staged in LDS, 8 ranks at a time;
+// after the barrier each thread folds its 4 elements over those ranks and,
+// at the end, stores its 4 results to every rank with one store each, so
+// that every store instruction of a wavefront writes consecutive output (1
+// KiB for float32 results).  Measured on the MI355X (8 ranks x 67,108,864,
+// rows 256 MiB apart, three interleaved runs on one GPU): 1024-element tiles
+// in the XCD order below 5.78 TB/s with float32 results and 6.04 with bf16;
+// 2048-element tiles 5.63 and 5.86 in launch order, 5.49 and 6.02 in XCD
+// order; the earlier design (128 threads of 16 elements, each storing 4
+// times per rank after a wave-local LDS transpose) 5.75 and 5.71.
+constexpr uint64_t kDqTile = 1024;
+constexpr int kDqThreads = (int)(kDqTile / 4);
+constexpr int kDqBatch = 8;                                   // ranks staged per pass
+constexpr unsigned kDqLds = kDqBatch * (unsigned)kDqTile;     // their int8 values
 
-// An exchange through LDS between the lanes of one wavefront: the LDS serves
-// a wavefront's accesses in issue order, so it takes no workgroup barrier
-// (whose release would also wait for the wavefront's global stores); this
-// waits for the wavefront's LDS writes issued so far and keeps the compiler
-// from moving memory accesses across it.
-__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-__device__ __forceinline__ void unpack_i8x16(u32x4 w, float* q) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) q[i] = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
+// Workgroups go to the 8 XCDs in turn (workgroup b to XCD b mod 8), each XCD
+// with its own L2.  The kDqLine tiles whose block scales share one 128-byte
+// line are given to workgroups of one XCD, so that the line is fetched once:
+// workgroup b = 8 slot + x takes tile ((slot / G) 8 + x) G + slot mod G, G =
+// kDqLine, over the whole groups of 8 G tiles; the rest keep their index.
+constexpr uint32_t kDqLine = (uint32_t)(32 * kQBlock / kDqTile);
+__device__ __forceinline__ uint64_t dq_tile(uint32_t b, uint64_t tiles) {
+  const uint64_t whole = tiles / (8 * kDqLine) * (8 * kDqLine);
+  if (b >= whole) return b;
+  const uint32_t x = b & 7u, slot = b >> 3;
+  return ((uint64_t)(slot / kDqLine) * 8 + x) * kDqLine + slot % kDqLine;
 }
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_dequant_reduce(QArgs a) {
-  extern __shared__ float qlds[];
+__global__ __launch_bounds__(kDqThreads) void k_dequant_reduce(QArgs a) {
+  extern __shared__ uint32_t qst[];  // [kDqBatch][kDqTile / 4] words of 4 int8 values
   constexpr int SZ = Ty<DT>::SZ;
-  constexpr int VO = Ty<DT>::V;  // output elements per 16-byte store
+  constexpr int LPR = (int)(kDqTile / 16);  // loading threads per rank
+  constexpr int RPL = kDqThreads / LPR;      // ranks per load instruction
   const int N = a.N;
-  const uint64_t t0 = (uint64_t)blockIdx.x * kDqTile;
+  const uint64_t t0 = dq_tile(blockIdx.x, gridDim.x) * kDqTile;
   const uint64_t t1 = t0 + kDqTile < a.M ? t0 + kDqTile : a.M;
   const uint32_t c0 = chunk_of(a.M, N, t0);
   if (a.vec_ok && t1 - t0 == kDqTile && c0 == chunk_of(a.M, N, t1 - 1)) {
-    const uint32_t lane = threadIdx.x, wl = lane & 63u, wv = lane >> 6;
-    const uint64_t el = t0 + (uint64_t)lane * kDqLane;
-    const uint64_t sb = (el / kQBlock) * 4;
-    float acc[kDqLane];
-    int r = (int)c0;
-    for (int j0 = 0; j0 < N; j0 += 8) {
-      u32x4 qw[8];
-      float sc[8];
-      int rr = r;
+    const uint32_t tid = threadIdx.x, ll = tid % LPR, ls = tid / LPR;
+    const uint64_t e4 = t0 + (uint64_t)tid * 4;  // this thread's 4 elements
+    const uint64_t sb = (e4 / kQBlock) * 4;
+    float acc[4];
+    int r = (int)c0;  // rank of the batch's first slot
+    for (int j0 = 0; j0 < N; j0 += kDqBatch) {
+      const int nb = N - j0 < kDqBatch ? N - j0 : kDqBatch;
+      if (j0) __syncthreads();  // the previous batch is read out of LDS
+      u32x4 w[kDqBatch / RPL];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {  // past the last rank the loads repeat valid ones
-        qw[k] = ldg(a.qb + (uint64_t)rr * a.qs + el);
-        sc[k] = *(const float*)(a.sb + (uint64_t)rr * a.ss + sb);
-        if (j0 + k + 1 < N) rr = rr + 1 == N ? 0 : rr + 1;
+      for (int q = 0; q < kDqBatch / RPL; ++q) {
+        const int k = q * RPL + (int)ls;
+        if (k < nb) {
+          const int rk = r + k < N ? r + k : r + k - N;
+          w[q] = ldg(a.qb + (uint64_t)rk * a.qs + t0 + (uint64_t)ll * 16);
+        }
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (j0 + k < N) {
-          float q[kDqLane];
-          unpack_i8x16(qw[k], q);
+      for (int q = 0; q < kDqBatch / RPL; ++q) {
+        const int k = q * RPL + (int)ls;
+        if (k < nb) *(u32x4*)(qst + k * (int)(kDqTile / 4) + ll * 4) = w[q];
+      }
+      float sc[kDqBatch];
 #pragma unroll
-          for (int i = 0; i < kDqLane; ++i) acc[i] = (j0 + k == 0) ? q[i] * sc[k] : q[i] * sc[k] + acc[i];
+      for (int k = 0; k < kDqBatch; ++k)
+        if (k < nb) {
+          const int rk = r + k < N ? r + k : r + k - N;
+          sc[k] = *(const float*)(a.sb + (uint64_t)rk * a.ss + sb);
         }
-      r = rr;  // the first rank of the next batch (rr moved past the last load)
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kDqBatch; ++k)
+        if (k < nb) {
+          const uint32_t qw = qst[k * (int)(kDqTile / 4) + tid];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float q = (float)(int8_t)(qw >> (8 * i));
+            acc[i] = (j0 + k == 0) ? q * sc[k] : q * sc[k] + acc[i];
+          }
+        }
+      r = r + nb < N ? r + nb : r + nb - N;
     }
-    // the wavefront's 1024 results in element order, then read back in the
-    // store layout: lane wl's store j covers elements j * 64 VO + wl VO ..
-    float* w = qlds + wv * (64 * kDqLane);
-#pragma unroll
-    for (int k = 0; k < kDqLane; k += 4) *(float4*)(w + wl * kDqLane + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
-    wave_lds_fence();
-    const uint64_t wbase = t0 + (uint64_t)wv * (64 * kDqLane);
-#pragma unroll
-    for (int j = 0; j < kDqLane / VO; ++j) {
-      const uint32_t x = (uint32_t)j * (64u * VO) + wl * VO;
-      float o[VO];
-#pragma unroll
-      for (int i = 0; i < VO; i += 4) *(float4*)(o + i) = *(const float4*)(w + x + i);
-      const u32x4 ov = pack<DT>(o);
-      char* d = a.rb + (wbase + x) * SZ;
-      for (int k = 0; k < N; ++k, d += a.rs) stg(d, ov);
-    }
+    char* d = a.rb + e4 * SZ;
+    for (int k = 0; k < N; ++k, d += a.rs) st4<DT>(d, acc);
   } else {
-    for (uint64_t e = t0 + threadIdx.x; e < t1; e += kBlock) {
+    for (uint64_t e = t0 + threadIdx.x; e < t1; e += kDqThreads) {
       const int c = (int)chunk_of(a.M, N, e);
       float acc = 0.0f;
       for (int j = 0, r = c; j < N; ++j, r = r + 1 == N ? 0 : r + 1) {
@@ -404,11 +406,12 @@ unsigned q_lds(int blocks_per_cu, int dflt) {
 // Default workgroups per CU, swept on the MI355X at 8 ranks x 67,108,864
 // elements (2 to 16 per CU): the compression step streams best at 16 (float32
 // gradients 6.41 TB/s against 5.69 at 8; bf16 6.46 against 5.17 at 8), the
-// reduction of the messages at 3 (5.75 float32 and 5.71 bf16 results, 5.35
-// and 5.36 at 8), the fused kernel, which keeps four ranks' loads in flight,
-// at 4 for float32 (5.89 TB/s) and 5 for bf16 (5.99 against 5.25 at 3).
+// reduction of the messages at 4 for float32 results and 6 for bf16 (5.78 and
+// 6.05 TB/s; 5.31 and 6.05 at 6, 5.54 and 5.51 at 4), the fused kernel, which
+// keeps four ranks' loads in flight, at 4 for float32 (5.89 TB/s) and 5 for
+// bf16 (5.99 against 5.25 at 3).
 int quant_blocks_per_cu(int) { return 16; }
-int dequant_blocks_per_cu(int) { return 3; }
+int dequant_blocks_per_cu(int dt) { return dt == DT_F32 ? 4 : 6; }
 int qfused_blocks_per_cu(int dt) { return dt == DT_F32 ? 4 : 5; }
 }  // namespace
 
@@ -427,7 +430,7 @@ hipError_t launch_dequant_reduce(const QLaunch& L) {
   const QArgs a = q_args(L);  // vec_ok: int8 rows, scales and results 16-byte aligned (base and stride)
   const uint64_t tiles = (L.M + kDqTile - 1) / kDqTile;
   if (tiles > 0x7fffffffull) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)tiles), blk(kBlock);
+  const dim3 grid((unsigned)tiles), blk(kDqThreads);
   unsigned lds = q_lds(L.blocks_per_cu, dequant_blocks_per_cu(L.dt));
   if (lds < kDqLds) lds = kDqLds;
   if (L.dt == DT_F32) CC_LAUNCH((k_dequant_reduce<DT_F32>), grid, blk, lds, L.st, a);
