@@ -214,7 +214,7 @@ def chunk_bounds(count: int, nranks: int):
 def all_reduce(send, recv=None, op: str = "sum", algo: str = "ring", fuse_depth: int = 0,
                workspace=None, stream=None, blocks_per_cu: int = 0, grid_sync: bool = False) -> None:
     """recv[r] = (+)_j send[j] for every rank r; send/recv are [N, M].
-    grid_sync: the stepwise ring's passes in one cooperative launch."""
+    grid_sync: the stepwise ring's passes in one launch, each pass waiting for the previous one."""
     recv = send if recv is None else recv
     N, M = send.shape
     if tuple(recv.shape) != (N, M) or recv.dtype != send.dtype:
