@@ -479,6 +479,53 @@ def rec_int32_ring(dev, nsets=64):
             "parity": par, "oracle_s": round(t, 3)}
 
 
+def rec_small_ring(dev):
+    """A small message: ring AllReduce SUM of 131,072 bf16 elements over 4
+    ranks, the size of the 4-chip SCCL measurement the AllReduce algorithm
+    notes quote in their 2-port ring section (15.757 us there, other
+    hardware: context, not a target).  GPU time from HIP-graph replays of the
+    fused ring, the fused 2-port ring, the stepwise ring (one kernel per
+    step, 6 steps) and the standalone ReduceScatter and AllGather; every
+    output compared bit for bit with the oracle."""
+    import torch
+
+    from ring_allreduce_reduction_02_amd import ccgpu, synth
+    N, M = 4, 131_072
+    S = M // N
+    xs = synth.gradient_inputs(N, M, "bf16", sigma=1e-2, workload=synth.W_SMALL_RING)
+    send = strided_ranks(N, M, torch.bfloat16, dev)
+    upload(xs, send)
+    outs = {k: strided_ranks(N, M, torch.bfloat16, dev) for k in ("ring", "ring_2port", "stepwise", "ag")}
+    shard = strided_ranks(N, S, torch.bfloat16, dev)
+    ws = ccgpu.make_workspace("all_reduce", N, M, "bf16", "ring", 1, dev)
+    us = {
+        "ring_fused_us": time_graph(lambda: ccgpu.all_reduce(send, outs["ring"]), 10, 32),
+        "ring_2port_fused_us": time_graph(lambda: ccgpu.all_reduce(send, outs["ring_2port"], algo="ring_2port"),
+                                          10, 32),
+        "ring_stepwise_us": time_graph(lambda: ccgpu.all_reduce(send, outs["stepwise"], fuse_depth=1, workspace=ws),
+                                       10, 32),
+        "reduce_scatter_us": time_graph(lambda: ccgpu.reduce_scatter(send, shard), 10, 32),
+        "all_gather_us": time_graph(lambda: ccgpu.all_gather(shard, outs["ag"]), 10, 32),
+    }
+    torch.cuda.synchronize()
+    got = {k: download(v) for k, v in outs.items()}
+    got_shard = download(shard)
+    cs = _oracle()
+    t, _, _, exp = oracle_run(lambda: cs.ring_all_reduce(xs, "sum", "bf16"))
+    exp2 = cs.ring2_all_reduce(xs, "sum", "bf16")
+    exp_rs = cs.ring_reduce_scatter(xs, "sum", "bf16")
+    exp_ag = cs.ring_all_gather(exp_rs, "bf16")
+    par = (all(same_bits(got["ring"][r], exp[r]) and same_bits(got["stepwise"][r], exp[r])
+               and same_bits(got["ring_2port"][r], exp2[r]) and same_bits(got_shard[r], exp_rs[r])
+               and same_bits(got["ag"][r], exp_ag[r]) for r in range(N)))
+    del outs, shard, send, ws
+    torch.cuda.empty_cache()
+    rec = {"section": "ring_n4_m131072_bf16", "rank_stride_bytes": rank_stride_bytes(M * 2)}
+    rec.update({k: round(v * 1e3, 2) for k, v in us.items()})
+    rec.update({"page_sccl_4chip_fp16_us": 15.757, "parity": par, "oracle_s": round(t, 3)})
+    return rec
+
+
 def bucket_layout(N, sizes, tensors):
     """The bucketed workload's per-rank flat buffers: tensors at the
     cc_bucket_plan offsets (25 MiB buckets, 128-element aligned), zero
@@ -1220,8 +1267,8 @@ def main():
         log("alpha-beta fit at N=8")
         ab = alpha_beta_n8(dev, args.pad_bytes)
     if not args.no_workloads:
-        for name, fn in (("int32 ring", rec_int32_ring), ("buckets", rec_buckets), ("zero3", rec_zero3),
-                         ("moe", rec_moe)):
+        for name, fn in (("int32 ring", rec_int32_ring), ("small bf16 ring", rec_small_ring), ("buckets", rec_buckets),
+                         ("zero3", rec_zero3), ("moe", rec_moe)):
             log(f"workload: {name}")
             emit(fn(dev))
     if args.extras:

@@ -23,6 +23,7 @@ W_GRAD_RING = 2       # ring AllReduce SUM, N=8, M=67,108,864 fp32 (and a bf16 t
 W_BUCKETS = 3         # bucketed gradient sync, N=8, 120 bf16 tensors
 W_ZERO3 = 4           # standalone RS then AG, N=16, M=33,554,432 fp32; int32 MAX/PROD
 W_MOE = 5             # MoE AllToAll(v), N=8, 4096 tokens, hidden 7168, top-8 of 64
+W_SMALL_RING = 6      # ring AllReduce SUM, N=4, M=131,072 bf16 (small-message case)
 
 
 def rng(workload: int, rank: int, sub: int = 0) -> np.random.Generator:

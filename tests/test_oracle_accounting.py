@@ -130,3 +130,20 @@ def test_bucketed_all_reduce_matches_per_bucket_ring():
         expect = sum(ten[r][t].astype(np.int64) for r in range(N))
         for r in range(N):
             assert np.array_equal(out[r][t], expect.astype(np.int32))
+
+
+def test_ring_time_model_70b_budgets(golden):
+    """The textbook's 70B gradient budgets: the ring's bandwidth term
+    2(N-1)/N * bytes / link bandwidth at the printed N and link speeds
+    (tests/golden/ring_70b_budget.json)."""
+    g = golden("ring_70b_budget.json")
+    for c in g["cases"]:
+        t = cs.ring_time_model(g["gradient_bytes"], c["N"], 0.0, 1 / (c["link_GBps"] * 1e9))
+        assert t == pytest.approx(c["seconds"], rel=c["printed_rel_precision"]), c
+        if "factor" in c:
+            sent = cs.ring_values_sent_per_rank(c["N"] * 1000, c["N"])
+            assert sent[0] / (c["N"] * 1000) == c["factor"]
+    # a dropped (N-1)/N or a single phase would miss the 64-GPU figure by 1.6% or 2x
+    assert cs.ring_time_model(140e9, 64, 0.0, 1 / 50e9) != pytest.approx(2 * 140 / 50, rel=1e-3)
+    ctx = g["context_not_a_pin"]
+    assert ctx["rs_us"] + ctx["ag_us"] + ctx["sync_us"] == pytest.approx(ctx["total_us"], abs=1e-9)
