@@ -373,6 +373,28 @@ __global__ __launch_bounds__(kBlock) void k_ring_ag_pass(GatArgs a) {
   ring_ag_tile<SZ>(a, blockIdx.x, a.s0, a.k);
 }
 
+// The standalone AllGather in one pass, with the N stores of a tile's
+// vectors shared between G groups of kBlock threads: every group loads the
+// tile's vectors of rank c's shard (the first load brings the lines into the
+// XCD's L2, the other group finds them there) and stores them to ranks g,
+// g + G, g + 2G, ...  Element-wise tiles run the pass's own path in the
+// first group.
+template <int SZ, int G>
+__global__ __launch_bounds__(kBlock * G) void k_ag_groups(GatArgs a) {
+  constexpr int V = 16 / SZ;
+  const int N = a.N;
+  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, N, a.vec_ok);
+  const uint32_t g = threadIdx.x / kBlock, lane = threadIdx.x % kBlock;
+  if (t.fast) {
+    const int c = (int)t.c;
+    const uint64_t e = t.e0 + (uint64_t)lane * V;
+    const u32x4 w = ldg(a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ);
+    for (int r = (int)g; r < N; r += G) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
+  } else if (g == 0) {
+    ring_ag_tile<SZ>(a, blockIdx.x, 0, N - 1);
+  }
+}
+
 // ------------------------------------------------------------------ descriptor steps
 
 // One step of a schedule given as descriptors (tree, double tree, 2-port
@@ -812,14 +834,44 @@ hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k) {
 // 8 from 6 on: the rule's 11-16 overfill the write queues (fp32, 2 GiB per
 // buffer: N = 4 6.35 TB/s at 10 against 5.46 at the rule's 14; N = 2 6.44
 // against 5.82 at 16; N = 6 6.28 at 8 against 5.91 at 10).
+// Store groups and workgroups per CU of the standalone AllGather, from
+// sweeps on the MI355X (fp32 and bf16, 2 GiB of output, rows by the
+// rank-stride rule; 1, 2, 4, 8 groups at 1-12 workgroups per CU).  Two groups
+// at an occupancy that keeps about 64-100 KiB of a tile's traffic in flight
+// per CU, against one thread storing to all N ranks at its own default, TB/s
+// (fp32, two runs): N = 8 6.35-6.44 (5.52-5.72), 9 6.04 (5.71-5.85), 16
+// 6.36-6.40 (5.93-6.11), 17 6.30-6.33 (5.89-6.06), 48 5.91-5.98 (4.10-4.18),
+// 64 6.01 (4.67-4.86); four or eight groups came within 2% of two where they
+// were not worse.  From 21 to 40 ranks and up to 7 one thread per vector
+// streams as well or better (N = 24 5.97-6.15 against 5.87-5.90 with two
+// groups, 33 6.13-6.24 against 5.78-5.81, 3-7 5.7-6.4).
+static int ag_groups(int N) { return (N >= 8 && N <= 20) || N > 40 ? 2 : 1; }
+static int ag_blocks_per_cu(int N) { return N <= 12 ? 3 : N <= 20 ? 2 : 1; }
+
+template <int SZ>
+static hipError_t launch_ag_groups(const GatArgs& a, unsigned tiles, unsigned lds, hipStream_t st) {
+  CC_LAUNCH((k_ag_groups<SZ, 2>), dim3(tiles), dim3(kBlock * 2), lds, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_ag_fused(const Gat& g) {
-  Gat c = g;
-  if (c.blocks_per_cu <= 0) {
-    const int b = default_blocks_per_cu(kVecBytes * (uint64_t)(g.N + 1), kSkewedTarget, 1);
-    const int cap = g.N < 6 ? 10 : 8;
-    c.blocks_per_cu = one_round_blocks(gat_tiles(g), b > cap ? cap : b);
+  // the grouped kernel is the standalone AllGather's (ag_mode 1), within
+  // 32-bit work-item counts
+  const int G = g.ag_mode == 1 && (uint64_t)gat_tiles(g) * kBlock * ag_groups(g.N) <= 0xffffffffull ? ag_groups(g.N) : 1;
+  if (G == 1) {
+    Gat c = g;
+    if (c.blocks_per_cu <= 0) {
+      const int b = default_blocks_per_cu(kVecBytes * (uint64_t)(g.N + 1), kSkewedTarget, 1);
+      const int cap = g.N < 6 ? 10 : 8;
+      c.blocks_per_cu = one_round_blocks(gat_tiles(g), b > cap ? cap : b);
+    }
+    return launch_ring_ag_pass(c, 0, g.N - 1);
   }
-  return launch_ring_ag_pass(c, 0, g.N - 1);
+  const GatArgs a = gat_args(g, 0, g.N - 1);
+  const unsigned tiles = gat_tiles(g);
+  const int bpc = g.blocks_per_cu > 0 ? g.blocks_per_cu : one_round_blocks(tiles, ag_blocks_per_cu(g.N));
+  const unsigned lds = lds_for_blocks_per_cu(bpc);
+  return g.esize == 2 ? launch_ag_groups<2>(a, tiles, lds, g.st) : launch_ag_groups<4>(a, tiles, lds, g.st);
 }
 
 hipError_t launch_hd_ag_step(const Gat& g, int d, int first) {

@@ -45,8 +45,8 @@ ENTRIES = {
                      "bucketed bf16 ring AllReduce, N=8, 120 tensors in 25 MiB buckets, up to 16 buckets per launch"),
     "rs_ring_n16": ("section", "k_ring_fused<1, 0, 16>", "cc_kernels.hip", "ring_fused_rs_f32_n16_m33554432",
                     "fused ring ReduceScatter, N=16, M=33554432 fp32 per rank"),
-    "ag_ring_n16": ("section", "k_ring_ag_pass<4>", "cc_steps.hip", "ring_ag_f32_n16_m33554432",
-                    "fused ring AllGather, N=16, 2097152 fp32 per rank gathered to 33554432"),
+    "ag_ring_n16": ("section", "k_ag_groups<4, 2>", "cc_steps.hip", "ag_groups_f32_n16_m33554432",
+                    "fused AllGather (two store groups per tile), N=16, 2097152 fp32 per rank gathered to 33554432"),
     "moe_dropless": ("section", "k_copies", "cc_copy.hip", "copies_moe_dispatch_dropless_n8_t4096_h7168",
                      "MoE AllToAll(v) dispatch, N=8, 4096 tokens top-8 of 64 experts (Zipf 1.2), rows of 7168 bf16"),
     "hier_2x2x2": ("section", "k_hier_fused<1, 0>", "cc_hier.hip", "hier_fused_f32_2x2x2_m67108864",
