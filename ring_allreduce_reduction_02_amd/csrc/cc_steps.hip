@@ -829,11 +829,6 @@ hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k) {
   return hipGetLastError();
 }
 
-// The standalone AllGather (one load, N stores per tile) follows the
-// write-heavy byte rule, capped at 10 workgroups per CU below 6 ranks and at
-// 8 from 6 on: the rule's 11-16 overfill the write queues (fp32, 2 GiB per
-// buffer: N = 4 6.35 TB/s at 10 against 5.46 at the rule's 14; N = 2 6.44
-// against 5.82 at 16; N = 6 6.28 at 8 against 5.91 at 10).
 // Store groups and workgroups per CU of the standalone AllGather, from
 // sweeps on the MI355X (fp32 and bf16, 2 GiB of output, rows by the
 // rank-stride rule; 1, 2, 4, 8 groups at 1-12 workgroups per CU).  Two groups
@@ -845,6 +840,9 @@ hipError_t launch_ring_ag_pass(const Gat& g, int s0, int k) {
 // were not worse.  From 21 to 40 ranks and up to 7 one thread per vector
 // streams as well or better (N = 24 5.97-6.15 against 5.87-5.90 with two
 // groups, 33 6.13-6.24 against 5.78-5.81, 3-7 5.7-6.4).
+// (Broadcast has the same one-to-N shape, but two groups did not beat its
+// single-thread kernel: N = 8 5.23-5.31 against 5.86-5.94 TB/s at these
+// occupancies, level within noise at 12-64 ranks.)
 static int ag_groups(int N) { return (N >= 8 && N <= 20) || N > 40 ? 2 : 1; }
 static int ag_blocks_per_cu(int N) { return N <= 12 ? 3 : N <= 20 ? 2 : 1; }
 
@@ -859,6 +857,11 @@ hipError_t launch_ag_fused(const Gat& g) {
   // 32-bit work-item counts
   const int G = g.ag_mode == 1 && (uint64_t)gat_tiles(g) * kBlock * ag_groups(g.N) <= 0xffffffffull ? ag_groups(g.N) : 1;
   if (G == 1) {
+    // one group follows the write-heavy byte rule, capped at 10 workgroups
+    // per CU below 6 ranks and at 8 from 6 on: the rule's 11-16 overfill the
+    // write queues (fp32, 2 GiB per buffer: N = 4 6.35 TB/s at 10 against
+    // 5.46 at the rule's 14; N = 2 6.44 against 5.82 at 16; N = 6 6.28 at 8
+    // against 5.91 at 10)
     Gat c = g;
     if (c.blocks_per_cu <= 0) {
       const int b = default_blocks_per_cu(kVecBytes * (uint64_t)(g.N + 1), kSkewedTarget, 1);
