@@ -1186,6 +1186,15 @@ def profile_section(name, dev, steps, warmup, pad_bytes=262_144):
         y = torch.empty(N, E * cap * H, device=dev, dtype=torch.bfloat16)
         fn = lambda: ccgpu.moe_dispatch_padded(x, y, Ce.tolist(), cap, H)
         nbytes = (int(np.minimum(Ce, cap).sum()) + N * E * cap) * H * 2
+        # the copy launches of one call: each step's descriptors in launches of
+        # up to 64 (a launch whose descriptors are all empty is skipped)
+        recs = ccgpu.all_to_all_plan("moe_dispatch", ccgpu.RankBuf(x.data_ptr(), x.stride(0) * 2),
+                                     ccgpu.RankBuf(y.data_ptr(), y.stride(0) * 2), Ce.tolist(), N,
+                                     elem_per_row=H, dtype="bf16", nexperts=E, capacity=cap)
+        by_step = {}
+        for st, _, _, nb in recs:
+            by_step.setdefault(st, []).append(nb)
+        launches = sum(1 for d in by_step.values() for i in range(0, len(d), 64) if sum(d[i:i + 64]) > 0)
     else:
         raise SystemExit(f"unknown profile section {name}")
     for _ in range(warmup):

@@ -400,8 +400,8 @@ cc_status_t cc_moe_capacity(int nranks, size_t tokens, int topk, int nexperts, i
  * expert l, a block of `capacity` rows: the first min(count, capacity) rows of
  * i's block for expert j*E/N + l, in order, then zero rows (E*capacity rows
  * per rank).  A row is elem_per_row elements.  send and recv must not overlap.
- * fuse_depth 0: one launch writes every slot (when nranks * nexperts <= 512
- * and the row counts fit 32 bits; otherwise block copies, several launches).
+ * fuse_depth 0: direct, every (source, expert) block as one copy of its kept
+ * rows and one zero fill of its free slots, 64 blocks per launch.
  * fuse_depth >= 1: pairwise, step k carries the blocks of the pairs (i, i+k). */
 cc_status_t cc_moe_dispatch_padded(cc_rankbuf_t send, cc_rankbuf_t recv, const size_t* counts, int nexperts,
                                    size_t capacity, size_t elem_per_row, cc_dtype_t dtype, int nranks,

@@ -50,11 +50,23 @@ struct CopyArgs {
   int esize;
 };
 
-constexpr uint64_t kCopyTile = (uint64_t)kCopyBlock * 16;
+constexpr int kCopyVecs = 2;                                  // 16-byte vectors per thread and tile
+constexpr uint64_t kCopyRow = (uint64_t)kCopyBlock * 16;       // one vector per thread
+constexpr uint64_t kCopyTile = kCopyRow * kCopyVecs;           // 4 KiB
 
 // Flat tiling over a list of copies: workgroup b copies tile (b - tpre[k]) of
 // descriptor k (found by binary search), so skewed block sizes still spread
-// over the whole chip.
+// over the whole chip.  A thread moves two vectors, both loaded before either
+// is stored.  Measured on the MI355X (the MoE dispatch, 8 ranks x 4096 tokens
+// x top-8, rows of 7168 bf16): one vector per thread (2 KiB tiles) 6.08-6.12
+// TB/s dropless and 5.62-5.66 for the capacity-padded pairwise dispatch; two
+// vectors 6.38 / 6.01 at full occupancy, 6.55 dropless at 12 workgroups per
+// CU; four vectors 6.06-6.34 / 5.70; 256 threads of one vector 6.16-6.22.
+// 12 workgroups per CU by default (the MoE dispatch above: 6.55 TB/s dropless
+// against 6.38 at full occupancy; the capacity-padded one at C = 1.25
+// 6.24-6.27 against 5.94-5.99, its combine 6.20-6.22 against 5.99-6.00)
+constexpr int kCopiesBlocksPerCu = 12;
+
 __global__ __launch_bounds__(kCopyBlock) void k_copies(CopyArgs a) {
   const uint64_t b = blockIdx.x;
   int lo = 0, hi = a.n;
@@ -71,130 +83,25 @@ __global__ __launch_bounds__(kCopyBlock) void k_copies(CopyArgs a) {
   if (src == nullptr) {  // a fill descriptor: zeros
     if ((a.vecmask >> k) & 1) {
       const u32x4 z = {0u, 0u, 0u, 0u};
-      for (uint64_t o = o0 + (uint64_t)threadIdx.x * 16; o < o1; o += kCopyTile) stg(dst + o, z);
+      for (uint64_t o = o0 + (uint64_t)threadIdx.x * 16; o < o1; o += kCopyRow) stg(dst + o, z);
     } else {
       for (uint64_t o = o0 + threadIdx.x; o < o1; o += kCopyBlock) dst[o] = 0;
     }
   } else if ((a.vecmask >> k) & 1) {
-    for (uint64_t o = o0 + (uint64_t)threadIdx.x * 16; o < o1; o += kCopyTile) stg(dst + o, ldg(src + o));
+    const uint64_t p = o0 + (uint64_t)threadIdx.x * 16;
+    u32x4 w[kCopyVecs];
+#pragma unroll
+    for (int u = 0; u < kCopyVecs; ++u)
+      if (p + u * kCopyRow < o1) w[u] = ldg(src + p + u * kCopyRow);
+#pragma unroll
+    for (int u = 0; u < kCopyVecs; ++u)
+      if (p + u * kCopyRow < o1) stg(dst + p + u * kCopyRow, w[u]);
   } else {
     for (uint64_t o = o0 + threadIdx.x; o < o1; o += kCopyBlock) dst[o] = src[o];
   }
 }
 
-// ------------------------------------------------------------------ capacity-padded MoE exchange
-
-struct MoeArgs {
-  const char* sb;
-  uint64_t ss;
-  char* db;
-  uint64_t ds;
-  uint64_t rowb;
-  uint32_t cap, N, E, epr;
-  uint32_t dispatch, vec_ok;
-  uint32_t rows_pre[kMaxRanks + 1];  // token rows of the ranks before i
-  uint32_t cnt[kMoeMaxBlocks];       // [N][E] rows token rank i routes to expert e
-};
-
-// rows of token rank i that precede its rows for expert e (sorted by expert)
-__device__ __forceinline__ uint32_t moe_disp(const MoeArgs& a, uint32_t i, uint32_t e) {
-  uint32_t d = 0;
-  for (uint32_t x = 0; x < e; ++x) d += a.cnt[i * a.E + x];
-  return d;
-}
-
-// Workgroup b writes output row b.  Dispatch: rows in the expert side's order
-// (expert rank j, then token rank i and local expert l, then slot s): slot s
-// of block (i, l) holds token row disp(i, e) + s when s < cnt(i, e), else
-// zeros.  Combine: token rank i's rows in order: row r of expert e's rows
-// comes back from slot r - disp(i, e) of block (i, l) on expert rank j when
-// that slot was kept (below the capacity), else zeros.  The indices are
-// uniform across the workgroup (scalar registers); the row is then a plain
-// streaming copy.
-__global__ __launch_bounds__(kCopyBlock) void k_moe_rows(MoeArgs a) {
-  const uint32_t idx = blockIdx.x;
-  const char* src = nullptr;
-  char* dst;
-  if (a.dispatch) {
-    const uint32_t b = idx / a.cap, s = idx - b * a.cap;
-    const uint32_t per_rank = a.N * a.epr;
-    const uint32_t j = b / per_rank, rem = b - j * per_rank;
-    const uint32_t i = rem / a.epr, l = rem - i * a.epr;
-    const uint32_t e = j * a.epr + l;
-    dst = a.db + (uint64_t)j * a.ds + ((uint64_t)rem * a.cap + s) * a.rowb;
-    if (s < a.cnt[i * a.E + e]) src = a.sb + (uint64_t)i * a.ss + ((uint64_t)moe_disp(a, i, e) + s) * a.rowb;
-  } else {
-    uint32_t i = 0;
-    while (i + 1 < a.N && a.rows_pre[i + 1] <= idx) ++i;
-    const uint32_t r = idx - a.rows_pre[i];
-    uint32_t e = 0, d = 0;
-    while (e + 1 < a.E && d + a.cnt[i * a.E + e] <= r) d += a.cnt[i * a.E + e++];
-    const uint32_t s = r - d;
-    dst = a.db + (uint64_t)i * a.ds + (uint64_t)r * a.rowb;
-    if (s < a.cap) {
-      const uint32_t j = e / a.epr, l = e - j * a.epr;
-      src = a.sb + (uint64_t)j * a.ss + ((uint64_t)(i * a.epr + l) * a.cap + s) * a.rowb;
-    }
-  }
-  if (a.vec_ok) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    if (src) {
-#pragma unroll 4
-      for (uint64_t o = (uint64_t)threadIdx.x * 16; o < a.rowb; o += kCopyTile) stg(dst + o, ldg(src + o));
-    } else {
-      for (uint64_t o = (uint64_t)threadIdx.x * 16; o < a.rowb; o += kCopyTile) stg(dst + o, z);
-    }
-  } else {
-    for (uint64_t o = threadIdx.x; o < a.rowb; o += kCopyBlock) dst[o] = src ? src[o] : (char)0;
-  }
-}
-
 }  // namespace
-
-bool moe_rows_fit(int N, int E, uint64_t cap, const uint64_t* cnt) {
-  if (N < 1 || N > kMaxRanks || E < N || E % N || (uint64_t)N * E > (uint64_t)kMoeMaxBlocks) return false;
-  if (cap == 0 || cap > 0xffffffffull) return false;
-  uint64_t rows = 0;
-  for (int i = 0; i < N; ++i) {
-    uint64_t ri = 0;
-    for (int e = 0; e < E; ++e) {
-      if (cnt[(size_t)i * E + e] > 0xffffffffull) return false;
-      ri += cnt[(size_t)i * E + e];
-    }
-    rows += ri;
-  }
-  // one workgroup of kCopyBlock threads per output row: the grid's x size and
-  // its work-items within 31 and 32 bits
-  const uint64_t lim = 0xffffffffull / kCopyBlock;
-  return rows <= lim && (uint64_t)N * E * cap <= lim;
-}
-
-hipError_t launch_moe_rows(const MoeLaunch& L) {
-  if (!moe_rows_fit(L.N, L.E, L.cap, L.cnt)) return hipErrorInvalidValue;
-  MoeArgs a;
-  a.sb = L.src; a.ss = L.ss; a.db = L.dst; a.ds = L.ds; a.rowb = L.rowb;
-  a.cap = (uint32_t)L.cap; a.N = (uint32_t)L.N; a.E = (uint32_t)L.E; a.epr = (uint32_t)(L.E / L.N);
-  a.dispatch = (uint32_t)L.dispatch;
-  a.vec_ok = ((((uintptr_t)L.src | (uintptr_t)L.dst | L.ss | L.ds | L.rowb) & 15u) == 0);
-  a.rows_pre[0] = 0;
-  for (int i = 0; i < L.N; ++i) {
-    uint64_t ri = 0;
-    for (int e = 0; e < L.E; ++e) {
-      a.cnt[i * L.E + e] = (uint32_t)L.cnt[(size_t)i * L.E + e];
-      ri += L.cnt[(size_t)i * L.E + e];
-    }
-    a.rows_pre[i + 1] = a.rows_pre[i] + (uint32_t)ri;
-  }
-  const uint64_t rows = L.dispatch ? (uint64_t)L.N * L.E * L.cap : a.rows_pre[L.N];
-  if (rows == 0 || L.rowb == 0) return hipSuccess;
-  const dim3 grid((unsigned)rows), blk(kCopyBlock);
-  // 8 workgroups per CU by default: the C = 1.25 dispatch of 8 ranks x 4096
-  // tokens (top-8 of 64 experts, rows of 14,336 bytes) ran at 5.66 TB/s
-  // against 5.49 at full occupancy, the combine at 5.72 against 5.56
-  const unsigned lds = lds_for_blocks_per_cu(L.blocks_per_cu > 0 ? L.blocks_per_cu : 8);
-  CC_LAUNCH(k_moe_rows, grid, blk, lds, L.st, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_bcast(const char* src, Side dst, int N, int skip, uint64_t nbytes, int vec_ok,
                         int blocks_per_cu, hipStream_t st) {
@@ -220,7 +127,7 @@ hipError_t launch_copies(const CopyDesc* d, int n, int esize, int blocks_per_cu,
   }
   if (a.n == 0) return hipSuccess;
   const dim3 grid((unsigned)a.tpre[a.n]), blk(kCopyBlock);
-  const unsigned lds = blocks_per_cu > 0 ? lds_for_blocks_per_cu(blocks_per_cu) : 0;
+  const unsigned lds = lds_for_blocks_per_cu(blocks_per_cu > 0 ? blocks_per_cu : kCopiesBlocksPerCu);
   CC_LAUNCH(k_copies, grid, blk, lds, st, a);
   return hipGetLastError();
 }

@@ -199,28 +199,4 @@ struct CopyDesc {
 };
 hipError_t launch_copies(const CopyDesc* d, int n, int esize, int blocks_per_cu, hipStream_t st);
 
-// ---- capacity-padded MoE exchange, direct schedule: one launch, one
-// workgroup per output row.  The dispatch writes every expert slot (kept rows
-// copied, the rest zero), the combine every token row (kept rows copied back,
-// dropped ones zero); cnt[i * E + e] = rows token rank i routes to expert e.
-constexpr int kMoeMaxBlocks = 512;  // nranks * nexperts in one launch
-struct MoeLaunch {
-  const char* src;   // the side read: token side (dispatch) or expert side (combine)
-  uint64_t ss;
-  char* dst;
-  uint64_t ds;
-  uint64_t rowb;
-  uint64_t cap;
-  int N;
-  int E;
-  int dispatch;
-  int blocks_per_cu;
-  const uint64_t* cnt;
-  hipStream_t st;
-};
-// false when the exchange does not fit one launch (N * E, 32-bit rows or the
-// grid): the caller then runs copy descriptors
-bool moe_rows_fit(int N, int E, uint64_t cap, const uint64_t* cnt);
-hipError_t launch_moe_rows(const MoeLaunch& L);
-
 }  // namespace cc

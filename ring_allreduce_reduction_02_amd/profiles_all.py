@@ -63,7 +63,7 @@ ENTRIES = {
                        "INT8 compression step with error feedback, N=8, M=67108864 fp32 gradients per rank"),
     "int8_dequant_f32": ("section", "k_dequant_reduce<1>", "cc_quant.hip", "dequant_reduce_f32_n8_m67108864",
                          "AllReduce of INT8 messages, N=8, M=67108864 elements per rank, fp32 result"),
-    "moe_padded_c125": ("section", "k_moe_rows", "cc_copy.hip", "moe_rows_dispatch_padded_c125_n8_t4096_h7168",
+    "moe_padded_c125": ("section", "k_copies", "cc_copy.hip", "copies_moe_dispatch_padded_c125_n8_t4096_h7168",
                         "capacity-padded MoE dispatch (C=1.25, capacity 640), N=8, 4096 tokens top-8 of 64 experts, "
                         "rows of 7168 bf16"),
 }
