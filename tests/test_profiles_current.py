@@ -1,0 +1,28 @@
+"""Every committed rocprofv3 summary under profiles/ was taken from the
+current kernel sources: the sha256 it recorded for the files that define its
+kernel equals theirs now (bench.py reports a profile's counter traffic only
+under the same condition), and its counter traffic is within 5% of its
+algorithmic bytes."""
+import glob
+import json
+import os
+
+import pytest
+
+from ring_allreduce_reduction_02_amd import profsum
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = sorted(glob.glob(os.path.join(ROOT, "profiles", "*_pmc.json")))
+
+
+def test_there_are_profiles():
+    assert len(PROFILES) >= 15
+
+
+@pytest.mark.parametrize("path", PROFILES, ids=[os.path.basename(p)[:-9] for p in PROFILES])
+def test_profile_matches_the_sources(path):
+    p = json.load(open(path))
+    assert p["kernel_source_sha256_16"] == profsum.sources_hash(p["kernel_sources"]), \
+        f"{os.path.basename(path)}: the kernel's sources changed since it was profiled"
+    assert 0.95 <= p["traffic_over_algorithmic"] <= 1.05
+    assert os.path.exists(path[:-len("_pmc.json")] + ".md")
