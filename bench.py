@@ -9,10 +9,11 @@ resident in HBM; its algorithmic traffic is 2*N*M*4 bytes (every rank's input
 read once, every rank's output written once).
 
 stdout carries one JSON object per line:
-  * first, one record per other workload -- the int32 ring at N = 4, the
-    bucketed bf16 gradient sync, the ZeRO-3 ReduceScatter / AllGather at
-    N = 16 and the MoE AllToAll(v) -- each with its timing, rank stride and a
-    bit-for-bit parity verdict against the oracle run on the same inputs;
+  * first, one record per other workload -- the int32 ring at N = 4, a small
+    bf16 ring (4 ranks x 131,072), the bucketed bf16 gradient sync, the
+    ZeRO-3 ReduceScatter / AllGather at N = 16 and the MoE AllToAll(v) --
+    each with its timing, rank stride and a bit-for-bit parity verdict
+    against the oracle run on the same inputs;
   * LAST, the headline line (at most 2 KB): GB/s, ms per step, % of peak,
     simulated busbw, the fused kernel's roofline (per-launch HIP event
     durations; HBM traffic from committed rocprofv3 counters while the kernel
