@@ -57,14 +57,13 @@ constexpr uint64_t kCopyTile = kCopyRow * kCopyVecs;           // 4 KiB
 // Flat tiling over a list of copies: workgroup b copies tile (b - tpre[k]) of
 // descriptor k (found by binary search), so skewed block sizes still spread
 // over the whole chip.  A thread moves two vectors, both loaded before either
-// is stored.  Measured on the MI355X (the MoE dispatch, 8 ranks x 4096 tokens
-// x top-8, rows of 7168 bf16): one vector per thread (2 KiB tiles) 6.08-6.12
-// TB/s dropless and 5.62-5.66 for the capacity-padded pairwise dispatch; two
-// vectors 6.38 / 6.01 at full occupancy, 6.55 dropless at 12 workgroups per
-// CU; four vectors 6.06-6.34 / 5.70; 256 threads of one vector 6.16-6.22.
-// 12 workgroups per CU by default (the MoE dispatch above: 6.55 TB/s dropless
-// against 6.38 at full occupancy; the capacity-padded one at C = 1.25
-// 6.24-6.27 against 5.94-5.99, its combine 6.20-6.22 against 5.99-6.00)
+// is stored, at 12 workgroups per CU by default.  Measured on the MI355X (the
+// MoE dispatch, 8 ranks x 4096 tokens x top-8, rows of 7168 bf16; dropless /
+// capacity-padded at C = 1.25, direct): one vector per thread (2 KiB tiles)
+// at full occupancy 6.08-6.12 / 5.62-5.66 TB/s (pairwise); two vectors at
+// full occupancy 6.38 / 5.94-5.99, at 12 per CU 6.53-6.55 / 6.24-6.28 (the
+// combine 6.20-6.23 against 5.99-6.00); four vectors 6.06-6.34 / 5.70; 256
+// threads of one vector 6.16-6.22 dropless.
 constexpr int kCopiesBlocksPerCu = 12;
 
 __global__ __launch_bounds__(kCopyBlock) void k_copies(CopyArgs a) {
