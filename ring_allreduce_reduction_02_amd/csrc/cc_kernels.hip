@@ -40,12 +40,14 @@ namespace {
 // registers in the schedule's order, then the AllGather as N stores.
 // ReduceScatter (rs_mode 1, ring and halving-doubling): only the owner is
 // written; the ring's fold then starts one rank later.
-template <int DT, int OP, int NR, int ALG>
+// U: 16-byte vectors per thread and rank (a tile of U kBlock vectors).
+template <int DT, int OP, int NR, int ALG, int U = 1>
 __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   typedef typename Ty<DT>::A A;
   constexpr int V = Ty<DT>::V;
+  constexpr int VT = V * U;  // elements per thread and tile
   constexpr int SZ = Ty<DT>::SZ;
-  static_assert(kUnroll == 1, "one 16-byte vector per thread");
+  static_assert(kUnroll == 1, "the tile size is kBlock U vectors");
   // ring: N ranks (NR when fixed at compile time); trees: the runtime rank
   // count, NR being the tree's leaf slots
   const int N = (ALG == ALG_RING && NR > 0) ? NR : a.N;
@@ -53,30 +55,44 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // so only a ReduceScatter needs the chunk of a tile
   const int tiling = (ALG != ALG_RING && !a.rs_mode) ? 1 : N;
   const TreeShape ts{a.tree_leaves, a.tree_pairs};
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, tiling, a.vec_ok);
+  const Tile<VT> t = a.tpc_log2 >= 0 ? tile_pow2<VT>(blockIdx.x, a.tpc_log2)
+                                      : tile_floor<VT>(blockIdx.x, a.M, tiling, a.vec_ok);
   if (t.fast) {
     // Every rank's tile starts at a workgroup-uniform address; a lane adds
-    // its own 16-byte offset (scalar base + 32-bit vector offset).
+    // its own 16-byte offset (scalar base + 32-bit vector offset), vector u
+    // of the thread another kBlock vectors on.
     const int c = (int)t.c;
     const int start = (ALG == ALG_RING && a.rs_mode) ? wrapN(c + 1, N) : c;
     const uint32_t lane = threadIdx.x * 16u;
+    constexpr uint32_t kStep = kBlock * 16u;
     const uint64_t eb = t.e0 * SZ;
-    A acc[V];
-    fold_vec<DT, OP, NR, ALG>(a.sb + eb, a.ss, N, start, lane, acc, ts);
-    const u32x4 w = pack<DT>(acc);
+    A acc[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) fold_vec<DT, OP, NR, ALG>(a.sb + eb, a.ss, N, start, lane + u * kStep, acc[u], ts);
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = pack<DT>(acc[u]);
     if (a.rs_mode) {
-      stg(a.rb + (uint64_t)c * a.rs + (t.e0 - a.bnd[c]) * SZ + lane, w);
+      char* d = a.rb + (uint64_t)c * a.rs + (t.e0 - a.bnd[c]) * SZ + lane;
+#pragma unroll
+      for (int u = 0; u < U; ++u) stg(d + u * kStep, w[u]);
     } else {
-      char* d = a.rb + eb;
+      char* d = a.rb + eb + lane;
       if constexpr (NR > 0) {
         if (N == NR) {  // the ring with NR > 0, a tree with every leaf slot used
 #pragma unroll
-          for (int r = 0; r < NR; ++r, d += a.rs) stg(d + lane, w);
+          for (int r = 0; r < NR; ++r, d += a.rs)
+#pragma unroll
+            for (int u = 0; u < U; ++u) stg(d + u * kStep, w[u]);
         } else {
-          for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
+          for (int r = 0; r < N; ++r, d += a.rs)
+#pragma unroll
+            for (int u = 0; u < U; ++u) stg(d + u * kStep, w[u]);
         }
       } else {
-        for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, w);
+        for (int r = 0; r < N; ++r, d += a.rs)
+#pragma unroll
+          for (int u = 0; u < U; ++u) stg(d + u * kStep, w[u]);
       }
     }
   } else {
@@ -86,7 +102,8 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     // the tile's first element and stores nothing.  A tree folds one element
     // at a time (its fold already has NR loads in flight).
     constexpr int G = ALG == ALG_RING ? elem_batch<V, NR>() : 1;
-    for (int g0 = 0; g0 < V; g0 += G) {
+    static_assert(VT % G == 0, "whole batches");
+    for (int g0 = 0; g0 < VT; g0 += G) {
       uint64_t ev[G], off[G];
       uint32_t cv[G];
       int st[G];
@@ -120,9 +137,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   }
 }
 
-template <int DT, int OP, int NR>
+template <int DT, int OP, int NR, int U>
 __global__ __launch_bounds__(kBlock) void k_ring_fused(FusedArgs a) {
-  fused_body<DT, OP, NR, ALG_RING>(a);
+  fused_body<DT, OP, NR, ALG_RING, U>(a);
 }
 
 // Halving-doubling (TREE_HD) and butterfly / binomial tree (TREE_BFLY) over
@@ -172,9 +189,23 @@ int default_blocks_per_cu(uint64_t traffic, uint64_t target, int min_blocks) {
 }
 
 
+// A grid of 8 to 16 one-vector tiles per CU (4 to 8 MiB per rank) takes two
+// vectors per thread: half the workgroups, each thread with twice the loads
+// in flight, in one round.  Measured on the MI355X (graph replays over
+// rotating buffer sets, one vector against two): int32 4 ranks x 1,048,576
+// 8.16-8.27 us against 6.64-6.70; fp32 8 ranks of 4 MiB 15.5-15.7 against
+// 12.5-12.6, of 8 MiB 28.3-28.8 against 26.8-26.9; fp32 16 ranks of 4 MiB
+// 32.8-33.0 against 26.1.  Below (the element-wise path of small chunks, then
+// twice the elements per thread) and above (2 MiB per rank level, 16 MiB and
+// up 2-25% slower) one vector per thread stays.
 hipError_t launch_ring_fused(const Red& r) {
-  const FusedArgs a = fused_args(r);
-  const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  FusedArgs a = fused_args(r);
+  const uint64_t tiles1 = num_tiles(r.M, r.dt);
+  const int cus = dev_info().cus;
+  const bool wide = cus > 0 && tiles1 >= 8ull * (uint64_t)cus && tiles1 <= 16ull * (uint64_t)cus;
+  if (wide) a.tpc_log2 = pow2_tiles_per_chunk_v(r.M, r.N, 2 * vec_elems(r.dt), r.vec_ok);
+  const uint64_t tile2 = 2ull * kBlock * vec_elems(r.dt);
+  const dim3 grid((unsigned)(wide ? (r.M + tile2 - 1) / tile2 : tiles1)), blk(kBlock);
   const bool runtime_n = r.N != 2 && r.N != 3 && r.N != 4 && r.N != 8 && r.N != 16;
   // Two measured exceptions to the byte rule (2 GiB per buffer, rows 256 KiB
   // beyond the payload apart): at N = 3, 8 workgroups per CU (6.44 fp32 and
@@ -192,15 +223,19 @@ hipError_t launch_ring_fused(const Red& r) {
                   : ar_fused_lds(r, ring_bpc);
   return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
-    switch (r.N) {
-      case 2: CC_LAUNCH((k_ring_fused<DT, OP, 2>), grid, blk, lds, r.st, a); break;
-      case 3: CC_LAUNCH((k_ring_fused<DT, OP, 3>), grid, blk, lds, r.st, a); break;
-      case 4: CC_LAUNCH((k_ring_fused<DT, OP, 4>), grid, blk, lds, r.st, a); break;
-      case 8: CC_LAUNCH((k_ring_fused<DT, OP, 8>), grid, blk, lds, r.st, a); break;
-      case 16: CC_LAUNCH((k_ring_fused<DT, OP, 16>), grid, blk, lds, r.st, a); break;
-      default: CC_LAUNCH((k_ring_fused<DT, OP, 0>), grid, blk, lds, r.st, a); break;
-    }
-    return hipGetLastError();
+    auto go = [&](auto u) {
+      constexpr int U = decltype(u)::value;
+      switch (r.N) {
+        case 2: CC_LAUNCH((k_ring_fused<DT, OP, 2, U>), grid, blk, lds, r.st, a); break;
+        case 3: CC_LAUNCH((k_ring_fused<DT, OP, 3, U>), grid, blk, lds, r.st, a); break;
+        case 4: CC_LAUNCH((k_ring_fused<DT, OP, 4, U>), grid, blk, lds, r.st, a); break;
+        case 8: CC_LAUNCH((k_ring_fused<DT, OP, 8, U>), grid, blk, lds, r.st, a); break;
+        case 16: CC_LAUNCH((k_ring_fused<DT, OP, 16, U>), grid, blk, lds, r.st, a); break;
+        default: CC_LAUNCH((k_ring_fused<DT, OP, 0, U>), grid, blk, lds, r.st, a); break;
+      }
+      return hipGetLastError();
+    };
+    return wide ? go(IC<2>{}) : go(IC<1>{});
   });
 }
 

@@ -34,16 +34,16 @@ LIMITER = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_
 # grid (one work-item per 16-byte vector of a rank's M elements).
 BENCH_GRID = {"ring_f32": 67108864 * 4 // 16, "ring_bf16": 67108864 * 2 // 16}
 ENTRIES = {
-    "ring_f32": ("bench", "k_ring_fused<1, 0, 8>", "cc_kernels.hip", "ring_fused_f32_n8_m67108864",
+    "ring_f32": ("bench", "k_ring_fused<1, 0, 8, 1>", "cc_kernels.hip", "ring_fused_f32_n8_m67108864",
                  "fused ring AllReduce, N=8 logical ranks, M=67108864 fp32 per rank (the benchmark's headline)"),
-    "ring_bf16": ("bench", "k_ring_fused<2, 0, 8>", "cc_kernels.hip", "ring_fused_bf16_n8_m67108864",
+    "ring_bf16": ("bench", "k_ring_fused<2, 0, 8, 1>", "cc_kernels.hip", "ring_fused_bf16_n8_m67108864",
                   "fused ring AllReduce, N=8 logical ranks, M=67108864 bf16 per rank (the headline's bf16 twin)"),
-    "int32_ring_rot": ("section", "k_ring_fused<0, 0, 4>", "cc_kernels.hip",
+    "int32_ring_rot": ("section", "k_ring_fused<0, 0, 4, 2>", "cc_kernels.hip",
                        "ring_fused_int32_n4_m1048576_rotating64",
                        "fused ring AllReduce, N=4, M=1048576 int32 per rank, 64 rotating buffer sets (2 GiB)"),
     "buckets_ring": ("section", "k_fused_seg<2, 0, 8, 0>", "cc_trees.hip", "fused_seg_bf16_n8_120_tensors",
                      "bucketed bf16 ring AllReduce, N=8, 120 tensors in 25 MiB buckets, up to 16 buckets per launch"),
-    "rs_ring_n16": ("section", "k_ring_fused<1, 0, 16>", "cc_kernels.hip", "ring_fused_rs_f32_n16_m33554432",
+    "rs_ring_n16": ("section", "k_ring_fused<1, 0, 16, 1>", "cc_kernels.hip", "ring_fused_rs_f32_n16_m33554432",
                     "fused ring ReduceScatter, N=16, M=33554432 fp32 per rank"),
     "ag_ring_n16": ("section", "k_ag_groups<4, 2>", "cc_steps.hip", "ag_groups_f32_n16_m33554432",
                     "fused AllGather (two store groups per tile), N=16, 2097152 fp32 per rank gathered to 33554432"),
