@@ -158,8 +158,11 @@ typedef struct {
  * the payload rounded up to a power of two, measured best or within 1-2% of
  * the best pad tried for 8 ranks of 256 MiB (256 MiB + 256 KiB), 16 of
  * 128 MiB, 32 of 64 MiB, 64 of 32 MiB and 8 bf16 ranks of 527 MiB
- * (1 GiB + 1 MiB: 6.35 TB/s against 5.82 with no padding).  The library
- * takes the stride as given. */
+ * (1 GiB + 1 MiB: 6.35 TB/s against 5.82 with no padding).  For 4 to 8
+ * ranks of 4 to 32 MiB that pad (32 KiB) is poor (8 fp32 ranks of 16 MiB:
+ * 4.25 TB/s against 6.10 with a 512 KiB pad) and a 1 MiB pad measured
+ * within 2-6% of the best; pads of 1/128 of the row were slow at every row
+ * size tried.  The library takes the stride as given. */
 typedef struct {
   void* base;
   size_t rank_stride_bytes;
