@@ -1151,9 +1151,9 @@ def profile_section(name, dev, steps, warmup, pad_bytes=262_144):
         y = strided_ranks(N, int(C.sum(0).max()) * H, torch.bfloat16, dev)
         fn = lambda: ccgpu.all_to_all(x, y, C.tolist(), H)
         nbytes = 2 * int(C.sum()) * H * 2
-    elif name in ("hier_2x2x2", "dbt_n8", "hier_8x8"):
+    elif name in ("hier_2x2x2", "dbt_n8", "hier_8x8", "hier_8x8_ag"):
         pad = pad_bytes
-        if name == "hier_8x8":
+        if name.startswith("hier_8x8"):
             N, M, pad = 64, 1 << 23, 0   # 64 ranks of 32 MiB stream best unpadded
         x = randn_ranks(N, M, gen, dev, pad)
         y = rank_tensor(N, M, torch.float32, pad, dev)
@@ -1162,7 +1162,16 @@ def profile_section(name, dev, steps, warmup, pad_bytes=262_144):
         else:
             dims = (2, 2, 2) if name == "hier_2x2x2" else (8, 8)
             fn = lambda: ccgpu.all_reduce_hierarchical(x, y, dims)
-        nbytes = 2 * N * M * 4
+        # 64 ranks of 32 MiB take the split form: the nested fold stored once
+        # (N M reads, M writes), then the AllGather from the owners (M reads,
+        # (N - 1) M writes); each launch is profiled against its own bytes
+        nbytes = {"hier_8x8": (N + 1) * M * 4, "hier_8x8_ag": N * M * 4}.get(name, 2 * N * M * 4)
+    elif name in ("ring_n64", "ring_n64_ag"):
+        N, M = 64, 1 << 23
+        x = randn_ranks(N, M, gen, dev, 0)
+        y = rank_tensor(N, M, torch.float32, 0, dev)
+        fn = lambda: ccgpu.all_reduce(x, y)   # the split form: ReduceScatter launch, AllGather launch
+        nbytes = (N + 1) * M * 4 if name == "ring_n64" else N * M * 4
     elif name in ("int8_ef_f32", "int8_ef_bf16", "int8_quant_f32", "int8_dequant_f32"):
         tdt = torch.bfloat16 if name == "int8_ef_bf16" else torch.float32
         g = strided_ranks(N, M, tdt, dev)
@@ -1208,8 +1217,8 @@ def profile_section(name, dev, steps, warmup, pad_bytes=262_144):
 
 
 PROFILE_SECTIONS = ("ring_f32, ring_bf16, int32_ring_rot, buckets_ring, rs_ring_n16, ag_ring_n16, moe_dropless, "
-                    "hier_2x2x2, hier_8x8, dbt_n8, int8_ef_f32, int8_ef_bf16, int8_quant_f32, int8_dequant_f32, "
-                    "moe_padded_c125")
+                    "hier_2x2x2, hier_8x8, hier_8x8_ag, ring_n64, ring_n64_ag, dbt_n8, int8_ef_f32, int8_ef_bf16, "
+                    "int8_quant_f32, int8_dequant_f32, moe_padded_c125")
 
 
 # ---------------------------------------------------------------- main

@@ -13,14 +13,6 @@ namespace {
 
 uint64_t q_blocks(uint64_t M) { return (M + kQBlock - 1) / kQBlock; }
 
-// floor(c*M/N), c = 0..N: the ring's chunks
-struct QBounds {
-  uint64_t b[kMaxRanks + 1];
-  QBounds(uint64_t M, int N) {
-    for (int c = 0; c <= N; ++c) b[c] = (uint64_t)(((unsigned __int128)c * M) / (unsigned)N);
-  }
-};
-
 cc_status_t q_checks(int nranks, cc_dtype_t dtype, const cc_config_t& cfg, uint64_t M) {
   cc_status_t s = common_checks(CC_COLL_ALL_REDUCE, nranks, dtype, &cfg);
   if (s) return s;
@@ -56,11 +48,11 @@ cc_status_t disjoint(const Side2* s, int n, int N, int same_a = -1, int same_b =
 }
 
 QLaunch q_launch(const cc_rankbuf_t& g, const cc_rankbuf_t& e, const cc_rankbuf_t& q, const cc_rankbuf_t& s,
-                 const cc_rankbuf_t& r, uint64_t M, const uint64_t* bnd, int N, int dt, int vec_ok,
+                 const cc_rankbuf_t& r, uint64_t M, int N, int dt, int vec_ok,
                  const cc_config_t& cfg, cc_stream_t st) {
   return QLaunch{(const char*)g.base, g.rank_stride_bytes, (char*)e.base, e.rank_stride_bytes,
                  (char*)q.base,       q.rank_stride_bytes, (char*)s.base, s.rank_stride_bytes,
-                 (char*)r.base,       r.rank_stride_bytes, M, bnd, N, dt, vec_ok, cfg.blocks_per_cu,
+                 (char*)r.base,       r.rank_stride_bytes, M, N, dt, vec_ok, cfg.blocks_per_cu,
                  (hipStream_t)st};
 }
 
@@ -88,7 +80,7 @@ cc_status_t cc_quantize_ef(cc_rankbuf_t grad, cc_rankbuf_t err, cc_rankbuf_t q, 
   if ((s = device_ready())) return s;
   const int vec_ok = al(grad) && al(err) && al(q) && al(scales);
   const cc_rankbuf_t none{nullptr, 0};
-  return hip_status(launch_quant_ef(q_launch(grad, err, q, scales, none, M, nullptr, N, (int)dtype, vec_ok, cfg,
+  return hip_status(launch_quant_ef(q_launch(grad, err, q, scales, none, M, N, (int)dtype, vec_ok, cfg,
                                              stream)),
                     "int8 quantize with error feedback");
 }
@@ -106,10 +98,9 @@ cc_status_t cc_all_reduce_dequant(cc_rankbuf_t q, cc_rankbuf_t scales, cc_rankbu
     if ((s = check_side(*x.b, x.n, N, x.name))) return s;
   if ((s = disjoint(sd, 3, N))) return s;
   if ((s = device_ready())) return s;
-  const QBounds bd(M, N);
   const int vec_ok = al(q) && al(scales) && al(recv);
   const cc_rankbuf_t none{nullptr, 0};
-  return hip_status(launch_dequant_reduce(q_launch(none, none, q, scales, recv, M, bd.b, N, (int)dtype, vec_ok, cfg,
+  return hip_status(launch_dequant_reduce(q_launch(none, none, q, scales, recv, M, N, (int)dtype, vec_ok, cfg,
                                                    stream)),
                     "all_reduce of int8 messages");
 }
@@ -140,16 +131,15 @@ cc_status_t cc_all_reduce_int8_ef(cc_rankbuf_t grad, cc_rankbuf_t err, cc_rankbu
         return fail(CC_ERR_INVALID_ARG, "the workspace overlaps %s", x.name);
   }
   if ((s = device_ready())) return s;
-  const QBounds bd(M, N);
   if (!need) {
     const int vec_ok = al(grad) && al(err) && al(recv);
-    return hip_status(launch_quant_ef_fused(q_launch(grad, err, qb, sb, recv, M, bd.b, N, (int)dtype, vec_ok, cfg,
+    return hip_status(launch_quant_ef_fused(q_launch(grad, err, qb, sb, recv, M, N, (int)dtype, vec_ok, cfg,
                                                      stream)),
                       "int8 all_reduce with error feedback");
   }
   const int vec_ok = al(grad) && al(err) && al(recv) && al(qb) && al(sb);
-  hipError_t e = launch_quant_ef(q_launch(grad, err, qb, sb, recv, M, bd.b, N, (int)dtype, vec_ok, cfg, stream));
-  if (e == hipSuccess) e = launch_dequant_reduce(q_launch(grad, err, qb, sb, recv, M, bd.b, N, (int)dtype, vec_ok, cfg, stream));
+  hipError_t e = launch_quant_ef(q_launch(grad, err, qb, sb, recv, M, N, (int)dtype, vec_ok, cfg, stream));
+  if (e == hipSuccess) e = launch_dequant_reduce(q_launch(grad, err, qb, sb, recv, M, N, (int)dtype, vec_ok, cfg, stream));
   return hip_status(e, "int8 all_reduce with error feedback (two kernels)");
 }
 

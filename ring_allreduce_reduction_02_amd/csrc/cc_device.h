@@ -178,17 +178,10 @@ __device__ __forceinline__ void opv(const typename Ty<DT>::A* x, typename Ty<DT>
 
 // ------------------------------------------------------------------ chunks
 
-// Chunk c holds [bnd[c], bnd[c+1]) with bnd[c] = floor(c*M/N) (computed on the
-// host).  The chunk of an element e is the number of inner boundaries at or
-// below e; with a workgroup-uniform e the loop runs on the scalar unit.
-__device__ __forceinline__ uint32_t chunk_in(const uint64_t* bnd, int N, uint64_t e) {
-  uint32_t c = 0;
-  for (int i = 1; i < N; ++i) c += bnd[i] <= e ? 1u : 0u;
-  return c;
-}
-// The same chunk when the bounds are exactly floor(c*M/N), as they are for
-// every schedule's chunks: floor(c*M/N) <= e holds for c <= ((e+1)*N - 1)/M,
-// so one quotient replaces the scan.  The quotient is below N <= 64: a float
+// Chunk c holds [floor(c*M/N), floor((c+1)*M/N)) for every schedule.  The
+// chunk of an element e is the largest c with floor(c*M/N) <= e, which holds
+// for c <= ((e+1)*N - 1)/M, so one quotient gives it with no scan over the
+// N+1 bounds.  The quotient is below N <= 64: a float
 // estimate through the reciprocal is within 2^-14 of num/M (each of the two
 // conversions, the reciprocal and the product adds at most about 2^-23
 // relative error), so its floor is off by at most one, and one 64-bit
@@ -240,26 +233,8 @@ struct Tile {
 };
 
 // The workgroup's element range and, when the whole tile is full-width and
-// lies in one chunk, that chunk (uniform across the workgroup).
-template <int V>
-__device__ __forceinline__ Tile<V> tile_at(uint64_t idx, uint64_t M, const uint64_t* bnd, int N, int vec_ok) {
-  const uint64_t tile = (uint64_t)kBlock * kUnroll * V;
-  Tile<V> t;
-  t.e0 = idx * tile;
-  t.e1 = t.e0 + tile < M ? t.e0 + tile : M;
-  const uint32_t c0 = chunk_in(bnd, N, t.e0);
-  const uint32_t c1 = chunk_in(bnd, N, t.e1 - 1);
-  t.c = c0;
-  t.fast = vec_ok && (t.e1 - t.e0) == tile && c0 == c1;
-  return t;
-}
-template <int V>
-__device__ __forceinline__ Tile<V> tile_of(uint64_t M, const uint64_t* bnd, int N, int vec_ok) {
-  return tile_at<V>(blockIdx.x, M, bnd, N, vec_ok);
-}
-// The same for chunks at the floor bounds floor(c M / N): the chunks of the
-// tile's first and last element by the closed form, a fixed cost instead of
-// a scan over the N+1 bounds (each step of which waits for a scalar load).
+// lies in one chunk, that chunk (uniform across the workgroup), from the
+// closed-form chunks of the tile's first and last element.
 template <int V>
 __device__ __forceinline__ Tile<V> tile_floor(uint64_t idx, uint64_t M, int N, int vec_ok) {
   const uint64_t tile = (uint64_t)kBlock * kUnroll * V;

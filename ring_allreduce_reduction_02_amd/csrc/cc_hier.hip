@@ -30,6 +30,7 @@ struct HierArgs {
   int top;
   int vec_ok;
   int tpc_log2;  // segments of exactly 2^k full tiles: log2 of k, else -1
+  int one;       // store each result once, to the owner of its flat ring chunk
   int p[kMaxHierLevels];
   int stride[kMaxHierLevels];
   uint32_t seg[kMaxRanks];       // the segments' chunk indices, 8 bits per level
@@ -145,6 +146,13 @@ __device__ __forceinline__ void hier_take(const HierLv& L, const HierPos& w, con
 
 constexpr int kHierBatch = 8;  // leaves loaded ahead of their folds
 
+// The rank that owns element e after a flat ring ReduceScatter: c - 1 for
+// its chunk c = floor(((e + 1) N - 1) / M).
+__device__ __forceinline__ int hier_owner(const HierArgs& a, uint64_t e) {
+  const int c = (int)chunk_of(a.M, a.N, e);
+  return c == 0 ? a.N - 1 : c - 1;
+}
+
 template <int DT, int OP>
 __global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
   typedef typename Ty<DT>::A A;
@@ -186,9 +194,20 @@ __global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
           hier_step(L, fw);
         }
     }
-    const u32x4 o = pack<DT>(a3);
-    char* d = a.rb + t.e0 * SZ;
-    for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, o);
+    if (a.one) {
+      const int o0 = hier_owner(a, t.e0);
+      if (o0 == hier_owner(a, t.e1 - 1)) {
+        stg(a.rb + (uint64_t)o0 * a.rs + t.e0 * SZ + lane, pack<DT>(a3));
+      } else {  // the tile holds a flat chunk bound
+        const uint64_t e = t.e0 + (uint64_t)threadIdx.x * V;
+#pragma unroll
+        for (int k = 0; k < V; ++k) st1<DT>(a.rb + (uint64_t)hier_owner(a, e + k) * a.rs + (e + k) * SZ, a3[k]);
+      }
+    } else {
+      const u32x4 o = pack<DT>(a3);
+      char* d = a.rb + t.e0 * SZ;
+      for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, o);
+    }
   } else {
     // a thread's elements are kBlock apart: the segment is looked up again
     // only when an element leaves the previous one's
@@ -221,10 +240,28 @@ __global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
             hier_step(L, fw);
           }
       }
-      for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, a3[0]);
+      if (a.one)
+        st1<DT>(a.rb + (uint64_t)hier_owner(a, e) * a.rs + e * SZ, a3[0]);
+      else
+        for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, a3[0]);
     }
   }
 }
+
+// The split form, as the flat ring's: the fold stored once, to the rank that
+// owns the element's flat ring chunk after a ReduceScatter, then the ring
+// AllGather's copy from those owners to every other rank.  Taken from 32
+// ranks of 4 MiB on.  Measured on the MI355X (graph replays over rotating
+// buffer sets of 1 GiB or more, rows by the rank-stride rule, fp32 and bf16;
+// split time over one-launch time): 64 ranks (8x8, 4x4x4, 2x32) 0.87-0.99
+// from 4 to 64 MiB per rank; 32 ranks (4x8, 2x16, 2x2x2x4) 0.88-0.96 at 4
+// and 8 MiB, 0.95-1.06 (mean 0.99) from 16 to 64 MiB.  The first launch, N
+// loads and one store per vector, streams best at 4 workgroups per CU (at
+// 64 MiB per rank 2x32 0.89-0.96 against 1.07-1.17 at 2, 0.92-1.00 at 3).
+bool hier_split(const Red& r) {
+  return r.N >= 32 && r.M * (uint64_t)(16 / vec_elems(r.dt)) >= (4ull << 20);
+}
+constexpr int kHierOneBlocks = 4;
 
 }  // namespace
 
@@ -243,14 +280,22 @@ hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int 
   }
   for (int s = 0; s < r.N; ++s) a.seg[s] = seg[s];
   for (int s = 0; s <= r.N; ++s) a.bnd[s] = segbnd[s];
+  a.one = hier_split(r) ? 1 : 0;
   const dim3 grid((unsigned)num_tiles(r.M, r.dt)), blk(kBlock);
+  const int bpc = a.one ? kHierOneBlocks : hier_blocks_per_cu(r.N);
   const unsigned lds = lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu
-                                                                 : one_round_blocks(num_tiles(r.M, r.dt), hier_blocks_per_cu(r.N)));
-  return by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
+                                                                 : one_round_blocks(num_tiles(r.M, r.dt), bpc));
+  hipError_t e = by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
     CC_LAUNCH((k_hier_fused<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });
+  if (e != hipSuccess || !a.one) return e;
+  // the AllGather from the owners of the flat ring chunks
+  uint64_t fb[kMaxRanks + 1];
+  for (int c = 0; c <= r.N; ++c) fb[c] = (uint64_t)(((unsigned __int128)c * r.M) / (unsigned)r.N);
+  const Gat g{r.recv, r.recv, r.M, fb, r.blocks_per_cu, r.N, 16 / vec_elems(r.dt), 0, r.vec_ok, r.st};
+  return launch_ag_fused(g);
 }
 
 }  // namespace cc

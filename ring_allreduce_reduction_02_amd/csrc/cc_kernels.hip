@@ -40,6 +40,9 @@ namespace {
 // registers in the schedule's order, then the AllGather as N stores.
 // ReduceScatter (rs_mode 1, ring and halving-doubling): only the owner is
 // written; the ring's fold then starts one rank later.
+// The ReduceScatter half of a split ring AllReduce (rs_mode 2): the
+// AllReduce's fold, stored only to the rank that owns the chunk after the
+// ReduceScatter (rank c-1 for chunk c), at the chunk's place in its vector.
 // U: 16-byte vectors per thread and rank (a tile of U kBlock vectors).
 template <int DT, int OP, int NR, int ALG, int U = 1>
 __device__ __forceinline__ void fused_body(const FusedArgs& a) {
@@ -62,7 +65,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     // its own 16-byte offset (scalar base + 32-bit vector offset), vector u
     // of the thread another kBlock vectors on.
     const int c = (int)t.c;
-    const int start = (ALG == ALG_RING && a.rs_mode) ? wrapN(c + 1, N) : c;
+    const int start = (ALG == ALG_RING && a.rs_mode == 1) ? wrapN(c + 1, N) : c;
     const uint32_t lane = threadIdx.x * 16u;
     constexpr uint32_t kStep = kBlock * 16u;
     const uint64_t eb = t.e0 * SZ;
@@ -72,8 +75,12 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     u32x4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) w[u] = pack<DT>(acc[u]);
-    if (a.rs_mode) {
+    if (a.rs_mode == 1) {
       char* d = a.rb + (uint64_t)c * a.rs + (t.e0 - a.bnd[c]) * SZ + lane;
+#pragma unroll
+      for (int u = 0; u < U; ++u) stg(d + u * kStep, w[u]);
+    } else if (a.rs_mode == 2) {
+      char* d = a.rb + (uint64_t)wrapN(c + N - 1, N) * a.rs + eb + lane;
 #pragma unroll
       for (int u = 0; u < U; ++u) stg(d + u * kStep, w[u]);
     } else {
@@ -115,7 +122,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
         ev[u] = ok[u] ? e : t.e0;
         off[u] = ev[u] * SZ;
         cv[u] = tiling == 1 ? 0u : chunk_of(a.M, tiling, ev[u]);
-        st[u] = (ALG == ALG_RING && a.rs_mode) ? wrapN((int)cv[u] + 1, N) : (int)cv[u];
+        st[u] = (ALG == ALG_RING && a.rs_mode == 1) ? wrapN((int)cv[u] + 1, N) : (int)cv[u];
       }
       A acc[G];
       if constexpr (ALG == ALG_RING) {
@@ -127,8 +134,10 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
 #pragma unroll
       for (int u = 0; u < G; ++u) {
         if (!ok[u]) continue;
-        if (a.rs_mode) {
+        if (a.rs_mode == 1) {
           st1<DT>(a.rb + (uint64_t)cv[u] * a.rs + (ev[u] - bound_of(a.M, tiling, cv[u])) * SZ, acc[u]);
+        } else if (a.rs_mode == 2) {
+          st1<DT>(a.rb + (uint64_t)wrapN((int)cv[u] + N - 1, N) * a.rs + off[u], acc[u]);
         } else {
           for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + off[u], acc[u]);
         }
@@ -198,8 +207,32 @@ int default_blocks_per_cu(uint64_t traffic, uint64_t target, int min_blocks) {
 // 32.8-33.0 against 26.1.  Below (the element-wise path of small chunks, then
 // twice the elements per thread) and above (2 MiB per rank level, 16 MiB and
 // up 2-25% slower) one vector per thread stays.
-hipError_t launch_ring_fused(const Red& r) {
+namespace {
+
+// The split form of the fused ring AllReduce: two launches, the ReduceScatter
+// (every chunk's fold stored to its owner only) and the AllGather (the
+// owner's chunk copied to the other ranks).  It moves (2N+1) M s bytes
+// against the one-launch form's 2 N M s, as two streams that are each read-
+// or write-heavy instead of one with N loads and N stores per vector, which
+// the HBM serves faster from 32 ranks on, for 4-byte elements from 8 MiB per
+// rank and for bf16 from 32 MiB.  Measured on the MI355X (graph replays over
+// rotating buffer sets of 1 GiB or more, rows by the rank-stride rule, two
+// runs of each form; split time over one-launch time, mean and range over N
+// = 32, 34, 36, 40, 44, ..., 64): fp32 8 MiB per rank 0.93 (0.89-0.97), 16
+// MiB 0.96 (0.91-1.01), 32 MiB 0.98 (0.94-1.01), 64 MiB 0.95 (0.92-0.96);
+// bf16 8 MiB 1.05 (0.92-1.14), 16 MiB 1.00 (0.97-1.07), 32 MiB 0.99
+// (0.93-1.04), 64 MiB 0.97 (0.94-1.02).  At 4 MiB per rank and below
+// (1.01-1.24 from 32 ranks, the second launch included) and below 32 ranks
+// (8-30 ranks at 16 and 64 MiB: 0.93-1.16) the one-launch form is as fast or
+// faster.
+bool ring_split(const Red& r) {
+  const uint64_t bytes = r.M * (uint64_t)(16 / vec_elems(r.dt));
+  return r.N >= 32 && bytes >= (r.dt == DT_BF16 ? 32ull << 20 : 8ull << 20);
+}
+
+hipError_t launch_ring_kernel(const Red& r, int mode) {
   FusedArgs a = fused_args(r);
+  a.rs_mode = mode;
   const uint64_t tiles1 = num_tiles(r.M, r.dt);
   const int cus = dev_info().cus;
   const bool wide = cus > 0 && tiles1 >= 8ull * (uint64_t)cus && tiles1 <= 16ull * (uint64_t)cus;
@@ -216,7 +249,7 @@ hipError_t launch_ring_fused(const Red& r) {
                        : (r.N == 2 && r.dt != DT_BF16) ? 6
                                                        : 0;
   const unsigned lds =
-      r.rs_mode ? rs_fused_lds(r)
+      mode ? rs_fused_lds(r)
       : runtime_n ? lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu
                                                               : one_round_blocks(num_tiles(r.M, r.dt),
                                                                                  batched_ring_blocks_per_cu(r.N, r.dt)))
@@ -237,6 +270,18 @@ hipError_t launch_ring_fused(const Red& r) {
     };
     return wide ? go(IC<2>{}) : go(IC<1>{});
   });
+}
+
+}  // namespace
+
+hipError_t launch_ring_fused(const Red& r) {
+  if (r.rs_mode == 0 && ring_split(r)) {
+    const hipError_t e = launch_ring_kernel(r, 2);
+    if (e != hipSuccess) return e;
+    const Gat g{r.recv, r.recv, r.M, r.bnd, r.blocks_per_cu, r.N, 16 / vec_elems(r.dt), 0, r.vec_ok, r.st};
+    return launch_ag_fused(g);
+  }
+  return launch_ring_kernel(r, r.rs_mode);
 }
 
 hipError_t launch_tree_fused(const Red& r, int tree) {

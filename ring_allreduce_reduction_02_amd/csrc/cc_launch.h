@@ -99,8 +99,9 @@ hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int 
 
 // ---- INT8 compression with error feedback: blocks of kQBlock elements of a
 // rank's vector, one float32 scale each.  g: gradients (dt), e: float32 error
-// accumulators, q: int8 values, s: float32 scales, r: results (dt); bnd: the
-// N chunks of the ring order.
+// accumulators, q: int8 values, s: float32 scales, r: results (dt).  The
+// reductions fold each element in the ring order of its chunk
+// [floor(c M / N), floor((c+1) M / N)).
 constexpr int kQBlock = 128;
 struct QLaunch {
   const char* g;
@@ -114,7 +115,6 @@ struct QLaunch {
   char* r;
   uint64_t rs;
   uint64_t M;
-  const uint64_t* bnd;
   int N;
   int dt;  // DT_F32 or DT_BF16
   int vec_ok;

@@ -28,7 +28,6 @@ struct QArgs {
   int N;
   int vec_ok;
   int tpc_log2;  // chunks of exactly 2^k full tiles: log2 of k, else -1
-  uint64_t bnd[kMaxRanks + 1];
 };
 
 // The compression kernels give every lane 4 consecutive elements of a rank,
@@ -391,8 +390,7 @@ QArgs q_args(const QLaunch& L) {
   a.sb = L.s; a.ss = L.ss;
   a.rb = L.r; a.rs = L.rs;
   a.M = L.M; a.N = L.N; a.vec_ok = L.vec_ok;
-  a.tpc_log2 = L.bnd ? pow2_tiles_per_chunk_v(L.M, L.N, kQLane, L.vec_ok) : -1;
-  for (int c = 0; c <= L.N; ++c) a.bnd[c] = L.bnd ? L.bnd[c] : 0;
+  a.tpc_log2 = pow2_tiles_per_chunk_v(L.M, L.N, kQLane, L.vec_ok);
   return a;
 }
 // dynamic LDS: the occupancy reservation (the caller's, else `dflt`
@@ -426,7 +424,7 @@ hipError_t launch_quant_ef(const QLaunch& L) {
 }
 
 hipError_t launch_dequant_reduce(const QLaunch& L) {
-  if (L.N < 1 || L.N > kMaxRanks || (L.dt != DT_F32 && L.dt != DT_BF16) || !L.bnd) return hipErrorInvalidValue;
+  if (L.N < 1 || L.N > kMaxRanks || (L.dt != DT_F32 && L.dt != DT_BF16)) return hipErrorInvalidValue;
   const QArgs a = q_args(L);  // vec_ok: int8 rows, scales and results 16-byte aligned (base and stride)
   const uint64_t tiles = (L.M + kDqTile - 1) / kDqTile;
   if (tiles > 0x7fffffffull) return hipErrorInvalidValue;
@@ -439,7 +437,7 @@ hipError_t launch_dequant_reduce(const QLaunch& L) {
 }
 
 hipError_t launch_quant_ef_fused(const QLaunch& L) {
-  if (L.N < 1 || L.N > kMaxRanks || (L.dt != DT_F32 && L.dt != DT_BF16) || !L.bnd) return hipErrorInvalidValue;
+  if (L.N < 1 || L.N > kMaxRanks || (L.dt != DT_F32 && L.dt != DT_BF16)) return hipErrorInvalidValue;
   const QArgs a = q_args(L);
   const dim3 grid((unsigned)((L.M + kQTile - 1) / kQTile)), blk(kBlock);
   const unsigned lds = q_lds(L.blocks_per_cu, qfused_blocks_per_cu(L.dt));

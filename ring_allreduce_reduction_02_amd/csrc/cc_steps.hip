@@ -373,12 +373,12 @@ __global__ __launch_bounds__(kBlock) void k_ring_ag_pass(GatArgs a) {
   ring_ag_tile<SZ>(a, blockIdx.x, a.s0, a.k);
 }
 
-// The standalone AllGather in one pass, with the N stores of a tile's
-// vectors shared between G groups of kBlock threads: every group loads the
-// tile's vectors of rank c's shard (the first load brings the lines into the
-// XCD's L2, the other group finds them there) and stores them to ranks g,
-// g + G, g + 2G, ...  Element-wise tiles run the pass's own path in the
-// first group.
+// The AllGather in one pass, with the N stores of a tile's vectors shared
+// between G groups of kBlock threads: every group loads the tile's vectors of
+// chunk c (the standalone AllGather's shard of rank c, or the AllReduce's
+// chunk on its owner; the first load brings the lines into the XCD's L2, the
+// other group finds them there) and stores them to ranks g, g + G, g + 2G,
+// ...  Element-wise tiles run the pass's own path in the first group.
 template <int SZ, int G>
 __global__ __launch_bounds__(kBlock * G) void k_ag_groups(GatArgs a) {
   constexpr int V = 16 / SZ;
@@ -388,8 +388,15 @@ __global__ __launch_bounds__(kBlock * G) void k_ag_groups(GatArgs a) {
   if (t.fast) {
     const int c = (int)t.c;
     const uint64_t e = t.e0 + (uint64_t)lane * V;
-    const u32x4 w = ldg(a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ);
-    for (int r = (int)g; r < N; r += G) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
+    if (a.mode == 1) {
+      const u32x4 w = ldg(a.sb + (uint64_t)c * a.ss + (e - a.bnd[c]) * SZ);
+      for (int r = (int)g; r < N; r += G) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
+    } else {  // AllReduce: from the owner, rank c-1, to every other rank
+      const int own = c == 0 ? N - 1 : c - 1;
+      const u32x4 w = ldg(a.rb + (uint64_t)own * a.rs + e * SZ);
+      for (int r = (int)g; r < N; r += G)
+        if (r != own) stg(a.rb + (uint64_t)r * a.rs + e * SZ, w);
+    }
   } else if (g == 0) {
     ring_ag_tile<SZ>(a, blockIdx.x, 0, N - 1);
   }
@@ -853,9 +860,8 @@ static hipError_t launch_ag_groups(const GatArgs& a, unsigned tiles, unsigned ld
 }
 
 hipError_t launch_ag_fused(const Gat& g) {
-  // the grouped kernel is the standalone AllGather's (ag_mode 1), within
-  // 32-bit work-item counts
-  const int G = g.ag_mode == 1 && (uint64_t)gat_tiles(g) * kBlock * ag_groups(g.N) <= 0xffffffffull ? ag_groups(g.N) : 1;
+  // the grouped kernel within 32-bit work-item counts
+  const int G = (uint64_t)gat_tiles(g) * kBlock * ag_groups(g.N) <= 0xffffffffull ? ag_groups(g.N) : 1;
   if (G == 1) {
     // one group follows the write-heavy byte rule, capped at 10 workgroups
     // per CU below 6 ranks and at 8 from 6 on: the rule's 11-16 overfill the

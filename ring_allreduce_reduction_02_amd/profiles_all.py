@@ -52,7 +52,17 @@ ENTRIES = {
     "hier_2x2x2": ("section", "k_hier_fused<1, 0>", "cc_hier.hip", "hier_fused_f32_2x2x2_m67108864",
                    "fused hierarchical AllReduce, grid 2x2x2 (N=8), M=67108864 fp32 per rank"),
     "hier_8x8": ("section", "k_hier_fused<1, 0>", "cc_hier.hip", "hier_fused_f32_8x8_m8388608",
-                 "fused hierarchical AllReduce, grid 8x8 (N=64), M=8388608 fp32 per rank"),
+                 "hierarchical AllReduce, grid 8x8 (N=64), M=8388608 fp32 per rank: the split form's first "
+                 "launch (nested fold stored once, to the owner of the element's flat ring chunk)"),
+    "hier_8x8_ag": ("section", "k_ag_groups<4, 2>", "cc_steps.hip", "ag_groups_hier_f32_8x8_m8388608",
+                    "hierarchical AllReduce, grid 8x8 (N=64), M=8388608 fp32 per rank: the split form's "
+                    "AllGather launch (owners' chunks to the other 63 ranks)"),
+    "ring_n64": ("section", "k_ring_fused<1, 0, 0, 1>", "cc_kernels.hip", "ring_split_rs_f32_n64_m8388608",
+                 "ring AllReduce, N=64, M=8388608 fp32 per rank: the split form's ReduceScatter launch "
+                 "(each chunk's fold stored to its owner)"),
+    "ring_n64_ag": ("section", "k_ag_groups<4, 2>", "cc_steps.hip", "ag_groups_ring_f32_n64_m8388608",
+                    "ring AllReduce, N=64, M=8388608 fp32 per rank: the split form's AllGather launch "
+                    "(owners' chunks to the other 63 ranks)"),
     "dbt_n8": ("section", "k_dbt_fused<1, 0, 8, true>", "cc_trees.hip", "dbt_fused_f32_n8_m67108864",
                "fused double binary tree AllReduce, N=8, M=67108864 fp32 per rank"),
     "int8_ef_f32": ("section", "k_quant_ef_fused<1>", "cc_quant.hip", "quant_ef_fused_f32_n8_m67108864",
