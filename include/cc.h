@@ -112,6 +112,11 @@ typedef enum {
  *  fuse_depth = 0: fully fused -- one kernel folds every rank's contribution
  *                  in registers in the schedule's order and writes the result
  *                  to every destination (read N*M, write N*M for AllReduce).
+ *                  The ring AllReduce from 32 ranks (from 8 MiB per rank for
+ *                  4-byte elements, 32 MiB for bf16) runs its two phases as
+ *                  two such kernels instead: each chunk's whole fold stored
+ *                  to its owner, then the owners' chunks copied to the other
+ *                  ranks (the same bits, M more elements read; faster there).
  *  fuse_depth = 1: stepwise -- one kernel per schedule step, each doing the
  *                  step's reads, combines and writes in HBM.
  *  fuse_depth = k: ring only -- k consecutive ring steps per kernel (other
@@ -343,7 +348,10 @@ cc_status_t cc_all_reduce_plan(cc_algo_t algo, int nranks, size_t count, cc_plan
  * most 4 levels of size > 1 (CC_ERR_UNSUPPORTED beyond).  cfg: algo must be
  * CC_ALGO_RING and grid_sync 0 (CC_ERR_UNSUPPORTED otherwise).
  *  fuse_depth = 0: one kernel folds every element's nested chains in
- *                  registers and writes every rank's result;
+ *                  registers and writes every rank's result (from 32 ranks
+ *                  of 4 MiB: writes it to the owner of the element's flat
+ *                  ring chunk, and a second kernel copies it from there to
+ *                  the other ranks; the same bits);
  *  fuse_depth >= 1: one kernel per ring step of the schedule, the groups of
  *                  a level side by side; partials live in recv (int32,
  *                  fp32) or in the workspace (bf16, fp32 per rank and
