@@ -314,42 +314,58 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant_reduce(QArgs a) {
   }
 }
 
-// Compression and reduction in one pass, no message in memory.
-template <int DT>
+// Compression and reduction in one pass, no message in memory.  A workgroup
+// takes U groups of kQTile elements (a thread's 4 elements in each) and
+// walks the ranks B at a time, loading a batch's gradients and accumulators
+// before it compresses them.  Measured on the MI355X (8 ranks x 67,108,864,
+// rows by the rank-stride rule, two interleaved runs, best occupancy of 1-5
+// workgroups per CU; TB/s of the kernel's bytes): U = 2, B = 1 5.85-5.88
+// fp32 (3 per CU) and 5.91 bf16 (4); U = 1, B = 4 (the earlier form)
+// 5.49-5.50 and 5.62; U = 2, B = 2 5.75-5.79 and 5.74-5.76; U = 4, B = 1
+// 5.53 and 5.56-5.59; U = 4, B = 2 5.38 and 5.53-5.56.
+constexpr int kQfU = 2, kQfB = 1;
+template <int DT, int U>
 __global__ __launch_bounds__(kBlock) void k_quant_ef_fused(QArgs a) {
   extern __shared__ float qred[];
   constexpr int V = kQLane;
   constexpr int SZ = Ty<DT>::SZ;
-  constexpr int B = 4;  // ranks loaded ahead of their compression
+  constexpr int B = kQfB;  // ranks loaded ahead of their compression
   const int N = a.N;
-  const Tile<V> t = a.tpc_log2 >= 0 ? tile_pow2<V>(blockIdx.x, a.tpc_log2) : tile_floor<V>(blockIdx.x, a.M, N, a.vec_ok);
+  const Tile<V * U> t = a.tpc_log2 >= 0 ? tile_pow2<V * U>(blockIdx.x, a.tpc_log2)
+                                        : tile_floor<V * U>(blockIdx.x, a.M, N, a.vec_ok);
   if (t.fast) {
     const uint32_t lane = threadIdx.x;
-    const uint64_t el = t.e0 + (uint64_t)lane * V;
-    float acc[V];
+    float acc[U][V];
     int r = (int)t.c;
     for (int j0 = 0; j0 < N; j0 += B) {
-      float x[B][V], e[B][V];
+      float x[B][U][V], e[B][U][V];
       int rs[B];
       int rr = r;
 #pragma unroll
       for (int k = 0; k < B; ++k) {  // past the last rank the loads repeat valid ones
         rs[k] = rr;
-        load_ge<DT>(a, t.e0, rr, lane, x[k], e[k]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_ge<DT>(a, t.e0 + u * kQTile, rr, lane, x[k][u], e[k][u]);
         if (j0 + k + 1 < N) rr = rr + 1 == N ? 0 : rr + 1;
       }
 #pragma unroll
       for (int k = 0; k < B; ++k)
         if (j0 + k < N) {
-          float v[V];
-          quant_lane<false>(x[k], e[k], v, a.eb + (uint64_t)rs[k] * a.es + el * 4, nullptr, nullptr);
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] = (j0 + k == 0) ? v[i] : v[i] + acc[i];
+          for (int u = 0; u < U; ++u) {
+            const uint64_t el = t.e0 + u * kQTile + (uint64_t)lane * V;
+            float v[V];
+            quant_lane<false>(x[k][u], e[k][u], v, a.eb + (uint64_t)rs[k] * a.es + el * 4, nullptr, nullptr);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[u][i] = (j0 + k == 0) ? v[i] : v[i] + acc[u][i];
+          }
         }
       r = rr;  // the first rank of the next batch (rr moved past the last load)
     }
-    char* d = a.rb + el * SZ;
-    for (int k = 0; k < N; ++k, d += a.rs) st4<DT>(d, acc);
+    char* d = a.rb + (t.e0 + (uint64_t)lane * V) * SZ;
+    for (int k = 0; k < N; ++k, d += a.rs)
+#pragma unroll
+      for (int u = 0; u < U; ++u) st4<DT>(d + u * kQTile * SZ, acc[u]);
   } else {
     // per block: the N scales first (they need every element of the block),
     // then each element folds in the ring order of its own chunk
@@ -405,12 +421,12 @@ unsigned q_lds(int blocks_per_cu, int dflt) {
 // elements (2 to 16 per CU): the compression step streams best at 16 (float32
 // gradients 6.41 TB/s against 5.69 at 8; bf16 6.46 against 5.17 at 8), the
 // reduction of the messages at 4 for float32 results and 6 for bf16 (5.78 and
-// 6.05 TB/s; 5.31 and 6.05 at 6, 5.54 and 5.51 at 4), the fused kernel, which
-// keeps four ranks' loads in flight, at 4 for float32 (5.89 TB/s) and 5 for
-// bf16 (5.99 against 5.25 at 3).
+// 6.05 TB/s; 5.31 and 6.05 at 6, 5.54 and 5.51 at 4), the fused kernel at 3
+// for float32 and 4 for bf16 (1-5 per CU: float32 5.85-5.88 against 2.79-5.19
+// at 1, 2, 4, 5; bf16 5.91 against 5.28-5.49 at 3 and 5).
 int quant_blocks_per_cu(int) { return 16; }
 int dequant_blocks_per_cu(int dt) { return dt == DT_F32 ? 4 : 6; }
-int qfused_blocks_per_cu(int dt) { return dt == DT_F32 ? 4 : 5; }
+int qfused_blocks_per_cu(int dt) { return dt == DT_F32 ? 3 : 4; }
 }  // namespace
 
 hipError_t launch_quant_ef(const QLaunch& L) {
@@ -438,11 +454,13 @@ hipError_t launch_dequant_reduce(const QLaunch& L) {
 
 hipError_t launch_quant_ef_fused(const QLaunch& L) {
   if (L.N < 1 || L.N > kMaxRanks || (L.dt != DT_F32 && L.dt != DT_BF16)) return hipErrorInvalidValue;
-  const QArgs a = q_args(L);
-  const dim3 grid((unsigned)((L.M + kQTile - 1) / kQTile)), blk(kBlock);
+  constexpr int U = kQfU;
+  QArgs a = q_args(L);
+  a.tpc_log2 = pow2_tiles_per_chunk_v(L.M, L.N, kQLane * U, L.vec_ok);
+  const dim3 grid((unsigned)((L.M + U * kQTile - 1) / (U * kQTile))), blk(kBlock);
   const unsigned lds = q_lds(L.blocks_per_cu, qfused_blocks_per_cu(L.dt));
-  if (L.dt == DT_F32) CC_LAUNCH((k_quant_ef_fused<DT_F32>), grid, blk, lds, L.st, a);
-  else CC_LAUNCH((k_quant_ef_fused<DT_BF16>), grid, blk, lds, L.st, a);
+  if (L.dt == DT_F32) CC_LAUNCH((k_quant_ef_fused<DT_F32, U>), grid, blk, lds, L.st, a);
+  else CC_LAUNCH((k_quant_ef_fused<DT_BF16, U>), grid, blk, lds, L.st, a);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ from ring_allreduce_reduction_02_amd import ccgpu
 from tests.gpu_util import DEV, alloc_ranks, bits, download, upload
 
 pytestmark = pytest.mark.gpu
-SIZES = [1, 13, 130, 6151, 20485, 65536]
+SIZES = [1, 13, 130, 6151, 12288, 20485, 65536]   # 12288: 3 ranks of four 1024-element tiles
 NS = [1, 2, 3, 8, 17]
 
 
