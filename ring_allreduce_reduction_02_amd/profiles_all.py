@@ -65,9 +65,9 @@ ENTRIES = {
                     "(owners' chunks to the other 63 ranks)"),
     "dbt_n8": ("section", "k_dbt_fused<1, 0, 8, true>", "cc_trees.hip", "dbt_fused_f32_n8_m67108864",
                "fused double binary tree AllReduce, N=8, M=67108864 fp32 per rank"),
-    "int8_ef_f32": ("section", "k_quant_ef_fused<1>", "cc_quant.hip", "quant_ef_fused_f32_n8_m67108864",
+    "int8_ef_f32": ("section", "k_quant_ef_fused<1, 2>", "cc_quant.hip", "quant_ef_fused_f32_n8_m67108864",
                     "fused INT8 AllReduce with error feedback, N=8, M=67108864 fp32 gradients per rank"),
-    "int8_ef_bf16": ("section", "k_quant_ef_fused<2>", "cc_quant.hip", "quant_ef_fused_bf16_n8_m67108864",
+    "int8_ef_bf16": ("section", "k_quant_ef_fused<2, 2>", "cc_quant.hip", "quant_ef_fused_bf16_n8_m67108864",
                      "fused INT8 AllReduce with error feedback, N=8, M=67108864 bf16 gradients per rank"),
     "int8_quant_f32": ("section", "k_quant_ef<1>", "cc_quant.hip", "quant_ef_f32_n8_m67108864",
                        "INT8 compression step with error feedback, N=8, M=67108864 fp32 gradients per rank"),
