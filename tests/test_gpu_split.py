@@ -117,3 +117,35 @@ def test_split_hierarchical(case):
     want = cs.hierarchical_all_reduce(xs, dims, op, dtype)
     for r in range(N):
         assert np.array_equal(bits(got[r]), bits(want[r])), (dims, M, dtype, op, offset, in_place, r)
+
+
+def test_split_forms_graph_replays():
+    """Both launches of the split forms captured into one HIP graph: every
+    replay, with eager work between them, equals the eager result."""
+    gen = torch.Generator(device="cuda:0").manual_seed(62)
+    x = torch.randn(32, F32_MIN + 5, generator=gen, device="cuda:0")
+    h = torch.randn(64, HIER_MIN, generator=gen, device="cuda:0")
+    ex, eh = torch.empty_like(x), torch.empty_like(h)
+    ccgpu.all_reduce(x, ex)
+    ccgpu.all_reduce_hierarchical(h, eh, (8, 8))
+    y, z = torch.empty_like(x), torch.empty_like(h)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ccgpu.all_reduce(x, y)
+        ccgpu.all_reduce_hierarchical(h, z, (8, 8))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ccgpu.all_reduce(x, y)
+        ccgpu.all_reduce_hierarchical(h, z, (8, 8))
+    for t in range(3):
+        say(f"split forms graph replay {t}")
+        y.fill_(3)
+        z.fill_(5)                       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), ex.view(torch.int32))
+        assert torch.equal(z.view(torch.int32), eh.view(torch.int32))

@@ -47,6 +47,7 @@ CASES = [
     (torch.bfloat16, "max", "double_tree", 1, False, 7, 300_000, 1_000),
     (torch.int32, "sum", "ring", 3, True, 16, 2_000_011, 3_001),
     (torch.float32, "sum", "ring", 0, False, 8, 1_048_576, 1_000),       # fused: no staging at all
+    (torch.float32, "sum", "ring", 0, False, 32, 2_097_152, 1_000),      # the split form, then one launch
 ]
 
 
