@@ -198,15 +198,6 @@ int default_blocks_per_cu(uint64_t traffic, uint64_t target, int min_blocks) {
 }
 
 
-// A grid of 8 to 16 one-vector tiles per CU (4 to 8 MiB per rank) takes two
-// vectors per thread: half the workgroups, each thread with twice the loads
-// in flight, in one round.  Measured on the MI355X (graph replays over
-// rotating buffer sets, one vector against two): int32 4 ranks x 1,048,576
-// 8.16-8.27 us against 6.64-6.70; fp32 8 ranks of 4 MiB 15.5-15.7 against
-// 12.5-12.6, of 8 MiB 28.3-28.8 against 26.8-26.9; fp32 16 ranks of 4 MiB
-// 32.8-33.0 against 26.1.  Below (the element-wise path of small chunks, then
-// twice the elements per thread) and above (2 MiB per rank level, 16 MiB and
-// up 2-25% slower) one vector per thread stays.
 namespace {
 
 // The split form of the fused ring AllReduce: two launches, the ReduceScatter
@@ -230,6 +221,17 @@ bool ring_split(const Red& r) {
   return r.N >= 32 && bytes >= (r.dt == DT_BF16 ? 32ull << 20 : 8ull << 20);
 }
 
+// A grid of 8 to 16 one-vector tiles per CU (4 to 8 MiB per rank) takes two
+// vectors per thread: half the workgroups, each thread with twice the loads
+// in flight, in one round.  Measured on the MI355X (graph replays over
+// rotating buffer sets, one vector against two): int32 4 ranks x 1,048,576
+// 8.16-8.27 us against 6.64-6.70; fp32 8 ranks of 4 MiB 15.5-15.7 against
+// 12.5-12.6, of 8 MiB 28.3-28.8 against 26.8-26.9; fp32 16 ranks of 4 MiB
+// 32.8-33.0 against 26.1.  Below (the element-wise path of small chunks, then
+// twice the elements per thread) and above (2 MiB per rank level, 16 MiB and
+// up 2-25% slower) one vector per thread stays.
+// mode: FusedArgs::rs_mode (0 AllReduce, 1 ReduceScatter, 2 the split form's
+// first launch).
 hipError_t launch_ring_kernel(const Red& r, int mode) {
   FusedArgs a = fused_args(r);
   a.rs_mode = mode;
