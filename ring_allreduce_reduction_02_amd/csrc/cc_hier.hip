@@ -153,6 +153,87 @@ __device__ __forceinline__ int hier_owner(const HierArgs& a, uint64_t e) {
   return c == 0 ? a.N - 1 : c - 1;
 }
 
+// The workgroup's tile: its segment, and whether it takes the vector path.
+template <int V>
+__device__ __forceinline__ Tile<V> hier_tile(const HierArgs& a) {
+  if (a.tpc_log2 >= 0) return tile_pow2<V>(blockIdx.x, a.tpc_log2);
+  const uint64_t tile = (uint64_t)kBlock * V;
+  Tile<V> t;
+  t.e0 = (uint64_t)blockIdx.x * tile;
+  t.e1 = t.e0 + tile < a.M ? t.e0 + tile : a.M;
+  t.c = hier_seg(a, t.e0);
+  t.fast = a.vec_ok && t.e1 - t.e0 == tile && t.e1 <= a.bnd[t.c + 1];
+  return t;
+}
+
+// A vector-path tile's results: to every rank, or once, to the owners.
+template <int DT>
+__device__ __forceinline__ void hier_store(const HierArgs& a, const Tile<Ty<DT>::V>& t,
+                                           const typename Ty<DT>::A (&res)[Ty<DT>::V]) {
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  const uint32_t lane = threadIdx.x * 16u;
+  if (a.one) {
+    const int o0 = hier_owner(a, t.e0);
+    if (o0 == hier_owner(a, t.e1 - 1)) {
+      stg(a.rb + (uint64_t)o0 * a.rs + t.e0 * SZ + lane, pack<DT>(res));
+    } else {  // the tile holds a flat chunk bound
+      const uint64_t e = t.e0 + (uint64_t)threadIdx.x * V;
+#pragma unroll
+      for (int k = 0; k < V; ++k) st1<DT>(a.rb + (uint64_t)hier_owner(a, e + k) * a.rs + (e + k) * SZ, res[k]);
+    }
+  } else {
+    const u32x4 o = pack<DT>(res);
+    char* d = a.rb + t.e0 * SZ;
+    for (int r = 0; r < a.N; ++r, d += a.rs) stg(d + lane, o);
+  }
+}
+
+// The element-wise path (a tile across segment bounds, a ragged tail,
+// unaligned buffers).
+template <int DT, int OP>
+__device__ __forceinline__ void hier_elems(const HierArgs& a, const Tile<Ty<DT>::V>& t) {
+  typedef typename Ty<DT>::A A;
+  constexpr int SZ = Ty<DT>::SZ;
+  const int N = a.N;
+  // a thread's elements are kBlock apart: the segment is looked up again
+  // only when an element leaves the previous one's
+  uint64_t slo = 1, shi = 0;
+  uint32_t scode = 0;
+  for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
+    if (e < slo || e >= shi) {
+      const uint32_t sg = hier_seg(a, e);
+      slo = a.bnd[sg];
+      shi = a.bnd[sg + 1];
+      scode = a.seg[sg];
+    }
+    const HierLv L = hier_lv(a, scode);
+    HierPos ld = hier_begin(L), fw = ld;
+    A a0[1], a1[1], a2[1], a3[1];
+    // batches of leaf loads in flight before their folds, as on the
+    // vector path (one load at a time left every element waiting N times)
+    for (int l0 = 0; l0 < N; l0 += kHierBatch) {
+      A raw[kHierBatch];
+#pragma unroll
+      for (int q = 0; q < kHierBatch; ++q) {
+        raw[q] = ld1<DT>(a.sb + (uint64_t)hier_rank(L, ld) * a.ss + e * SZ);
+        hier_step(L, ld);
+      }
+#pragma unroll
+      for (int q = 0; q < kHierBatch; ++q)
+        if (l0 + q < N) {
+          const A x[1] = {raw[q]};
+          hier_take<DT, OP, 1>(L, fw, x, a0, a1, a2, a3);
+          hier_step(L, fw);
+        }
+    }
+    if (a.one)
+      st1<DT>(a.rb + (uint64_t)hier_owner(a, e) * a.rs + e * SZ, a3[0]);
+    else
+      for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, a3[0]);
+  }
+}
+
 template <int DT, int OP>
 __global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
   typedef typename Ty<DT>::A A;
@@ -160,92 +241,101 @@ __global__ __launch_bounds__(kBlock) void k_hier_fused(HierArgs a) {
   constexpr int SZ = Ty<DT>::SZ;
   static_assert(kMaxHierLevels == 4, "four levels");
   const int N = a.N;
-  Tile<V> t;
-  if (a.tpc_log2 >= 0) {
-    t = tile_pow2<V>(blockIdx.x, a.tpc_log2);
-  } else {
-    const uint64_t tile = (uint64_t)kBlock * V;
-    t.e0 = (uint64_t)blockIdx.x * tile;
-    t.e1 = t.e0 + tile < a.M ? t.e0 + tile : a.M;
-    t.c = hier_seg(a, t.e0);
-    t.fast = a.vec_ok && t.e1 - t.e0 == tile && t.e1 <= a.bnd[t.c + 1];
+  const Tile<V> t = hier_tile<V>(a);
+  if (!t.fast) {
+    hier_elems<DT, OP>(a, t);
+    return;
   }
-  if (t.fast) {
-    const uint32_t lane = threadIdx.x * 16u;
-    const char* s0 = a.sb + t.e0 * SZ;
-    const HierLv L = hier_lv(a, a.seg[t.c]);
-    HierPos ld = hier_begin(L), fw = ld;
-    A a0[V], a1[V], a2[V], a3[V];
-    for (int l0 = 0; l0 < N; l0 += kHierBatch) {
-      // every load of the batch is issued before the first fold; past the
-      // last leaf the walk has wrapped to valid ranks whose values go unused
-      u32x4 raw[kHierBatch];
+  const uint32_t lane = threadIdx.x * 16u;
+  const char* s0 = a.sb + t.e0 * SZ;
+  const HierLv L = hier_lv(a, a.seg[t.c]);
+  HierPos ld = hier_begin(L), fw = ld;
+  A a0[V], a1[V], a2[V], a3[V];
+  for (int l0 = 0; l0 < N; l0 += kHierBatch) {
+    // every load of the batch is issued before the first fold; past the
+    // last leaf the walk has wrapped to valid ranks whose values go unused
+    u32x4 raw[kHierBatch];
 #pragma unroll
-      for (int q = 0; q < kHierBatch; ++q) {
-        raw[q] = ldg(s0 + (uint64_t)hier_rank(L, ld) * a.ss + lane);
-        hier_step(L, ld);
-      }
-#pragma unroll
-      for (int q = 0; q < kHierBatch; ++q)
-        if (l0 + q < N) {
-          A x[V];
-          unpack<DT>(raw[q], x);
-          hier_take<DT, OP, V>(L, fw, x, a0, a1, a2, a3);
-          hier_step(L, fw);
-        }
+    for (int q = 0; q < kHierBatch; ++q) {
+      raw[q] = ldg(s0 + (uint64_t)hier_rank(L, ld) * a.ss + lane);
+      hier_step(L, ld);
     }
-    if (a.one) {
-      const int o0 = hier_owner(a, t.e0);
-      if (o0 == hier_owner(a, t.e1 - 1)) {
-        stg(a.rb + (uint64_t)o0 * a.rs + t.e0 * SZ + lane, pack<DT>(a3));
-      } else {  // the tile holds a flat chunk bound
-        const uint64_t e = t.e0 + (uint64_t)threadIdx.x * V;
 #pragma unroll
-        for (int k = 0; k < V; ++k) st1<DT>(a.rb + (uint64_t)hier_owner(a, e + k) * a.rs + (e + k) * SZ, a3[k]);
+    for (int q = 0; q < kHierBatch; ++q)
+      if (l0 + q < N) {
+        A x[V];
+        unpack<DT>(raw[q], x);
+        hier_take<DT, OP, V>(L, fw, x, a0, a1, a2, a3);
+        hier_step(L, fw);
       }
-    } else {
-      const u32x4 o = pack<DT>(a3);
-      char* d = a.rb + t.e0 * SZ;
-      for (int r = 0; r < N; ++r, d += a.rs) stg(d + lane, o);
-    }
-  } else {
-    // a thread's elements are kBlock apart: the segment is looked up again
-    // only when an element leaves the previous one's
-    uint64_t slo = 1, shi = 0;
-    uint32_t scode = 0;
-    for (uint64_t e = t.e0 + threadIdx.x; e < t.e1; e += kBlock) {
-      if (e < slo || e >= shi) {
-        const uint32_t sg = hier_seg(a, e);
-        slo = a.bnd[sg];
-        shi = a.bnd[sg + 1];
-        scode = a.seg[sg];
-      }
-      const HierLv L = hier_lv(a, scode);
-      HierPos ld = hier_begin(L), fw = ld;
-      A a0[1], a1[1], a2[1], a3[1];
-      // batches of leaf loads in flight before their folds, as on the
-      // vector path (one load at a time left every element waiting N times)
-      for (int l0 = 0; l0 < N; l0 += kHierBatch) {
-        A raw[kHierBatch];
+  }
+  hier_store<DT>(a, t, a3);
+}
+
+// The same fold with the grid fixed at compile time (level sizes P0..P3, 1
+// beyond the grid's levels): a leaf's position in every chain is a constant
+// of its index, so the joins are straight-line code without selects, and
+// only the ranks (from the segment's first coordinates) are computed at run
+// time, on the scalar unit.  Taken for bf16 on the grids below, where a lane
+// folds eight elements per leaf and the runtime walk's selects cost most.
+// Measured on the MI355X (best of two runs each, on one machine, rows by the
+// hierarchical workload's layout): bf16 8x8 and 4x4x4 of 2 MiB per rank
+// 5.48-5.68 TB/s against 4.44-4.71; 8x8 and 4x4x4 of 32 MiB (the split
+// form) 5.60-5.98 against 5.48-5.92; 2x2x2, 4x2, 2x4 of 256 MiB 6.33-6.38
+// against 6.23-6.30 at the default 3 workgroups per CU.  For fp32 the
+// runtime walk was as fast or faster (2x2x2 6.36-6.39 against 6.22-6.29).
+template <int P0, int P1, int P2, int P3>
+__device__ __forceinline__ int grid_rank(const HierLv& L, int q) {
+  const int j[4] = {q % P0, (q / P0) % P1, (q / (P0 * P1)) % P2, q / (P0 * P1 * P2)};
+  const int p[4] = {P0, P1, P2, P3};
+  int r = 0;
 #pragma unroll
-        for (int q = 0; q < kHierBatch; ++q) {
-          raw[q] = ld1<DT>(a.sb + (uint64_t)hier_rank(L, ld) * a.ss + e * SZ);
-          hier_step(L, ld);
+  for (int i = 0; i < 4; ++i) {
+    const int c = L.f[i] + j[i];
+    r += (c >= p[i] ? c - p[i] : c) * L.sd[i];
+  }
+  return r;
+}
+
+template <int DT, int OP, int P0, int P1, int P2, int P3>
+__global__ __launch_bounds__(kBlock) void k_hier_grid(HierArgs a) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  constexpr int SZ = Ty<DT>::SZ;
+  constexpr int NL = P0 * P1 * P2 * P3;
+  const Tile<V> t = hier_tile<V>(a);
+  if (!t.fast) {
+    hier_elems<DT, OP>(a, t);
+    return;
+  }
+  const uint32_t lane = threadIdx.x * 16u;
+  const char* s0 = a.sb + t.e0 * SZ;
+  const HierLv L = hier_lv(a, a.seg[t.c]);
+  A a0[V], a1[V], a2[V], a3[V];
+#pragma unroll
+  for (int q0 = 0; q0 < NL; q0 += kHierBatch) {
+    u32x4 raw[kHierBatch];
+#pragma unroll
+    for (int k = 0; k < kHierBatch; ++k)
+      if (q0 + k < NL) raw[k] = ldg(s0 + (uint64_t)grid_rank<P0, P1, P2, P3>(L, q0 + k) * a.ss + lane);
+#pragma unroll
+    for (int k = 0; k < kHierBatch; ++k) {
+      const int q = q0 + k;
+      if (q >= NL) break;
+      const int j0 = q % P0, j1 = (q / P0) % P1, j2 = (q / (P0 * P1)) % P2, j3 = q / (P0 * P1 * P2);
+      A x[V];
+      unpack<DT>(raw[k], x);
+      hier_join<DT, OP, V>(j0 == 0, x, a0);
+      if (j0 + 1 == P0) {
+        hier_join<DT, OP, V>(j1 == 0, a0, a1);
+        if (j1 + 1 == P1) {
+          hier_join<DT, OP, V>(j2 == 0, a1, a2);
+          if (j2 + 1 == P2) hier_join<DT, OP, V>(j3 == 0, a2, a3);
         }
-#pragma unroll
-        for (int q = 0; q < kHierBatch; ++q)
-          if (l0 + q < N) {
-            const A x[1] = {raw[q]};
-            hier_take<DT, OP, 1>(L, fw, x, a0, a1, a2, a3);
-            hier_step(L, fw);
-          }
       }
-      if (a.one)
-        st1<DT>(a.rb + (uint64_t)hier_owner(a, e) * a.rs + e * SZ, a3[0]);
-      else
-        for (int r = 0; r < N; ++r) st1<DT>(a.rb + (uint64_t)r * a.rs + e * SZ, a3[0]);
     }
   }
+  hier_store<DT>(a, t, a3);
 }
 
 // The split form, as the flat ring's: the fold stored once, to the rank that
@@ -285,8 +375,25 @@ hipError_t launch_hier_fused(const Red& r, const int* p, const int* stride, int 
   const int bpc = a.one ? kHierOneBlocks : hier_blocks_per_cu(r.N);
   const unsigned lds = lds_for_blocks_per_cu(r.blocks_per_cu > 0 ? r.blocks_per_cu
                                                                  : one_round_blocks(num_tiles(r.M, r.dt), bpc));
+  // the level sizes (each at most kMaxRanks) as one number
+  const int g4 = ((a.p[0] * 65 + a.p[1]) * 65 + a.p[2]) * 65 + a.p[3];
   hipError_t e = by_dt_op(r.dt, r.op, [&](auto dt, auto op) {
     constexpr int DT = decltype(dt)::value, OP = decltype(op)::value;
+    if constexpr (DT == DT_BF16) {
+#define CC_GRID(P0, P1, P2, P3)                                                  \
+  case ((P0 * 65 + P1) * 65 + P2) * 65 + P3:                                   \
+    CC_LAUNCH((k_hier_grid<DT, OP, P0, P1, P2, P3>), grid, blk, lds, r.st, a); \
+    return hipGetLastError();
+      switch (g4) {
+        CC_GRID(2, 2, 2, 1)
+        CC_GRID(4, 2, 1, 1)
+        CC_GRID(2, 4, 1, 1)
+        CC_GRID(8, 8, 1, 1)
+        CC_GRID(4, 4, 4, 1)
+        default: break;
+      }
+#undef CC_GRID
+    }
     CC_LAUNCH((k_hier_fused<DT, OP>), grid, blk, lds, r.st, a);
     return hipGetLastError();
   });

@@ -18,7 +18,8 @@ from tests.test_gpu_parity import SIZES, check_equal, inputs
 
 pytestmark = pytest.mark.gpu
 
-DIMS = [(2, 2), (4, 2), (2, 4), (3, 2, 2), (2, 3), (8, 2), (2, 2, 2, 2), (4, 1), (1, 4), (2, 1, 3), (8, 8)]
+DIMS = [(2, 2), (4, 2), (2, 4), (2, 2, 2), (3, 2, 2), (2, 3), (8, 2), (2, 2, 2, 2), (4, 1), (1, 4), (2, 1, 3), (8, 8),
+        (4, 4, 4), (2, 1, 2, 2)]
 
 
 def say(*a):
@@ -101,7 +102,7 @@ def _segment_marks(M, dims):
     return np.array(sorted(marks))
 
 
-@pytest.mark.parametrize("dims", [(4, 2), (2, 2, 2), (8, 8), (3, 1, 2, 2)])
+@pytest.mark.parametrize("dims", [(4, 2), (2, 4), (2, 2, 2), (8, 8), (4, 4, 4), (3, 1, 2, 2)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_hierarchical_large_sampled(dims, dtype):
     """Many tiles per segment: fused and stepwise give the same bits

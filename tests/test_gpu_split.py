@@ -101,6 +101,9 @@ HIER_MIN = (4 << 20) // 4       # fp32 elements per rank where the hierarchical 
     ((2, 16), "int32", HIER_MIN, "prod", 0, 0, False),
     ((4, 8), "bf16", 2 * HIER_MIN, "max", 1, 0, False),     # bf16 at 4 MiB, unaligned
     ((2, 2, 8), "f32", HIER_MIN + 5, "sum", 0, 0, True),    # in place
+    ((4, 4, 4), "f32", HIER_MIN - 64, "sum", 0, 0, False),  # below: one launch, compile-time grid
+    ((4, 4, 4), "bf16", 2 * HIER_MIN, "sum", 0, 0, False),  # split, compile-time grid
+    ((8, 8), "bf16", 2 * HIER_MIN - 8, "prod", 0, 0, False),
 ])
 def test_split_hierarchical(case):
     dims, dtype, M, op, offset, pad, in_place = case
