@@ -56,10 +56,13 @@ def emit(rec: dict) -> None:
 def rank_stride_bytes(row_bytes):
     """Rank stride for rows of row_bytes: the payload rounded up to a power of
     two P, plus max(32 KiB, P/1024) (equal offsets of the ranks then spread
-    over the HBM channels)."""
+    over the HBM channels), or plus 1 MiB for P of 4 to 32 MiB, where the
+    smaller pad measured 1-40% slower at 4 to 64 ranks."""
     p = 256
     while p < row_bytes:
         p *= 2
+    if (4 << 20) <= p <= (32 << 20):
+        return p + (1 << 20)
     return p + max(32_768, p // 1024)
 
 

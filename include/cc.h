@@ -162,12 +162,13 @@ typedef struct {
  * padded by 256 KiB lose a third).  A stride of P + max(32 KiB, P / 1024), P
  * the payload rounded up to a power of two, measured best or within 1-2% of
  * the best pad tried for 8 ranks of 256 MiB (256 MiB + 256 KiB), 16 of
- * 128 MiB, 32 of 64 MiB, 64 of 32 MiB and 8 bf16 ranks of 527 MiB
- * (1 GiB + 1 MiB: 6.35 TB/s against 5.82 with no padding).  For 4 to 8
- * ranks of 4 to 32 MiB that pad (32 KiB) is poor (8 fp32 ranks of 16 MiB:
- * 4.25 TB/s against 6.10 with a 512 KiB pad) and a 1 MiB pad measured
- * within 2-6% of the best; pads of 1/128 of the row were slow at every row
- * size tried.  The library takes the stride as given. */
+ * 128 MiB, 32 of 64 MiB and 8 bf16 ranks of 527 MiB (1 GiB + 1 MiB: 6.35
+ * TB/s against 5.82 with no padding).  For P of 4 to 32 MiB that pad (32
+ * KiB) is poor, and P + 1 MiB measured best or within 6% of the best pad
+ * tried (32 KiB to 2.25 MiB) at 4 to 64 ranks (fp32 AllReduce: 8 ranks of
+ * 16 MiB 5.80 TB/s against 3.57 with 32 KiB, 64 of 32 MiB 6.18 against
+ * 6.06); pads of 1/128 of the row were slow at every row size tried.  The
+ * library takes the stride as given. */
 typedef struct {
   void* base;
   size_t rank_stride_bytes;
