@@ -112,11 +112,11 @@ typedef enum {
  *  fuse_depth = 0: fully fused -- one kernel folds every rank's contribution
  *                  in registers in the schedule's order and writes the result
  *                  to every destination (read N*M, write N*M for AllReduce).
- *                  The ring AllReduce from 32 ranks (from 8 MiB per rank for
- *                  4-byte elements, 32 MiB for bf16) runs its two phases as
- *                  two such kernels instead: each chunk's whole fold stored
- *                  to its owner, then the owners' chunks copied to the other
- *                  ranks (the same bits, M more elements read; faster there).
+ *                  The ring AllReduce from 32 ranks of 16 MiB runs its two
+ *                  phases as two such kernels instead: each chunk's whole
+ *                  fold stored to its owner, then the owners' chunks copied
+ *                  to the other ranks (the same bits, M more elements read;
+ *                  faster there).
  *  fuse_depth = 1: stepwise -- one kernel per schedule step, each doing the
  *                  step's reads, combines and writes in HBM.
  *  fuse_depth = k: ring only -- k consecutive ring steps per kernel (other

@@ -343,11 +343,12 @@ __global__ __launch_bounds__(kBlock) void k_hier_grid(HierArgs a) {
 // AllGather's copy from those owners to every other rank.  Taken from 32
 // ranks of 4 MiB on.  Measured on the MI355X (graph replays over rotating
 // buffer sets of 1 GiB or more, rows by the rank-stride rule, fp32 and bf16;
-// split time over one-launch time): 64 ranks (8x8, 4x4x4, 2x32) 0.87-0.99
-// from 4 to 64 MiB per rank; 32 ranks (4x8, 2x16, 2x2x2x4) 0.88-0.96 at 4
-// and 8 MiB, 0.95-1.06 (mean 0.99) from 16 to 64 MiB.  The first launch, N
-// loads and one store per vector, streams best at 4 workgroups per CU (at
-// 64 MiB per rank 2x32 0.89-0.96 against 1.07-1.17 at 2, 0.92-1.00 at 3).
+// split time over one-launch time): 64 ranks (8x8, 4x4x4, 2x32) 0.83-0.92
+// from 4 to 32 MiB per rank, 0.87-0.99 at 64 MiB, 0.96-1.00 at 2 MiB; 32
+// ranks (4x8, 2x16, 2x2x2x4) 0.89-1.00 from 4 to 32 MiB, 0.95-1.01 at 64
+// MiB, 1.03-1.08 at 2 MiB.  The first launch, N loads and one store per
+// vector, streams best at 4 workgroups per CU (at 64 MiB per rank 2x32
+// 0.89-0.96 against 1.07-1.17 at 2, 0.92-1.00 at 3).
 bool hier_split(const Red& r) {
   return r.N >= 32 && r.M * (uint64_t)(16 / vec_elems(r.dt)) >= (4ull << 20);
 }

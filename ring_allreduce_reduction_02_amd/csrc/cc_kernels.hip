@@ -205,20 +205,17 @@ namespace {
 // owner's chunk copied to the other ranks).  It moves (2N+1) M s bytes
 // against the one-launch form's 2 N M s, as two streams that are each read-
 // or write-heavy instead of one with N loads and N stores per vector, which
-// the HBM serves faster from 32 ranks on, for 4-byte elements from 8 MiB per
-// rank and for bf16 from 32 MiB.  Measured on the MI355X (graph replays over
-// rotating buffer sets of 1 GiB or more, rows by the rank-stride rule, two
-// runs of each form; split time over one-launch time, mean and range over N
-// = 32, 34, 36, 40, 44, ..., 64): fp32 8 MiB per rank 0.93 (0.89-0.97), 16
-// MiB 0.96 (0.91-1.01), 32 MiB 0.98 (0.94-1.01), 64 MiB 0.95 (0.92-0.96);
-// bf16 8 MiB 1.05 (0.92-1.14), 16 MiB 1.00 (0.97-1.07), 32 MiB 0.99
-// (0.93-1.04), 64 MiB 0.97 (0.94-1.02).  At 4 MiB per rank and below
-// (1.01-1.24 from 32 ranks, the second launch included) and below 32 ranks
-// (8-30 ranks at 16 and 64 MiB: 0.93-1.16) the one-launch form is as fast or
-// faster.
+// the HBM serves faster from 32 ranks of 16 MiB on.  Measured on the MI355X
+// (graph replays over rotating buffer sets of 1 GiB or more, rows by the
+// rank-stride rule, two runs of each form; split time over one-launch time,
+// mean and range over N = 32, 40, 48, 56, 64): fp32 16 MiB per rank 0.89
+// (0.85-0.93), 32 MiB 0.92 (0.88-0.96), 64 MiB 0.95 (0.92-0.96); bf16
+// 16 MiB 0.93 (0.86-0.97), 32 MiB 0.95 (0.89-0.98), 64 MiB 0.97 (0.94-1.02).
+// At 8 MiB (fp32 1.00, bf16 1.06), 4 MiB and below (1.04-1.24, the second
+// launch included) and below 32 ranks (28 ranks: 0.99-1.26) the one-launch
+// form is as fast or faster.
 bool ring_split(const Red& r) {
-  const uint64_t bytes = r.M * (uint64_t)(16 / vec_elems(r.dt));
-  return r.N >= 32 && bytes >= (r.dt == DT_BF16 ? 32ull << 20 : 8ull << 20);
+  return r.N >= 32 && r.M * (uint64_t)(16 / vec_elems(r.dt)) >= (16ull << 20);
 }
 
 // A grid of 8 to 16 one-vector tiles per CU (4 to 8 MiB per rank) takes two

@@ -1,8 +1,7 @@
 """GPU parity of the split forms of the fused AllReduce against the oracle's
 step simulators, every element of every rank bit for bit.  The ring: a
 ReduceScatter launch that stores each chunk's fold to its owner, then an
-AllGather launch from the owners (from 32 ranks on, from 8 MiB per rank for
-4-byte elements and from 32 MiB for bf16).  The hierarchical AllReduce: the
+AllGather launch from the owners (from 32 ranks of 16 MiB on).  The hierarchical AllReduce: the
 nested fold stored once, to the owner of the element's flat ring chunk, then
 the same AllGather (from 32 ranks of 4 MiB on).  Both sides of the size and
 rank thresholds, ragged chunks and segments, unaligned and in-place buffers,
@@ -20,8 +19,8 @@ from tests.gpu_util import alloc_ranks, bits, download, upload
 
 pytestmark = pytest.mark.gpu
 
-F32_MIN = (8 << 20) // 4        # elements per rank where 4-byte elements split
-BF16_MIN = (32 << 20) // 2
+F32_MIN = (16 << 20) // 4       # elements per rank where the ring splits: 4-byte elements
+BF16_MIN = (16 << 20) // 2      # and bf16
 
 
 def say(*a):
