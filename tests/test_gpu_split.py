@@ -151,3 +151,17 @@ def test_split_forms_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int32), ex.view(torch.int32))
         assert torch.equal(z.view(torch.int32), eh.view(torch.int32))
+
+
+def test_split_ring_seeded_sweep():
+    """Seeded draws around the ring's thresholds: rank counts 28-64, element
+    counts a few elements either side of 16 MiB per rank, every type and
+    operator, aligned or not, against the step simulator."""
+    g = np.random.default_rng(63)
+    for case in range(6):
+        dtype = ["f32", "bf16", "int32"][case % 3]
+        es = 2 if dtype == "bf16" else 4
+        N = int(g.integers(28, 65))
+        M = (16 << 20) // es + int(g.integers(-40, 41))
+        op = ["sum", "max", "prod"][int(g.integers(0, 3))]
+        check(N, M, dtype, op, offset=int(g.integers(0, 2)), pad=int(g.integers(0, 3)) * 8, seed=case)
