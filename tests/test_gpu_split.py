@@ -165,3 +165,29 @@ def test_split_ring_seeded_sweep():
         M = (16 << 20) // es + int(g.integers(-40, 41))
         op = ["sum", "max", "prod"][int(g.integers(0, 3))]
         check(N, M, dtype, op, offset=int(g.integers(0, 2)), pad=int(g.integers(0, 3)) * 8, seed=case)
+
+
+def test_split_hierarchical_seeded_sweep():
+    """Seeded grids of 24-64 ranks in two to four levels, a few elements
+    either side of 4 MiB per rank, every type and operator."""
+    g = np.random.default_rng(64)
+    grids = [(4, 8), (8, 4), (2, 16), (4, 4, 2), (2, 2, 2, 4), (8, 8), (4, 4, 4), (3, 8), (2, 3, 5), (6, 6)]
+    for case in range(5):
+        dims = grids[int(g.integers(0, len(grids)))]
+        dtype = ["f32", "bf16", "int32"][case % 3]
+        es = 2 if dtype == "bf16" else 4
+        N, M = math.prod(dims), (4 << 20) // es + int(g.integers(-40, 41))
+        op = ["sum", "max", "prod"][int(g.integers(0, 3))]
+        offset = int(g.integers(0, 2))
+        say(f"seeded split hierarchical {dims} {dtype} M={M} {op} offset={offset}")
+        xs = inputs(N, M, dtype, op, 100 + case)
+        send = upload(xs, dtype, 0, offset)
+        recv = alloc_ranks(N, M, dtype, 0, offset)
+        ccgpu.all_reduce_hierarchical(send, recv, dims, op=op)
+        torch.cuda.synchronize()
+        got = download(recv, dtype)
+        del send, recv
+        torch.cuda.empty_cache()
+        want = cs.hierarchical_all_reduce(xs, dims, op, dtype)
+        for r in range(N):
+            assert np.array_equal(bits(got[r]), bits(want[r])), (dims, M, dtype, op, offset, r)
