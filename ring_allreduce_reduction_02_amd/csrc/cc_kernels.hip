@@ -36,6 +36,58 @@ namespace {
 // ------------------------------------------------------------------ fused kernels
 
 
+// The ring fold of one 16-byte vector per rank for a runtime rank count, in
+// batches of 8 ranks in the chain's order (the first rank in the first
+// batch), each batch's loads issued before the previous batch is folded,
+// two register sets in turn.  Taken for bf16, whose lanes unpack and add
+// eight values per load: measured on the MI355X (graph replays over
+// rotating buffer sets, rows by the rank-stride rule, N = 6, 12, 20, 24,
+// 28, 40) 16 MiB per rank 5.07-5.40 TB/s against 4.55-4.97, 64 MiB 5.32-6.09
+// against 5.36-5.85, 4 MiB level (3.30-4.16 against 3.31-4.32); fp32 in this
+// form took four times the registers and ran at 2.1-5.6 TB/s against
+// 5.0-6.2, so it keeps the one-set loop of fold_vec.
+template <int DT, int OP>
+__device__ __forceinline__ void fold_ring_pipelined(const char* s0, uint64_t ss, int N, int start, uint32_t lane,
+                                                    typename Ty<DT>::A* acc) {
+  typedef typename Ty<DT>::A A;
+  constexpr int V = Ty<DT>::V;
+  const char* p = s0 + (uint64_t)start * ss;
+  int r = start;
+  auto load8 = [&](u32x4(&buf)[8], int j) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (j + q < N) {
+        if (j + q > 0) {
+          r = r + 1 == N ? 0 : r + 1;
+          p = r == 0 ? s0 : p + ss;
+        }
+        buf[q] = ldg(p + lane);
+      }
+  };
+  auto fold8 = [&](const u32x4(&buf)[8], int j) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (j + q < N) {
+        A x[V];
+        unpack<DT>(buf[q], x);
+        if (j + q == 0) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] = x[i];
+        } else {
+          opv<DT, OP>(x, acc);
+        }
+      }
+  };
+  u32x4 ba[8], bb[8];
+  load8(ba, 0);
+  for (int j = 0; j < N; j += 16) {
+    load8(bb, j + 8);
+    fold8(ba, j);
+    load8(ba, j + 16);
+    fold8(bb, j + 8);
+  }
+}
+
 // AllReduce (rs_mode 0): every chunk's N-1 ReduceScatter steps folded in
 // registers in the schedule's order, then the AllGather as N stores.
 // ReduceScatter (rs_mode 1, ring and halving-doubling): only the owner is
@@ -71,7 +123,12 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     const uint64_t eb = t.e0 * SZ;
     A acc[U][V];
 #pragma unroll
-    for (int u = 0; u < U; ++u) fold_vec<DT, OP, NR, ALG>(a.sb + eb, a.ss, N, start, lane + u * kStep, acc[u], ts);
+    for (int u = 0; u < U; ++u) {
+      if constexpr (ALG == ALG_RING && NR == 0 && DT == DT_BF16)
+        fold_ring_pipelined<DT, OP>(a.sb + eb, a.ss, N, start, lane + u * kStep, acc[u]);
+      else
+        fold_vec<DT, OP, NR, ALG>(a.sb + eb, a.ss, N, start, lane + u * kStep, acc[u], ts);
+    }
     u32x4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) w[u] = pack<DT>(acc[u]);
