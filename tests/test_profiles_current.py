@@ -26,3 +26,16 @@ def test_profile_matches_the_sources(path):
         f"{os.path.basename(path)}: the kernel's sources changed since it was profiled"
     assert 0.95 <= p["traffic_over_algorithmic"] <= 1.05
     assert os.path.exists(path[:-len("_pmc.json")] + ".md")
+
+
+def test_every_profile_entry_has_its_summary():
+    """Each kernel the regeneration script profiles has a committed summary
+    whose recorded kernel is that entry's kernel and source."""
+    from ring_allreduce_reduction_02_amd import profiles_all
+    for name, (_, kernel, csrc, out, _) in profiles_all.ENTRIES.items():
+        path = os.path.join(ROOT, "profiles", out + "_pmc.json")
+        assert os.path.exists(path), name
+        p = json.load(open(path))
+        assert kernel in p["kernel"], (name, p["kernel"])
+        assert csrc in p["kernel_sources"], (name, p["kernel_sources"])
+    assert len(PROFILES) == len({e[3] for e in profiles_all.ENTRIES.values()})
